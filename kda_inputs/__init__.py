@@ -1,0 +1,196 @@
+"""Seeded synthetic inputs for the KDA gated delta-rule core.
+
+This module only draws random numbers and lays them out; it holds none of the
+recurrence's arithmetic.  Both the HIP path (through its tests and the bench)
+and the fp64 oracle are fed from here, so the two always see the same bytes.
+
+Recipe (one per workload, all values fp32 in the end):
+
+* q, k : standard normal draws, then scaled to unit L2 norm over the
+  head dimension as x / sqrt(sum x^2 + eps), eps = 1e-6 (the L2 form the
+  config page gives for the block's front end, field ``l2_eps``), in fp64.
+* v    : standard normal.
+* gate : uniform on [lo, 0] (a per-channel log-decay; lo = -5 or -0.5).
+* beta : sigmoid of a standard normal draw (the core receives beta already
+  passed through a sigmoid, workspace page, field ``beta``).
+* state: 0.02 * standard normal, or zeros.
+
+Every array is a pure function of (workload seed, array id, sequence, row
+block): rows are drawn in blocks of ``ROW_BLOCK`` tokens from
+``SeedSequence([seed, array_id, b, block])``, so a sequence can be generated
+slab by slab, in parallel, and rows T..T+n of a longer draw continue a
+shorter one exactly.
+
+Memory layouts (token-major, heads inside):
+  q, k, v, gate, out : [B][rows][H][D]
+  beta               : [B][rows][H]
+  state              : [B][H][D (key)][D (value)]
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
+
+import numpy as np
+
+D = 128
+ROW_BLOCK = 256
+L2_EPS = 1e-6
+
+# array ids inside a workload's seed space
+ID_STATE, ID_Q, ID_K, ID_V, ID_GATE, ID_BETA = 0, 1, 2, 3, 4, 5
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic workload: sizes, value distributions and seed."""
+
+    name: str
+    mode: str          # "prefill", "decode" or "decode_k"
+    batch: int
+    heads: int
+    T: int             # tokens per sequence (rows walked, k for decode_k)
+    chunk: int         # prefill chunk width (0 for the recurrent forms)
+    gate_lo: float
+    state_std: float   # 0.0 = zero initial state
+    seed: int
+    n_snap: int = 0
+    pad_value: float | None = None   # fill of rows >= T (prefill only)
+    pad_extra_rows: int = 0          # rows allocated beyond T_pad
+    tail_steps: int = 0              # decode steps after the prefill
+
+
+WORKLOADS = {
+    # prefill, 1 sequence, H=2, T=64, C=16, zero state
+    "prefill_h2_t64_c16": Workload("prefill_h2_t64_c16", "prefill", 1, 2, 64, 16, -5.0, 0.0, 1001),
+    # single-token decode, B=64, H=32, 128 MiB state updated in place
+    "decode_b64_h32": Workload("decode_b64_h32", "decode", 64, 32, 1, 0, -5.0, 0.02, 1002),
+    # chunked prefill, T=8192, H=32, C=64, pad filled with 1e4 plus one extra chunk
+    "prefill_h32_t8192_c64": Workload("prefill_h32_t8192_c64", "prefill", 1, 32, 8192, 64, -5.0, 0.02, 1003,
+                                      pad_value=1e4, pad_extra_rows=64),
+    # decode_k speculative verify, k=4 rows, B=128, H=32, 4 snapshots
+    "decode_k4_b128_h32": Workload("decode_k4_b128_h32", "decode_k", 128, 32, 4, 0, -5.0, 0.02, 1004, n_snap=4),
+    # long-context prefill 4 x 32768, slow decay, then 16 decode steps
+    "prefill_b4_h32_t32768_c64": Workload("prefill_b4_h32_t32768_c64", "prefill", 4, 32, 32768, 64, -0.5, 0.02,
+                                          1005, tail_steps=16),
+}
+
+
+def _rng(seed: int, array_id: int, b: int, block: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, array_id, b, block])))
+
+
+def _draw_rows(seed: int, array_id: int, b: int, r0: int, r1: int, heads: int, per_row: int,
+               kind: str, gate_lo: float = 0.0) -> np.ndarray:
+    """Rows [r0, r1) of one array of one sequence, shape [r1-r0, heads*per_row], fp64."""
+    out = np.empty((r1 - r0, heads * per_row), dtype=np.float64)
+    blk0, blk1 = r0 // ROW_BLOCK, (r1 - 1) // ROW_BLOCK
+    for blk in range(blk0, blk1 + 1):
+        lo = max(r0, blk * ROW_BLOCK)
+        hi = min(r1, (blk + 1) * ROW_BLOCK)
+        n_prefix = hi - blk * ROW_BLOCK          # draw the block's prefix, keep [lo, hi)
+        g = _rng(seed, array_id, b, blk)
+        if kind == "normal":
+            x = g.standard_normal((n_prefix, heads * per_row), dtype=np.float32).astype(np.float64)
+        elif kind == "uniform":
+            x = g.random((n_prefix, heads * per_row), dtype=np.float32).astype(np.float64)
+        else:
+            raise ValueError(kind)
+        out[lo - r0:hi - r0] = x[lo - blk * ROW_BLOCK:]
+    if kind == "uniform":
+        out = gate_lo * out          # [lo, 0]
+    return out
+
+
+def _l2_rows(x: np.ndarray, heads: int) -> np.ndarray:
+    y = x.reshape(x.shape[0], heads, D)
+    return (y / np.sqrt((y * y).sum(-1, keepdims=True) + L2_EPS)).reshape(x.shape)
+
+
+def sequence_rows(seed: int, b: int, r0: int, r1: int, heads: int, gate_lo: float) -> dict:
+    """q, k, v, gate [rows, H, D] and beta [rows, H] (fp32) for rows [r0, r1) of sequence b."""
+    q = _l2_rows(_draw_rows(seed, ID_Q, b, r0, r1, heads, D, "normal"), heads)
+    k = _l2_rows(_draw_rows(seed, ID_K, b, r0, r1, heads, D, "normal"), heads)
+    v = _draw_rows(seed, ID_V, b, r0, r1, heads, D, "normal")
+    gate = _draw_rows(seed, ID_GATE, b, r0, r1, heads, D, "uniform", gate_lo)
+    z = _draw_rows(seed, ID_BETA, b, r0, r1, heads, 1, "normal")
+    beta = 1.0 / (1.0 + np.exp(-z))
+    n = r1 - r0
+    return {
+        "q": q.astype(np.float32).reshape(n, heads, D),
+        "k": k.astype(np.float32).reshape(n, heads, D),
+        "v": v.astype(np.float32).reshape(n, heads, D),
+        "gate": gate.astype(np.float32).reshape(n, heads, D),
+        "beta": beta.astype(np.float32).reshape(n, heads),
+    }
+
+
+def initial_state(seed: int, b: int, heads: int, std: float) -> np.ndarray:
+    """[H, D, D] fp32 initial state of sequence b (zeros when std == 0)."""
+    if std == 0.0:
+        return np.zeros((heads, D, D), dtype=np.float32)
+    g = _rng(seed, ID_STATE, b, 0)
+    return (std * g.standard_normal((heads, D, D), dtype=np.float32)).astype(np.float32)
+
+
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def make_batch(seed: int, batch: int, heads: int, rows: int, gate_lo: float, state_std: float,
+               alloc_rows: int | None = None, pad_value: float | None = None, row0: int = 0,
+               threads: int | None = None) -> dict:
+    """A whole batch of inputs.
+
+    ``rows`` token rows [row0, row0+rows) of each sequence are drawn; the arrays are
+    allocated with ``alloc_rows`` >= rows rows per sequence, the rows past ``rows``
+    filled with ``pad_value`` (NaN-free zeros when None).
+    """
+    alloc_rows = rows if alloc_rows is None else alloc_rows
+    assert alloc_rows >= rows
+    fill = 0.0 if pad_value is None else pad_value
+    arrays = {
+        name: np.full((batch, alloc_rows, heads, D), fill, dtype=np.float32) for name in ("q", "k", "v", "gate")
+    }
+    arrays["beta"] = np.full((batch, alloc_rows, heads), fill, dtype=np.float32)
+    state = np.empty((batch, heads, D, D), dtype=np.float32)
+
+    jobs = []
+    for b in range(batch):
+        for s in range(0, rows, ROW_BLOCK * 4):
+            jobs.append((b, s, min(rows, s + ROW_BLOCK * 4)))
+
+    def work(job):
+        b, s, e = job
+        part = sequence_rows(seed, b, row0 + s, row0 + e, heads, gate_lo)
+        for name, val in part.items():
+            arrays[name][b, s:e] = val
+
+    def work_state(b):
+        state[b] = initial_state(seed, b, heads, state_std)
+
+    with ThreadPoolExecutor(threads or default_threads()) as ex:
+        list(ex.map(work, jobs))
+        list(ex.map(work_state, range(batch)))
+    arrays["state"] = state
+    return arrays
+
+
+def workload_inputs(w: Workload, batch: int | None = None, heads: int | None = None, T: int | None = None,
+                    threads: int | None = None) -> dict:
+    """Inputs of a workload, optionally at a reduced batch / heads / T (same seeds).
+
+    Prefill inputs are allocated with T_pad = ceil(T/chunk)*chunk rows plus
+    ``pad_extra_rows``; rows >= T hold ``pad_value``.
+    """
+    B = w.batch if batch is None else batch
+    H = w.heads if heads is None else heads
+    T_ = w.T if T is None else T
+    if w.mode == "prefill":
+        t_pad = -(-T_ // w.chunk) * w.chunk
+        alloc = t_pad + w.pad_extra_rows
+    else:
+        alloc = T_
+    return make_batch(w.seed, B, H, T_, w.gate_lo, w.state_std, alloc_rows=alloc, pad_value=w.pad_value,
+                      threads=threads)

@@ -1,0 +1,116 @@
+"""fp64 CPU oracle of the KDA gated delta-rule core (test infrastructure only).
+
+Only the tests, ``__graft_entry__.smoke()`` and the bench's ``cpu_baseline``
+leg may import this package.  It wraps ``kda_oracle.c`` through ctypes and
+takes / returns numpy arrays; see that file's header for the exact recurrence,
+the chunked form and every layout.
+
+Parity status: pinned.  tests/test_oracle_pins.py checks it against closed
+forms, exact rational brute force on tiny inputs and invariants of the method
+(state untouched at beta=0/gate=0, the delta-rule fixed point S^T k = v at
+beta=1, per-row exponential averages for basis keys, decay-before-update order
+on a scalar head, chunked == serial, pad independence, linearity, column
+equivariance, continuation).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+_f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
+_f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        path = _build.LIB
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+            _build.build()
+        lib = ctypes.CDLL(path)
+        i = ctypes.c_int
+        lib.kda_oracle_serial.argtypes = [_f32p] * 5 + [_f64p, _f64p, ctypes.c_void_p] + [i] * 7
+        lib.kda_oracle_serial.restype = i
+        lib.kda_oracle_chunked.argtypes = [_f32p] * 5 + [_f64p, _f64p] + [i] * 7
+        lib.kda_oracle_chunked.restype = i
+        lib.kda_oracle_chunk_stages.argtypes = [_f32p] * 5 + [i] * 8 + [_f64p, _f64p] + [ctypes.c_void_p] * 7
+        lib.kda_oracle_chunk_stages.restype = i
+        lib.kda_oracle_threads.argtypes = [i]
+        lib.kda_oracle_threads.restype = i
+        _lib = lib
+    return _lib
+
+
+def _f32(x):
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def _shape(q, beta):
+    if q.ndim != 4:
+        raise ValueError("q/k/v/gate must be [B][rows][H][D]")
+    B, rows, H, D = q.shape
+    if beta.shape != (B, rows, H):
+        raise ValueError("beta must be [B][rows][H]")
+    return B, rows, H, D
+
+
+def threads(requested: int = 0) -> int:
+    return _load().kda_oracle_threads(requested)
+
+
+def serial(q, k, v, gate, beta, state, T: int | None = None, n_snap: int = 0, nthreads: int = 0):
+    """Token-by-token fp64 recurrence.
+
+    Returns (out [B][T][H][D], state [B][H][D][D], snaps [n_snap][B][H][D][D] or None,
+    threads used), all fp64.  ``state`` may be float32 or float64; it is not modified.
+    """
+    q, k, v, gate, beta = map(_f32, (q, k, v, gate, beta))
+    B, rows, H, D = _shape(q, beta)
+    T = rows if T is None else T
+    st = np.array(state, dtype=np.float64, order="C", copy=True)
+    if st.shape != (B, H, D, D):
+        raise ValueError("state must be [B][H][D][D]")
+    out = np.zeros((B, T, H, D), dtype=np.float64)
+    snaps = np.zeros((n_snap, B, H, D, D), dtype=np.float64) if n_snap > 0 else None
+    sp = snaps.ctypes.data if snaps is not None else None
+    rc = _load().kda_oracle_serial(q, k, v, gate, beta, st, out, sp, n_snap, B, H, D, T, rows, nthreads)
+    if rc < 1:
+        raise ValueError("kda_oracle_serial rejected its arguments")
+    return out, st, snaps, rc
+
+
+def chunked(q, k, v, gate, beta, state, chunk: int, T: int | None = None, nthreads: int = 0):
+    """Chunked (WY/UT) fp64 form; returns (out, state, threads used)."""
+    q, k, v, gate, beta = map(_f32, (q, k, v, gate, beta))
+    B, rows, H, D = _shape(q, beta)
+    T = rows if T is None else T
+    st = np.array(state, dtype=np.float64, order="C", copy=True)
+    out = np.zeros((B, T, H, D), dtype=np.float64)
+    rc = _load().kda_oracle_chunked(q, k, v, gate, beta, st, out, B, H, D, T, rows, chunk, nthreads)
+    if rc < 1:
+        raise ValueError("kda_oracle_chunked rejected its arguments")
+    return out, st, rc
+
+
+def chunk_stages(q, k, v, gate, beta, S0, b: int, h: int, t0: int, n: int) -> dict:
+    """Intermediates of one chunk (rows [t0, t0+n) of (b, h)) from incoming state S0 [D][D]."""
+    q, k, v, gate, beta = map(_f32, (q, k, v, gate, beta))
+    B, rows, H, D = _shape(q, beta)
+    S = np.array(S0, dtype=np.float64, order="C", copy=True)
+    res = {
+        "O": np.zeros((n, D)), "G": np.zeros((n, D)), "A": np.zeros((n, n)), "Tinv": np.zeros((n, n)),
+        "W": np.zeros((n, D)), "U": np.zeros((n, D)), "M": np.zeros((n, n)), "Delta": np.zeros((n, D)),
+    }
+    rc = _load().kda_oracle_chunk_stages(
+        q, k, v, gate, beta, B, H, D, rows, b, h, t0, n, S, res["O"], res["G"].ctypes.data,
+        res["A"].ctypes.data, res["Tinv"].ctypes.data, res["W"].ctypes.data, res["U"].ctypes.data,
+        res["M"].ctypes.data, res["Delta"].ctypes.data)
+    if rc != 0:
+        raise ValueError("kda_oracle_chunk_stages rejected its arguments")
+    res["S"] = S
+    return res
