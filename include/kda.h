@@ -1,0 +1,147 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) KDA gated delta-rule core.
+ *
+ * The core is the per-head gated delta-rule recurrence over an FP32
+ * [heads, 128, 128] key-major state (config page, config.rs:
+ * Glm5NextKdaConfig::recurrent_state_elems; head_dim is fixed at 128 by
+ * Glm5NextKdaConfig::validate).  For every token t of a sequence and every
+ * head, with gate the per-channel log-decay (workspace page, field "gate")
+ * and beta already passed through a sigmoid (workspace page, field "beta"):
+ *
+ *     S <- diag(exp(gate_t)) S                 decay, one factor per key row
+ *     delta = beta_t (v_t - S^T k_t)
+ *     S <- S + k_t delta^T
+ *     out_t = S^T q_t                          post-update state, no scale
+ *
+ * The decay comes before the delta correction: the recurrent kernels of the
+ * kernel-table page (Glm5NextKdaKernels, fields recurrent / recurrent_smem)
+ * share the *decayed* state column between their two passes.  q and k are
+ * expected L2-normalised and v raw (module page, pipeline line); the core
+ * itself normalises nothing.  A caller that wants a 1/sqrt(d) attention scale
+ * pre-scales q.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  * All tensor pointers are DEVICE pointers to contiguous FP32 memory owned
+ *    by the caller.  The library allocates nothing and keeps no state between
+ *    calls (module page: the forward calls allocate nothing and write only
+ *    into the caller's workspace and sequence state).
+ *  * Layouts (token-major, heads inside, D = 128):
+ *        q, k, v, gate, out : [batch][rows][heads][D]
+ *        beta               : [batch][rows][heads]
+ *        state              : [batch][heads][D key][D value]  (value index contiguous)
+ *        snapshots          : [n_snapshots][batch][heads][D][D]
+ *    rows = T_pad = ceil(T / chunk) * chunk for kda_chunk_prefill (the
+ *    workspace page pads prefill buffers to whole chunks), rows = T for
+ *    kda_recurrent_k and rows = 1 for kda_recurrent_step.
+ *  * Inputs are read-only.  state is read and updated in place (layer page:
+ *    decode updates the state in place).  out rows >= T are never written.
+ *  * out, state, snapshots and workspace must not overlap each other or any
+ *    input; an overlap of the ranges implied by the sizes is refused.
+ *  * stream is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *    are asynchronous on that stream: a return of KDA_OK means the work was
+ *    validated and enqueued.  Faults during execution surface at the caller's
+ *    next synchronisation, as for any HIP launch.
+ *  * Every argument check runs on the host before anything is enqueued; on any
+ *    error nothing is launched and no buffer is touched (config page:
+ *    validate refuses a bad geometry instead of running it).
+ *  * Calls are reentrant; concurrent calls on different streams are safe as
+ *    long as their buffers do not overlap.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_HEAD_DIM 128
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = -1, /* null pointer, size < 1, n_snapshots out of range, overlap, overflow */
+    KDA_ERR_UNSUPPORTED = -2, /* chunk not in {16, 32, 64}                                             */
+    KDA_ERR_WORKSPACE = -3,   /* workspace smaller than kda_chunk_prefill_workspace_bytes()           */
+    KDA_ERR_HIP = -4          /* the HIP runtime refused a launch                                     */
+} kda_status;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* kda_status_string(int status);
+
+/*
+ * Workspace bytes kda_chunk_prefill needs for (batch, heads, T, chunk), or 0
+ * when the arguments are invalid (batch/heads/T < 1, unsupported chunk, size
+ * overflow).  The workspace holds, per (sequence, head, chunk), the chunk's
+ * WY/UT intermediates written by the prepare kernel and read by the scan
+ * kernel (kernel-table page, fields chunk_prepare / chunk_scan).  It is
+ * scratch: contents on entry are ignored and undefined on exit.
+ */
+size_t kda_chunk_prefill_workspace_bytes(int batch, int heads, int T, int chunk);
+
+/*
+ * Chunked prefill over T tokens per sequence, starting from the carried
+ * state (layer page, Glm5NextKdaLayer::prefill; kernel-table page,
+ * chunk_prepare + chunk_scan).
+ *
+ *   q, k, v, gate : [batch][T_pad][heads][128], T_pad = ceil(T/chunk)*chunk
+ *   beta          : [batch][T_pad][heads]
+ *   state         : [batch][heads][128][128], in: carried state, out: state after token T-1
+ *   out           : [batch][T_pad][heads][128]; rows t < T receive the core output
+ *   chunk         : 16, 32 or 64 (changes rounding only, never the result beyond it)
+ *   workspace     : device scratch of at least kda_chunk_prefill_workspace_bytes() bytes
+ *
+ * Rows t >= T of every input may hold anything, NaN and inf included: the
+ * kernels select them away before any arithmetic (layer page,
+ * prefill_with_pad_fill: positions at or past t are ignored in-kernel).
+ * Accuracy: the chunk factorisation splits each pairwise decay
+ * exp(G_r - G_s) into two factors taken about a reference row at most 8
+ * rows away, so every factor stays finite as long as the gates of any 8
+ * consecutive tokens sum to more than -88 per channel (for instance every
+ * gate >= -11); the pages bound the gate from below (config page,
+ * gate_lower_bound).
+ */
+int kda_chunk_prefill(const float* q, const float* k, const float* v, const float* gate, const float* beta,
+                      float* state, float* out, int batch, int heads, int T, int chunk, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * One recurrent decode step: one token per sequence (layer page,
+ * Glm5NextKdaLayer::decode; kernel-table page, recurrent_smem).  Each head
+ * state is read from HBM once and written once; the decayed state stays in
+ * registers between the read-out and the update.
+ *
+ *   q, k, v, gate, out : [batch][1][heads][128];  beta : [batch][1][heads]
+ *   state              : [batch][heads][128][128], updated in place
+ *
+ * Bit-for-bit equal to kda_recurrent_k with T = 1.
+ */
+int kda_recurrent_step(const float* q, const float* k, const float* v, const float* gate, const float* beta,
+                       float* state, float* out, int batch, int heads, void* stream);
+
+/*
+ * T rows of each sequence walked one at a time with the state held on chip
+ * (layer page, Glm5NextKdaLayer::decode_k: speculative verify and prefill
+ * sub-chunks; the row-serial walker stateful_row).
+ *
+ *   q, k, v, gate, out : [batch][T][heads][128];  beta : [batch][T][heads]
+ *   state              : [batch][heads][128][128]; out: state after row T-1
+ *   snapshots          : [n_snapshots][batch][heads][128][128]; snapshot t
+ *                        receives the state after row t, for t < n_snapshots
+ *                        (rows past n_snapshots take none); may be NULL when
+ *                        n_snapshots == 0
+ *   n_snapshots        : 0 <= n_snapshots <= T
+ *
+ * T == 0 is refused (the layer page refuses k == 0).  out, the final state
+ * and every snapshot equal T successive kda_recurrent_step calls bit for bit.
+ */
+int kda_recurrent_k(const float* q, const float* k, const float* v, const float* gate, const float* beta,
+                    float* state, float* out, float* snapshots, int n_snapshots, int batch, int heads, int T,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,173 @@
+"""Python binding of the MI355X KDA gated delta-rule core.
+
+Argument marshalling only: every step of the core runs in the HIP kernels of
+``libkda_amd.so`` behind the C ABI of ``include/kda.h``.  The functions carry
+the C names; tensors must be contiguous float32 CUDA (HIP) tensors in the
+layouts the header documents.  PyTorch provides device memory and the stream
+(the current torch stream unless one is given).  There is no CPU fallback: if
+the library cannot be loaded every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda_amd.so")
+HEAD_DIM = 128
+
+KDA_OK = 0
+KDA_ERR_INVALID_ARG = -1
+KDA_ERR_UNSUPPORTED = -2
+KDA_ERR_WORKSPACE = -3
+KDA_ERR_HIP = -4
+
+EXPORTED = ("kda_status_string", "kda_chunk_prefill_workspace_bytes", "kda_chunk_prefill", "kda_recurrent_step",
+            "kda_recurrent_k")
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {kda_status_string(status)} ({status})")
+        self.status = status
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libkda_amd.so (building it first only if it does not exist)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(path)
+    p, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.kda_status_string.argtypes = [i]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_chunk_prefill_workspace_bytes.argtypes = [i, i, i, i]
+    lib.kda_chunk_prefill_workspace_bytes.restype = sz
+    lib.kda_chunk_prefill.argtypes = [p] * 7 + [i] * 4 + [p, sz, p]
+    lib.kda_chunk_prefill.restype = i
+    lib.kda_recurrent_step.argtypes = [p] * 7 + [i, i, p]
+    lib.kda_recurrent_step.restype = i
+    lib.kda_recurrent_k.argtypes = [p] * 8 + [i] * 4 + [p]
+    lib.kda_recurrent_k.restype = i
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def kda_status_string(status: int) -> str:
+    return load_library().kda_status_string(int(status)).decode()
+
+
+def kda_chunk_prefill_workspace_bytes(batch: int, heads: int, T: int, chunk: int) -> int:
+    return int(load_library().kda_chunk_prefill_workspace_bytes(batch, heads, T, chunk))
+
+
+def _stream_ptr(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(name: str, t: torch.Tensor, shape: tuple) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _vec_shapes(q: torch.Tensor):
+    if q.dim() != 4 or q.shape[-1] != HEAD_DIM:
+        raise ValueError(f"q must be [batch][rows][heads][{HEAD_DIM}]")
+    B, rows, H, _ = q.shape
+    return B, rows, H
+
+
+def kda_recurrent_k(q, k, v, gate, beta, state, out=None, snapshots=None, n_snapshots: int = 0, stream=None):
+    """Walk the rows of each sequence one at a time (decode_k).  Returns ``out``.
+
+    q, k, v, gate: [B][T][H][128]; beta: [B][T][H]; state: [B][H][128][128] (in place);
+    snapshots: [>= n_snapshots][B][H][128][128] receives the state after rows 0..n_snapshots-1.
+    """
+    B, T, H = _vec_shapes(q)
+    vs = (B, T, H, HEAD_DIM)
+    if out is None:
+        out = torch.empty(vs, dtype=torch.float32, device=q.device)
+    args = [_check(n, t, vs) for n, t in (("q", q), ("k", k), ("v", v), ("gate", gate))]
+    args.append(_check("beta", beta, (B, T, H)))
+    args.append(_check("state", state, (B, H, HEAD_DIM, HEAD_DIM)))
+    args.append(_check("out", out, vs))
+    snap_ptr = None
+    if n_snapshots:
+        if snapshots is None or snapshots.dim() != 5 or snapshots.shape[0] < n_snapshots:
+            raise ValueError("snapshots must be [>= n_snapshots][B][H][128][128]")
+        snap_ptr = _check("snapshots", snapshots, (snapshots.shape[0], B, H, HEAD_DIM, HEAD_DIM))
+    rc = load_library().kda_recurrent_k(*args, snap_ptr, int(n_snapshots), B, H, T, _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_recurrent_k", rc)
+    return out
+
+
+def kda_recurrent_step(q, k, v, gate, beta, state, out=None, stream=None):
+    """One decode token per sequence.  q, k, v, gate: [B][1][H][128]; beta: [B][1][H]."""
+    B, rows, H = _vec_shapes(q)
+    if rows != 1:
+        raise ValueError("kda_recurrent_step takes one row per sequence")
+    vs = (B, 1, H, HEAD_DIM)
+    if out is None:
+        out = torch.empty(vs, dtype=torch.float32, device=q.device)
+    args = [_check(n, t, vs) for n, t in (("q", q), ("k", k), ("v", v), ("gate", gate))]
+    args.append(_check("beta", beta, (B, 1, H)))
+    args.append(_check("state", state, (B, H, HEAD_DIM, HEAD_DIM)))
+    args.append(_check("out", out, vs))
+    rc = load_library().kda_recurrent_step(*args, B, H, _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_recurrent_step", rc)
+    return out
+
+
+def kda_chunk_prefill(q, k, v, gate, beta, state, T: int, chunk: int, out=None, workspace=None, stream=None):
+    """Chunked prefill of T tokens per sequence.  Returns ``out``.
+
+    q, k, v, gate, out: [B][T_pad][H][128] with T_pad = ceil(T/chunk)*chunk; beta: [B][T_pad][H];
+    state: [B][H][128][128] (in place); workspace: a uint8 CUDA tensor of at least
+    kda_chunk_prefill_workspace_bytes(B, H, T, chunk) bytes (allocated here when None).
+    """
+    B, rows, H = _vec_shapes(q)
+    if chunk not in (16, 32, 64):
+        raise KdaError("kda_chunk_prefill", KDA_ERR_UNSUPPORTED)
+    t_pad = -(-int(T) // chunk) * chunk
+    if rows != t_pad:
+        raise ValueError(f"inputs must hold T_pad = {t_pad} rows per sequence, got {rows}")
+    vs = (B, t_pad, H, HEAD_DIM)
+    if out is None:
+        out = torch.empty(vs, dtype=torch.float32, device=q.device)
+    need = kda_chunk_prefill_workspace_bytes(B, H, int(T), chunk)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if not (workspace.device.type == "cuda" and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    args = [_check(n, t, vs) for n, t in (("q", q), ("k", k), ("v", v), ("gate", gate))]
+    args.append(_check("beta", beta, (B, t_pad, H)))
+    args.append(_check("state", state, (B, H, HEAD_DIM, HEAD_DIM)))
+    args.append(_check("out", out, vs))
+    rc = load_library().kda_chunk_prefill(*args, B, H, int(T), chunk, workspace.data_ptr(), ws_bytes,
+                                          _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_chunk_prefill", rc)
+    return out

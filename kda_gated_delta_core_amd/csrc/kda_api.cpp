@@ -1,0 +1,130 @@
+// C ABI of the KDA core (declared in include/kda.h): argument checks on the
+// host, then launches on the caller's stream.  Nothing here allocates.
+#include "kda.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda_internal.h"
+
+#define KDA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int64_t kMaxElems = INT64_C(1) << 46;  // keeps every byte offset far inside int64
+
+// a * b * ..., or -1 when any factor is < 0 or the product passes kMaxElems
+int64_t mul(std::initializer_list<int64_t> xs)
+{
+    int64_t p = 1;
+    for (int64_t x : xs) {
+        if (x < 0) return -1;
+        if (x != 0 && p > kMaxElems / x) return -1;
+        p *= x;
+    }
+    return p;
+}
+
+struct Range {
+    const void* p;
+    int64_t bytes;
+};
+
+bool overlap(const Range& a, const Range& b)
+{
+    if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + (uintptr_t)b.bytes && b0 < a0 + (uintptr_t)a.bytes;
+}
+
+// every written range against every other range
+bool any_overlap(const Range* ranges, int n, int n_written)
+{
+    for (int i = 0; i < n_written; ++i)
+        for (int j = 0; j < n; ++j)
+            if (j != i && overlap(ranges[i], ranges[j])) return true;
+    return false;
+}
+
+bool chunk_ok(int chunk) { return chunk == 16 || chunk == 32 || chunk == 64; }
+
+int64_t prefill_ws_bytes(int batch, int heads, int T, int chunk)
+{
+    if (batch < 1 || heads < 1 || T < 1 || !chunk_ok(chunk)) return -1;
+    const int64_t nchunks = ((int64_t)T + chunk - 1) / chunk;
+    const int64_t recs = mul({batch, heads, nchunks});
+    if (recs < 0 || recs > 0x7fffffffLL) return -1;  // one prepare workgroup per record
+    const int64_t floats = mul({recs, (int64_t)kda::chunk_record_floats(chunk)});
+    return floats < 0 ? -1 : floats * 4;
+}
+
+}  // namespace
+
+KDA_API const char* kda_status_string(int status)
+{
+    switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: null pointer, size out of range or overlapping buffers";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: chunk must be 16, 32 or 64";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace smaller than kda_chunk_prefill_workspace_bytes()";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime refused a launch";
+    default: return "unknown kda status";
+    }
+}
+
+KDA_API size_t kda_chunk_prefill_workspace_bytes(int batch, int heads, int T, int chunk)
+{
+    const int64_t b = prefill_ws_bytes(batch, heads, T, chunk);
+    return b < 0 ? 0 : (size_t)b;
+}
+
+KDA_API int kda_chunk_prefill(const float* q, const float* k, const float* v, const float* gate, const float* beta,
+                              float* state, float* out, int batch, int heads, int T, int chunk, void* workspace,
+                              size_t workspace_bytes, void* stream)
+{
+    if (!q || !k || !v || !gate || !beta || !state || !out) return KDA_ERR_INVALID_ARG;
+    if (batch < 1 || heads < 1 || T < 1) return KDA_ERR_INVALID_ARG;
+    if (!chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
+    const int64_t need = prefill_ws_bytes(batch, heads, T, chunk);
+    const int64_t t_pad = ((int64_t)T + chunk - 1) / chunk * chunk;
+    const int64_t vec = mul({batch, t_pad, heads, KDA_HEAD_DIM});
+    const int64_t sca = mul({batch, t_pad, heads});
+    const int64_t st = mul({batch, heads, KDA_HEAD_DIM, KDA_HEAD_DIM});
+    if (need < 0 || vec < 0 || sca < 0 || st < 0 || t_pad > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)batch * heads > 0x7fffffffLL / 64) return KDA_ERR_INVALID_ARG;  // scan grid
+    if (!workspace || workspace_bytes < (size_t)need) return KDA_ERR_WORKSPACE;
+    const Range r[] = {{out, vec * 4}, {state, st * 4}, {workspace, need}, {q, vec * 4}, {k, vec * 4},
+                       {v, vec * 4},   {gate, vec * 4}, {beta, sca * 4}};
+    if (any_overlap(r, 8, 3)) return KDA_ERR_INVALID_ARG;
+    const int rc = kda::launch_chunk_prefill(q, k, v, gate, beta, state, out, batch, heads, T, (int)t_pad, chunk,
+                                             static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
+    return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+KDA_API int kda_recurrent_k(const float* q, const float* k, const float* v, const float* gate, const float* beta,
+                            float* state, float* out, float* snapshots, int n_snapshots, int batch, int heads,
+                            int T, void* stream)
+{
+    if (!q || !k || !v || !gate || !beta || !state || !out) return KDA_ERR_INVALID_ARG;
+    if (batch < 1 || heads < 1 || T < 1) return KDA_ERR_INVALID_ARG;
+    if (n_snapshots < 0 || n_snapshots > T || (n_snapshots > 0 && !snapshots)) return KDA_ERR_INVALID_ARG;
+    const int64_t vec = mul({batch, T, heads, KDA_HEAD_DIM});
+    const int64_t sca = mul({batch, T, heads});
+    const int64_t st = mul({batch, heads, KDA_HEAD_DIM, KDA_HEAD_DIM});
+    const int64_t sn = mul({n_snapshots, batch, heads, KDA_HEAD_DIM, KDA_HEAD_DIM});
+    if (vec < 0 || sca < 0 || st < 0 || sn < 0) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)batch * heads > kda::recurrent_max_units()) return KDA_ERR_INVALID_ARG;
+    const Range r[] = {{out, vec * 4}, {state, st * 4}, {n_snapshots ? snapshots : nullptr, sn * 4},
+                       {q, vec * 4},   {k, vec * 4},    {v, vec * 4},
+                       {gate, vec * 4}, {beta, sca * 4}};
+    if (any_overlap(r, 8, 3)) return KDA_ERR_INVALID_ARG;
+    const int rc = kda::launch_recurrent(q, k, v, gate, beta, state, out, n_snapshots ? snapshots : nullptr,
+                                         n_snapshots, batch, heads, T, static_cast<hipStream_t>(stream));
+    return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+KDA_API int kda_recurrent_step(const float* q, const float* k, const float* v, const float* gate, const float* beta,
+                               float* state, float* out, int batch, int heads, void* stream)
+{
+    return kda_recurrent_k(q, k, v, gate, beta, state, out, nullptr, 0, batch, heads, 1, stream);
+}

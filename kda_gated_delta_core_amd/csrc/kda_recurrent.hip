@@ -1,0 +1,162 @@
+// Recurrent (decode) form of the KDA gated delta-rule core, gfx950.
+//
+// One kernel serves both decode entry points: a single token per sequence is
+// the T = 1 case of the row-serial walk, so kda_recurrent_step and
+// kda_recurrent_k execute the same instructions and agree bit for bit
+// (layer page, Glm5NextKdaLayer::decode_k: the row path must match k serial
+// decodes exactly).
+//
+// Memory plan (kernel-table page, recurrent_smem: one state read and one
+// state write per step, the decayed state kept on chip between the two
+// passes).  A workgroup owns one (sequence, head, value slice); its 256
+// threads load the slice of the 64 KiB head state straight into VGPRs with
+// 16-byte loads (thread = 4 adjacent value columns x kRows key rows, a wave
+// covers whole 512-byte rows), keep it there for all rows of the walk, and
+// write it back once.  Per row the only cross-thread traffic is the
+// reduction of the read-outs over the key index: a xor-shuffle across the
+// row groups inside the wave plus one LDS exchange across the four waves.
+// No atomics: every thread sums in the same fixed order, so results are
+// deterministic.
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <int NSLICE>
+struct RecGeom {
+    static constexpr int kThreads = 256;
+    static constexpr int kCols = kD / NSLICE;           // value columns per workgroup
+    static constexpr int kColGroups = kCols / 4;        // float4 column groups
+    static constexpr int kRowGroups = kThreads / kColGroups;
+    static constexpr int kRows = kD / kRowGroups;       // key rows per thread
+    static constexpr int kWaves = kThreads / 64;
+    static_assert(kColGroups <= 64 && 64 % kColGroups == 0, "a wave must hold whole row groups");
+};
+
+// Value slices per head.  Part of the arithmetic contract: the reduction tree
+// depends on it, and both decode entry points use this one instance.
+constexpr int kRecSlices = 2;
+
+template <int NSLICE>
+__global__ __launch_bounds__(256) void recurrent_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                                        const float* __restrict__ v,
+                                                        const float* __restrict__ gate,
+                                                        const float* __restrict__ beta, float* __restrict__ state,
+                                                        float* __restrict__ out, float* __restrict__ snaps,
+                                                        int n_snap, int batch, int heads, int T)
+{
+    using G = RecGeom<NSLICE>;
+    const int tid = threadIdx.x;
+    const int slice = blockIdx.x % NSLICE;
+    const int bh = blockIdx.x / NSLICE;  // b * heads + h
+    const int b = bh / heads, h = bh % heads;
+    const int cg = tid % G::kColGroups;
+    const int rg = tid / G::kColGroups;
+    const int wave = tid / 64;
+    const int lane = tid % 64;
+    const int col = slice * G::kCols + 4 * cg;
+
+    __shared__ float s_k[kD], s_q[kD], s_a[kD];
+    __shared__ float s_red[G::kWaves][9][G::kColGroups];
+
+    float* const S_head = state + (size_t)bh * kD * kD;
+    float4 s[G::kRows];
+#pragma unroll
+    for (int m = 0; m < G::kRows; ++m) s[m] = ld4(S_head + (size_t)(rg + G::kRowGroups * m) * kD + col);
+
+    for (int t = 0; t < T; ++t) {
+        const size_t row = ((size_t)b * T + t) * heads + h;  // (b, t, h)
+        if (tid < kD) {
+            s_k[tid] = k[row * kD + tid];
+            s_q[tid] = q[row * kD + tid];
+            s_a[tid] = expf(gate[row * kD + tid]);
+        }
+        const float bt = beta[row];
+        const float4 vv = ld4(v + row * kD + col);
+        __syncthreads();
+
+        // decay in place, then partial read-outs with the key and the query
+        float red[9];
+#pragma unroll
+        for (int x = 0; x < 9; ++x) red[x] = 0.f;
+        float kr[G::kRows];
+#pragma unroll
+        for (int m = 0; m < G::kRows; ++m) {
+            const int i = rg + G::kRowGroups * m;
+            const float a = s_a[i], kk = s_k[i], qq = s_q[i];
+            kr[m] = kk;
+            s[m].x *= a;
+            s[m].y *= a;
+            s[m].z *= a;
+            s[m].w *= a;
+            red[0] = fmaf(kk, s[m].x, red[0]);
+            red[1] = fmaf(kk, s[m].y, red[1]);
+            red[2] = fmaf(kk, s[m].z, red[2]);
+            red[3] = fmaf(kk, s[m].w, red[3]);
+            red[4] = fmaf(qq, s[m].x, red[4]);
+            red[5] = fmaf(qq, s[m].y, red[5]);
+            red[6] = fmaf(qq, s[m].z, red[6]);
+            red[7] = fmaf(qq, s[m].w, red[7]);
+            red[8] = fmaf(qq, kk, red[8]);
+        }
+        // reduce over the row groups of this wave ...
+#pragma unroll
+        for (int off = G::kColGroups; off < 64; off <<= 1) {
+#pragma unroll
+            for (int x = 0; x < 9; ++x) red[x] += __shfl_xor(red[x], off);
+        }
+        // ... then over the waves, in wave order
+        if (lane < G::kColGroups) {
+#pragma unroll
+            for (int x = 0; x < 9; ++x) s_red[wave][x][lane] = red[x];
+        }
+        __syncthreads();
+        float tot[9];
+#pragma unroll
+        for (int x = 0; x < 9; ++x) {
+            float acc = s_red[0][x][cg];
+#pragma unroll
+            for (int w = 1; w < G::kWaves; ++w) acc += s_red[w][x][cg];
+            tot[x] = acc;
+        }
+        // delta = beta (v - S^T k);  out = S_dec^T q + (q.k) delta  (= S_new^T q)
+        float4 d, o;
+        d.x = bt * (vv.x - tot[0]);
+        d.y = bt * (vv.y - tot[1]);
+        d.z = bt * (vv.z - tot[2]);
+        d.w = bt * (vv.w - tot[3]);
+        o.x = fmaf(tot[8], d.x, tot[4]);
+        o.y = fmaf(tot[8], d.y, tot[5]);
+        o.z = fmaf(tot[8], d.z, tot[6]);
+        o.w = fmaf(tot[8], d.w, tot[7]);
+        if (rg == 0) st4(out + row * kD + col, o);
+#pragma unroll
+        for (int m = 0; m < G::kRows; ++m) {
+            s[m].x = fmaf(kr[m], d.x, s[m].x);
+            s[m].y = fmaf(kr[m], d.y, s[m].y);
+            s[m].z = fmaf(kr[m], d.z, s[m].z);
+            s[m].w = fmaf(kr[m], d.w, s[m].w);
+        }
+        if (t < n_snap) {
+            float* snap = snaps + ((size_t)t * batch * heads + bh) * kD * kD;
+#pragma unroll
+            for (int m = 0; m < G::kRows; ++m) st4(snap + (size_t)(rg + G::kRowGroups * m) * kD + col, s[m]);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < G::kRows; ++m) st4(S_head + (size_t)(rg + G::kRowGroups * m) * kD + col, s[m]);
+}
+
+int launch_recurrent(const float* q, const float* k, const float* v, const float* gate, const float* beta,
+                     float* state, float* out, float* snaps, int n_snap, int batch, int heads, int T,
+                     hipStream_t stream)
+{
+    const unsigned grid = (unsigned)batch * (unsigned)heads * kRecSlices;
+    hipLaunchKernelGGL(recurrent_kernel<kRecSlices>, dim3(grid), dim3(256), 0, stream, q, k, v, gate, beta, state,
+                       out, snaps, n_snap, batch, heads, T);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+long long recurrent_max_units() { return 0x7fffffffLL / kRecSlices; }
+
+}  // namespace kda

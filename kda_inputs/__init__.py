@@ -81,49 +81,43 @@ def _rng(seed: int, array_id: int, b: int, block: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, array_id, b, block])))
 
 
-def _draw_rows(seed: int, array_id: int, b: int, r0: int, r1: int, heads: int, per_row: int,
-               kind: str, gate_lo: float = 0.0) -> np.ndarray:
-    """Rows [r0, r1) of one array of one sequence, shape [r1-r0, heads*per_row], fp64."""
-    out = np.empty((r1 - r0, heads * per_row), dtype=np.float64)
-    blk0, blk1 = r0 // ROW_BLOCK, (r1 - 1) // ROW_BLOCK
-    for blk in range(blk0, blk1 + 1):
+def _block(seed: int, array_id: int, b: int, blk: int, n_prefix: int, width: int, kind: str) -> np.ndarray:
+    """The first n_prefix rows of row block ``blk`` of one array, shape [n_prefix, width], fp32."""
+    g = _rng(seed, array_id, b, blk)
+    if kind == "normal":
+        return g.standard_normal((n_prefix, width), dtype=np.float32)
+    return g.random((n_prefix, width), dtype=np.float32)
+
+
+def fill_rows(seed: int, b: int, r0: int, r1: int, heads: int, gate_lo: float, dst: dict) -> None:
+    """Write rows [r0, r1) of sequence b into dst["q"|"k"|"v"|"gate"] ([r1-r0, H, D] views)
+    and dst["beta"] ([r1-r0, H]), one row block at a time."""
+    width = heads * D
+    for blk in range(r0 // ROW_BLOCK, (r1 - 1) // ROW_BLOCK + 1):
         lo = max(r0, blk * ROW_BLOCK)
         hi = min(r1, (blk + 1) * ROW_BLOCK)
-        n_prefix = hi - blk * ROW_BLOCK          # draw the block's prefix, keep [lo, hi)
-        g = _rng(seed, array_id, b, blk)
-        if kind == "normal":
-            x = g.standard_normal((n_prefix, heads * per_row), dtype=np.float32).astype(np.float64)
-        elif kind == "uniform":
-            x = g.random((n_prefix, heads * per_row), dtype=np.float32).astype(np.float64)
-        else:
-            raise ValueError(kind)
-        out[lo - r0:hi - r0] = x[lo - blk * ROW_BLOCK:]
-    if kind == "uniform":
-        out = gate_lo * out          # [lo, 0]
-    return out
-
-
-def _l2_rows(x: np.ndarray, heads: int) -> np.ndarray:
-    y = x.reshape(x.shape[0], heads, D)
-    return (y / np.sqrt((y * y).sum(-1, keepdims=True) + L2_EPS)).reshape(x.shape)
+        n_prefix = hi - blk * ROW_BLOCK
+        cut = slice(lo - blk * ROW_BLOCK, n_prefix)
+        rows = slice(lo - r0, hi - r0)
+        n = hi - lo
+        for name, aid in (("q", ID_Q), ("k", ID_K)):
+            x = _block(seed, aid, b, blk, n_prefix, width, "normal")[cut].astype(np.float64).reshape(n, heads, D)
+            x /= np.sqrt((x * x).sum(-1, keepdims=True) + L2_EPS)
+            dst[name][rows] = x
+        dst["v"][rows] = _block(seed, ID_V, b, blk, n_prefix, width, "normal")[cut].reshape(n, heads, D)
+        u = _block(seed, ID_GATE, b, blk, n_prefix, width, "uniform")[cut].astype(np.float64)
+        dst["gate"][rows] = (gate_lo * u).reshape(n, heads, D)
+        z = _block(seed, ID_BETA, b, blk, n_prefix, heads, "normal")[cut].astype(np.float64)
+        dst["beta"][rows] = 1.0 / (1.0 + np.exp(-z))
 
 
 def sequence_rows(seed: int, b: int, r0: int, r1: int, heads: int, gate_lo: float) -> dict:
     """q, k, v, gate [rows, H, D] and beta [rows, H] (fp32) for rows [r0, r1) of sequence b."""
-    q = _l2_rows(_draw_rows(seed, ID_Q, b, r0, r1, heads, D, "normal"), heads)
-    k = _l2_rows(_draw_rows(seed, ID_K, b, r0, r1, heads, D, "normal"), heads)
-    v = _draw_rows(seed, ID_V, b, r0, r1, heads, D, "normal")
-    gate = _draw_rows(seed, ID_GATE, b, r0, r1, heads, D, "uniform", gate_lo)
-    z = _draw_rows(seed, ID_BETA, b, r0, r1, heads, 1, "normal")
-    beta = 1.0 / (1.0 + np.exp(-z))
     n = r1 - r0
-    return {
-        "q": q.astype(np.float32).reshape(n, heads, D),
-        "k": k.astype(np.float32).reshape(n, heads, D),
-        "v": v.astype(np.float32).reshape(n, heads, D),
-        "gate": gate.astype(np.float32).reshape(n, heads, D),
-        "beta": beta.astype(np.float32).reshape(n, heads),
-    }
+    out = {name: np.empty((n, heads, D), dtype=np.float32) for name in ("q", "k", "v", "gate")}
+    out["beta"] = np.empty((n, heads), dtype=np.float32)
+    fill_rows(seed, b, r0, r1, heads, gate_lo, out)
+    return out
 
 
 def initial_state(seed: int, b: int, heads: int, std: float) -> np.ndarray:
@@ -158,14 +152,12 @@ def make_batch(seed: int, batch: int, heads: int, rows: int, gate_lo: float, sta
 
     jobs = []
     for b in range(batch):
-        for s in range(0, rows, ROW_BLOCK * 4):
-            jobs.append((b, s, min(rows, s + ROW_BLOCK * 4)))
+        for s in range(0, rows, ROW_BLOCK):
+            jobs.append((b, s, min(rows, s + ROW_BLOCK)))
 
     def work(job):
         b, s, e = job
-        part = sequence_rows(seed, b, row0 + s, row0 + e, heads, gate_lo)
-        for name, val in part.items():
-            arrays[name][b, s:e] = val
+        fill_rows(seed, b, row0 + s, row0 + e, heads, gate_lo, {name: a[b, s:e] for name, a in arrays.items()})
 
     def work_state(b):
         state[b] = initial_state(seed, b, heads, state_std)

@@ -1,0 +1,119 @@
+"""CPU checks of the C ABI: the library loads, exports what include/kda.h declares,
+and refuses bad arguments on the host before touching any buffer or the GPU.
+None of these calls reaches a kernel launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import kda_gated_delta_core_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+# fake, never-dereferenced device addresses, far apart so no range overlaps
+P = [0x10000000000 * (i + 1) for i in range(10)]
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kda.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(kda.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+    assert not {e for e in exported if e.startswith("kda_")} - set(names)
+
+
+def test_status_strings(lib):
+    for code, tag in [(0, "KDA_OK"), (-1, "INVALID_ARG"), (-2, "UNSUPPORTED"), (-3, "WORKSPACE"), (-4, "HIP")]:
+        assert tag in kda.kda_status_string(code)
+    assert "unknown" in kda.kda_status_string(7)
+
+
+def test_workspace_bytes():
+    for B, H, T, C in [(1, 2, 64, 16), (1, 32, 8192, 64), (4, 32, 32768, 64), (3, 5, 100, 32), (2, 1, 1, 16)]:
+        n = -(-T // C)
+        rec = 4 * C * 128 + C * C + 128
+        assert kda.kda_chunk_prefill_workspace_bytes(B, H, T, C) == B * H * n * rec * 4
+    for bad in [(0, 1, 1, 16), (1, 0, 1, 16), (1, 1, 0, 16), (1, 1, 1, 8), (1, 1, 1, 128), (-1, 1, 1, 64)]:
+        assert kda.kda_chunk_prefill_workspace_bytes(*bad) == 0
+    assert kda.kda_chunk_prefill_workspace_bytes(1 << 20, 1 << 10, 1 << 20, 64) == 0  # overflow
+
+
+def _prefill(lib, ptrs=None, B=1, H=2, T=64, C=16, ws=None, ws_bytes=None):
+    p = list(ptrs or P[:7])
+    need = kda.kda_chunk_prefill_workspace_bytes(B, H, T, C)
+    return lib.kda_chunk_prefill(*p, B, H, T, C, P[7] if ws is None else ws,
+                                 need if ws_bytes is None else ws_bytes, None)
+
+
+def test_prefill_refusals(lib):
+    for i in range(7):
+        p = list(P[:7])
+        p[i] = None
+        assert _prefill(lib, ptrs=p) == kda.KDA_ERR_INVALID_ARG
+    assert _prefill(lib, B=0) == kda.KDA_ERR_INVALID_ARG
+    assert _prefill(lib, H=0) == kda.KDA_ERR_INVALID_ARG
+    assert _prefill(lib, T=0) == kda.KDA_ERR_INVALID_ARG
+    assert _prefill(lib, T=-5) == kda.KDA_ERR_INVALID_ARG
+    for C in (0, 8, 48, 128):
+        assert lib.kda_chunk_prefill(*P[:7], 1, 2, 64, C, P[7], 1 << 30, None) == kda.KDA_ERR_UNSUPPORTED
+    assert _prefill(lib, ws_bytes=1000) == kda.KDA_ERR_WORKSPACE
+    assert lib.kda_chunk_prefill(*P[:7], 1, 2, 64, 16, None, 1 << 30, None) == kda.KDA_ERR_WORKSPACE
+    # out overlapping q, state overlapping out, workspace overlapping state
+    p = list(P[:7])
+    p[6] = P[0] + 64
+    assert _prefill(lib, ptrs=p) == kda.KDA_ERR_INVALID_ARG
+    p = list(P[:7])
+    p[5] = P[6] + 4
+    assert _prefill(lib, ptrs=p) == kda.KDA_ERR_INVALID_ARG
+    assert _prefill(lib, ws=P[5] + 128) == kda.KDA_ERR_INVALID_ARG
+    # size overflow
+    assert lib.kda_chunk_prefill(*P[:7], 1 << 20, 1 << 10, 1 << 20, 64, P[7], 1 << 62, None) == \
+        kda.KDA_ERR_INVALID_ARG
+
+
+def test_recurrent_refusals(lib):
+    for i in range(7):
+        p = list(P[:7])
+        p[i] = None
+        assert lib.kda_recurrent_step(*p, 4, 2, None) == kda.KDA_ERR_INVALID_ARG
+        assert lib.kda_recurrent_k(*p, None, 0, 4, 2, 3, None) == kda.KDA_ERR_INVALID_ARG
+    assert lib.kda_recurrent_step(*P[:7], 0, 2, None) == kda.KDA_ERR_INVALID_ARG
+    assert lib.kda_recurrent_step(*P[:7], 2, 0, None) == kda.KDA_ERR_INVALID_ARG
+    assert lib.kda_recurrent_k(*P[:7], None, 0, 4, 2, 0, None) == kda.KDA_ERR_INVALID_ARG   # k == 0
+    assert lib.kda_recurrent_k(*P[:7], P[8], 4, 4, 2, 3, None) == kda.KDA_ERR_INVALID_ARG  # n_snap > T
+    assert lib.kda_recurrent_k(*P[:7], P[8], -1, 4, 2, 3, None) == kda.KDA_ERR_INVALID_ARG
+    assert lib.kda_recurrent_k(*P[:7], None, 2, 4, 2, 3, None) == kda.KDA_ERR_INVALID_ARG  # snapshots NULL
+    # snapshots overlapping the state
+    assert lib.kda_recurrent_k(*P[:7], P[5] + 256, 2, 4, 2, 3, None) == kda.KDA_ERR_INVALID_ARG
+    # state overlapping an input
+    p = list(P[:7])
+    p[5] = P[2] + 16
+    assert lib.kda_recurrent_step(*p, 4, 2, None) == kda.KDA_ERR_INVALID_ARG
+    assert lib.kda_recurrent_k(*P[:7], None, 0, 1 << 20, 1 << 12, 1 << 20, None) == kda.KDA_ERR_INVALID_ARG
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 2, 128)
+    b = torch.zeros(1, 1, 2)
+    s = torch.zeros(1, 2, 128, 128)
+    with pytest.raises(ValueError):
+        kda.kda_recurrent_step(x, x, x, x, b, s, out=torch.zeros_like(x), stream=0)

@@ -1,0 +1,110 @@
+"""GPU parity of the recurrent (decode) forms against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import kda_inputs as ki
+import oracle
+from kda_testlib import SENTINEL, announce, assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_step(kda, x, B, H):
+    import torch
+    st = dev(x["state"])
+    out = torch.full((B, 1, H, 128), SENTINEL, device="cuda")
+    kda.kda_recurrent_step(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["gate"]), dev(x["beta"]), st, out=out)
+    torch.cuda.synchronize()
+    return host(out), host(st)
+
+
+@pytest.mark.parametrize("B,H", [(1, 1), (3, 5), (64, 32)])
+def test_decode_step_matches_oracle(device, B, H):
+    import kda_gated_delta_core_amd as kda
+    w = ki.WORKLOADS["decode_b64_h32"]
+    announce(f"kda_recurrent_step seed={w.seed} B={B} H={H}")
+    x = ki.make_batch(w.seed, B, H, 1, w.gate_lo, w.state_std)
+    out, st = _run_step(kda, x, B, H)
+    o_ref, s_ref, _, _ = oracle.serial(x["q"], x["k"], x["v"], x["gate"], x["beta"], x["state"])
+    assert_close("out", out, o_ref)
+    assert_close("state", st, s_ref)
+
+
+def test_decode_step_extreme_gates(device):
+    """Very negative and zero gates, beta at 0 and 1: the decode form has no range limit."""
+    import kda_gated_delta_core_amd as kda
+    B, H = 2, 4
+    announce("kda_recurrent_step extreme gates")
+    x = ki.make_batch(7, B, H, 1, -5.0, 0.02)
+    x["gate"][0] = -60.0
+    x["gate"][1, :, :2] = 0.0
+    x["beta"][1, :, 0] = 0.0
+    x["beta"][1, :, 1] = 1.0
+    out, st = _run_step(kda, x, B, H)
+    o_ref, s_ref, _, _ = oracle.serial(x["q"], x["k"], x["v"], x["gate"], x["beta"], x["state"])
+    assert_close("out", out, o_ref)
+    assert_close("state", st, s_ref)
+
+
+def _decode_k(kda, x, B, H, T, n_snap, n_slots=None):
+    import torch
+    st = dev(x["state"])
+    out = torch.full((B, T, H, 128), SENTINEL, device="cuda")
+    n_slots = n_snap if n_slots is None else n_slots
+    snaps = torch.full((max(n_slots, 1), B, H, 128, 128), SENTINEL, device="cuda")
+    kda.kda_recurrent_k(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["gate"]), dev(x["beta"]), st, out=out,
+                        snapshots=snaps if n_snap else None, n_snapshots=n_snap)
+    torch.cuda.synchronize()
+    return out, st, snaps
+
+
+@pytest.mark.parametrize("B,H,T,n_snap", [(2, 3, 4, 4), (1, 2, 7, 3), (5, 1, 1, 1), (3, 2, 9, 0)])
+def test_decode_k_matches_oracle(device, B, H, T, n_snap):
+    import kda_gated_delta_core_amd as kda
+    w = ki.WORKLOADS["decode_k4_b128_h32"]
+    announce(f"kda_recurrent_k seed={w.seed} B={B} H={H} T={T} n_snap={n_snap}")
+    x = ki.make_batch(w.seed, B, H, T, w.gate_lo, w.state_std)
+    out, st, snaps = _decode_k(kda, x, B, H, T, n_snap, n_slots=n_snap + 1)
+    o_ref, s_ref, sn_ref, _ = oracle.serial(x["q"], x["k"], x["v"], x["gate"], x["beta"], x["state"],
+                                            n_snap=n_snap)
+    assert_close("out", host(out), o_ref)
+    assert_close("state", host(st), s_ref)
+    sn = host(snaps)
+    for t in range(n_snap):
+        assert_close(f"snapshot[{t}]", sn[t], sn_ref[t])
+    # the slot after the last snapshot is never written
+    assert np.all(sn[n_snap] == SENTINEL)
+
+
+def test_decode_k_full_size_bitwise_and_sampled_parity(device):
+    """decode_k at B=128, H=32, k=4 with 4 snapshots: bit-identical to 4 serial steps,
+    and equal to the oracle on sampled sequences."""
+    import torch
+    import kda_gated_delta_core_amd as kda
+    w = ki.WORKLOADS["decode_k4_b128_h32"]
+    B, H, T = w.batch, w.heads, w.T
+    announce(f"kda_recurrent_k full size seed={w.seed} B={B} H={H} T={T}")
+    x = ki.workload_inputs(w)
+    out, st, snaps = _decode_k(kda, x, B, H, T, w.n_snap)
+    # the same rows through T single steps
+    st2 = dev(x["state"])
+    outs = []
+    for t in range(T):
+        sl = lambda a: dev(a[:, t:t + 1])
+        o = torch.empty((B, 1, H, 128), device="cuda")
+        kda.kda_recurrent_step(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["gate"]), sl(x["beta"]), st2, out=o)
+        torch.cuda.synchronize()
+        assert torch.equal(st2, snaps[t]), f"snapshot {t} differs from step {t}"
+        outs.append(o)
+    assert torch.equal(torch.cat(outs, 1), out)
+    assert torch.equal(st2, st)
+    # oracle on a sample of sequences
+    sel = [0, 37, 127]
+    sub = {n: np.ascontiguousarray(a[sel]) for n, a in x.items()}
+    o_ref, s_ref, sn_ref, _ = oracle.serial(sub["q"], sub["k"], sub["v"], sub["gate"], sub["beta"], sub["state"],
+                                            n_snap=w.n_snap)
+    assert_close("out", host(out)[sel], o_ref)
+    assert_close("state", host(st)[sel], s_ref)
+    sn = host(snaps)
+    for t in range(w.n_snap):
+        assert_close(f"snapshot[{t}]", sn[t][sel], sn_ref[t])

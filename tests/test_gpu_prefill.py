@@ -1,0 +1,165 @@
+"""GPU parity of the chunked prefill against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import kda_inputs as ki
+import oracle
+from kda_testlib import SENTINEL, announce, assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _prefill(kda, x, T, C, state=None, rows=None):
+    """Run kda_chunk_prefill on host arrays x (rows >= T_pad ignored); returns (out, state, ws) tensors."""
+    import torch
+    B, _, H, _ = x["q"].shape
+    t_pad = -(-T // C) * C
+    v = lambda a: dev(a[:, :t_pad])
+    st = dev(x["state"]) if state is None else state
+    out = torch.full((B, t_pad, H, 128), SENTINEL, device="cuda")
+    ws = torch.empty(kda.kda_chunk_prefill_workspace_bytes(B, H, T, C), dtype=torch.uint8, device="cuda")
+    kda.kda_chunk_prefill(v(x["q"]), v(x["k"]), v(x["v"]), v(x["gate"]), v(x["beta"]), st, T, C, out=out,
+                          workspace=ws)
+    torch.cuda.synchronize()
+    return out, st, ws
+
+
+def _check_against_oracle(x, T, out, st, tag=""):
+    o_ref, s_ref, _, _ = oracle.serial(x["q"], x["k"], x["v"], x["gate"], x["beta"], x["state"], T=T)
+    o = host(out)
+    assert_close(f"{tag}core", o[:, :T], o_ref)
+    assert_close(f"{tag}state", host(st), s_ref)
+    assert np.all(o[:, T:] == SENTINEL), "rows >= T of out were written"
+
+
+def test_prefill_small_workload(device):
+    import kda_gated_delta_core_amd as kda
+    w = ki.WORKLOADS["prefill_h2_t64_c16"]
+    announce(f"kda_chunk_prefill {w.name} seed={w.seed}")
+    x = ki.workload_inputs(w)
+    out, st, _ = _prefill(kda, x, w.T, w.chunk)
+    _check_against_oracle(x, w.T, out, st)
+
+
+@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("T", [1, 17, 64, 100, 130])
+def test_prefill_ragged(device, T, C):
+    import kda_gated_delta_core_amd as kda
+    announce(f"kda_chunk_prefill ragged B=2 H=3 T={T} C={C}")
+    t_pad = -(-T // C) * C
+    x = ki.make_batch(2000 + T, 2, 3, T, -5.0, 0.02, alloc_rows=t_pad, pad_value=1e4)
+    out, st, _ = _prefill(kda, x, T, C)
+    _check_against_oracle(x, T, out, st)
+
+
+def test_prefill_pad_values_are_ignored_bitwise(device):
+    """positions >= T are ignored in-kernel whatever fills them (layer page, prefill_with_pad_fill)."""
+    import torch
+    import kda_gated_delta_core_amd as kda
+    T, C = 100, 64
+    announce(f"kda_chunk_prefill pad invariance T={T} C={C}")
+    base = ki.make_batch(3001, 2, 3, T, -5.0, 0.02, alloc_rows=128, pad_value=0.0)
+    results = []
+    for pad in (0.0, 1e4, np.inf, -np.inf, np.nan):
+        x = {n: a.copy() for n, a in base.items()}
+        for n in ("q", "k", "v", "gate", "beta"):
+            x[n][:, T:] = pad
+        out, st, _ = _prefill(kda, x, T, C)
+        results.append((out, st))
+    for out, st in results[1:]:
+        assert torch.equal(out, results[0][0])
+        assert torch.equal(st, results[0][1])
+    _check_against_oracle(base, T, *results[0])
+
+
+def test_prefill_workspace_stages(device):
+    """The chunk record the prepare kernel writes, stage by stage against the oracle's
+    intermediates (workspace page: the oracle compares stage by stage)."""
+    import kda_gated_delta_core_amd as kda
+    T, C, H = 150, 64, 2
+    announce(f"kda_chunk_prefill stages T={T} C={C}")
+    x = ki.make_batch(4001, 1, H, T, -5.0, 0.02, alloc_rows=192, pad_value=np.nan)
+    _, _, ws = _prefill(kda, x, T, C)
+    rec_f = 4 * C * 128 + C * C + 128
+    ws = host(ws).view(np.float32).reshape(H, -1, rec_f)
+    for h, c in [(0, 0), (1, 1), (1, 2)]:
+        n = min(C, T - c * C)
+        stg = oracle.chunk_stages(x["q"], x["k"], x["v"], x["gate"], x["beta"], np.zeros((128, 128)), 0, h,
+                                  c * C, n)
+        rec = ws[h, c]
+        W, U, Qh = rec[:C * 128].reshape(C, 128), rec[C * 128:2 * C * 128].reshape(C, 128), \
+            rec[2 * C * 128:3 * C * 128].reshape(C, 128)
+        KtT = rec[3 * C * 128:4 * C * 128].reshape(128, C)
+        M = rec[4 * C * 128:4 * C * 128 + C * C].reshape(C, C)
+        gam = rec[4 * C * 128 + C * C:]
+        G = stg["G"]
+        q = x["q"][0, c * C:c * C + n, h].astype(np.float64)
+        k = x["k"][0, c * C:c * C + n, h].astype(np.float64)
+        tag = f"h{h}c{c} "
+        assert_close(tag + "W", W[:n], stg["W"])
+        assert_close(tag + "U", U[:n], stg["U"])
+        assert_close(tag + "M", M[:n, :n], stg["M"])
+        assert_close(tag + "Qhat", Qh[:n], np.exp(G) * q)
+        assert_close(tag + "Ktil^T", KtT[:, :n], (np.exp(G[-1] - G) * k).T)
+        assert_close(tag + "gamma", gam, np.exp(G[-1]))
+        for name, a in (("W", W[n:]), ("U", U[n:]), ("Qhat", Qh[n:]), ("Kt", KtT[:, n:]), ("M", M[n:]),
+                        ("M", M[:, n:])):
+            assert np.all(a == 0), f"{tag}{name} pad rows not zero"
+
+
+def test_prefill_then_decode_equals_serial(device):
+    import torch
+    import kda_gated_delta_core_amd as kda
+    T, n_dec, C, B, H = 200, 5, 64, 2, 3
+    announce(f"kda_chunk_prefill T={T} then {n_dec} x kda_recurrent_step")
+    x = ki.make_batch(5001, B, H, T + n_dec, -5.0, 0.02)
+    pre = {n: np.ascontiguousarray(a[:, :T]) if n != "state" else a for n, a in x.items()}
+    t_pad = -(-T // C) * C
+    pre = {n: (np.concatenate([a, np.full((B, t_pad - T) + a.shape[2:], np.nan, np.float32)], 1)
+               if n != "state" else a) for n, a in pre.items()}
+    out, st, _ = _prefill(kda, pre, T, C)
+    outs = [host(out)[:, :T]]
+    for t in range(T, T + n_dec):
+        sl = lambda a: dev(a[:, t:t + 1])
+        o = torch.empty((B, 1, H, 128), device="cuda")
+        kda.kda_recurrent_step(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["gate"]), sl(x["beta"]), st, out=o)
+        outs.append(host(o))
+    torch.cuda.synchronize()
+    o_ref, s_ref, _, _ = oracle.serial(x["q"], x["k"], x["v"], x["gate"], x["beta"], x["state"])
+    assert_close("core", np.concatenate(outs, 1), o_ref)
+    assert_close("state", host(st), s_ref)
+
+
+def test_prefill_split_across_calls(device):
+    import kda_gated_delta_core_amd as kda
+    T1, T2, B, H = 96, 70, 1, 4
+    announce(f"kda_chunk_prefill split {T1}+{T2}")
+    x = ki.make_batch(6001, B, H, T1 + T2, -5.0, 0.02)
+    a = {n: (np.ascontiguousarray(v[:, :T1]) if n != "state" else v) for n, v in x.items()}
+    b2 = {n: (np.ascontiguousarray(v[:, T1:]) if n != "state" else v) for n, v in x.items()}
+    b2 = {n: (np.concatenate([v, np.zeros((B, 96 - T2) + v.shape[2:], np.float32)], 1) if n != "state" else v)
+          for n, v in b2.items()}
+    out1, st, _ = _prefill(kda, a, T1, 32)
+    out2, st, _ = _prefill(kda, b2, T2, 32, state=st)
+    o_ref, s_ref, _, _ = oracle.serial(x["q"], x["k"], x["v"], x["gate"], x["beta"], x["state"])
+    assert_close("core", np.concatenate([host(out1)[:, :T1], host(out2)[:, :T2]], 1), o_ref)
+    assert_close("state", host(st), s_ref)
+
+
+def test_prefill_h32_t8192_full_size(device):
+    """T=8192, H=32, C=64, pads (one extra chunk too) filled with 1e4; oracle on sampled heads."""
+    import kda_gated_delta_core_amd as kda
+    w = ki.WORKLOADS["prefill_h32_t8192_c64"]
+    announce(f"kda_chunk_prefill {w.name} seed={w.seed} (generating inputs)")
+    x = ki.workload_inputs(w)
+    announce("running GPU prefill")
+    out, st, _ = _prefill(kda, x, w.T, w.chunk)
+    o = host(out)
+    assert np.all(o[:, w.T:] == SENTINEL)
+    for h in (0, 13, 31):
+        announce(f"oracle head {h}")
+        sub = {n: np.ascontiguousarray(a[:, :w.T, h:h + 1]) if n != "state" else np.ascontiguousarray(a[:, h:h + 1])
+               for n, a in x.items()}
+        o_ref, s_ref, _, _ = oracle.serial(sub["q"], sub["k"], sub["v"], sub["gate"], sub["beta"], sub["state"])
+        assert_close(f"h{h} core", o[:, :w.T, h:h + 1], o_ref)
+        assert_close(f"h{h} state", host(st)[:, h:h + 1], s_ref)
