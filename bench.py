@@ -1,0 +1,331 @@
+#!/usr/bin/env python3
+"""Throughput of the KDA gated delta-rule core on one MI355X.
+
+Headline (the ``value`` of the JSON line): single-token decode of 64
+sequences x 32 heads, FP32 128x128 key-major state per head updated in place
+(kda_recurrent_step), in tokens/s.  One step = one call over the whole batch.
+The same run also times the other workloads of the core and reports each
+under ``workloads``: the T=8192 chunked prefill, the k=4 decode_k with
+snapshots, the 4 x 32768 long-context prefill followed by 16 decode steps,
+and the small T=64 prefill.
+
+Inputs are seeded synthetic tensors (kda_inputs) resident in HBM before the
+timed region.  Decode states are rotated over buffers totalling >= 1 GiB so
+the 256 MB Infinity Cache cannot hold them: every step reads and writes HBM.
+
+``roofline`` describes the dominant kernel of the headline (the recurrent
+kernel): algorithmic bytes per launch / average launch duration from HIP
+events around each launch on the launch stream, against 8 TB/s.
+``cpu_baseline`` times the fp64 oracle on the host cores (rank 0, N=1).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA core tokens/s + achieved HBM GB/s (decode) / MFMA % (prefill), 1 MI355X"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense FP32 matrix, vendor figure
+D = 128
+STATE_BYTES = D * D * 4
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- algorithmic work
+def decode_bytes(B: int, H: int, T: int = 1, n_snap: int = 0) -> int:
+    """State read + write (+ snapshot writes) + q, k, v, gate reads + out write + beta reads."""
+    per_head = 2 * STATE_BYTES + n_snap * STATE_BYTES + T * (4 * D * 4 + D * 4 + 4)
+    return B * H * per_head
+
+
+def prefill_flops(B: int, H: int, T: int, C: int) -> float:
+    """Per token-head: 6 d^2 (W S, Qhat S, Ktil^T Delta) + 5 C d (lower-triangular A, M, W, U,
+    M Delta) + C^2 / 3 (triangular inverse)."""
+    return float(B) * H * T * (6 * D * D + 5 * C * D + C * C / 3.0)
+
+
+def prefill_bytes(B: int, H: int, T: int) -> int:
+    return B * H * (2 * STATE_BYTES + T * (4 * D * 4 + D * 4 + 4))
+
+
+# ---------------------------------------------------------------- timing
+class Timer:
+    """K launches, each bracketed by HIP events on the launch stream, plus wall clock
+    between device synchronisations."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, steps: int, warmup: int):
+        torch = self.torch
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ev[i][0].record()
+            fn(warmup + i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        launches = [a.elapsed_time(b) * 1e-3 for a, b in ev]
+        launches.sort()
+        return {
+            "wall_s": wall,
+            "s_per_step": wall / steps,
+            "launch_avg_s": sum(launches) / len(launches),
+            "launch_median_s": launches[len(launches) // 2],
+            "launch_min_s": launches[0],
+        }
+
+
+# ---------------------------------------------------------------- workloads
+def bench_decode(torch, kda, ki, steps, warmup, timer):
+    w = ki.WORKLOADS["decode_b64_h32"]
+    B, H = w.batch, w.heads
+    x = ki.workload_inputs(w)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    q, k, v, g, b = (dev(x[n]) for n in ("q", "k", "v", "gate", "beta"))
+    n_buf = max(2, -(-(1 << 30) // (B * H * STATE_BYTES)))  # >= 1 GiB of states
+    states = [dev(x["state"]) for _ in range(n_buf)]
+    out = torch.empty((B, 1, H, D), device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        kda.kda_recurrent_step(q, k, v, g, b, states[i % n_buf], out=out, stream=stream)
+
+    r = timer.run(step, steps, warmup)
+    nbytes = decode_bytes(B, H)
+    return w, r, nbytes, n_buf
+
+
+def bench_decode_k(torch, kda, ki, steps, warmup, timer):
+    w = ki.WORKLOADS["decode_k4_b128_h32"]
+    B, H, T = w.batch, w.heads, w.T
+    x = ki.workload_inputs(w)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    q, k, v, g, b = (dev(x[n]) for n in ("q", "k", "v", "gate", "beta"))
+    n_buf = max(2, -(-(1 << 30) // (B * H * STATE_BYTES)))
+    states = [dev(x["state"]) for _ in range(n_buf)]
+    snaps = torch.empty((w.n_snap, B, H, D, D), device="cuda")
+    out = torch.empty((B, T, H, D), device="cuda")
+
+    def step(i):
+        kda.kda_recurrent_k(q, k, v, g, b, states[i % n_buf], out=out, snapshots=snaps, n_snapshots=w.n_snap)
+
+    r = timer.run(step, steps, warmup)
+    return w, r, decode_bytes(B, H, T, w.n_snap)
+
+
+def bench_prefill(torch, kda, ki, name, steps, warmup, timer):
+    w = ki.WORKLOADS[name]
+    B, H, T, C = w.batch, w.heads, w.T, w.chunk
+    t_pad = -(-T // C) * C
+    dev = lambda a: torch.from_numpy(a).cuda()
+    tens = {}
+    # generate one sequence at a time and move it to the GPU (bounded host memory)
+    for n in ("q", "k", "v", "gate"):
+        tens[n] = torch.empty((B, t_pad, H, D), device="cuda")
+    tens["beta"] = torch.empty((B, t_pad, H), device="cuda")
+    state0 = torch.empty((B, H, D, D), device="cuda")
+    for s in range(B):
+        part = _sequence(ki, w, s, T, t_pad)
+        for n in tens:
+            tens[n][s].copy_(dev(part[n][0]))
+        state0[s].copy_(dev(part["state"][0]))
+    state = state0.clone()
+    out = torch.empty((B, t_pad, H, D), device="cuda")
+    ws = torch.empty(kda.kda_chunk_prefill_workspace_bytes(B, H, T, C), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        kda.kda_chunk_prefill(tens["q"], tens["k"], tens["v"], tens["gate"], tens["beta"], state, T, C, out=out,
+                              workspace=ws)
+
+    r = timer.run(step, steps, warmup)
+    extra = {}
+    if w.tail_steps:
+        # decode steps continuing from the prefill's final state (rows T.. of the same streams)
+        state.copy_(state0)
+        step(0)
+        tail = _tail_inputs(ki, w, torch)
+        o = torch.empty((B, 1, H, D), device="cuda")
+
+        def dstep(i):
+            j = i % w.tail_steps
+            kda.kda_recurrent_step(*(tail[n][j] for n in ("q", "k", "v", "gate", "beta")), state, out=o)
+
+        rt = timer.run(dstep, w.tail_steps, 0)
+        extra = {"tail_steps": w.tail_steps, "tail_us_per_step": rt["s_per_step"] * 1e6,
+                 "tail_kernel_us": rt["launch_avg_s"] * 1e6, "tail_tokens_per_s": B / rt["s_per_step"]}
+    return w, r, extra
+
+
+def _sequence(ki, w, s, T, t_pad):
+    import numpy as np
+    arrays = {n: np.full((1, t_pad, w.heads, D), 0.0 if w.pad_value is None else w.pad_value, np.float32)
+              for n in ("q", "k", "v", "gate")}
+    arrays["beta"] = np.full((1, t_pad, w.heads), 0.0 if w.pad_value is None else w.pad_value, np.float32)
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = [(r, min(T, r + ki.ROW_BLOCK)) for r in range(0, T, ki.ROW_BLOCK)]
+    with ThreadPoolExecutor(ki.default_threads()) as ex:
+        list(ex.map(lambda j: ki.fill_rows(w.seed, s, j[0], j[1], w.heads, w.gate_lo,
+                                           {n: a[0, j[0]:j[1]] for n, a in arrays.items()}), jobs))
+    arrays["state"] = ki.initial_state(w.seed, s, w.heads, w.state_std)[None]
+    return arrays
+
+
+def _tail_inputs(ki, w, torch):
+    import numpy as np
+    rows = [ki.sequence_rows(w.seed, s, w.T, w.T + w.tail_steps, w.heads, w.gate_lo) for s in range(w.batch)]
+    tail = {}
+    for n in ("q", "k", "v", "gate", "beta"):
+        a = np.stack([r[n] for r in rows])            # [B, steps, H, (D)]
+        tail[n] = [torch.from_numpy(np.ascontiguousarray(a[:, j:j + 1])).cuda() for j in range(w.tail_steps)]
+    return tail
+
+
+# ---------------------------------------------------------------- cpu baseline
+def cpu_baseline(ki, budget_s: float = 12.0):
+    """The fp64 oracle (as it stands) on the headline workload: repeated full decode steps of
+    all 64 x 32 heads until about budget_s of CPU time has passed."""
+    import oracle
+    w = ki.WORKLOADS["decode_b64_h32"]
+    x = ki.workload_inputs(w)
+    state = x["state"].astype("float64")
+    reps, t0 = 0, time.perf_counter()
+    threads = 1
+    while True:
+        _, state, _, threads = oracle.serial(x["q"], x["k"], x["v"], x["gate"], x["beta"], state)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 100000:
+            break
+    return {"value": w.batch * reps / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full decode steps (B=64, H=32, one token each) of the fp64 oracle, "
+                      f"{el:.1f} s wall on {threads} threads, os.cpu_count()={os.cpu_count()}"}
+
+
+# ---------------------------------------------------------------- traffic from committed counters
+def committed_traffic(kernel_src: str, profile: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    sha = hashlib.sha256(open(os.path.join(ROOT, kernel_src), "rb").read()).hexdigest()[:16]
+    if fields.get("kernel_source_sha256_16") != sha:
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only", default="", help="comma list of workloads to time (default: all)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-probe", action="store_true", help="time one plain 1 GiB device copy and exit")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the core needs no collective and "
+                                   "--gpus above 1 is not supported", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import kda_gated_delta_core_amd as kda
+    import kda_inputs as ki
+
+    kda.load_library()
+    timer = Timer(torch)
+    if args.copy_probe:
+        n = 1 << 28  # 1 GiB of fp32
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        r = timer.run(lambda i: dst.copy_(src), 20, 3)
+        log(f"copy probe: 1 GiB read + 1 GiB write, {2 * n * 4 / r['launch_avg_s'] / 1e9:.1f} GB/s")
+        return
+
+    only = set(filter(None, args.only.split(",")))
+    want = lambda n: not only or n in only
+    workloads = {}
+
+    headline = None
+    if want("decode_b64_h32"):
+        log("decode_b64_h32")
+        w, r, nbytes, n_buf = bench_decode(torch, kda, ki, args.steps, args.warmup, timer)
+        gbs = nbytes / r["launch_avg_s"] / 1e9
+        headline = (w, r, nbytes, n_buf, gbs)
+        workloads[w.name] = {"tokens_per_s": w.batch / r["s_per_step"], "us_per_step": r["s_per_step"] * 1e6,
+                             "kernel_us": r["launch_avg_s"] * 1e6, "GB_per_s": gbs,
+                             "hbm_frac": gbs / HBM_PEAK_GBS, "state_buffers_rotated": n_buf}
+    if want("decode_k4_b128_h32"):
+        log("decode_k4_b128_h32")
+        w, r, nbytes = bench_decode_k(torch, kda, ki, max(10, args.steps // 2), args.warmup, timer)
+        gbs = nbytes / r["launch_avg_s"] / 1e9
+        workloads[w.name] = {"tokens_per_s": w.batch * w.T / r["s_per_step"], "us_per_call": r["s_per_step"] * 1e6,
+                             "kernel_us": r["launch_avg_s"] * 1e6, "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+    for name, steps in (("prefill_h32_t8192_c64", 20), ("prefill_b4_h32_t32768_c64", 4),
+                        ("prefill_h2_t64_c16", 50)):
+        if not want(name):
+            continue
+        log(name)
+        w, r, extra = bench_prefill(torch, kda, ki, name, steps, 2, timer)
+        fl = prefill_flops(w.batch, w.heads, w.T, w.chunk)
+        tf = fl / r["launch_avg_s"] / 1e12
+        res = {"tokens_per_s": w.batch * w.T / r["s_per_step"], "ms_per_call": r["s_per_step"] * 1e3,
+               "call_ms": r["launch_avg_s"] * 1e3, "algorithmic_TFLOP_per_s": tf,
+               "mfma_frac": tf / MFMA_F32_PEAK_TFLOPS,
+               "GB_per_s": prefill_bytes(w.batch, w.heads, w.T) / r["launch_avg_s"] / 1e9}
+        res.update(extra)
+        workloads[name] = res
+    for name, res in workloads.items():
+        log(f"{name}: " + ", ".join(f"{k}={v:.4g}" if isinstance(v, float) else f"{k}={v}"
+                                    for k, v in res.items()))
+
+    line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic"}
+    if headline is not None:
+        w, r, nbytes, n_buf, gbs = headline
+        traffic = committed_traffic("kda_gated_delta_core_amd/csrc/kda_recurrent.hip",
+                                    "recurrent_decode_b64_h32_counters.txt")
+        line.update({
+            "value": w.batch / r["s_per_step"], "unit": "tokens/s", "ms_per_step": r["s_per_step"] * 1e3,
+            "config": {"workload": w.name, "op": "kda_recurrent_step", "batch": w.batch, "heads": w.heads,
+                       "head_dim": D, "tokens_per_step": w.batch, "state_dtype": "f32",
+                       "state_buffers_rotated": n_buf},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
+                         "kernel": "recurrent_kernel", "algorithmic_bytes_per_launch": nbytes,
+                         "kernel_avg_us": r["launch_avg_s"] * 1e6},
+        })
+    line["workloads"] = workloads
+    if not args.no_cpu and headline is not None:
+        log("cpu baseline (fp64 oracle)")
+        line["cpu_baseline"] = cpu_baseline(ki)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -101,7 +101,13 @@ def test_prefill_workspace_stages(device):
         assert_close(tag + "M", M[:n, :n], stg["M"])
         assert_close(tag + "Qhat", Qh[:n], np.exp(G) * q)
         assert_close(tag + "Ktil^T", KtT[:, :n], (np.exp(G[-1] - G) * k).T)
-        assert_close(tag + "gamma", gam, np.exp(G[-1]))
+        # gamma = e^{G_last} is far below the fp32 range for most channels at these gates:
+        # compare where the reference is representable, require exact zeros elsewhere
+        g_ref = np.exp(G[-1])
+        big = g_ref > 1e-30
+        assert np.all(np.abs(gam[~big]) < 1e-30)
+        if big.any():
+            assert_close(tag + "gamma", gam[big], g_ref[big])
         for name, a in (("W", W[n:]), ("U", U[n:]), ("Qhat", Qh[n:]), ("Kt", KtT[:, n:]), ("M", M[n:]),
                         ("M", M[:, n:])):
             assert np.all(a == 0), f"{tag}{name} pad rows not zero"
