@@ -61,21 +61,27 @@ __device__ __forceinline__ float comp(const float4& v, int e)
     return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
 }
 
+constexpr int kPrepThreads = 512;  // 8 waves: one per 16-column block in the W/U stage
+
 template <int C>
-__global__ __launch_bounds__(256) void chunk_prepare_kernel(const float* __restrict__ q, const float* __restrict__ k,
-                                                            const float* __restrict__ v,
-                                                            const float* __restrict__ gate,
-                                                            const float* __restrict__ beta, float* __restrict__ ws,
-                                                            int heads, int T, int t_pad, int nchunks)
+__global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ gate, const float* __restrict__ beta, float* __restrict__ ws, int heads, int T,
+    int t_pad, int nchunks)
 {
     using G = ChunkGeom<C>;
     constexpr int NT = G::kTiles, LD = G::kLd, LDC = G::kLdc;
+    constexpr int NW = kPrepThreads / 64;
+    constexpr int NV4 = C * 32 / kPrepThreads;  // float4 per thread per [C][128] input
+    static_assert(NV4 >= 1 && NW == 8, "geometry");
     __shared__ float sK[C * LD];
-    __shared__ float sQ[C * LD];    // q; later beta e^G k
-    __shared__ float sL[C * LD];    // block-local log2 cumulative decay; later beta v
-    __shared__ float sA[C * LDC];   // beta-scaled strictly lower A
-    __shared__ float sT[C * LDC];   // (I + A)^-1
-    __shared__ float sBlk[NT * kD]; // log2 decay of each whole 16-row block
+    __shared__ float sQ[C * LD];
+    __shared__ float sL[C * LD];     // block-local cumulative log2 decay
+    __shared__ float sA[C * LDC];    // beta-scaled strictly lower A
+    __shared__ float sT[C * LDC];    // (I + A)^-1
+    __shared__ float sBlk[NT * kD];  // log2 decay of each whole 16-row block
+    __shared__ float sPre[NT * kD];  // sum of the block totals before block R
+    __shared__ float sSuf[NT * kD];  // sum of the block totals after block R
     __shared__ float sBeta[C];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -86,54 +92,80 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(const float* __restr
     const int t0 = c * C;
     float* const rec = ws + (size_t)blockIdx.x * G::kRecord;
     const size_t row0 = ((size_t)b * t_pad + t0) * heads + h;  // (b, t0, h)
+    const int nvalid = T - t0 < C ? T - t0 : C;                // rows of this chunk below T
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
 
-    // 1. stage K and Q; rows >= T are selected to zero
-    for (int e = tid; e < C * 32; e += 256) {
-        const int r = e >> 5, c4 = (e & 31) * 4;
-        const bool ok = t0 + r < T;
+    // 1. every global read of the kernel is issued here; rows >= T are then
+    //    replaced by zeros with selects (the reads stay inside T_pad rows)
+    float4 kk[NV4], qq[NV4], gg[NV4];
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+        const int e = tid + kPrepThreads * i, r = e >> 5, c4 = (e & 31) * 4;
         const size_t off = (row0 + (size_t)r * heads) * kD + c4;
-        const float4 kk = ok ? ld4(k + off) : z4;
-        const float4 qq = ok ? ld4(q + off) : z4;
-        lds4_st(&sK[r * LD + c4], kk);
-        lds4_st(&sQ[r * LD + c4], qq);
+        kk[i] = ld4(k + off);
+        qq[i] = ld4(q + off);
+        gg[i] = ld4(gate + off);
     }
-    // block-local cumulative log2 decay
-    for (int e = tid; e < NT * kD; e += 256) {
-        const int j = e & (kD - 1), R = e >> 7;
+    // V in the B-operand layout of the U tiles: rows 16 y + 4 q4 + e, column 16 wave + l16
+    float vb[NT][4];
+#pragma unroll
+    for (int y = 0; y < NT; ++y)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            vb[y][e] = v[(row0 + (size_t)(16 * y + 4 * q4 + e) * heads) * kD + 16 * wave + l16];
+    const float braw = tid < C ? beta[row0 + (size_t)tid * heads] : 0.f;
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+        const int e = tid + kPrepThreads * i, r = e >> 5, c4 = (e & 31) * 4;
+        const bool ok = r < nvalid;
+        lds4_st(&sK[r * LD + c4], ok ? kk[i] : z4);
+        lds4_st(&sQ[r * LD + c4], ok ? qq[i] : z4);
+        const float4 g = ok ? gg[i] : z4;
+        lds4_st(&sL[r * LD + c4], make_float4(g.x * kLog2e, g.y * kLog2e, g.z * kLog2e, g.w * kLog2e));
+    }
+#pragma unroll
+    for (int y = 0; y < NT; ++y)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vb[y][e] = 16 * y + 4 * q4 + e < nvalid ? vb[y][e] : 0.f;
+    if (tid < C) sBeta[tid] = tid < nvalid ? braw : 0.f;
+    __syncthreads();
+
+    // 2. cumulative sums inside each 16-row block, then per-column block prefixes
+    if (tid < NT * kD) {
+        const int j = tid & (kD - 1), R = tid >> 7;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = sL[(16 * R + r) * LD + j];
         float acc = 0.f;
-        for (int r = 16 * R; r < 16 * R + 16; ++r) {
-            const bool ok = t0 + r < T;
-            const float g = ok ? gate[(row0 + (size_t)r * heads) * kD + j] : 0.f;
-            acc = fmaf(g, kLog2e, acc);
-            sL[r * LD + j] = acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            acc += x[r];
+            sL[(16 * R + r) * LD + j] = acc;
         }
         sBlk[R * kD + j] = acc;
     }
-    if (tid < C) sBeta[tid] = (t0 + tid < T) ? beta[row0 + (size_t)tid * heads] : 0.f;
+    __syncthreads();
+    if (tid < kD) {
+        float bl[NT];
+#pragma unroll
+        for (int R = 0; R < NT; ++R) bl[R] = sBlk[R * kD + tid];
+        float pre = 0.f, suf = 0.f;
+#pragma unroll
+        for (int R = 0; R < NT; ++R) {
+            sPre[R * kD + tid] = pre;
+            pre += bl[R];
+        }
+#pragma unroll
+        for (int R = NT - 1; R >= 0; --R) {
+            sSuf[R * kD + tid] = suf;
+            suf += bl[R];
+        }
+        rec[G::kOffGam + tid] = exp2_fast(pre);  // gamma = e^{G_last}
+    }
     __syncthreads();
 
-    // 2. Qhat = e^G o Q, Ktil^T = (e^{G_last - G} o K)^T and gamma = e^{G_last}
-    for (int e = tid; e < C * kD; e += 256) {
-        const int r = e >> 7, j = e & (kD - 1), R = r >> 4;
-        float pre = 0.f;
-        for (int X = 0; X < R; ++X) pre += sBlk[X * kD + j];
-        rec[G::kOffQ + e] = sQ[r * LD + j] * exp2_fast(pre + sL[r * LD + j]);
-    }
-    for (int e = tid; e < C * kD; e += 256) {
-        const int j = e / C, r = e % C, R = r >> 4;
-        float suf = 0.f;
-        for (int X = R + 1; X < NT; ++X) suf += sBlk[X * kD + j];
-        rec[G::kOffKt + e] = sK[r * LD + j] * exp2_fast(suf + (sBlk[R * kD + j] - sL[r * LD + j]));
-    }
-    if (tid < kD) {
-        float tot = 0.f;
-        for (int X = 0; X < NT; ++X) tot += sBlk[X * kD + tid];
-        rec[G::kOffGam + tid] = exp2_fast(tot);
-    }
-
-    // 3. A and M, one 16x16 block pair (R, S <= R) per wave at a time
-    for (int p = wave; p < G::kPairs; p += 4) {
+    // 3a. A and M, one 16x16 block pair (R, S <= R) per wave at a time
+    for (int p = wave; p < G::kPairs; p += NW) {
         int R = 0;
         while ((R + 1) * (R + 2) / 2 <= p) ++R;
         const int S = p - R * (R + 1) / 2;
@@ -149,15 +181,16 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(const float* __restr
             const float4 ls = lds4(&sL[sb * LD + i0]);
             float4 er, es;  // log2 exponents of the row and column factors
             if (S < R) {
-                float4 mid = z4;
-                for (int X = S + 1; X < R; ++X) {
-                    const float4 bx = lds4(&sBlk[X * kD + i0]);
-                    mid.x += bx.x; mid.y += bx.y; mid.z += bx.z; mid.w += bx.w;
-                }
+                // reference: last row of block S.  Row factor 2^(L_r + blocks S+1..R-1),
+                // column factor 2^(B_S - L_s); both <= 1 for gates <= 0
+                const float4 pr = lds4(&sPre[R * kD + i0]);
+                const float4 ps = lds4(&sPre[(S + 1) * kD + i0]);
                 const float4 bs = lds4(&sBlk[S * kD + i0]);
-                er = make_float4(lr.x + mid.x, lr.y + mid.y, lr.z + mid.z, lr.w + mid.w);
+                er = make_float4(lr.x + (pr.x - ps.x), lr.y + (pr.y - ps.y), lr.z + (pr.z - ps.z),
+                                 lr.w + (pr.w - ps.w));
                 es = make_float4(bs.x - ls.x, bs.y - ls.y, bs.z - ls.z, bs.w - ls.w);
             } else {
+                // reference: row 7 of the block; each factor spans at most 8 gates
                 const float4 lm = lds4(&sL[(16 * R + 7) * LD + i0]);
                 er = make_float4(lr.x - lm.x, lr.y - lm.y, lr.z - lm.z, lr.w - lm.w);
                 es = make_float4(lm.x - ls.x, lm.y - ls.y, lm.z - ls.z, lm.w - ls.w);
@@ -177,10 +210,35 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(const float* __restr
             rec[G::kOffM + (size_t)r * C + s] = (S < R || s <= r) ? accM[e] : 0.f;
         }
     }
-    for (int e = tid; e < C * C; e += 256) {
+    // 3b. Qhat = e^G o Q and Ktil^T = (e^{G_last - G} o K)^T straight to the record,
+    //     the upper blocks of M as zeros
+#pragma unroll 4
+    for (int e = tid; e < C * kD; e += kPrepThreads) {
+        const int r = e >> 7, j = e & (kD - 1), R = r >> 4;
+        rec[G::kOffQ + e] = sQ[r * LD + j] * exp2_fast(sPre[R * kD + j] + sL[r * LD + j]);
+    }
+#pragma unroll 4
+    for (int e = tid; e < C * kD; e += kPrepThreads) {
+        const int j = e / C, r = e % C, R = r >> 4;
+        rec[G::kOffKt + e] =
+            sK[r * LD + j] * exp2_fast(sSuf[R * kD + j] + (sBlk[R * kD + j] - sL[r * LD + j]));
+    }
+    for (int e = tid; e < C * C; e += kPrepThreads) {
         const int r = e / C, s = e % C;
         if ((s >> 4) > (r >> 4)) rec[G::kOffM + e] = 0.f;
     }
+    // 3c. right-hand sides of W and U in the B-operand layout of this wave's
+    //     column block: beta e^G o K and beta V at rows 16 y + 4 q4 + e
+    float bw[NT][4], bu[NT][4];
+#pragma unroll
+    for (int y = 0; y < NT; ++y)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int s = 16 * y + 4 * q4 + e, i = 16 * wave + l16;
+            const float bb = sBeta[s];
+            bw[y][e] = bb * (exp2_fast(sPre[y * kD + i] + sL[s * LD + i]) * sK[s * LD + i]);
+            bu[y][e] = bb * vb[y][e];
+        }
     __syncthreads();
 
     // 4a. T_RR = (I + A_RR)^-1 for each diagonal block, by forward substitution
@@ -200,6 +258,7 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(const float* __restr
     __syncthreads();
     // 4b. off-diagonal blocks, by distance from the diagonal:
     //     T_RS = -T_RR sum_{X=S}^{R-1} A_RX T_XS
+#pragma unroll
     for (int d = 1; d < NT; ++d) {
         const int S = wave, R = wave + d;
         if (R < NT) {
@@ -220,39 +279,146 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(const float* __restr
         __syncthreads();
     }
 
-    // 5. right-hand sides: beta e^G o K (over Q, now dead) and beta V (over the decay table)
-    for (int e = tid; e < C * kD; e += 256) {
-        const int r = e >> 7, j = e & (kD - 1), R = r >> 4;
-        float pre = 0.f;
-        for (int X = 0; X < R; ++X) pre += sBlk[X * kD + j];
-        sQ[r * LD + j] = sBeta[r] * (exp2_fast(pre + sL[r * LD + j]) * sK[r * LD + j]);
-    }
-    __syncthreads();
-    for (int e = tid; e < C * 32; e += 256) {
-        const int r = e >> 5, c4 = (e & 31) * 4;
-        const bool ok = t0 + r < T;
-        const float4 vv = ok ? ld4(v + (row0 + (size_t)r * heads) * kD + c4) : z4;
-        const float bb = sBeta[r];
-        lds4_st(&sL[r * LD + c4], make_float4(bb * vv.x, bb * vv.y, bb * vv.z, bb * vv.w));
-    }
-    __syncthreads();
-
-    // 6. W = T (beta e^G o K) and U = T (beta V), 16x16 output tiles
-    for (int job = wave; job < 2 * NT * 8; job += 4) {
-        const int which = job / (NT * 8);
-        const int X = (job >> 3) % NT, cc = job & 7;
-        const float* Bm = which ? sL : sQ;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int Y = 0; Y <= X; ++Y) {
-            const float4 t4 = lds4(&sT[(16 * X + l16) * LDC + 16 * Y + 4 * q4]);
+    // 5. W = T (beta e^G o K) and U = T (beta V): this wave's 16-column block, all row tiles
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                acc = mfma4(comp(t4, e), Bm[(16 * Y + 4 * q4 + e) * LD + 16 * cc + l16], acc);
+    for (int X = 0; X < NT; ++X) {
+        floatx4 accW = {0.f, 0.f, 0.f, 0.f}, accU = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int y = 0; y <= X; ++y) {
+            const float4 t4 = lds4(&sT[(16 * X + l16) * LDC + 16 * y + 4 * q4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                accW = mfma4(comp(t4, e), bw[y][e], accW);
+                accU = mfma4(comp(t4, e), bu[y][e], accU);
+            }
         }
-        float* dst = rec + (which ? G::kOffU : G::kOffW);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[(size_t)(16 * X + 4 * q4 + e) * kD + 16 * cc + l16] = acc[e];
+        for (int e = 0; e < 4; ++e) {
+            const size_t o = (size_t)(16 * X + 4 * q4 + e) * kD + 16 * wave + l16;
+            rec[G::kOffW + o] = accW[e];
+            rec[G::kOffU + o] = accU[e];
+        }
     }
+}
+
+// Operands one wave of the scan reads from a chunk record, prefetched a chunk
+// ahead into registers.
+template <int C>
+struct ScanOps {
+    static constexpr int NT = C / 16;
+    float4 w[8];        // W rows of the Delta tile owned by this wave
+    float u[4];         // U tile (this wave's lanes)
+    float4 qh[8];       // Qhat rows of the output tile owned by this wave
+    float4 m[NT];       // M rows of that output tile (upper blocks are zero)
+    float4 kt[2][NT];   // Ktil^T rows of the two state tiles this wave updates
+    float4 g[2];        // gamma for those rows
+};
+
+template <int C>
+__device__ __forceinline__ void scan_load(ScanOps<C>& o, const float* rec, bool has_d, int xd, bool has_p, int xp,
+                                          int wave, int l16, int q4, int v0)
+{
+    using G = ChunkGeom<C>;
+    constexpr int NT = C / 16;
+    if (has_d) {
+        const float* wr = rec + G::kOffW + (size_t)(16 * xd + l16) * kD + 4 * q4;
+#pragma unroll
+        for (int tau = 0; tau < 8; ++tau) o.w[tau] = ld4(wr + 16 * tau);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o.u[e] = rec[G::kOffU + (size_t)(16 * xd + 4 * q4 + e) * kD + v0 + l16];
+    }
+    if (has_p) {
+        const float* qr = rec + G::kOffQ + (size_t)(16 * xp + l16) * kD + 4 * q4;
+#pragma unroll
+        for (int tau = 0; tau < 8; ++tau) o.qh[tau] = ld4(qr + 16 * tau);
+        const float* mr = rec + G::kOffM + (size_t)(16 * xp + l16) * C + 4 * q4;
+#pragma unroll
+        for (int y = 0; y < NT; ++y) o.m[y] = ld4(mr + 16 * y);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int tile = 2 * wave + s;
+        const float* kr = rec + G::kOffKt + (size_t)(16 * tile + l16) * C + 4 * q4;
+#pragma unroll
+        for (int y = 0; y < NT; ++y) o.kt[s][y] = ld4(kr + 16 * y);
+        o.g[s] = ld4(rec + G::kOffGam + 16 * tile + 4 * q4);
+    }
+}
+
+// One chunk of the scan for one wave: Delta tile, state tiles, output tile.
+template <int C>
+__device__ __forceinline__ void scan_chunk(const ScanOps<C>& cur, floatx4 (&S)[8], floatx4 (*sDelta)[64],
+                                       floatx4 (*sS)[64], float* __restrict__ out, int c, bool has_d, int xd,
+                                       bool has_p, int xp, int wave, int lane, int l16, int q4, int v0, int b,
+                                       int h, int heads, int T, int t_pad)
+{
+    constexpr int NT = C / 16;
+    // 1. Delta = U - W S for tile xd
+    if (has_d) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tau = 0; tau < 8; ++tau) {
+            acc = mfma4(cur.w[tau].x, S[tau][0], acc);
+            acc = mfma4(cur.w[tau].y, S[tau][1], acc);
+            acc = mfma4(cur.w[tau].z, S[tau][2], acc);
+            acc = mfma4(cur.w[tau].w, S[tau][3], acc);
+        }
+        floatx4 d;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = cur.u[e] - acc[e];
+        sDelta[xd][lane] = d;
+    }
+    __syncthreads();
+    floatx4 dl[NT];
+#pragma unroll
+    for (int y = 0; y < NT; ++y) dl[y] = sDelta[y][lane];
+
+    // 2. S <- diag(gamma) S + Ktil^T Delta for tiles 2 wave, 2 wave + 1
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        if ((s >> 1) != wave) continue;
+        const int i = s & 1;
+        floatx4 acc;
+        acc[0] = cur.g[i].x * S[s][0];
+        acc[1] = cur.g[i].y * S[s][1];
+        acc[2] = cur.g[i].z * S[s][2];
+        acc[3] = cur.g[i].w * S[s][3];
+#pragma unroll
+        for (int y = 0; y < NT; ++y) {
+            acc = mfma4(cur.kt[i][y].x, dl[y][0], acc);
+            acc = mfma4(cur.kt[i][y].y, dl[y][1], acc);
+            acc = mfma4(cur.kt[i][y].z, dl[y][2], acc);
+            acc = mfma4(cur.kt[i][y].w, dl[y][3], acc);
+        }
+        sS[s][lane] = acc;
+    }
+
+    // 3. O = Qhat S + M Delta for tile xp (S still holds the chunk's incoming state)
+    if (has_p) {
+        floatx4 P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tau = 0; tau < 8; ++tau) {
+            P = mfma4(cur.qh[tau].x, S[tau][0], P);
+            P = mfma4(cur.qh[tau].y, S[tau][1], P);
+            P = mfma4(cur.qh[tau].z, S[tau][2], P);
+            P = mfma4(cur.qh[tau].w, S[tau][3], P);
+        }
+#pragma unroll
+        for (int y = 0; y < NT; ++y) {
+            P = mfma4(cur.m[y].x, dl[y][0], P);
+            P = mfma4(cur.m[y].y, dl[y][1], P);
+            P = mfma4(cur.m[y].z, dl[y][2], P);
+            P = mfma4(cur.m[y].w, dl[y][3], P);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = c * C + 16 * xp + 4 * q4 + e;
+            if (t < T) out[(((size_t)b * t_pad + t) * heads + h) * kD + v0 + l16] = P[e];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) S[s] = sS[s][lane];
 }
 
 template <int C>
@@ -273,6 +439,12 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const float* __restrict
     const int l16 = lane & 15, q4 = lane >> 4;
     const int v0 = 16 * slice;
 
+    // Work of this wave in every chunk: the Delta tile xd (if xd < NT), the
+    // output tile xp (if xp < NT) and the state tiles 2 wave, 2 wave + 1.
+    const int xd = wave;
+    const int xp = ((wave - NT) % 4 + 4) % 4;
+    const bool has_d = xd < NT, has_p = xp < NT;
+
     __shared__ floatx4 sDelta[NT][64];
     __shared__ floatx4 sS[8][64];
 
@@ -285,81 +457,22 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const float* __restrict
 #pragma unroll
         for (int e = 0; e < 4; ++e) S[s][e] = S_head[(size_t)(16 * s + 4 * q4 + e) * kD + v0 + l16];
 
-    int own = -1;  // output tile finished by this wave
-    for (int j = NT; j < 2 * NT; ++j)
-        if ((j & 3) == wave) own = j - NT;
-
-    for (int c = 0; c < nchunks; ++c) {
-        const float* rec = ws + ((size_t)bh * nchunks + c) * G::kRecord;
-        floatx4 P = {0.f, 0.f, 0.f, 0.f};
-        // phase 1: Delta tiles (W S) and the Qhat S part of the output tiles
-        for (int job = wave; job < 2 * NT; job += 4) {
-            const bool is_delta = job < NT;
-            const int X = is_delta ? job : job - NT;
-            const float* Am = rec + (is_delta ? G::kOffW : G::kOffQ) + (size_t)(16 * X + l16) * kD + 4 * q4;
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int tau = 0; tau < 8; ++tau) {
-                const float4 a4 = ld4(Am + 16 * tau);
-                acc = mfma4(a4.x, S[tau][0], acc);
-                acc = mfma4(a4.y, S[tau][1], acc);
-                acc = mfma4(a4.z, S[tau][2], acc);
-                acc = mfma4(a4.w, S[tau][3], acc);
-            }
-            if (is_delta) {
-                floatx4 d;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    d[e] = rec[G::kOffU + (size_t)(16 * X + 4 * q4 + e) * kD + v0 + l16] - acc[e];
-                sDelta[X][lane] = d;
-            } else {
-                P = acc;
-            }
-        }
-        __syncthreads();
-        // phase 2a: O = Qhat S + M Delta
-        if (own >= 0) {
-            const int X = own;
-            const float* Mm = rec + G::kOffM + (size_t)(16 * X + l16) * C + 4 * q4;
-            for (int Y = 0; Y <= X; ++Y) {
-                const floatx4 d = sDelta[Y][lane];
-                const float4 m4 = ld4(Mm + 16 * Y);
-                P = mfma4(m4.x, d[0], P);
-                P = mfma4(m4.y, d[1], P);
-                P = mfma4(m4.z, d[2], P);
-                P = mfma4(m4.w, d[3], P);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = c * C + 16 * X + 4 * q4 + e;
-                if (t < T) out[(((size_t)b * t_pad + t) * heads + h) * kD + v0 + l16] = P[e];
-            }
-        }
-        // phase 2b: S <- diag(gamma) S + Ktil^T Delta, tiles 2 wave and 2 wave + 1
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            if ((s >> 1) != wave) continue;
-            const float4 g4 = ld4(rec + G::kOffGam + 16 * s + 4 * q4);
-            floatx4 acc;
-            acc[0] = g4.x * S[s][0];
-            acc[1] = g4.y * S[s][1];
-            acc[2] = g4.z * S[s][2];
-            acc[3] = g4.w * S[s][3];
-            const float* Km = rec + G::kOffKt + (size_t)(16 * s + l16) * C + 4 * q4;
-#pragma unroll
-            for (int Y = 0; Y < NT; ++Y) {
-                const floatx4 d = sDelta[Y][lane];
-                const float4 k4 = ld4(Km + 16 * Y);
-                acc = mfma4(k4.x, d[0], acc);
-                acc = mfma4(k4.y, d[1], acc);
-                acc = mfma4(k4.z, d[2], acc);
-                acc = mfma4(k4.w, d[3], acc);
-            }
-            sS[s][lane] = acc;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int s = 0; s < 8; ++s) S[s] = sS[s][lane];
+    const float* const rec0 = ws + (size_t)bh * nchunks * G::kRecord;
+    // Two operand buffers in ping-pong: while one chunk is computed from one
+    // buffer, the loads of the next chunk land in the other (no register
+    // copies, so no wait on the prefetch before it is needed).
+    ScanOps<C> opA, opB;
+    scan_load<C>(opA, rec0, has_d, xd, has_p, xp, wave, l16, q4, v0);
+    for (int c = 0; c < nchunks; c += 2) {
+        const int c1 = c + 1 < nchunks ? c + 1 : c;
+        scan_load<C>(opB, rec0 + (size_t)c1 * G::kRecord, has_d, xd, has_p, xp, wave, l16, q4, v0);
+        scan_chunk<C>(opA, S, sDelta, sS, out, c, has_d, xd, has_p, xp, wave, lane, l16, q4, v0, b, h, heads, T,
+                      t_pad);
+        if (c + 1 >= nchunks) break;
+        const int c2 = c + 2 < nchunks ? c + 2 : c + 1;
+        scan_load<C>(opA, rec0 + (size_t)c2 * G::kRecord, has_d, xd, has_p, xp, wave, l16, q4, v0);
+        scan_chunk<C>(opB, S, sDelta, sS, out, c + 1, has_d, xd, has_p, xp, wave, lane, l16, q4, v0, b, h, heads,
+                      T, t_pad);
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -376,7 +489,7 @@ static int launch_chunk(const float* q, const float* k, const float* v, const fl
 {
     const int nchunks = t_pad / C;
     const long long n_bh = (long long)batch * heads;
-    hipLaunchKernelGGL(chunk_prepare_kernel<C>, dim3((unsigned)(n_bh * nchunks)), dim3(256), 0, stream, q, k, v,
+    hipLaunchKernelGGL(chunk_prepare_kernel<C>, dim3((unsigned)(n_bh * nchunks)), dim3(kPrepThreads), 0, stream, q, k, v,
                        gate, beta, ws, heads, T, t_pad, nchunks);
     if (hipGetLastError() != hipSuccess) return -1;
     const unsigned grid = (unsigned)(((n_bh + 7) / 8) * 64);
