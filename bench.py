@@ -247,6 +247,7 @@ def main():
     ap.add_argument("--only", default="", help="comma list of workloads to time (default: all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--copy-probe", action="store_true", help="time one plain 1 GiB device copy and exit")
+    ap.add_argument("--reps", type=int, default=0, help="override the repetitions of every workload (profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the core needs no collective and "
@@ -263,7 +264,7 @@ def main():
         n = 1 << 28  # 1 GiB of fp32
         src = torch.randn(n, device="cuda")
         dst = torch.empty_like(src)
-        r = timer.run(lambda i: dst.copy_(src), 20, 3)
+        r = timer.run(lambda i: dst.copy_(src), args.reps or 20, 0 if args.reps else 3)
         log(f"copy probe: 1 GiB read + 1 GiB write, {2 * n * 4 / r['launch_avg_s'] / 1e9:.1f} GB/s")
         return
 
@@ -274,7 +275,7 @@ def main():
     headline = None
     if want("decode_b64_h32"):
         log("decode_b64_h32")
-        w, r, nbytes, n_buf = bench_decode(torch, kda, ki, args.steps, args.warmup, timer)
+        w, r, nbytes, n_buf = bench_decode(torch, kda, ki, args.reps or args.steps, args.warmup, timer)
         gbs = nbytes / r["launch_avg_s"] / 1e9
         headline = (w, r, nbytes, n_buf, gbs)
         workloads[w.name] = {"tokens_per_s": w.batch / r["s_per_step"], "us_per_step": r["s_per_step"] * 1e6,
@@ -282,7 +283,7 @@ def main():
                              "hbm_frac": gbs / HBM_PEAK_GBS, "state_buffers_rotated": n_buf}
     if want("decode_k4_b128_h32"):
         log("decode_k4_b128_h32")
-        w, r, nbytes = bench_decode_k(torch, kda, ki, max(10, args.steps // 2), args.warmup, timer)
+        w, r, nbytes = bench_decode_k(torch, kda, ki, args.reps or max(10, args.steps // 2), args.warmup, timer)
         gbs = nbytes / r["launch_avg_s"] / 1e9
         workloads[w.name] = {"tokens_per_s": w.batch * w.T / r["s_per_step"], "us_per_call": r["s_per_step"] * 1e6,
                              "kernel_us": r["launch_avg_s"] * 1e6, "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
@@ -291,7 +292,7 @@ def main():
         if not want(name):
             continue
         log(name)
-        w, r, extra = bench_prefill(torch, kda, ki, name, steps, 2, timer)
+        w, r, extra = bench_prefill(torch, kda, ki, name, args.reps or steps, 0 if args.reps else 2, timer)
         fl = prefill_flops(w.batch, w.heads, w.T, w.chunk)
         tf = fl / r["launch_avg_s"] / 1e12
         res = {"tokens_per_s": w.batch * w.T / r["s_per_step"], "ms_per_call": r["s_per_step"] * 1e3,

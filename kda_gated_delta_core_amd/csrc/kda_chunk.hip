@@ -61,6 +61,24 @@ __device__ __forceinline__ float comp(const float4& v, int e)
     return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
 }
 
+// A-operand tile order.  A matrix stored as 16x16 tiles, tile t = a * n_cols + b
+// covering rows 16a.. and columns 16b.., each tile as [lane][4]: lane l holds
+// the four consecutive columns 16b + 4 (l / 16) + 0..3 of row 16a + l % 16, which
+// is what lane l feeds to four successive 16x16x4 MFMA steps.  A wave then
+// loads one tile with a single contiguous 1 KiB access.
+__device__ __forceinline__ size_t atile_index(int tile, int row_in, int col_in)
+{
+    const int lane = (col_in >> 2) * 16 + row_in;
+    return ((size_t)tile * 64 + lane) * 4 + (col_in & 3);
+}
+// inverse: element e of an A-tiled matrix with n_cols column tiles -> (row, col)
+__device__ __forceinline__ void atile_coords(int e, int n_cols, int& row, int& col)
+{
+    const int tile = e >> 8, lane = (e >> 2) & 63;
+    row = (tile / n_cols) * 16 + (lane & 15);
+    col = (tile % n_cols) * 16 + (lane >> 4) * 4 + (e & 3);
+}
+
 constexpr int kPrepThreads = 512;  // 8 waves: one per 16-column block in the W/U stage
 
 template <int C>
@@ -207,25 +225,30 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * R + 4 * q4 + e, s = 16 * S + l16;
             sA[r * LDC + s] = (S < R || s < r) ? sBeta[r] * accA[e] : 0.f;
-            rec[G::kOffM + (size_t)r * C + s] = (S < R || s <= r) ? accM[e] : 0.f;
+            rec[G::kOffM + atile_index(R * NT + S, r & 15, s & 15)] = (S < R || s <= r) ? accM[e] : 0.f;
         }
     }
-    // 3b. Qhat = e^G o Q and Ktil^T = (e^{G_last - G} o K)^T straight to the record,
-    //     the upper blocks of M as zeros
+    // 3b. Qhat = e^G o Q and Ktil^T = (e^{G_last - G} o K)^T straight to the record
+    //     in A-operand tile order (consecutive threads write consecutive floats),
+    //     the upper blocks of M as zero tiles
 #pragma unroll 4
     for (int e = tid; e < C * kD; e += kPrepThreads) {
-        const int r = e >> 7, j = e & (kD - 1), R = r >> 4;
-        rec[G::kOffQ + e] = sQ[r * LD + j] * exp2_fast(sPre[R * kD + j] + sL[r * LD + j]);
+        int row, col;
+        atile_coords(e, 8, row, col);            // Qhat tile (row block, column block)
+        const int R = row >> 4;
+        rec[G::kOffQ + e] = sQ[row * LD + col] * exp2_fast(sPre[R * kD + col] + sL[row * LD + col]);
     }
 #pragma unroll 4
     for (int e = tid; e < C * kD; e += kPrepThreads) {
-        const int j = e / C, r = e % C, R = r >> 4;
+        int i, r;
+        atile_coords(e, NT, i, r);               // Ktil^T tile: row = key channel i, column = chunk row r
+        const int R = r >> 4;
         rec[G::kOffKt + e] =
-            sK[r * LD + j] * exp2_fast(sSuf[R * kD + j] + (sBlk[R * kD + j] - sL[r * LD + j]));
+            sK[r * LD + i] * exp2_fast(sSuf[R * kD + i] + (sBlk[R * kD + i] - sL[r * LD + i]));
     }
     for (int e = tid; e < C * C; e += kPrepThreads) {
-        const int r = e / C, s = e % C;
-        if ((s >> 4) > (r >> 4)) rec[G::kOffM + e] = 0.f;
+        const int tile = e >> 8;
+        if (tile % NT > tile / NT) rec[G::kOffM + e] = 0.f;
     }
     // 3c. right-hand sides of W and U in the B-operand layout of this wave's
     //     column block: beta e^G o K and beta V at rows 16 y + 4 q4 + e
@@ -293,122 +316,113 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
             }
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const size_t o = (size_t)(16 * X + 4 * q4 + e) * kD + 16 * wave + l16;
-            rec[G::kOffW + o] = accW[e];
-            rec[G::kOffU + o] = accU[e];
-        }
+        for (int e = 0; e < 4; ++e) rec[G::kOffW + atile_index(X * 8 + wave, 4 * q4 + e, l16)] = accW[e];
+        // U in the scan's accumulator layout: [row tile][16-column block][lane][4]
+        st4(rec + G::kOffU + ((size_t)(X * 8 + wave) * 64 + lane) * 4,
+            make_float4(accU[0], accU[1], accU[2], accU[3]));
     }
 }
 
+constexpr int kScanThreads = 512;  // 8 waves, two per SIMD
+
 // Operands one wave of the scan reads from a chunk record, prefetched a chunk
-// ahead into registers.
+// ahead into registers.  Wave roles inside a chunk (NT = C / 16 row tiles):
+//   wave < NT           Delta tile xd = wave:   Delta = U - W S
+//   NT <= wave < 2 NT   output tile xp = wave - NT:  O = Qhat S + M Delta
+//   every wave          state tile `wave`:      S <- diag(gamma) S + Ktil^T Delta
 template <int C>
 struct ScanOps {
     static constexpr int NT = C / 16;
-    float4 w[8];        // W rows of the Delta tile owned by this wave
-    float u[4];         // U tile (this wave's lanes)
-    float4 qh[8];       // Qhat rows of the output tile owned by this wave
-    float4 m[NT];       // M rows of that output tile (upper blocks are zero)
-    float4 kt[2][NT];   // Ktil^T rows of the two state tiles this wave updates
-    float4 g[2];        // gamma for those rows
+    float4 a[8];     // W rows of the Delta tile, or Qhat rows of the output tile
+    float4 x[NT];    // Delta waves: U tile (every x[y] holds it); output waves: M rows (upper blocks zero)
+    float4 kt[NT];   // Ktil^T rows of this wave's state tile
+    float4 g;        // gamma at those rows
 };
 
+// Every wave issues the same load sequence (only the addresses depend on its
+// role), so the wait counts the compiler derives stay exact across the loop.
 template <int C>
-__device__ __forceinline__ void scan_load(ScanOps<C>& o, const float* rec, bool has_d, int xd, bool has_p, int xp,
-                                          int wave, int l16, int q4, int v0)
+__device__ __forceinline__ void scan_load(ScanOps<C>& o, const float* rec, bool is_d, int xd, bool is_p, int xp,
+                                          int wave, int lane, int l16, int q4, int slice)
 {
     using G = ChunkGeom<C>;
     constexpr int NT = C / 16;
-    if (has_d) {
-        const float* wr = rec + G::kOffW + (size_t)(16 * xd + l16) * kD + 4 * q4;
+    const int xa = is_d ? xd : (is_p ? xp : 0);
+    const float* ar = rec + (is_d ? G::kOffW : G::kOffQ) + ((size_t)xa * 8 * 64 + lane) * 4;
 #pragma unroll
-        for (int tau = 0; tau < 8; ++tau) o.w[tau] = ld4(wr + 16 * tau);
+    for (int tau = 0; tau < 8; ++tau) o.a[tau] = ld4(ar + tau * 256);
+    const float* ur = rec + G::kOffU + ((size_t)((is_d ? xd : 0) * 8 + slice) * 64 + lane) * 4;
+    const float* mr = rec + G::kOffM + ((size_t)(is_p ? xp : 0) * NT * 64 + lane) * 4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o.u[e] = rec[G::kOffU + (size_t)(16 * xd + 4 * q4 + e) * kD + v0 + l16];
-    }
-    if (has_p) {
-        const float* qr = rec + G::kOffQ + (size_t)(16 * xp + l16) * kD + 4 * q4;
+    for (int y = 0; y < NT; ++y) o.x[y] = ld4(is_d ? ur : mr + y * 256);
+    const float* kr = rec + G::kOffKt + ((size_t)wave * NT * 64 + lane) * 4;
 #pragma unroll
-        for (int tau = 0; tau < 8; ++tau) o.qh[tau] = ld4(qr + 16 * tau);
-        const float* mr = rec + G::kOffM + (size_t)(16 * xp + l16) * C + 4 * q4;
-#pragma unroll
-        for (int y = 0; y < NT; ++y) o.m[y] = ld4(mr + 16 * y);
-    }
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        const int tile = 2 * wave + s;
-        const float* kr = rec + G::kOffKt + (size_t)(16 * tile + l16) * C + 4 * q4;
-#pragma unroll
-        for (int y = 0; y < NT; ++y) o.kt[s][y] = ld4(kr + 16 * y);
-        o.g[s] = ld4(rec + G::kOffGam + 16 * tile + 4 * q4);
-    }
+    for (int y = 0; y < NT; ++y) o.kt[y] = ld4(kr + y * 256);
+    o.g = ld4(rec + G::kOffGam + 16 * wave + 4 * q4);
 }
 
-// One chunk of the scan for one wave: Delta tile, state tiles, output tile.
+// One chunk of the scan for one wave.  The state lives in LDS only, in two
+// buffers: sS[cur] holds the chunk's incoming state, sS[cur ^ 1] receives the
+// outgoing one.  Tile s, element e of lane l is S[16 s + 4 (l / 16) + e][v0 + l % 16],
+// which is directly the B operand of the 16x16x4 MFMA over the key index.
 template <int C>
-__device__ __forceinline__ void scan_chunk(const ScanOps<C>& cur, floatx4 (&S)[8], floatx4 (*sDelta)[64],
-                                       floatx4 (*sS)[64], float* __restrict__ out, int c, bool has_d, int xd,
-                                       bool has_p, int xp, int wave, int lane, int l16, int q4, int v0, int b,
-                                       int h, int heads, int T, int t_pad)
+__device__ __forceinline__ void scan_chunk(const ScanOps<C>& cur, floatx4 (*sIn)[64], floatx4 (*sOut)[64],
+                                           floatx4 (*sDelta)[64], float* __restrict__ out, int c, bool is_d,
+                                           int xd, bool is_p, int xp, int wave, int lane, int q4, int v0, int l16,
+                                           int b, int h, int heads, int T, int t_pad)
 {
     constexpr int NT = C / 16;
-    // 1. Delta = U - W S for tile xd
-    if (has_d) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    // A. W S (Delta waves) or Qhat S (output waves) against the chunk's incoming state
+    floatx4 P = {0.f, 0.f, 0.f, 0.f};
+    if (is_d || is_p) {
 #pragma unroll
         for (int tau = 0; tau < 8; ++tau) {
-            acc = mfma4(cur.w[tau].x, S[tau][0], acc);
-            acc = mfma4(cur.w[tau].y, S[tau][1], acc);
-            acc = mfma4(cur.w[tau].z, S[tau][2], acc);
-            acc = mfma4(cur.w[tau].w, S[tau][3], acc);
+            const floatx4 st = sIn[tau][lane];
+            P = mfma4(cur.a[tau].x, st[0], P);
+            P = mfma4(cur.a[tau].y, st[1], P);
+            P = mfma4(cur.a[tau].z, st[2], P);
+            P = mfma4(cur.a[tau].w, st[3], P);
         }
-        floatx4 d;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) d[e] = cur.u[e] - acc[e];
-        sDelta[xd][lane] = d;
+        if (is_d) {
+            floatx4 d;
+            d[0] = cur.x[0].x - P[0];
+            d[1] = cur.x[0].y - P[1];
+            d[2] = cur.x[0].z - P[2];
+            d[3] = cur.x[0].w - P[3];
+            sDelta[xd][lane] = d;
+        }
     }
     __syncthreads();
     floatx4 dl[NT];
 #pragma unroll
     for (int y = 0; y < NT; ++y) dl[y] = sDelta[y][lane];
 
-    // 2. S <- diag(gamma) S + Ktil^T Delta for tiles 2 wave, 2 wave + 1
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        if ((s >> 1) != wave) continue;
-        const int i = s & 1;
+    // B1. state tile `wave`
+    {
+        const floatx4 so = sIn[wave][lane];
         floatx4 acc;
-        acc[0] = cur.g[i].x * S[s][0];
-        acc[1] = cur.g[i].y * S[s][1];
-        acc[2] = cur.g[i].z * S[s][2];
-        acc[3] = cur.g[i].w * S[s][3];
+        acc[0] = cur.g.x * so[0];
+        acc[1] = cur.g.y * so[1];
+        acc[2] = cur.g.z * so[2];
+        acc[3] = cur.g.w * so[3];
 #pragma unroll
         for (int y = 0; y < NT; ++y) {
-            acc = mfma4(cur.kt[i][y].x, dl[y][0], acc);
-            acc = mfma4(cur.kt[i][y].y, dl[y][1], acc);
-            acc = mfma4(cur.kt[i][y].z, dl[y][2], acc);
-            acc = mfma4(cur.kt[i][y].w, dl[y][3], acc);
+            acc = mfma4(cur.kt[y].x, dl[y][0], acc);
+            acc = mfma4(cur.kt[y].y, dl[y][1], acc);
+            acc = mfma4(cur.kt[y].z, dl[y][2], acc);
+            acc = mfma4(cur.kt[y].w, dl[y][3], acc);
         }
-        sS[s][lane] = acc;
+        sOut[wave][lane] = acc;
     }
-
-    // 3. O = Qhat S + M Delta for tile xp (S still holds the chunk's incoming state)
-    if (has_p) {
-        floatx4 P = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int tau = 0; tau < 8; ++tau) {
-            P = mfma4(cur.qh[tau].x, S[tau][0], P);
-            P = mfma4(cur.qh[tau].y, S[tau][1], P);
-            P = mfma4(cur.qh[tau].z, S[tau][2], P);
-            P = mfma4(cur.qh[tau].w, S[tau][3], P);
-        }
+    // B2. output tile: O = Qhat S + M Delta over the blocks y <= xp
+    if (is_p) {
 #pragma unroll
         for (int y = 0; y < NT; ++y) {
-            P = mfma4(cur.m[y].x, dl[y][0], P);
-            P = mfma4(cur.m[y].y, dl[y][1], P);
-            P = mfma4(cur.m[y].z, dl[y][2], P);
-            P = mfma4(cur.m[y].w, dl[y][3], P);
+            if (y > xp) continue;
+            P = mfma4(cur.x[y].x, dl[y][0], P);
+            P = mfma4(cur.x[y].y, dl[y][1], P);
+            P = mfma4(cur.x[y].z, dl[y][2], P);
+            P = mfma4(cur.x[y].w, dl[y][3], P);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -417,14 +431,12 @@ __device__ __forceinline__ void scan_chunk(const ScanOps<C>& cur, floatx4 (&S)[8
         }
     }
     __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 8; ++s) S[s] = sS[s][lane];
 }
 
 template <int C>
-__global__ __launch_bounds__(256) void chunk_scan_kernel(const float* __restrict__ ws, float* __restrict__ state,
-                                                         float* __restrict__ out, int n_bh, int heads, int T,
-                                                         int t_pad, int nchunks)
+__global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(const float* __restrict__ ws,
+                                                                  float* __restrict__ state, float* __restrict__ out,
+                                                                  int n_bh, int heads, int T, int t_pad, int nchunks)
 {
     using G = ChunkGeom<C>;
     constexpr int NT = G::kTiles;
@@ -438,48 +450,41 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const float* __restrict
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
     const int v0 = 16 * slice;
-
-    // Work of this wave in every chunk: the Delta tile xd (if xd < NT), the
-    // output tile xp (if xp < NT) and the state tiles 2 wave, 2 wave + 1.
-    const int xd = wave;
-    const int xp = ((wave - NT) % 4 + 4) % 4;
-    const bool has_d = xd < NT, has_p = xp < NT;
+    const bool is_d = wave < NT, is_p = wave >= NT && wave < 2 * NT;
+    const int xd = wave, xp = wave - NT;
 
     __shared__ floatx4 sDelta[NT][64];
-    __shared__ floatx4 sS[8][64];
+    __shared__ floatx4 sS[2][8][64];
 
-    // state slice as eight 16x16 accumulator tiles: tile s, element e of lane l
-    // holds S[16 s + 4 (l / 16) + e][v0 + l % 16]; every wave keeps a full copy
     float* const S_head = state + (size_t)bh * kD * kD;
-    floatx4 S[8];
+    {
+        floatx4 st;
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) S[s][e] = S_head[(size_t)(16 * s + 4 * q4 + e) * kD + v0 + l16];
-
+        for (int e = 0; e < 4; ++e) st[e] = S_head[(size_t)(16 * wave + 4 * q4 + e) * kD + v0 + l16];
+        sS[0][wave][lane] = st;
+    }
     const float* const rec0 = ws + (size_t)bh * nchunks * G::kRecord;
     // Two operand buffers in ping-pong: while one chunk is computed from one
     // buffer, the loads of the next chunk land in the other (no register
     // copies, so no wait on the prefetch before it is needed).
     ScanOps<C> opA, opB;
-    scan_load<C>(opA, rec0, has_d, xd, has_p, xp, wave, l16, q4, v0);
+    scan_load<C>(opA, rec0, is_d, xd, is_p, xp, wave, lane, l16, q4, slice);
+    __syncthreads();
     for (int c = 0; c < nchunks; c += 2) {
         const int c1 = c + 1 < nchunks ? c + 1 : c;
-        scan_load<C>(opB, rec0 + (size_t)c1 * G::kRecord, has_d, xd, has_p, xp, wave, l16, q4, v0);
-        scan_chunk<C>(opA, S, sDelta, sS, out, c, has_d, xd, has_p, xp, wave, lane, l16, q4, v0, b, h, heads, T,
-                      t_pad);
+        scan_load<C>(opB, rec0 + (size_t)c1 * G::kRecord, is_d, xd, is_p, xp, wave, lane, l16, q4, slice);
+        scan_chunk<C>(opA, sS[0], sS[1], sDelta, out, c, is_d, xd, is_p, xp, wave, lane, q4, v0, l16, b, h, heads,
+                      T, t_pad);
         if (c + 1 >= nchunks) break;
         const int c2 = c + 2 < nchunks ? c + 2 : c + 1;
-        scan_load<C>(opA, rec0 + (size_t)c2 * G::kRecord, has_d, xd, has_p, xp, wave, l16, q4, v0);
-        scan_chunk<C>(opB, S, sDelta, sS, out, c + 1, has_d, xd, has_p, xp, wave, lane, l16, q4, v0, b, h, heads,
-                      T, t_pad);
+        scan_load<C>(opA, rec0 + (size_t)c2 * G::kRecord, is_d, xd, is_p, xp, wave, lane, l16, q4, slice);
+        scan_chunk<C>(opB, sS[1], sS[0], sDelta, out, c + 1, is_d, xd, is_p, xp, wave, lane, q4, v0, l16, b, h,
+                      heads, T, t_pad);
     }
+    // the final state is in sS[nchunks & 1]
+    const floatx4 st = sS[nchunks & 1][wave][lane];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        if ((s >> 1) != wave) continue;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) S_head[(size_t)(16 * s + 4 * q4 + e) * kD + v0 + l16] = S[s][e];
-    }
+    for (int e = 0; e < 4; ++e) S_head[(size_t)(16 * wave + 4 * q4 + e) * kD + v0 + l16] = st[e];
 }
 
 template <int C>
@@ -493,7 +498,7 @@ static int launch_chunk(const float* q, const float* k, const float* v, const fl
                        gate, beta, ws, heads, T, t_pad, nchunks);
     if (hipGetLastError() != hipSuccess) return -1;
     const unsigned grid = (unsigned)(((n_bh + 7) / 8) * 64);
-    hipLaunchKernelGGL(chunk_scan_kernel<C>, dim3(grid), dim3(256), 0, stream, ws, state, out, (int)n_bh, heads, T,
+    hipLaunchKernelGGL(chunk_scan_kernel<C>, dim3(grid), dim3(kScanThreads), 0, stream, ws, state, out, (int)n_bh, heads, T,
                        t_pad, nchunks);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

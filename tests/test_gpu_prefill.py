@@ -24,6 +24,13 @@ def _prefill(kda, x, T, C, state=None, rows=None):
     return out, st, ws
 
 
+def _unswizzle_a(buf, n_row_tiles, n_col_tiles):
+    """Matrix from the A-tile order of the workspace records: tile (a, b), lane l, element e
+    holds row 16a + l % 16, column 16b + 4 (l // 16) + e."""
+    t = buf.reshape(n_row_tiles, n_col_tiles, 4, 16, 4)        # a, b, l//16, l%16, e
+    return t.transpose(0, 3, 1, 2, 4).reshape(16 * n_row_tiles, 16 * n_col_tiles)
+
+
 def _check_against_oracle(x, T, out, st, tag=""):
     o_ref, s_ref, _, _ = oracle.serial(x["q"], x["k"], x["v"], x["gate"], x["beta"], x["state"], T=T)
     o = host(out)
@@ -87,10 +94,13 @@ def test_prefill_workspace_stages(device):
         stg = oracle.chunk_stages(x["q"], x["k"], x["v"], x["gate"], x["beta"], np.zeros((128, 128)), 0, h,
                                   c * C, n)
         rec = ws[h, c]
-        W, U, Qh = rec[:C * 128].reshape(C, 128), rec[C * 128:2 * C * 128].reshape(C, 128), \
-            rec[2 * C * 128:3 * C * 128].reshape(C, 128)
-        KtT = rec[3 * C * 128:4 * C * 128].reshape(128, C)
-        M = rec[4 * C * 128:4 * C * 128 + C * C].reshape(C, C)
+        W = _unswizzle_a(rec[:C * 128], C // 16, 8)
+        Qh = _unswizzle_a(rec[2 * C * 128:3 * C * 128], C // 16, 8)
+        # U is stored in 16x16 accumulator tiles: [row tile X][column block j][lane][e]
+        Usw = rec[C * 128:2 * C * 128].reshape(C // 16, 8, 4, 16, 4)   # X, j, lane//16, lane%16, e
+        U = Usw.transpose(0, 2, 4, 1, 3).reshape(C, 128)               # row 16X+4(l//16)+e, col 16j+l%16
+        KtT = _unswizzle_a(rec[3 * C * 128:4 * C * 128], 8, C // 16)
+        M = _unswizzle_a(rec[4 * C * 128:4 * C * 128 + C * C], C // 16, C // 16)
         gam = rec[4 * C * 128 + C * C:]
         G = stg["G"]
         q = x["q"][0, c * C:c * C + n, h].astype(np.float64)
