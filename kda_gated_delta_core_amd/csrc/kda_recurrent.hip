@@ -35,7 +35,38 @@ struct RecGeom {
 
 // Value slices per head.  Part of the arithmetic contract: the reduction tree
 // depends on it, and both decode entry points use this one instance.
-constexpr int kRecSlices = 2;
+#ifndef KDA_REC_SLICES
+#define KDA_REC_SLICES 2
+#endif
+constexpr int kRecSlices = KDA_REC_SLICES;
+
+// State traffic is streamed once per call: non-temporal hints keep it from
+// displacing other data in the caches.
+#ifndef KDA_REC_NONTEMPORAL
+#define KDA_REC_NONTEMPORAL 1
+#endif
+__device__ __forceinline__ float4 state_ld(const float* p)
+{
+#if KDA_REC_NONTEMPORAL
+    const float4* q = reinterpret_cast<const float4*>(p);
+    return make_float4(__builtin_nontemporal_load(&q->x), __builtin_nontemporal_load(&q->y),
+                       __builtin_nontemporal_load(&q->z), __builtin_nontemporal_load(&q->w));
+#else
+    return ld4(p);
+#endif
+}
+__device__ __forceinline__ void state_st(float* p, float4 v)
+{
+#if KDA_REC_NONTEMPORAL
+    float4* q = reinterpret_cast<float4*>(p);
+    __builtin_nontemporal_store(v.x, &q->x);
+    __builtin_nontemporal_store(v.y, &q->y);
+    __builtin_nontemporal_store(v.z, &q->z);
+    __builtin_nontemporal_store(v.w, &q->w);
+#else
+    st4(p, v);
+#endif
+}
 
 template <int NSLICE>
 __global__ __launch_bounds__(256) void recurrent_kernel(const float* __restrict__ q, const float* __restrict__ k,
@@ -62,7 +93,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const float* __restrict_
     float* const S_head = state + (size_t)bh * kD * kD;
     float4 s[G::kRows];
 #pragma unroll
-    for (int m = 0; m < G::kRows; ++m) s[m] = ld4(S_head + (size_t)(rg + G::kRowGroups * m) * kD + col);
+    for (int m = 0; m < G::kRows; ++m) s[m] = state_ld(S_head + (size_t)(rg + G::kRowGroups * m) * kD + col);
 
     for (int t = 0; t < T; ++t) {
         const size_t row = ((size_t)b * T + t) * heads + h;  // (b, t, h)
@@ -140,11 +171,11 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const float* __restrict_
         if (t < n_snap) {
             float* snap = snaps + ((size_t)t * batch * heads + bh) * kD * kD;
 #pragma unroll
-            for (int m = 0; m < G::kRows; ++m) st4(snap + (size_t)(rg + G::kRowGroups * m) * kD + col, s[m]);
+            for (int m = 0; m < G::kRows; ++m) state_st(snap + (size_t)(rg + G::kRowGroups * m) * kD + col, s[m]);
         }
     }
 #pragma unroll
-    for (int m = 0; m < G::kRows; ++m) st4(S_head + (size_t)(rg + G::kRowGroups * m) * kD + col, s[m]);
+    for (int m = 0; m < G::kRows; ++m) state_st(S_head + (size_t)(rg + G::kRowGroups * m) * kD + col, s[m]);
 }
 
 int launch_recurrent(const float* q, const float* k, const float* v, const float* gate, const float* beta,
