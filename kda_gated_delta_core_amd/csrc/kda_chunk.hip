@@ -5,17 +5,19 @@
 //
 //  chunk_prepare  one workgroup per (sequence, head, chunk), all chunks in
 //                 parallel.  Builds the chunk's WY/UT factors in LDS with FP32
-//                 MFMA and writes one workspace record:
-//                   W = T diag(beta)(e^G o K), U = T diag(beta) V,
-//                   Qhat = e^G o Q, Ktil^T = (e^{G_last - G} o K)^T,
-//                   M (lower-triangular decayed Q K^T), gamma = e^{G_last},
-//                 with G the per-channel cumulative log-decay inside the chunk,
-//                 A the strictly lower decayed K K^T scaled by beta and
-//                 T = (I + A)^-1.
+//                 MFMA: G the per-channel cumulative log-decay inside the chunk,
+//                 A the strictly lower decayed K K^T scaled by beta, T = (I + A)^-1,
+//                 M the lower-triangular decayed Q K^T,
+//                   W = T diag(beta)(e^G o K),  U = T diag(beta) V,
+//                 and writes one workspace record with W, U,
+//                   P = e^G o Q - M W,  R = M U,
+//                   Ktil^T = (e^{G_last - G} o K)^T,  gamma = e^{G_last}.
+//                 (O = (e^G o Q) S + M (U - W S) = P S + R, so the output no
+//                 longer waits for Delta inside the scan.)
 //  chunk_scan     one workgroup per (sequence, head, 16-column value slice),
-//                 serial over chunks, its 128x16 state slice resident in
-//                 registers.  Per chunk:
-//                   Delta = U - W S,  O = Qhat S + M Delta,
+//                 serial over chunks, its 128x16 state slice resident on chip.
+//                 Per chunk:
+//                   Delta = U - W S,  O = P S + R,
 //                   S <- diag(gamma) S + Ktil^T Delta
 //                 all as 16x16x4 FP32 MFMA tiles.  Value columns never mix, so
 //                 the eight slices of a head run independently; they are
@@ -43,12 +45,12 @@ struct ChunkGeom {
     static constexpr int kTiles = C / 16;      // 16-row tiles per chunk
     static constexpr int kLd = kD + 4;         // LDS row stride of [C][128] tables (floats)
     static constexpr int kLdc = C + 4;         // LDS row stride of [C][C] tables
-    static constexpr size_t kOffW = 0;
-    static constexpr size_t kOffU = (size_t)C * kD;
-    static constexpr size_t kOffQ = 2 * (size_t)C * kD;
-    static constexpr size_t kOffKt = 3 * (size_t)C * kD;
-    static constexpr size_t kOffM = 4 * (size_t)C * kD;
-    static constexpr size_t kOffGam = kOffM + (size_t)C * C;
+    static constexpr size_t kOffW = 0;                      // W     A tiles [C/16][8]
+    static constexpr size_t kOffU = (size_t)C * kD;         // U     accumulator tiles [C/16][8]
+    static constexpr size_t kOffP = 2 * (size_t)C * kD;     // P     A tiles [C/16][8]
+    static constexpr size_t kOffR = 3 * (size_t)C * kD;     // R     accumulator tiles [C/16][8]
+    static constexpr size_t kOffKt = 4 * (size_t)C * kD;    // Ktil^T A tiles [8][C/16]
+    static constexpr size_t kOffGam = 5 * (size_t)C * kD;   // gamma [128]
     static constexpr size_t kRecord = kOffGam + kD;
     static constexpr int kPairs = kTiles * (kTiles + 1) / 2;
     static_assert(kRecord == chunk_record_floats(C), "record layout");
@@ -97,6 +99,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
     __shared__ float sL[C * LD];     // block-local cumulative log2 decay
     __shared__ float sA[C * LDC];    // beta-scaled strictly lower A
     __shared__ float sT[C * LDC];    // (I + A)^-1
+    __shared__ float sM[C * LDC];    // lower-triangular decayed Q K^T
     __shared__ float sBlk[NT * kD];  // log2 decay of each whole 16-row block
     __shared__ float sPre[NT * kD];  // sum of the block totals before block R
     __shared__ float sSuf[NT * kD];  // sum of the block totals after block R
@@ -225,19 +228,11 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * R + 4 * q4 + e, s = 16 * S + l16;
             sA[r * LDC + s] = (S < R || s < r) ? sBeta[r] * accA[e] : 0.f;
-            rec[G::kOffM + atile_index(R * NT + S, r & 15, s & 15)] = (S < R || s <= r) ? accM[e] : 0.f;
+            sM[r * LDC + s] = (S < R || s <= r) ? accM[e] : 0.f;
         }
     }
-    // 3b. Qhat = e^G o Q and Ktil^T = (e^{G_last - G} o K)^T straight to the record
-    //     in A-operand tile order (consecutive threads write consecutive floats),
-    //     the upper blocks of M as zero tiles
-#pragma unroll 4
-    for (int e = tid; e < C * kD; e += kPrepThreads) {
-        int row, col;
-        atile_coords(e, 8, row, col);            // Qhat tile (row block, column block)
-        const int R = row >> 4;
-        rec[G::kOffQ + e] = sQ[row * LD + col] * exp2_fast(sPre[R * kD + col] + sL[row * LD + col]);
-    }
+    // 3b. Ktil^T = (e^{G_last - G} o K)^T straight to the record in A-operand
+    //     tile order (consecutive threads write consecutive floats)
 #pragma unroll 4
     for (int e = tid; e < C * kD; e += kPrepThreads) {
         int i, r;
@@ -246,21 +241,21 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         rec[G::kOffKt + e] =
             sK[r * LD + i] * exp2_fast(sSuf[R * kD + i] + (sBlk[R * kD + i] - sL[r * LD + i]));
     }
-    for (int e = tid; e < C * C; e += kPrepThreads) {
-        const int tile = e >> 8;
-        if (tile % NT > tile / NT) rec[G::kOffM + e] = 0.f;
-    }
     // 3c. right-hand sides of W and U in the B-operand layout of this wave's
     //     column block: beta e^G o K and beta V at rows 16 y + 4 q4 + e
-    float bw[NT][4], bu[NT][4];
+    //     (and e^G o Q at the same positions: the accumulator layout of this
+    //     wave's output tiles)
+    float bw[NT][4], bu[NT][4], qh[NT][4];
 #pragma unroll
     for (int y = 0; y < NT; ++y)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int s = 16 * y + 4 * q4 + e, i = 16 * wave + l16;
             const float bb = sBeta[s];
-            bw[y][e] = bb * (exp2_fast(sPre[y * kD + i] + sL[s * LD + i]) * sK[s * LD + i]);
+            const float gam = exp2_fast(sPre[y * kD + i] + sL[s * LD + i]);
+            bw[y][e] = bb * (gam * sK[s * LD + i]);
             bu[y][e] = bb * vb[y][e];
+            qh[y][e] = gam * sQ[s * LD + i];
         }
     __syncthreads();
 
@@ -302,7 +297,9 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         __syncthreads();
     }
 
-    // 5. W = T (beta e^G o K) and U = T (beta V): this wave's 16-column block, all row tiles
+    // 5. W = T (beta e^G o K) and U = T (beta V): this wave's 16-column block, all
+    //    row tiles; the accumulator tiles stay in registers for step 6
+    floatx4 wt[NT], ut[NT];
 #pragma unroll
     for (int X = 0; X < NT; ++X) {
         floatx4 accW = {0.f, 0.f, 0.f, 0.f}, accU = {0.f, 0.f, 0.f, 0.f};
@@ -315,26 +312,47 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
                 accU = mfma4(comp(t4, e), bu[y][e], accU);
             }
         }
+        wt[X] = accW;
+        ut[X] = accU;
 #pragma unroll
         for (int e = 0; e < 4; ++e) rec[G::kOffW + atile_index(X * 8 + wave, 4 * q4 + e, l16)] = accW[e];
         // U in the scan's accumulator layout: [row tile][16-column block][lane][4]
         st4(rec + G::kOffU + ((size_t)(X * 8 + wave) * 64 + lane) * 4,
             make_float4(accU[0], accU[1], accU[2], accU[3]));
     }
+    // 6. P = e^G o Q - M W and R = M U.  The W and U accumulator tiles are, lane
+    //    for lane, the B operands of the products over the chunk rows.
+#pragma unroll
+    for (int X = 0; X < NT; ++X) {
+        floatx4 mw = {0.f, 0.f, 0.f, 0.f}, mu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int y = 0; y <= X; ++y) {
+            const float4 m4 = lds4(&sM[(16 * X + l16) * LDC + 16 * y + 4 * q4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                mw = mfma4(comp(m4, e), wt[y][e], mw);
+                mu = mfma4(comp(m4, e), ut[y][e], mu);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            rec[G::kOffP + atile_index(X * 8 + wave, 4 * q4 + e, l16)] = qh[X][e] - mw[e];
+        st4(rec + G::kOffR + ((size_t)(X * 8 + wave) * 64 + lane) * 4, make_float4(mu[0], mu[1], mu[2], mu[3]));
+    }
 }
 
 constexpr int kScanThreads = 512;  // 8 waves, two per SIMD
 
-// Operands one wave of the scan reads from a chunk record, prefetched a chunk
-// ahead into registers.  Wave roles inside a chunk (NT = C / 16 row tiles):
-//   wave < NT           Delta tile xd = wave:   Delta = U - W S
-//   NT <= wave < 2 NT   output tile xp = wave - NT:  O = Qhat S + M Delta
-//   every wave          state tile `wave`:      S <- diag(gamma) S + Ktil^T Delta
+// Operands one wave of the scan reads from a chunk record, prefetched two
+// chunks ahead into registers.  Wave roles inside a chunk (NT = C / 16 row tiles):
+//   wave < NT           Delta tile xd = wave:          Delta = U - W S
+//   NT <= wave < 2 NT   output tile xp = wave - NT:    O = P S + R
+//   every wave          state tile `wave`:             S <- diag(gamma) S + Ktil^T Delta
 template <int C>
 struct ScanOps {
     static constexpr int NT = C / 16;
-    float4 a[8];     // W rows of the Delta tile, or Qhat rows of the output tile
-    float4 x[NT];    // Delta waves: U tile (every x[y] holds it); output waves: M rows (upper blocks zero)
+    float4 a[8];     // W rows of the Delta tile, or P rows of the output tile
+    float4 x;        // U tile (Delta waves) or R tile (output waves), accumulator layout
     float4 kt[NT];   // Ktil^T rows of this wave's state tile
     float4 g;        // gamma at those rows
 };
@@ -343,18 +361,15 @@ struct ScanOps {
 // role), so the wait counts the compiler derives stay exact across the loop.
 template <int C>
 __device__ __forceinline__ void scan_load(ScanOps<C>& o, const float* rec, bool is_d, int xd, bool is_p, int xp,
-                                          int wave, int lane, int l16, int q4, int slice)
+                                          int wave, int lane, int q4, int slice)
 {
     using G = ChunkGeom<C>;
     constexpr int NT = C / 16;
     const int xa = is_d ? xd : (is_p ? xp : 0);
-    const float* ar = rec + (is_d ? G::kOffW : G::kOffQ) + ((size_t)xa * 8 * 64 + lane) * 4;
+    const float* ar = rec + (is_d ? G::kOffW : G::kOffP) + ((size_t)xa * 8 * 64 + lane) * 4;
 #pragma unroll
     for (int tau = 0; tau < 8; ++tau) o.a[tau] = ld4(ar + tau * 256);
-    const float* ur = rec + G::kOffU + ((size_t)((is_d ? xd : 0) * 8 + slice) * 64 + lane) * 4;
-    const float* mr = rec + G::kOffM + ((size_t)(is_p ? xp : 0) * NT * 64 + lane) * 4;
-#pragma unroll
-    for (int y = 0; y < NT; ++y) o.x[y] = ld4(is_d ? ur : mr + y * 256);
+    o.x = ld4(rec + (is_d ? G::kOffU : G::kOffR) + ((size_t)(xa * 8 + slice) * 64 + lane) * 4);
     const float* kr = rec + G::kOffKt + ((size_t)wave * NT * 64 + lane) * 4;
 #pragma unroll
     for (int y = 0; y < NT; ++y) o.kt[y] = ld4(kr + y * 256);
@@ -362,8 +377,8 @@ __device__ __forceinline__ void scan_load(ScanOps<C>& o, const float* rec, bool 
 }
 
 // One chunk of the scan for one wave.  The state lives in LDS only, in two
-// buffers: sS[cur] holds the chunk's incoming state, sS[cur ^ 1] receives the
-// outgoing one.  Tile s, element e of lane l is S[16 s + 4 (l / 16) + e][v0 + l % 16],
+// buffers: sIn holds the chunk's incoming state, sOut receives the outgoing
+// one.  Tile s, element e of lane l is S[16 s + 4 (l / 16) + e][v0 + l % 16],
 // which is directly the B operand of the 16x16x4 MFMA over the key index.
 template <int C>
 __device__ __forceinline__ void scan_chunk(const ScanOps<C>& cur, floatx4 (*sIn)[64], floatx4 (*sOut)[64],
@@ -372,33 +387,45 @@ __device__ __forceinline__ void scan_chunk(const ScanOps<C>& cur, floatx4 (*sIn)
                                            int b, int h, int heads, int T, int t_pad)
 {
     constexpr int NT = C / 16;
-    // A. W S (Delta waves) or Qhat S (output waves) against the chunk's incoming state
-    floatx4 P = {0.f, 0.f, 0.f, 0.f};
+    // A. Delta = U - W S (Delta waves) and O = R + P S (output waves)
     if (is_d || is_p) {
+        floatx4 st[8];
+#pragma unroll
+        for (int tau = 0; tau < 8; ++tau) st[tau] = sIn[tau][lane];
+        floatx4 acc;
+        acc[0] = is_p ? cur.x.x : 0.f;
+        acc[1] = is_p ? cur.x.y : 0.f;
+        acc[2] = is_p ? cur.x.z : 0.f;
+        acc[3] = is_p ? cur.x.w : 0.f;
 #pragma unroll
         for (int tau = 0; tau < 8; ++tau) {
-            const floatx4 st = sIn[tau][lane];
-            P = mfma4(cur.a[tau].x, st[0], P);
-            P = mfma4(cur.a[tau].y, st[1], P);
-            P = mfma4(cur.a[tau].z, st[2], P);
-            P = mfma4(cur.a[tau].w, st[3], P);
+            acc = mfma4(cur.a[tau].x, st[tau][0], acc);
+            acc = mfma4(cur.a[tau].y, st[tau][1], acc);
+            acc = mfma4(cur.a[tau].z, st[tau][2], acc);
+            acc = mfma4(cur.a[tau].w, st[tau][3], acc);
         }
         if (is_d) {
             floatx4 d;
-            d[0] = cur.x[0].x - P[0];
-            d[1] = cur.x[0].y - P[1];
-            d[2] = cur.x[0].z - P[2];
-            d[3] = cur.x[0].w - P[3];
+            d[0] = cur.x.x - acc[0];
+            d[1] = cur.x.y - acc[1];
+            d[2] = cur.x.z - acc[2];
+            d[3] = cur.x.w - acc[3];
             sDelta[xd][lane] = d;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = c * C + 16 * xp + 4 * q4 + e;
+                if (t < T) out[(((size_t)b * t_pad + t) * heads + h) * kD + v0 + l16] = acc[e];
+            }
         }
     }
     __syncthreads();
-    floatx4 dl[NT];
-#pragma unroll
-    for (int y = 0; y < NT; ++y) dl[y] = sDelta[y][lane];
 
-    // B1. state tile `wave`
+    // B. state tile `wave`
     {
+        floatx4 dl[NT];
+#pragma unroll
+        for (int y = 0; y < NT; ++y) dl[y] = sDelta[y][lane];
         const floatx4 so = sIn[wave][lane];
         floatx4 acc;
         acc[0] = cur.g.x * so[0];
@@ -413,22 +440,6 @@ __device__ __forceinline__ void scan_chunk(const ScanOps<C>& cur, floatx4 (*sIn)
             acc = mfma4(cur.kt[y].w, dl[y][3], acc);
         }
         sOut[wave][lane] = acc;
-    }
-    // B2. output tile: O = Qhat S + M Delta over the blocks y <= xp
-    if (is_p) {
-#pragma unroll
-        for (int y = 0; y < NT; ++y) {
-            if (y > xp) continue;
-            P = mfma4(cur.x[y].x, dl[y][0], P);
-            P = mfma4(cur.x[y].y, dl[y][1], P);
-            P = mfma4(cur.x[y].z, dl[y][2], P);
-            P = mfma4(cur.x[y].w, dl[y][3], P);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = c * C + 16 * xp + 4 * q4 + e;
-            if (t < T) out[(((size_t)b * t_pad + t) * heads + h) * kD + v0 + l16] = P[e];
-        }
     }
     __syncthreads();
 }
@@ -464,22 +475,26 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(const float* _
         sS[0][wave][lane] = st;
     }
     const float* const rec0 = ws + (size_t)bh * nchunks * G::kRecord;
-    // Two operand buffers in ping-pong: while one chunk is computed from one
-    // buffer, the loads of the next chunk land in the other (no register
-    // copies, so no wait on the prefetch before it is needed).
-    ScanOps<C> opA, opB;
-    scan_load<C>(opA, rec0, is_d, xd, is_p, xp, wave, lane, l16, q4, slice);
+    auto rec = [&](int cc) { return rec0 + (size_t)(cc < nchunks ? cc : nchunks - 1) * G::kRecord; };
+    // Three operand buffers in rotation: while one chunk is computed, the loads
+    // of the next two are in flight (no register copies between the buffers,
+    // so no wait on a prefetch before it is needed).
+    ScanOps<C> op0, op1, op2;
+    scan_load<C>(op0, rec(0), is_d, xd, is_p, xp, wave, lane, q4, slice);
+    scan_load<C>(op1, rec(1), is_d, xd, is_p, xp, wave, lane, q4, slice);
     __syncthreads();
-    for (int c = 0; c < nchunks; c += 2) {
-        const int c1 = c + 1 < nchunks ? c + 1 : c;
-        scan_load<C>(opB, rec0 + (size_t)c1 * G::kRecord, is_d, xd, is_p, xp, wave, lane, l16, q4, slice);
-        scan_chunk<C>(opA, sS[0], sS[1], sDelta, out, c, is_d, xd, is_p, xp, wave, lane, q4, v0, l16, b, h, heads,
-                      T, t_pad);
+    for (int c = 0; c < nchunks; c += 3) {
+        scan_load<C>(op2, rec(c + 2), is_d, xd, is_p, xp, wave, lane, q4, slice);
+        scan_chunk<C>(op0, sS[c & 1], sS[(c + 1) & 1], sDelta, out, c, is_d, xd, is_p, xp, wave, lane, q4, v0, l16,
+                      b, h, heads, T, t_pad);
         if (c + 1 >= nchunks) break;
-        const int c2 = c + 2 < nchunks ? c + 2 : c + 1;
-        scan_load<C>(opA, rec0 + (size_t)c2 * G::kRecord, is_d, xd, is_p, xp, wave, lane, l16, q4, slice);
-        scan_chunk<C>(opB, sS[1], sS[0], sDelta, out, c + 1, is_d, xd, is_p, xp, wave, lane, q4, v0, l16, b, h,
-                      heads, T, t_pad);
+        scan_load<C>(op0, rec(c + 3), is_d, xd, is_p, xp, wave, lane, q4, slice);
+        scan_chunk<C>(op1, sS[(c + 1) & 1], sS[c & 1], sDelta, out, c + 1, is_d, xd, is_p, xp, wave, lane, q4, v0,
+                      l16, b, h, heads, T, t_pad);
+        if (c + 2 >= nchunks) break;
+        scan_load<C>(op1, rec(c + 4), is_d, xd, is_p, xp, wave, lane, q4, slice);
+        scan_chunk<C>(op2, sS[c & 1], sS[(c + 1) & 1], sDelta, out, c + 2, is_d, xd, is_p, xp, wave, lane, q4, v0,
+                      l16, b, h, heads, T, t_pad);
     }
     // the final state is in sS[nchunks & 1]
     const floatx4 st = sS[nchunks & 1][wave][lane];

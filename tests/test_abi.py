@@ -49,7 +49,7 @@ def test_status_strings(lib):
 def test_workspace_bytes():
     for B, H, T, C in [(1, 2, 64, 16), (1, 32, 8192, 64), (4, 32, 32768, 64), (3, 5, 100, 32), (2, 1, 1, 16)]:
         n = -(-T // C)
-        rec = 4 * C * 128 + C * C + 128
+        rec = 5 * C * 128 + 128
         assert kda.kda_chunk_prefill_workspace_bytes(B, H, T, C) == B * H * n * rec * 4
     for bad in [(0, 1, 1, 16), (1, 0, 1, 16), (1, 1, 0, 16), (1, 1, 1, 8), (1, 1, 1, 128), (-1, 1, 1, 64)]:
         assert kda.kda_chunk_prefill_workspace_bytes(*bad) == 0

@@ -31,6 +31,13 @@ def _unswizzle_a(buf, n_row_tiles, n_col_tiles):
     return t.transpose(0, 3, 1, 2, 4).reshape(16 * n_row_tiles, 16 * n_col_tiles)
 
 
+def _unswizzle_acc(buf, n_row_tiles):
+    """Matrix [16 n_row_tiles][128] from accumulator tiles [X][j][lane][e]: row 16X + 4 (l // 16) + e,
+    column 16j + l % 16."""
+    t = buf.reshape(n_row_tiles, 8, 4, 16, 4)                  # X, j, l//16, l%16, e
+    return t.transpose(0, 2, 4, 1, 3).reshape(16 * n_row_tiles, 128)
+
+
 def _check_against_oracle(x, T, out, st, tag=""):
     o_ref, s_ref, _, _ = oracle.serial(x["q"], x["k"], x["v"], x["gate"], x["beta"], x["state"], T=T)
     o = host(out)
@@ -87,29 +94,29 @@ def test_prefill_workspace_stages(device):
     announce(f"kda_chunk_prefill stages T={T} C={C}")
     x = ki.make_batch(4001, 1, H, T, -5.0, 0.02, alloc_rows=192, pad_value=np.nan)
     _, _, ws = _prefill(kda, x, T, C)
-    rec_f = 4 * C * 128 + C * C + 128
+    rec_f = 5 * C * 128 + 128
     ws = host(ws).view(np.float32).reshape(H, -1, rec_f)
     for h, c in [(0, 0), (1, 1), (1, 2)]:
         n = min(C, T - c * C)
         stg = oracle.chunk_stages(x["q"], x["k"], x["v"], x["gate"], x["beta"], np.zeros((128, 128)), 0, h,
                                   c * C, n)
         rec = ws[h, c]
-        W = _unswizzle_a(rec[:C * 128], C // 16, 8)
-        Qh = _unswizzle_a(rec[2 * C * 128:3 * C * 128], C // 16, 8)
-        # U is stored in 16x16 accumulator tiles: [row tile X][column block j][lane][e]
-        Usw = rec[C * 128:2 * C * 128].reshape(C // 16, 8, 4, 16, 4)   # X, j, lane//16, lane%16, e
-        U = Usw.transpose(0, 2, 4, 1, 3).reshape(C, 128)               # row 16X+4(l//16)+e, col 16j+l%16
-        KtT = _unswizzle_a(rec[3 * C * 128:4 * C * 128], 8, C // 16)
-        M = _unswizzle_a(rec[4 * C * 128:4 * C * 128 + C * C], C // 16, C // 16)
-        gam = rec[4 * C * 128 + C * C:]
+        blk = lambda i: rec[i * C * 128:(i + 1) * C * 128]
+        W = _unswizzle_a(blk(0), C // 16, 8)
+        U = _unswizzle_acc(blk(1), C // 16)
+        P = _unswizzle_a(blk(2), C // 16, 8)
+        R = _unswizzle_acc(blk(3), C // 16)
+        KtT = _unswizzle_a(blk(4), 8, C // 16)
+        gam = rec[5 * C * 128:]
         G = stg["G"]
         q = x["q"][0, c * C:c * C + n, h].astype(np.float64)
         k = x["k"][0, c * C:c * C + n, h].astype(np.float64)
         tag = f"h{h}c{c} "
         assert_close(tag + "W", W[:n], stg["W"])
         assert_close(tag + "U", U[:n], stg["U"])
-        assert_close(tag + "M", M[:n, :n], stg["M"])
-        assert_close(tag + "Qhat", Qh[:n], np.exp(G) * q)
+        # the record holds P = e^G o Q - M W and R = M U (O = P S + R)
+        assert_close(tag + "P", P[:n], np.exp(G) * q - stg["M"] @ stg["W"])
+        assert_close(tag + "R", R[:n], stg["M"] @ stg["U"])
         assert_close(tag + "Ktil^T", KtT[:, :n], (np.exp(G[-1] - G) * k).T)
         # gamma = e^{G_last} is far below the fp32 range for most channels at these gates:
         # compare where the reference is representable, require exact zeros elsewhere
@@ -118,8 +125,7 @@ def test_prefill_workspace_stages(device):
         assert np.all(np.abs(gam[~big]) < 1e-30)
         if big.any():
             assert_close(tag + "gamma", gam[big], g_ref[big])
-        for name, a in (("W", W[n:]), ("U", U[n:]), ("Qhat", Qh[n:]), ("Kt", KtT[:, n:]), ("M", M[n:]),
-                        ("M", M[:, n:])):
+        for name, a in (("W", W[n:]), ("U", U[n:]), ("P", P[n:]), ("R", R[n:]), ("Kt", KtT[:, n:])):
             assert np.all(a == 0), f"{tag}{name} pad rows not zero"
 
 
