@@ -83,261 +83,384 @@ __device__ __forceinline__ void atile_coords(int e, int n_cols, int& row, int& c
 
 constexpr int kPrepThreads = 512;  // 8 waves: one per 16-column block in the W/U stage
 
+// Inputs of one chunk as one thread of chunk_prepare loads them.
+template <int C>
+struct PrepInputs {
+    static constexpr int NV4 = C * 32 / kPrepThreads;
+    float4 k[NV4], q[NV4], g[NV4];  // row-major [C][128] pieces
+    float beta;
+};
+
+// Issue every global read of chunk `gc` (global index b * nchunks * heads-major).
+// The reads stay inside the T_pad rows of the chunk; pad rows are masked later.
+template <int C>
+__device__ __forceinline__ void prep_load(PrepInputs<C>& in, const float* __restrict__ q,
+                                          const float* __restrict__ k, const float* __restrict__ gate,
+                                          const float* __restrict__ beta, size_t row0, int heads, int tid)
+{
+    constexpr int NV4 = PrepInputs<C>::NV4;
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+        const int e = tid + kPrepThreads * i, r = e >> 5, c4 = (e & 31) * 4;
+        const size_t off = (row0 + (size_t)r * heads) * kD + c4;
+        in.k[i] = ld4(k + off);
+        in.q[i] = ld4(q + off);
+        in.g[i] = ld4(gate + off);
+    }
+    in.beta = tid < C ? beta[row0 + (size_t)tid * heads] : 0.f;
+}
+
+// V of one chunk in the B-operand layout of this wave's U tiles (rows
+// 16 y + 4 q4 + e, column 16 wave + l16).  Rows >= T are selected away where
+// the values are used, so that nothing here waits for the loads.
+template <int C>
+__device__ __forceinline__ void prep_load_v(float (&vb)[C / 16][4], const float* __restrict__ v, size_t row0,
+                                            int heads, int wave, int l16, int q4)
+{
+#pragma unroll
+    for (int y = 0; y < C / 16; ++y)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            vb[y][e] = v[(row0 + (size_t)(16 * y + 4 * q4 + e) * heads) * kD + 16 * wave + l16];
+}
+
+// Rows >= T (nvalid and beyond) are replaced by zeros with selects, then the
+// chunk goes to LDS (gate in log2 units).
+template <int C>
+__device__ __forceinline__ void prep_stage(const PrepInputs<C>& in, float* sK, float* sQ, float* sL, float* sBeta,
+                                           int nvalid, int tid)
+{
+    using G = ChunkGeom<C>;
+    constexpr int NV4 = PrepInputs<C>::NV4, LD = G::kLd;
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+        const int e = tid + kPrepThreads * i, r = e >> 5, c4 = (e & 31) * 4;
+        const bool ok = r < nvalid;
+        lds4_st(&sK[r * LD + c4], ok ? in.k[i] : z4);
+        lds4_st(&sQ[r * LD + c4], ok ? in.q[i] : z4);
+        const float4 g = ok ? in.g[i] : z4;
+        lds4_st(&sL[r * LD + c4], make_float4(g.x * kLog2e, g.y * kLog2e, g.z * kLog2e, g.w * kLog2e));
+    }
+    if (tid < C) sBeta[tid] = tid < nvalid ? in.beta : 0.f;
+}
+
+// Partial A and M tile of block pair (R, S <= R) over the channel steps
+// [16 TAU0, 16 TAU1): lane l accumulates rows 16R + 4(l/16) + e, columns 16S + l%16.
+template <int C, int TAU0, int TAU1>
+__device__ __forceinline__ void am_pair(int R, int S, const float* sK, const float* sQ, const float* sL,
+                                        const float* sPre, const float* sBlk, int l16, int q4, floatx4& accA,
+                                        floatx4& accM)
+{
+    constexpr int LD = ChunkGeom<C>::kLd;
+    const int ra = 16 * R + l16, sb = 16 * S + l16;
+#pragma unroll
+    for (int tau = TAU0; tau < TAU1; ++tau) {
+        const int i0 = 16 * tau + 4 * q4;
+        const float4 kr = lds4(&sK[ra * LD + i0]);
+        const float4 qr = lds4(&sQ[ra * LD + i0]);
+        const float4 lr = lds4(&sL[ra * LD + i0]);
+        const float4 ks = lds4(&sK[sb * LD + i0]);
+        const float4 ls = lds4(&sL[sb * LD + i0]);
+        float4 er, es;  // log2 exponents of the row and column factors
+        if (S < R) {
+            // reference: last row of block S.  Row factor 2^(L_r + blocks S+1..R-1),
+            // column factor 2^(B_S - L_s); both <= 1 for gates <= 0
+            const float4 pr = lds4(&sPre[R * kD + i0]);
+            const float4 ps = lds4(&sPre[(S + 1) * kD + i0]);
+            const float4 bs = lds4(&sBlk[S * kD + i0]);
+            er = make_float4(lr.x + (pr.x - ps.x), lr.y + (pr.y - ps.y), lr.z + (pr.z - ps.z), lr.w + (pr.w - ps.w));
+            es = make_float4(bs.x - ls.x, bs.y - ls.y, bs.z - ls.z, bs.w - ls.w);
+        } else {
+            // reference: row 7 of the block; each factor spans at most 8 gates
+            const float4 lm = lds4(&sL[(16 * R + 7) * LD + i0]);
+            er = make_float4(lr.x - lm.x, lr.y - lm.y, lr.z - lm.z, lr.w - lm.w);
+            es = make_float4(lm.x - ls.x, lm.y - ls.y, lm.z - ls.z, lm.w - ls.w);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float xr = exp2_fast(comp(er, e));
+            const float yc = comp(ks, e) * exp2_fast(comp(es, e));
+            accA = mfma4(comp(kr, e) * xr, yc, accA);
+            accM = mfma4(comp(qr, e) * xr, yc, accM);
+        }
+    }
+}
+
+// beta row scaling and the triangular masks, then A and M tiles to LDS
+template <int C>
+__device__ __forceinline__ void am_store(int R, int S, const floatx4& accA, const floatx4& accM, float* sA,
+                                         float* sM, const float* sBeta, int l16, int q4)
+{
+    constexpr int LDC = ChunkGeom<C>::kLdc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int r = 16 * R + 4 * q4 + e, s = 16 * S + l16;
+        sA[r * LDC + s] = (S < R || s < r) ? sBeta[r] * accA[e] : 0.f;
+        sM[r * LDC + s] = (S < R || s <= r) ? accM[e] : 0.f;
+    }
+}
+
+__device__ __forceinline__ void pair_of(int p, int& R, int& S)
+{
+    R = 0;
+    while ((R + 1) * (R + 2) / 2 <= p) ++R;
+    S = p - R * (R + 1) / 2;
+}
+
+// Persistent: one workgroup per CU walks the chunks gc = blockIdx.x, +gridDim.x, ...
+// (gc = (b * heads + h) * nchunks + c).  The inputs of the next chunk are in
+// flight into registers during the whole of the current one and are staged into
+// LDS at its end.
 template <int C>
 __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ gate, const float* __restrict__ beta, float* __restrict__ ws, int heads, int T,
-    int t_pad, int nchunks)
+    int t_pad, int nchunks, int n_total)
 {
     using G = ChunkGeom<C>;
     constexpr int NT = G::kTiles, LD = G::kLd, LDC = G::kLdc;
     constexpr int NW = kPrepThreads / 64;
-    constexpr int NV4 = C * 32 / kPrepThreads;  // float4 per thread per [C][128] input
-    static_assert(NV4 >= 1 && NW == 8, "geometry");
+    constexpr int kSplit = G::kPairs > NW ? G::kPairs - NW : 0;  // pairs computed in two channel halves
+    static_assert(PrepInputs<C>::NV4 >= 1 && NW == 8 && kSplit <= 2, "geometry");
     __shared__ float sK[C * LD];
     __shared__ float sQ[C * LD];
     __shared__ float sL[C * LD];     // block-local cumulative log2 decay
     __shared__ float sA[C * LDC];    // beta-scaled strictly lower A
-    __shared__ float sT[C * LDC];    // (I + A)^-1
+    __shared__ float sT[C * LDC];    // (I + A)^-1; before that, partial tiles of the split pairs
     __shared__ float sM[C * LDC];    // lower-triangular decayed Q K^T
     __shared__ float sBlk[NT * kD];  // log2 decay of each whole 16-row block
     __shared__ float sPre[NT * kD];  // sum of the block totals before block R
     __shared__ float sSuf[NT * kD];  // sum of the block totals after block R
     __shared__ float sBeta[C];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l16 = lane & 15, q4 = lane >> 4;
-    const int c = blockIdx.x % nchunks;
-    const int bh = blockIdx.x / nchunks;
-    const int b = bh / heads, h = bh % heads;
-    const int t0 = c * C;
-    float* const rec = ws + (size_t)blockIdx.x * G::kRecord;
-    const size_t row0 = ((size_t)b * t_pad + t0) * heads + h;  // (b, t0, h)
-    const int nvalid = T - t0 < C ? T - t0 : C;                // rows of this chunk below T
-    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int stride = gridDim.x;
+    floatx4* const sPart = reinterpret_cast<floatx4*>(sT);  // [kSplit][2][64]
 
-    // 1. every global read of the kernel is issued here; rows >= T are then
-    //    replaced by zeros with selects (the reads stay inside T_pad rows)
-    float4 kk[NV4], qq[NV4], gg[NV4];
-#pragma unroll
-    for (int i = 0; i < NV4; ++i) {
-        const int e = tid + kPrepThreads * i, r = e >> 5, c4 = (e & 31) * 4;
-        const size_t off = (row0 + (size_t)r * heads) * kD + c4;
-        kk[i] = ld4(k + off);
-        qq[i] = ld4(q + off);
-        gg[i] = ld4(gate + off);
-    }
-    // V in the B-operand layout of the U tiles: rows 16 y + 4 q4 + e, column 16 wave + l16
-    float vb[NT][4];
-#pragma unroll
-    for (int y = 0; y < NT; ++y)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            vb[y][e] = v[(row0 + (size_t)(16 * y + 4 * q4 + e) * heads) * kD + 16 * wave + l16];
-    const float braw = tid < C ? beta[row0 + (size_t)tid * heads] : 0.f;
-#pragma unroll
-    for (int i = 0; i < NV4; ++i) {
-        const int e = tid + kPrepThreads * i, r = e >> 5, c4 = (e & 31) * 4;
-        const bool ok = r < nvalid;
-        lds4_st(&sK[r * LD + c4], ok ? kk[i] : z4);
-        lds4_st(&sQ[r * LD + c4], ok ? qq[i] : z4);
-        const float4 g = ok ? gg[i] : z4;
-        lds4_st(&sL[r * LD + c4], make_float4(g.x * kLog2e, g.y * kLog2e, g.z * kLog2e, g.w * kLog2e));
-    }
-#pragma unroll
-    for (int y = 0; y < NT; ++y)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vb[y][e] = 16 * y + 4 * q4 + e < nvalid ? vb[y][e] : 0.f;
-    if (tid < C) sBeta[tid] = tid < nvalid ? braw : 0.f;
-    __syncthreads();
+    auto row0_of = [&](int gc) {
+        const int bh = gc / nchunks, c = gc % nchunks;
+        return ((size_t)(bh / heads) * t_pad + (size_t)c * C) * heads + (bh % heads);
+    };
+    auto nvalid_of = [&](int gc) {
+        const int t0 = (gc % nchunks) * C;
+        return T - t0 < C ? T - t0 : C;
+    };
 
-    // 2. cumulative sums inside each 16-row block, then per-column block prefixes
-    if (tid < NT * kD) {
-        const int j = tid & (kD - 1), R = tid >> 7;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = sL[(16 * R + r) * LD + j];
-        float acc = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            acc += x[r];
-            sL[(16 * R + r) * LD + j] = acc;
-        }
-        sBlk[R * kD + j] = acc;
+    int gc = blockIdx.x;
+    PrepInputs<C> in;
+    if (gc < n_total) {
+        prep_load<C>(in, q, k, gate, beta, row0_of(gc), heads, threadIdx.x);
+        prep_stage<C>(in, sK, sQ, sL, sBeta, nvalid_of(gc), threadIdx.x);
     }
     __syncthreads();
-    if (tid < kD) {
-        float bl[NT];
-#pragma unroll
-        for (int R = 0; R < NT; ++R) bl[R] = sBlk[R * kD + tid];
-        float pre = 0.f, suf = 0.f;
-#pragma unroll
-        for (int R = 0; R < NT; ++R) {
-            sPre[R * kD + tid] = pre;
-            pre += bl[R];
-        }
-#pragma unroll
-        for (int R = NT - 1; R >= 0; --R) {
-            sSuf[R * kD + tid] = suf;
-            suf += bl[R];
-        }
-        rec[G::kOffGam + tid] = exp2_fast(pre);  // gamma = e^{G_last}
-    }
-    __syncthreads();
+    if (gc + stride < n_total) prep_load<C>(in, q, k, gate, beta, row0_of(gc + stride), heads, threadIdx.x);
 
-    // 3a. A and M, one 16x16 block pair (R, S <= R) per wave at a time
-    for (int p = wave; p < G::kPairs; p += NW) {
-        int R = 0;
-        while ((R + 1) * (R + 2) / 2 <= p) ++R;
-        const int S = p - R * (R + 1) / 2;
-        const int ra = 16 * R + l16, sb = 16 * S + l16;
-        floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
+    for (; gc < n_total; gc += stride) {
+        // Lane indices re-derived behind an opaque copy: address arithmetic is
+        // then recomputed in each phase instead of being hoisted out of the loop
+        // (dozens of hoisted lane-dependent addresses would spill, and their
+        // reloads would wait behind the in-flight loads of the next chunk).
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        float* const rec = ws + (size_t)gc * G::kRecord;
+        float vb[NT][4];  // needed only at step 5: its latency hides behind steps 2-4
+        prep_load_v<C>(vb, v, row0_of(gc), heads, wave, l16, q4);
+        const int nvalid = nvalid_of(gc);
+
+        // 2. cumulative sums inside each 16-row block, then per-column block prefixes
+        if (tid < NT * kD) {
+            const int j = tid & (kD - 1), R = tid >> 7;
+            float x[16];
 #pragma unroll
-        for (int tau = 0; tau < 8; ++tau) {
-            const int i0 = 16 * tau + 4 * q4;
-            const float4 kr = lds4(&sK[ra * LD + i0]);
-            const float4 qr = lds4(&sQ[ra * LD + i0]);
-            const float4 lr = lds4(&sL[ra * LD + i0]);
-            const float4 ks = lds4(&sK[sb * LD + i0]);
-            const float4 ls = lds4(&sL[sb * LD + i0]);
-            float4 er, es;  // log2 exponents of the row and column factors
-            if (S < R) {
-                // reference: last row of block S.  Row factor 2^(L_r + blocks S+1..R-1),
-                // column factor 2^(B_S - L_s); both <= 1 for gates <= 0
-                const float4 pr = lds4(&sPre[R * kD + i0]);
-                const float4 ps = lds4(&sPre[(S + 1) * kD + i0]);
-                const float4 bs = lds4(&sBlk[S * kD + i0]);
-                er = make_float4(lr.x + (pr.x - ps.x), lr.y + (pr.y - ps.y), lr.z + (pr.z - ps.z),
-                                 lr.w + (pr.w - ps.w));
-                es = make_float4(bs.x - ls.x, bs.y - ls.y, bs.z - ls.z, bs.w - ls.w);
-            } else {
-                // reference: row 7 of the block; each factor spans at most 8 gates
-                const float4 lm = lds4(&sL[(16 * R + 7) * LD + i0]);
-                er = make_float4(lr.x - lm.x, lr.y - lm.y, lr.z - lm.z, lr.w - lm.w);
-                es = make_float4(lm.x - ls.x, lm.y - ls.y, lm.z - ls.z, lm.w - ls.w);
+            for (int r = 0; r < 16; ++r) x[r] = sL[(16 * R + r) * LD + j];
+            float acc = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                acc += x[r];
+                sL[(16 * R + r) * LD + j] = acc;
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float xr = exp2_fast(comp(er, e));
-                const float yc = comp(ks, e) * exp2_fast(comp(es, e));
-                accA = mfma4(comp(kr, e) * xr, yc, accA);
-                accM = mfma4(comp(qr, e) * xr, yc, accM);
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * R + 4 * q4 + e, s = 16 * S + l16;
-            sA[r * LDC + s] = (S < R || s < r) ? sBeta[r] * accA[e] : 0.f;
-            sM[r * LDC + s] = (S < R || s <= r) ? accM[e] : 0.f;
-        }
-    }
-    // 3b. Ktil^T = (e^{G_last - G} o K)^T straight to the record in A-operand
-    //     tile order (consecutive threads write consecutive floats)
-#pragma unroll 4
-    for (int e = tid; e < C * kD; e += kPrepThreads) {
-        int i, r;
-        atile_coords(e, NT, i, r);               // Ktil^T tile: row = key channel i, column = chunk row r
-        const int R = r >> 4;
-        rec[G::kOffKt + e] =
-            sK[r * LD + i] * exp2_fast(sSuf[R * kD + i] + (sBlk[R * kD + i] - sL[r * LD + i]));
-    }
-    // 3c. right-hand sides of W and U in the B-operand layout of this wave's
-    //     column block: beta e^G o K and beta V at rows 16 y + 4 q4 + e
-    //     (and e^G o Q at the same positions: the accumulator layout of this
-    //     wave's output tiles)
-    float bw[NT][4], bu[NT][4], qh[NT][4];
-#pragma unroll
-    for (int y = 0; y < NT; ++y)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int s = 16 * y + 4 * q4 + e, i = 16 * wave + l16;
-            const float bb = sBeta[s];
-            const float gam = exp2_fast(sPre[y * kD + i] + sL[s * LD + i]);
-            bw[y][e] = bb * (gam * sK[s * LD + i]);
-            bu[y][e] = bb * vb[y][e];
-            qh[y][e] = gam * sQ[s * LD + i];
-        }
-    __syncthreads();
-
-    // 4a. T_RR = (I + A_RR)^-1 for each diagonal block, by forward substitution
-    if (wave < NT && lane < 16) {
-        const int base = 16 * wave;
-        float x[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float acc = (i == lane) ? 1.f : 0.f;
-#pragma unroll
-            for (int m = 0; m < i; ++m) acc = fmaf(-sA[(base + i) * LDC + base + m], x[m], acc);
-            x[i] = acc;
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sT[(base + i) * LDC + base + lane] = x[i];
-    }
-    __syncthreads();
-    // 4b. off-diagonal blocks, by distance from the diagonal:
-    //     T_RS = -T_RR sum_{X=S}^{R-1} A_RX T_XS
-#pragma unroll
-    for (int d = 1; d < NT; ++d) {
-        const int S = wave, R = wave + d;
-        if (R < NT) {
-            floatx4 zacc = {0.f, 0.f, 0.f, 0.f};
-            for (int X = S; X < R; ++X) {
-                const float4 a4 = lds4(&sA[(16 * R + l16) * LDC + 16 * X + 4 * q4]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    zacc = mfma4(comp(a4, e), sT[(16 * X + 4 * q4 + e) * LDC + 16 * S + l16], zacc);
-            }
-            const float4 t4 = lds4(&sT[(16 * R + l16) * LDC + 16 * R + 4 * q4]);
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc = mfma4(comp(t4, e), zacc[e], acc);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sT[(16 * R + 4 * q4 + e) * LDC + 16 * S + l16] = -acc[e];
+            sBlk[R * kD + j] = acc;
         }
         __syncthreads();
-    }
+        if (tid < kD) {
+            float bl[NT];
+#pragma unroll
+            for (int R = 0; R < NT; ++R) bl[R] = sBlk[R * kD + tid];
+            float pre = 0.f, suf = 0.f;
+#pragma unroll
+            for (int R = 0; R < NT; ++R) {
+                sPre[R * kD + tid] = pre;
+                pre += bl[R];
+            }
+#pragma unroll
+            for (int R = NT - 1; R >= 0; --R) {
+                sSuf[R * kD + tid] = suf;
+                suf += bl[R];
+            }
+            rec[G::kOffGam + tid] = exp2_fast(pre);  // gamma = e^{G_last}
+        }
+        __syncthreads();
 
-    // 5. W = T (beta e^G o K) and U = T (beta V): this wave's 16-column block, all
-    //    row tiles; the accumulator tiles stay in registers for step 6
-    floatx4 wt[NT], ut[NT];
-#pragma unroll
-    for (int X = 0; X < NT; ++X) {
-        floatx4 accW = {0.f, 0.f, 0.f, 0.f}, accU = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int y = 0; y <= X; ++y) {
-            const float4 t4 = lds4(&sT[(16 * X + l16) * LDC + 16 * y + 4 * q4]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                accW = mfma4(comp(t4, e), bw[y][e], accW);
-                accU = mfma4(comp(t4, e), bu[y][e], accU);
+        // 3a. A and M on the 16x16 block pairs (R, S <= R): one pair per wave, the
+        //     pairs beyond the eighth in two channel halves on waves 0..2 kSplit-1
+        int R, S;
+        if (wave < G::kPairs) {
+            floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
+            pair_of(wave, R, S);
+            am_pair<C, 0, 8>(R, S, sK, sQ, sL, sPre, sBlk, l16, q4, accA, accM);
+            am_store<C>(R, S, accA, accM, sA, sM, sBeta, l16, q4);
+        }
+        floatx4 hA = {0.f, 0.f, 0.f, 0.f}, hM = {0.f, 0.f, 0.f, 0.f};
+        const bool split = wave < 2 * kSplit;
+        if (split) {
+            pair_of(NW + (wave >> 1), R, S);
+            if (wave & 1) am_pair<C, 4, 8>(R, S, sK, sQ, sL, sPre, sBlk, l16, q4, hA, hM);
+            else {
+                am_pair<C, 0, 4>(R, S, sK, sQ, sL, sPre, sBlk, l16, q4, hA, hM);
+                sPart[((wave >> 1) * 2 + 0) * 64 + lane] = hA;
+                sPart[((wave >> 1) * 2 + 1) * 64 + lane] = hM;
             }
         }
-        wt[X] = accW;
-        ut[X] = accU;
+        // 3b. Ktil^T = (e^{G_last - G} o K)^T as A tiles: wave w builds tiles (row
+        //     block s of key channels, column block y of chunk rows) for s = w,
+        //     one float4 store per lane (lane l: channel 16 s + l%16, rows 16 y + 4(l/16)..)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rec[G::kOffW + atile_index(X * 8 + wave, 4 * q4 + e, l16)] = accW[e];
-        // U in the scan's accumulator layout: [row tile][16-column block][lane][4]
-        st4(rec + G::kOffU + ((size_t)(X * 8 + wave) * 64 + lane) * 4,
-            make_float4(accU[0], accU[1], accU[2], accU[3]));
-    }
-    // 6. P = e^G o Q - M W and R = M U.  The W and U accumulator tiles are, lane
-    //    for lane, the B operands of the products over the chunk rows.
-#pragma unroll
-    for (int X = 0; X < NT; ++X) {
-        floatx4 mw = {0.f, 0.f, 0.f, 0.f}, mu = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int y = 0; y <= X; ++y) {
-            const float4 m4 = lds4(&sM[(16 * X + l16) * LDC + 16 * y + 4 * q4]);
+        for (int y = 0; y < NT; ++y) {
+            const int i = 16 * wave + l16;
+            const float bl = sBlk[y * kD + i], sf = sSuf[y * kD + i];
+            float4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                mw = mfma4(comp(m4, e), wt[y][e], mw);
-                mu = mfma4(comp(m4, e), ut[y][e], mu);
+                const int r = 16 * y + 4 * q4 + e;
+                const float val = sK[r * LD + i] * exp2_fast(sf + (bl - sL[r * LD + i]));
+                if (e == 0) o.x = val;
+                if (e == 1) o.y = val;
+                if (e == 2) o.z = val;
+                if (e == 3) o.w = val;
             }
+            st4(rec + G::kOffKt + ((size_t)(wave * NT + y) * 64 + lane) * 4, o);
         }
+        __syncthreads();
+        // finish the split pairs
+        if (split && (wave & 1)) {
+            const floatx4 pa = sPart[((wave >> 1) * 2 + 0) * 64 + lane];
+            const floatx4 pm = sPart[((wave >> 1) * 2 + 1) * 64 + lane];
+            floatx4 a, m;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            rec[G::kOffP + atile_index(X * 8 + wave, 4 * q4 + e, l16)] = qh[X][e] - mw[e];
-        st4(rec + G::kOffR + ((size_t)(X * 8 + wave) * 64 + lane) * 4, make_float4(mu[0], mu[1], mu[2], mu[3]));
+            for (int e = 0; e < 4; ++e) {
+                a[e] = pa[e] + hA[e];
+                m[e] = pm[e] + hM[e];
+            }
+            am_store<C>(R, S, a, m, sA, sM, sBeta, l16, q4);
+        }
+        __syncthreads();
+
+        // 4a. T_RR = (I + A_RR)^-1 for each diagonal block, by forward substitution
+        if (wave < NT && lane < 16) {
+            const int base = 16 * wave;
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float acc = (i == lane) ? 1.f : 0.f;
+#pragma unroll
+                for (int m = 0; m < i; ++m) acc = fmaf(-sA[(base + i) * LDC + base + m], x[m], acc);
+                x[i] = acc;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sT[(base + i) * LDC + base + lane] = x[i];
+        }
+        __syncthreads();
+        // 4b. off-diagonal blocks, by distance from the diagonal:
+        //     T_RS = -T_RR sum_{X=S}^{R-1} A_RX T_XS
+#pragma unroll
+        for (int d = 1; d < NT; ++d) {
+            const int S2 = wave, R2 = wave + d;
+            if (R2 < NT) {
+                floatx4 zacc = {0.f, 0.f, 0.f, 0.f};
+                for (int X = S2; X < R2; ++X) {
+                    const float4 a4 = lds4(&sA[(16 * R2 + l16) * LDC + 16 * X + 4 * q4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        zacc = mfma4(comp(a4, e), sT[(16 * X + 4 * q4 + e) * LDC + 16 * S2 + l16], zacc);
+                }
+                const float4 t4 = lds4(&sT[(16 * R2 + l16) * LDC + 16 * R2 + 4 * q4]);
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc = mfma4(comp(t4, e), zacc[e], acc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sT[(16 * R2 + 4 * q4 + e) * LDC + 16 * S2 + l16] = -acc[e];
+            }
+            __syncthreads();
+        }
+
+        // 4c. right-hand sides of W and U in the B-operand layout of this wave's
+        //     column block: beta e^G o K and beta V at rows 16 y + 4 q4 + e, and
+        //     e^G o Q at the same positions (the accumulator layout of the P tiles)
+        float bw[NT][4], bu[NT][4], qh[NT][4];
+#pragma unroll
+        for (int y = 0; y < NT; ++y)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s_ = 16 * y + 4 * q4 + e, i = 16 * wave + l16;
+                const float bb = sBeta[s_];
+                const float gam = exp2_fast(sPre[y * kD + i] + sL[s_ * LD + i]);
+                bw[y][e] = bb * (gam * sK[s_ * LD + i]);
+                bu[y][e] = bb * (s_ < nvalid ? vb[y][e] : 0.f);
+                qh[y][e] = gam * sQ[s_ * LD + i];
+            }
+
+        // 5. W = T (beta e^G o K) and U = T (beta V): this wave's 16-column block, all
+        //    row tiles; the accumulator tiles stay in registers for step 6
+        floatx4 wt[NT], ut[NT];
+#pragma unroll
+        for (int X = 0; X < NT; ++X) {
+            floatx4 accW = {0.f, 0.f, 0.f, 0.f}, accU = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int y = 0; y <= X; ++y) {
+                const float4 t4 = lds4(&sT[(16 * X + l16) * LDC + 16 * y + 4 * q4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    accW = mfma4(comp(t4, e), bw[y][e], accW);
+                    accU = mfma4(comp(t4, e), bu[y][e], accU);
+                }
+            }
+            wt[X] = accW;
+            ut[X] = accU;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rec[G::kOffW + atile_index(X * 8 + wave, 4 * q4 + e, l16)] = accW[e];
+            // U in the scan's accumulator layout: [row tile][16-column block][lane][4]
+            st4(rec + G::kOffU + ((size_t)(X * 8 + wave) * 64 + lane) * 4,
+                make_float4(accU[0], accU[1], accU[2], accU[3]));
+        }
+        // 6. P = e^G o Q - M W and R = M U.  The W and U accumulator tiles are, lane
+        //    for lane, the B operands of the products over the chunk rows.
+#pragma unroll
+        for (int X = 0; X < NT; ++X) {
+            floatx4 mw = {0.f, 0.f, 0.f, 0.f}, mu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int y = 0; y <= X; ++y) {
+                const float4 m4 = lds4(&sM[(16 * X + l16) * LDC + 16 * y + 4 * q4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    mw = mfma4(comp(m4, e), wt[y][e], mw);
+                    mu = mfma4(comp(m4, e), ut[y][e], mu);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                rec[G::kOffP + atile_index(X * 8 + wave, 4 * q4 + e, l16)] = qh[X][e] - mw[e];
+            st4(rec + G::kOffR + ((size_t)(X * 8 + wave) * 64 + lane) * 4, make_float4(mu[0], mu[1], mu[2], mu[3]));
+        }
+        __syncthreads();
+        // stage the next chunk (loaded during this one) and start loading the one after
+        const int gn = gc + stride;
+        if (gn < n_total) {
+            prep_stage<C>(in, sK, sQ, sL, sBeta, nvalid_of(gn), tid);
+            if (gn + stride < n_total) prep_load<C>(in, q, k, gate, beta, row0_of(gn + stride), heads, tid);
+        }
+        __syncthreads();
     }
 }
 
@@ -509,8 +632,15 @@ static int launch_chunk(const float* q, const float* k, const float* v, const fl
 {
     const int nchunks = t_pad / C;
     const long long n_bh = (long long)batch * heads;
-    hipLaunchKernelGGL(chunk_prepare_kernel<C>, dim3((unsigned)(n_bh * nchunks)), dim3(kPrepThreads), 0, stream, q, k, v,
-                       gate, beta, ws, heads, T, t_pad, nchunks);
+    const int n_total = (int)(n_bh * nchunks);
+    // one persistent prepare workgroup per compute unit (its LDS use allows one)
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+        return -1;
+    const int grid_p = n_total < n_cu ? n_total : n_cu;
+    hipLaunchKernelGGL(chunk_prepare_kernel<C>, dim3((unsigned)grid_p), dim3(kPrepThreads), 0, stream, q, k, v,
+                       gate, beta, ws, heads, T, t_pad, nchunks, n_total);
     if (hipGetLastError() != hipSuccess) return -1;
     const unsigned grid = (unsigned)(((n_bh + 7) / 8) * 64);
     hipLaunchKernelGGL(chunk_scan_kernel<C>, dim3(grid), dim3(kScanThreads), 0, stream, ws, state, out, (int)n_bh, heads, T,
