@@ -201,6 +201,23 @@ __device__ __forceinline__ void am_store(int R, int S, const floatx4& accA, cons
     }
 }
 
+// An accumulator tile (lane l, element e = row 4(l/16) + e, column l%16) rewritten
+// in A-tile lane order (lane l = row l%16, columns 4(l/16) + 0..3) through a
+// wave-private 1 KiB LDS scratch, so the tile leaves with one float4 store per lane.
+__device__ __forceinline__ float4 acc_to_atile(const floatx4& acc, float* scratch, int lane)
+{
+    const int l16 = lane & 15, q4 = lane >> 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        // element (row 4 q4 + e, column l16) belongs to A-lane (l16 / 4) * 16 + 4 q4 + e, slot l16 % 4
+        scratch[((l16 >> 2) * 16 + 4 * q4 + e) * 4 + (l16 & 3)] = acc[e];
+    }
+    __builtin_amdgcn_wave_barrier();
+    const float4 r = lds4(&scratch[lane * 4]);
+    __builtin_amdgcn_wave_barrier();
+    return r;
+}
+
 __device__ __forceinline__ void pair_of(int p, int& R, int& S)
 {
     R = 0;
@@ -412,7 +429,11 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
             }
 
         // 5. W = T (beta e^G o K) and U = T (beta V): this wave's 16-column block, all
-        //    row tiles; the accumulator tiles stay in registers for step 6
+        //    row tiles; the accumulator tiles stay in registers for step 6.  The K
+        //    table is dead until the next chunk is staged: its LDS holds the
+        //    wave-private transpose scratch.
+        static_assert(C * LD >= NW * 256, "transpose scratch");
+        float* const xpose = sK + wave * 256;
         floatx4 wt[NT], ut[NT];
 #pragma unroll
         for (int X = 0; X < NT; ++X) {
@@ -428,8 +449,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
             }
             wt[X] = accW;
             ut[X] = accU;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) rec[G::kOffW + atile_index(X * 8 + wave, 4 * q4 + e, l16)] = accW[e];
+            st4(rec + G::kOffW + ((size_t)(X * 8 + wave) * 64 + lane) * 4, acc_to_atile(accW, xpose, lane));
             // U in the scan's accumulator layout: [row tile][16-column block][lane][4]
             st4(rec + G::kOffU + ((size_t)(X * 8 + wave) * 64 + lane) * 4,
                 make_float4(accU[0], accU[1], accU[2], accU[3]));
@@ -448,9 +468,10 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
                     mu = mfma4(comp(m4, e), ut[y][e], mu);
                 }
             }
+            floatx4 pt;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                rec[G::kOffP + atile_index(X * 8 + wave, 4 * q4 + e, l16)] = qh[X][e] - mw[e];
+            for (int e = 0; e < 4; ++e) pt[e] = qh[X][e] - mw[e];
+            st4(rec + G::kOffP + ((size_t)(X * 8 + wave) * 64 + lane) * 4, acc_to_atile(pt, xpose, lane));
             st4(rec + G::kOffR + ((size_t)(X * 8 + wave) * 64 + lane) * 4, make_float4(mu[0], mu[1], mu[2], mu[3]));
         }
         __syncthreads();
