@@ -58,6 +58,9 @@ extern "C" {
 #endif
 
 #define KDA_HEAD_DIM 128
+/* Largest head count kda_chunk_prefill accepts (byte offsets inside one chunk
+ * of a sequence stay below 2^31). */
+#define KDA_PREFILL_MAX_HEADS 16384
 
 typedef enum {
     KDA_OK = 0,
@@ -91,6 +94,7 @@ size_t kda_chunk_prefill_workspace_bytes(int batch, int heads, int T, int chunk)
  *   out           : [batch][T_pad][heads][128]; rows t < T receive the core output
  *   chunk         : 16, 32 or 64 (changes rounding only, never the result beyond it)
  *   workspace     : device scratch of at least kda_chunk_prefill_workspace_bytes() bytes
+ *   heads         : at most KDA_PREFILL_MAX_HEADS (else KDA_ERR_INVALID_ARG)
  *
  * Rows t >= T of every input may hold anything, NaN and inf included: the
  * kernels select them away before any arithmetic (layer page,

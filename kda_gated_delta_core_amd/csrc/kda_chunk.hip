@@ -24,13 +24,23 @@
 //                 placed on one XCD so the head's records are fetched into
 //                 that XCD's L2 once.
 //
-// Decay handling: G is accumulated in log2 units, separately inside each
-// 16-row block, so no cumulative sum grows beyond 16 gates.  Every pairwise
-// factor exp(G_r - G_s) in A and M is split about a reference row: the last
-// row of the earlier block for off-diagonal blocks (both factors <= 1), row 7
-// of the block for diagonal blocks (each factor spans at most 8 gates).  Pad
-// rows (t >= T) are replaced by zeros with selects before any arithmetic, so
-// NaN or inf there never reaches a result.
+// Decay handling: the gate is accumulated in log2 units, separately inside
+// each 16-row block (L), so no running sum grows beyond 16 gates.  One pass
+// turns K and Q into tables decayed about row 7 of their own block,
+//   Kr = K o 2^(L - L7),  Qr = Q o 2^(L - L7),  Kc = K o 2^(L7 - L)
+// (each factor spans at most 8 gates), with two exponentials per element.
+// Everything else needs only per-channel factors on top of those tables:
+//   diagonal blocks of A, M   Kr Kc^T, Qr Kc^T              (no rescaling)
+//   block pair S < R          (Kr o X_RS)(Kc o Y_S)^T      X_RS = 2^(G7_R - Gend_S),
+//                             Y_S = 2^(Gend_S - G7_S): both operands are then
+//                             decayed about the last row of block S, every
+//                             factor <= 1, so an underflow drops only terms
+//                             below the smallest normal float
+//   e^G o K, e^G o Q          Kr o 2^(G7_R), Qr o 2^(G7_R)
+//   Ktil                      Kc o 2^(Glast - G7_R)
+// (G: cumulative log2 decay from the chunk start; G7_R, Gend_R: at row 7 and
+// at the last row of block R).  Pad rows (t >= T) are replaced by zeros with
+// selects before any arithmetic, so NaN or inf there never reaches a result.
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -145,44 +155,38 @@ __device__ __forceinline__ void prep_stage(const PrepInputs<C>& in, float* sK, f
     if (tid < C) sBeta[tid] = tid < nvalid ? in.beta : 0.f;
 }
 
+// index of block pair (R, S < R) among the pairs below the diagonal
+__device__ __forceinline__ int below_index(int R, int S) { return R * (R - 1) / 2 + S; }
+
 // Partial A and M tile of block pair (R, S <= R) over the channel steps
-// [16 TAU0, 16 TAU1): lane l accumulates rows 16R + 4(l/16) + e, columns 16S + l%16.
+// [16 TAU0, 16 TAU1), from the decayed tables: lane l accumulates rows
+// 16R + 4(l/16) + e, columns 16S + l%16.
 template <int C, int TAU0, int TAU1>
-__device__ __forceinline__ void am_pair(int R, int S, const float* sK, const float* sQ, const float* sL,
-                                        const float* sPre, const float* sBlk, int l16, int q4, floatx4& accA,
+__device__ __forceinline__ void am_pair(int R, int S, const float* sKr, const float* sQr, const float* sKc,
+                                        const float* sX, const float* sY, int l16, int q4, floatx4& accA,
                                         floatx4& accM)
 {
     constexpr int LD = ChunkGeom<C>::kLd;
     const int ra = 16 * R + l16, sb = 16 * S + l16;
+    const float* const xv = sX + (S < R ? below_index(R, S) : 0) * kD;
 #pragma unroll
     for (int tau = TAU0; tau < TAU1; ++tau) {
         const int i0 = 16 * tau + 4 * q4;
-        const float4 kr = lds4(&sK[ra * LD + i0]);
-        const float4 qr = lds4(&sQ[ra * LD + i0]);
-        const float4 lr = lds4(&sL[ra * LD + i0]);
-        const float4 ks = lds4(&sK[sb * LD + i0]);
-        const float4 ls = lds4(&sL[sb * LD + i0]);
-        float4 er, es;  // log2 exponents of the row and column factors
+        float4 kr = lds4(&sKr[ra * LD + i0]);
+        float4 qr = lds4(&sQr[ra * LD + i0]);
+        float4 kc = lds4(&sKc[sb * LD + i0]);
         if (S < R) {
-            // reference: last row of block S.  Row factor 2^(L_r + blocks S+1..R-1),
-            // column factor 2^(B_S - L_s); both <= 1 for gates <= 0
-            const float4 pr = lds4(&sPre[R * kD + i0]);
-            const float4 ps = lds4(&sPre[(S + 1) * kD + i0]);
-            const float4 bs = lds4(&sBlk[S * kD + i0]);
-            er = make_float4(lr.x + (pr.x - ps.x), lr.y + (pr.y - ps.y), lr.z + (pr.z - ps.z), lr.w + (pr.w - ps.w));
-            es = make_float4(bs.x - ls.x, bs.y - ls.y, bs.z - ls.z, bs.w - ls.w);
-        } else {
-            // reference: row 7 of the block; each factor spans at most 8 gates
-            const float4 lm = lds4(&sL[(16 * R + 7) * LD + i0]);
-            er = make_float4(lr.x - lm.x, lr.y - lm.y, lr.z - lm.z, lr.w - lm.w);
-            es = make_float4(lm.x - ls.x, lm.y - ls.y, lm.z - ls.z, lm.w - ls.w);
+            // move both factors to the last row of block S
+            const float4 x = lds4(&xv[i0]);
+            const float4 y = lds4(&sY[S * kD + i0]);
+            kr = make_float4(kr.x * x.x, kr.y * x.y, kr.z * x.z, kr.w * x.w);
+            qr = make_float4(qr.x * x.x, qr.y * x.y, qr.z * x.z, qr.w * x.w);
+            kc = make_float4(kc.x * y.x, kc.y * y.y, kc.z * y.z, kc.w * y.w);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float xr = exp2_fast(comp(er, e));
-            const float yc = comp(ks, e) * exp2_fast(comp(es, e));
-            accA = mfma4(comp(kr, e) * xr, yc, accA);
-            accM = mfma4(comp(qr, e) * xr, yc, accM);
+            accA = mfma4(comp(kr, e), comp(kc, e), accA);
+            accM = mfma4(comp(qr, e), comp(kc, e), accM);
         }
     }
 }
@@ -240,15 +244,17 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
     constexpr int NW = kPrepThreads / 64;
     constexpr int kSplit = G::kPairs > NW ? G::kPairs - NW : 0;  // pairs computed in two channel halves
     static_assert(PrepInputs<C>::NV4 >= 1 && NW == 8 && kSplit <= 2, "geometry");
-    __shared__ float sK[C * LD];
-    __shared__ float sQ[C * LD];
-    __shared__ float sL[C * LD];     // block-local cumulative log2 decay
+    constexpr int NX = NT > 1 ? NT * (NT - 1) / 2 : 1;  // block pairs below the diagonal
+    __shared__ float sKr[C * LD];    // K, then K o 2^(L - L7)
+    __shared__ float sQr[C * LD];    // Q, then Q o 2^(L - L7)
+    __shared__ float sKc[C * LD];    // log2 gates, then K o 2^(L7 - L); transpose scratch after step 3
     __shared__ float sA[C * LDC];    // beta-scaled strictly lower A
     __shared__ float sT[C * LDC];    // (I + A)^-1; before that, partial tiles of the split pairs
     __shared__ float sM[C * LDC];    // lower-triangular decayed Q K^T
-    __shared__ float sBlk[NT * kD];  // log2 decay of each whole 16-row block
-    __shared__ float sPre[NT * kD];  // sum of the block totals before block R
-    __shared__ float sSuf[NT * kD];  // sum of the block totals after block R
+    __shared__ float sE[NT * kD];    // 2^(G7_R)          (L7 of each block during step 2)
+    __shared__ float sF[NT * kD];    // 2^(Glast - G7_R)  (block totals during step 2)
+    __shared__ float sY[NT * kD];    // 2^(Gend_R - G7_R)
+    __shared__ float sX[NX * kD];    // 2^(G7_R - Gend_S), S < R
     __shared__ float sBeta[C];
 
     const int stride = gridDim.x;
@@ -267,7 +273,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
     PrepInputs<C> in;
     if (gc < n_total) {
         prep_load<C>(in, q, k, gate, beta, row0_of(gc), heads, threadIdx.x);
-        prep_stage<C>(in, sK, sQ, sL, sBeta, nvalid_of(gc), threadIdx.x);
+        prep_stage<C>(in, sKr, sQr, sKc, sBeta, nvalid_of(gc), threadIdx.x);
     }
     __syncthreads();
     if (gc + stride < n_total) prep_load<C>(in, q, k, gate, beta, row0_of(gc + stride), heads, threadIdx.x);
@@ -286,35 +292,54 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         prep_load_v<C>(vb, v, row0_of(gc), heads, wave, l16, q4);
         const int nvalid = nvalid_of(gc);
 
-        // 2. cumulative sums inside each 16-row block, then per-column block prefixes
+        // 2. block-local cumulative log2 decay L of each column, then the tables
+        //    decayed about row 7 of the block (L7 and the block totals wait in sE, sF)
         if (tid < NT * kD) {
             const int j = tid & (kD - 1), R = tid >> 7;
-            float x[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] = sL[(16 * R + r) * LD + j];
+            float L[16];
             float acc = 0.f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                acc += x[r];
-                sL[(16 * R + r) * LD + j] = acc;
+                acc += sKc[(16 * R + r) * LD + j];
+                L[r] = acc;
             }
-            sBlk[R * kD + j] = acc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int o = (16 * R + r) * LD + j;
+                const float er = exp2_fast(L[r] - L[7]), ec = exp2_fast(L[7] - L[r]);
+                const float kk = sKr[o];
+                sKr[o] = kk * er;
+                sQr[o] = sQr[o] * er;
+                sKc[o] = kk * ec;
+            }
+            sE[R * kD + j] = L[7];
+            sF[R * kD + j] = L[15];
         }
         __syncthreads();
+        //    per-channel factors, each exponent summed from block-local pieces
         if (tid < kD) {
-            float bl[NT];
-#pragma unroll
-            for (int R = 0; R < NT; ++R) bl[R] = sBlk[R * kD + tid];
-            float pre = 0.f, suf = 0.f;
+            float l7[NT], bl[NT];
 #pragma unroll
             for (int R = 0; R < NT; ++R) {
-                sPre[R * kD + tid] = pre;
-                pre += bl[R];
+                l7[R] = sE[R * kD + tid];
+                bl[R] = sF[R * kD + tid];
             }
+            float pre = 0.f;
 #pragma unroll
-            for (int R = NT - 1; R >= 0; --R) {
-                sSuf[R * kD + tid] = suf;
-                suf += bl[R];
+            for (int R = 0; R < NT; ++R) {
+                float suf = 0.f;
+#pragma unroll
+                for (int X = R + 1; X < NT; ++X) suf += bl[X];
+                sE[R * kD + tid] = exp2_fast(pre + l7[R]);
+                sF[R * kD + tid] = exp2_fast((bl[R] - l7[R]) + suf);
+                sY[R * kD + tid] = exp2_fast(bl[R] - l7[R]);
+                float mid = 0.f;  // blocks strictly between S and R, summed from R down
+#pragma unroll
+                for (int S = R - 1; S >= 0; --S) {
+                    sX[below_index(R, S) * kD + tid] = exp2_fast(l7[R] + mid);
+                    mid += bl[S];
+                }
+                pre += bl[R];
             }
             rec[G::kOffGam + tid] = exp2_fast(pre);  // gamma = e^{G_last}
         }
@@ -326,16 +351,16 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         if (wave < G::kPairs) {
             floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
             pair_of(wave, R, S);
-            am_pair<C, 0, 8>(R, S, sK, sQ, sL, sPre, sBlk, l16, q4, accA, accM);
+            am_pair<C, 0, 8>(R, S, sKr, sQr, sKc, sX, sY, l16, q4, accA, accM);
             am_store<C>(R, S, accA, accM, sA, sM, sBeta, l16, q4);
         }
         floatx4 hA = {0.f, 0.f, 0.f, 0.f}, hM = {0.f, 0.f, 0.f, 0.f};
         const bool split = wave < 2 * kSplit;
         if (split) {
             pair_of(NW + (wave >> 1), R, S);
-            if (wave & 1) am_pair<C, 4, 8>(R, S, sK, sQ, sL, sPre, sBlk, l16, q4, hA, hM);
+            if (wave & 1) am_pair<C, 4, 8>(R, S, sKr, sQr, sKc, sX, sY, l16, q4, hA, hM);
             else {
-                am_pair<C, 0, 4>(R, S, sK, sQ, sL, sPre, sBlk, l16, q4, hA, hM);
+                am_pair<C, 0, 4>(R, S, sKr, sQr, sKc, sX, sY, l16, q4, hA, hM);
                 sPart[((wave >> 1) * 2 + 0) * 64 + lane] = hA;
                 sPart[((wave >> 1) * 2 + 1) * 64 + lane] = hM;
             }
@@ -346,12 +371,12 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
 #pragma unroll
         for (int y = 0; y < NT; ++y) {
             const int i = 16 * wave + l16;
-            const float bl = sBlk[y * kD + i], sf = sSuf[y * kD + i];
+            const float f = sF[y * kD + i];
             float4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * y + 4 * q4 + e;
-                const float val = sK[r * LD + i] * exp2_fast(sf + (bl - sL[r * LD + i]));
+                const float val = sKc[r * LD + i] * f;
                 if (e == 0) o.x = val;
                 if (e == 1) o.y = val;
                 if (e == 2) o.z = val;
@@ -422,18 +447,18 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
             for (int e = 0; e < 4; ++e) {
                 const int s_ = 16 * y + 4 * q4 + e, i = 16 * wave + l16;
                 const float bb = sBeta[s_];
-                const float gam = exp2_fast(sPre[y * kD + i] + sL[s_ * LD + i]);
-                bw[y][e] = bb * (gam * sK[s_ * LD + i]);
+                const float ev = sE[y * kD + i];
+                bw[y][e] = bb * (sKr[s_ * LD + i] * ev);
                 bu[y][e] = bb * (s_ < nvalid ? vb[y][e] : 0.f);
-                qh[y][e] = gam * sQ[s_ * LD + i];
+                qh[y][e] = sQr[s_ * LD + i] * ev;
             }
 
         // 5. W = T (beta e^G o K) and U = T (beta V): this wave's 16-column block, all
-        //    row tiles; the accumulator tiles stay in registers for step 6.  The K
-        //    table is dead until the next chunk is staged: its LDS holds the
-        //    wave-private transpose scratch.
+        //    row tiles; the accumulator tiles stay in registers for step 6.  The Kc
+        //    table is dead from step 3 until the next chunk is staged: its LDS holds
+        //    the wave-private transpose scratch.
         static_assert(C * LD >= NW * 256, "transpose scratch");
-        float* const xpose = sK + wave * 256;
+        float* const xpose = sKc + wave * 256;
         floatx4 wt[NT], ut[NT];
 #pragma unroll
         for (int X = 0; X < NT; ++X) {
@@ -478,7 +503,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         // stage the next chunk (loaded during this one) and start loading the one after
         const int gn = gc + stride;
         if (gn < n_total) {
-            prep_stage<C>(in, sK, sQ, sL, sBeta, nvalid_of(gn), tid);
+            prep_stage<C>(in, sKr, sQr, sKc, sBeta, nvalid_of(gn), tid);
             if (gn + stride < n_total) prep_load<C>(in, q, k, gate, beta, row0_of(gn + stride), heads, tid);
         }
         __syncthreads();
@@ -501,38 +526,66 @@ struct ScanOps {
     float4 g;        // gamma at those rows
 };
 
-// Every wave issues the same load sequence (only the addresses depend on its
-// role), so the wait counts the compiler derives stay exact across the loop.
+// Byte offsets of one wave's operands inside a chunk record; they do not
+// change from chunk to chunk, so they are computed once.
+struct ScanOffsets {
+    int a;   // W rows of the Delta tile or P rows of the output tile (8 A tiles, 1 KiB apart)
+    int x;   // U or R tile of this slice
+    int kt;  // Ktil^T rows of the state tile (NT A tiles, 1 KiB apart)
+    int g;   // gamma at those rows
+};
+
 template <int C>
-__device__ __forceinline__ void scan_load(ScanOps<C>& o, const float* rec, bool is_d, int xd, bool is_p, int xp,
-                                          int wave, int lane, int q4, int slice)
+__device__ __forceinline__ ScanOffsets scan_offsets(bool is_d, int xd, bool is_p, int xp, int wave, int lane, int q4,
+                                                    int slice)
 {
     using G = ChunkGeom<C>;
     constexpr int NT = C / 16;
     const int xa = is_d ? xd : (is_p ? xp : 0);
-    const float* ar = rec + (is_d ? G::kOffW : G::kOffP) + ((size_t)xa * 8 * 64 + lane) * 4;
+    ScanOffsets o;
+    o.a = (int)((is_d ? G::kOffW : G::kOffP) + ((size_t)xa * 8 * 64 + lane) * 4) * 4;
+    o.x = (int)((is_d ? G::kOffU : G::kOffR) + ((size_t)(xa * 8 + slice) * 64 + lane) * 4) * 4;
+    o.kt = (int)(G::kOffKt + ((size_t)wave * NT * 64 + lane) * 4) * 4;
+    o.g = (int)(G::kOffGam + 16 * wave + 4 * q4) * 4;
+    return o;
+}
+
+// Every wave issues the same load sequence (only its lane offsets depend on
+// its role), so the wait counts the compiler derives stay exact across the
+// loop; the record address lives in scalar registers, so issuing the loads
+// needs no vector registers beyond their destinations.
+template <int C>
+__device__ __forceinline__ void scan_load(ScanOps<C>& o, rsrc_t rec, const ScanOffsets& off)
+{
+    constexpr int NT = C / 16;
 #pragma unroll
-    for (int tau = 0; tau < 8; ++tau) o.a[tau] = ld4(ar + tau * 256);
-    o.x = ld4(rec + (is_d ? G::kOffU : G::kOffR) + ((size_t)(xa * 8 + slice) * 64 + lane) * 4);
-    const float* kr = rec + G::kOffKt + ((size_t)wave * NT * 64 + lane) * 4;
+    for (int tau = 0; tau < 8; ++tau) o.a[tau] = buf_ld4(rec, off.a, tau * 1024);
+    o.x = buf_ld4(rec, off.x, 0);
 #pragma unroll
-    for (int y = 0; y < NT; ++y) o.kt[y] = ld4(kr + y * 256);
-    o.g = ld4(rec + G::kOffGam + 16 * wave + 4 * q4);
+    for (int y = 0; y < NT; ++y) o.kt[y] = buf_ld4(rec, off.kt, y * 1024);
+    o.g = buf_ld4(rec, off.g, 0);
 }
 
 // One chunk of the scan for one wave.  The state lives in LDS only, in two
 // buffers: sIn holds the chunk's incoming state, sOut receives the outgoing
 // one.  Tile s, element e of lane l is S[16 s + 4 (l / 16) + e][v0 + l % 16],
 // which is directly the B operand of the 16x16x4 MFMA over the key index.
+// The operands of a later chunk are loaded into `nxt` one tile after every
+// four MFMAs, so the compute unit's vector-memory path takes them while the
+// matrix core works instead of in one burst that the waves wait behind.
 template <int C>
-__device__ __forceinline__ void scan_chunk(const ScanOps<C>& cur, floatx4 (*sIn)[64], floatx4 (*sOut)[64],
-                                           floatx4 (*sDelta)[64], float* __restrict__ out, int c, bool is_d,
-                                           int xd, bool is_p, int xp, int wave, int lane, int q4, int v0, int l16,
-                                           int b, int h, int heads, int T, int t_pad)
+__device__ __forceinline__ void scan_chunk(const ScanOps<C>& cur, ScanOps<C>& nxt, rsrc_t nrec,
+                                           const ScanOffsets& off, floatx4 (*sIn)[64], floatx4 (*sOut)[64],
+                                           floatx4 (*sDelta)[64], float* __restrict__ out_b, int out_voff, int c,
+                                           bool is_d, int xd, bool is_p, int xp, int wave, int lane, int q4,
+                                           int heads, int T)
 {
     constexpr int NT = C / 16;
+    // at C = 64 every wave has a role in step A: no branch, so the wait counts
+    // the compiler derives never merge a path that issued loads with one that did not
+    constexpr bool kAllRoles = 2 * NT == kScanThreads / 64;
     // A. Delta = U - W S (Delta waves) and O = R + P S (output waves)
-    if (is_d || is_p) {
+    if (kAllRoles || is_d || is_p) {
         floatx4 st[8];
 #pragma unroll
         for (int tau = 0; tau < 8; ++tau) st[tau] = sIn[tau][lane];
@@ -547,7 +600,10 @@ __device__ __forceinline__ void scan_chunk(const ScanOps<C>& cur, floatx4 (*sIn)
             acc = mfma4(cur.a[tau].y, st[tau][1], acc);
             acc = mfma4(cur.a[tau].z, st[tau][2], acc);
             acc = mfma4(cur.a[tau].w, st[tau][3], acc);
+            nxt.a[tau] = buf_ld4(nrec, off.a, tau * 1024);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        nxt.x = buf_ld4(nrec, off.x, 0);
         if (is_d) {
             floatx4 d;
             d[0] = cur.x.x - acc[0];
@@ -556,12 +612,18 @@ __device__ __forceinline__ void scan_chunk(const ScanOps<C>& cur, floatx4 (*sIn)
             d[3] = cur.x.w - acc[3];
             sDelta[xd][lane] = d;
         } else {
+            // rows c C + 16 xp + 4 q4 + e of this sequence's output, columns v0 + l16
+            const rsrc_t ob = make_rsrc(out_b + (size_t)c * C * heads * kD, (uint32_t)(C * heads * kD * 4));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = c * C + 16 * xp + 4 * q4 + e;
-                if (t < T) out[(((size_t)b * t_pad + t) * heads + h) * kD + v0 + l16] = acc[e];
+                if (t < T) buf_st1(ob, out_voff, e * heads * kD * 4, acc[e]);
             }
         }
+    } else {
+#pragma unroll
+        for (int tau = 0; tau < 8; ++tau) nxt.a[tau] = buf_ld4(nrec, off.a, tau * 1024);
+        nxt.x = buf_ld4(nrec, off.x, 0);
     }
     __syncthreads();
 
@@ -582,7 +644,10 @@ __device__ __forceinline__ void scan_chunk(const ScanOps<C>& cur, floatx4 (*sIn)
             acc = mfma4(cur.kt[y].y, dl[y][1], acc);
             acc = mfma4(cur.kt[y].z, dl[y][2], acc);
             acc = mfma4(cur.kt[y].w, dl[y][3], acc);
+            nxt.kt[y] = buf_ld4(nrec, off.kt, y * 1024);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        nxt.g = buf_ld4(nrec, off.g, 0);
         sOut[wave][lane] = acc;
     }
     __syncthreads();
@@ -612,6 +677,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(const float* _
     __shared__ floatx4 sS[2][8][64];
 
     float* const S_head = state + (size_t)bh * kD * kD;
+    float* const out_b = out + (size_t)b * t_pad * heads * kD;
+    const int out_voff = ((16 * xp + 4 * q4) * heads * kD + h * kD + v0 + l16) * 4;
     {
         floatx4 st;
 #pragma unroll
@@ -619,26 +686,27 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(const float* _
         sS[0][wave][lane] = st;
     }
     const float* const rec0 = ws + (size_t)bh * nchunks * G::kRecord;
-    auto rec = [&](int cc) { return rec0 + (size_t)(cc < nchunks ? cc : nchunks - 1) * G::kRecord; };
+    auto rec = [&](int cc) {
+        return make_rsrc(rec0 + (size_t)(cc < nchunks ? cc : nchunks - 1) * G::kRecord, (uint32_t)(G::kRecord * 4));
+    };
+    const ScanOffsets off = scan_offsets<C>(is_d, xd, is_p, xp, wave, lane, q4, slice);
     // Three operand buffers in rotation: while one chunk is computed, the loads
-    // of the next two are in flight (no register copies between the buffers,
-    // so no wait on a prefetch before it is needed).
+    // of the next are in flight and those of the one after are being issued
+    // (no register copies between the buffers, so no wait on a prefetch
+    // before it is needed).
     ScanOps<C> op0, op1, op2;
-    scan_load<C>(op0, rec(0), is_d, xd, is_p, xp, wave, lane, q4, slice);
-    scan_load<C>(op1, rec(1), is_d, xd, is_p, xp, wave, lane, q4, slice);
+    scan_load<C>(op0, rec(0), off);
+    scan_load<C>(op1, rec(1), off);
     __syncthreads();
     for (int c = 0; c < nchunks; c += 3) {
-        scan_load<C>(op2, rec(c + 2), is_d, xd, is_p, xp, wave, lane, q4, slice);
-        scan_chunk<C>(op0, sS[c & 1], sS[(c + 1) & 1], sDelta, out, c, is_d, xd, is_p, xp, wave, lane, q4, v0, l16,
-                      b, h, heads, T, t_pad);
+        scan_chunk<C>(op0, op2, rec(c + 2), off, sS[c & 1], sS[(c + 1) & 1], sDelta, out_b, out_voff, c, is_d, xd,
+                      is_p, xp, wave, lane, q4, heads, T);
         if (c + 1 >= nchunks) break;
-        scan_load<C>(op0, rec(c + 3), is_d, xd, is_p, xp, wave, lane, q4, slice);
-        scan_chunk<C>(op1, sS[(c + 1) & 1], sS[c & 1], sDelta, out, c + 1, is_d, xd, is_p, xp, wave, lane, q4, v0,
-                      l16, b, h, heads, T, t_pad);
+        scan_chunk<C>(op1, op0, rec(c + 3), off, sS[(c + 1) & 1], sS[c & 1], sDelta, out_b, out_voff, c + 1, is_d,
+                      xd, is_p, xp, wave, lane, q4, heads, T);
         if (c + 2 >= nchunks) break;
-        scan_load<C>(op1, rec(c + 4), is_d, xd, is_p, xp, wave, lane, q4, slice);
-        scan_chunk<C>(op2, sS[c & 1], sS[(c + 1) & 1], sDelta, out, c + 2, is_d, xd, is_p, xp, wave, lane, q4, v0,
-                      l16, b, h, heads, T, t_pad);
+        scan_chunk<C>(op2, op1, rec(c + 4), off, sS[c & 1], sS[(c + 1) & 1], sDelta, out_b, out_voff, c + 2, is_d,
+                      xd, is_p, xp, wave, lane, q4, heads, T);
     }
     // the final state is in sS[nchunks & 1]
     const floatx4 st = sS[nchunks & 1][wave][lane];

@@ -13,6 +13,34 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 __device__ __forceinline__ void st4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
 
+// Raw buffer access: a descriptor (base address, size in bytes) held in scalar
+// registers plus a 32-bit per-lane byte offset and a wave-uniform byte offset.
+// Lane offsets computed once outside a loop then need no per-iteration vector
+// address registers.  Offsets at or past the size read zeros and drop stores.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 raw (untyped) buffer, 32-bit elements
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
+}
+__device__ __forceinline__ float4 buf_ld4(rsrc_t r, int voff, int soff)
+{
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ float buf_ld1(rsrc_t r, int voff, int soff)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ void buf_st4(rsrc_t r, int voff, int soff, float4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), r, voff,
+                                           soff, 0);
+}
+__device__ __forceinline__ void buf_st1(rsrc_t r, int voff, int soff, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, voff, soff, 0);
+}
+
 // One 16x16x4 FP32 MFMA step:  acc[16x16] += A[16x4] * B[4x16].
 // Lane l supplies A[l % 16][l / 16] in `a` and B[l / 16][l % 16] in `b`;
 // acc element r of lane l is C[4 * (l / 16) + r][l % 16].

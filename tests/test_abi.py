@@ -87,6 +87,8 @@ def test_prefill_refusals(lib):
     # size overflow
     assert lib.kda_chunk_prefill(*P[:7], 1 << 20, 1 << 10, 1 << 20, 64, P[7], 1 << 62, None) == \
         kda.KDA_ERR_INVALID_ARG
+    # more heads than the in-chunk offsets allow
+    assert lib.kda_chunk_prefill(*P[:7], 1, 16385, 64, 16, P[7], 1 << 40, None) == kda.KDA_ERR_INVALID_ARG
 
 
 def test_recurrent_refusals(lib):
