@@ -101,37 +101,47 @@ struct PrepInputs {
     float beta;
 };
 
-// Issue every global read of chunk `gc` (global index b * nchunks * heads-major).
-// The reads stay inside the T_pad rows of the chunk; pad rows are masked later.
+// Raw buffer descriptors over the C rows of one chunk of one (sequence, head)
+// in each input; row0 = (b T_pad + first row) heads + h.
+struct PrepSrc {
+    rsrc_t q, k, g, v, b;
+};
 template <int C>
-__device__ __forceinline__ void prep_load(PrepInputs<C>& in, const float* __restrict__ q,
-                                          const float* __restrict__ k, const float* __restrict__ gate,
-                                          const float* __restrict__ beta, size_t row0, int heads, int tid)
+__device__ __forceinline__ PrepSrc prep_src(const float* q, const float* k, const float* v, const float* gate,
+                                            const float* beta, size_t row0, int heads)
 {
-    constexpr int NV4 = PrepInputs<C>::NV4;
+    const uint32_t vec = (uint32_t)(C * heads * kD * 4), sca = (uint32_t)(C * heads * 4);
+    return {make_rsrc(q + row0 * kD, vec), make_rsrc(k + row0 * kD, vec), make_rsrc(gate + row0 * kD, vec),
+            make_rsrc(v + row0 * kD, vec), make_rsrc(beta + row0, sca)};
+}
+
+// One row-major input of a chunk as thread tid holds it: rows tid/32 + 16 i,
+// columns 4 (tid % 32) + 0..3.  Pad rows are loaded like the others and masked
+// when staged.
+template <int C>
+__device__ __forceinline__ void prep_load_part(float4 (&dst)[PrepInputs<C>::NV4], rsrc_t src, int heads, int tid)
+{
+    const int voff = ((tid >> 5) * heads * kD + (tid & 31) * 4) * 4;
 #pragma unroll
-    for (int i = 0; i < NV4; ++i) {
-        const int e = tid + kPrepThreads * i, r = e >> 5, c4 = (e & 31) * 4;
-        const size_t off = (row0 + (size_t)r * heads) * kD + c4;
-        in.k[i] = ld4(k + off);
-        in.q[i] = ld4(q + off);
-        in.g[i] = ld4(gate + off);
-    }
-    in.beta = tid < C ? beta[row0 + (size_t)tid * heads] : 0.f;
+    for (int i = 0; i < PrepInputs<C>::NV4; ++i) dst[i] = buf_ld4(src, voff, i * 16 * heads * kD * 4);
+}
+template <int C>
+__device__ __forceinline__ float prep_load_beta(rsrc_t src, int heads, int tid)
+{
+    return tid < C ? buf_ld1(src, tid * heads * 4, 0) : 0.f;
 }
 
 // V of one chunk in the B-operand layout of this wave's U tiles (rows
 // 16 y + 4 q4 + e, column 16 wave + l16).  Rows >= T are selected away where
 // the values are used, so that nothing here waits for the loads.
 template <int C>
-__device__ __forceinline__ void prep_load_v(float (&vb)[C / 16][4], const float* __restrict__ v, size_t row0,
-                                            int heads, int wave, int l16, int q4)
+__device__ __forceinline__ void prep_load_v(float (&vb)[C / 16][4], rsrc_t src, int heads, int wave, int l16, int q4)
 {
+    const int voff = (4 * q4 * heads * kD + 16 * wave + l16) * 4;
 #pragma unroll
     for (int y = 0; y < C / 16; ++y)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            vb[y][e] = v[(row0 + (size_t)(16 * y + 4 * q4 + e) * heads) * kD + 16 * wave + l16];
+        for (int e = 0; e < 4; ++e) vb[y][e] = buf_ld1(src, voff, (16 * y + e) * heads * kD * 4);
 }
 
 // Rows >= T (nvalid and beyond) are replaced by zeros with selects, then the
@@ -230,9 +240,9 @@ __device__ __forceinline__ void pair_of(int p, int& R, int& S)
 }
 
 // Persistent: one workgroup per CU walks the chunks gc = blockIdx.x, +gridDim.x, ...
-// (gc = (b * heads + h) * nchunks + c).  The inputs of the next chunk are in
-// flight into registers during the whole of the current one and are staged into
-// LDS at its end.
+// (gc = (b * heads + h) * nchunks + c).  The inputs of the next chunk are read
+// into registers while the current one is computed and are staged into LDS at
+// its end.
 template <int C>
 __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
@@ -272,11 +282,14 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
     int gc = blockIdx.x;
     PrepInputs<C> in;
     if (gc < n_total) {
-        prep_load<C>(in, q, k, gate, beta, row0_of(gc), heads, threadIdx.x);
+        const PrepSrc src = prep_src<C>(q, k, v, gate, beta, row0_of(gc), heads);
+        prep_load_part<C>(in.k, src.k, heads, threadIdx.x);
+        prep_load_part<C>(in.q, src.q, heads, threadIdx.x);
+        prep_load_part<C>(in.g, src.g, heads, threadIdx.x);
+        in.beta = prep_load_beta<C>(src.b, heads, threadIdx.x);
         prep_stage<C>(in, sKr, sQr, sKc, sBeta, nvalid_of(gc), threadIdx.x);
     }
     __syncthreads();
-    if (gc + stride < n_total) prep_load<C>(in, q, k, gate, beta, row0_of(gc + stride), heads, threadIdx.x);
 
     for (; gc < n_total; gc += stride) {
         // Lane indices re-derived behind an opaque copy: address arithmetic is
@@ -288,9 +301,15 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         const int lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         float* const rec = ws + (size_t)gc * G::kRecord;
-        float vb[NT][4];  // needed only at step 5: its latency hides behind steps 2-4
-        prep_load_v<C>(vb, v, row0_of(gc), heads, wave, l16, q4);
+        float vb[NT][4];  // needed only at step 4c: its latency hides behind steps 2-4
+        prep_load_v<C>(vb, prep_src<C>(q, k, v, gate, beta, row0_of(gc), heads).v, heads, wave, l16, q4);
         const int nvalid = nvalid_of(gc);
+        // The next chunk's inputs are read in three parts, at steps 3, 5 and 6,
+        // so the vector-memory path takes them while the matrix cores work.  The
+        // last chunk of a workgroup re-reads a valid chunk instead of branching,
+        // which keeps every wave's load sequence, and so its wait counts, fixed.
+        const int gn = gc + stride;
+        const PrepSrc nsrc = prep_src<C>(q, k, v, gate, beta, row0_of(gn < n_total ? gn : gc), heads);
 
         // 2. block-local cumulative log2 decay L of each column, then the tables
         //    decayed about row 7 of the block (L7 and the block totals wait in sE, sF)
@@ -347,6 +366,9 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
 
         // 3a. A and M on the 16x16 block pairs (R, S <= R): one pair per wave, the
         //     pairs beyond the eighth in two channel halves on waves 0..2 kSplit-1
+        __builtin_amdgcn_sched_barrier(0);
+        prep_load_part<C>(in.k, nsrc.k, heads, tid);
+        __builtin_amdgcn_sched_barrier(0);
         int R, S;
         if (wave < G::kPairs) {
             floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
@@ -459,6 +481,9 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         //    the wave-private transpose scratch.
         static_assert(C * LD >= NW * 256, "transpose scratch");
         float* const xpose = sKc + wave * 256;
+        __builtin_amdgcn_sched_barrier(0);
+        prep_load_part<C>(in.q, nsrc.q, heads, tid);
+        __builtin_amdgcn_sched_barrier(0);
         floatx4 wt[NT], ut[NT];
 #pragma unroll
         for (int X = 0; X < NT; ++X) {
@@ -481,6 +506,10 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         }
         // 6. P = e^G o Q - M W and R = M U.  The W and U accumulator tiles are, lane
         //    for lane, the B operands of the products over the chunk rows.
+        __builtin_amdgcn_sched_barrier(0);
+        prep_load_part<C>(in.g, nsrc.g, heads, tid);
+        in.beta = prep_load_beta<C>(nsrc.b, heads, tid);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int X = 0; X < NT; ++X) {
             floatx4 mw = {0.f, 0.f, 0.f, 0.f}, mu = {0.f, 0.f, 0.f, 0.f};
@@ -500,12 +529,9 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
             st4(rec + G::kOffR + ((size_t)(X * 8 + wave) * 64 + lane) * 4, make_float4(mu[0], mu[1], mu[2], mu[3]));
         }
         __syncthreads();
-        // stage the next chunk (loaded during this one) and start loading the one after
-        const int gn = gc + stride;
-        if (gn < n_total) {
-            prep_stage<C>(in, sKr, sQr, sKc, sBeta, nvalid_of(gn), tid);
-            if (gn + stride < n_total) prep_load<C>(in, q, k, gate, beta, row0_of(gn + stride), heads, tid);
-        }
+        // stage the next chunk (loaded during this one; after the last chunk the
+        // staged copy is unused)
+        prep_stage<C>(in, sKr, sQr, sKc, sBeta, nvalid_of(gn < n_total ? gn : gc), tid);
         __syncthreads();
     }
 }
