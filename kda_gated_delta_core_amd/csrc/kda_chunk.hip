@@ -3,11 +3,14 @@
 // Two kernels, as the kernel-table page splits the prefill (fields
 // chunk_prepare and chunk_scan):
 //
-//  chunk_prepare  one workgroup per (sequence, head, chunk), all chunks in
-//                 parallel.  Builds the chunk's WY/UT factors in LDS with FP32
-//                 MFMA: G the per-channel cumulative log-decay inside the chunk,
-//                 A the strictly lower decayed K K^T scaled by beta, T = (I + A)^-1,
-//                 M the lower-triangular decayed Q K^T,
+//  chunk_prepare  chunks are independent: one persistent workgroup per compute
+//                 unit walks (sequence, head, chunk) triples.  Builds the
+//                 chunk's WY/UT factors in LDS with FP32 MFMA: G the
+//                 per-channel cumulative log-decay inside the chunk, A the
+//                 strictly lower decayed K K^T scaled by beta, T = (I + A)^-1
+//                 (only its 16x16 diagonal blocks are inverted; the rest is
+//                 block forward substitution on the right-hand sides), M the
+//                 lower-triangular decayed Q K^T,
 //                   W = T diag(beta)(e^G o K),  U = T diag(beta) V,
 //                 and writes one workspace record with W, U,
 //                   P = e^G o Q - M W,  R = M U,
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
     __shared__ float sQr[C * LD];    // Q, then Q o 2^(L - L7)
     __shared__ float sKc[C * LD];    // log2 gates, then K o 2^(L7 - L); transpose scratch after step 3
     __shared__ float sA[C * LDC];    // beta-scaled strictly lower A
-    __shared__ float sT[C * LDC];    // (I + A)^-1; before that, partial tiles of the split pairs
+    __shared__ float sT[C * LDC];    // diagonal blocks of (I + A)^-1; before that, partial tiles of the split pairs
     __shared__ float sM[C * LDC];    // lower-triangular decayed Q K^T
     __shared__ float sE[NT * kD];    // 2^(G7_R)          (L7 of each block during step 2)
     __shared__ float sF[NT * kD];    // 2^(Glast - G7_R)  (block totals during step 2)
@@ -436,29 +439,6 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
             for (int i = 0; i < 16; ++i) sT[(base + i) * LDC + base + lane] = x[i];
         }
         __syncthreads();
-        // 4b. off-diagonal blocks, by distance from the diagonal:
-        //     T_RS = -T_RR sum_{X=S}^{R-1} A_RX T_XS
-#pragma unroll
-        for (int d = 1; d < NT; ++d) {
-            const int S2 = wave, R2 = wave + d;
-            if (R2 < NT) {
-                floatx4 zacc = {0.f, 0.f, 0.f, 0.f};
-                for (int X = S2; X < R2; ++X) {
-                    const float4 a4 = lds4(&sA[(16 * R2 + l16) * LDC + 16 * X + 4 * q4]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        zacc = mfma4(comp(a4, e), sT[(16 * X + 4 * q4 + e) * LDC + 16 * S2 + l16], zacc);
-                }
-                const float4 t4 = lds4(&sT[(16 * R2 + l16) * LDC + 16 * R2 + 4 * q4]);
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc = mfma4(comp(t4, e), zacc[e], acc);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sT[(16 * R2 + 4 * q4 + e) * LDC + 16 * S2 + l16] = -acc[e];
-            }
-            __syncthreads();
-        }
-
         // 4c. right-hand sides of W and U in the B-operand layout of this wave's
         //     column block: beta e^G o K and beta V at rows 16 y + 4 q4 + e, and
         //     e^G o Q at the same positions (the accumulator layout of the P tiles)
@@ -475,10 +455,13 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
                 qh[y][e] = sQr[s_ * LD + i] * ev;
             }
 
-        // 5. W = T (beta e^G o K) and U = T (beta V): this wave's 16-column block, all
-        //    row tiles; the accumulator tiles stay in registers for step 6.  The Kc
-        //    table is dead from step 3 until the next chunk is staged: its LDS holds
-        //    the wave-private transpose scratch.
+        // 5. W = T (beta e^G o K) and U = T (beta V) for this wave's 16-column block,
+        //    by block forward substitution on the right-hand sides,
+        //      Z_X = RHS_X - sum_{Y < X} A_XY W_Y,   W_X = T_XX Z_X,
+        //    so the blocks of T below the diagonal are never formed.  The
+        //    accumulator tiles stay in registers for step 6.  The Kc table is dead
+        //    from step 3 until the next chunk is staged: its LDS holds the
+        //    wave-private transpose scratch.
         static_assert(C * LD >= NW * 256, "transpose scratch");
         float* const xpose = sKc + wave * 256;
         __builtin_amdgcn_sched_barrier(0);
@@ -487,15 +470,27 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         floatx4 wt[NT], ut[NT];
 #pragma unroll
         for (int X = 0; X < NT; ++X) {
-            floatx4 accW = {0.f, 0.f, 0.f, 0.f}, accU = {0.f, 0.f, 0.f, 0.f};
+            floatx4 zw, zu;
 #pragma unroll
-            for (int y = 0; y <= X; ++y) {
-                const float4 t4 = lds4(&sT[(16 * X + l16) * LDC + 16 * y + 4 * q4]);
+            for (int e = 0; e < 4; ++e) {
+                zw[e] = bw[X][e];
+                zu[e] = bu[X][e];
+            }
+#pragma unroll
+            for (int Y = 0; Y < X; ++Y) {
+                const float4 a4 = lds4(&sA[(16 * X + l16) * LDC + 16 * Y + 4 * q4]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    accW = mfma4(comp(t4, e), bw[y][e], accW);
-                    accU = mfma4(comp(t4, e), bu[y][e], accU);
+                    zw = mfma4(-comp(a4, e), wt[Y][e], zw);
+                    zu = mfma4(-comp(a4, e), ut[Y][e], zu);
                 }
+            }
+            const float4 t4 = lds4(&sT[(16 * X + l16) * LDC + 16 * X + 4 * q4]);
+            floatx4 accW = {0.f, 0.f, 0.f, 0.f}, accU = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                accW = mfma4(comp(t4, e), zw[e], accW);
+                accU = mfma4(comp(t4, e), zu[e], accU);
             }
             wt[X] = accW;
             ut[X] = accU;
