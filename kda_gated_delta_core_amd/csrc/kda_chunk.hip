@@ -719,16 +719,24 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(const float* _
     scan_load<C>(op0, rec(0), off);
     scan_load<C>(op1, rec(1), off);
     __syncthreads();
-    for (int c = 0; c < nchunks; c += 3) {
+    // Whole rounds of three chunks, then the remaining one or two: the loop has
+    // a single back edge, so the wait counts at its head see only the state in
+    // which a round ends.
+    int c = 0;
+    for (; c + 3 <= nchunks; c += 3) {
         scan_chunk<C>(op0, op2, rec(c + 2), off, sS[c & 1], sS[(c + 1) & 1], sDelta, out_b, out_voff, c, is_d, xd,
                       is_p, xp, wave, lane, q4, heads, T);
-        if (c + 1 >= nchunks) break;
         scan_chunk<C>(op1, op0, rec(c + 3), off, sS[(c + 1) & 1], sS[c & 1], sDelta, out_b, out_voff, c + 1, is_d,
                       xd, is_p, xp, wave, lane, q4, heads, T);
-        if (c + 2 >= nchunks) break;
         scan_chunk<C>(op2, op1, rec(c + 4), off, sS[c & 1], sS[(c + 1) & 1], sDelta, out_b, out_voff, c + 2, is_d,
                       xd, is_p, xp, wave, lane, q4, heads, T);
     }
+    if (c < nchunks)
+        scan_chunk<C>(op0, op2, rec(c + 2), off, sS[c & 1], sS[(c + 1) & 1], sDelta, out_b, out_voff, c, is_d, xd,
+                      is_p, xp, wave, lane, q4, heads, T);
+    if (c + 1 < nchunks)
+        scan_chunk<C>(op1, op0, rec(c + 3), off, sS[(c + 1) & 1], sS[c & 1], sDelta, out_b, out_voff, c + 1, is_d,
+                      xd, is_p, xp, wave, lane, q4, heads, T);
     // the final state is in sS[nchunks & 1]
     const floatx4 st = sS[nchunks & 1][wave][lane];
 #pragma unroll
