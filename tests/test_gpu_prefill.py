@@ -185,3 +185,44 @@ def test_prefill_h32_t8192_full_size(device):
         o_ref, s_ref, _, _ = oracle.serial(sub["q"], sub["k"], sub["v"], sub["gate"], sub["beta"], sub["state"])
         assert_close(f"h{h} core", o[:, :w.T, h:h + 1], o_ref)
         assert_close(f"h{h} state", host(st)[:, h:h + 1], s_ref)
+
+
+@pytest.mark.timeout(900)
+def test_prefill_b4_t32768_then_decode_full_size(device):
+    """4 sequences x T=32768, H=32, C=64, gates in [-0.5, 0] (long memory), then 16 decode steps per
+    sequence from the prefilled states (rows T.. of the same streams); the oracle walks one sampled
+    head of each sequence through all T + 16 rows."""
+    import torch
+    import kda_gated_delta_core_amd as kda
+    w = ki.WORKLOADS["prefill_b4_h32_t32768_c64"]
+    B, H, T = w.batch, w.heads, w.T
+    announce(f"kda_chunk_prefill {w.name} seed={w.seed} (generating inputs)")
+    x = ki.workload_inputs(w)
+    announce("running GPU prefill")
+    out, st, ws = _prefill(kda, x, T, w.chunk)
+    del ws
+    st_pre = host(st)
+    announce(f"running {w.tail_steps} x kda_recurrent_step")
+    rows = [ki.sequence_rows(w.seed, s, T, T + w.tail_steps, H, w.gate_lo) for s in range(B)]
+    tail = {n: np.stack([r[n] for r in rows]) for n in ("q", "k", "v", "gate", "beta")}  # [B, steps, H(, D)]
+    outs = []
+    for j in range(w.tail_steps):
+        sl = lambda a: dev(np.ascontiguousarray(a[:, j:j + 1]))
+        o = torch.empty((B, 1, H, 128), device="cuda")
+        kda.kda_recurrent_step(sl(tail["q"]), sl(tail["k"]), sl(tail["v"]), sl(tail["gate"]), sl(tail["beta"]), st,
+                               out=o)
+        outs.append(host(o))
+    tail_out = np.concatenate(outs, 1)
+    st_end = host(st)
+    for b, h in ((0, 0), (1, 11), (2, 22), (3, 31)):
+        announce(f"oracle sequence {b} head {h}")
+        sub = {n: np.ascontiguousarray(x[n][b:b + 1, :T, h:h + 1]) for n in ("q", "k", "v", "gate", "beta")}
+        o_ref, s_ref, _, _ = oracle.serial(sub["q"], sub["k"], sub["v"], sub["gate"], sub["beta"],
+                                           x["state"][b:b + 1, h:h + 1])
+        o_gpu = out[b:b + 1, :T, h:h + 1].cpu().numpy()
+        assert_close(f"b{b} h{h} core", o_gpu, o_ref)
+        assert_close(f"b{b} h{h} state after prefill", st_pre[b:b + 1, h:h + 1], s_ref)
+        tsub = {n: np.ascontiguousarray(tail[n][b:b + 1, :, h:h + 1]) for n in tail}
+        o2, s2, _, _ = oracle.serial(tsub["q"], tsub["k"], tsub["v"], tsub["gate"], tsub["beta"], s_ref)
+        assert_close(f"b{b} h{h} decode tail core", tail_out[b:b + 1, :, h:h + 1], o2)
+        assert_close(f"b{b} h{h} final state", st_end[b:b + 1, h:h + 1], s2)
