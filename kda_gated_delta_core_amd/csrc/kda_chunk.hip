@@ -105,15 +105,17 @@ struct PrepInputs {
 };
 
 // Raw buffer descriptors over the C rows of one chunk of one (sequence, head)
-// in each input; row0 = (b T_pad + first row) heads + h.
+// in each input; row0 = (b T_pad + first row) heads + h.  With `live` false
+// the descriptors cover zero bytes: loads through them return zeros without
+// touching memory, so a wave can issue its usual load sequence for no chunk.
 struct PrepSrc {
     rsrc_t q, k, g, v, b;
 };
 template <int C>
 __device__ __forceinline__ PrepSrc prep_src(const float* q, const float* k, const float* v, const float* gate,
-                                            const float* beta, size_t row0, int heads)
+                                            const float* beta, size_t row0, int heads, bool live = true)
 {
-    const uint32_t vec = (uint32_t)(C * heads * kD * 4), sca = (uint32_t)(C * heads * 4);
+    const uint32_t vec = live ? (uint32_t)(C * heads * kD * 4) : 0u, sca = live ? (uint32_t)(C * heads * 4) : 0u;
     return {make_rsrc(q + row0 * kD, vec), make_rsrc(k + row0 * kD, vec), make_rsrc(gate + row0 * kD, vec),
             make_rsrc(v + row0 * kD, vec), make_rsrc(beta + row0, sca)};
 }
@@ -308,11 +310,12 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         prep_load_v<C>(vb, prep_src<C>(q, k, v, gate, beta, row0_of(gc), heads).v, heads, wave, l16, q4);
         const int nvalid = nvalid_of(gc);
         // The next chunk's inputs are read in three parts, at steps 3, 5 and 6,
-        // so the vector-memory path takes them while the matrix cores work.  The
-        // last chunk of a workgroup re-reads a valid chunk instead of branching,
-        // which keeps every wave's load sequence, and so its wait counts, fixed.
+        // so the vector-memory path takes them while the matrix cores work.
+        // After a workgroup's last chunk the loads go through empty descriptors
+        // instead of being branched around, which keeps every wave's load
+        // sequence, and so its wait counts, fixed.
         const int gn = gc + stride;
-        const PrepSrc nsrc = prep_src<C>(q, k, v, gate, beta, row0_of(gn < n_total ? gn : gc), heads);
+        const PrepSrc nsrc = prep_src<C>(q, k, v, gate, beta, row0_of(gn < n_total ? gn : gc), heads, gn < n_total);
 
         // 2. block-local cumulative log2 decay L of each column, then the tables
         //    decayed about row 7 of the block (L7 and the block totals wait in sE, sF)
