@@ -221,18 +221,23 @@ __device__ __forceinline__ void am_store(int R, int S, const floatx4& accA, cons
 }
 
 // An accumulator tile (lane l, element e = row 4(l/16) + e, column l%16) rewritten
-// in A-tile lane order (lane l = row l%16, columns 4(l/16) + 0..3) through a
-// wave-private 1 KiB LDS scratch, so the tile leaves with one float4 store per lane.
+// in A-tile lane order (lane L = row L%16, columns 4(L/16) + 0..3) through a
+// wave-private 1 KiB LDS scratch, so the tile leaves with one float4 store per
+// lane.  Lane L's four values sit in float4 slot L ^ (2 (L >> 4) + ((L >> 3) & 1))
+// rather than slot L: each scalar write of the 64 lanes then spreads over all
+// banks instead of 8 of them, and the float4 read back stays conflict-free.
+__device__ __forceinline__ int atile_slot(int L) { return L ^ (2 * (L >> 4) + ((L >> 3) & 1)); }
+
 __device__ __forceinline__ float4 acc_to_atile(const floatx4& acc, float* scratch, int lane)
 {
     const int l16 = lane & 15, q4 = lane >> 4;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        // element (row 4 q4 + e, column l16) belongs to A-lane (l16 / 4) * 16 + 4 q4 + e, slot l16 % 4
-        scratch[((l16 >> 2) * 16 + 4 * q4 + e) * 4 + (l16 & 3)] = acc[e];
+        // element (row 4 q4 + e, column l16) belongs to A-lane (l16 / 4) * 16 + 4 q4 + e, position l16 % 4
+        scratch[atile_slot((l16 >> 2) * 16 + 4 * q4 + e) * 4 + (l16 & 3)] = acc[e];
     }
     __builtin_amdgcn_wave_barrier();
-    const float4 r = lds4(&scratch[lane * 4]);
+    const float4 r = lds4(&scratch[atile_slot(lane) * 4]);
     __builtin_amdgcn_wave_barrier();
     return r;
 }
