@@ -40,7 +40,7 @@ struct RecGeom {
 #endif
 constexpr int kRecSlices = KDA_REC_SLICES;
 
-// State traffic is streamed once per call: non-temporal hints keep it from
+// The carried state is streamed once per call: non-temporal hints keep it from
 // displacing other data in the caches.
 #ifndef KDA_REC_NONTEMPORAL
 #define KDA_REC_NONTEMPORAL 1
@@ -169,9 +169,11 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const float* __restrict_
             s[m].w = fmaf(kr[m], d.w, s[m].w);
         }
         if (t < n_snap) {
+            // snapshots are ordinary (cacheable) stores: a caller verifying
+            // speculative rows reads the accepted one back soon after
             float* snap = snaps + ((size_t)t * batch * heads + bh) * kD * kD;
 #pragma unroll
-            for (int m = 0; m < G::kRows; ++m) state_st(snap + (size_t)(rg + G::kRowGroups * m) * kD + col, s[m]);
+            for (int m = 0; m < G::kRows; ++m) st4(snap + (size_t)(rg + G::kRowGroups * m) * kD + col, s[m]);
         }
     }
 #pragma unroll
