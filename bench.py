@@ -238,6 +238,43 @@ def cpu_baseline(ki, budget_s: float = 12.0):
                       f"{el:.1f} s wall on {threads} threads, os.cpu_count()={os.cpu_count()}"}
 
 
+# ---------------------------------------------------------------- practical HBM ceilings
+def traffic_probe(torch, timer):
+    """The decode kernels' access patterns with none of their arithmetic: each 256-thread
+    workgroup reads one 32 KiB state slice and writes it back in place (decode, B=64 H=32,
+    8 rotated 128 MiB buffers) or to five 256 MiB regions (decode_k, B=128 H=32: 4 snapshots +
+    the state).  GB/s of the bytes moved, best of plain and non-temporal accesses."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "kda_gated_delta_core_amd", "libkda_probe.so"))
+    lib.probe_state_traffic.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p]
+    res = {}
+    units = 64 * 32 * 2
+    bufs = [torch.zeros(units * 8192, device="cuda") for _ in range(8)]
+    best = 0.0
+    for nt in (0, 1):
+        def fn(i, nt=nt):
+            b = bufs[i % 8]
+            assert lib.probe_state_traffic(b.data_ptr(), b.data_ptr(), units, 1, units * 8192, nt, None) == 0
+        r = timer.run(fn, 200, 20)
+        best = max(best, 2 * units * 32768 / r["launch_avg_s"] / 1e9)
+    res["decode_b64_h32_pattern_GB_per_s"] = best
+    del bufs
+    units = 128 * 32 * 2
+    src = torch.zeros(units * 8192, device="cuda")
+    dst = torch.zeros(5 * units * 8192, device="cuda")
+    best = 0.0
+    for nt in (0, 1):
+        def fn(i, nt=nt):
+            assert lib.probe_state_traffic(src.data_ptr(), dst.data_ptr(), units, 5, units * 8192, nt, None) == 0
+        r = timer.run(fn, 50, 5)
+        best = max(best, 6 * units * 32768 / r["launch_avg_s"] / 1e9)
+    res["decode_k4_b128_h32_pattern_GB_per_s"] = best
+    for k, v in res.items():
+        log(f"traffic probe {k}: {v:.0f}")
+    return res
+
+
 # ---------------------------------------------------------------- traffic from committed counters
 def committed_traffic(kernel_src: str, profile: str):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken
@@ -268,6 +305,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--copy-probe", action="store_true", help="time a plain 1 GiB device copy kernel (1 GiB read + 1 GiB written per launch) and exit")
     ap.add_argument("--reps", type=int, default=0, help="override the repetitions of every workload (profiling)")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="time a traffic-only kernel with the decode and decode_k access patterns and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the core needs no collective and "
@@ -287,6 +326,10 @@ def main():
         # an elementwise kernel (not a runtime blit) so counter collection sees it as a dispatch
         r = timer.run(lambda i: torch.mul(src, 1.0, out=dst), args.reps or 20, 0 if args.reps else 3)
         log(f"copy probe: 1 GiB read + 1 GiB write per launch, {2 * n * 4 / r['launch_avg_s'] / 1e9:.1f} GB/s")
+        return
+
+    if args.traffic_probe:
+        print(json.dumps({"traffic_probe": traffic_probe(torch, timer)}), flush=True)
         return
 
     only = set(filter(None, args.only.split(",")))

@@ -10,6 +10,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda_amd.so")
 SOURCES = ["kda_api.cpp", "kda_recurrent.hip", "kda_chunk.hip"]
+# measurement tooling, a library of its own (not part of the KDA C ABI)
+PROBE_LIB = os.path.join(PKG, "libkda_probe.so")
+PROBE_SOURCES = ["kda_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -20,27 +23,32 @@ FLAGS = [
 ]
 
 
-def build(force: bool = True, verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    deps = srcs + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
-    deps.append(os.path.join(ROOT, "include", "kda.h"))
-    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= max(os.path.getmtime(d) for d in deps):
-        return LIB
+def _link(lib: str, sources: list, verbose: bool) -> None:
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = []
-    for s in srcs:
+    for s in sources:
         o = os.path.join(objdir, os.path.basename(s) + ".o")
-        lang = ["-x", "hip"] if s.endswith(".hip") else ["-x", "hip"]
-        cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *lang, "-c", s, "-o", o]
+        cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-x", "hip", "-c", s, "-o", o]
         if verbose:
             print(" ".join(cmd))
         subprocess.run(cmd, check=True)
         objs.append(o)
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    tmp = lib + ".tmp%d" % os.getpid()
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], check=True)
+    os.replace(tmp, lib)
+
+
+def build(force: bool = True, verbose: bool = False) -> str:
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    deps = srcs + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
+    deps.append(os.path.join(ROOT, "include", "kda.h"))
+    probe_srcs = [os.path.join(CSRC, s) for s in PROBE_SOURCES]
+    stale = lambda lib, d: not os.path.exists(lib) or os.path.getmtime(lib) < max(os.path.getmtime(x) for x in d)
+    if force or stale(LIB, deps):
+        _link(LIB, srcs, verbose)
+    if force or stale(PROBE_LIB, probe_srcs):
+        _link(PROBE_LIB, probe_srcs, verbose)
     return LIB
 
 
