@@ -542,38 +542,42 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
 constexpr int kScanThreads = 512;  // 8 waves, two per SIMD
 
 // Operands one wave of the scan reads from a chunk record, prefetched two
-// chunks ahead into registers.  Wave roles inside a chunk (NT = C / 16 row tiles):
+// chunks ahead into registers.  A workgroup owns NCT adjacent 16-column tiles
+// of the value index (16 NCT columns of one head).  Wave roles inside a chunk
+// (NT = C / 16 row tiles):
 //   wave < NT           Delta tile xd = wave:          Delta = U - W S
 //   NT <= wave < 2 NT   output tile xp = wave - NT:    O = P S + R
-//   every wave          state tile `wave`:             S <- diag(gamma) S + Ktil^T Delta
-template <int C>
+//   every wave          state tile row block `wave`:   S <- diag(gamma) S + Ktil^T Delta
+// The A operands (W or P rows, Ktil^T rows) serve all NCT column tiles; each
+// column tile is an independent MFMA chain.
+template <int C, int NCT>
 struct ScanOps {
     static constexpr int NT = C / 16;
-    float4 a[8];     // W rows of the Delta tile, or P rows of the output tile
-    float4 x;        // U tile (Delta waves) or R tile (output waves), accumulator layout
-    float4 kt[NT];   // Ktil^T rows of this wave's state tile
-    float4 g;        // gamma at those rows
+    float4 a[8];       // W rows of the Delta tile, or P rows of the output tile
+    float4 x[NCT];     // U tiles (Delta waves) or R tiles (output waves), accumulator layout
+    float4 kt[NT];     // Ktil^T rows of this wave's state row block
+    float4 g;          // gamma at those rows
 };
 
 // Byte offsets of one wave's operands inside a chunk record; they do not
 // change from chunk to chunk, so they are computed once.
 struct ScanOffsets {
     int a;   // W rows of the Delta tile or P rows of the output tile (8 A tiles, 1 KiB apart)
-    int x;   // U or R tile of this slice
-    int kt;  // Ktil^T rows of the state tile (NT A tiles, 1 KiB apart)
+    int x;   // first U or R tile of this workgroup's columns (NCT tiles, 1 KiB apart)
+    int kt;  // Ktil^T rows of the state row block (NT A tiles, 1 KiB apart)
     int g;   // gamma at those rows
 };
 
 template <int C>
 __device__ __forceinline__ ScanOffsets scan_offsets(bool is_d, int xd, bool is_p, int xp, int wave, int lane, int q4,
-                                                    int slice)
+                                                    int ct0)
 {
     using G = ChunkGeom<C>;
     constexpr int NT = C / 16;
     const int xa = is_d ? xd : (is_p ? xp : 0);
     ScanOffsets o;
     o.a = (int)((is_d ? G::kOffW : G::kOffP) + ((size_t)xa * 8 * 64 + lane) * 4) * 4;
-    o.x = (int)((is_d ? G::kOffU : G::kOffR) + ((size_t)(xa * 8 + slice) * 64 + lane) * 4) * 4;
+    o.x = (int)((is_d ? G::kOffU : G::kOffR) + ((size_t)(xa * 8 + ct0) * 64 + lane) * 4) * 4;
     o.kt = (int)(G::kOffKt + ((size_t)wave * NT * 64 + lane) * 4) * 4;
     o.g = (int)(G::kOffGam + 16 * wave + 4 * q4) * 4;
     return o;
@@ -583,13 +587,14 @@ __device__ __forceinline__ ScanOffsets scan_offsets(bool is_d, int xd, bool is_p
 // its role), so the wait counts the compiler derives stay exact across the
 // loop; the record address lives in scalar registers, so issuing the loads
 // needs no vector registers beyond their destinations.
-template <int C>
-__device__ __forceinline__ void scan_load(ScanOps<C>& o, rsrc_t rec, const ScanOffsets& off)
+template <int C, int NCT>
+__device__ __forceinline__ void scan_load(ScanOps<C, NCT>& o, rsrc_t rec, const ScanOffsets& off)
 {
     constexpr int NT = C / 16;
 #pragma unroll
     for (int tau = 0; tau < 8; ++tau) o.a[tau] = buf_ld4(rec, off.a, tau * 1024);
-    o.x = buf_ld4(rec, off.x, 0);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) o.x[ct] = buf_ld4(rec, off.x, ct * 1024);
 #pragma unroll
     for (int y = 0; y < NT; ++y) o.kt[y] = buf_ld4(rec, off.kt, y * 1024);
     o.g = buf_ld4(rec, off.g, 0);
@@ -597,17 +602,17 @@ __device__ __forceinline__ void scan_load(ScanOps<C>& o, rsrc_t rec, const ScanO
 
 // One chunk of the scan for one wave.  The state lives in LDS only, in two
 // buffers: sIn holds the chunk's incoming state, sOut receives the outgoing
-// one.  Tile s, element e of lane l is S[16 s + 4 (l / 16) + e][v0 + l % 16],
+// one.  Tile (s, ct), element e of lane l is S[16 s + 4 (l / 16) + e][v0 + 16 ct + l % 16],
 // which is directly the B operand of the 16x16x4 MFMA over the key index.
 // The operands of a later chunk are loaded into `nxt` one tile after every
-// four MFMAs, so the compute unit's vector-memory path takes them while the
-// matrix core works instead of in one burst that the waves wait behind.
-template <int C>
-__device__ __forceinline__ void scan_chunk(const ScanOps<C>& cur, ScanOps<C>& nxt, rsrc_t nrec,
-                                           const ScanOffsets& off, floatx4 (*sIn)[64], floatx4 (*sOut)[64],
-                                           floatx4 (*sDelta)[64], float* __restrict__ out_b, int out_voff, int c,
-                                           bool is_d, int xd, bool is_p, int xp, int wave, int lane, int q4,
-                                           int heads, int T)
+// group of MFMAs, so the compute unit's vector-memory path takes them while
+// the matrix core works instead of in one burst that the waves wait behind.
+template <int C, int NCT>
+__device__ __forceinline__ void scan_chunk(const ScanOps<C, NCT>& cur, ScanOps<C, NCT>& nxt, rsrc_t nrec,
+                                           const ScanOffsets& off, floatx4 (*sIn)[NCT][64],
+                                           floatx4 (*sOut)[NCT][64], floatx4 (*sDelta)[NCT][64],
+                                           float* __restrict__ out_b, int out_voff, int c, bool is_d, int xd,
+                                           bool is_p, int xp, int wave, int lane, int q4, int heads, int T)
 {
     constexpr int NT = C / 16;
     // at C = 64 every wave has a role in step A: no branch, so the wait counts
@@ -615,140 +620,176 @@ __device__ __forceinline__ void scan_chunk(const ScanOps<C>& cur, ScanOps<C>& nx
     constexpr bool kAllRoles = 2 * NT == kScanThreads / 64;
     // A. Delta = U - W S (Delta waves) and O = R + P S (output waves)
     if (kAllRoles || is_d || is_p) {
-        floatx4 st[8];
+        floatx4 st[8][NCT];
 #pragma unroll
-        for (int tau = 0; tau < 8; ++tau) st[tau] = sIn[tau][lane];
-        floatx4 acc;
-        acc[0] = is_p ? cur.x.x : 0.f;
-        acc[1] = is_p ? cur.x.y : 0.f;
-        acc[2] = is_p ? cur.x.z : 0.f;
-        acc[3] = is_p ? cur.x.w : 0.f;
+        for (int tau = 0; tau < 8; ++tau)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) st[tau][ct] = sIn[tau][ct][lane];
+        floatx4 acc[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            acc[ct][0] = is_p ? cur.x[ct].x : 0.f;
+            acc[ct][1] = is_p ? cur.x[ct].y : 0.f;
+            acc[ct][2] = is_p ? cur.x[ct].z : 0.f;
+            acc[ct][3] = is_p ? cur.x[ct].w : 0.f;
+        }
 #pragma unroll
         for (int tau = 0; tau < 8; ++tau) {
-            acc = mfma4(cur.a[tau].x, st[tau][0], acc);
-            acc = mfma4(cur.a[tau].y, st[tau][1], acc);
-            acc = mfma4(cur.a[tau].z, st[tau][2], acc);
-            acc = mfma4(cur.a[tau].w, st[tau][3], acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) acc[ct] = mfma4(comp(cur.a[tau], e), st[tau][ct][e], acc[ct]);
             nxt.a[tau] = buf_ld4(nrec, off.a, tau * 1024);
             __builtin_amdgcn_sched_barrier(0);
         }
-        nxt.x = buf_ld4(nrec, off.x, 0);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) nxt.x[ct] = buf_ld4(nrec, off.x, ct * 1024);
         if (is_d) {
-            floatx4 d;
-            d[0] = cur.x.x - acc[0];
-            d[1] = cur.x.y - acc[1];
-            d[2] = cur.x.z - acc[2];
-            d[3] = cur.x.w - acc[3];
-            sDelta[xd][lane] = d;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                floatx4 d;
+                d[0] = cur.x[ct].x - acc[ct][0];
+                d[1] = cur.x[ct].y - acc[ct][1];
+                d[2] = cur.x[ct].z - acc[ct][2];
+                d[3] = cur.x[ct].w - acc[ct][3];
+                sDelta[xd][ct][lane] = d;
+            }
         } else {
-            // rows c C + 16 xp + 4 q4 + e of this sequence's output, columns v0 + l16
+            // rows c C + 16 xp + 4 q4 + e of this sequence's output, columns v0 + 16 ct + l16
             const rsrc_t ob = make_rsrc(out_b + (size_t)c * C * heads * kD, (uint32_t)(C * heads * kD * 4));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = c * C + 16 * xp + 4 * q4 + e;
-                if (t < T) buf_st1(ob, out_voff, e * heads * kD * 4, acc[e]);
+                if (t < T) {
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) buf_st1(ob, out_voff + 64 * ct, e * heads * kD * 4, acc[ct][e]);
+                }
             }
         }
     } else {
 #pragma unroll
         for (int tau = 0; tau < 8; ++tau) nxt.a[tau] = buf_ld4(nrec, off.a, tau * 1024);
-        nxt.x = buf_ld4(nrec, off.x, 0);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) nxt.x[ct] = buf_ld4(nrec, off.x, ct * 1024);
     }
     __syncthreads();
 
-    // B. state tile `wave`
+    // B. state row block `wave`, all NCT column tiles
     {
-        floatx4 dl[NT];
+        floatx4 dl[NT][NCT];
 #pragma unroll
-        for (int y = 0; y < NT; ++y) dl[y] = sDelta[y][lane];
-        const floatx4 so = sIn[wave][lane];
-        floatx4 acc;
-        acc[0] = cur.g.x * so[0];
-        acc[1] = cur.g.y * so[1];
-        acc[2] = cur.g.z * so[2];
-        acc[3] = cur.g.w * so[3];
+        for (int y = 0; y < NT; ++y)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) dl[y][ct] = sDelta[y][ct][lane];
+        floatx4 acc[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const floatx4 so = sIn[wave][ct][lane];
+            acc[ct][0] = cur.g.x * so[0];
+            acc[ct][1] = cur.g.y * so[1];
+            acc[ct][2] = cur.g.z * so[2];
+            acc[ct][3] = cur.g.w * so[3];
+        }
 #pragma unroll
         for (int y = 0; y < NT; ++y) {
-            acc = mfma4(cur.kt[y].x, dl[y][0], acc);
-            acc = mfma4(cur.kt[y].y, dl[y][1], acc);
-            acc = mfma4(cur.kt[y].z, dl[y][2], acc);
-            acc = mfma4(cur.kt[y].w, dl[y][3], acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) acc[ct] = mfma4(comp(cur.kt[y], e), dl[y][ct][e], acc[ct]);
             nxt.kt[y] = buf_ld4(nrec, off.kt, y * 1024);
             __builtin_amdgcn_sched_barrier(0);
         }
         nxt.g = buf_ld4(nrec, off.g, 0);
-        sOut[wave][lane] = acc;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) sOut[wave][ct][lane] = acc[ct];
     }
     __syncthreads();
 }
 
-template <int C>
+// One workgroup per (sequence, head, group of 16 NCT value columns); the 8 / NCT
+// groups of a head are mapped to one XCD (blockIdx % 8) so the head's records
+// are fetched into that XCD's L2 once.
+template <int C, int NCT>
 __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(const float* __restrict__ ws,
                                                                   float* __restrict__ state, float* __restrict__ out,
                                                                   int n_bh, int heads, int T, int t_pad, int nchunks)
 {
     using G = ChunkGeom<C>;
     constexpr int NT = G::kTiles;
-    // blockIdx -> (head, slice) so that all eight slices of a head share an XCD
+    constexpr int kGroups = 8 / NCT;  // column groups per head
     const int n = blockIdx.x;
     const int xcd = n & 7, k8 = n >> 3;
-    const int slice = k8 & 7;
-    const int bh = (k8 >> 3) * 8 + xcd;
+    const int slice = k8 % kGroups;
+    const int bh = (k8 / kGroups) * 8 + xcd;
     if (bh >= n_bh) return;
     const int b = bh / heads, h = bh % heads;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
-    const int v0 = 16 * slice;
+    const int ct0 = NCT * slice, v0 = 16 * ct0;
     const bool is_d = wave < NT, is_p = wave >= NT && wave < 2 * NT;
     const int xd = wave, xp = wave - NT;
 
-    __shared__ floatx4 sDelta[NT][64];
-    __shared__ floatx4 sS[2][8][64];
+    __shared__ floatx4 sDelta[NT][NCT][64];
+    __shared__ floatx4 sS[2][8][NCT][64];
 
     float* const S_head = state + (size_t)bh * kD * kD;
     float* const out_b = out + (size_t)b * t_pad * heads * kD;
     const int out_voff = ((16 * xp + 4 * q4) * heads * kD + h * kD + v0 + l16) * 4;
-    {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
         floatx4 st;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st[e] = S_head[(size_t)(16 * wave + 4 * q4 + e) * kD + v0 + l16];
-        sS[0][wave][lane] = st;
+        for (int e = 0; e < 4; ++e) st[e] = S_head[(size_t)(16 * wave + 4 * q4 + e) * kD + v0 + 16 * ct + l16];
+        sS[0][wave][ct][lane] = st;
     }
     const float* const rec0 = ws + (size_t)bh * nchunks * G::kRecord;
     auto rec = [&](int cc) {
         return make_rsrc(rec0 + (size_t)(cc < nchunks ? cc : nchunks - 1) * G::kRecord, (uint32_t)(G::kRecord * 4));
     };
-    const ScanOffsets off = scan_offsets<C>(is_d, xd, is_p, xp, wave, lane, q4, slice);
+    const ScanOffsets off = scan_offsets<C>(is_d, xd, is_p, xp, wave, lane, q4, ct0);
     // Three operand buffers in rotation: while one chunk is computed, the loads
     // of the next are in flight and those of the one after are being issued
     // (no register copies between the buffers, so no wait on a prefetch
     // before it is needed).
-    ScanOps<C> op0, op1, op2;
-    scan_load<C>(op0, rec(0), off);
-    scan_load<C>(op1, rec(1), off);
+    ScanOps<C, NCT> op0, op1, op2;
+    scan_load<C, NCT>(op0, rec(0), off);
+    scan_load<C, NCT>(op1, rec(1), off);
     __syncthreads();
     // Whole rounds of three chunks, then the remaining one or two: the loop has
     // a single back edge, so the wait counts at its head see only the state in
     // which a round ends.
     int c = 0;
     for (; c + 3 <= nchunks; c += 3) {
-        scan_chunk<C>(op0, op2, rec(c + 2), off, sS[c & 1], sS[(c + 1) & 1], sDelta, out_b, out_voff, c, is_d, xd,
-                      is_p, xp, wave, lane, q4, heads, T);
-        scan_chunk<C>(op1, op0, rec(c + 3), off, sS[(c + 1) & 1], sS[c & 1], sDelta, out_b, out_voff, c + 1, is_d,
-                      xd, is_p, xp, wave, lane, q4, heads, T);
-        scan_chunk<C>(op2, op1, rec(c + 4), off, sS[c & 1], sS[(c + 1) & 1], sDelta, out_b, out_voff, c + 2, is_d,
-                      xd, is_p, xp, wave, lane, q4, heads, T);
+        scan_chunk<C, NCT>(op0, op2, rec(c + 2), off, sS[c & 1], sS[(c + 1) & 1], sDelta, out_b, out_voff, c, is_d,
+                           xd, is_p, xp, wave, lane, q4, heads, T);
+        scan_chunk<C, NCT>(op1, op0, rec(c + 3), off, sS[(c + 1) & 1], sS[c & 1], sDelta, out_b, out_voff, c + 1,
+                           is_d, xd, is_p, xp, wave, lane, q4, heads, T);
+        scan_chunk<C, NCT>(op2, op1, rec(c + 4), off, sS[c & 1], sS[(c + 1) & 1], sDelta, out_b, out_voff, c + 2,
+                           is_d, xd, is_p, xp, wave, lane, q4, heads, T);
     }
     if (c < nchunks)
-        scan_chunk<C>(op0, op2, rec(c + 2), off, sS[c & 1], sS[(c + 1) & 1], sDelta, out_b, out_voff, c, is_d, xd,
-                      is_p, xp, wave, lane, q4, heads, T);
+        scan_chunk<C, NCT>(op0, op2, rec(c + 2), off, sS[c & 1], sS[(c + 1) & 1], sDelta, out_b, out_voff, c, is_d,
+                           xd, is_p, xp, wave, lane, q4, heads, T);
     if (c + 1 < nchunks)
-        scan_chunk<C>(op1, op0, rec(c + 3), off, sS[(c + 1) & 1], sS[c & 1], sDelta, out_b, out_voff, c + 1, is_d,
-                      xd, is_p, xp, wave, lane, q4, heads, T);
+        scan_chunk<C, NCT>(op1, op0, rec(c + 3), off, sS[(c + 1) & 1], sS[c & 1], sDelta, out_b, out_voff, c + 1,
+                           is_d, xd, is_p, xp, wave, lane, q4, heads, T);
     // the final state is in sS[nchunks & 1]
-    const floatx4 st = sS[nchunks & 1][wave][lane];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) S_head[(size_t)(16 * wave + 4 * q4 + e) * kD + v0 + l16] = st[e];
+    for (int ct = 0; ct < NCT; ++ct) {
+        const floatx4 st = sS[nchunks & 1][wave][ct][lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S_head[(size_t)(16 * wave + 4 * q4 + e) * kD + v0 + 16 * ct + l16] = st[e];
+    }
+}
+
+template <int C, int NCT>
+static int launch_scan(const float* ws, float* state, float* out, long long n_bh, int heads, int T, int t_pad,
+                       int nchunks, hipStream_t stream)
+{
+    const unsigned grid = (unsigned)(((n_bh + 7) / 8) * 64 / NCT);
+    hipLaunchKernelGGL((chunk_scan_kernel<C, NCT>), dim3(grid), dim3(kScanThreads), 0, stream, ws, state, out,
+                       (int)n_bh, heads, T, t_pad, nchunks);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 template <int C>
@@ -768,10 +809,14 @@ static int launch_chunk(const float* q, const float* k, const float* v, const fl
     hipLaunchKernelGGL(chunk_prepare_kernel<C>, dim3((unsigned)grid_p), dim3(kPrepThreads), 0, stream, q, k, v,
                        gate, beta, ws, heads, T, t_pad, nchunks, n_total);
     if (hipGetLastError() != hipSuccess) return -1;
-    const unsigned grid = (unsigned)(((n_bh + 7) / 8) * 64);
-    hipLaunchKernelGGL(chunk_scan_kernel<C>, dim3(grid), dim3(kScanThreads), 0, stream, ws, state, out, (int)n_bh, heads, T,
-                       t_pad, nchunks);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
+    // 32-column workgroups when 16-column ones would not fit the compute units
+    // in one round and 32-column ones still fill them (results are the same
+    // bits either way: value columns never mix)
+    if constexpr (C == 64) {
+        if (n_bh * 8 > n_cu && n_bh * 4 >= n_cu)
+            return launch_scan<C, 2>(ws, state, out, n_bh, heads, T, t_pad, nchunks, stream);
+    }
+    return launch_scan<C, 1>(ws, state, out, n_bh, heads, T, t_pad, nchunks, stream);
 }
 
 int launch_chunk_prefill(const float* q, const float* k, const float* v, const float* gate, const float* beta,

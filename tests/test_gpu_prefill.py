@@ -226,3 +226,15 @@ def test_prefill_b4_t32768_then_decode_full_size(device):
         o2, s2, _, _ = oracle.serial(tsub["q"], tsub["k"], tsub["v"], tsub["gate"], tsub["beta"], s_ref)
         assert_close(f"b{b} h{h} decode tail core", tail_out[b:b + 1, :, h:h + 1], o2)
         assert_close(f"b{b} h{h} final state", st_end[b:b + 1, h:h + 1], s2)
+
+
+@pytest.mark.parametrize("B,H,T", [(2, 32, 200), (3, 25, 130)])
+def test_prefill_wide_column_groups(device, B, H, T):
+    """Enough (sequence, head) pairs that, on a 256-CU part, the scan takes 32 value columns per
+    workgroup (B*H*8 > 256 >= ... B*H*4); B*H = 75 also leaves a partly filled XCD group."""
+    import kda_gated_delta_core_amd as kda
+    C = 64
+    announce(f"kda_chunk_prefill B={B} H={H} T={T} C={C}")
+    x = ki.make_batch(7001 + B, B, H, T, -5.0, 0.02, alloc_rows=-(-T // C) * C, pad_value=float("nan"))
+    out, st, _ = _prefill(kda, x, T, C)
+    _check_against_oracle(x, T, out, st)
