@@ -242,11 +242,12 @@ __device__ __forceinline__ float4 acc_to_atile(const floatx4& acc, float* scratc
     return r;
 }
 
-__device__ __forceinline__ void pair_of(int p, int& R, int& S)
+// block pair (R, S < R) with below-diagonal index j (the inverse of below_index)
+__device__ __forceinline__ void below_pair(int j, int& R, int& S)
 {
-    R = 0;
-    while ((R + 1) * (R + 2) / 2 <= p) ++R;
-    S = p - R * (R + 1) / 2;
+    R = 1;
+    while (R * (R + 1) / 2 <= j) ++R;
+    S = j - R * (R - 1) / 2;
 }
 
 // Persistent: one workgroup per CU walks the chunks gc = blockIdx.x, +gridDim.x, ...
@@ -262,14 +263,19 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
     using G = ChunkGeom<C>;
     constexpr int NT = G::kTiles, LD = G::kLd, LDC = G::kLdc;
     constexpr int NW = kPrepThreads / 64;
-    constexpr int kSplit = G::kPairs > NW ? G::kPairs - NW : 0;  // pairs computed in two channel halves
-    static_assert(PrepInputs<C>::NV4 >= 1 && NW == 8 && kSplit <= 2, "geometry");
+    // block pairs below the diagonal: the first four whole on waves 0..3, the rest
+    // in two channel halves on waves 0..2 kSplit-1; diagonal pair R on wave 4 + R
+    constexpr int kBelow = NT * (NT - 1) / 2;
+    constexpr int kSplit = kBelow > 4 ? kBelow - 4 : 0;
+    constexpr int LDT = 20;  // row stride of the inverted diagonal blocks
+    static_assert(PrepInputs<C>::NV4 >= 1 && NW == 8 && NT <= 4 && kSplit <= 2, "geometry");
     constexpr int NX = NT > 1 ? NT * (NT - 1) / 2 : 1;  // block pairs below the diagonal
     __shared__ float sKr[C * LD];    // K, then K o 2^(L - L7)
     __shared__ float sQr[C * LD];    // Q, then Q o 2^(L - L7)
     __shared__ float sKc[C * LD];    // log2 gates, then K o 2^(L7 - L); transpose scratch after step 3
     __shared__ float sA[C * LDC];    // beta-scaled strictly lower A
-    __shared__ float sT[C * LDC];    // diagonal blocks of (I + A)^-1; before that, partial tiles of the split pairs
+    __shared__ float sTd[NT * 16 * LDT];  // the inverted diagonal blocks (I + A_RR)^-1
+    __shared__ floatx4 sPart[(kSplit > 0 ? kSplit : 1) * 2 * 64];  // first channel halves of the split pairs
     __shared__ float sM[C * LDC];    // lower-triangular decayed Q K^T
     __shared__ float sE[NT * kD];    // 2^(G7_R)          (L7 of each block during step 2)
     __shared__ float sF[NT * kD];    // 2^(Glast - G7_R)  (block totals during step 2)
@@ -278,7 +284,6 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
     __shared__ float sBeta[C];
 
     const int stride = gridDim.x;
-    floatx4* const sPart = reinterpret_cast<floatx4*>(sT);  // [kSplit][2][64]
 
     auto row0_of = [&](int gc) {
         const int bh = gc / nchunks, c = gc % nchunks;
@@ -375,22 +380,45 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         }
         __syncthreads();
 
-        // 3a. A and M on the 16x16 block pairs (R, S <= R): one pair per wave, the
-        //     pairs beyond the eighth in two channel halves on waves 0..2 kSplit-1
+        // 3a. A and M on the 16x16 block pairs (R, S <= R).  Waves 4.. take the
+        //     diagonal pairs and, as soon as their block of A is in LDS, invert
+        //     it, (I + A_RR)^-1 by forward substitution (one lane per column),
+        //     while waves 0..3 are still on the pairs below the diagonal.
         __builtin_amdgcn_sched_barrier(0);
         prep_load_part<C>(in.k, nsrc.k, heads, tid);
         __builtin_amdgcn_sched_barrier(0);
         int R, S;
-        if (wave < G::kPairs) {
+        if (wave >= 4) {
+            R = S = wave - 4;
+            if (R < NT) {
+                floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
+                am_pair<C, 0, 8>(R, S, sKr, sQr, sKc, sX, sY, l16, q4, accA, accM);
+                am_store<C>(R, S, accA, accM, sA, sM, sBeta, l16, q4);
+                __builtin_amdgcn_wave_barrier();  // the wave reads back the block it wrote
+                if (lane < 16) {
+                    const int base = 16 * R;
+                    float x[16];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        float acc = (i == lane) ? 1.f : 0.f;
+#pragma unroll
+                        for (int m = 0; m < i; ++m) acc = fmaf(-sA[(base + i) * LDC + base + m], x[m], acc);
+                        x[i] = acc;
+                    }
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sTd[(16 * R + i) * LDT + lane] = x[i];
+                }
+            }
+        } else if (wave < kBelow) {
             floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
-            pair_of(wave, R, S);
+            below_pair(wave, R, S);
             am_pair<C, 0, 8>(R, S, sKr, sQr, sKc, sX, sY, l16, q4, accA, accM);
             am_store<C>(R, S, accA, accM, sA, sM, sBeta, l16, q4);
         }
         floatx4 hA = {0.f, 0.f, 0.f, 0.f}, hM = {0.f, 0.f, 0.f, 0.f};
         const bool split = wave < 2 * kSplit;
         if (split) {
-            pair_of(NW + (wave >> 1), R, S);
+            below_pair(4 + (wave >> 1), R, S);
             if (wave & 1) am_pair<C, 4, 8>(R, S, sKr, sQr, sKc, sX, sY, l16, q4, hA, hM);
             else {
                 am_pair<C, 0, 4>(R, S, sKr, sQr, sKc, sX, sY, l16, q4, hA, hM);
@@ -432,21 +460,6 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         }
         __syncthreads();
 
-        // 4a. T_RR = (I + A_RR)^-1 for each diagonal block, by forward substitution
-        if (wave < NT && lane < 16) {
-            const int base = 16 * wave;
-            float x[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float acc = (i == lane) ? 1.f : 0.f;
-#pragma unroll
-                for (int m = 0; m < i; ++m) acc = fmaf(-sA[(base + i) * LDC + base + m], x[m], acc);
-                x[i] = acc;
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sT[(base + i) * LDC + base + lane] = x[i];
-        }
-        __syncthreads();
         // 4c. right-hand sides of W and U in the B-operand layout of this wave's
         //     column block: beta e^G o K and beta V at rows 16 y + 4 q4 + e, and
         //     e^G o Q at the same positions (the accumulator layout of the P tiles)
@@ -493,7 +506,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
                     zu = mfma4(-comp(a4, e), ut[Y][e], zu);
                 }
             }
-            const float4 t4 = lds4(&sT[(16 * X + l16) * LDC + 16 * X + 4 * q4]);
+            const float4 t4 = lds4(&sTd[(16 * X + l16) * LDT + 4 * q4]);
             floatx4 accW = {0.f, 0.f, 0.f, 0.f}, accU = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
