@@ -95,6 +95,8 @@ size_t kda_chunk_prefill_workspace_bytes(int batch, int heads, int T, int chunk)
  *   chunk         : 16, 32 or 64 (changes rounding only, never the result beyond it)
  *   workspace     : device scratch of at least kda_chunk_prefill_workspace_bytes() bytes
  *   heads         : at most KDA_PREFILL_MAX_HEADS (else KDA_ERR_INVALID_ARG)
+ *   batch * heads * T_pad / chunk (the number of chunk records) at most 2^30
+ *                   (else KDA_ERR_INVALID_ARG)
  *
  * Rows t >= T of every input may hold anything, NaN and inf included: the
  * kernels select them away before any arithmetic (layer page,

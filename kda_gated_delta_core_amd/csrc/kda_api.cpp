@@ -93,6 +93,7 @@ KDA_API int kda_chunk_prefill(const float* q, const float* k, const float* v, co
     if (need < 0 || vec < 0 || sca < 0 || st < 0 || t_pad > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
     if ((int64_t)batch * heads > 0x7fffffffLL / 64) return KDA_ERR_INVALID_ARG;  // scan grid
     if (heads > KDA_PREFILL_MAX_HEADS) return KDA_ERR_INVALID_ARG;  // 32-bit in-chunk byte offsets
+    if ((int64_t)batch * heads * (t_pad / chunk) > (1LL << 30)) return KDA_ERR_INVALID_ARG;  // chunk index
     if (!workspace || workspace_bytes < (size_t)need) return KDA_ERR_WORKSPACE;
     const Range r[] = {{out, vec * 4}, {state, st * 4}, {workspace, need}, {q, vec * 4}, {k, vec * 4},
                        {v, vec * 4},   {gate, vec * 4}, {beta, sca * 4}};

@@ -89,6 +89,14 @@ def test_prefill_refusals(lib):
         kda.KDA_ERR_INVALID_ARG
     # more heads than the in-chunk offsets allow
     assert lib.kda_chunk_prefill(*P[:7], 1, 16385, 64, 16, P[7], 1 << 40, None) == kda.KDA_ERR_INVALID_ARG
+    # more chunk records than the chunk index allows: 1024 x 16 x (2^16 + 1) chunks of 16 rows
+    # (fake buffers 2^52 bytes apart, so only that limit can refuse the call)
+    far = [(i + 1) << 52 for i in range(8)]
+    args = (1 << 10, 1 << 4, (1 << 16) * 16 + 1, 16)
+    assert kda.kda_chunk_prefill_workspace_bytes(*args) > 0
+    assert lib.kda_chunk_prefill(*far[:7], *args, far[7], 1 << 62, None) == kda.KDA_ERR_INVALID_ARG
+    args = (1 << 10, 1 << 4, (1 << 16) * 16, 16)  # exactly 2^30 records: accepted up to the launch
+    assert lib.kda_chunk_prefill_workspace_bytes(*args) > 0
 
 
 def test_recurrent_refusals(lib):
