@@ -17,15 +17,16 @@
 //                   Ktil^T = (e^{G_last - G} o K)^T,  gamma = e^{G_last}.
 //                 (O = (e^G o Q) S + M (U - W S) = P S + R, so the output no
 //                 longer waits for Delta inside the scan.)
-//  chunk_scan     one workgroup per (sequence, head, 16-column value slice),
-//                 serial over chunks, its 128x16 state slice resident on chip.
-//                 Per chunk:
+//  chunk_scan     one workgroup per (sequence, head, group of 16 or 32 value
+//                 columns), serial over chunks, its 128-row state slice
+//                 resident on chip.  Per chunk:
 //                   Delta = U - W S,  O = P S + R,
 //                   S <- diag(gamma) S + Ktil^T Delta
 //                 all as 16x16x4 FP32 MFMA tiles.  Value columns never mix, so
-//                 the eight slices of a head run independently; they are
-//                 placed on one XCD so the head's records are fetched into
-//                 that XCD's L2 once.
+//                 the column groups of a head run independently (and the group
+//                 width does not change a bit of the result); they are placed
+//                 on one XCD so the head's records are fetched into that XCD's
+//                 L2 once.
 //
 // Decay handling: the gate is accumulated in log2 units, separately inside
 // each 16-row block (L), so no running sum grows beyond 16 gates.  One pass
