@@ -102,11 +102,13 @@ size_t kda_chunk_prefill_workspace_bytes(int batch, int heads, int T, int chunk)
  * kernels select them away before any arithmetic (layer page,
  * prefill_with_pad_fill: positions at or past t are ignored in-kernel).
  * Accuracy: the chunk factorisation splits each pairwise decay
- * exp(G_r - G_s) into two factors taken about a reference row at most 8
- * rows away, so every factor stays finite as long as the gates of any 8
- * consecutive tokens sum to more than -88 per channel (for instance every
- * gate >= -11); the pages bound the gate from below (config page,
- * gate_lower_bound).
+ * exp(G_r - G_s) inside a 16-token block into two FP32 factors taken about
+ * the block's eighth row, so a factor can span 8 gates.  Results meet the
+ * stated tolerance for every gate >= -9 (tested there); from about -11 on,
+ * factors leave the normal FP32 range and the output loses accuracy (the
+ * final state does not).  The pages bound the gate from below (config page,
+ * gate_lower_bound) without printing the value; the decode entry points
+ * have no such limit.
  */
 int kda_chunk_prefill(const float* q, const float* k, const float* v, const float* gate, const float* beta,
                       float* state, float* out, int batch, int heads, int T, int chunk, void* workspace,

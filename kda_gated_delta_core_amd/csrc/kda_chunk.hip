@@ -32,7 +32,9 @@
 // each 16-row block (L), so no running sum grows beyond 16 gates.  One pass
 // turns K and Q into tables decayed about row 7 of their own block,
 //   Kr = K o 2^(L - L7),  Qr = Q o 2^(L - L7),  Kc = K o 2^(L7 - L)
-// (each factor spans at most 8 gates), with two exponentials per element.
+// (each factor spans at most 8 gates, so it stays a normal float for gates
+// down to about -9; below that the diagonal terms flush), with two
+// exponentials per element.
 // Everything else needs only per-channel factors on top of those tables:
 //   diagonal blocks of A, M   Kr Kc^T, Qr Kc^T              (no rescaling)
 //   block pair S < R          (Kr o X_RS)(Kc o Y_S)^T      X_RS = 2^(G7_R - Gend_S),

@@ -238,3 +238,23 @@ def test_prefill_wide_column_groups(device, B, H, T):
     x = ki.make_batch(7001 + B, B, H, T, -5.0, 0.02, alloc_rows=-(-T // C) * C, pad_value=float("nan"))
     out, st, _ = _prefill(kda, x, T, C)
     _check_against_oracle(x, T, out, st)
+
+
+@pytest.mark.parametrize("C", [16, 64])
+def test_prefill_gate_domain_edges(device, C):
+    """Gates at the edge of the chunked path's stated domain (every gate >= -9): channels at
+    exactly -9 on every row, at 0, alternating runs, gates drawn on [-9, 0]; beta outside
+    [0, 1] as well (any finite beta is allowed)."""
+    import kda_gated_delta_core_amd as kda
+    B, H, T = 2, 3, 150
+    announce(f"kda_chunk_prefill gate-domain edges C={C}")
+    t_pad = -(-T // C) * C
+    x = ki.make_batch(8100 + C, B, H, T, -9.0, 0.02, alloc_rows=t_pad, pad_value=-1e30)
+    x["gate"][0, :T, :, :16] = -9.0           # strongest decay allowed, every row
+    x["gate"][0, :T, :, 16:32] = 0.0          # no decay
+    x["gate"][1, :T:2, 1, :] = -9.0           # alternating strong / drawn decay
+    x["gate"][1, :T, 2, 64:] = -9.0
+    x["beta"][1, :T, 2] = 1.7
+    x["beta"][0, :T, 1] = -0.3
+    out, st, _ = _prefill(kda, x, T, C)
+    _check_against_oracle(x, T, out, st)
