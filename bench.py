@@ -240,35 +240,35 @@ def cpu_baseline(ki, budget_s: float = 12.0):
 
 # ---------------------------------------------------------------- practical HBM ceilings
 def traffic_probe(torch, timer):
-    """The decode kernels' access patterns with none of their arithmetic: each 256-thread
-    workgroup reads one 32 KiB state slice and writes it back in place (decode, B=64 H=32,
-    8 rotated 128 MiB buffers) or to five 256 MiB regions (decode_k, B=128 H=32: 4 snapshots +
-    the state).  GB/s of the bytes moved, best of plain and non-temporal accesses."""
+    """The decode kernel's state access pattern with none of its arithmetic (libkda_probe.so):
+    each head state is read and written back in place (decode, B=64 H=32, 8 rotated 128 MiB
+    buffers) or written to five 256 MiB regions (decode_k, B=128 H=32: 4 snapshots + the
+    state).  GB/s of the bytes moved, best of plain and non-temporal accesses."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "kda_gated_delta_core_amd", "libkda_probe.so"))
     lib.probe_state_traffic.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p]
     res = {}
-    units = 64 * 32 * 2
-    bufs = [torch.zeros(units * 8192, device="cuda") for _ in range(8)]
+    heads = 64 * 32
+    bufs = [torch.zeros(heads * 16384, device="cuda") for _ in range(8)]
     best = 0.0
     for nt in (0, 1):
         def fn(i, nt=nt):
             b = bufs[i % 8]
-            assert lib.probe_state_traffic(b.data_ptr(), b.data_ptr(), units, 1, units * 8192, nt, None) == 0
+            assert lib.probe_state_traffic(b.data_ptr(), b.data_ptr(), heads, 1, heads * 16384, nt, None) == 0
         r = timer.run(fn, 200, 20)
-        best = max(best, 2 * units * 32768 / r["launch_avg_s"] / 1e9)
+        best = max(best, 2 * heads * 65536 / r["launch_avg_s"] / 1e9)
     res["decode_b64_h32_pattern_GB_per_s"] = best
     del bufs
-    units = 128 * 32 * 2
-    src = torch.zeros(units * 8192, device="cuda")
-    dst = torch.zeros(5 * units * 8192, device="cuda")
+    heads = 128 * 32
+    src = torch.zeros(heads * 16384, device="cuda")
+    dst = torch.zeros(5 * heads * 16384, device="cuda")
     best = 0.0
     for nt in (0, 1):
         def fn(i, nt=nt):
-            assert lib.probe_state_traffic(src.data_ptr(), dst.data_ptr(), units, 5, units * 8192, nt, None) == 0
+            assert lib.probe_state_traffic(src.data_ptr(), dst.data_ptr(), heads, 5, heads * 16384, nt, None) == 0
         r = timer.run(fn, 50, 5)
-        best = max(best, 6 * units * 32768 / r["launch_avg_s"] / 1e9)
+        best = max(best, 6 * heads * 65536 / r["launch_avg_s"] / 1e9)
     res["decode_k4_b128_h32_pattern_GB_per_s"] = best
     for k, v in res.items():
         log(f"traffic probe {k}: {v:.0f}")

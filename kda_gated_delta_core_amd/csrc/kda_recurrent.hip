@@ -11,8 +11,10 @@
 // passes).  A workgroup owns one (sequence, head, value slice); its 256
 // threads load the slice of the 64 KiB head state straight into VGPRs with
 // 16-byte loads (thread = 4 adjacent value columns x kRows key rows, a wave
-// covers whole 512-byte rows), keep it there for all rows of the walk, and
-// write it back once.  Per row the only cross-thread traffic is the
+// covers whole 128-byte row segments), keep it there for all rows of the walk,
+// and write it back once.  The slices of one head go to blocks 8 apart, which
+// the dispatcher places on the same XCD, so each 512-byte state row is read
+// and written through one L2.  Per row the only cross-thread traffic is the
 // reduction of the read-outs over the key index: a xor-shuffle across the
 // row groups inside the wave plus one LDS exchange across the four waves.
 // No atomics: every thread sums in the same fixed order, so results are
@@ -36,7 +38,7 @@ struct RecGeom {
 // Value slices per head.  Part of the arithmetic contract: the reduction tree
 // depends on it, and both decode entry points use this one instance.
 #ifndef KDA_REC_SLICES
-#define KDA_REC_SLICES 2
+#define KDA_REC_SLICES 4
 #endif
 constexpr int kRecSlices = KDA_REC_SLICES;
 
@@ -78,8 +80,11 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const float* __restrict_
 {
     using G = RecGeom<NSLICE>;
     const int tid = threadIdx.x;
-    const int slice = blockIdx.x % NSLICE;
-    const int bh = blockIdx.x / NSLICE;  // b * heads + h
+    // blocks come in groups of 8 * NSLICE: 8 heads, slice s of head j at 8 s + j
+    const int r = blockIdx.x % (8 * NSLICE);
+    const int slice = r / 8;
+    const int bh = blockIdx.x / (8 * NSLICE) * 8 + r % 8;  // b * heads + h
+    if (bh >= batch * heads) return;  // padding of the last group (the whole block leaves)
     const int b = bh / heads, h = bh % heads;
     const int cg = tid % G::kColGroups;
     const int rg = tid / G::kColGroups;
@@ -184,12 +189,12 @@ int launch_recurrent(const float* q, const float* k, const float* v, const float
                      float* state, float* out, float* snaps, int n_snap, int batch, int heads, int T,
                      hipStream_t stream)
 {
-    const unsigned grid = (unsigned)batch * (unsigned)heads * kRecSlices;
+    const unsigned grid = ((unsigned)batch * (unsigned)heads + 7u) / 8u * 8u * kRecSlices;
     hipLaunchKernelGGL(recurrent_kernel<kRecSlices>, dim3(grid), dim3(256), 0, stream, q, k, v, gate, beta, state,
                        out, snaps, n_snap, batch, heads, T);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-long long recurrent_max_units() { return 0x7fffffffLL / kRecSlices; }
+long long recurrent_max_units() { return 0x7fffffffLL / kRecSlices - 8; }
 
 }  // namespace kda
