@@ -556,6 +556,8 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
 }
 
 constexpr int kScanThreads = 512;  // 8 waves, two per SIMD
+constexpr int kOutRow = 20;                // LDS row stride (floats) of a staged 16x16 output tile
+constexpr int kOutTile = 16 * kOutRow;
 
 // Operands one wave of the scan reads from a chunk record, prefetched two
 // chunks ahead into registers.  A workgroup owns NCT adjacent 16-column tiles
@@ -564,6 +566,10 @@ constexpr int kScanThreads = 512;  // 8 waves, two per SIMD
 //   wave < NT           Delta tile xd = wave:          Delta = U - W S
 //   NT <= wave < 2 NT   output tile xp = wave - NT:    O = P S + R
 //   every wave          state tile row block `wave`:   S <- diag(gamma) S + Ktil^T Delta
+//   wave < NT           after that, stores output tile xd (staged in LDS by
+//                       the output wave): the output waves are the younger
+//                       ones on each SIMD, whose MFMAs issue last, so the
+//                       stores go to the waves that wait for them.
 // The A operands (W or P rows, Ktil^T rows) serve all NCT column tiles; each
 // column tile is an independent MFMA chain.
 template <int C, int NCT>
@@ -627,8 +633,9 @@ template <int C, int NCT>
 __device__ __forceinline__ void scan_chunk(const ScanOps<C, NCT>& cur, ScanOps<C, NCT>& nxt, rsrc_t nrec,
                                            const ScanOffsets& off, floatx4 (*sIn)[NCT][64],
                                            floatx4 (*sOut)[NCT][64], floatx4 (*sDelta)[NCT][64],
-                                           float* __restrict__ out_b, int out_voff, int c, bool is_d, int xd,
-                                           bool is_p, int xp, int wave, int lane, int q4, int heads, int T)
+                                           float (*sO)[NCT][kOutTile], float* __restrict__ out_b, int out_voff,
+                                           int c, bool is_d, int xd, bool is_p, int xp, int wave, int lane, int q4,
+                                           int heads, int T)
 {
     constexpr int NT = C / 16;
     // at C = 64 every wave has a role in step A: no branch, so the wait counts
@@ -641,23 +648,33 @@ __device__ __forceinline__ void scan_chunk(const ScanOps<C, NCT>& cur, ScanOps<C
         for (int tau = 0; tau < 8; ++tau)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) st[tau][ct] = sIn[tau][ct][lane];
-        floatx4 acc[NCT];
+        __builtin_amdgcn_sched_barrier(0);  // all eight reads in flight before the first MFMA
+        // two independent accumulation chains per column tile (even and odd
+        // key steps), so that a wave left alone on its SIMD still keeps the
+        // matrix core busy instead of waiting out each MFMA's latency
+        floatx4 acc[NCT], acc2[NCT];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             acc[ct][0] = is_p ? cur.x[ct].x : 0.f;
             acc[ct][1] = is_p ? cur.x[ct].y : 0.f;
             acc[ct][2] = is_p ? cur.x[ct].z : 0.f;
             acc[ct][3] = is_p ? cur.x[ct].w : 0.f;
+            acc2[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int tau = 0; tau < 8; ++tau) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+            for (int e = 0; e < 4; e += 2)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) acc[ct] = mfma4(comp(cur.a[tau], e), st[tau][ct][e], acc[ct]);
+                for (int ct = 0; ct < NCT; ++ct) {
+                    acc[ct] = mfma4(comp(cur.a[tau], e), st[tau][ct][e], acc[ct]);
+                    acc2[ct] = mfma4(comp(cur.a[tau], e + 1), st[tau][ct][e + 1], acc2[ct]);
+                }
             nxt.a[tau] = buf_ld4(nrec, off.a, tau * 1024);
             __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) acc[ct] += acc2[ct];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) nxt.x[ct] = buf_ld4(nrec, off.x, ct * 1024);
         if (is_d) {
@@ -671,16 +688,13 @@ __device__ __forceinline__ void scan_chunk(const ScanOps<C, NCT>& cur, ScanOps<C
                 sDelta[xd][ct][lane] = d;
             }
         } else {
-            // rows c C + 16 xp + 4 q4 + e of this sequence's output, columns v0 + 16 ct + l16
-            const rsrc_t ob = make_rsrc(out_b + (size_t)c * C * heads * kD, (uint32_t)(C * heads * kD * 4));
+            // output tile xp to LDS, row-major (row stride kOutRow: the 64
+            // lanes' writes of one element e hit 64 different banks)
+            const int l16 = lane & 15;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = c * C + 16 * xp + 4 * q4 + e;
-                if (t < T) {
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) buf_st1(ob, out_voff + 64 * ct, e * heads * kD * 4, acc[ct][e]);
-                }
-            }
+                for (int e = 0; e < 4; ++e) sO[xp][ct][(4 * q4 + e) * kOutRow + l16] = acc[ct][e];
         }
     } else {
 #pragma unroll
@@ -697,7 +711,7 @@ __device__ __forceinline__ void scan_chunk(const ScanOps<C, NCT>& cur, ScanOps<C
         for (int y = 0; y < NT; ++y)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) dl[y][ct] = sDelta[y][ct][lane];
-        floatx4 acc[NCT];
+        floatx4 acc[NCT], acc2[NCT];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             const floatx4 so = sIn[wave][ct][lane];
@@ -705,19 +719,37 @@ __device__ __forceinline__ void scan_chunk(const ScanOps<C, NCT>& cur, ScanOps<C
             acc[ct][1] = cur.g.y * so[1];
             acc[ct][2] = cur.g.z * so[2];
             acc[ct][3] = cur.g.w * so[3];
+            acc2[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int y = 0; y < NT; ++y) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+            for (int e = 0; e < 4; e += 2)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) acc[ct] = mfma4(comp(cur.kt[y], e), dl[y][ct][e], acc[ct]);
+                for (int ct = 0; ct < NCT; ++ct) {
+                    acc[ct] = mfma4(comp(cur.kt[y], e), dl[y][ct][e], acc[ct]);
+                    acc2[ct] = mfma4(comp(cur.kt[y], e + 1), dl[y][ct][e + 1], acc2[ct]);
+                }
             nxt.kt[y] = buf_ld4(nrec, off.kt, y * 1024);
             __builtin_amdgcn_sched_barrier(0);
         }
         nxt.g = buf_ld4(nrec, off.g, 0);
 #pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) acc[ct] += acc2[ct];
+#pragma unroll
         for (int ct = 0; ct < NCT; ++ct) sOut[wave][ct][lane] = acc[ct];
+    }
+    // C. output tile xd: row lane / 4 of the tile, columns 4 (lane % 4) + 0..3 of
+    // each 16-column tile, one 16-byte store per lane and column tile
+    if (is_d) {
+        const int r = lane >> 2, j = lane & 3;
+        const int t = c * C + 16 * xd + r;
+        if (t < T) {
+            const rsrc_t ob = make_rsrc(out_b + (size_t)c * C * heads * kD, (uint32_t)(C * heads * kD * 4));
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+                buf_st4(ob, out_voff, 64 * ct, lds4(&sO[xd][ct][r * kOutRow + 4 * j]));
+        }
     }
     __syncthreads();
 }
@@ -747,10 +779,13 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(const float* _
 
     __shared__ floatx4 sDelta[NT][NCT][64];
     __shared__ floatx4 sS[2][8][NCT][64];
+    __shared__ __attribute__((aligned(16))) float sO[NT][NCT][kOutTile];
 
     float* const S_head = state + (size_t)bh * kD * kD;
     float* const out_b = out + (size_t)b * t_pad * heads * kD;
-    const int out_voff = ((16 * xp + 4 * q4) * heads * kD + h * kD + v0 + l16) * 4;
+    // byte offset of this lane's output row (16 xd + lane / 4) and columns
+    // v0 + 4 (lane % 4) + 0..3 inside a chunk's output rows
+    const int out_voff = ((16 * xd + (lane >> 2)) * heads * kD + h * kD + v0 + 4 * (lane & 3)) * 4;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
         floatx4 st;
@@ -776,18 +811,18 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(const float* _
     // which a round ends.
     int c = 0;
     for (; c + 3 <= nchunks; c += 3) {
-        scan_chunk<C, NCT>(op0, op2, rec(c + 2), off, sS[c & 1], sS[(c + 1) & 1], sDelta, out_b, out_voff, c, is_d,
+        scan_chunk<C, NCT>(op0, op2, rec(c + 2), off, sS[c & 1], sS[(c + 1) & 1], sDelta, sO, out_b, out_voff, c, is_d,
                            xd, is_p, xp, wave, lane, q4, heads, T);
-        scan_chunk<C, NCT>(op1, op0, rec(c + 3), off, sS[(c + 1) & 1], sS[c & 1], sDelta, out_b, out_voff, c + 1,
+        scan_chunk<C, NCT>(op1, op0, rec(c + 3), off, sS[(c + 1) & 1], sS[c & 1], sDelta, sO, out_b, out_voff, c + 1,
                            is_d, xd, is_p, xp, wave, lane, q4, heads, T);
-        scan_chunk<C, NCT>(op2, op1, rec(c + 4), off, sS[c & 1], sS[(c + 1) & 1], sDelta, out_b, out_voff, c + 2,
+        scan_chunk<C, NCT>(op2, op1, rec(c + 4), off, sS[c & 1], sS[(c + 1) & 1], sDelta, sO, out_b, out_voff, c + 2,
                            is_d, xd, is_p, xp, wave, lane, q4, heads, T);
     }
     if (c < nchunks)
-        scan_chunk<C, NCT>(op0, op2, rec(c + 2), off, sS[c & 1], sS[(c + 1) & 1], sDelta, out_b, out_voff, c, is_d,
+        scan_chunk<C, NCT>(op0, op2, rec(c + 2), off, sS[c & 1], sS[(c + 1) & 1], sDelta, sO, out_b, out_voff, c, is_d,
                            xd, is_p, xp, wave, lane, q4, heads, T);
     if (c + 1 < nchunks)
-        scan_chunk<C, NCT>(op1, op0, rec(c + 3), off, sS[(c + 1) & 1], sS[c & 1], sDelta, out_b, out_voff, c + 1,
+        scan_chunk<C, NCT>(op1, op0, rec(c + 3), off, sS[(c + 1) & 1], sS[c & 1], sDelta, sO, out_b, out_voff, c + 1,
                            is_d, xd, is_p, xp, wave, lane, q4, heads, T);
     // the final state is in sS[nchunks & 1]
 #pragma unroll
