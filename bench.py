@@ -7,7 +7,8 @@ sequences x 32 heads, FP32 128x128 key-major state per head updated in place
 The same run also times the other workloads of the core and reports each
 under ``workloads``: the T=8192 chunked prefill, the k=4 decode_k with
 snapshots, the 4 x 32768 long-context prefill followed by 16 decode steps,
-and the small T=64 prefill.
+the small T=64 prefill, and the sigmoid-gated RMSNorm that follows the core
+(kda_gated_rmsnorm) on the output of the T=8192 prefill and of a decode step.
 
 Inputs are seeded synthetic tensors (kda_inputs) resident in HBM before the
 timed region.  Decode states are rotated over buffers totalling >= 1 GiB so
@@ -125,6 +126,30 @@ def bench_decode_k(torch, kda, ki, steps, warmup, timer):
 
     r = timer.run(step, steps, warmup)
     return w, r, decode_bytes(B, H, T, w.n_snap)
+
+
+def norm_bytes(rows: int, heads: int) -> int:
+    """Algorithmic bytes of one gated RMSNorm call: FP32 core read, BF16 gate read, BF16 output
+    written (512 + 256 + 256 per (token, head)) and the BF16 weight read once."""
+    return rows * heads * (4 * D + 2 * D + 2 * D) + 2 * D
+
+
+def bench_norm(torch, kda, ki, name, steps, warmup, timer):
+    rows, heads, seed = ki.NORM_WORKLOADS[name]
+    x = ki.norm_inputs(seed, rows, heads)
+    bits = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).cuda()
+    core0, gate0, w = torch.from_numpy(x["core"]).cuda(), bits(x["out_gate"]), bits(x["o_norm"])
+    # buffer sets rotated over >= 1 GiB so the 256 MB Infinity Cache cannot serve them
+    n_set = max(2, -(-(1 << 30) // (norm_bytes(rows, heads))))
+    sets = [(core0.clone(), gate0.clone(), torch.empty_like(gate0)) for _ in range(n_set)]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        c, g, o = sets[i % n_set]
+        kda.kda_gated_rmsnorm(c, g, w, ki.NORM_EPS, out=o, stream=stream)
+
+    r = timer.run(step, steps, warmup)
+    return r, norm_bytes(rows, heads), n_set
 
 
 def bench_prefill(torch, kda, ki, name, steps, warmup, timer):
@@ -367,6 +392,16 @@ def main():
                "GB_per_s": prefill_bytes(w.batch, w.heads, w.T) / r["launch_avg_s"] / 1e9}
         res.update(extra)
         workloads[name] = res
+    for name in ki.NORM_WORKLOADS:
+        if not want(name):
+            continue
+        log(name)
+        r, nbytes, n_set = bench_norm(torch, kda, ki, name, args.reps or args.steps, args.warmup, timer)
+        rows, heads, _ = ki.NORM_WORKLOADS[name]
+        gbs = nbytes / r["launch_avg_s"] / 1e9
+        workloads[name] = {"tokens_per_s": rows / r["s_per_step"], "us_per_call": r["s_per_step"] * 1e6,
+                           "kernel_us": r["launch_avg_s"] * 1e6, "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                           "buffer_sets_rotated": n_set}
     for name, res in workloads.items():
         log(f"{name}: " + ", ".join(f"{k}={v:.4g}" if isinstance(v, float) else f"{k}={v}"
                                     for k, v in res.items()))

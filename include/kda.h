@@ -22,8 +22,9 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- *  * All tensor pointers are DEVICE pointers to contiguous FP32 memory owned
- *    by the caller.  The library allocates nothing and keeps no state between
+ *  * All tensor pointers are DEVICE pointers to contiguous memory owned by
+ *    the caller, FP32 unless a declaration says BF16, and 16-byte aligned
+ *    (beta: 4-byte aligned); a misaligned pointer is refused.  The library allocates nothing and keeps no state between
  *    calls (module page: the forward calls allocate nothing and write only
  *    into the caller's workspace and sequence state).
  *  * Layouts (token-major, heads inside, D = 128):
@@ -52,6 +53,7 @@
 #define KDA_H_
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -61,10 +63,12 @@ extern "C" {
 /* Largest head count kda_chunk_prefill accepts (byte offsets inside one chunk
  * of a sequence stay below 2^31). */
 #define KDA_PREFILL_MAX_HEADS 16384
+/* Smallest eps kda_gated_rmsnorm accepts. */
+#define KDA_GATED_RMSNORM_MIN_EPS 1e-30f
 
 typedef enum {
     KDA_OK = 0,
-    KDA_ERR_INVALID_ARG = -1, /* null pointer, size < 1, n_snapshots out of range, overlap, overflow */
+    KDA_ERR_INVALID_ARG = -1, /* null or misaligned pointer, size < 1, bad n_snapshots / eps, overlap, overflow */
     KDA_ERR_UNSUPPORTED = -2, /* chunk not in {16, 32, 64}                                             */
     KDA_ERR_WORKSPACE = -3,   /* workspace smaller than kda_chunk_prefill_workspace_bytes()           */
     KDA_ERR_HIP = -4          /* the HIP runtime refused a launch                                     */
@@ -147,6 +151,36 @@ int kda_recurrent_step(const float* q, const float* k, const float* v, const flo
 int kda_recurrent_k(const float* q, const float* k, const float* v, const float* gate, const float* beta,
                     float* state, float* out, float* snapshots, int n_snapshots, int batch, int heads, int T,
                     void* stream);
+
+/*
+ * The step after the core: sigmoid-gated RMSNorm of the core's output (module
+ * page, pipeline line: the core output goes through a sigmoid-gated RMSNorm
+ * with weight o_norm and gate g_b(g_a(h)) before o_proj; the page notes that
+ * o_norm gates with a sigmoid, not SiLU).  Independently for every row r and
+ * head h, over the 128 value channels j of x = core[r][h]:
+ *
+ *     out[r][h][j] = x_j / sqrt(mean_i x_i^2 + eps) * o_norm[j] * sigmoid(out_gate[r][h][j])
+ *
+ *   core     : [rows][heads][128] FP32, e.g. the out of the entry points
+ *              above with rows = batch * their row count
+ *   out_gate : [rows][heads][128] BF16 (raw 16-bit patterns), the output gate
+ *              (workspace page, field out_gate: [T, qkv] BF16)
+ *   o_norm   : [128] BF16, one weight per channel shared by every head (config
+ *              page, Glm5NextKdaWeights::o_norm: [head_dim] BF16)
+ *   out      : [rows][heads][128] BF16 (workspace page, field o_norm_out)
+ *   eps      : rms_norm_eps (config page), finite and
+ *              >= KDA_GATED_RMSNORM_MIN_EPS
+ *
+ * Rows are independent; padded prefill rows (t >= T) are processed like any
+ * other and give whatever their core holds.  The scale is formed in FP64, so
+ * any finite core is handled without overflow; the products are FP32 and the
+ * result is rounded to nearest even, within one BF16 unit in the last place
+ * of the exact value.  out must not overlap an input.  Refusals
+ * (KDA_ERR_INVALID_ARG): a null pointer, rows or heads < 1, eps out of range,
+ * rows * heads above 2^34 - 8, overlap.
+ */
+int kda_gated_rmsnorm(const float* core, const uint16_t* out_gate, const uint16_t* o_norm, uint16_t* out,
+                      int rows, int heads, float eps, void* stream);
 
 #ifdef __cplusplus
 }

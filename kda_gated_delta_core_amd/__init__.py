@@ -2,8 +2,8 @@
 
 Argument marshalling only: every step of the core runs in the HIP kernels of
 ``libkda_amd.so`` behind the C ABI of ``include/kda.h``.  The functions carry
-the C names; tensors must be contiguous float32 CUDA (HIP) tensors in the
-layouts the header documents.  PyTorch provides device memory and the stream
+the C names; tensors must be contiguous CUDA (HIP) tensors, float32 unless
+the header says BF16 (then torch.bfloat16), in the layouts it documents.  PyTorch provides device memory and the stream
 (the current torch stream unless one is given).  There is no CPU fallback: if
 the library cannot be loaded every call raises.
 """
@@ -25,7 +25,8 @@ KDA_ERR_WORKSPACE = -3
 KDA_ERR_HIP = -4
 
 EXPORTED = ("kda_status_string", "kda_chunk_prefill_workspace_bytes", "kda_chunk_prefill", "kda_recurrent_step",
-            "kda_recurrent_k")
+            "kda_recurrent_k", "kda_gated_rmsnorm")
+GATED_RMSNORM_MIN_EPS = 1e-30
 
 _lib = None
 
@@ -57,6 +58,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_recurrent_step.restype = i
     lib.kda_recurrent_k.argtypes = [p] * 8 + [i] * 4 + [p]
     lib.kda_recurrent_k.restype = i
+    lib.kda_gated_rmsnorm.argtypes = [p] * 4 + [i, i, ctypes.c_float, p]
+    lib.kda_gated_rmsnorm.restype = i
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -76,13 +79,13 @@ def _stream_ptr(stream) -> int | None:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _check(name: str, t: torch.Tensor, shape: tuple) -> int:
+def _check(name: str, t: torch.Tensor, shape: tuple, dtype=torch.float32) -> int:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must live on the GPU")
-    if t.dtype != torch.float32:
-        raise TypeError(f"{name} must be float32")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if tuple(t.shape) != tuple(shape):
@@ -170,4 +173,25 @@ def kda_chunk_prefill(q, k, v, gate, beta, state, T: int, chunk: int, out=None, 
                                           _stream_ptr(stream))
     if rc != KDA_OK:
         raise KdaError("kda_chunk_prefill", rc)
+    return out
+
+
+def kda_gated_rmsnorm(core, out_gate, o_norm, eps: float, out=None, stream=None):
+    """Sigmoid-gated RMSNorm over the last (128-channel) dimension.  Returns ``out``.
+
+    core: float32 [..., H, 128] (e.g. the [B][rows][H][128] output of the core);
+    out_gate: bfloat16 of the same shape; o_norm: bfloat16 [128]; out: bfloat16 like out_gate.
+    """
+    if not isinstance(core, torch.Tensor) or core.dim() < 2 or core.shape[-1] != HEAD_DIM:
+        raise ValueError(f"core must be [..., heads, {HEAD_DIM}]")
+    shape = tuple(core.shape)
+    H = shape[-2]
+    rows = core.numel() // (H * HEAD_DIM) if H else 0
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=core.device)
+    args = [_check("core", core, shape), _check("out_gate", out_gate, shape, torch.bfloat16),
+            _check("o_norm", o_norm, (HEAD_DIM,), torch.bfloat16), _check("out", out, shape, torch.bfloat16)]
+    rc = load_library().kda_gated_rmsnorm(*args, rows, H, float(eps), _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_gated_rmsnorm", rc)
     return out

@@ -3,6 +3,7 @@
 #include "kda.h"
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "kda_internal.h"
@@ -46,6 +47,14 @@ bool any_overlap(const Range* ranges, int n, int n_written)
     return false;
 }
 
+// the kernels move tensors with 16-byte vector accesses (beta with 4-byte ones)
+bool aligned(std::initializer_list<const void*> ps, uintptr_t a = 16)
+{
+    for (const void* p : ps)
+        if ((uintptr_t)p % a) return false;
+    return true;
+}
+
 bool chunk_ok(int chunk) { return chunk == 16 || chunk == 32 || chunk == 64; }
 
 int64_t prefill_ws_bytes(int batch, int heads, int T, int chunk)
@@ -83,6 +92,7 @@ KDA_API int kda_chunk_prefill(const float* q, const float* k, const float* v, co
                               size_t workspace_bytes, void* stream)
 {
     if (!q || !k || !v || !gate || !beta || !state || !out) return KDA_ERR_INVALID_ARG;
+    if (!aligned({q, k, v, gate, state, out, workspace}) || !aligned({beta}, 4)) return KDA_ERR_INVALID_ARG;
     if (batch < 1 || heads < 1 || T < 1) return KDA_ERR_INVALID_ARG;
     if (!chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
     const int64_t need = prefill_ws_bytes(batch, heads, T, chunk);
@@ -108,6 +118,7 @@ KDA_API int kda_recurrent_k(const float* q, const float* k, const float* v, cons
                             int T, void* stream)
 {
     if (!q || !k || !v || !gate || !beta || !state || !out) return KDA_ERR_INVALID_ARG;
+    if (!aligned({q, k, v, gate, state, out, snapshots}) || !aligned({beta}, 4)) return KDA_ERR_INVALID_ARG;
     if (batch < 1 || heads < 1 || T < 1) return KDA_ERR_INVALID_ARG;
     if (n_snapshots < 0 || n_snapshots > T || (n_snapshots > 0 && !snapshots)) return KDA_ERR_INVALID_ARG;
     const int64_t vec = mul({batch, T, heads, KDA_HEAD_DIM});
@@ -129,4 +140,19 @@ KDA_API int kda_recurrent_step(const float* q, const float* k, const float* v, c
                                float* state, float* out, int batch, int heads, void* stream)
 {
     return kda_recurrent_k(q, k, v, gate, beta, state, out, nullptr, 0, batch, heads, 1, stream);
+}
+
+KDA_API int kda_gated_rmsnorm(const float* core, const uint16_t* out_gate, const uint16_t* o_norm, uint16_t* out,
+                              int rows, int heads, float eps, void* stream)
+{
+    if (!core || !out_gate || !o_norm || !out || rows < 1 || heads < 1) return KDA_ERR_INVALID_ARG;
+    if (!aligned({core, out_gate, o_norm, out})) return KDA_ERR_INVALID_ARG;
+    if (!(isfinite(eps) && eps >= KDA_GATED_RMSNORM_MIN_EPS)) return KDA_ERR_INVALID_ARG;
+    const int64_t n_vec = mul({rows, heads});
+    const int64_t elems = mul({n_vec, KDA_HEAD_DIM});
+    if (n_vec < 0 || elems < 0 || n_vec > INT64_C(0x7fffffff) * 8) return KDA_ERR_INVALID_ARG;  // grid bound
+    const Range r[] = {{out, elems * 2}, {core, elems * 4}, {out_gate, elems * 2}, {o_norm, KDA_HEAD_DIM * 2}};
+    if (any_overlap(r, 4, 1)) return KDA_ERR_INVALID_ARG;
+    const int rc = kda::launch_gated_rmsnorm(core, out_gate, o_norm, out, n_vec, eps, static_cast<hipStream_t>(stream));
+    return rc == 0 ? KDA_OK : KDA_ERR_HIP;
 }

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace kda {
 
@@ -30,5 +31,8 @@ long long recurrent_max_units();
 int launch_chunk_prefill(const float* q, const float* k, const float* v, const float* gate, const float* beta,
                          float* state, float* out, int batch, int heads, int T, int t_pad, int chunk,
                          float* workspace, hipStream_t stream);
+
+int launch_gated_rmsnorm(const float* core, const uint16_t* gate, const uint16_t* weight, uint16_t* out,
+                         long long n_vec, float eps, hipStream_t stream);
 
 }  // namespace kda

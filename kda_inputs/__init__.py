@@ -15,6 +15,14 @@ Recipe (one per workload, all values fp32 in the end):
   passed through a sigmoid, workspace page, field ``beta``).
 * state: 0.02 * standard normal, or zeros.
 
+Inputs of the gated RMSNorm that follows the core (norm_inputs):
+
+* core     : standard normal, fp32, [rows][heads][D].
+* out_gate : standard normal, rounded to BF16 (round to nearest even) and
+  kept as 16-bit patterns (a projection output of unit scale).
+* o_norm   : 1 + 0.1 * standard normal, BF16 patterns, [D] (a norm weight
+  near one).
+
 Every array is a pure function of (workload seed, array id, sequence, row
 block): rows are drawn in blocks of ``ROW_BLOCK`` tokens from
 ``SeedSequence([seed, array_id, b, block])``, so a sequence can be generated
@@ -40,6 +48,15 @@ L2_EPS = 1e-6
 
 # array ids inside a workload's seed space
 ID_STATE, ID_Q, ID_K, ID_V, ID_GATE, ID_BETA = 0, 1, 2, 3, 4, 5
+ID_CORE, ID_OUT_GATE, ID_O_NORM = 6, 7, 8
+# rms_norm_eps of the gated RMSNorm workloads (the pages name the config key, not its value)
+NORM_EPS = 1e-6
+# (rows, heads, seed) of the gated RMSNorm workloads: the output of the T=8192 prefill and of one
+# B=64 decode step, both H=32
+NORM_WORKLOADS = {
+    "gated_rmsnorm_t8192_h32": (8192, 32, 1006),
+    "gated_rmsnorm_b64_h32": (64, 32, 1007),
+}
 
 
 @dataclass(frozen=True)
@@ -186,3 +203,17 @@ def workload_inputs(w: Workload, batch: int | None = None, heads: int | None = N
         alloc = T_
     return make_batch(w.seed, B, H, T_, w.gate_lo, w.state_std, alloc_rows=alloc, pad_value=w.pad_value,
                       threads=threads)
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Finite fp32 values to BF16 bit patterns (uint16), rounding to nearest even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def norm_inputs(seed: int, rows: int, heads: int) -> dict:
+    """core [rows][heads][D] fp32, out_gate [rows][heads][D] and o_norm [D] as BF16 bit patterns."""
+    core = _rng(seed, ID_CORE, 0, 0).standard_normal((rows, heads, D), dtype=np.float32)
+    g = _rng(seed, ID_OUT_GATE, 0, 0).standard_normal((rows, heads, D), dtype=np.float32)
+    w = 1.0 + 0.1 * _rng(seed, ID_O_NORM, 0, 0).standard_normal(D, dtype=np.float32)
+    return {"core": core, "out_gate": to_bf16_bits(g), "o_norm": to_bf16_bits(w.astype(np.float32))}

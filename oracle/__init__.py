@@ -5,12 +5,17 @@ leg may import this package.  It wraps ``kda_oracle.c`` through ctypes and
 takes / returns numpy arrays; see that file's header for the exact recurrence,
 the chunked form and every layout.
 
+``gated_rmsnorm`` (the sigmoid-gated RMSNorm that follows the core) is plain
+numpy in fp64.
+
 Parity status: pinned.  tests/test_oracle_pins.py checks it against closed
 forms, exact rational brute force on tiny inputs and invariants of the method
 (state untouched at beta=0/gate=0, the delta-rule fixed point S^T k = v at
 beta=1, per-row exponential averages for basis keys, decay-before-update order
 on a scalar head, chunked == serial, pad independence, linearity, column
-equivariance, continuation).
+equivariance, continuation).  gated_rmsnorm is pinned against torch's own
+rms_norm and sigmoid in fp64, closed forms (one-hot rows, gate 0 and +-inf),
+scale invariance and unit mean square (tests/test_oracle_norm_pins.py).
 """
 from __future__ import annotations
 
@@ -114,3 +119,24 @@ def chunk_stages(q, k, v, gate, beta, S0, b: int, h: int, t0: int, n: int) -> di
         raise ValueError("kda_oracle_chunk_stages rejected its arguments")
     res["S"] = S
     return res
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """BF16 bit patterns to float64: a BF16 value is the upper 16 bits of an IEEE float32."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def gated_rmsnorm(core, out_gate_bits, o_norm_bits, eps: float) -> np.ndarray:
+    """Sigmoid-gated RMSNorm, fp64 (module page, pipeline line: RMSNorm with weight o_norm, gated by
+    a sigmoid of g_b(g_a(h)); workspace page, fields out_gate and o_norm_out; config page,
+    Glm5NextKdaWeights::o_norm [head_dim]; config page, rms_norm_eps).  For every vector x over the last axis of
+    core: x / sqrt(mean(x^2) + eps) * w * sigmoid(g).  eps is widened from float32, the precision
+    the C ABI takes it in."""
+    x = np.asarray(core, dtype=np.float64)
+    w = bf16_to_f64(o_norm_bits)
+    g = bf16_to_f64(out_gate_bits)
+    e = float(np.float32(eps))
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-g))
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + e) * w * sig

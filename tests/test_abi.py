@@ -7,6 +7,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 import kda_gated_delta_core_amd as kda
 
@@ -27,6 +28,12 @@ def declared_functions():
 @pytest.fixture(scope="module")
 def lib():
     return kda.load_library()
+
+
+# The refusal tests pass fake, never-mapped device addresses: a check that regressed would launch a
+# kernel on them.  They run only where no GPU is visible (counting devices does not initialise one).
+no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                            reason="refusal tests use fake device addresses; run where no GPU is visible")
 
 
 def test_exports_every_declared_symbol(lib):
@@ -63,6 +70,7 @@ def _prefill(lib, ptrs=None, B=1, H=2, T=64, C=16, ws=None, ws_bytes=None):
                                  need if ws_bytes is None else ws_bytes, None)
 
 
+@no_gpu
 def test_prefill_refusals(lib):
     for i in range(7):
         p = list(P[:7])
@@ -99,6 +107,7 @@ def test_prefill_refusals(lib):
     assert lib.kda_chunk_prefill_workspace_bytes(*args) > 0
 
 
+@no_gpu
 def test_recurrent_refusals(lib):
     for i in range(7):
         p = list(P[:7])
@@ -127,3 +136,43 @@ def test_python_binding_rejects_cpu_tensors():
     s = torch.zeros(1, 2, 128, 128)
     with pytest.raises(ValueError):
         kda.kda_recurrent_step(x, x, x, x, b, s, out=torch.zeros_like(x), stream=0)
+
+
+@no_gpu
+def test_gated_rmsnorm_refusals(lib):
+    f = lib.kda_gated_rmsnorm
+    ok = kda.KDA_ERR_INVALID_ARG
+    for i in range(4):
+        p = list(P[:4])
+        p[i] = None
+        assert f(*p, 4, 2, 1e-6, None) == ok
+    assert f(*P[:4], 0, 2, 1e-6, None) == ok
+    assert f(*P[:4], 4, 0, 1e-6, None) == ok
+    assert f(*P[:4], -1, 2, 1e-6, None) == ok
+    for eps in (0.0, -1e-6, 1e-31, float("nan"), float("inf")):
+        assert f(*P[:4], 4, 2, eps, None) == ok, eps
+    # out overlapping core, out_gate or o_norm
+    for i in range(3):
+        p = list(P[:4])
+        p[3] = P[i] + 2
+        assert f(*p, 4, 2, 1e-6, None) == ok
+    # more vectors than the grid can hold: rows * heads = 2^34 (fake buffers 2^52 bytes apart)
+    far = [(i + 1) << 52 for i in range(4)]
+    assert f(*far, 1 << 20, 1 << 14, 1e-6, None) == ok
+
+
+@no_gpu
+def test_misaligned_pointers_are_refused(lib):
+    bad = kda.KDA_ERR_INVALID_ARG
+    for i in range(7):
+        p = list(P[:7])
+        p[i] += 4 if i != 4 else 2  # beta needs 4-byte alignment, the others 16-byte
+        assert _prefill(lib, ptrs=p) == bad, i
+        assert lib.kda_recurrent_k(*p, None, 0, 4, 2, 3, None) == bad, i
+        assert lib.kda_recurrent_step(*p, 4, 2, None) == bad, i
+    assert lib.kda_recurrent_k(*P[:7], P[8] + 8, 2, 4, 2, 3, None) == bad  # misaligned snapshots
+    assert _prefill(lib, ws=P[7] + 8) == bad
+    for i in range(4):
+        p = list(P[:4])
+        p[i] += 8
+        assert lib.kda_gated_rmsnorm(*p, 4, 2, 1e-6, None) == bad, i
