@@ -7,8 +7,10 @@ sequences x 32 heads, FP32 128x128 key-major state per head updated in place
 The same run also times the other workloads of the core and reports each
 under ``workloads``: the T=8192 chunked prefill, the k=4 decode_k with
 snapshots, the 4 x 32768 long-context prefill followed by 16 decode steps,
-the small T=64 prefill, and the sigmoid-gated RMSNorm that follows the core
-(kda_gated_rmsnorm) on the output of the T=8192 prefill and of a decode step.
+the small T=64 prefill, the decode front end before the core
+(kda_decode_front_end: conv1d update + SiLU + L2, one step at B=64 and the
+k=4 rows at B=128), and the sigmoid-gated RMSNorm after it (kda_gated_rmsnorm)
+on the output of the T=8192 prefill and of a decode step.
 
 Inputs are seeded synthetic tensors (kda_inputs) resident in HBM before the
 timed region.  Decode states are rotated over buffers totalling >= 1 GiB so
@@ -150,6 +152,37 @@ def bench_norm(torch, kda, ki, name, steps, warmup, timer):
 
     r = timer.run(step, steps, warmup)
     return r, norm_bytes(rows, heads), n_set
+
+
+def front_end_bytes(B: int, T: int, H: int, K: int, n_snap: int) -> int:
+    """Algorithmic bytes of one decode front-end call: BF16 qkv read, FP32 q, k, v written, the FP32
+    conv state read and written, snapshots written, BF16 conv weights read once."""
+    C = 3 * H * D
+    return B * T * C * (2 + 4) + B * C * K * 4 * (2 + n_snap) + C * K * 2
+
+
+def bench_front_end(torch, kda, ki, name, steps, warmup, timer):
+    B, T, H, K, seed = ki.FRONT_END_WORKLOADS[name]
+    n_snap = T if T > 1 else 0
+    x = ki.front_end_inputs(seed, B, T, H, K)
+    bits = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).cuda()
+    qkv0, w, st0 = bits(x["qkv"]), bits(x["conv_w"]), torch.from_numpy(x["conv_state"]).cuda()
+    vs = (B, T, H, D)
+    per_set = front_end_bytes(B, T, H, K, n_snap)
+    n_set = max(2, -(-(1 << 30) // per_set))
+    sets = []
+    for _ in range(n_set):
+        snaps = torch.empty((n_snap, B, 3 * H * D, K), device="cuda") if n_snap else None
+        sets.append((qkv0.clone(), st0.clone(), *(torch.empty(vs, device="cuda") for _ in range(3)), snaps))
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        qkv, st, q, k, v, snaps = sets[i % n_set]
+        kda.kda_decode_front_end(qkv, w, st, H, ki.L2_EPS, q=q, k=k, v=v, conv_snapshots=snaps,
+                                 n_snapshots=n_snap, stream=stream)
+
+    r = timer.run(step, steps, warmup)
+    return r, per_set, n_set, B * T
 
 
 def bench_prefill(torch, kda, ki, name, steps, warmup, timer):
@@ -392,6 +425,15 @@ def main():
                "GB_per_s": prefill_bytes(w.batch, w.heads, w.T) / r["launch_avg_s"] / 1e9}
         res.update(extra)
         workloads[name] = res
+    for name in ki.FRONT_END_WORKLOADS:
+        if not want(name):
+            continue
+        log(name)
+        r, nbytes, n_set, tokens = bench_front_end(torch, kda, ki, name, args.reps or args.steps, args.warmup, timer)
+        gbs = nbytes / r["launch_avg_s"] / 1e9
+        workloads[name] = {"tokens_per_s": tokens / r["s_per_step"], "us_per_call": r["s_per_step"] * 1e6,
+                           "kernel_us": r["launch_avg_s"] * 1e6, "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                           "buffer_sets_rotated": n_set}
     for name in ki.NORM_WORKLOADS:
         if not want(name):
             continue

@@ -63,13 +63,16 @@ extern "C" {
 /* Largest head count kda_chunk_prefill accepts (byte offsets inside one chunk
  * of a sequence stay below 2^31). */
 #define KDA_PREFILL_MAX_HEADS 16384
-/* Smallest eps kda_gated_rmsnorm accepts. */
+/* Smallest eps kda_gated_rmsnorm and kda_decode_front_end accept. */
 #define KDA_GATED_RMSNORM_MIN_EPS 1e-30f
+/* Largest conv_kernel kda_decode_front_end accepts (config page, validate:
+ * the conv kernels keep the sliding window in 4 registers). */
+#define KDA_FRONT_END_MAX_CONV_KERNEL 4
 
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARG = -1, /* null or misaligned pointer, size < 1, bad n_snapshots / eps, overlap, overflow */
-    KDA_ERR_UNSUPPORTED = -2, /* chunk not in {16, 32, 64}                                             */
+    KDA_ERR_UNSUPPORTED = -2, /* chunk not in {16, 32, 64}; conv_kernel above 4                          */
     KDA_ERR_WORKSPACE = -3,   /* workspace smaller than kda_chunk_prefill_workspace_bytes()           */
     KDA_ERR_HIP = -4          /* the HIP runtime refused a launch                                     */
 } kda_status;
@@ -181,6 +184,47 @@ int kda_recurrent_k(const float* q, const float* k, const float* v, const float*
  */
 int kda_gated_rmsnorm(const float* core, const uint16_t* out_gate, const uint16_t* o_norm, uint16_t* out,
                       int rows, int heads, float eps, void* stream);
+
+/*
+ * The step before the core on the decode path: the depthwise causal conv1d
+ * update, SiLU and L2 on q and k in one call (module page, pipeline line:
+ * conv1d + SiLU, then L2 on q and k only, v never normalised; decode fuses
+ * conv, SiLU and L2 in one kernel; the conv state keeps conv_kernel slots and
+ * is shifted left before convolving).  T rows of each sequence are walked in
+ * order (T = 1 for a decode step, T = k for decode_k).  For every row and
+ * every channel c of conv_dim = 3 * heads * 128 (q | k | v, in that order):
+ *
+ *     slots <- (slots[1], ..., slots[K-1], qkv[c])      K = conv_kernel
+ *     y      = sum_k conv_w[c][k] * slots[k]            slot K-1 holds the newest input
+ *     y      = y * sigmoid(y)
+ *     q, k  : each head's 128 values scaled by 1 / sqrt(sum y^2 + l2_eps); v as is
+ *
+ *   qkv            : [batch][T][conv_dim] BF16 (workspace page, qkv_proj:
+ *                    [T, conv_dim] BF16, q | k | v per token)
+ *   conv_w         : [conv_dim][conv_kernel] BF16, no bias (config page,
+ *                    Glm5NextKdaWeights::conv)
+ *   conv_state     : [batch][conv_dim][conv_kernel] FP32, read and updated in
+ *                    place (config page, conv_state_elems)
+ *   q, k, v        : [batch][T][heads][128] FP32, the inputs of
+ *                    kda_recurrent_step / kda_recurrent_k
+ *   conv_snapshots : [n_snapshots][batch][conv_dim][conv_kernel] FP32, the
+ *                    conv state after row t for t < n_snapshots (the conv half
+ *                    of decode_k's snapshots, layer page); NULL when
+ *                    n_snapshots == 0
+ *   conv_kernel    : 1..4 (KDA_ERR_UNSUPPORTED above 4)
+ *   l2_eps         : finite, >= KDA_GATED_RMSNORM_MIN_EPS, added inside the
+ *                    square root (config page, l2_eps)
+ *
+ * The conv state only ever holds inputs, so it is exact; q, k, v carry FP32
+ * rounding of the conv sum and the SiLU (the L2 scale is formed in FP64).
+ * Outputs, conv_state and conv_snapshots must not overlap each other or an
+ * input.  Refusals (KDA_ERR_INVALID_ARG): a null pointer, batch, heads or T
+ * < 1, heads > KDA_PREFILL_MAX_HEADS, n_snapshots outside [0, T], conv_kernel
+ * < 1, l2_eps out of range, overlap.
+ */
+int kda_decode_front_end(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q, float* k,
+                         float* v, float* conv_snapshots, int n_snapshots, int batch, int heads, int T,
+                         int conv_kernel, float l2_eps, void* stream);
 
 #ifdef __cplusplus
 }

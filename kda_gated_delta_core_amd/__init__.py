@@ -25,7 +25,7 @@ KDA_ERR_WORKSPACE = -3
 KDA_ERR_HIP = -4
 
 EXPORTED = ("kda_status_string", "kda_chunk_prefill_workspace_bytes", "kda_chunk_prefill", "kda_recurrent_step",
-            "kda_recurrent_k", "kda_gated_rmsnorm")
+            "kda_recurrent_k", "kda_gated_rmsnorm", "kda_decode_front_end")
 GATED_RMSNORM_MIN_EPS = 1e-30
 
 _lib = None
@@ -60,6 +60,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_recurrent_k.restype = i
     lib.kda_gated_rmsnorm.argtypes = [p] * 4 + [i, i, ctypes.c_float, p]
     lib.kda_gated_rmsnorm.restype = i
+    lib.kda_decode_front_end.argtypes = [p] * 7 + [i] * 5 + [ctypes.c_float, p]
+    lib.kda_decode_front_end.restype = i
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -195,3 +197,36 @@ def kda_gated_rmsnorm(core, out_gate, o_norm, eps: float, out=None, stream=None)
     if rc != KDA_OK:
         raise KdaError("kda_gated_rmsnorm", rc)
     return out
+
+
+def kda_decode_front_end(qkv, conv_w, conv_state, heads: int, l2_eps: float, q=None, k=None, v=None,
+                         conv_snapshots=None, n_snapshots: int = 0, stream=None):
+    """Conv1d update + SiLU + L2(q, k) over T rows per sequence.  Returns (q, k, v).
+
+    qkv: bfloat16 [B][T][3 H 128]; conv_w: bfloat16 [3 H 128][K]; conv_state: float32 [B][3 H 128][K]
+    (in place); q, k, v: float32 [B][T][H][128]; conv_snapshots: float32 [>= n][B][3 H 128][K].
+    """
+    if not isinstance(qkv, torch.Tensor) or qkv.dim() != 3:
+        raise ValueError("qkv must be [batch][T][3 * heads * 128]")
+    B, T, C = qkv.shape
+    if C != 3 * heads * HEAD_DIM:
+        raise ValueError(f"qkv has {C} channels, expected 3 * {heads} * {HEAD_DIM}")
+    if conv_w.dim() != 2:
+        raise ValueError("conv_w must be [conv_dim][conv_kernel]")
+    K = conv_w.shape[1]
+    vs = (B, T, heads, HEAD_DIM)
+    q = torch.empty(vs, dtype=torch.float32, device=qkv.device) if q is None else q
+    k = torch.empty(vs, dtype=torch.float32, device=qkv.device) if k is None else k
+    v = torch.empty(vs, dtype=torch.float32, device=qkv.device) if v is None else v
+    args = [_check("qkv", qkv, (B, T, C), torch.bfloat16), _check("conv_w", conv_w, (C, K), torch.bfloat16),
+            _check("conv_state", conv_state, (B, C, K)), _check("q", q, vs), _check("k", k, vs), _check("v", v, vs)]
+    snap_ptr = None
+    if n_snapshots:
+        if conv_snapshots is None or conv_snapshots.dim() != 4 or conv_snapshots.shape[0] < n_snapshots:
+            raise ValueError("conv_snapshots must be [>= n_snapshots][B][conv_dim][conv_kernel]")
+        snap_ptr = _check("conv_snapshots", conv_snapshots, (conv_snapshots.shape[0], B, C, K))
+    rc = load_library().kda_decode_front_end(*args, snap_ptr, int(n_snapshots), B, heads, T, K, float(l2_eps),
+                                             _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_decode_front_end", rc)
+    return q, k, v

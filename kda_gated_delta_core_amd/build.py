@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda_amd.so")
-SOURCES = ["kda_api.cpp", "kda_recurrent.hip", "kda_chunk.hip", "kda_norm.hip"]
+SOURCES = ["kda_api.cpp", "kda_recurrent.hip", "kda_chunk.hip", "kda_norm.hip", "kda_front_end.hip"]
 # measurement tooling, a library of its own (not part of the KDA C ABI)
 PROBE_LIB = os.path.join(PKG, "libkda_probe.so")
 PROBE_SOURCES = ["kda_probe.hip"]

@@ -156,3 +156,32 @@ KDA_API int kda_gated_rmsnorm(const float* core, const uint16_t* out_gate, const
     const int rc = kda::launch_gated_rmsnorm(core, out_gate, o_norm, out, n_vec, eps, static_cast<hipStream_t>(stream));
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
 }
+
+KDA_API int kda_decode_front_end(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q, float* k,
+                                 float* v, float* conv_snapshots, int n_snapshots, int batch, int heads, int T,
+                                 int conv_kernel, float l2_eps, void* stream)
+{
+    if (!qkv || !conv_w || !conv_state || !q || !k || !v) return KDA_ERR_INVALID_ARG;
+    if (!aligned({qkv, conv_w, conv_state, q, k, v, conv_snapshots})) return KDA_ERR_INVALID_ARG;
+    if (batch < 1 || heads < 1 || T < 1 || heads > KDA_PREFILL_MAX_HEADS) return KDA_ERR_INVALID_ARG;
+    if (n_snapshots < 0 || n_snapshots > T || (n_snapshots > 0 && !conv_snapshots)) return KDA_ERR_INVALID_ARG;
+    if (conv_kernel < 1) return KDA_ERR_INVALID_ARG;
+    if (conv_kernel > KDA_FRONT_END_MAX_CONV_KERNEL) return KDA_ERR_UNSUPPORTED;
+    if (!(isfinite(l2_eps) && l2_eps >= KDA_GATED_RMSNORM_MIN_EPS)) return KDA_ERR_INVALID_ARG;
+    const int64_t C = 3 * (int64_t)heads * KDA_HEAD_DIM;
+    const int64_t x = mul({batch, T, C});
+    const int64_t w = mul({C, conv_kernel});
+    const int64_t st = mul({batch, C, conv_kernel});
+    const int64_t sn = mul({n_snapshots, batch, C, conv_kernel});
+    const int64_t vec = mul({batch, T, heads, KDA_HEAD_DIM});
+    if (x < 0 || w < 0 || st < 0 || sn < 0 || vec < 0) return KDA_ERR_INVALID_ARG;
+    if (mul({batch, 3, heads}) > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;  // one workgroup per head vector
+    const Range r[] = {{q, vec * 4},  {k, vec * 4},       {v, vec * 4},
+                       {conv_state, st * 4}, {n_snapshots ? conv_snapshots : nullptr, sn * 4},
+                       {qkv, x * 2},  {conv_w, w * 2}};
+    if (any_overlap(r, 7, 5)) return KDA_ERR_INVALID_ARG;
+    const int rc = kda::launch_front_end(qkv, conv_w, conv_state, q, k, v, n_snapshots ? conv_snapshots : nullptr,
+                                         n_snapshots, batch, heads, T, conv_kernel, l2_eps,
+                                         static_cast<hipStream_t>(stream));
+    return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}

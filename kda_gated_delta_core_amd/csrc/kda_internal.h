@@ -32,6 +32,10 @@ int launch_chunk_prefill(const float* q, const float* k, const float* v, const f
                          float* state, float* out, int batch, int heads, int T, int t_pad, int chunk,
                          float* workspace, hipStream_t stream);
 
+int launch_front_end(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q, float* k, float* v,
+                     float* snaps, int n_snap, int batch, int heads, int T, int conv_kernel, float l2_eps,
+                     hipStream_t stream);
+
 int launch_gated_rmsnorm(const float* core, const uint16_t* gate, const uint16_t* weight, uint16_t* out,
                          long long n_vec, float eps, hipStream_t stream);
 

@@ -23,6 +23,13 @@ Inputs of the gated RMSNorm that follows the core (norm_inputs):
 * o_norm   : 1 + 0.1 * standard normal, BF16 patterns, [D] (a norm weight
   near one).
 
+Inputs of the decode front end (front_end_inputs), conv_dim = 3 * heads * D:
+
+* qkv        : standard normal rounded to BF16, [B][T][conv_dim] (q | k | v).
+* conv_w     : 0.5 * standard normal rounded to BF16, [conv_dim][K].
+* conv_state : standard normal rounded to BF16 values, stored FP32,
+  [B][conv_dim][K] (the window of past inputs it holds in use).
+
 Every array is a pure function of (workload seed, array id, sequence, row
 block): rows are drawn in blocks of ``ROW_BLOCK`` tokens from
 ``SeedSequence([seed, array_id, b, block])``, so a sequence can be generated
@@ -49,6 +56,13 @@ L2_EPS = 1e-6
 # array ids inside a workload's seed space
 ID_STATE, ID_Q, ID_K, ID_V, ID_GATE, ID_BETA = 0, 1, 2, 3, 4, 5
 ID_CORE, ID_OUT_GATE, ID_O_NORM = 6, 7, 8
+ID_QKV, ID_CONV_W, ID_CONV_STATE = 9, 10, 11
+# (batch, rows, heads, conv_kernel, seed) of the decode front-end workloads: one decode step of the
+# B=64 H=32 workload, and the k=4 rows of the B=128 decode_k workload
+FRONT_END_WORKLOADS = {
+    "front_end_b64_h32_k4": (64, 1, 32, 4, 1008),
+    "front_end_b128_h32_k4_rows4": (128, 4, 32, 4, 1009),
+}
 # rms_norm_eps of the gated RMSNorm workloads (the pages name the config key, not its value)
 NORM_EPS = 1e-6
 # (rows, heads, seed) of the gated RMSNorm workloads: the output of the T=8192 prefill and of one
@@ -207,7 +221,7 @@ def workload_inputs(w: Workload, batch: int | None = None, heads: int | None = N
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Finite fp32 values to BF16 bit patterns (uint16), rounding to nearest even."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32).astype(np.uint64)  # keeps the shape
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
@@ -217,3 +231,16 @@ def norm_inputs(seed: int, rows: int, heads: int) -> dict:
     g = _rng(seed, ID_OUT_GATE, 0, 0).standard_normal((rows, heads, D), dtype=np.float32)
     w = 1.0 + 0.1 * _rng(seed, ID_O_NORM, 0, 0).standard_normal(D, dtype=np.float32)
     return {"core": core, "out_gate": to_bf16_bits(g), "o_norm": to_bf16_bits(w.astype(np.float32))}
+
+
+def front_end_inputs(seed: int, batch: int, rows: int, heads: int, conv_kernel: int) -> dict:
+    """qkv [B][rows][3 H D] and conv_w [3 H D][K] as BF16 patterns, conv_state [B][3 H D][K] fp32."""
+    C = 3 * heads * D
+    qkv = np.empty((batch, rows, C), dtype=np.uint16)
+    st = np.empty((batch, C, conv_kernel), dtype=np.float32)
+    for b in range(batch):
+        qkv[b] = to_bf16_bits(_rng(seed, ID_QKV, b, 0).standard_normal((rows, C), dtype=np.float32))
+        s = to_bf16_bits(_rng(seed, ID_CONV_STATE, b, 0).standard_normal((C, conv_kernel), dtype=np.float32))
+        st[b] = (s.astype(np.uint32) << 16).view(np.float32)
+    w = 0.5 * _rng(seed, ID_CONV_W, 0, 0).standard_normal((C, conv_kernel), dtype=np.float32)
+    return {"qkv": qkv, "conv_w": to_bf16_bits(w.astype(np.float32)), "conv_state": st}

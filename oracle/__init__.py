@@ -140,3 +140,41 @@ def gated_rmsnorm(core, out_gate_bits, o_norm_bits, eps: float) -> np.ndarray:
     with np.errstate(over="ignore"):
         sig = 1.0 / (1.0 + np.exp(-g))
     return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + e) * w * sig
+
+
+def decode_front_end(qkv_bits, conv_w_bits, conv_state, heads: int, l2_eps: float, n_snap: int = 0):
+    """The decode front end, fp64, token by token (module page, pipeline line: conv1d + SiLU, then L2
+    on q and k only; the conv state keeps conv_kernel slots and is shifted left before convolving;
+    decode fuses conv, SiLU and L2.  Workspace page, qkv_proj [T, conv_dim] BF16 with q | k | v per
+    token; config page, Glm5NextKdaWeights::conv [conv_dim, conv_kernel] BF16 (depthwise, no bias),
+    conv_state_elems [conv_dim, conv_kernel] FP32, l2_eps applied as 1/sqrt(sum + eps)).
+
+    qkv_bits [B][T][3 H D] and conv_w_bits [3 H D][K] are BF16 patterns, conv_state [B][3 H D][K]
+    (not modified).  Per token: the K slots shift left by one and the new input enters the last
+    slot; y = sum_k w[k] * slot[k] (slot K-1 newest, the causal convolution); y = y * sigmoid(y);
+    the q and k parts are scaled per head by 1 / sqrt(sum y^2 + eps).  Returns q, k, v
+    [B][T][H][D], the final conv state [B][3 H D][K] and the states after rows 0..n_snap-1
+    [n_snap][B][3 H D][K], all fp64."""
+    x = bf16_to_f64(qkv_bits)
+    w = bf16_to_f64(conv_w_bits)
+    s = np.array(conv_state, dtype=np.float64, copy=True)
+    B, T, C = x.shape
+    D = C // (3 * heads)
+    e = float(np.float32(l2_eps))
+    outs = np.zeros((3, B, T, heads, D))
+    snaps = np.zeros((n_snap, B, C, s.shape[-1]))
+    for t in range(T):
+        s[:, :, :-1] = s[:, :, 1:].copy()
+        s[:, :, -1] = x[:, t]
+        y = np.sum(s * w[None], axis=-1)
+        with np.errstate(over="ignore"):
+            y = y / (1.0 + np.exp(-y))
+        y = y.reshape(B, 3, heads, D)
+        for part in range(3):
+            yp = y[:, part]
+            if part < 2:
+                yp = yp / np.sqrt(np.sum(yp * yp, axis=-1, keepdims=True) + e)
+            outs[part, :, t] = yp
+        if t < n_snap:
+            snaps[t] = s
+    return outs[0], outs[1], outs[2], s, snaps

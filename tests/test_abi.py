@@ -176,3 +176,34 @@ def test_misaligned_pointers_are_refused(lib):
         p = list(P[:4])
         p[i] += 8
         assert lib.kda_gated_rmsnorm(*p, 4, 2, 1e-6, None) == bad, i
+
+
+@no_gpu
+def test_decode_front_end_refusals(lib):
+    f = lib.kda_decode_front_end
+    bad = kda.KDA_ERR_INVALID_ARG
+    ok_args = (4, 2, 3, 4, 1e-6)  # batch, heads, T, conv_kernel, eps (n_snapshots 0)
+    for i in range(6):
+        p = list(P[:6])
+        p[i] = None
+        assert f(*p, None, 0, *ok_args, None) == bad, i
+        p = list(P[:6])
+        p[i] += 8
+        assert f(*p, None, 0, *ok_args, None) == bad, i
+    assert f(*P[:6], None, 0, 0, 2, 3, 4, 1e-6, None) == bad
+    assert f(*P[:6], None, 0, 4, 0, 3, 4, 1e-6, None) == bad
+    assert f(*P[:6], None, 0, 4, 2, 0, 4, 1e-6, None) == bad
+    assert f(*P[:6], None, 0, 4, 16385, 3, 4, 1e-6, None) == bad
+    assert f(*P[:6], None, 2, *ok_args, None) == bad           # snapshots NULL
+    assert f(*P[:6], P[6], 4, *ok_args, None) == bad           # n_snapshots > T
+    assert f(*P[:6], P[6], -1, *ok_args, None) == bad
+    assert f(*P[:6], P[6] + 8, 1, *ok_args, None) == bad       # misaligned snapshots
+    assert f(*P[:6], None, 0, 4, 2, 3, 0, 1e-6, None) == bad
+    assert f(*P[:6], None, 0, 4, 2, 3, 5, 1e-6, None) == kda.KDA_ERR_UNSUPPORTED
+    for eps in (0.0, -1.0, float("nan"), float("inf")):
+        assert f(*P[:6], None, 0, 4, 2, 3, 4, eps, None) == bad
+    # outputs overlapping an input or each other
+    for i, j in ((3, 0), (4, 3), (2, 5), (5, 1)):
+        p = list(P[:6])
+        p[i] = p[j] + 16
+        assert f(*p, None, 0, *ok_args, None) == bad, (i, j)
