@@ -7,7 +7,8 @@ sequences x 32 heads, FP32 128x128 key-major state per head updated in place
 The same run also times the other workloads of the core and reports each
 under ``workloads``: the T=8192 chunked prefill, the k=4 decode_k with
 snapshots, the 4 x 32768 long-context prefill followed by 16 decode steps,
-the small T=64 prefill, the decode front end before the core
+the small T=64 prefill, a packed prefill of 23 sequences of mixed lengths
+(32768 tokens, kda_chunk_prefill_varlen), the decode front end before the core
 (kda_decode_front_end: conv1d update + SiLU + L2, one step at B=64 and the
 k=4 rows at B=128), and the sigmoid-gated RMSNorm after it (kda_gated_rmsnorm)
 on the output of the T=8192 prefill and of a decode step.
@@ -183,6 +184,24 @@ def bench_front_end(torch, kda, ki, name, steps, warmup, timer):
 
     r = timer.run(step, steps, warmup)
     return r, per_set, n_set, B * T
+
+
+def bench_varlen(torch, kda, ki, name, steps, warmup, timer):
+    total, H, C, mean_len, seed = ki.VARLEN_WORKLOADS[name]
+    lens = ki.varlen_lengths(seed, total, mean_len)
+    x = ki.varlen_inputs(seed, lens, H, -5.0, 0.02)
+    d = {n: torch.from_numpy(x[n]).cuda() for n in ("q", "k", "v", "gate", "beta", "state", "cu_seqlens")}
+    out = torch.empty_like(d["q"])
+    ws = torch.empty(kda.kda_chunk_prefill_varlen_workspace_bytes(len(lens), H, total, C), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        kda.kda_chunk_prefill_varlen(d["q"], d["k"], d["v"], d["gate"], d["beta"], d["state"], d["cu_seqlens"], C,
+                                     out=out, workspace=ws, stream=stream)
+
+    r = timer.run(step, steps, warmup)
+    return r, lens, H, C
 
 
 def bench_prefill(torch, kda, ki, name, steps, warmup, timer):
@@ -425,6 +444,17 @@ def main():
                "GB_per_s": prefill_bytes(w.batch, w.heads, w.T) / r["launch_avg_s"] / 1e9}
         res.update(extra)
         workloads[name] = res
+    for name in ki.VARLEN_WORKLOADS:
+        if not want(name):
+            continue
+        log(name)
+        r, lens, H, C = bench_varlen(torch, kda, ki, name, args.reps or 20, 0 if args.reps else 20, timer)
+        fl = sum(prefill_flops(1, H, n, C) for n in lens)
+        tf = fl / r["launch_avg_s"] / 1e12
+        workloads[name] = {"tokens_per_s": sum(lens) / r["s_per_step"], "ms_per_call": r["s_per_step"] * 1e3,
+                           "call_ms": r["launch_avg_s"] * 1e3, "algorithmic_TFLOP_per_s": tf,
+                           "mfma_frac": tf / MFMA_F32_PEAK_TFLOPS, "sequences": len(lens),
+                           "min_len": min(lens), "max_len": max(lens)}
     for name in ki.FRONT_END_WORKLOADS:
         if not want(name):
             continue

@@ -63,6 +63,8 @@ extern "C" {
 /* Largest head count kda_chunk_prefill accepts (byte offsets inside one chunk
  * of a sequence stay below 2^31). */
 #define KDA_PREFILL_MAX_HEADS 16384
+/* Most sequences one kda_chunk_prefill_varlen call takes. */
+#define KDA_VARLEN_MAX_SEQS (1 << 20)
 /* Smallest eps kda_gated_rmsnorm and kda_decode_front_end accept. */
 #define KDA_GATED_RMSNORM_MIN_EPS 1e-30f
 /* Largest conv_kernel kda_decode_front_end accepts (config page, validate:
@@ -120,6 +122,37 @@ size_t kda_chunk_prefill_workspace_bytes(int batch, int heads, int T, int chunk)
 int kda_chunk_prefill(const float* q, const float* k, const float* v, const float* gate, const float* beta,
                       float* state, float* out, int batch, int heads, int T, int chunk, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * Chunked prefill of a packed batch of sequences of their own lengths
+ * (varlen).  Same computation as kda_chunk_prefill for every sequence, with
+ * the sequences stored back to back instead of padded to a common length (the
+ * pages pad prefill buffers per call to a whole number of chunks, workspace
+ * page; here each sequence's last chunk is cut at its end instead).
+ *
+ *   q, k, v, gate, out : [total_tokens][heads][128];  beta : [total_tokens][heads]
+ *   state              : [n_seqs][heads][128][128], read and updated in place
+ *   cu_seqlens         : DEVICE int32 [n_seqs + 1]; sequence s holds tokens
+ *                        cu_seqlens[s] .. cu_seqlens[s + 1] - 1.  Expected
+ *                        0 = cu_seqlens[0] <= ... <= cu_seqlens[n_seqs] <=
+ *                        total_tokens.  The values are read on the device only:
+ *                        each is clamped to [0, total_tokens] and raised to the
+ *                        largest before it, so any content stays inside the
+ *                        buffers (an empty sequence leaves its state as is).
+ *   workspace          : >= kda_chunk_prefill_varlen_workspace_bytes(n_seqs,
+ *                        heads, total_tokens, chunk) bytes (records for up to
+ *                        heads * (total_tokens / chunk + n_seqs) chunks, then
+ *                        the clamped offsets)
+ *
+ * out rows outside every sequence are not written.  Each sequence's result
+ * equals the bits of kda_chunk_prefill on that sequence alone.  Refusals as
+ * kda_chunk_prefill, plus n_seqs outside [1, KDA_VARLEN_MAX_SEQS] or
+ * total_tokens < 1 (KDA_ERR_INVALID_ARG).
+ */
+size_t kda_chunk_prefill_varlen_workspace_bytes(int n_seqs, int heads, int total_tokens, int chunk);
+int kda_chunk_prefill_varlen(const float* q, const float* k, const float* v, const float* gate, const float* beta,
+                             float* state, float* out, const int* cu_seqlens, int n_seqs, int heads, int total_tokens,
+                             int chunk, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One recurrent decode step: one token per sequence (layer page,

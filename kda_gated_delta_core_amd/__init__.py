@@ -25,7 +25,8 @@ KDA_ERR_WORKSPACE = -3
 KDA_ERR_HIP = -4
 
 EXPORTED = ("kda_status_string", "kda_chunk_prefill_workspace_bytes", "kda_chunk_prefill", "kda_recurrent_step",
-            "kda_recurrent_k", "kda_gated_rmsnorm", "kda_decode_front_end")
+            "kda_recurrent_k", "kda_gated_rmsnorm", "kda_decode_front_end",
+            "kda_chunk_prefill_varlen_workspace_bytes", "kda_chunk_prefill_varlen")
 GATED_RMSNORM_MIN_EPS = 1e-30
 
 _lib = None
@@ -58,6 +59,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_recurrent_step.restype = i
     lib.kda_recurrent_k.argtypes = [p] * 8 + [i] * 4 + [p]
     lib.kda_recurrent_k.restype = i
+    lib.kda_chunk_prefill_varlen_workspace_bytes.argtypes = [i, i, i, i]
+    lib.kda_chunk_prefill_varlen_workspace_bytes.restype = sz
+    lib.kda_chunk_prefill_varlen.argtypes = [p] * 8 + [i] * 4 + [p, sz, p]
+    lib.kda_chunk_prefill_varlen.restype = i
     lib.kda_gated_rmsnorm.argtypes = [p] * 4 + [i, i, ctypes.c_float, p]
     lib.kda_gated_rmsnorm.restype = i
     lib.kda_decode_front_end.argtypes = [p] * 7 + [i] * 5 + [ctypes.c_float, p]
@@ -230,3 +235,40 @@ def kda_decode_front_end(qkv, conv_w, conv_state, heads: int, l2_eps: float, q=N
     if rc != KDA_OK:
         raise KdaError("kda_decode_front_end", rc)
     return q, k, v
+
+
+def kda_chunk_prefill_varlen_workspace_bytes(n_seqs: int, heads: int, total_tokens: int, chunk: int) -> int:
+    return int(load_library().kda_chunk_prefill_varlen_workspace_bytes(n_seqs, heads, total_tokens, chunk))
+
+
+def kda_chunk_prefill_varlen(q, k, v, gate, beta, state, cu_seqlens, chunk: int, out=None, workspace=None,
+                             stream=None):
+    """Chunked prefill of packed sequences of their own lengths.  Returns ``out``.
+
+    q, k, v, gate, out: [total][H][128]; beta: [total][H]; state: [n_seqs][H][128][128] (in place);
+    cu_seqlens: int32 CUDA tensor [n_seqs + 1] of token offsets.
+    """
+    if not isinstance(q, torch.Tensor) or q.dim() != 3 or q.shape[-1] != HEAD_DIM:
+        raise ValueError(f"q must be [total_tokens][heads][{HEAD_DIM}]")
+    total, H, _ = q.shape
+    if not (isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.dim() == 1 and cu_seqlens.numel() >= 2):
+        raise ValueError("cu_seqlens must be a 1-d tensor of n_seqs + 1 offsets")
+    n = cu_seqlens.numel() - 1
+    vs = (total, H, HEAD_DIM)
+    if out is None:
+        out = torch.empty(vs, dtype=torch.float32, device=q.device)
+    need = kda_chunk_prefill_varlen_workspace_bytes(n, H, total, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if not (workspace.device.type == "cuda" and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    args = [_check(nm, t, vs) for nm, t in (("q", q), ("k", k), ("v", v), ("gate", gate))]
+    args.append(_check("beta", beta, (total, H)))
+    args.append(_check("state", state, (n, H, HEAD_DIM, HEAD_DIM)))
+    args.append(_check("out", out, vs))
+    args.append(_check("cu_seqlens", cu_seqlens, (n + 1,), torch.int32))
+    rc = load_library().kda_chunk_prefill_varlen(*args, n, H, total, chunk, workspace.data_ptr(),
+                                                 workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_chunk_prefill_varlen", rc)
+    return out

@@ -113,6 +113,64 @@ KDA_API int kda_chunk_prefill(const float* q, const float* k, const float* v, co
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 
+namespace {
+
+// records and metadata of the varlen workspace: (record floats, byte size) or -1
+struct VarlenWs {
+    int64_t max_records, meta_offset_floats, bytes;
+};
+VarlenWs varlen_ws(int n_seqs, int heads, int total, int chunk)
+{
+    VarlenWs w{-1, -1, -1};
+    if (n_seqs < 1 || heads < 1 || total < 1 || !chunk_ok(chunk) || n_seqs > KDA_VARLEN_MAX_SEQS) return w;
+    const int64_t recs = mul({heads, (int64_t)total / chunk + n_seqs});  // >= heads * sum ceil(len / chunk)
+    if (recs < 0 || recs > (1LL << 30)) return w;
+    const int64_t floats = mul({recs, (int64_t)kda::chunk_record_floats(chunk)});
+    if (floats < 0) return w;
+    const int64_t meta = (floats + 63) / 64 * 64;  // 256-byte aligned
+    w.max_records = recs;
+    w.meta_offset_floats = meta;
+    w.bytes = meta * 4 + 2 * ((int64_t)n_seqs + 1) * 4;
+    return w;
+}
+
+}  // namespace
+
+KDA_API size_t kda_chunk_prefill_varlen_workspace_bytes(int n_seqs, int heads, int total_tokens, int chunk)
+{
+    const VarlenWs w = varlen_ws(n_seqs, heads, total_tokens, chunk);
+    return w.bytes < 0 ? 0 : (size_t)w.bytes;
+}
+
+KDA_API int kda_chunk_prefill_varlen(const float* q, const float* k, const float* v, const float* gate,
+                                     const float* beta, float* state, float* out, const int* cu_seqlens, int n_seqs,
+                                     int heads, int total_tokens, int chunk, void* workspace, size_t workspace_bytes,
+                                     void* stream)
+{
+    if (!q || !k || !v || !gate || !beta || !state || !out || !cu_seqlens) return KDA_ERR_INVALID_ARG;
+    if (!aligned({q, k, v, gate, state, out, workspace}) || !aligned({beta, cu_seqlens}, 4))
+        return KDA_ERR_INVALID_ARG;
+    if (n_seqs < 1 || heads < 1 || total_tokens < 1 || n_seqs > KDA_VARLEN_MAX_SEQS) return KDA_ERR_INVALID_ARG;
+    if (!chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
+    if (heads > KDA_PREFILL_MAX_HEADS) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)n_seqs * heads > 0x7fffffffLL / 64) return KDA_ERR_INVALID_ARG;  // scan grid
+    const VarlenWs w = varlen_ws(n_seqs, heads, total_tokens, chunk);
+    const int64_t vec = mul({total_tokens, heads, KDA_HEAD_DIM});
+    const int64_t sca = mul({total_tokens, heads});
+    const int64_t st = mul({n_seqs, heads, KDA_HEAD_DIM, KDA_HEAD_DIM});
+    if (w.bytes < 0 || vec < 0 || sca < 0 || st < 0) return KDA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < (size_t)w.bytes) return KDA_ERR_WORKSPACE;
+    const Range r[] = {{out, vec * 4}, {state, st * 4}, {workspace, w.bytes}, {q, vec * 4},
+                       {k, vec * 4},   {v, vec * 4},    {gate, vec * 4},      {beta, sca * 4},
+                       {cu_seqlens, ((int64_t)n_seqs + 1) * 4}};
+    if (any_overlap(r, 9, 3)) return KDA_ERR_INVALID_ARG;
+    const int rc = kda::launch_chunk_prefill_varlen(q, k, v, gate, beta, state, out, cu_seqlens, n_seqs, heads,
+                                                    total_tokens, chunk, static_cast<float*>(workspace),
+                                                    (size_t)w.meta_offset_floats, w.max_records,
+                                                    static_cast<hipStream_t>(stream));
+    return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
 KDA_API int kda_recurrent_k(const float* q, const float* k, const float* v, const float* gate, const float* beta,
                             float* state, float* out, float* snapshots, int n_snapshots, int batch, int heads,
                             int T, void* stream)

@@ -73,6 +73,83 @@ struct ChunkGeom {
 };
 
 __device__ __forceinline__ float4 lds4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+// Where the inputs of one chunk record are.  Rows are [token][head] rows of
+// 128 floats: row0 = first token * heads + head.  nvalid = tokens of the
+// sequence in the chunk (the rest are selected away); span = rows readable
+// from row0 before the end of the input buffers, at most C * heads.
+struct ChunkPos {
+    size_t row0;
+    int nvalid;
+    int span;
+};
+// One (sequence, head) of the scan: its first token, its length, its chunks
+// and the index of its first record.
+struct SeqPos {
+    size_t tok0;
+    int T;
+    int nchunks;
+    size_t rec0;
+};
+
+// Sequences of one common length T, each padded to t_pad = nchunks * C rows:
+// inputs [B][t_pad][heads][128]; records in (sequence, head, chunk) order.
+struct DenseLayout {
+    int heads, T, t_pad, nchunks, n_total;
+    __device__ int records() const { return n_total; }
+    template <int C>
+    __device__ ChunkPos chunk(int gc) const
+    {
+        const int bh = gc / nchunks, c = gc % nchunks;
+        ChunkPos p;
+        p.row0 = ((size_t)(bh / heads) * t_pad + (size_t)c * C) * heads + (bh % heads);
+        p.nvalid = T - c * C < C ? T - c * C : C;
+        p.span = C * heads;
+        return p;
+    }
+    __device__ SeqPos seq(int bh) const
+    {
+        return {(size_t)(bh / heads) * t_pad, T, nchunks, (size_t)bh * nchunks};
+    }
+};
+
+// Sequences of their own lengths packed back to back: inputs [total][heads][128],
+// sequence s at tokens cu[s] .. cu[s + 1] - 1; cb[s] = chunks of the sequences
+// before s; records in (sequence, head, chunk) order.  cu and cb are the
+// clamped, non-decreasing copies the setup kernel writes into the workspace.
+struct VarlenLayout {
+    int heads, total, n_seqs;
+    const int* cu;
+    const int* cb;
+    __device__ int records() const { return cb[n_seqs] * heads; }
+    template <int C>
+    __device__ ChunkPos chunk(int gc) const
+    {
+        // the sequence: the last s with cb[s] <= gc / heads (it has at least one chunk)
+        const int x = gc / heads;
+        int lo = 0, hi = n_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cb[mid] <= x) lo = mid;
+            else hi = mid - 1;
+        }
+        const int ns = cb[lo + 1] - cb[lo], local = gc - cb[lo] * heads;
+        const int h = local / ns, c = local % ns;
+        const int tok = cu[lo] + c * C, len = cu[lo + 1] - cu[lo];
+        ChunkPos p;
+        p.row0 = (size_t)tok * heads + h;
+        p.nvalid = len - c * C < C ? len - c * C : C;
+        const long long left = (long long)(total - tok) * heads - h;
+        p.span = left < C * heads ? (int)left : C * heads;
+        return p;
+    }
+    __device__ SeqPos seq(int bh) const
+    {
+        const int s = bh / heads, h = bh % heads;
+        const int ns = cb[s + 1] - cb[s];
+        return {(size_t)cu[s], cu[s + 1] - cu[s], ns, (size_t)cb[s] * heads + (size_t)h * ns};
+    }
+};
 __device__ __forceinline__ void lds4_st(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
 __device__ __forceinline__ float comp(const float4& v, int e)
 {
@@ -107,18 +184,19 @@ struct PrepInputs {
     float beta;
 };
 
-// Raw buffer descriptors over the C rows of one chunk of one (sequence, head)
-// in each input; row0 = (b T_pad + first row) heads + h.  With `live` false
-// the descriptors cover zero bytes: loads through them return zeros without
-// touching memory, so a wave can issue its usual load sequence for no chunk.
+// Raw buffer descriptors over the rows of one chunk of one (sequence, head) in
+// each input, from row p.row0 and p.span rows long (rows past the end of the
+// buffers read as zeros).  With `live` false the descriptors cover zero bytes:
+// loads through them return zeros without touching memory, so a wave can
+// issue its usual load sequence for no chunk.
 struct PrepSrc {
     rsrc_t q, k, g, v, b;
 };
-template <int C>
 __device__ __forceinline__ PrepSrc prep_src(const float* q, const float* k, const float* v, const float* gate,
-                                            const float* beta, size_t row0, int heads, bool live = true)
+                                            const float* beta, const ChunkPos& p, bool live = true)
 {
-    const uint32_t vec = live ? (uint32_t)(C * heads * kD * 4) : 0u, sca = live ? (uint32_t)(C * heads * 4) : 0u;
+    const uint32_t vec = live ? (uint32_t)p.span * (kD * 4) : 0u, sca = live ? (uint32_t)p.span * 4 : 0u;
+    const size_t row0 = p.row0;
     return {make_rsrc(q + row0 * kD, vec), make_rsrc(k + row0 * kD, vec), make_rsrc(gate + row0 * kD, vec),
             make_rsrc(v + row0 * kD, vec), make_rsrc(beta + row0, sca)};
 }
@@ -253,15 +331,15 @@ __device__ __forceinline__ void below_pair(int j, int& R, int& S)
     S = j - R * (R - 1) / 2;
 }
 
-// Persistent: one workgroup per CU walks the chunks gc = blockIdx.x, +gridDim.x, ...
-// (gc = (b * heads + h) * nchunks + c).  The inputs of the next chunk are read
-// into registers while the current one is computed and are staged into LDS at
-// its end.
-template <int C>
+// Persistent: one workgroup per CU walks the records gc = blockIdx.x, +gridDim.x,
+// ... (record gc of the layout: (sequence, head, chunk) in that order).  The
+// inputs of the next chunk are read into registers while the current one is
+// computed and are staged into LDS at its end.
+template <int C, class Layout>
 __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const float* __restrict__ gate, const float* __restrict__ beta, float* __restrict__ ws, int heads, int T,
-    int t_pad, int nchunks, int n_total)
+    const float* __restrict__ gate, const float* __restrict__ beta, float* __restrict__ ws, int heads,
+    Layout layout)
 {
     using G = ChunkGeom<C>;
     constexpr int NT = G::kTiles, LD = G::kLd, LDC = G::kLdc;
@@ -288,24 +366,18 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
 
     const int stride = gridDim.x;
 
-    auto row0_of = [&](int gc) {
-        const int bh = gc / nchunks, c = gc % nchunks;
-        return ((size_t)(bh / heads) * t_pad + (size_t)c * C) * heads + (bh % heads);
-    };
-    auto nvalid_of = [&](int gc) {
-        const int t0 = (gc % nchunks) * C;
-        return T - t0 < C ? T - t0 : C;
-    };
-
+    const int n_total = layout.records();
     int gc = blockIdx.x;
     PrepInputs<C> in;
+    ChunkPos pos;  // of record gc
     if (gc < n_total) {
-        const PrepSrc src = prep_src<C>(q, k, v, gate, beta, row0_of(gc), heads);
+        pos = layout.template chunk<C>(gc);
+        const PrepSrc src = prep_src(q, k, v, gate, beta, pos);
         prep_load_part<C>(in.k, src.k, heads, threadIdx.x);
         prep_load_part<C>(in.q, src.q, heads, threadIdx.x);
         prep_load_part<C>(in.g, src.g, heads, threadIdx.x);
         in.beta = prep_load_beta<C>(src.b, heads, threadIdx.x);
-        prep_stage<C>(in, sKr, sQr, sKc, sBeta, nvalid_of(gc), threadIdx.x);
+        prep_stage<C>(in, sKr, sQr, sKc, sBeta, pos.nvalid, threadIdx.x);
     }
     __syncthreads();
 
@@ -320,15 +392,16 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         float* const rec = ws + (size_t)gc * G::kRecord;
         float vb[NT][4];  // needed only at step 4c: its latency hides behind steps 2-4
-        prep_load_v<C>(vb, prep_src<C>(q, k, v, gate, beta, row0_of(gc), heads).v, heads, wave, l16, q4);
-        const int nvalid = nvalid_of(gc);
+        prep_load_v<C>(vb, prep_src(q, k, v, gate, beta, pos).v, heads, wave, l16, q4);
+        const int nvalid = pos.nvalid;
         // The next chunk's inputs are read in three parts, at steps 3, 5 and 6,
         // so the vector-memory path takes them while the matrix cores work.
         // After a workgroup's last chunk the loads go through empty descriptors
         // instead of being branched around, which keeps every wave's load
         // sequence, and so its wait counts, fixed.
         const int gn = gc + stride;
-        const PrepSrc nsrc = prep_src<C>(q, k, v, gate, beta, row0_of(gn < n_total ? gn : gc), heads, gn < n_total);
+        const ChunkPos npos = gn < n_total ? layout.template chunk<C>(gn) : pos;
+        const PrepSrc nsrc = prep_src(q, k, v, gate, beta, npos, gn < n_total);
 
         // 2. block-local cumulative log2 decay L of each column, then the tables
         //    decayed about row 7 of the block (L7 and the block totals wait in sE, sF)
@@ -550,7 +623,8 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         __syncthreads();
         // stage the next chunk (loaded during this one; after the last chunk the
         // staged copy is unused)
-        prep_stage<C>(in, sKr, sQr, sKc, sBeta, nvalid_of(gn < n_total ? gn : gc), tid);
+        prep_stage<C>(in, sKr, sQr, sKc, sBeta, npos.nvalid, tid);
+        pos = npos;
         __syncthreads();
     }
 }
@@ -757,10 +831,10 @@ __device__ __forceinline__ void scan_chunk(const ScanOps<C, NCT>& cur, ScanOps<C
 // One workgroup per (sequence, head, group of 16 NCT value columns); the 8 / NCT
 // groups of a head are mapped to one XCD (blockIdx % 8) so the head's records
 // are fetched into that XCD's L2 once.
-template <int C, int NCT>
+template <int C, int NCT, class Layout>
 __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(const float* __restrict__ ws,
                                                                   float* __restrict__ state, float* __restrict__ out,
-                                                                  int n_bh, int heads, int T, int t_pad, int nchunks)
+                                                                  int n_bh, int heads, Layout layout)
 {
     using G = ChunkGeom<C>;
     constexpr int NT = G::kTiles;
@@ -770,7 +844,10 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(const float* _
     const int slice = k8 % kGroups;
     const int bh = (k8 / kGroups) * 8 + xcd;
     if (bh >= n_bh) return;
-    const int b = bh / heads, h = bh % heads;
+    const SeqPos sq = layout.seq(bh);
+    const int nchunks = sq.nchunks, T = sq.T;
+    if (nchunks == 0) return;  // an empty sequence: its state is left as it is
+    const int h = bh % heads;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
     const int ct0 = NCT * slice, v0 = 16 * ct0;
@@ -782,7 +859,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(const float* _
     __shared__ __attribute__((aligned(16))) float sO[NT][NCT][kOutTile];
 
     float* const S_head = state + (size_t)bh * kD * kD;
-    float* const out_b = out + (size_t)b * t_pad * heads * kD;
+    float* const out_b = out + sq.tok0 * heads * kD;
     // byte offset of this lane's output row (16 xd + lane / 4) and columns
     // v0 + 4 (lane % 4) + 0..3 inside a chunk's output rows
     const int out_voff = ((16 * xd + (lane >> 2)) * heads * kD + h * kD + v0 + 4 * (lane & 3)) * 4;
@@ -793,7 +870,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(const float* _
         for (int e = 0; e < 4; ++e) st[e] = S_head[(size_t)(16 * wave + 4 * q4 + e) * kD + v0 + 16 * ct + l16];
         sS[0][wave][ct][lane] = st;
     }
-    const float* const rec0 = ws + (size_t)bh * nchunks * G::kRecord;
+    const float* const rec0 = ws + sq.rec0 * G::kRecord;
     auto rec = [&](int cc) {
         return make_rsrc(rec0 + (size_t)(cc < nchunks ? cc : nchunks - 1) * G::kRecord, (uint32_t)(G::kRecord * 4));
     };
@@ -833,41 +910,52 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(const float* _
     }
 }
 
-template <int C, int NCT>
-static int launch_scan(const float* ws, float* state, float* out, long long n_bh, int heads, int T, int t_pad,
-                       int nchunks, hipStream_t stream)
+template <int C, int NCT, class Layout>
+static int launch_scan(const float* ws, float* state, float* out, long long n_bh, int heads, const Layout& layout,
+                       hipStream_t stream)
 {
     const unsigned grid = (unsigned)(((n_bh + 7) / 8) * 64 / NCT);
-    hipLaunchKernelGGL((chunk_scan_kernel<C, NCT>), dim3(grid), dim3(kScanThreads), 0, stream, ws, state, out,
-                       (int)n_bh, heads, T, t_pad, nchunks);
+    hipLaunchKernelGGL((chunk_scan_kernel<C, NCT, Layout>), dim3(grid), dim3(kScanThreads), 0, stream, ws, state,
+                       out, (int)n_bh, heads, layout);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-template <int C>
+// max_records bounds the layout's record count (exact for the dense layout)
+template <int C, class Layout>
 static int launch_chunk(const float* q, const float* k, const float* v, const float* gate, const float* beta,
-                        float* state, float* out, int batch, int heads, int T, int t_pad, float* ws,
-                        hipStream_t stream)
+                        float* state, float* out, long long n_bh, int heads, long long max_records, float* ws,
+                        const Layout& layout, hipStream_t stream)
 {
-    const int nchunks = t_pad / C;
-    const long long n_bh = (long long)batch * heads;
-    const int n_total = (int)(n_bh * nchunks);
     // one persistent prepare workgroup per compute unit (its LDS use allows one)
     int dev = 0, n_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
         return -1;
-    const int grid_p = n_total < n_cu ? n_total : n_cu;
-    hipLaunchKernelGGL(chunk_prepare_kernel<C>, dim3((unsigned)grid_p), dim3(kPrepThreads), 0, stream, q, k, v,
-                       gate, beta, ws, heads, T, t_pad, nchunks, n_total);
-    if (hipGetLastError() != hipSuccess) return -1;
+    const int grid_p = max_records < n_cu ? (int)max_records : n_cu;
+    if (grid_p > 0) {
+        hipLaunchKernelGGL((chunk_prepare_kernel<C, Layout>), dim3((unsigned)grid_p), dim3(kPrepThreads), 0, stream,
+                           q, k, v, gate, beta, ws, heads, layout);
+        if (hipGetLastError() != hipSuccess) return -1;
+    }
     // 32-column workgroups when 16-column ones would not fit the compute units
     // in one round and 32-column ones still fill them (results are the same
     // bits either way: value columns never mix)
     if constexpr (C == 64) {
         if (n_bh * 8 > n_cu && n_bh * 4 >= n_cu)
-            return launch_scan<C, 2>(ws, state, out, n_bh, heads, T, t_pad, nchunks, stream);
+            return launch_scan<C, 2>(ws, state, out, n_bh, heads, layout, stream);
     }
-    return launch_scan<C, 1>(ws, state, out, n_bh, heads, T, t_pad, nchunks, stream);
+    return launch_scan<C, 1>(ws, state, out, n_bh, heads, layout, stream);
+}
+
+template <int C>
+static int launch_dense(const float* q, const float* k, const float* v, const float* gate, const float* beta,
+                        float* state, float* out, int batch, int heads, int T, int t_pad, float* ws,
+                        hipStream_t stream)
+{
+    const int nchunks = t_pad / C;
+    const long long n_bh = (long long)batch * heads;
+    const DenseLayout layout{heads, T, t_pad, nchunks, (int)(n_bh * nchunks)};
+    return launch_chunk<C>(q, k, v, gate, beta, state, out, n_bh, heads, n_bh * nchunks, ws, layout, stream);
 }
 
 int launch_chunk_prefill(const float* q, const float* k, const float* v, const float* gate, const float* beta,
@@ -875,9 +963,79 @@ int launch_chunk_prefill(const float* q, const float* k, const float* v, const f
                          float* workspace, hipStream_t stream)
 {
     switch (chunk) {
-    case 16: return launch_chunk<16>(q, k, v, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream);
-    case 32: return launch_chunk<32>(q, k, v, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream);
-    case 64: return launch_chunk<64>(q, k, v, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream);
+    case 16: return launch_dense<16>(q, k, v, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream);
+    case 32: return launch_dense<32>(q, k, v, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream);
+    case 64: return launch_dense<64>(q, k, v, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream);
+    default: return -1;
+    }
+}
+
+// Varlen set-up, one workgroup: token offsets clamped to [0, total] and made
+// non-decreasing (so no later access leaves the buffers whatever the caller
+// passed), and the chunk offsets cb[s] = sum over s' < s of ceil(len(s') / C).
+constexpr int kSetupThreads = 1024;
+__global__ __launch_bounds__(kSetupThreads) void varlen_setup_kernel(const int* __restrict__ cu_in, int n_seqs,
+                                                                     int total, int C, int* __restrict__ cu,
+                                                                     int* __restrict__ cb)
+{
+    __shared__ int s_max[kSetupThreads], s_sum[kSetupThreads];
+    const int tid = threadIdx.x, n = n_seqs + 1;
+    const int per = (n + kSetupThreads - 1) / kSetupThreads, i0 = tid * per, i1 = i0 + per < n ? i0 + per : n;
+    auto clamp = [&](int x) { return x < 0 ? 0 : (x > total ? total : x); };
+    // pass 1: the running maximum of this thread's entries
+    int m = 0;
+    for (int i = i0; i < i1; ++i) m = max(m, clamp(cu_in[i]));
+    s_max[tid] = m;
+    __syncthreads();
+    for (int off = 1; off < kSetupThreads; off <<= 1) {  // inclusive max-scan over the threads
+        const int o = tid >= off ? s_max[tid - off] : 0;
+        __syncthreads();
+        s_max[tid] = max(s_max[tid], o);
+        __syncthreads();
+    }
+    // pass 2: offsets and this thread's chunk count
+    int run = tid > 0 ? s_max[tid - 1] : 0, chunks = 0;
+    for (int i = i0; i < i1; ++i) {
+        const int prev = run;
+        run = max(run, clamp(cu_in[i]));
+        cu[i] = run;
+        if (i > 0) chunks += (run - prev + C - 1) / C;  // sequence i - 1 ends at run
+    }
+    s_sum[tid] = chunks;
+    __syncthreads();
+    for (int off = 1; off < kSetupThreads; off <<= 1) {  // inclusive sum-scan over the threads
+        const int o = tid >= off ? s_sum[tid - off] : 0;
+        __syncthreads();
+        s_sum[tid] += o;
+        __syncthreads();
+    }
+    // pass 3: chunk offsets (this thread's own offsets, read back; the one
+    // before its range is the previous thread's running maximum)
+    int prev = tid > 0 ? s_max[tid - 1] : 0, acc = tid > 0 ? s_sum[tid - 1] : 0;
+    for (int i = i0; i < i1; ++i) {
+        const int cur = cu[i];
+        if (i > 0) acc += (cur - prev + C - 1) / C;
+        cb[i] = acc;
+        prev = cur;
+    }
+}
+
+int launch_chunk_prefill_varlen(const float* q, const float* k, const float* v, const float* gate, const float* beta,
+                                float* state, float* out, const int* cu_seqlens, int n_seqs, int heads, int total,
+                                int chunk, float* workspace, size_t meta_offset_floats, long long max_records,
+                                hipStream_t stream)
+{
+    int* const cu = reinterpret_cast<int*>(workspace + meta_offset_floats);
+    int* const cb = cu + (n_seqs + 1);
+    hipLaunchKernelGGL(varlen_setup_kernel, dim3(1), dim3(kSetupThreads), 0, stream, cu_seqlens, n_seqs, total,
+                       chunk, cu, cb);
+    if (hipGetLastError() != hipSuccess) return -1;
+    const VarlenLayout layout{heads, total, n_seqs, cu, cb};
+    const long long n_bh = (long long)n_seqs * heads;
+    switch (chunk) {
+    case 16: return launch_chunk<16>(q, k, v, gate, beta, state, out, n_bh, heads, max_records, workspace, layout, stream);
+    case 32: return launch_chunk<32>(q, k, v, gate, beta, state, out, n_bh, heads, max_records, workspace, layout, stream);
+    case 64: return launch_chunk<64>(q, k, v, gate, beta, state, out, n_bh, heads, max_records, workspace, layout, stream);
     default: return -1;
     }
 }

@@ -32,6 +32,11 @@ int launch_chunk_prefill(const float* q, const float* k, const float* v, const f
                          float* state, float* out, int batch, int heads, int T, int t_pad, int chunk,
                          float* workspace, hipStream_t stream);
 
+int launch_chunk_prefill_varlen(const float* q, const float* k, const float* v, const float* gate, const float* beta,
+                                float* state, float* out, const int* cu_seqlens, int n_seqs, int heads, int total,
+                                int chunk, float* workspace, size_t meta_offset_floats, long long max_records,
+                                hipStream_t stream);
+
 int launch_front_end(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q, float* k, float* v,
                      float* snaps, int n_snap, int batch, int heads, int T, int conv_kernel, float l2_eps,
                      hipStream_t stream);

@@ -23,6 +23,11 @@ Inputs of the gated RMSNorm that follows the core (norm_inputs):
 * o_norm   : 1 + 0.1 * standard normal, BF16 patterns, [D] (a norm weight
   near one).
 
+Packed variable-length batches (varlen_lengths, varlen_inputs): sequence
+lengths drawn log-normally (so short and long sequences mix) and cut so they
+sum to the total; the token rows are one make_batch stream cut at the
+lengths, and each sequence has its own initial state.
+
 Inputs of the decode front end (front_end_inputs), conv_dim = 3 * heads * D:
 
 * qkv        : standard normal rounded to BF16, [B][T][conv_dim] (q | k | v).
@@ -62,6 +67,10 @@ ID_QKV, ID_CONV_W, ID_CONV_STATE = 9, 10, 11
 FRONT_END_WORKLOADS = {
     "front_end_b64_h32_k4": (64, 1, 32, 4, 1008),
     "front_end_b128_h32_k4_rows4": (128, 4, 32, 4, 1009),
+}
+# varlen prefill workloads: (total tokens, heads, chunk, mean sequence length, seed)
+VARLEN_WORKLOADS = {
+    "prefill_varlen_h32_t32768_c64": (32768, 32, 64, 2048, 1010),
 }
 # rms_norm_eps of the gated RMSNorm workloads (the pages name the config key, not its value)
 NORM_EPS = 1e-6
@@ -244,3 +253,31 @@ def front_end_inputs(seed: int, batch: int, rows: int, heads: int, conv_kernel: 
         st[b] = (s.astype(np.uint32) << 16).view(np.float32)
     w = 0.5 * _rng(seed, ID_CONV_W, 0, 0).standard_normal((C, conv_kernel), dtype=np.float32)
     return {"qkv": qkv, "conv_w": to_bf16_bits(w.astype(np.float32)), "conv_state": st}
+
+
+def varlen_lengths(seed: int, total: int, mean_len: int) -> list:
+    """Sequence lengths (each >= 1) summing to total: log-normal draws around mean_len."""
+    g = _rng(seed, 12, 0, 0)
+    lens, acc = [], 0
+    while acc < total:
+        n = max(1, int(round(mean_len * float(np.exp(g.normal(-0.5, 1.0))))))
+        n = min(n, total - acc)
+        lens.append(n)
+        acc += n
+    return lens
+
+
+def varlen_inputs(seed: int, lengths: list, heads: int, gate_lo: float, state_std: float,
+                  pad_tokens: int = 0, threads: int | None = None) -> dict:
+    """Packed [total][H][D] inputs (beta [total][H]) of sequences of the given lengths, with
+    cu_seqlens (int32 [n + 1]) and per-sequence states [n][H][D][D].  The token rows are one
+    stream (sequence 0 of make_batch over all rows, cut at the lengths); state s is the state of
+    sequence s of make_batch's recipe.  pad_tokens rows of zeros after the last sequence belong
+    to none."""
+    used = int(sum(lengths))
+    x = make_batch(seed, 1, heads, max(used, 1), gate_lo, 0.0, alloc_rows=max(used, 1) + pad_tokens,
+                   threads=threads)
+    out = {name: np.ascontiguousarray(x[name][0, :used + pad_tokens]) for name in ("q", "k", "v", "gate", "beta")}
+    out["state"] = np.stack([initial_state(seed, s, heads, state_std) for s in range(len(lengths))])
+    out["cu_seqlens"] = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    return out

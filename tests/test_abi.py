@@ -207,3 +207,42 @@ def test_decode_front_end_refusals(lib):
         p = list(P[:6])
         p[i] = p[j] + 16
         assert f(*p, None, 0, *ok_args, None) == bad, (i, j)
+
+
+@no_gpu
+def test_varlen_refusals(lib):
+    f = lib.kda_chunk_prefill_varlen
+    bad = kda.KDA_ERR_INVALID_ARG
+    need = kda.kda_chunk_prefill_varlen_workspace_bytes(3, 2, 100, 16)
+    assert need > 0
+    # records for heads * (total / chunk + n_seqs) chunks, then 2 (n_seqs + 1) int32 offsets
+    rec = 5 * 16 * 128 + 128
+    assert need == (-(-(2 * (100 // 16 + 3) * rec) // 64) * 64) * 4 + 2 * 4 * 4
+    for bad_args in [(0, 2, 100, 16), (3, 0, 100, 16), (3, 2, 0, 16), (3, 2, 100, 8), ((1 << 20) + 1, 1, 100, 16)]:
+        assert kda.kda_chunk_prefill_varlen_workspace_bytes(*bad_args) == 0
+    args = lambda **kw: dict(dict(n=3, H=2, total=100, C=16, ws=P[9], wsb=need), **kw)
+
+    def call(ptrs=None, **kw):
+        a = args(**kw)
+        p = list(P[:8]) if ptrs is None else ptrs
+        return f(*p, a["n"], a["H"], a["total"], a["C"], a["ws"], a["wsb"], None)
+    for i in range(8):
+        p = list(P[:8])
+        p[i] = None
+        assert call(p) == bad, i
+        p = list(P[:8])
+        p[i] += 2 if i in (4, 7) else 4  # beta and cu_seqlens need 4-byte alignment, the rest 16
+        assert call(p) == bad, i
+    assert call(n=0) == bad
+    assert call(H=0) == bad
+    assert call(total=0) == bad
+    assert call(C=48) == kda.KDA_ERR_UNSUPPORTED
+    assert call(wsb=need - 1) == kda.KDA_ERR_WORKSPACE
+    assert call(ws=None) == kda.KDA_ERR_WORKSPACE
+    p = list(P[:8])
+    p[6] = P[0] + 16  # out over q
+    assert call(p) == bad
+    p = list(P[:8])
+    p[7] = P[5] + 16  # cu_seqlens inside the state
+    assert call(p) == bad
+    assert call(ws=P[6] + 64) == bad  # workspace over out
