@@ -272,3 +272,4 @@ def kda_chunk_prefill_varlen(q, k, v, gate, beta, state, cu_seqlens, chunk: int,
     if rc != KDA_OK:
         raise KdaError("kda_chunk_prefill_varlen", rc)
     return out
+

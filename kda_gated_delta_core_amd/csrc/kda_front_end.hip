@@ -28,7 +28,7 @@
 // reduces sum y^2 in FP64 with shuffles alone (no barrier), which makes the
 // scale exact for any finite input.  The arithmetic does not depend on T, so
 // T rows in one call equal T one-row calls bit for bit.
-#include "kda_common.h"
+#include "kda_front_end.h"
 #include "kda_internal.h"
 
 namespace kda {
@@ -37,8 +37,6 @@ namespace {
 
 constexpr int kFeThreads = 256;             // four head vectors per workgroup, one per wave
 constexpr int kFeVecs = kFeThreads / 64;
-
-__device__ __forceinline__ float fe_bf16(uint32_t bits) { return __uint_as_float(bits << 16); }
 
 // one wave per (sequence, part, head) vector; lane l owns channels l and l + 64
 template <int K>
@@ -59,23 +57,9 @@ __global__ __launch_bounds__(kFeThreads) void front_end_kernel(const unsigned sh
     const int C = 3 * heads * kD;
     const size_t cv = (size_t)vec * kD;  // first channel of the vector
 
-    float w[2][K], s[2][K];
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int i = 0; i < K; ++i) w[m][i] = fe_bf16(conv_w[(cv + lane + 64 * m) * K + i]);
+    FeLane<K> f;
     float* const st = conv_state + ((size_t)b * C + cv) * K;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        float* const p = st + (size_t)(lane + 64 * m) * K;
-        if constexpr (K == 4) {
-            const float4 a = *reinterpret_cast<const float4*>(p);
-            s[m][0] = a.x; s[m][1] = a.y; s[m][2] = a.z; s[m][3] = a.w;
-        } else {
-#pragma unroll
-            for (int i = 0; i < K; ++i) s[m][i] = p[i];
-        }
-    }
+    fe_load(f, conv_w, st, cv, lane);
     float* const out = part == 0 ? q_out : (part == 1 ? k_out : v_out);
     const unsigned short* const xp = qkv + (size_t)b * T * C + cv + lane;  // row 0, channel l
     unsigned short xn0 = xp[0], xn1 = xp[64];
@@ -87,47 +71,13 @@ __global__ __launch_bounds__(kFeThreads) void front_end_kernel(const unsigned sh
             xn1 = xp[(size_t)(t + 1) * C + 64];
         }
         float y[2];
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-#pragma unroll
-            for (int i = 0; i + 1 < K; ++i) s[m][i] = s[m][i + 1];
-            s[m][K - 1] = fe_bf16(m == 0 ? x0 : x1);
-            float a = w[m][0] * s[m][0];
-#pragma unroll
-            for (int i = 1; i < K; ++i) a = fmaf(w[m][i], s[m][i], a);
-            y[m] = a / (1.0f + expf(-a));
-        }
-        if (part < 2) {
-            double ss = (double)y[0] * y[0] + (double)y[1] * y[1];
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off);
-            const double r = 1.0 / sqrt(ss + eps);
-            y[0] = (float)(y[0] * r);
-            y[1] = (float)(y[1] * r);
-        }
+        fe_row(f, x0, x1, part < 2, eps, y);
         float* const o = out + (row * heads + h) * kD + lane;
         o[0] = y[0];
         o[64] = y[1];
-        if (t < n_snap) {
-            float* const sn = snaps + (((size_t)t * batch + b) * C + cv) * K;
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                float* const p = sn + (size_t)(lane + 64 * m) * K;
-                if constexpr (K == 4) *reinterpret_cast<float4*>(p) = make_float4(s[m][0], s[m][1], s[m][2], s[m][3]);
-                else
-#pragma unroll
-                    for (int i = 0; i < K; ++i) p[i] = s[m][i];
-            }
-        }
+        if (t < n_snap) fe_store(f, snaps + (((size_t)t * batch + b) * C + cv) * K, lane);
     }
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        float* const p = st + (size_t)(lane + 64 * m) * K;
-        if constexpr (K == 4) *reinterpret_cast<float4*>(p) = make_float4(s[m][0], s[m][1], s[m][2], s[m][3]);
-        else
-#pragma unroll
-            for (int i = 0; i < K; ++i) p[i] = s[m][i];
-    }
+    fe_store(f, st, lane);
 }
 
 }  // namespace

@@ -70,6 +70,82 @@ __device__ __forceinline__ void state_st(float* p, float4 v)
 #endif
 }
 
+// One row of the walk for one thread of a slice: decay of its state rows,
+// partial read-outs, the reduction over key rows (xor shuffles inside the
+// wave, then the slice's waves in order through s_red), delta, the rank-1
+// update.  Returns the thread's four outputs (stored by row group 0).  The
+// caller has staged the key, query and decay of the row in LDS and passes the
+// thread's four values of v and the row's beta.
+template <int NSLICE>
+__device__ __forceinline__ float4 rec_row(float4 (&s)[RecGeom<NSLICE>::kRows], const float* s_k, const float* s_q,
+                                          const float* s_a, float (*s_red)[9][RecGeom<NSLICE>::kColGroups],
+                                          float4 vv, float bt, int cg, int rg, int wave, int lane)
+{
+    using G = RecGeom<NSLICE>;
+    // decay in place, then partial read-outs with the key and the query
+    float red[9];
+#pragma unroll
+    for (int x = 0; x < 9; ++x) red[x] = 0.f;
+    float kr[G::kRows];
+#pragma unroll
+    for (int m = 0; m < G::kRows; ++m) {
+        const int i = rg + G::kRowGroups * m;
+        const float a = s_a[i], kk = s_k[i], qq = s_q[i];
+        kr[m] = kk;
+        s[m].x *= a;
+        s[m].y *= a;
+        s[m].z *= a;
+        s[m].w *= a;
+        red[0] = fmaf(kk, s[m].x, red[0]);
+        red[1] = fmaf(kk, s[m].y, red[1]);
+        red[2] = fmaf(kk, s[m].z, red[2]);
+        red[3] = fmaf(kk, s[m].w, red[3]);
+        red[4] = fmaf(qq, s[m].x, red[4]);
+        red[5] = fmaf(qq, s[m].y, red[5]);
+        red[6] = fmaf(qq, s[m].z, red[6]);
+        red[7] = fmaf(qq, s[m].w, red[7]);
+        red[8] = fmaf(qq, kk, red[8]);
+    }
+    // reduce over the row groups of this wave ...
+#pragma unroll
+    for (int off = G::kColGroups; off < 64; off <<= 1) {
+#pragma unroll
+        for (int x = 0; x < 9; ++x) red[x] += __shfl_xor(red[x], off);
+    }
+    // ... then over the waves, in wave order
+    if (lane < G::kColGroups) {
+#pragma unroll
+        for (int x = 0; x < 9; ++x) s_red[wave][x][lane] = red[x];
+    }
+    __syncthreads();
+    float tot[9];
+#pragma unroll
+    for (int x = 0; x < 9; ++x) {
+        float acc = s_red[0][x][cg];
+#pragma unroll
+        for (int w = 1; w < G::kWaves; ++w) acc += s_red[w][x][cg];
+        tot[x] = acc;
+    }
+    // delta = beta (v - S^T k);  out = S_dec^T q + (q.k) delta  (= S_new^T q)
+    float4 d, o;
+    d.x = bt * (vv.x - tot[0]);
+    d.y = bt * (vv.y - tot[1]);
+    d.z = bt * (vv.z - tot[2]);
+    d.w = bt * (vv.w - tot[3]);
+    o.x = fmaf(tot[8], d.x, tot[4]);
+    o.y = fmaf(tot[8], d.y, tot[5]);
+    o.z = fmaf(tot[8], d.z, tot[6]);
+    o.w = fmaf(tot[8], d.w, tot[7]);
+#pragma unroll
+    for (int m = 0; m < G::kRows; ++m) {
+        s[m].x = fmaf(kr[m], d.x, s[m].x);
+        s[m].y = fmaf(kr[m], d.y, s[m].y);
+        s[m].z = fmaf(kr[m], d.z, s[m].z);
+        s[m].w = fmaf(kr[m], d.w, s[m].w);
+    }
+    return o;
+}
+
 template <int NSLICE>
 __global__ __launch_bounds__(256) void recurrent_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                         const float* __restrict__ v,
@@ -110,69 +186,8 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const float* __restrict_
         const float bt = beta[row];
         const float4 vv = ld4(v + row * kD + col);
         __syncthreads();
-
-        // decay in place, then partial read-outs with the key and the query
-        float red[9];
-#pragma unroll
-        for (int x = 0; x < 9; ++x) red[x] = 0.f;
-        float kr[G::kRows];
-#pragma unroll
-        for (int m = 0; m < G::kRows; ++m) {
-            const int i = rg + G::kRowGroups * m;
-            const float a = s_a[i], kk = s_k[i], qq = s_q[i];
-            kr[m] = kk;
-            s[m].x *= a;
-            s[m].y *= a;
-            s[m].z *= a;
-            s[m].w *= a;
-            red[0] = fmaf(kk, s[m].x, red[0]);
-            red[1] = fmaf(kk, s[m].y, red[1]);
-            red[2] = fmaf(kk, s[m].z, red[2]);
-            red[3] = fmaf(kk, s[m].w, red[3]);
-            red[4] = fmaf(qq, s[m].x, red[4]);
-            red[5] = fmaf(qq, s[m].y, red[5]);
-            red[6] = fmaf(qq, s[m].z, red[6]);
-            red[7] = fmaf(qq, s[m].w, red[7]);
-            red[8] = fmaf(qq, kk, red[8]);
-        }
-        // reduce over the row groups of this wave ...
-#pragma unroll
-        for (int off = G::kColGroups; off < 64; off <<= 1) {
-#pragma unroll
-            for (int x = 0; x < 9; ++x) red[x] += __shfl_xor(red[x], off);
-        }
-        // ... then over the waves, in wave order
-        if (lane < G::kColGroups) {
-#pragma unroll
-            for (int x = 0; x < 9; ++x) s_red[wave][x][lane] = red[x];
-        }
-        __syncthreads();
-        float tot[9];
-#pragma unroll
-        for (int x = 0; x < 9; ++x) {
-            float acc = s_red[0][x][cg];
-#pragma unroll
-            for (int w = 1; w < G::kWaves; ++w) acc += s_red[w][x][cg];
-            tot[x] = acc;
-        }
-        // delta = beta (v - S^T k);  out = S_dec^T q + (q.k) delta  (= S_new^T q)
-        float4 d, o;
-        d.x = bt * (vv.x - tot[0]);
-        d.y = bt * (vv.y - tot[1]);
-        d.z = bt * (vv.z - tot[2]);
-        d.w = bt * (vv.w - tot[3]);
-        o.x = fmaf(tot[8], d.x, tot[4]);
-        o.y = fmaf(tot[8], d.y, tot[5]);
-        o.z = fmaf(tot[8], d.z, tot[6]);
-        o.w = fmaf(tot[8], d.w, tot[7]);
+        const float4 o = rec_row<NSLICE>(s, s_k, s_q, s_a, s_red, vv, bt, cg, rg, wave, lane);
         if (rg == 0) st4(out + row * kD + col, o);
-#pragma unroll
-        for (int m = 0; m < G::kRows; ++m) {
-            s[m].x = fmaf(kr[m], d.x, s[m].x);
-            s[m].y = fmaf(kr[m], d.y, s[m].y);
-            s[m].z = fmaf(kr[m], d.z, s[m].z);
-            s[m].w = fmaf(kr[m], d.w, s[m].w);
-        }
         if (t < n_snap) {
             // snapshots are ordinary (cacheable) stores: a caller verifying
             // speculative rows reads the accepted one back soon after
