@@ -246,3 +246,17 @@ def test_varlen_refusals(lib):
     p[7] = P[5] + 16  # cu_seqlens inside the state
     assert call(p) == bad
     assert call(ws=P[6] + 64) == bad  # workspace over out
+
+
+def test_library_allocates_copies_and_synchronises_nothing():
+    """The library's only HIP imports are kernel registration, launch and device queries: no
+    allocation, copy, fill or synchronisation can happen inside any entry point (module page: the
+    forward calls allocate nothing)."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", kda.LIB_PATH], capture_output=True, text=True).stdout
+    hip = {line.split()[-1].split("@")[0] for line in out.splitlines() if "hip" in line.lower()}
+    allowed = {"__hipPopCallConfiguration", "__hipPushCallConfiguration", "__hipRegisterFatBinary",
+               "__hipRegisterFunction", "__hipUnregisterFatBinary", "hipDeviceGetAttribute", "hipGetDevice",
+               "hipGetLastError", "hipLaunchKernel"}
+    assert hip <= allowed, sorted(hip - allowed)
+    for bad in ("Malloc", "Free", "Memcpy", "Memset", "Synchronize", "HostRegister"):
+        assert not any(bad in name for name in hip), bad

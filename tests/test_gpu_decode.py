@@ -108,3 +108,21 @@ def test_decode_k_full_size_bitwise_and_sampled_parity(device):
     sn = host(snaps)
     for t in range(w.n_snap):
         assert_close(f"snapshot[{t}]", sn[t][sel], sn_ref[t])
+
+
+def test_decode_k_rollback_to_a_snapshot(device):
+    """Speculative verify: walk 5 rows with snapshots, accept 2, restore snapshot 1 and walk the
+    remaining rows again: outputs and final state equal the first walk's, bit for bit (the state
+    buffer and its snapshots are the resume points)."""
+    import torch
+    import kda_gated_delta_core_amd as kda
+    B, H, T = 3, 2, 5
+    announce(f"kda_recurrent_k rollback B={B} H={H} T={T}")
+    x = ki.make_batch(1404, B, H, T, -5.0, 0.02)
+    out, st, snaps = _decode_k(kda, x, B, H, T, T)
+    st2 = snaps[1].clone()  # the state after row 1
+    rest = lambda a: dev(np.ascontiguousarray(a[:, 2:]))
+    out2 = kda.kda_recurrent_k(rest(x["q"]), rest(x["k"]), rest(x["v"]), rest(x["gate"]), rest(x["beta"]), st2)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out[:, 2:])
+    assert torch.equal(st2, st)
