@@ -28,6 +28,12 @@
 //                 on one XCD so the head's records are fetched into that XCD's
 //                 L2 once.
 //
+// Both kernels take a layout: DenseLayout (sequences of one length, padded to
+// whole chunks) or VarlenLayout (sequences of their own lengths packed back
+// to back, located through offsets a one-workgroup set-up kernel clamps and
+// counts into the workspace).  Only the index arithmetic differs; a sequence
+// gets the same bits either way.
+//
 // Decay handling: the gate is accumulated in log2 units, separately inside
 // each 16-row block (L), so no running sum grows beyond 16 gates.  One pass
 // turns K and Q into tables decayed about row 7 of their own block,
