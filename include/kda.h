@@ -34,7 +34,9 @@
  *        snapshots          : [n_snapshots][batch][heads][D][D]
  *    rows = T_pad = ceil(T / chunk) * chunk for kda_chunk_prefill (the
  *    workspace page pads prefill buffers to whole chunks), rows = T for
- *    kda_recurrent_k and rows = 1 for kda_recurrent_step.
+ *    kda_recurrent_k and rows = 1 for kda_recurrent_step.  The packed
+ *    (varlen) prefill, the decode front end and the gated RMSNorm state
+ *    their own layouts at their declarations.
  *  * Inputs are read-only.  state is read and updated in place (layer page:
  *    decode updates the state in place).  out rows >= T are never written.
  *  * out, state, snapshots and workspace must not overlap each other or any
@@ -75,7 +77,7 @@ typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARG = -1, /* null or misaligned pointer, size < 1, bad n_snapshots / eps, overlap, overflow */
     KDA_ERR_UNSUPPORTED = -2, /* chunk not in {16, 32, 64}; conv_kernel above 4                          */
-    KDA_ERR_WORKSPACE = -3,   /* workspace smaller than kda_chunk_prefill_workspace_bytes()           */
+    KDA_ERR_WORKSPACE = -3,   /* workspace smaller than the matching *_workspace_bytes() query        */
     KDA_ERR_HIP = -4          /* the HIP runtime refused a launch                                     */
 } kda_status;
 
