@@ -258,3 +258,35 @@ def test_prefill_gate_domain_edges(device, C):
     x["beta"][0, :T, 1] = -0.3
     out, st, _ = _prefill(kda, x, T, C)
     _check_against_oracle(x, T, out, st)
+
+
+@pytest.mark.parametrize("B,H,T,C", [(1, 1, 1, 64), (300, 1, 17, 16), (2, 129, 33, 32), (5, 7, 64, 64)])
+def test_prefill_odd_shapes(device, B, H, T, C):
+    """One head and one token; many sequences of one head; a head count that leaves the scan's
+    8-head XCD groups and 8-column groups partly filled; whole chunks only."""
+    import kda_gated_delta_core_amd as kda
+    announce(f"kda_chunk_prefill odd shape B={B} H={H} T={T} C={C}")
+    t_pad = -(-T // C) * C
+    x = ki.make_batch(9100 + B + H, B, H, T, -5.0, 0.02, alloc_rows=t_pad, pad_value=float("nan"))
+    out, st, _ = _prefill(kda, x, T, C)
+    _check_against_oracle(x, T, out, st)
+
+
+@pytest.mark.timeout(600)
+def test_prefill_max_heads(device):
+    """KDA_PREFILL_MAX_HEADS heads (the most the header allows) in one call, sampled heads against
+    the oracle."""
+    import kda_gated_delta_core_amd as kda
+    B, H, T, C = 1, 16384, 20, 16
+    announce(f"kda_chunk_prefill max heads B={B} H={H} T={T} C={C}")
+    t_pad = -(-T // C) * C
+    x = ki.make_batch(9200, B, H, T, -5.0, 0.02, alloc_rows=t_pad)
+    out, st, _ = _prefill(kda, x, T, C)
+    o, s = host(out), host(st)
+    assert np.all(o[:, T:] == SENTINEL)
+    sel = [0, 1, 8191, 12345, H - 1]
+    sub = {n: np.ascontiguousarray(a[:, :, sel]) if a.ndim >= 3 and n != "state" else a for n, a in x.items()}
+    sub["state"] = np.ascontiguousarray(x["state"][:, sel])
+    o_ref, s_ref, _, _ = oracle.serial(sub["q"], sub["k"], sub["v"], sub["gate"], sub["beta"], sub["state"], T=T)
+    assert_close("core", o[:, :T][:, :, sel], o_ref)
+    assert_close("state", s[:, sel], s_ref)
