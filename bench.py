@@ -11,7 +11,9 @@ the small T=64 prefill, a packed prefill of 23 sequences of mixed lengths
 (32768 tokens, kda_chunk_prefill_varlen), the decode front end before the core
 (kda_decode_front_end: conv1d update + SiLU + L2, one step at B=64 and the
 k=4 rows at B=128), and the sigmoid-gated RMSNorm after it (kda_gated_rmsnorm)
-on the output of the T=8192 prefill and of a decode step.
+on the output of the T=8192 prefill and of a decode step.  The decode step,
+decode_k and the front end are also timed in their BF16 forms (the front end
+writing BF16 q | k | v packed per token, the core reading them).
 
 Inputs are seeded synthetic tensors (kda_inputs) resident in HBM before the
 timed region.  Decode states are rotated over buffers totalling >= 1 GiB so
@@ -48,9 +50,10 @@ def log(msg: str):
 
 
 # ---------------------------------------------------------------- algorithmic work
-def decode_bytes(B: int, H: int, T: int = 1, n_snap: int = 0) -> int:
-    """State read + write (+ snapshot writes) + q, k, v, gate reads + out write + beta reads."""
-    per_head = 2 * STATE_BYTES + n_snap * STATE_BYTES + T * (4 * D * 4 + D * 4 + 4)
+def decode_bytes(B: int, H: int, T: int = 1, n_snap: int = 0, qkv_bytes: int = 4) -> int:
+    """State read + write (+ snapshot writes) + q, k, v reads (qkv_bytes per element: 4 FP32, 2 BF16)
+    + gate read + out write + beta reads."""
+    per_head = 2 * STATE_BYTES + n_snap * STATE_BYTES + T * (3 * D * qkv_bytes + D * 4 + D * 4 + 4)
     return B * H * per_head
 
 
@@ -94,41 +97,56 @@ class Timer:
 
 
 # ---------------------------------------------------------------- workloads
-def bench_decode(torch, kda, ki, steps, warmup, timer):
+def _packed_bf16(torch, ki, x):
+    """q, k, v of a workload rounded to BF16 and packed per token as [B][T][3][H][D] on the device."""
+    import numpy as np
+    bits = np.stack([ki.to_bf16_bits(x[n]) for n in ("q", "k", "v")], axis=2)
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def bench_decode(torch, kda, ki, steps, warmup, timer, bf16=False):
     w = ki.WORKLOADS["decode_b64_h32"]
     B, H = w.batch, w.heads
     x = ki.workload_inputs(w)
     dev = lambda a: torch.from_numpy(a).cuda()
     q, k, v, g, b = (dev(x[n]) for n in ("q", "k", "v", "gate", "beta"))
+    qkv = _packed_bf16(torch, ki, x) if bf16 else None
     n_buf = max(2, -(-(1 << 30) // (B * H * STATE_BYTES)))  # >= 1 GiB of states
     states = [dev(x["state"]) for _ in range(n_buf)]
     out = torch.empty((B, 1, H, D), device="cuda")
     stream = torch.cuda.current_stream()
 
     def step(i):
-        kda.kda_recurrent_step(q, k, v, g, b, states[i % n_buf], out=out, stream=stream)
+        if bf16:
+            kda.kda_recurrent_step_bf16(qkv, g, b, states[i % n_buf], out=out, stream=stream)
+        else:
+            kda.kda_recurrent_step(q, k, v, g, b, states[i % n_buf], out=out, stream=stream)
 
     r = timer.run(step, steps, warmup)
-    nbytes = decode_bytes(B, H)
+    nbytes = decode_bytes(B, H, qkv_bytes=2 if bf16 else 4)
     return w, r, nbytes, n_buf
 
 
-def bench_decode_k(torch, kda, ki, steps, warmup, timer):
+def bench_decode_k(torch, kda, ki, steps, warmup, timer, bf16=False):
     w = ki.WORKLOADS["decode_k4_b128_h32"]
     B, H, T = w.batch, w.heads, w.T
     x = ki.workload_inputs(w)
     dev = lambda a: torch.from_numpy(a).cuda()
     q, k, v, g, b = (dev(x[n]) for n in ("q", "k", "v", "gate", "beta"))
+    qkv = _packed_bf16(torch, ki, x) if bf16 else None
     n_buf = max(2, -(-(1 << 30) // (B * H * STATE_BYTES)))
     states = [dev(x["state"]) for _ in range(n_buf)]
     snaps = torch.empty((w.n_snap, B, H, D, D), device="cuda")
     out = torch.empty((B, T, H, D), device="cuda")
 
     def step(i):
-        kda.kda_recurrent_k(q, k, v, g, b, states[i % n_buf], out=out, snapshots=snaps, n_snapshots=w.n_snap)
+        if bf16:
+            kda.kda_recurrent_k_bf16(qkv, g, b, states[i % n_buf], out=out, snapshots=snaps, n_snapshots=w.n_snap)
+        else:
+            kda.kda_recurrent_k(q, k, v, g, b, states[i % n_buf], out=out, snapshots=snaps, n_snapshots=w.n_snap)
 
     r = timer.run(step, steps, warmup)
-    return w, r, decode_bytes(B, H, T, w.n_snap)
+    return w, r, decode_bytes(B, H, T, w.n_snap, qkv_bytes=2 if bf16 else 4)
 
 
 def norm_bytes(rows: int, heads: int) -> int:
@@ -155,32 +173,41 @@ def bench_norm(torch, kda, ki, name, steps, warmup, timer):
     return r, norm_bytes(rows, heads), n_set
 
 
-def front_end_bytes(B: int, T: int, H: int, K: int, n_snap: int) -> int:
-    """Algorithmic bytes of one decode front-end call: BF16 qkv read, FP32 q, k, v written, the FP32
-    conv state read and written, snapshots written, BF16 conv weights read once."""
+def front_end_bytes(B: int, T: int, H: int, K: int, n_snap: int, out_bytes: int = 4) -> int:
+    """Algorithmic bytes of one decode front-end call: BF16 qkv read, q, k, v written (out_bytes per
+    element: 4 FP32, 2 BF16), the FP32 conv state read and written, snapshots written, BF16 conv
+    weights read once."""
     C = 3 * H * D
-    return B * T * C * (2 + 4) + B * C * K * 4 * (2 + n_snap) + C * K * 2
+    return B * T * C * (2 + out_bytes) + B * C * K * 4 * (2 + n_snap) + C * K * 2
 
 
-def bench_front_end(torch, kda, ki, name, steps, warmup, timer):
+def bench_front_end(torch, kda, ki, name, steps, warmup, timer, bf16=False):
     B, T, H, K, seed = ki.FRONT_END_WORKLOADS[name]
     n_snap = T if T > 1 else 0
     x = ki.front_end_inputs(seed, B, T, H, K)
     bits = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).cuda()
     qkv0, w, st0 = bits(x["qkv"]), bits(x["conv_w"]), torch.from_numpy(x["conv_state"]).cuda()
     vs = (B, T, H, D)
-    per_set = front_end_bytes(B, T, H, K, n_snap)
+    per_set = front_end_bytes(B, T, H, K, n_snap, 2 if bf16 else 4)
     n_set = max(2, -(-(1 << 30) // per_set))
     sets = []
     for _ in range(n_set):
         snaps = torch.empty((n_snap, B, 3 * H * D, K), device="cuda") if n_snap else None
-        sets.append((qkv0.clone(), st0.clone(), *(torch.empty(vs, device="cuda") for _ in range(3)), snaps))
+        if bf16:
+            outs = (torch.empty_like(qkv0), None, None)
+        else:
+            outs = tuple(torch.empty(vs, device="cuda") for _ in range(3))
+        sets.append((qkv0.clone(), st0.clone(), *outs, snaps))
     stream = torch.cuda.current_stream()
 
     def step(i):
         qkv, st, q, k, v, snaps = sets[i % n_set]
-        kda.kda_decode_front_end(qkv, w, st, H, ki.L2_EPS, q=q, k=k, v=v, conv_snapshots=snaps,
-                                 n_snapshots=n_snap, stream=stream)
+        if bf16:
+            kda.kda_decode_front_end_bf16(qkv, w, st, H, ki.L2_EPS, conv_out=q, conv_snapshots=snaps,
+                                          n_snapshots=n_snap, stream=stream)
+        else:
+            kda.kda_decode_front_end(qkv, w, st, H, ki.L2_EPS, q=q, k=k, v=v, conv_snapshots=snaps,
+                                     n_snapshots=n_snap, stream=stream)
 
     r = timer.run(step, steps, warmup)
     return r, per_set, n_set, B * T
@@ -428,6 +455,24 @@ def main():
         gbs = nbytes / r["launch_avg_s"] / 1e9
         workloads[w.name] = {"tokens_per_s": w.batch * w.T / r["s_per_step"], "us_per_call": r["s_per_step"] * 1e6,
                              "kernel_us": r["launch_avg_s"] * 1e6, "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+    # the same two decode workloads reading BF16 q | k | v packed per token (the BF16 front end's output)
+    if want("decode_bf16_b64_h32"):
+        log("decode_bf16_b64_h32")
+        w, r, nbytes, _ = bench_decode(torch, kda, ki, args.reps or args.steps, args.warmup, timer, bf16=True)
+        gbs = nbytes / r["launch_avg_s"] / 1e9
+        workloads["decode_bf16_b64_h32"] = {"tokens_per_s": w.batch / r["s_per_step"],
+                                            "us_per_step": r["s_per_step"] * 1e6,
+                                            "kernel_us": r["launch_avg_s"] * 1e6, "GB_per_s": gbs,
+                                            "hbm_frac": gbs / HBM_PEAK_GBS}
+    if want("decode_k4_bf16_b128_h32"):
+        log("decode_k4_bf16_b128_h32")
+        w, r, nbytes = bench_decode_k(torch, kda, ki, args.reps or max(10, args.steps // 2), args.warmup, timer,
+                                      bf16=True)
+        gbs = nbytes / r["launch_avg_s"] / 1e9
+        workloads["decode_k4_bf16_b128_h32"] = {"tokens_per_s": w.batch * w.T / r["s_per_step"],
+                                                "us_per_call": r["s_per_step"] * 1e6,
+                                                "kernel_us": r["launch_avg_s"] * 1e6, "GB_per_s": gbs,
+                                                "hbm_frac": gbs / HBM_PEAK_GBS}
     # (timed calls, untimed warm-up calls): the first ~20 calls on fresh buffers run ~10% slower
     # than the steady state, so the shorter prefill gets a warm-up as long as its timed run
     for name, steps, warm in (("prefill_h32_t8192_c64", 20, 20), ("prefill_b4_h32_t32768_c64", 4, 3),
@@ -455,15 +500,18 @@ def main():
                            "call_ms": r["launch_avg_s"] * 1e3, "algorithmic_TFLOP_per_s": tf,
                            "mfma_frac": tf / MFMA_F32_PEAK_TFLOPS, "sequences": len(lens),
                            "min_len": min(lens), "max_len": max(lens)}
-    for name in ki.FRONT_END_WORKLOADS:
-        if not want(name):
-            continue
-        log(name)
-        r, nbytes, n_set, tokens = bench_front_end(torch, kda, ki, name, args.reps or args.steps, args.warmup, timer)
-        gbs = nbytes / r["launch_avg_s"] / 1e9
-        workloads[name] = {"tokens_per_s": tokens / r["s_per_step"], "us_per_call": r["s_per_step"] * 1e6,
-                           "kernel_us": r["launch_avg_s"] * 1e6, "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
-                           "buffer_sets_rotated": n_set}
+    for base in ki.FRONT_END_WORKLOADS:
+        for bf16 in (False, True):
+            name = base.replace("front_end_", "front_end_bf16_") if bf16 else base
+            if not want(name):
+                continue
+            log(name)
+            r, nbytes, n_set, tokens = bench_front_end(torch, kda, ki, base, args.reps or args.steps, args.warmup,
+                                                       timer, bf16=bf16)
+            gbs = nbytes / r["launch_avg_s"] / 1e9
+            workloads[name] = {"tokens_per_s": tokens / r["s_per_step"], "us_per_call": r["s_per_step"] * 1e6,
+                               "kernel_us": r["launch_avg_s"] * 1e6, "GB_per_s": gbs,
+                               "hbm_frac": gbs / HBM_PEAK_GBS, "buffer_sets_rotated": n_set}
     for name in ki.NORM_WORKLOADS:
         if not want(name):
             continue

@@ -35,8 +35,8 @@
  *    rows = T_pad = ceil(T / chunk) * chunk for kda_chunk_prefill (the
  *    workspace page pads prefill buffers to whole chunks), rows = T for
  *    kda_recurrent_k and rows = 1 for kda_recurrent_step.  The packed
- *    (varlen) prefill, the decode front end and the gated RMSNorm state
- *    their own layouts at their declarations.
+ *    (varlen) prefill, the decode front end, the BF16 decode forms and the
+ *    gated RMSNorm state their own layouts at their declarations.
  *  * Inputs are read-only.  state is read and updated in place (layer page:
  *    decode updates the state in place).  out rows >= T are never written.
  *  * out, state, snapshots and workspace must not overlap each other or any
@@ -191,6 +191,29 @@ int kda_recurrent_k(const float* q, const float* k, const float* v, const float*
                     void* stream);
 
 /*
+ * The two decode entry points above with BF16 q, k, v packed per token, as
+ * the decode front end leaves them (workspace page, conv_out: [T, conv_dim]
+ * BF16 after conv and SiLU, with L2 already applied on the decode path;
+ * module page: every projection of the block runs in BF16).  gate, beta,
+ * state, out and snapshots are as above (FP32).
+ *
+ *   qkv : [batch][T][3][heads][128] BF16 (raw 16-bit patterns): q, then k,
+ *         then v of every head for each token, i.e. the [batch][T][conv_dim]
+ *         conv_out of kda_decode_front_end_bf16
+ *
+ * BF16 widens to FP32 exactly and the arithmetic is that of the FP32 entry
+ * points, so the results equal kda_recurrent_k / kda_recurrent_step on the
+ * widened q, k, v bit for bit; kda_recurrent_step_bf16 equals
+ * kda_recurrent_k_bf16 with T = 1, and T rows of kda_recurrent_k_bf16 equal T
+ * successive kda_recurrent_step_bf16 calls bit for bit.  Refusals are those of
+ * kda_recurrent_k, with qkv in place of q, k and v.
+ */
+int kda_recurrent_k_bf16(const uint16_t* qkv, const float* gate, const float* beta, float* state, float* out,
+                         float* snapshots, int n_snapshots, int batch, int heads, int T, void* stream);
+int kda_recurrent_step_bf16(const uint16_t* qkv, const float* gate, const float* beta, float* state, float* out,
+                            int batch, int heads, void* stream);
+
+/*
  * The step after the core: sigmoid-gated RMSNorm of the core's output (module
  * page, pipeline line: the core output goes through a sigmoid-gated RMSNorm
  * with weight o_norm and gate g_b(g_a(h)) before o_proj; the page notes that
@@ -260,6 +283,23 @@ int kda_gated_rmsnorm(const float* core, const uint16_t* out_gate, const uint16_
 int kda_decode_front_end(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q, float* k,
                          float* v, float* conv_snapshots, int n_snapshots, int batch, int heads, int T,
                          int conv_kernel, float l2_eps, void* stream);
+
+/*
+ * kda_decode_front_end with its output in BF16, in the input's own layout
+ * (workspace page, conv_out: [T, conv_dim] BF16 after conv + SiLU, L2 fused
+ * in on the decode path), ready for kda_recurrent_step_bf16 /
+ * kda_recurrent_k_bf16:
+ *
+ *   conv_out : [batch][T][conv_dim] BF16 = [batch][T][3][heads][128]
+ *
+ * Every value is the FP32 result kda_decode_front_end writes, rounded to the
+ * nearest BF16 (ties to even); conv_state and conv_snapshots are updated
+ * exactly as there.  All other arguments, conventions and refusals are those
+ * of kda_decode_front_end; conv_out must not overlap any other buffer.
+ */
+int kda_decode_front_end_bf16(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, uint16_t* conv_out,
+                              float* conv_snapshots, int n_snapshots, int batch, int heads, int T, int conv_kernel,
+                              float l2_eps, void* stream);
 
 #ifdef __cplusplus
 }

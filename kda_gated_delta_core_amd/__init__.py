@@ -26,7 +26,8 @@ KDA_ERR_HIP = -4
 
 EXPORTED = ("kda_status_string", "kda_chunk_prefill_workspace_bytes", "kda_chunk_prefill", "kda_recurrent_step",
             "kda_recurrent_k", "kda_gated_rmsnorm", "kda_decode_front_end",
-            "kda_chunk_prefill_varlen_workspace_bytes", "kda_chunk_prefill_varlen")
+            "kda_chunk_prefill_varlen_workspace_bytes", "kda_chunk_prefill_varlen", "kda_recurrent_k_bf16",
+            "kda_recurrent_step_bf16", "kda_decode_front_end_bf16")
 GATED_RMSNORM_MIN_EPS = 1e-30
 
 _lib = None
@@ -67,6 +68,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_gated_rmsnorm.restype = i
     lib.kda_decode_front_end.argtypes = [p] * 7 + [i] * 5 + [ctypes.c_float, p]
     lib.kda_decode_front_end.restype = i
+    lib.kda_recurrent_k_bf16.argtypes = [p] * 6 + [i] * 4 + [p]
+    lib.kda_recurrent_k_bf16.restype = i
+    lib.kda_recurrent_step_bf16.argtypes = [p] * 5 + [i, i, p]
+    lib.kda_recurrent_step_bf16.restype = i
+    lib.kda_decode_front_end_bf16.argtypes = [p] * 5 + [i] * 5 + [ctypes.c_float, p]
+    lib.kda_decode_front_end_bf16.restype = i
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -147,6 +154,54 @@ def kda_recurrent_step(q, k, v, gate, beta, state, out=None, stream=None):
     rc = load_library().kda_recurrent_step(*args, B, H, _stream_ptr(stream))
     if rc != KDA_OK:
         raise KdaError("kda_recurrent_step", rc)
+    return out
+
+
+def _packed_qkv(qkv, gate):
+    """Shapes of a BF16 q | k | v tensor, [B][T][3 H 128] or [B][T][3][H][128], against gate [B][T][H][128]."""
+    B, T, H = _vec_shapes(gate)
+    if not isinstance(qkv, torch.Tensor) or qkv.dim() not in (3, 5):
+        raise ValueError("qkv must be [batch][T][3 * heads * 128] or [batch][T][3][heads][128]")
+    shape = (B, T, 3 * H * HEAD_DIM) if qkv.dim() == 3 else (B, T, 3, H, HEAD_DIM)
+    return B, T, H, _check("qkv", qkv, shape, torch.bfloat16)
+
+
+def kda_recurrent_k_bf16(qkv, gate, beta, state, out=None, snapshots=None, n_snapshots: int = 0, stream=None):
+    """kda_recurrent_k with BF16 q | k | v packed per token (the BF16 front end's conv_out).  Returns ``out``.
+
+    qkv: bfloat16 [B][T][3 H 128] (or [B][T][3][H][128]); gate: [B][T][H][128]; beta: [B][T][H];
+    state: [B][H][128][128] (in place); snapshots: [>= n_snapshots][B][H][128][128].
+    """
+    B, T, H, qkv_ptr = _packed_qkv(qkv, gate)
+    vs = (B, T, H, HEAD_DIM)
+    if out is None:
+        out = torch.empty(vs, dtype=torch.float32, device=gate.device)
+    args = [qkv_ptr, _check("gate", gate, vs), _check("beta", beta, (B, T, H)),
+            _check("state", state, (B, H, HEAD_DIM, HEAD_DIM)), _check("out", out, vs)]
+    snap_ptr = None
+    if n_snapshots:
+        if snapshots is None or snapshots.dim() != 5 or snapshots.shape[0] < n_snapshots:
+            raise ValueError("snapshots must be [>= n_snapshots][B][H][128][128]")
+        snap_ptr = _check("snapshots", snapshots, (snapshots.shape[0], B, H, HEAD_DIM, HEAD_DIM))
+    rc = load_library().kda_recurrent_k_bf16(*args, snap_ptr, int(n_snapshots), B, H, T, _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_recurrent_k_bf16", rc)
+    return out
+
+
+def kda_recurrent_step_bf16(qkv, gate, beta, state, out=None, stream=None):
+    """One decode token per sequence from BF16 q | k | v.  qkv: [B][1][3 H 128]; gate: [B][1][H][128]."""
+    B, T, H, qkv_ptr = _packed_qkv(qkv, gate)
+    if T != 1:
+        raise ValueError("kda_recurrent_step_bf16 takes one row per sequence")
+    vs = (B, 1, H, HEAD_DIM)
+    if out is None:
+        out = torch.empty(vs, dtype=torch.float32, device=gate.device)
+    args = [qkv_ptr, _check("gate", gate, vs), _check("beta", beta, (B, 1, H)),
+            _check("state", state, (B, H, HEAD_DIM, HEAD_DIM)), _check("out", out, vs)]
+    rc = load_library().kda_recurrent_step_bf16(*args, B, H, _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_recurrent_step_bf16", rc)
     return out
 
 
@@ -235,6 +290,33 @@ def kda_decode_front_end(qkv, conv_w, conv_state, heads: int, l2_eps: float, q=N
     if rc != KDA_OK:
         raise KdaError("kda_decode_front_end", rc)
     return q, k, v
+
+
+def kda_decode_front_end_bf16(qkv, conv_w, conv_state, heads: int, l2_eps: float, conv_out=None,
+                              conv_snapshots=None, n_snapshots: int = 0, stream=None):
+    """kda_decode_front_end with BF16 output in the input's layout.  Returns conv_out [B][T][3 H 128] bfloat16."""
+    if not isinstance(qkv, torch.Tensor) or qkv.dim() != 3:
+        raise ValueError("qkv must be [batch][T][3 * heads * 128]")
+    B, T, C = qkv.shape
+    if C != 3 * heads * HEAD_DIM:
+        raise ValueError(f"qkv has {C} channels, expected 3 * {heads} * {HEAD_DIM}")
+    if conv_w.dim() != 2:
+        raise ValueError("conv_w must be [conv_dim][conv_kernel]")
+    K = conv_w.shape[1]
+    if conv_out is None:
+        conv_out = torch.empty((B, T, C), dtype=torch.bfloat16, device=qkv.device)
+    args = [_check("qkv", qkv, (B, T, C), torch.bfloat16), _check("conv_w", conv_w, (C, K), torch.bfloat16),
+            _check("conv_state", conv_state, (B, C, K)), _check("conv_out", conv_out, (B, T, C), torch.bfloat16)]
+    snap_ptr = None
+    if n_snapshots:
+        if conv_snapshots is None or conv_snapshots.dim() != 4 or conv_snapshots.shape[0] < n_snapshots:
+            raise ValueError("conv_snapshots must be [>= n_snapshots][B][conv_dim][conv_kernel]")
+        snap_ptr = _check("conv_snapshots", conv_snapshots, (conv_snapshots.shape[0], B, C, K))
+    rc = load_library().kda_decode_front_end_bf16(*args, snap_ptr, int(n_snapshots), B, heads, T, K, float(l2_eps),
+                                                  _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_decode_front_end_bf16", rc)
+    return conv_out
 
 
 def kda_chunk_prefill_varlen_workspace_bytes(n_seqs: int, heads: int, total_tokens: int, chunk: int) -> int:

@@ -171,12 +171,15 @@ KDA_API int kda_chunk_prefill_varlen(const float* q, const float* k, const float
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 
-KDA_API int kda_recurrent_k(const float* q, const float* k, const float* v, const float* gate, const float* beta,
-                            float* state, float* out, float* snapshots, int n_snapshots, int batch, int heads,
-                            int T, void* stream)
+namespace {
+
+// decode_k with FP32 q, k, v or, when qkv is not null, packed BF16 q | k | v rows
+int recurrent_checked(const float* q, const float* k, const float* v, const uint16_t* qkv, const float* gate,
+                      const float* beta, float* state, float* out, float* snapshots, int n_snapshots, int batch,
+                      int heads, int T, void* stream)
 {
-    if (!q || !k || !v || !gate || !beta || !state || !out) return KDA_ERR_INVALID_ARG;
-    if (!aligned({q, k, v, gate, state, out, snapshots}) || !aligned({beta}, 4)) return KDA_ERR_INVALID_ARG;
+    if ((!qkv && (!q || !k || !v)) || !gate || !beta || !state || !out) return KDA_ERR_INVALID_ARG;
+    if (!aligned({q, k, v, qkv, gate, state, out, snapshots}) || !aligned({beta}, 4)) return KDA_ERR_INVALID_ARG;
     if (batch < 1 || heads < 1 || T < 1) return KDA_ERR_INVALID_ARG;
     if (n_snapshots < 0 || n_snapshots > T || (n_snapshots > 0 && !snapshots)) return KDA_ERR_INVALID_ARG;
     const int64_t vec = mul({batch, T, heads, KDA_HEAD_DIM});
@@ -185,19 +188,45 @@ KDA_API int kda_recurrent_k(const float* q, const float* k, const float* v, cons
     const int64_t sn = mul({n_snapshots, batch, heads, KDA_HEAD_DIM, KDA_HEAD_DIM});
     if (vec < 0 || sca < 0 || st < 0 || sn < 0) return KDA_ERR_INVALID_ARG;
     if ((int64_t)batch * heads > kda::recurrent_max_units()) return KDA_ERR_INVALID_ARG;
-    const Range r[] = {{out, vec * 4}, {state, st * 4}, {n_snapshots ? snapshots : nullptr, sn * 4},
-                       {q, vec * 4},   {k, vec * 4},    {v, vec * 4},
-                       {gate, vec * 4}, {beta, sca * 4}};
-    if (any_overlap(r, 8, 3)) return KDA_ERR_INVALID_ARG;
-    const int rc = kda::launch_recurrent(q, k, v, gate, beta, state, out, n_snapshots ? snapshots : nullptr,
-                                         n_snapshots, batch, heads, T, static_cast<hipStream_t>(stream));
+    const Range r[] = {{out, vec * 4},  {state, st * 4}, {n_snapshots ? snapshots : nullptr, sn * 4},
+                       {q, vec * 4},    {k, vec * 4},    {v, vec * 4},
+                       {qkv, vec * 6},  {gate, vec * 4}, {beta, sca * 4}};
+    if (any_overlap(r, 9, 3)) return KDA_ERR_INVALID_ARG;
+    const int rc = kda::launch_recurrent(qkv ? nullptr : q, qkv ? nullptr : k, qkv ? nullptr : v, qkv, gate, beta,
+                                         state, out, n_snapshots ? snapshots : nullptr, n_snapshots, batch, heads, T,
+                                         static_cast<hipStream_t>(stream));
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+KDA_API int kda_recurrent_k(const float* q, const float* k, const float* v, const float* gate, const float* beta,
+                            float* state, float* out, float* snapshots, int n_snapshots, int batch, int heads,
+                            int T, void* stream)
+{
+    if (!q || !k || !v) return KDA_ERR_INVALID_ARG;
+    return recurrent_checked(q, k, v, nullptr, gate, beta, state, out, snapshots, n_snapshots, batch, heads, T,
+                             stream);
 }
 
 KDA_API int kda_recurrent_step(const float* q, const float* k, const float* v, const float* gate, const float* beta,
                                float* state, float* out, int batch, int heads, void* stream)
 {
     return kda_recurrent_k(q, k, v, gate, beta, state, out, nullptr, 0, batch, heads, 1, stream);
+}
+
+KDA_API int kda_recurrent_k_bf16(const uint16_t* qkv, const float* gate, const float* beta, float* state, float* out,
+                                 float* snapshots, int n_snapshots, int batch, int heads, int T, void* stream)
+{
+    if (!qkv) return KDA_ERR_INVALID_ARG;
+    return recurrent_checked(nullptr, nullptr, nullptr, qkv, gate, beta, state, out, snapshots, n_snapshots, batch,
+                             heads, T, stream);
+}
+
+KDA_API int kda_recurrent_step_bf16(const uint16_t* qkv, const float* gate, const float* beta, float* state,
+                                    float* out, int batch, int heads, void* stream)
+{
+    return kda_recurrent_k_bf16(qkv, gate, beta, state, out, nullptr, 0, batch, heads, 1, stream);
 }
 
 KDA_API int kda_gated_rmsnorm(const float* core, const uint16_t* out_gate, const uint16_t* o_norm, uint16_t* out,
@@ -215,12 +244,15 @@ KDA_API int kda_gated_rmsnorm(const float* core, const uint16_t* out_gate, const
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 
-KDA_API int kda_decode_front_end(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q, float* k,
-                                 float* v, float* conv_snapshots, int n_snapshots, int batch, int heads, int T,
-                                 int conv_kernel, float l2_eps, void* stream)
+namespace {
+
+// the front end with FP32 q, k, v outputs or, when conv_out is not null, BF16 conv_out
+int front_end_checked(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q, float* k, float* v,
+                      uint16_t* conv_out, float* conv_snapshots, int n_snapshots, int batch, int heads, int T,
+                      int conv_kernel, float l2_eps, void* stream)
 {
-    if (!qkv || !conv_w || !conv_state || !q || !k || !v) return KDA_ERR_INVALID_ARG;
-    if (!aligned({qkv, conv_w, conv_state, q, k, v, conv_snapshots})) return KDA_ERR_INVALID_ARG;
+    if (!qkv || !conv_w || !conv_state || (!conv_out && (!q || !k || !v))) return KDA_ERR_INVALID_ARG;
+    if (!aligned({qkv, conv_w, conv_state, q, k, v, conv_out, conv_snapshots})) return KDA_ERR_INVALID_ARG;
     if (batch < 1 || heads < 1 || T < 1 || heads > KDA_PREFILL_MAX_HEADS) return KDA_ERR_INVALID_ARG;
     if (n_snapshots < 0 || n_snapshots > T || (n_snapshots > 0 && !conv_snapshots)) return KDA_ERR_INVALID_ARG;
     if (conv_kernel < 1) return KDA_ERR_INVALID_ARG;
@@ -233,13 +265,34 @@ KDA_API int kda_decode_front_end(const uint16_t* qkv, const uint16_t* conv_w, fl
     const int64_t sn = mul({n_snapshots, batch, C, conv_kernel});
     const int64_t vec = mul({batch, T, heads, KDA_HEAD_DIM});
     if (x < 0 || w < 0 || st < 0 || sn < 0 || vec < 0) return KDA_ERR_INVALID_ARG;
-    if (mul({batch, 3, heads}) > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;  // one workgroup per head vector
-    const Range r[] = {{q, vec * 4},  {k, vec * 4},       {v, vec * 4},
+    if (mul({batch, 3, heads}) > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;  // one wave per head vector
+    if (conv_out) q = k = v = nullptr;
+    const Range r[] = {{q, vec * 4},          {k, vec * 4}, {v, vec * 4}, {conv_out, x * 2},
                        {conv_state, st * 4}, {n_snapshots ? conv_snapshots : nullptr, sn * 4},
-                       {qkv, x * 2},  {conv_w, w * 2}};
-    if (any_overlap(r, 7, 5)) return KDA_ERR_INVALID_ARG;
-    const int rc = kda::launch_front_end(qkv, conv_w, conv_state, q, k, v, n_snapshots ? conv_snapshots : nullptr,
-                                         n_snapshots, batch, heads, T, conv_kernel, l2_eps,
-                                         static_cast<hipStream_t>(stream));
+                       {qkv, x * 2},          {conv_w, w * 2}};
+    if (any_overlap(r, 8, 6)) return KDA_ERR_INVALID_ARG;
+    const int rc = kda::launch_front_end(qkv, conv_w, conv_state, q, k, v, conv_out,
+                                         n_snapshots ? conv_snapshots : nullptr, n_snapshots, batch, heads, T,
+                                         conv_kernel, l2_eps, static_cast<hipStream_t>(stream));
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+KDA_API int kda_decode_front_end(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q, float* k,
+                                 float* v, float* conv_snapshots, int n_snapshots, int batch, int heads, int T,
+                                 int conv_kernel, float l2_eps, void* stream)
+{
+    if (!q || !k || !v) return KDA_ERR_INVALID_ARG;
+    return front_end_checked(qkv, conv_w, conv_state, q, k, v, nullptr, conv_snapshots, n_snapshots, batch, heads, T,
+                             conv_kernel, l2_eps, stream);
+}
+
+KDA_API int kda_decode_front_end_bf16(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state,
+                                      uint16_t* conv_out, float* conv_snapshots, int n_snapshots, int batch,
+                                      int heads, int T, int conv_kernel, float l2_eps, void* stream)
+{
+    if (!conv_out) return KDA_ERR_INVALID_ARG;
+    return front_end_checked(qkv, conv_w, conv_state, nullptr, nullptr, nullptr, conv_out, conv_snapshots,
+                             n_snapshots, batch, heads, T, conv_kernel, l2_eps, stream);
 }

@@ -13,6 +13,17 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 __device__ __forceinline__ void st4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
 
+// BF16 is the top half of an IEEE binary32: widening is exact
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// binary32 -> BF16, round to nearest even; a NaN stays a (quiet) NaN of the same sign
+__device__ __forceinline__ uint32_t f32_to_bf16(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
 // Raw buffer access: a descriptor (base address, size in bytes) held in scalar
 // registers plus a 32-bit per-lane byte offset and a wave-uniform byte offset.
 // Lane offsets computed once outside a loop then need no per-iteration vector

@@ -8,8 +8,6 @@
 
 namespace kda {
 
-__device__ __forceinline__ float fe_bf16(uint32_t bits) { return __uint_as_float(bits << 16); }
-
 // the K slots (conv state) and K weights of one lane's two channels
 template <int K>
 struct FeLane {
@@ -24,7 +22,7 @@ __device__ __forceinline__ void fe_load(FeLane<K>& f, const unsigned short* __re
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int i = 0; i < K; ++i) f.w[m][i] = fe_bf16(conv_w[(cv + lane + 64 * m) * K + i]);
+        for (int i = 0; i < K; ++i) f.w[m][i] = bf16_to_f32(conv_w[(cv + lane + 64 * m) * K + i]);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
         const float* const p = st + (size_t)(lane + 64 * m) * K;
@@ -63,7 +61,7 @@ __device__ __forceinline__ void fe_row(FeLane<K>& f, unsigned short x0, unsigned
     for (int m = 0; m < 2; ++m) {
 #pragma unroll
         for (int i = 0; i + 1 < K; ++i) f.s[m][i] = f.s[m][i + 1];
-        f.s[m][K - 1] = fe_bf16(m == 0 ? x0 : x1);
+        f.s[m][K - 1] = bf16_to_f32(m == 0 ? x0 : x1);
         float a = f.w[m][0] * f.s[m][0];
 #pragma unroll
         for (int i = 1; i < K; ++i) a = fmaf(f.w[m][i], f.s[m][i], a);

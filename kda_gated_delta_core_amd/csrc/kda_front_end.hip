@@ -14,8 +14,11 @@
 // qkv BF16 [B][T][conv_dim] (workspace page, qkv_proj), w BF16 [conv_dim][K]
 // (config page, Glm5NextKdaWeights::conv), conv state FP32 [B][conv_dim][K]
 // (config page, conv_state_elems), l2_eps applied inside the square root
-// (config page, l2_eps).  Outputs q, k, v FP32 [B][T][H][128], the layout of
-// kda_recurrent_step / kda_recurrent_k.
+// (config page, l2_eps).  Outputs either q, k, v FP32 [B][T][H][128], the
+// layout of kda_recurrent_step / kda_recurrent_k, or BF16 conv_out in the
+// input's own [B][T][conv_dim] layout (workspace page, conv_out: BF16, L2
+// already applied on the decode path), rounded to nearest even from the same
+// FP32 values, which kda_recurrent_step_bf16 / kda_recurrent_k_bf16 read.
 //
 // One wave per (sequence, part, head) vector; lane l owns channels l and
 // l + 64 and keeps their K slots and K weights in registers for all T rows, so
@@ -39,12 +42,13 @@ constexpr int kFeThreads = 256;             // four head vectors per workgroup, 
 constexpr int kFeVecs = kFeThreads / 64;
 
 // one wave per (sequence, part, head) vector; lane l owns channels l and l + 64
-template <int K>
+template <int K, bool kBf16Out>
 __global__ __launch_bounds__(kFeThreads) void front_end_kernel(const unsigned short* __restrict__ qkv,
                                                                const unsigned short* __restrict__ conv_w,
                                                                float* __restrict__ conv_state,
                                                                float* __restrict__ q_out, float* __restrict__ k_out,
                                                                float* __restrict__ v_out,
+                                                               unsigned short* __restrict__ conv_out,
                                                                float* __restrict__ snaps, int n_snap, int batch,
                                                                int heads, int T, double eps)
 {
@@ -72,30 +76,50 @@ __global__ __launch_bounds__(kFeThreads) void front_end_kernel(const unsigned sh
         }
         float y[2];
         fe_row(f, x0, x1, part < 2, eps, y);
-        float* const o = out + (row * heads + h) * kD + lane;
-        o[0] = y[0];
-        o[64] = y[1];
+        if constexpr (kBf16Out) {
+            unsigned short* const o = conv_out + (row * 3 * heads + vec) * kD + lane;  // [b][t][part][h][.]
+            o[0] = (unsigned short)f32_to_bf16(y[0]);
+            o[64] = (unsigned short)f32_to_bf16(y[1]);
+        } else {
+            float* const o = out + (row * heads + h) * kD + lane;
+            o[0] = y[0];
+            o[64] = y[1];
+        }
         if (t < n_snap) fe_store(f, snaps + (((size_t)t * batch + b) * C + cv) * K, lane);
     }
     fe_store(f, st, lane);
 }
 
+template <int K>
+void launch_fe(dim3 grid, const unsigned short* x, const unsigned short* w, float* conv_state, float* q, float* k,
+               float* v, unsigned short* conv_out, float* snaps, int n_snap, int batch, int heads, int T, double eps,
+               hipStream_t stream)
+{
+    if (conv_out)
+        hipLaunchKernelGGL((front_end_kernel<K, true>), grid, dim3(kFeThreads), 0, stream, x, w, conv_state, nullptr,
+                           nullptr, nullptr, conv_out, snaps, n_snap, batch, heads, T, eps);
+    else
+        hipLaunchKernelGGL((front_end_kernel<K, false>), grid, dim3(kFeThreads), 0, stream, x, w, conv_state, q, k, v,
+                           nullptr, snaps, n_snap, batch, heads, T, eps);
+}
+
 }  // namespace
 
 int launch_front_end(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q, float* k, float* v,
-                     float* snaps, int n_snap, int batch, int heads, int T, int conv_kernel, float l2_eps,
-                     hipStream_t stream)
+                     uint16_t* conv_out, float* snaps, int n_snap, int batch, int heads, int T, int conv_kernel,
+                     float l2_eps, hipStream_t stream)
 {
     const long long n_vec = (long long)batch * 3 * heads;
-    const dim3 grid((unsigned)((n_vec + kFeVecs - 1) / kFeVecs)), block(kFeThreads);
+    const dim3 grid((unsigned)((n_vec + kFeVecs - 1) / kFeVecs));
     const auto* x = reinterpret_cast<const unsigned short*>(qkv);
     const auto* w = reinterpret_cast<const unsigned short*>(conv_w);
+    auto* co = reinterpret_cast<unsigned short*>(conv_out);
     const double eps = l2_eps;
     switch (conv_kernel) {
-    case 1: hipLaunchKernelGGL(front_end_kernel<1>, grid, block, 0, stream, x, w, conv_state, q, k, v, snaps, n_snap, batch, heads, T, eps); break;
-    case 2: hipLaunchKernelGGL(front_end_kernel<2>, grid, block, 0, stream, x, w, conv_state, q, k, v, snaps, n_snap, batch, heads, T, eps); break;
-    case 3: hipLaunchKernelGGL(front_end_kernel<3>, grid, block, 0, stream, x, w, conv_state, q, k, v, snaps, n_snap, batch, heads, T, eps); break;
-    case 4: hipLaunchKernelGGL(front_end_kernel<4>, grid, block, 0, stream, x, w, conv_state, q, k, v, snaps, n_snap, batch, heads, T, eps); break;
+    case 1: launch_fe<1>(grid, x, w, conv_state, q, k, v, co, snaps, n_snap, batch, heads, T, eps, stream); break;
+    case 2: launch_fe<2>(grid, x, w, conv_state, q, k, v, co, snaps, n_snap, batch, heads, T, eps, stream); break;
+    case 3: launch_fe<3>(grid, x, w, conv_state, q, k, v, co, snaps, n_snap, batch, heads, T, eps, stream); break;
+    case 4: launch_fe<4>(grid, x, w, conv_state, q, k, v, co, snaps, n_snap, batch, heads, T, eps, stream); break;
     default: return -1;
     }
     return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -23,9 +23,10 @@ namespace kda {
 // lower-triangular decayed Q K^T of the chunk.
 constexpr size_t chunk_record_floats(int C) { return 5 * (size_t)C * 128 + 128; }
 
-int launch_recurrent(const float* q, const float* k, const float* v, const float* gate, const float* beta,
-                     float* state, float* out, float* snaps, int n_snap, int batch, int heads, int T,
-                     hipStream_t stream);
+// q, k, v FP32 [B][T][H][128]; or, when qkv is not null, q | k | v BF16 [B][T][3][H][128] from qkv
+int launch_recurrent(const float* q, const float* k, const float* v, const uint16_t* qkv, const float* gate,
+                     const float* beta, float* state, float* out, float* snaps, int n_snap, int batch, int heads,
+                     int T, hipStream_t stream);
 long long recurrent_max_units();
 
 int launch_chunk_prefill(const float* q, const float* k, const float* v, const float* gate, const float* beta,
@@ -37,9 +38,10 @@ int launch_chunk_prefill_varlen(const float* q, const float* k, const float* v, 
                                 int chunk, float* workspace, size_t meta_offset_floats, long long max_records,
                                 hipStream_t stream);
 
+// outputs FP32 q, k, v [B][T][H][128]; or, when conv_out is not null, BF16 [B][T][3][H][128] there
 int launch_front_end(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q, float* k, float* v,
-                     float* snaps, int n_snap, int batch, int heads, int T, int conv_kernel, float l2_eps,
-                     hipStream_t stream);
+                     uint16_t* conv_out, float* snaps, int n_snap, int batch, int heads, int T, int conv_kernel,
+                     float l2_eps, hipStream_t stream);
 
 int launch_gated_rmsnorm(const float* core, const uint16_t* gate, const uint16_t* weight, uint16_t* out,
                          long long n_vec, float eps, hipStream_t stream);

@@ -31,16 +31,6 @@ constexpr int kGroups = kNormThreads / kLanes;           // vector groups per bl
 constexpr int kGroupVecs = 2;                            // vectors per group
 constexpr int kVecPerBlock = kGroups * kGroupVecs;
 
-__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
-
-// round to nearest even; NaN stays a (quiet) NaN of the same sign
-__device__ __forceinline__ uint32_t f32_to_bf16(float x)
-{
-    const uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
 __device__ __forceinline__ float sigmoid(float g) { return 1.0f / (1.0f + expf(-g)); }
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // 8 BF16 values

@@ -19,6 +19,13 @@
 // row groups inside the wave plus one LDS exchange across the four waves.
 // No atomics: every thread sums in the same fixed order, so results are
 // deterministic.
+//
+// Inputs come in two forms: FP32 q, k, v as three [B][T][H][128] arrays, or
+// BF16 q | k | v packed per token as [B][T][3][H][128], the layout the decode
+// front end writes (workspace page, conv_out: BF16 [T, conv_dim] after conv,
+// SiLU and, on the decode path, L2).  BF16 widens to FP32 exactly and the row
+// body is shared, so the BF16 form on BF16 data gives the bits of the FP32
+// form on the widened values.
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -146,9 +153,10 @@ __device__ __forceinline__ float4 rec_row(float4 (&s)[RecGeom<NSLICE>::kRows], c
     return o;
 }
 
-template <int NSLICE>
+template <int NSLICE, bool kPackedBf16>
 __global__ __launch_bounds__(256) void recurrent_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                         const float* __restrict__ v,
+                                                        const unsigned short* __restrict__ qkv,
                                                         const float* __restrict__ gate,
                                                         const float* __restrict__ beta, float* __restrict__ state,
                                                         float* __restrict__ out, float* __restrict__ snaps,
@@ -178,13 +186,30 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const float* __restrict_
 
     for (int t = 0; t < T; ++t) {
         const size_t row = ((size_t)b * T + t) * heads + h;  // (b, t, h)
-        if (tid < kD) {
-            s_k[tid] = k[row * kD + tid];
-            s_q[tid] = q[row * kD + tid];
-            s_a[tid] = expf(gate[row * kD + tid]);
+        float bt;
+        float4 vv;
+        if constexpr (kPackedBf16) {
+            // q of head h in token (b, t); k and v follow at a stride of heads * 128
+            const unsigned short* const x = qkv + (((size_t)b * T + t) * 3 * heads + h) * kD;
+            const size_t part = (size_t)heads * kD;
+            if (tid < kD) {
+                s_k[tid] = bf16_to_f32(x[part + tid]);
+                s_q[tid] = bf16_to_f32(x[tid]);
+                s_a[tid] = expf(gate[row * kD + tid]);
+            }
+            bt = beta[row];
+            const uint2 u = *reinterpret_cast<const uint2*>(x + 2 * part + col);
+            vv = make_float4(bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xffffu),
+                             bf16_to_f32(u.y >> 16));
+        } else {
+            if (tid < kD) {
+                s_k[tid] = k[row * kD + tid];
+                s_q[tid] = q[row * kD + tid];
+                s_a[tid] = expf(gate[row * kD + tid]);
+            }
+            bt = beta[row];
+            vv = ld4(v + row * kD + col);
         }
-        const float bt = beta[row];
-        const float4 vv = ld4(v + row * kD + col);
         __syncthreads();
         const float4 o = rec_row<NSLICE>(s, s_k, s_q, s_a, s_red, vv, bt, cg, rg, wave, lane);
         if (rg == 0) st4(out + row * kD + col, o);
@@ -200,13 +225,18 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const float* __restrict_
     for (int m = 0; m < G::kRows; ++m) state_st(S_head + (size_t)(rg + G::kRowGroups * m) * kD + col, s[m]);
 }
 
-int launch_recurrent(const float* q, const float* k, const float* v, const float* gate, const float* beta,
-                     float* state, float* out, float* snaps, int n_snap, int batch, int heads, int T,
-                     hipStream_t stream)
+int launch_recurrent(const float* q, const float* k, const float* v, const uint16_t* qkv, const float* gate,
+                     const float* beta, float* state, float* out, float* snaps, int n_snap, int batch, int heads,
+                     int T, hipStream_t stream)
 {
     const unsigned grid = ((unsigned)batch * (unsigned)heads + 7u) / 8u * 8u * kRecSlices;
-    hipLaunchKernelGGL(recurrent_kernel<kRecSlices>, dim3(grid), dim3(256), 0, stream, q, k, v, gate, beta, state,
-                       out, snaps, n_snap, batch, heads, T);
+    const auto* x = reinterpret_cast<const unsigned short*>(qkv);
+    if (qkv)
+        hipLaunchKernelGGL((recurrent_kernel<kRecSlices, true>), dim3(grid), dim3(256), 0, stream, nullptr, nullptr,
+                           nullptr, x, gate, beta, state, out, snaps, n_snap, batch, heads, T);
+    else
+        hipLaunchKernelGGL((recurrent_kernel<kRecSlices, false>), dim3(grid), dim3(256), 0, stream, q, k, v, nullptr,
+                           gate, beta, state, out, snaps, n_snap, batch, heads, T);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

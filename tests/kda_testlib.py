@@ -39,3 +39,24 @@ def assert_close(name: str, gpu, ref, atol: float = ATOL, rtol: float = RTOL_L2)
 
 def announce(msg: str):
     print(f"[gpu] {msg}", flush=True)
+
+
+def assert_within_one_ulp(name, got, ref):
+    """got: BF16 values as float64; ref: exact fp64 values.  Every finite element within one BF16
+    unit in the last place of the exact value (what FP32 arithmetic and one rounding to nearest can
+    guarantee), NaN where the exact value is NaN, and exact zeros kept."""
+    import torch
+    ref = np.asarray(ref, dtype=np.float64)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), name
+    g, r = got[fin], ref[fin]
+    a = np.abs(r)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    ulp = np.where(a > 0, 2.0 ** np.maximum(e - 7, -133), 2.0 ** -133)
+    err = np.abs(g - r)
+    worst = float(np.max(err / ulp)) if err.size else 0.0
+    exact = torch.from_numpy(r).to(torch.bfloat16).double().numpy()
+    n_exact = int(np.sum(g == exact))
+    print(f"{name}: worst {worst:.3f} ulp, {n_exact}/{err.size} equal to the rounded exact value", flush=True)
+    assert worst <= 1.0, name
+    assert np.all(g[a == 0] == 0), name

@@ -210,6 +210,58 @@ def test_decode_front_end_refusals(lib):
 
 
 @no_gpu
+def test_bf16_decode_refusals(lib):
+    bad = kda.KDA_ERR_INVALID_ARG
+    # kda_recurrent_k_bf16 / _step_bf16: qkv, gate, beta, state, out
+    fk, fs = lib.kda_recurrent_k_bf16, lib.kda_recurrent_step_bf16
+    for i in range(5):
+        p = list(P[:5])
+        p[i] = None
+        assert fk(*p, None, 0, 4, 2, 3, None) == bad, i
+        assert fs(*p, 4, 2, None) == bad, i
+        p = list(P[:5])
+        p[i] += 2 if i == 2 else 8  # beta needs 4-byte alignment, the others 16-byte
+        assert fk(*p, None, 0, 4, 2, 3, None) == bad, i
+        assert fs(*p, 4, 2, None) == bad, i
+    assert fk(*P[:5], None, 0, 4, 2, 0, None) == bad            # k == 0
+    assert fk(*P[:5], None, 0, 0, 2, 3, None) == bad
+    assert fk(*P[:5], None, 0, 4, 0, 3, None) == bad
+    assert fk(*P[:5], P[6], 4, 4, 2, 3, None) == bad            # n_snapshots > T
+    assert fk(*P[:5], None, 2, 4, 2, 3, None) == bad            # snapshots NULL
+    assert fk(*P[:5], P[6] + 8, 2, 4, 2, 3, None) == bad        # misaligned snapshots
+    # out over the packed rows (3 * 2 bytes per q element), the state over out, snapshots over the state
+    p = list(P[:5])
+    p[4] = P[0] + 4 * 3 * 3 * 128 * 2 - 16  # B=4, H=3: the last 16 bytes of the rows
+    assert fs(*p, 4, 3, None) == bad
+    p = list(P[:5])
+    p[3] = P[4] + 16
+    assert fs(*p, 4, 2, None) == bad
+    assert fk(*P[:5], P[3] + 256, 2, 4, 2, 3, None) == bad
+    assert fk(*P[:5], None, 0, 1 << 20, 1 << 12, 1 << 20, None) == bad  # size overflow
+    # kda_decode_front_end_bf16: qkv, conv_w, conv_state, conv_out
+    f = lib.kda_decode_front_end_bf16
+    ok_args = (4, 2, 3, 4, 1e-6)
+    for i in range(4):
+        p = list(P[:4])
+        p[i] = None
+        assert f(*p, None, 0, *ok_args, None) == bad, i
+        p = list(P[:4])
+        p[i] += 8
+        assert f(*p, None, 0, *ok_args, None) == bad, i
+    assert f(*P[:4], None, 0, 4, 2, 3, 5, 1e-6, None) == kda.KDA_ERR_UNSUPPORTED
+    assert f(*P[:4], None, 0, 4, 2, 3, 4, 0.0, None) == bad
+    assert f(*P[:4], None, 2, *ok_args, None) == bad            # snapshots NULL
+    assert f(*P[:4], P[6], 4, *ok_args, None) == bad            # n_snapshots > T
+    p = list(P[:4])
+    p[3] = P[0] + 16                                            # conv_out over qkv
+    assert f(*p, None, 0, *ok_args, None) == bad
+    p = list(P[:4])
+    p[3] = P[2] + 16                                            # conv_out over the conv state
+    assert f(*p, None, 0, *ok_args, None) == bad
+    assert f(*P[:4], P[3] + 16, 1, *ok_args, None) == bad       # snapshots over conv_out
+
+
+@no_gpu
 def test_varlen_refusals(lib):
     f = lib.kda_chunk_prefill_varlen
     bad = kda.KDA_ERR_INVALID_ARG

@@ -8,7 +8,7 @@ import torch
 
 import kda_inputs as ki
 import oracle
-from kda_testlib import announce
+from kda_testlib import announce, assert_within_one_ulp
 
 pytestmark = pytest.mark.gpu
 D = 128
@@ -34,24 +34,6 @@ def _run(kda, core, gate_bits, w_bits, eps, out=None):
     got = kda.kda_gated_rmsnorm(c, _dev_bits(gate_bits), _dev_bits(w_bits), eps, out=out)
     torch.cuda.synchronize()
     return oracle.bf16_to_f64(_host_f64(got))
-
-
-def assert_within_one_ulp(name, got, ref):
-    """got: BF16 values as float64; ref: exact fp64 values."""
-    ref = np.asarray(ref, dtype=np.float64)
-    fin = np.isfinite(ref)
-    assert np.array_equal(np.isnan(got), np.isnan(ref)), name
-    g, r = got[fin], ref[fin]
-    a = np.abs(r)
-    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
-    ulp = np.where(a > 0, 2.0 ** np.maximum(e - 7, -133), 2.0 ** -133)
-    err = np.abs(g - r)
-    worst = float(np.max(err / ulp)) if err.size else 0.0
-    exact = torch.from_numpy(r).to(torch.bfloat16).double().numpy()
-    n_exact = int(np.sum(g == exact))
-    print(f"{name}: worst {worst:.3f} ulp, {n_exact}/{err.size} equal to the rounded exact value", flush=True)
-    assert worst <= 1.0, name
-    assert np.all(g[a == 0] == 0), name
 
 
 @pytest.mark.parametrize("rows,heads,scale", [(37, 3, 1.0), (1, 1, 1e-3), (5, 32, 1e3), (64, 32, 1.0)])
