@@ -6,6 +6,12 @@ the C names; tensors must be contiguous CUDA (HIP) tensors, float32 unless
 the header says BF16 (then torch.bfloat16), in the layouts it documents.  PyTorch provides device memory and the stream
 (the current torch stream unless one is given).  There is no CPU fallback: if
 the library cannot be loaded every call raises.
+
+Outputs the binding allocates (``out=None`` and the like) are allocated on the
+current stream, like the result of any torch operation; a caller launching on
+another stream keeps them alive until that stream is done, or passes its own.
+A prefill workspace the binding allocates is allocated on the launch stream,
+so its memory is reused only by work ordered after the call.
 """
 from __future__ import annotations
 
@@ -91,6 +97,20 @@ def _stream_ptr(stream) -> int | None:
     if stream is None:
         stream = torch.cuda.current_stream()
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _workspace(nbytes: int, device, stream) -> torch.Tensor:
+    """A workspace the binding allocates for one call.  It is allocated on the stream the call is
+    launched on: the caching allocator then hands its memory out again only to work ordered after
+    this call on that stream, even though the tensor is dropped as soon as the call returns."""
+    if stream is None:
+        s = torch.cuda.current_stream(device)
+    elif isinstance(stream, torch.cuda.Stream):
+        s = stream
+    else:
+        s = torch.cuda.ExternalStream(int(stream), device=device)
+    with torch.cuda.stream(s):
+        return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
 def _check(name: str, t: torch.Tensor, shape: tuple, dtype=torch.float32) -> int:
@@ -223,7 +243,7 @@ def kda_chunk_prefill(q, k, v, gate, beta, state, T: int, chunk: int, out=None, 
         out = torch.empty(vs, dtype=torch.float32, device=q.device)
     need = kda_chunk_prefill_workspace_bytes(B, H, int(T), chunk)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q.device, stream)
     if not (workspace.device.type == "cuda" and workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous GPU tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
@@ -341,7 +361,7 @@ def kda_chunk_prefill_varlen(q, k, v, gate, beta, state, cu_seqlens, chunk: int,
         out = torch.empty(vs, dtype=torch.float32, device=q.device)
     need = kda_chunk_prefill_varlen_workspace_bytes(n, H, total, chunk)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q.device, stream)
     if not (workspace.device.type == "cuda" and workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous GPU tensor")
     args = [_check(nm, t, vs) for nm, t in (("q", q), ("k", k), ("v", v), ("gate", gate))]
