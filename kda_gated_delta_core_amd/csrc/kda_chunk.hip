@@ -80,14 +80,16 @@ struct ChunkGeom {
 
 __device__ __forceinline__ float4 lds4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
-// Where the inputs of one chunk record are.  Rows are [token][head] rows of
-// 128 floats: row0 = first token * heads + head.  nvalid = tokens of the
-// sequence in the chunk (the rest are selected away); span = rows readable
-// from row0 before the end of the input buffers, at most C * heads.
+// Where the inputs of one chunk record are, and which record it is.  Rows are
+// [token][head] rows of 128 floats: row0 = first token * heads + head.  nvalid
+// = tokens of the sequence in the chunk (the rest are selected away); span =
+// rows readable from row0 before the end of the input buffers, at most
+// C * heads; rec = the record's index in the workspace.
 struct ChunkPos {
     size_t row0;
     int nvalid;
     int span;
+    int rec;
 };
 // One (sequence, head) of the scan: its first token, its length, its chunks
 // and the index of its first record.
@@ -99,18 +101,24 @@ struct SeqPos {
 };
 
 // Sequences of one common length T, each padded to t_pad = nchunks * C rows:
-// inputs [B][t_pad][heads][128]; records in (sequence, head, chunk) order.
+// inputs [B][t_pad][heads][128]; records stored in (sequence, head, chunk)
+// order.  The prepare takes them in (sequence, chunk, head) order: the records
+// in flight at one time then read every head of a run of consecutive tokens,
+// a dense region of the inputs, rather than every chunk of a few heads,
+// 512-byte rows scattered over the whole sequence.
 struct DenseLayout {
     int heads, T, t_pad, nchunks, n_total;
     __device__ int records() const { return n_total; }
     template <int C>
-    __device__ ChunkPos chunk(int gc) const
+    __device__ ChunkPos chunk(int i) const  // i-th record in processing order
     {
-        const int bh = gc / nchunks, c = gc % nchunks;
+        const int per_seq = nchunks * heads;
+        const int b = i / per_seq, c = (i % per_seq) / heads, h = i % heads;
         ChunkPos p;
-        p.row0 = ((size_t)(bh / heads) * t_pad + (size_t)c * C) * heads + (bh % heads);
+        p.row0 = ((size_t)b * t_pad + (size_t)c * C) * heads + h;
         p.nvalid = T - c * C < C ? T - c * C : C;
         p.span = C * heads;
+        p.rec = (b * heads + h) * nchunks + c;
         return p;
     }
     __device__ SeqPos seq(int bh) const
@@ -121,7 +129,8 @@ struct DenseLayout {
 
 // Sequences of their own lengths packed back to back: inputs [total][heads][128],
 // sequence s at tokens cu[s] .. cu[s + 1] - 1; cb[s] = chunks of the sequences
-// before s; records in (sequence, head, chunk) order.  cu and cb are the
+// before s; records stored in (sequence, head, chunk) order and prepared in
+// (sequence, chunk, head) order, as for DenseLayout.  cu and cb are the
 // clamped, non-decreasing copies the setup kernel writes into the workspace.
 struct VarlenLayout {
     int heads, total, n_seqs;
@@ -129,24 +138,25 @@ struct VarlenLayout {
     const int* cb;
     __device__ int records() const { return cb[n_seqs] * heads; }
     template <int C>
-    __device__ ChunkPos chunk(int gc) const
+    __device__ ChunkPos chunk(int i) const  // i-th record in processing order
     {
-        // the sequence: the last s with cb[s] <= gc / heads (it has at least one chunk)
-        const int x = gc / heads;
+        // the sequence: the last s with cb[s] <= i / heads (it has at least one chunk)
+        const int x = i / heads;
         int lo = 0, hi = n_seqs - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (cb[mid] <= x) lo = mid;
             else hi = mid - 1;
         }
-        const int ns = cb[lo + 1] - cb[lo], local = gc - cb[lo] * heads;
-        const int h = local / ns, c = local % ns;
+        const int ns = cb[lo + 1] - cb[lo], local = i - cb[lo] * heads;
+        const int c = local / heads, h = local % heads;
         const int tok = cu[lo] + c * C, len = cu[lo + 1] - cu[lo];
         ChunkPos p;
         p.row0 = (size_t)tok * heads + h;
         p.nvalid = len - c * C < C ? len - c * C : C;
         const long long left = (long long)(total - tok) * heads - h;
         p.span = left < C * heads ? (int)left : C * heads;
+        p.rec = cb[lo] * heads + h * ns + c;
         return p;
     }
     __device__ SeqPos seq(int bh) const
@@ -338,9 +348,10 @@ __device__ __forceinline__ void below_pair(int j, int& R, int& S)
 }
 
 // Persistent: one workgroup per CU walks the records gc = blockIdx.x, +gridDim.x,
-// ... (record gc of the layout: (sequence, head, chunk) in that order).  The
-// inputs of the next chunk are read into registers while the current one is
-// computed and are staged into LDS at its end.
+// ... of the layout's processing order (the layout gives each one's inputs and
+// its place in the workspace).  The inputs of the next chunk are read into
+// registers while the current one is computed and are staged into LDS at its
+// end.
 template <int C, class Layout>
 __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
@@ -375,7 +386,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
     const int n_total = layout.records();
     int gc = blockIdx.x;
     PrepInputs<C> in;
-    ChunkPos pos;  // of record gc
+    ChunkPos pos;  // of the gc-th record in processing order
     if (gc < n_total) {
         pos = layout.template chunk<C>(gc);
         const PrepSrc src = prep_src(q, k, v, gate, beta, pos);
@@ -396,7 +407,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         asm volatile("" : "+v"(tid));
         const int lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        float* const rec = ws + (size_t)gc * G::kRecord;
+        float* const rec = ws + (size_t)pos.rec * G::kRecord;
         float vb[NT][4];  // needed only at step 4c: its latency hides behind steps 2-4
         prep_load_v<C>(vb, prep_src(q, k, v, gate, beta, pos).v, heads, wave, l16, q4);
         const int nvalid = pos.nvalid;
