@@ -347,6 +347,16 @@ __device__ __forceinline__ void below_pair(int j, int& R, int& S)
     S = j - R * (R - 1) / 2;
 }
 
+// Record stores of chunk_prepare are non-temporal: a prefill's records are
+// written once and read back by the scan only after the whole prepare, by which
+// time the caches hold the last records written, not the first ones the scan
+// wants (T=8192, H=32: 673 MB of records).  Streaming them past the caches made
+// the T=8192 prefill 3.8% faster.
+__device__ __forceinline__ void rec_st4(float* p, float4 v)
+{
+    __builtin_nontemporal_store(floatx4{v.x, v.y, v.z, v.w}, reinterpret_cast<floatx4*>(p));
+}
+
 // Persistent: one workgroup per CU walks the records gc = blockIdx.x, +gridDim.x,
 // ... of the layout's processing order (the layout gives each one's inputs and
 // its place in the workspace).  The inputs of the next chunk are read into
@@ -536,7 +546,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
                 if (e == 2) o.z = val;
                 if (e == 3) o.w = val;
             }
-            st4(rec + G::kOffKt + ((size_t)(wave * NT + y) * 64 + lane) * 4, o);
+            rec_st4(rec + G::kOffKt + ((size_t)(wave * NT + y) * 64 + lane) * 4, o);
         }
         __syncthreads();
         // finish the split pairs
@@ -608,9 +618,9 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
             }
             wt[X] = accW;
             ut[X] = accU;
-            st4(rec + G::kOffW + ((size_t)(X * 8 + wave) * 64 + lane) * 4, acc_to_atile(accW, xpose, lane));
+            rec_st4(rec + G::kOffW + ((size_t)(X * 8 + wave) * 64 + lane) * 4, acc_to_atile(accW, xpose, lane));
             // U in the scan's accumulator layout: [row tile][16-column block][lane][4]
-            st4(rec + G::kOffU + ((size_t)(X * 8 + wave) * 64 + lane) * 4,
+            rec_st4(rec + G::kOffU + ((size_t)(X * 8 + wave) * 64 + lane) * 4,
                 make_float4(accU[0], accU[1], accU[2], accU[3]));
         }
         // 6. P = e^G o Q - M W and R = M U.  The W and U accumulator tiles are, lane
@@ -634,8 +644,8 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
             floatx4 pt;
 #pragma unroll
             for (int e = 0; e < 4; ++e) pt[e] = qh[X][e] - mw[e];
-            st4(rec + G::kOffP + ((size_t)(X * 8 + wave) * 64 + lane) * 4, acc_to_atile(pt, xpose, lane));
-            st4(rec + G::kOffR + ((size_t)(X * 8 + wave) * 64 + lane) * 4, make_float4(mu[0], mu[1], mu[2], mu[3]));
+            rec_st4(rec + G::kOffP + ((size_t)(X * 8 + wave) * 64 + lane) * 4, acc_to_atile(pt, xpose, lane));
+            rec_st4(rec + G::kOffR + ((size_t)(X * 8 + wave) * 64 + lane) * 4, make_float4(mu[0], mu[1], mu[2], mu[3]));
         }
         __syncthreads();
         // stage the next chunk (loaded during this one; after the last chunk the
