@@ -39,8 +39,10 @@ def _jobs(kda):
         x = ki.varlen_inputs(1601, lens, 8, -5.0, 0.02)
         d = {n: torch.from_numpy(x[n]).cuda() for n in ("q", "k", "v", "gate", "beta", "state", "cu_seqlens")}
         out = torch.zeros_like(d["q"])
+        ws = torch.empty(kda.kda_chunk_prefill_varlen_workspace_bytes(len(lens), 8, sum(lens), 64),
+                         dtype=torch.uint8, device="cuda")
         launch = lambda s: kda.kda_chunk_prefill_varlen(d["q"], d["k"], d["v"], d["gate"], d["beta"], d["state"],
-                                                        d["cu_seqlens"], 64, out=out, stream=s)
+                                                        d["cu_seqlens"], 64, out=out, workspace=ws, stream=s)
         return launch, lambda: (out, d["state"])
     jobs.append(("kda_chunk_prefill_varlen 4 sequences H=8", varlen))
 
@@ -138,3 +140,23 @@ def test_binding_workspace_is_not_handed_out_while_its_call_runs(device):
     torch.cuda.synchronize()
     assert bool((other == 0xA5).all()), "the call's workspace memory was handed out while the call ran"
     assert torch.equal(out, ref_out) and torch.equal(d["state"], ref_state)
+
+
+def test_calls_with_caller_buffers_allocate_nothing(device):
+    """With every output and workspace passed in, a round of calls of every entry point leaves torch's
+    allocator where it was (the library itself links no HIP allocation call)."""
+    import kda_gated_delta_core_amd as kda
+    jobs = _jobs(kda)
+    ready = [setup() for _, setup in jobs]
+    for launch, _ in ready:  # first round: any lazy initialisation of the runtime happens here
+        launch(None)
+    torch.cuda.synchronize()
+    state = lambda: (torch.cuda.memory_stats()["allocation.all.allocated"], torch.cuda.memory_allocated(),
+                     torch.cuda.memory_reserved())
+    before = state()
+    announce(f"allocator before: {before[0]} allocations so far, {before[1]} B allocated, {before[2]} B reserved")
+    for _ in range(3):
+        for launch, _ in ready:
+            launch(None)
+    torch.cuda.synchronize()
+    assert state() == before, (before, state())
