@@ -629,23 +629,38 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         prep_load_part<C>(in.g, nsrc.g, heads, tid);
         in.beta = prep_load_beta<C>(nsrc.b, heads, tid);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int X = 0; X < NT; ++X) {
-            floatx4 mw = {0.f, 0.f, 0.f, 0.f}, mu = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int y = 0; y <= X; ++y) {
-                const float4 m4 = lds4(&sM[(16 * X + l16) * LDC + 16 * y + 4 * q4]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    mw = mfma4(comp(m4, e), wt[y][e], mw);
-                    mu = mfma4(comp(m4, e), ut[y][e], mu);
-                }
-            }
+        //    Row blocks X and NT - 1 - X go together (equal work, 4 (NT + 1) MFMAs
+        //    each way), so four independent accumulation chains keep the matrix
+        //    core busy instead of two; each block's sum runs in the same order.
+        auto put_pr = [&](int X, const floatx4& mw, const floatx4& mu) {
             floatx4 pt;
 #pragma unroll
             for (int e = 0; e < 4; ++e) pt[e] = qh[X][e] - mw[e];
             rec_st4(rec + G::kOffP + ((size_t)(X * 8 + wave) * 64 + lane) * 4, acc_to_atile(pt, xpose, lane));
             rec_st4(rec + G::kOffR + ((size_t)(X * 8 + wave) * 64 + lane) * 4, make_float4(mu[0], mu[1], mu[2], mu[3]));
+        };
+#pragma unroll
+        for (int X0 = 0; X0 < (NT + 1) / 2; ++X0) {
+            const int X1 = NT - 1 - X0;  // == X0 for the middle block of an odd count
+            floatx4 mw0 = {0.f, 0.f, 0.f, 0.f}, mu0 = {0.f, 0.f, 0.f, 0.f};
+            floatx4 mw1 = {0.f, 0.f, 0.f, 0.f}, mu1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int y = 0; y <= X1; ++y) {
+                const float4 m1 = lds4(&sM[(16 * X1 + l16) * LDC + 16 * y + 4 * q4]);
+                float4 m0 = m1;
+                if (X1 != X0 && y <= X0) m0 = lds4(&sM[(16 * X0 + l16) * LDC + 16 * y + 4 * q4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    mw1 = mfma4(comp(m1, e), wt[y][e], mw1);
+                    mu1 = mfma4(comp(m1, e), ut[y][e], mu1);
+                    if (X1 != X0 && y <= X0) {
+                        mw0 = mfma4(comp(m0, e), wt[y][e], mw0);
+                        mu0 = mfma4(comp(m0, e), ut[y][e], mu0);
+                    }
+                }
+            }
+            if (X1 != X0) put_pr(X0, mw0, mu0);
+            put_pr(X1, mw1, mu1);
         }
         __syncthreads();
         // stage the next chunk (loaded during this one; after the last chunk the
