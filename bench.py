@@ -13,7 +13,9 @@ the small T=64 prefill, a packed prefill of 23 sequences of mixed lengths
 k=4 rows at B=128), and the sigmoid-gated RMSNorm after it (kda_gated_rmsnorm)
 on the output of the T=8192 prefill and of a decode step.  The decode step,
 decode_k and the front end are also timed in their BF16 forms (the front end
-writing BF16 q | k | v packed per token, the core reading them).
+writing BF16 q | k | v packed per token, the core reading them).  The
+prefill's front end (kda_prefill_front_end) is timed at the T=8192 H=32
+prefill's shape.
 
 Inputs are seeded synthetic tensors (kda_inputs) resident in HBM before the
 timed region.  Decode states are rotated over buffers totalling >= 1 GiB so
@@ -208,6 +210,33 @@ def bench_front_end(torch, kda, ki, name, steps, warmup, timer, bf16=False):
         else:
             kda.kda_decode_front_end(qkv, w, st, H, ki.L2_EPS, q=q, k=k, v=v, conv_snapshots=snaps,
                                      n_snapshots=n_snap, stream=stream)
+
+    r = timer.run(step, steps, warmup)
+    return r, per_set, n_set, B * T
+
+
+def prefill_front_end_bytes(B: int, T: int, H: int, K: int) -> int:
+    """Algorithmic bytes of one prefill front-end call: BF16 qkv read, FP32 q, k, v rows < T written, the
+    FP32 conv state read and written, BF16 conv weights read once."""
+    C = 3 * H * D
+    return B * T * C * (2 + 4) + 2 * B * C * K * 4 + C * K * 2
+
+
+def bench_prefill_front_end(torch, kda, ki, name, steps, warmup, timer):
+    B, T, H, K, chunk, seed = ki.PREFILL_FRONT_END_WORKLOADS[name]
+    x = ki.front_end_inputs(seed, B, T, H, K)
+    bits = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).cuda()
+    qkv0, w, st0 = bits(x["qkv"]), bits(x["conv_w"]), torch.from_numpy(x["conv_state"]).cuda()
+    t_pad = -(-T // chunk) * chunk
+    per_set = prefill_front_end_bytes(B, T, H, K)
+    n_set = max(2, -(-(1 << 30) // per_set))
+    sets = [(qkv0.clone(), st0.clone(), *(torch.empty((B, t_pad, H, D), device="cuda") for _ in range(3)))
+            for _ in range(n_set)]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        qkv, st, q, k, v = sets[i % n_set]
+        kda.kda_prefill_front_end(qkv, w, st, H, chunk, ki.L2_EPS, q=q, k=k, v=v, stream=stream)
 
     r = timer.run(step, steps, warmup)
     return r, per_set, n_set, B * T
@@ -512,6 +541,15 @@ def main():
             workloads[name] = {"tokens_per_s": tokens / r["s_per_step"], "us_per_call": r["s_per_step"] * 1e6,
                                "kernel_us": r["launch_avg_s"] * 1e6, "GB_per_s": gbs,
                                "hbm_frac": gbs / HBM_PEAK_GBS, "buffer_sets_rotated": n_set}
+    for name in ki.PREFILL_FRONT_END_WORKLOADS:
+        if not want(name):
+            continue
+        log(name)
+        r, nbytes, n_set, tokens = bench_prefill_front_end(torch, kda, ki, name, args.reps or 50, args.warmup, timer)
+        gbs = nbytes / r["launch_avg_s"] / 1e9
+        workloads[name] = {"tokens_per_s": tokens / r["s_per_step"], "us_per_call": r["s_per_step"] * 1e6,
+                           "kernel_us": r["launch_avg_s"] * 1e6, "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                           "buffer_sets_rotated": n_set}
     for name in ki.NORM_WORKLOADS:
         if not want(name):
             continue

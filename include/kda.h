@@ -301,6 +301,35 @@ int kda_decode_front_end_bf16(const uint16_t* qkv, const uint16_t* conv_w, float
                               float* conv_snapshots, int n_snapshots, int batch, int heads, int T, int conv_kernel,
                               float l2_eps, void* stream);
 
+/*
+ * The step before the core on the prefill path: the same conv1d update, SiLU
+ * and L2 on q and k as kda_decode_front_end, over the T tokens of a prefill,
+ * written into the chunk-padded FP32 inputs kda_chunk_prefill reads
+ * (workspace page, q_f32 / k_f32 / v_f32: [T_pad, qkv] FP32, post-L2 q,
+ * post-L2 k, raw v, prefill only; module page, pipeline line).  The pages
+ * round the conv output to BF16 (conv_out) before the L2; here conv, SiLU
+ * and L2 are one pass and the values stay FP32 throughout.
+ *
+ *   qkv        : [batch][T][conv_dim] BF16, q | k | v per token (qkv_proj)
+ *   conv_w     : [conv_dim][conv_kernel] BF16
+ *   conv_state : [batch][conv_dim][conv_kernel] FP32, read, then advanced in
+ *                place by the T inputs (afterwards it holds the inputs of the
+ *                last conv_kernel tokens, older slots first, as T single
+ *                decode front-end rows would leave it)
+ *   q, k, v    : [batch][T_pad][heads][128] FP32, T_pad = ceil(T / chunk) *
+ *                chunk: the q, k, v of kda_chunk_prefill for the same T and
+ *                chunk.  Rows >= T are not written.
+ *   chunk      : 16, 32 or 64 (KDA_ERR_UNSUPPORTED otherwise)
+ *
+ * Every row equals, bit for bit, the row kda_decode_front_end computes when
+ * it walks the same T tokens from the same conv state.  All other arguments,
+ * conventions and refusals are those of kda_decode_front_end (no snapshots).
+ * The work is two launches on the stream (the outputs, then the conv state).
+ */
+int kda_prefill_front_end(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q, float* k,
+                          float* v, int batch, int heads, int T, int chunk, int conv_kernel, float l2_eps,
+                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,7 @@ KDA_ERR_HIP = -4
 EXPORTED = ("kda_status_string", "kda_chunk_prefill_workspace_bytes", "kda_chunk_prefill", "kda_recurrent_step",
             "kda_recurrent_k", "kda_gated_rmsnorm", "kda_decode_front_end",
             "kda_chunk_prefill_varlen_workspace_bytes", "kda_chunk_prefill_varlen", "kda_recurrent_k_bf16",
-            "kda_recurrent_step_bf16", "kda_decode_front_end_bf16")
+            "kda_recurrent_step_bf16", "kda_decode_front_end_bf16", "kda_prefill_front_end")
 GATED_RMSNORM_MIN_EPS = 1e-30
 
 _lib = None
@@ -80,6 +80,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_recurrent_step_bf16.restype = i
     lib.kda_decode_front_end_bf16.argtypes = [p] * 5 + [i] * 5 + [ctypes.c_float, p]
     lib.kda_decode_front_end_bf16.restype = i
+    lib.kda_prefill_front_end.argtypes = [p] * 6 + [i] * 5 + [ctypes.c_float, p]
+    lib.kda_prefill_front_end.restype = i
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -337,6 +339,37 @@ def kda_decode_front_end_bf16(qkv, conv_w, conv_state, heads: int, l2_eps: float
     if rc != KDA_OK:
         raise KdaError("kda_decode_front_end_bf16", rc)
     return conv_out
+
+
+def kda_prefill_front_end(qkv, conv_w, conv_state, heads: int, chunk: int, l2_eps: float, q=None, k=None, v=None,
+                          stream=None):
+    """Conv1d + SiLU + L2(q, k) over the T tokens of a prefill.  Returns (q, k, v).
+
+    qkv: bfloat16 [B][T][3 H 128]; conv_w: bfloat16 [3 H 128][K]; conv_state: float32 [B][3 H 128][K]
+    (advanced in place); q, k, v: float32 [B][T_pad][H][128], T_pad = ceil(T / chunk) * chunk (rows >= T
+    are not written), ready for kda_chunk_prefill(..., T, chunk).
+    """
+    if not isinstance(qkv, torch.Tensor) or qkv.dim() != 3:
+        raise ValueError("qkv must be [batch][T][3 * heads * 128]")
+    B, T, C = qkv.shape
+    if C != 3 * heads * HEAD_DIM:
+        raise ValueError(f"qkv has {C} channels, expected 3 * {heads} * {HEAD_DIM}")
+    if chunk not in (16, 32, 64):
+        raise KdaError("kda_prefill_front_end", KDA_ERR_UNSUPPORTED)
+    if conv_w.dim() != 2:
+        raise ValueError("conv_w must be [conv_dim][conv_kernel]")
+    K = conv_w.shape[1]
+    t_pad = -(-int(T) // chunk) * chunk
+    vs = (B, t_pad, heads, HEAD_DIM)
+    q = torch.empty(vs, dtype=torch.float32, device=qkv.device) if q is None else q
+    k = torch.empty(vs, dtype=torch.float32, device=qkv.device) if k is None else k
+    v = torch.empty(vs, dtype=torch.float32, device=qkv.device) if v is None else v
+    args = [_check("qkv", qkv, (B, T, C), torch.bfloat16), _check("conv_w", conv_w, (C, K), torch.bfloat16),
+            _check("conv_state", conv_state, (B, C, K)), _check("q", q, vs), _check("k", k, vs), _check("v", v, vs)]
+    rc = load_library().kda_prefill_front_end(*args, B, heads, T, chunk, K, float(l2_eps), _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_prefill_front_end", rc)
+    return q, k, v
 
 
 def kda_chunk_prefill_varlen_workspace_bytes(n_seqs: int, heads: int, total_tokens: int, chunk: int) -> int:

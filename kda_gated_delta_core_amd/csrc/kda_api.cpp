@@ -296,3 +296,30 @@ KDA_API int kda_decode_front_end_bf16(const uint16_t* qkv, const uint16_t* conv_
     return front_end_checked(qkv, conv_w, conv_state, nullptr, nullptr, nullptr, conv_out, conv_snapshots,
                              n_snapshots, batch, heads, T, conv_kernel, l2_eps, stream);
 }
+
+KDA_API int kda_prefill_front_end(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q, float* k,
+                                  float* v, int batch, int heads, int T, int chunk, int conv_kernel, float l2_eps,
+                                  void* stream)
+{
+    if (!qkv || !conv_w || !conv_state || !q || !k || !v) return KDA_ERR_INVALID_ARG;
+    if (!aligned({qkv, conv_w, conv_state, q, k, v})) return KDA_ERR_INVALID_ARG;
+    if (batch < 1 || heads < 1 || T < 1 || heads > KDA_PREFILL_MAX_HEADS) return KDA_ERR_INVALID_ARG;
+    if (conv_kernel < 1) return KDA_ERR_INVALID_ARG;
+    if (!(isfinite(l2_eps) && l2_eps >= KDA_GATED_RMSNORM_MIN_EPS)) return KDA_ERR_INVALID_ARG;
+    if (!chunk_ok(chunk) || conv_kernel > KDA_FRONT_END_MAX_CONV_KERNEL) return KDA_ERR_UNSUPPORTED;
+    const int64_t t_pad = ((int64_t)T + chunk - 1) / chunk * chunk;
+    const int64_t C = 3 * (int64_t)heads * KDA_HEAD_DIM;
+    const int64_t x = mul({batch, T, C});
+    const int64_t w = mul({C, conv_kernel});
+    const int64_t st = mul({batch, C, conv_kernel});
+    const int64_t vec = mul({batch, t_pad, heads, KDA_HEAD_DIM});
+    if (x < 0 || w < 0 || st < 0 || vec < 0 || t_pad > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
+    // one wave per (sequence, 32-token strip, part, head) vector; one thread per (sequence, channel)
+    if (mul({batch, (T + 31) / 32, 3, heads}) > 0x7fffffffLL || mul({batch, C}) > 0x7fffffffLL)
+        return KDA_ERR_INVALID_ARG;
+    const Range r[] = {{q, vec * 4}, {k, vec * 4}, {v, vec * 4}, {conv_state, st * 4}, {qkv, x * 2}, {conv_w, w * 2}};
+    if (any_overlap(r, 6, 4)) return KDA_ERR_INVALID_ARG;
+    const int rc = kda::launch_prefill_front_end(qkv, conv_w, conv_state, q, k, v, batch, heads, T, (int)t_pad,
+                                                 conv_kernel, l2_eps, static_cast<hipStream_t>(stream));
+    return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}

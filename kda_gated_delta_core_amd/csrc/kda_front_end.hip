@@ -28,9 +28,9 @@
 // channels per lane, which leave every other 16 bytes of a range to a second
 // instruction, were 13% slower on the 4-row walk with snapshots.  The next
 // row's inputs are loaded while the current row is computed.  A q or k wave
-// reduces sum y^2 in FP64 with shuffles alone (no barrier), which makes the
-// scale exact for any finite input.  The arithmetic does not depend on T, so
-// T rows in one call equal T one-row calls bit for bit.
+// reduces sum y^2 in FP64 with DPP lane moves alone (no barrier), so the sum
+// neither overflows nor flushes for any finite input.  The arithmetic does not
+// depend on T, so T rows in one call equal T one-row calls bit for bit.
 #include "kda_front_end.h"
 #include "kda_internal.h"
 
@@ -103,7 +103,124 @@ void launch_fe(dim3 grid, const unsigned short* x, const unsigned short* w, floa
                            nullptr, snaps, n_snap, batch, heads, T, eps);
 }
 
+// Prefill form: the same computation over a whole prefill, parallel over
+// tokens.  One wave per (sequence, strip of kFeStrip tokens, part, head)
+// vector: its K slots start as the inputs of the K times before the strip (the
+// conv state's slot K + time for times before the call), then it walks the
+// strip's rows with the decode form's per-row body, so every row gets the bits
+// the decode form walking all T rows gives it.  Outputs go to the chunk-padded
+// [B][t_pad][H][128] rows of kda_chunk_prefill; rows >= T are not written.  The
+// conv state is left alone here (earlier strips read it) and advanced by
+// prefill_conv_state_kernel afterwards.
+constexpr int kFeStrip = 32;
+
+template <int K>
+__global__ __launch_bounds__(kFeThreads) void prefill_front_end_kernel(const unsigned short* __restrict__ qkv,
+                                                                       const unsigned short* __restrict__ conv_w,
+                                                                       const float* __restrict__ conv_state,
+                                                                       float* __restrict__ q_out,
+                                                                       float* __restrict__ k_out,
+                                                                       float* __restrict__ v_out, int batch,
+                                                                       int heads, int T, int t_pad, int n_strips,
+                                                                       double eps)
+{
+    const int lane = threadIdx.x % 64;
+    const long long gv = (long long)blockIdx.x * kFeVecs + threadIdx.x / 64;
+    const int n_part = 3 * heads;
+    if (gv >= (long long)batch * n_strips * n_part) return;  // whole waves leave; no workgroup barrier below
+    const int vec = (int)(gv % n_part);
+    const long long bs = gv / n_part;
+    const int strip = (int)(bs % n_strips), b = (int)(bs / n_strips);
+    const int part = vec / heads, h = vec % heads;
+    const int C = 3 * heads * kD;
+    const size_t cv = (size_t)vec * kD;  // first channel of the vector
+    const int t0 = strip * kFeStrip, t1 = min(T, t0 + kFeStrip);
+
+    FeLane<K> f;
+    const unsigned short* const xp = qkv + (size_t)b * T * C + cv + lane;  // row 0, channel l
+    const float* const st = conv_state + ((size_t)b * C + cv) * K;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+            f.w[m][i] = bf16_to_f32(conv_w[(cv + lane + 64 * m) * K + i]);
+            const int tau = t0 - K + i;  // the time slot i holds before row t0
+            f.s[m][i] = tau >= 0 ? bf16_to_f32(xp[(size_t)tau * C + 64 * m]) : st[(size_t)(lane + 64 * m) * K + K + tau];
+        }
+    }
+    float* const out = part == 0 ? q_out : (part == 1 ? k_out : v_out);
+    unsigned short xn0 = xp[(size_t)t0 * C], xn1 = xp[(size_t)t0 * C + 64];
+    for (int t = t0; t < t1; ++t) {
+        const unsigned short x0 = xn0, x1 = xn1;
+        if (t + 1 < t1) {
+            xn0 = xp[(size_t)(t + 1) * C];
+            xn1 = xp[(size_t)(t + 1) * C + 64];
+        }
+        float y[2];
+        fe_row(f, x0, x1, part < 2, eps, y);
+        float* const o = out + (((size_t)b * t_pad + t) * heads + h) * kD + lane;
+        o[0] = y[0];
+        o[64] = y[1];
+    }
+}
+
+// After the prefill: the conv state of every (sequence, channel) becomes the
+// inputs of the last K times (from the old state for times before the call).
+// One thread per (sequence, channel); it reads its old slots before writing.
+template <int K>
+__global__ __launch_bounds__(256) void prefill_conv_state_kernel(const unsigned short* __restrict__ qkv,
+                                                                 float* __restrict__ conv_state, int batch, int C,
+                                                                 int T)
+{
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;  // b * C + channel
+    if (i >= (long long)batch * C) return;
+    const long long b = i / C, c = i % C;
+    float* const st = conv_state + (size_t)i * K;
+    float old[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) old[j] = st[j];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const int tau = T - K + j;  // before the call when < 0: old slot K + tau
+        float keep = old[0];
+#pragma unroll
+        for (int u = 1; u < K; ++u) keep = (u == K + tau) ? old[u] : keep;
+        st[j] = tau >= 0 ? bf16_to_f32(qkv[((size_t)b * T + tau) * C + c]) : keep;
+    }
+}
+
+template <int K>
+void launch_prefill_fe(const unsigned short* x, const unsigned short* w, float* conv_state, float* q, float* k,
+                       float* v, int batch, int heads, int T, int t_pad, double eps, hipStream_t stream)
+{
+    const int n_strips = (T + kFeStrip - 1) / kFeStrip;
+    const long long n_vec = (long long)batch * n_strips * 3 * heads;
+    hipLaunchKernelGGL(prefill_front_end_kernel<K>, dim3((unsigned)((n_vec + kFeVecs - 1) / kFeVecs)),
+                       dim3(kFeThreads), 0, stream, x, w, conv_state, q, k, v, batch, heads, T, t_pad, n_strips, eps);
+    const int C = 3 * heads * kD;
+    const long long n_ch = (long long)batch * C;
+    hipLaunchKernelGGL(prefill_conv_state_kernel<K>, dim3((unsigned)((n_ch + 255) / 256)), dim3(256), 0, stream, x,
+                       conv_state, batch, C, T);
+}
+
 }  // namespace
+
+int launch_prefill_front_end(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q, float* k,
+                             float* v, int batch, int heads, int T, int t_pad, int conv_kernel, float l2_eps,
+                             hipStream_t stream)
+{
+    const auto* x = reinterpret_cast<const unsigned short*>(qkv);
+    const auto* w = reinterpret_cast<const unsigned short*>(conv_w);
+    const double eps = l2_eps;
+    switch (conv_kernel) {
+    case 1: launch_prefill_fe<1>(x, w, conv_state, q, k, v, batch, heads, T, t_pad, eps, stream); break;
+    case 2: launch_prefill_fe<2>(x, w, conv_state, q, k, v, batch, heads, T, t_pad, eps, stream); break;
+    case 3: launch_prefill_fe<3>(x, w, conv_state, q, k, v, batch, heads, T, t_pad, eps, stream); break;
+    case 4: launch_prefill_fe<4>(x, w, conv_state, q, k, v, batch, heads, T, t_pad, eps, stream); break;
+    default: return -1;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
 
 int launch_front_end(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q, float* k, float* v,
                      uint16_t* conv_out, float* snaps, int n_snap, int batch, int heads, int T, int conv_kernel,

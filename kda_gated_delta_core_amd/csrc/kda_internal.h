@@ -43,6 +43,11 @@ int launch_front_end(const uint16_t* qkv, const uint16_t* conv_w, float* conv_st
                      uint16_t* conv_out, float* snaps, int n_snap, int batch, int heads, int T, int conv_kernel,
                      float l2_eps, hipStream_t stream);
 
+// prefill front end: q, k, v FP32 [B][t_pad][H][128], rows < T written; conv state advanced by T inputs
+int launch_prefill_front_end(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q, float* k,
+                             float* v, int batch, int heads, int T, int t_pad, int conv_kernel, float l2_eps,
+                             hipStream_t stream);
+
 int launch_gated_rmsnorm(const float* core, const uint16_t* gate, const uint16_t* weight, uint16_t* out,
                          long long n_vec, float eps, hipStream_t stream);
 

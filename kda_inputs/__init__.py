@@ -68,6 +68,11 @@ FRONT_END_WORKLOADS = {
     "front_end_b64_h32_k4": (64, 1, 32, 4, 1008),
     "front_end_b128_h32_k4_rows4": (128, 4, 32, 4, 1009),
 }
+# (batch, tokens, heads, conv_kernel, chunk, seed) of the prefill front-end workloads: the front end of
+# the T=8192 H=32 C=64 prefill
+PREFILL_FRONT_END_WORKLOADS = {
+    "prefill_front_end_t8192_h32_k4": (1, 8192, 32, 4, 64, 1011),
+}
 # varlen prefill workloads: (total tokens, heads, chunk, mean sequence length, seed)
 VARLEN_WORKLOADS = {
     "prefill_varlen_h32_t32768_c64": (32768, 32, 64, 2048, 1010),

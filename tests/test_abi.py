@@ -262,6 +262,34 @@ def test_bf16_decode_refusals(lib):
 
 
 @no_gpu
+def test_prefill_front_end_refusals(lib):
+    f = lib.kda_prefill_front_end
+    bad = kda.KDA_ERR_INVALID_ARG
+    ok_args = (4, 2, 37, 64, 4, 1e-6)  # batch, heads, T, chunk, conv_kernel, eps
+    for i in range(6):
+        p = list(P[:6])
+        p[i] = None
+        assert f(*p, *ok_args, None) == bad, i
+        p = list(P[:6])
+        p[i] += 8
+        assert f(*p, *ok_args, None) == bad, i
+    assert f(*P[:6], 0, 2, 37, 64, 4, 1e-6, None) == bad
+    assert f(*P[:6], 4, 0, 37, 64, 4, 1e-6, None) == bad
+    assert f(*P[:6], 4, 2, 0, 64, 4, 1e-6, None) == bad
+    assert f(*P[:6], 4, 16385, 37, 64, 4, 1e-6, None) == bad
+    assert f(*P[:6], 4, 2, 37, 64, 0, 1e-6, None) == bad
+    assert f(*P[:6], 4, 2, 37, 48, 4, 1e-6, None) == kda.KDA_ERR_UNSUPPORTED
+    assert f(*P[:6], 4, 2, 37, 64, 5, 1e-6, None) == kda.KDA_ERR_UNSUPPORTED
+    for eps in (0.0, -1.0, float("nan"), float("inf")):
+        assert f(*P[:6], 4, 2, 37, 64, 4, eps, None) == bad
+    # q over the qkv rows, the conv state over v, k over q
+    for i, j in ((3, 0), (2, 5), (4, 3)):
+        p = list(P[:6])
+        p[i] = p[j] + 16
+        assert f(*p, *ok_args, None) == bad, (i, j)
+
+
+@no_gpu
 def test_varlen_refusals(lib):
     f = lib.kda_chunk_prefill_varlen
     bad = kda.KDA_ERR_INVALID_ARG
