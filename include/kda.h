@@ -273,8 +273,10 @@ int kda_gated_rmsnorm(const float* core, const uint16_t* out_gate, const uint16_
  *   l2_eps         : finite, >= KDA_GATED_RMSNORM_MIN_EPS, added inside the
  *                    square root (config page, l2_eps)
  *
- * The conv state only ever holds inputs, so it is exact; q, k, v carry FP32
- * rounding of the conv sum and the SiLU (the L2 scale is formed in FP64).
+ * The conv state only ever holds inputs, so it is exact; q, k, v carry the
+ * FP32 rounding of the conv sum and a few units of 2^-24 from the SiLU (the
+ * hardware exp2 and reciprocal); the L2 sum of squares and scale are formed
+ * in FP64, so no finite input overflows or flushes them.
  * Outputs, conv_state and conv_snapshots must not overlap each other or an
  * input.  Refusals (KDA_ERR_INVALID_ARG): a null pointer, batch, heads or T
  * < 1, heads > KDA_PREFILL_MAX_HEADS, n_snapshots outside [0, T], conv_kernel
