@@ -35,8 +35,9 @@
  *    rows = T_pad = ceil(T / chunk) * chunk for kda_chunk_prefill (the
  *    workspace page pads prefill buffers to whole chunks), rows = T for
  *    kda_recurrent_k and rows = 1 for kda_recurrent_step.  The packed
- *    (varlen) prefill, the decode front end, the BF16 decode forms and the
- *    gated RMSNorm state their own layouts at their declarations.
+ *    (varlen) prefill, the decode and prefill front ends, the BF16 decode
+ *    forms and the gated RMSNorm state their own layouts at their
+ *    declarations.
  *  * Inputs are read-only.  state is read and updated in place (layer page:
  *    decode updates the state in place).  out rows >= T are never written.
  *  * out, state, snapshots and workspace must not overlap each other or any
@@ -67,9 +68,9 @@ extern "C" {
 #define KDA_PREFILL_MAX_HEADS 16384
 /* Most sequences one kda_chunk_prefill_varlen call takes. */
 #define KDA_VARLEN_MAX_SEQS (1 << 20)
-/* Smallest eps kda_gated_rmsnorm and kda_decode_front_end accept. */
+/* Smallest eps kda_gated_rmsnorm and the front ends accept. */
 #define KDA_GATED_RMSNORM_MIN_EPS 1e-30f
-/* Largest conv_kernel kda_decode_front_end accepts (config page, validate:
+/* Largest conv_kernel the front ends accept (config page, validate:
  * the conv kernels keep the sliding window in 4 registers). */
 #define KDA_FRONT_END_MAX_CONV_KERNEL 4
 
