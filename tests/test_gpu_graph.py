@@ -74,3 +74,107 @@ def test_graph_replays_of_decode_steps_and_prefill(device):
             if i == len(got) - 2:  # prefill output: rows < T only (rows >= T are not written)
                 a, b = a[:, :T], b[:, :T]
             assert torch.equal(a, b), f"replay {rep}, tensor {i}"
+
+
+def _capture_and_replay(kda, name, work, reset, results, reps=3):
+    """Eager reference, capture `work` on a side stream, then replays with eager work, resets and
+    synchronisations between them; every replay must equal the eager run bit for bit."""
+    reset()
+    work(None)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in results()]
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        reset()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, pool=torch.cuda.graph_pool_handle(), stream=s):
+            work(s)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(reps):
+        for t in results():  # outputs poisoned first, then the carried states (also results) restored
+            if t.is_floating_point():
+                t.fill_(float("nan"))
+        reset()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(results(), ref)):
+            assert torch.equal(a, b), f"{name}: replay {rep}, tensor {i}"
+
+
+def _bits(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def test_graph_replays_of_the_bf16_decode_chain(device):
+    """BF16 front end -> kda_recurrent_k_bf16 (snapshots) -> gated RMSNorm, captured as one graph."""
+    import kda_gated_delta_core_amd as kda
+    B, T, H, K = 8, 4, 4, 4
+    announce(f"graph capture: BF16 decode chain B={B} k={T} H={H}")
+    fx = ki.front_end_inputs(1510, B, T, H, K)
+    core = ki.make_batch(1511, B, H, T, -5.0, 0.02)
+    nx = ki.norm_inputs(1512, B * T, H)
+    qkv, w, og, on = _bits(fx["qkv"]), _bits(fx["conv_w"]), _bits(nx["out_gate"]), _bits(nx["o_norm"])
+    g, b = torch.from_numpy(core["gate"]).cuda(), torch.from_numpy(core["beta"]).cuda()
+    cst0, st0 = torch.from_numpy(fx["conv_state"]).cuda(), torch.from_numpy(core["state"]).cuda()
+    cst, st = torch.empty_like(cst0), torch.empty_like(st0)
+    conv_out = torch.empty((B, T, 3 * H * 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((B, T, H, 128), device="cuda")
+    snaps = torch.empty((T, B, H, 128, 128), device="cuda")
+    y = torch.empty((B * T, H, 128), dtype=torch.bfloat16, device="cuda")
+
+    def work(s):
+        kda.kda_decode_front_end_bf16(qkv, w, cst, H, ki.L2_EPS, conv_out=conv_out, stream=s)
+        kda.kda_recurrent_k_bf16(conv_out, g, b, st, out=out, snapshots=snaps, n_snapshots=T, stream=s)
+        kda.kda_gated_rmsnorm(out.view(B * T, H, 128), og, on, ki.NORM_EPS, out=y, stream=s)
+
+    def reset():
+        cst.copy_(cst0)
+        st.copy_(st0)
+
+    _capture_and_replay(kda, "BF16 decode chain", work, reset, lambda: (conv_out, cst, out, st, snaps, y))
+
+
+def test_graph_replays_of_the_prefill_chain(device):
+    """Prefill front end -> chunked prefill -> gated RMSNorm, and a varlen prefill, captured as one graph."""
+    import kda_gated_delta_core_amd as kda
+    B, T, H, K, C = 2, 300, 4, 4, 64
+    announce(f"graph capture: prefill chain B={B} T={T} H={H}, varlen prefill")
+    t_pad = -(-T // C) * C
+    fx = ki.front_end_inputs(1520, B, T, H, K)
+    core = ki.make_batch(1521, B, H, T, -5.0, 0.02, alloc_rows=t_pad)
+    nx = ki.norm_inputs(1522, B * t_pad, H)
+    qkv, w, og, on = _bits(fx["qkv"]), _bits(fx["conv_w"]), _bits(nx["out_gate"]), _bits(nx["o_norm"])
+    g, b = torch.from_numpy(core["gate"]).cuda(), torch.from_numpy(core["beta"]).cuda()
+    cst0, st0 = torch.from_numpy(fx["conv_state"]).cuda(), torch.from_numpy(core["state"]).cuda()
+    cst, st = torch.empty_like(cst0), torch.empty_like(st0)
+    q, k, v = (torch.zeros((B, t_pad, H, 128), device="cuda") for _ in range(3))
+    out = torch.zeros((B, t_pad, H, 128), device="cuda")
+    ws = torch.empty(kda.kda_chunk_prefill_workspace_bytes(B, H, T, C), dtype=torch.uint8, device="cuda")
+    y = torch.empty((B * t_pad, H, 128), dtype=torch.bfloat16, device="cuda")
+    lens = [100, 1, 257]
+    vx = ki.varlen_inputs(1523, lens, H, -5.0, 0.02)
+    vd = {n: torch.from_numpy(vx[n]).cuda() for n in ("q", "k", "v", "gate", "beta", "cu_seqlens")}
+    vst0 = torch.from_numpy(vx["state"]).cuda()
+    vst, vout = torch.empty_like(vst0), torch.zeros_like(vd["q"])
+    vws = torch.empty(kda.kda_chunk_prefill_varlen_workspace_bytes(len(lens), H, sum(lens), C), dtype=torch.uint8,
+                      device="cuda")
+
+    def work(s):
+        kda.kda_prefill_front_end(qkv, w, cst, H, C, ki.L2_EPS, q=q, k=k, v=v, stream=s)
+        kda.kda_chunk_prefill(q, k, v, g, b, st, T, C, out=out, workspace=ws, stream=s)
+        kda.kda_gated_rmsnorm(out.view(B * t_pad, H, 128), og, on, ki.NORM_EPS, out=y, stream=s)
+        kda.kda_chunk_prefill_varlen(vd["q"], vd["k"], vd["v"], vd["gate"], vd["beta"], vst, vd["cu_seqlens"], C,
+                                     out=vout, workspace=vws, stream=s)
+
+    def reset():
+        cst.copy_(cst0)
+        st.copy_(st0)
+        vst.copy_(vst0)
+
+    # rows >= T of q, k, v and out are never written: compare rows < T; those rows stay zero, so the
+    # norm's rows for them are zero too and the whole norm output is compared
+    _capture_and_replay(kda, "prefill chain", work, reset,
+                        lambda: (q[:, :T], k[:, :T], v[:, :T], cst, out[:, :T], st, y, vout, vst))
