@@ -15,7 +15,10 @@ on the output of the T=8192 prefill and of a decode step.  The decode step,
 decode_k and the front end are also timed in their BF16 forms (the front end
 writing BF16 q | k | v packed per token, the core reading them).  The
 prefill's front end (kda_prefill_front_end) is timed at the T=8192 H=32
-prefill's shape.
+prefill's shape.  Two chain lines time the block's steps together: the
+decode step on BF16 q | k | v (front end, core, gated RMSNorm) replayed from
+one HIP graph over 8 state sets, and the T=8192 prefill (front end, chunked
+prefill, gated RMSNorm).
 
 Inputs are seeded synthetic tensors (kda_inputs) resident in HBM before the
 timed region.  Decode states are rotated over buffers totalling >= 1 GiB so
@@ -240,6 +243,83 @@ def bench_prefill_front_end(torch, kda, ki, name, steps, warmup, timer):
 
     r = timer.run(step, steps, warmup)
     return r, per_set, n_set, B * T
+
+
+def bench_decode_chain(torch, kda, ki, reps):
+    """The decode step of the block on BF16 q | k | v: front end -> kda_recurrent_step_bf16 -> gated RMSNorm
+    at B=64 H=32, captured as one HIP graph of 8 steps, each on its own state set (8 x 128 MiB of recurrent
+    state, so replays stream HBM), replayed back to back.  Returns (us per step, bytes per step)."""
+    w = ki.WORKLOADS["decode_b64_h32"]
+    B, H = w.batch, w.heads
+    FB, FT, FH, K, fseed = ki.FRONT_END_WORKLOADS["front_end_b64_h32_k4"]
+    rows, nh, nseed = ki.NORM_WORKLOADS["gated_rmsnorm_b64_h32"]
+    assert (FB, FT, FH) == (B, 1, H) and (rows, nh) == (B, H)
+    x = ki.workload_inputs(w)
+    fx = ki.front_end_inputs(fseed, B, 1, H, K)
+    nx = ki.norm_inputs(nseed, rows, H)
+    bits = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).cuda()
+    qkv, cw, og, on = bits(fx["qkv"]), bits(fx["conv_w"]), bits(nx["out_gate"]), bits(nx["o_norm"])
+    g, b = torch.from_numpy(x["gate"]).cuda(), torch.from_numpy(x["beta"]).cuda()
+    n_set = 8
+    sets = [dict(cst=torch.from_numpy(fx["conv_state"]).cuda(), st=torch.from_numpy(x["state"]).cuda(),
+                 co=torch.empty((B, 1, 3 * H * D), dtype=torch.bfloat16, device="cuda"),
+                 out=torch.empty((B, 1, H, D), device="cuda"),
+                 y=torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")) for _ in range(n_set)]
+
+    def chain(z):
+        kda.kda_decode_front_end_bf16(qkv, cw, z["cst"], H, ki.L2_EPS, conv_out=z["co"])
+        kda.kda_recurrent_step_bf16(z["co"], g, b, z["st"], out=z["out"])
+        kda.kda_gated_rmsnorm(z["out"].view(B, H, D), og, on, ki.NORM_EPS, out=z["y"])
+
+    for z in sets:
+        chain(z)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for z in sets:
+            chain(z)
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * n_set)
+    nbytes = (front_end_bytes(B, 1, H, K, 0, out_bytes=2) + decode_bytes(B, H, qkv_bytes=2) + norm_bytes(B, H))
+    return us, nbytes
+
+
+def bench_prefill_chain(torch, kda, ki, steps, warmup, timer):
+    """The prefill of the block at T=8192 H=32 C=64: prefill front end -> kda_chunk_prefill -> gated RMSNorm
+    of the T rows, timed eagerly as one step."""
+    B, T, H, K, C, fseed = ki.PREFILL_FRONT_END_WORKLOADS["prefill_front_end_t8192_h32_k4"]
+    w = ki.WORKLOADS["prefill_h32_t8192_c64"]
+    rows, nh, nseed = ki.NORM_WORKLOADS["gated_rmsnorm_t8192_h32"]
+    assert (B, T, H, C) == (w.batch, w.T, w.heads, w.chunk) and (rows, nh) == (T, H)
+    t_pad = -(-T // C) * C
+    fx = ki.front_end_inputs(fseed, B, T, H, K)
+    x = ki.workload_inputs(w)
+    nx = ki.norm_inputs(nseed, rows, H)
+    bits = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).cuda()
+    qkv, cw, og, on = bits(fx["qkv"]), bits(fx["conv_w"]), bits(nx["out_gate"]), bits(nx["o_norm"])
+    cst = torch.from_numpy(fx["conv_state"]).cuda()
+    g = torch.from_numpy(x["gate"][:, :t_pad].copy()).cuda()
+    b = torch.from_numpy(x["beta"][:, :t_pad].copy()).cuda()
+    st = torch.from_numpy(x["state"]).cuda()
+    q, k, v, out = (torch.empty((B, t_pad, H, D), device="cuda") for _ in range(4))
+    ws = torch.empty(kda.kda_chunk_prefill_workspace_bytes(B, H, T, C), dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        kda.kda_prefill_front_end(qkv, cw, cst, H, C, ki.L2_EPS, q=q, k=k, v=v, stream=stream)
+        kda.kda_chunk_prefill(q, k, v, g, b, st, T, C, out=out, workspace=ws, stream=stream)
+        kda.kda_gated_rmsnorm(out[0, :T], og, on, ki.NORM_EPS, out=y, stream=stream)
+
+    return timer.run(step, steps, warmup), B * T
 
 
 def bench_varlen(torch, kda, ki, name, steps, warmup, timer):
@@ -550,6 +630,20 @@ def main():
         workloads[name] = {"tokens_per_s": tokens / r["s_per_step"], "us_per_call": r["s_per_step"] * 1e6,
                            "kernel_us": r["launch_avg_s"] * 1e6, "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
                            "buffer_sets_rotated": n_set}
+    if want("decode_chain_bf16_b64_h32"):
+        log("decode_chain_bf16_b64_h32")
+        us, nbytes = bench_decode_chain(torch, kda, ki, args.reps or 50)
+        workloads["decode_chain_bf16_b64_h32"] = {
+            "tokens_per_s": 64 / (us * 1e-6), "us_per_step": us, "GB_per_s": nbytes / (us * 1e-6) / 1e9,
+            "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "steps": "front end (BF16 out) + kda_recurrent_step_bf16 + gated RMSNorm, replayed from one HIP graph"}
+    if want("prefill_chain_t8192_h32"):
+        log("prefill_chain_t8192_h32")
+        r, tokens = bench_prefill_chain(torch, kda, ki, args.reps or 20, 0 if args.reps else 20, timer)
+        workloads["prefill_chain_t8192_h32"] = {
+            "tokens_per_s": tokens / r["s_per_step"], "ms_per_call": r["s_per_step"] * 1e3,
+            "device_ms": r["launch_avg_s"] * 1e3,
+            "steps": "kda_prefill_front_end + kda_chunk_prefill + gated RMSNorm"}
     for name in ki.NORM_WORKLOADS:
         if not want(name):
             continue
