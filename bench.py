@@ -322,6 +322,29 @@ def bench_prefill_chain(torch, kda, ki, steps, warmup, timer):
     return timer.run(step, steps, warmup), B * T
 
 
+def bench_prefill_front_end_varlen(torch, kda, ki, name, steps, warmup, timer, K=4):
+    """kda_prefill_front_end_varlen over the packed sequences of a varlen prefill workload."""
+    import numpy as np
+    total, H, C, mean_len, seed = ki.VARLEN_WORKLOADS[name]
+    lens = ki.varlen_lengths(seed, total, mean_len)
+    fx = ki.front_end_inputs(seed, 1, total, H, K)
+    st0 = ki.front_end_inputs(seed + 1, len(lens), 1, H, K)["conv_state"]
+    bits = lambda a: torch.from_numpy(np.ascontiguousarray(a).view("int16")).view(torch.bfloat16).cuda()
+    qkv, w = bits(fx["qkv"][0]), bits(fx["conv_w"])
+    st = torch.from_numpy(st0).cuda()
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
+    q, k, v = (torch.empty((total, H, D), device="cuda") for _ in range(3))
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        kda.kda_prefill_front_end_varlen(qkv, w, st, cu, H, ki.L2_EPS, q=q, k=k, v=v, stream=stream)
+
+    r = timer.run(step, steps, warmup)
+    Cd = 3 * H * D
+    nbytes = total * Cd * 6 + 2 * len(lens) * Cd * K * 4 + Cd * K * 2
+    return r, nbytes, total
+
+
 def bench_varlen(torch, kda, ki, name, steps, warmup, timer):
     total, H, C, mean_len, seed = ki.VARLEN_WORKLOADS[name]
     lens = ki.varlen_lengths(seed, total, mean_len)
@@ -621,6 +644,15 @@ def main():
             workloads[name] = {"tokens_per_s": tokens / r["s_per_step"], "us_per_call": r["s_per_step"] * 1e6,
                                "kernel_us": r["launch_avg_s"] * 1e6, "GB_per_s": gbs,
                                "hbm_frac": gbs / HBM_PEAK_GBS, "buffer_sets_rotated": n_set}
+    for name in ki.VARLEN_WORKLOADS:
+        fe_name = name.replace("prefill_varlen_", "prefill_front_end_varlen_").replace("_c64", "_k4")
+        if not want(fe_name):
+            continue
+        log(fe_name)
+        r, nbytes, tokens = bench_prefill_front_end_varlen(torch, kda, ki, name, args.reps or 50, args.warmup, timer)
+        gbs = nbytes / r["launch_avg_s"] / 1e9
+        workloads[fe_name] = {"tokens_per_s": tokens / r["s_per_step"], "us_per_call": r["s_per_step"] * 1e6,
+                              "kernel_us": r["launch_avg_s"] * 1e6, "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
     for name in ki.PREFILL_FRONT_END_WORKLOADS:
         if not want(name):
             continue

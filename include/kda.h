@@ -333,6 +333,34 @@ int kda_prefill_front_end(const uint16_t* qkv, const uint16_t* conv_w, float* co
                           float* v, int batch, int heads, int T, int chunk, int conv_kernel, float l2_eps,
                           void* stream);
 
+/*
+ * kda_prefill_front_end for sequences of their own lengths packed back to
+ * back, producing the inputs of kda_chunk_prefill_varlen.
+ *
+ *   qkv        : [total_tokens][conv_dim] BF16
+ *   conv_state : [n_seqs][conv_dim][conv_kernel] FP32, one per sequence, each
+ *                advanced in place by its own tokens (an empty sequence keeps
+ *                its state)
+ *   q, k, v    : [total_tokens][heads][128] FP32; rows of sequence s are
+ *                cu_seqlens[s] .. cu_seqlens[s + 1] - 1; rows from
+ *                cu_seqlens[n_seqs] on belong to no sequence and are not
+ *                written
+ *   cu_seqlens : DEVICE int32 [n_seqs + 1], expected 0 = cu_seqlens[0] <= ...
+ *                <= cu_seqlens[n_seqs] <= total_tokens (as for
+ *                kda_chunk_prefill_varlen)
+ *
+ * No conv window reaches across a sequence boundary: the first row of each
+ * sequence starts from that sequence's conv state.  Every row equals, bit
+ * for bit, what kda_decode_front_end computes walking its sequence alone.
+ * The offsets are read clamped to [0, total_tokens], so no content moves an
+ * access outside the buffers; offsets that break the expected order give
+ * unspecified values.  n_seqs at most KDA_VARLEN_MAX_SEQS; other arguments
+ * and refusals as for kda_prefill_front_end (no chunk).
+ */
+int kda_prefill_front_end_varlen(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q, float* k,
+                                 float* v, const int* cu_seqlens, int n_seqs, int heads, int total_tokens,
+                                 int conv_kernel, float l2_eps, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

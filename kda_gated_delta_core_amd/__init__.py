@@ -33,7 +33,8 @@ KDA_ERR_HIP = -4
 EXPORTED = ("kda_status_string", "kda_chunk_prefill_workspace_bytes", "kda_chunk_prefill", "kda_recurrent_step",
             "kda_recurrent_k", "kda_gated_rmsnorm", "kda_decode_front_end",
             "kda_chunk_prefill_varlen_workspace_bytes", "kda_chunk_prefill_varlen", "kda_recurrent_k_bf16",
-            "kda_recurrent_step_bf16", "kda_decode_front_end_bf16", "kda_prefill_front_end")
+            "kda_recurrent_step_bf16", "kda_decode_front_end_bf16", "kda_prefill_front_end",
+            "kda_prefill_front_end_varlen")
 GATED_RMSNORM_MIN_EPS = 1e-30
 
 _lib = None
@@ -82,6 +83,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_decode_front_end_bf16.restype = i
     lib.kda_prefill_front_end.argtypes = [p] * 6 + [i] * 5 + [ctypes.c_float, p]
     lib.kda_prefill_front_end.restype = i
+    lib.kda_prefill_front_end_varlen.argtypes = [p] * 7 + [i] * 4 + [ctypes.c_float, p]
+    lib.kda_prefill_front_end_varlen.restype = i
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -369,6 +372,37 @@ def kda_prefill_front_end(qkv, conv_w, conv_state, heads: int, chunk: int, l2_ep
     rc = load_library().kda_prefill_front_end(*args, B, heads, T, chunk, K, float(l2_eps), _stream_ptr(stream))
     if rc != KDA_OK:
         raise KdaError("kda_prefill_front_end", rc)
+    return q, k, v
+
+
+def kda_prefill_front_end_varlen(qkv, conv_w, conv_state, cu_seqlens, heads: int, l2_eps: float, q=None, k=None,
+                                 v=None, stream=None):
+    """kda_prefill_front_end over packed sequences.  Returns (q, k, v), each float32 [total][H][128].
+
+    qkv: bfloat16 [total][3 H 128]; conv_state: float32 [n][3 H 128][K] (one per sequence, advanced in place);
+    cu_seqlens: int32 CUDA tensor [n + 1] of token offsets.
+    """
+    if not isinstance(qkv, torch.Tensor) or qkv.dim() != 2:
+        raise ValueError("qkv must be [total_tokens][3 * heads * 128]")
+    total, C = qkv.shape
+    if C != 3 * heads * HEAD_DIM:
+        raise ValueError(f"qkv has {C} channels, expected 3 * {heads} * {HEAD_DIM}")
+    if not (isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.dim() == 1 and cu_seqlens.numel() >= 2):
+        raise ValueError("cu_seqlens must be a 1-d tensor of n_seqs + 1 offsets")
+    n = cu_seqlens.numel() - 1
+    if conv_w.dim() != 2:
+        raise ValueError("conv_w must be [conv_dim][conv_kernel]")
+    K = conv_w.shape[1]
+    vs = (total, heads, HEAD_DIM)
+    q = torch.empty(vs, dtype=torch.float32, device=qkv.device) if q is None else q
+    k = torch.empty(vs, dtype=torch.float32, device=qkv.device) if k is None else k
+    v = torch.empty(vs, dtype=torch.float32, device=qkv.device) if v is None else v
+    args = [_check("qkv", qkv, (total, C), torch.bfloat16), _check("conv_w", conv_w, (C, K), torch.bfloat16),
+            _check("conv_state", conv_state, (n, C, K)), _check("q", q, vs), _check("k", k, vs), _check("v", v, vs),
+            _check("cu_seqlens", cu_seqlens, (n + 1,), torch.int32)]
+    rc = load_library().kda_prefill_front_end_varlen(*args, n, heads, total, K, float(l2_eps), _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_prefill_front_end_varlen", rc)
     return q, k, v
 
 

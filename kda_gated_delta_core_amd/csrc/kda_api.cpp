@@ -323,3 +323,32 @@ KDA_API int kda_prefill_front_end(const uint16_t* qkv, const uint16_t* conv_w, f
                                                  conv_kernel, l2_eps, static_cast<hipStream_t>(stream));
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
 }
+
+KDA_API int kda_prefill_front_end_varlen(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q,
+                                         float* k, float* v, const int* cu_seqlens, int n_seqs, int heads,
+                                         int total_tokens, int conv_kernel, float l2_eps, void* stream)
+{
+    if (!qkv || !conv_w || !conv_state || !q || !k || !v || !cu_seqlens) return KDA_ERR_INVALID_ARG;
+    if (!aligned({qkv, conv_w, conv_state, q, k, v}) || !aligned({cu_seqlens}, 4)) return KDA_ERR_INVALID_ARG;
+    if (n_seqs < 1 || n_seqs > KDA_VARLEN_MAX_SEQS || heads < 1 || heads > KDA_PREFILL_MAX_HEADS || total_tokens < 1)
+        return KDA_ERR_INVALID_ARG;
+    if (conv_kernel < 1) return KDA_ERR_INVALID_ARG;
+    if (!(isfinite(l2_eps) && l2_eps >= KDA_GATED_RMSNORM_MIN_EPS)) return KDA_ERR_INVALID_ARG;
+    if (conv_kernel > KDA_FRONT_END_MAX_CONV_KERNEL) return KDA_ERR_UNSUPPORTED;
+    const int64_t C = 3 * (int64_t)heads * KDA_HEAD_DIM;
+    const int64_t x = mul({total_tokens, C});
+    const int64_t w = mul({C, conv_kernel});
+    const int64_t st = mul({n_seqs, C, conv_kernel});
+    const int64_t vec = mul({total_tokens, heads, KDA_HEAD_DIM});
+    if (x < 0 || w < 0 || st < 0 || vec < 0) return KDA_ERR_INVALID_ARG;
+    // one wave per (32-token strip, part, head) vector; one thread per (sequence, channel)
+    if (mul({(total_tokens + 31) / 32, 3, heads}) > 0x7fffffffLL || mul({n_seqs, C}) > 0x7fffffffLL)
+        return KDA_ERR_INVALID_ARG;
+    const Range r[] = {{q, vec * 4},  {k, vec * 4},       {v, vec * 4}, {conv_state, st * 4},
+                       {qkv, x * 2},  {conv_w, w * 2},    {cu_seqlens, ((int64_t)n_seqs + 1) * 4}};
+    if (any_overlap(r, 7, 4)) return KDA_ERR_INVALID_ARG;
+    const int rc = kda::launch_prefill_front_end_varlen(qkv, conv_w, conv_state, q, k, v, cu_seqlens, n_seqs, heads,
+                                                        total_tokens, conv_kernel, l2_eps,
+                                                        static_cast<hipStream_t>(stream));
+    return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}

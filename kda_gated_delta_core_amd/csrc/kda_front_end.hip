@@ -189,6 +189,130 @@ __global__ __launch_bounds__(256) void prefill_conv_state_kernel(const unsigned 
     }
 }
 
+// Varlen form: sequences packed back to back (tokens cu[s] .. cu[s + 1] - 1 of
+// qkv [total][conv_dim]), each with its own conv state [n][conv_dim][K];
+// outputs [total][H][128], the inputs of kda_chunk_prefill_varlen.  Waves take
+// fixed strips of kFeStrip packed tokens; a strip may cross sequences, and at
+// the first row of a sequence the slots are re-seeded from that sequence's
+// conv state, so no window reaches across a boundary.  The offsets are read
+// clamped to [0, total], which keeps every access inside the buffers whatever
+// they hold (offsets that are not non-decreasing give unspecified values).
+__device__ __forceinline__ int fe_cu(const int* cu, int s, int total)
+{
+    const int c = cu[s];
+    return c < 0 ? 0 : (c > total ? total : c);
+}
+
+template <int K>
+__global__ __launch_bounds__(kFeThreads) void prefill_front_end_varlen_kernel(
+    const unsigned short* __restrict__ qkv, const unsigned short* __restrict__ conv_w,
+    const float* __restrict__ conv_state, float* __restrict__ q_out, float* __restrict__ k_out,
+    float* __restrict__ v_out, const int* __restrict__ cu, int n_seqs, int heads, int total, int n_strips, double eps)
+{
+    const int lane = threadIdx.x % 64;
+    const long long gv = (long long)blockIdx.x * kFeVecs + threadIdx.x / 64;
+    const int n_part = 3 * heads;
+    if (gv >= (long long)n_strips * n_part) return;  // whole waves leave; no workgroup barrier below
+    const int vec = (int)(gv % n_part), strip = (int)(gv / n_part);
+    const int part = vec / heads, h = vec % heads;
+    const int C = 3 * heads * kD;
+    const size_t cv = (size_t)vec * kD;
+    // rows past the last sequence (cu[n] .. total - 1) belong to none and are not written
+    const int t0 = strip * kFeStrip, t1 = min(min(total, t0 + kFeStrip), fe_cu(cu, n_seqs, total));
+    if (t0 >= t1) return;
+    // the sequence of row t0: the last s with cu[s] <= t0 (wave-uniform, scalar loads)
+    int lo = 0, hi = n_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (fe_cu(cu, mid, total) <= t0) lo = mid;
+        else hi = mid - 1;
+    }
+    int sq = lo, nxt = fe_cu(cu, sq + 1, total);  // the row where the sequence after sq begins
+    FeLane<K> f;
+    const unsigned short* const xp = qkv + cv + lane;  // row 0, channel l
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int i = 0; i < K; ++i) f.w[m][i] = bf16_to_f32(conv_w[(cv + lane + 64 * m) * K + i]);
+    auto seed = [&](int s, int t) {  // slots before row t of sequence s
+        // its first row; at most t, so the state slot below stays in [0, K) whatever the offsets hold
+        const int start = min(fe_cu(cu, s, total), t);
+        const float* const st = conv_state + ((size_t)s * C + cv) * K;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int i = 0; i < K; ++i) {
+                const int tau = t - K + i;  // packed row slot i holds; before the sequence: state slot
+                f.s[m][i] = tau >= start ? bf16_to_f32(xp[(size_t)tau * C + 64 * m])
+                                         : st[(size_t)(lane + 64 * m) * K + K + (tau - start)];
+            }
+    };
+    seed(sq, t0);
+    float* const out = part == 0 ? q_out : (part == 1 ? k_out : v_out);
+    unsigned short xn0 = xp[(size_t)t0 * C], xn1 = xp[(size_t)t0 * C + 64];
+    for (int t = t0; t < t1; ++t) {
+        const unsigned short x0 = xn0, x1 = xn1;
+        if (t + 1 < t1) {
+            xn0 = xp[(size_t)(t + 1) * C];
+            xn1 = xp[(size_t)(t + 1) * C + 64];
+        }
+        if (t >= nxt) {  // row t opens a later sequence (skipping empty ones): fresh slots from its state
+            while (sq + 1 < n_seqs && fe_cu(cu, sq + 1, total) <= t) ++sq;
+            nxt = sq + 1 < n_seqs ? fe_cu(cu, sq + 1, total) : total;
+            seed(sq, t);
+        }
+        float y[2];
+        fe_row(f, x0, x1, part < 2, eps, y);
+        float* const o = out + ((size_t)t * heads + h) * kD + lane;
+        o[0] = y[0];
+        o[64] = y[1];
+    }
+}
+
+// After a varlen prefill: each sequence's conv state becomes the inputs of its
+// last K tokens (old slots for times before its start).  One thread per
+// (sequence, channel); an empty sequence keeps its state.
+template <int K>
+__global__ __launch_bounds__(256) void prefill_conv_state_varlen_kernel(const unsigned short* __restrict__ qkv,
+                                                                        float* __restrict__ conv_state,
+                                                                        const int* __restrict__ cu, int n_seqs,
+                                                                        int C, int total)
+{
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;  // s * C + channel
+    if (i >= (long long)n_seqs * C) return;
+    const int s = (int)(i / C), c = (int)(i % C);
+    const int a = fe_cu(cu, s, total), e = max(a, fe_cu(cu, s + 1, total));
+    const int len = e - a;
+    float* const st = conv_state + (size_t)i * K;
+    float old[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) old[j] = st[j];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const int tau = len - K + j;  // local time; before the sequence when < 0: old slot K + tau
+        float keep = old[0];
+#pragma unroll
+        for (int u = 1; u < K; ++u) keep = (u == K + tau) ? old[u] : keep;
+        st[j] = tau >= 0 ? bf16_to_f32(qkv[(size_t)(a + tau) * C + c]) : keep;
+    }
+}
+
+template <int K>
+void launch_prefill_fe_varlen(const unsigned short* x, const unsigned short* w, float* conv_state, float* q, float* k,
+                              float* v, const int* cu, int n_seqs, int heads, int total, double eps,
+                              hipStream_t stream)
+{
+    const int n_strips = (total + kFeStrip - 1) / kFeStrip;
+    const long long n_vec = (long long)n_strips * 3 * heads;
+    hipLaunchKernelGGL(prefill_front_end_varlen_kernel<K>, dim3((unsigned)((n_vec + kFeVecs - 1) / kFeVecs)),
+                       dim3(kFeThreads), 0, stream, x, w, conv_state, q, k, v, cu, n_seqs, heads, total, n_strips,
+                       eps);
+    const int C = 3 * heads * kD;
+    const long long n_ch = (long long)n_seqs * C;
+    hipLaunchKernelGGL(prefill_conv_state_varlen_kernel<K>, dim3((unsigned)((n_ch + 255) / 256)), dim3(256), 0,
+                       stream, x, conv_state, cu, n_seqs, C, total);
+}
+
 template <int K>
 void launch_prefill_fe(const unsigned short* x, const unsigned short* w, float* conv_state, float* q, float* k,
                        float* v, int batch, int heads, int T, int t_pad, double eps, hipStream_t stream)
@@ -217,6 +341,23 @@ int launch_prefill_front_end(const uint16_t* qkv, const uint16_t* conv_w, float*
     case 2: launch_prefill_fe<2>(x, w, conv_state, q, k, v, batch, heads, T, t_pad, eps, stream); break;
     case 3: launch_prefill_fe<3>(x, w, conv_state, q, k, v, batch, heads, T, t_pad, eps, stream); break;
     case 4: launch_prefill_fe<4>(x, w, conv_state, q, k, v, batch, heads, T, t_pad, eps, stream); break;
+    default: return -1;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_prefill_front_end_varlen(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q,
+                                    float* k, float* v, const int* cu_seqlens, int n_seqs, int heads, int total,
+                                    int conv_kernel, float l2_eps, hipStream_t stream)
+{
+    const auto* x = reinterpret_cast<const unsigned short*>(qkv);
+    const auto* w = reinterpret_cast<const unsigned short*>(conv_w);
+    const double eps = l2_eps;
+    switch (conv_kernel) {
+    case 1: launch_prefill_fe_varlen<1>(x, w, conv_state, q, k, v, cu_seqlens, n_seqs, heads, total, eps, stream); break;
+    case 2: launch_prefill_fe_varlen<2>(x, w, conv_state, q, k, v, cu_seqlens, n_seqs, heads, total, eps, stream); break;
+    case 3: launch_prefill_fe_varlen<3>(x, w, conv_state, q, k, v, cu_seqlens, n_seqs, heads, total, eps, stream); break;
+    case 4: launch_prefill_fe_varlen<4>(x, w, conv_state, q, k, v, cu_seqlens, n_seqs, heads, total, eps, stream); break;
     default: return -1;
     }
     return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -48,6 +48,11 @@ int launch_prefill_front_end(const uint16_t* qkv, const uint16_t* conv_w, float*
                              float* v, int batch, int heads, int T, int t_pad, int conv_kernel, float l2_eps,
                              hipStream_t stream);
 
+// varlen prefill front end: qkv [total][conv_dim], conv state [n][conv_dim][K], q, k, v [total][H][128]
+int launch_prefill_front_end_varlen(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q,
+                                    float* k, float* v, const int* cu_seqlens, int n_seqs, int heads, int total,
+                                    int conv_kernel, float l2_eps, hipStream_t stream);
+
 int launch_gated_rmsnorm(const float* core, const uint16_t* gate, const uint16_t* weight, uint16_t* out,
                          long long n_vec, float eps, hipStream_t stream);
 

@@ -290,6 +290,31 @@ def test_prefill_front_end_refusals(lib):
 
 
 @no_gpu
+def test_prefill_front_end_varlen_refusals(lib):
+    f = lib.kda_prefill_front_end_varlen
+    bad = kda.KDA_ERR_INVALID_ARG
+    ok_args = (3, 2, 100, 4, 1e-6)  # n_seqs, heads, total, conv_kernel, eps
+    for i in range(7):
+        p = list(P[:7])
+        p[i] = None
+        assert f(*p, *ok_args, None) == bad, i
+        p = list(P[:7])
+        p[i] += 2 if i == 6 else 8  # cu_seqlens needs 4-byte alignment, the rest 16
+        assert f(*p, *ok_args, None) == bad, i
+    assert f(*P[:7], 0, 2, 100, 4, 1e-6, None) == bad
+    assert f(*P[:7], (1 << 20) + 1, 2, 100, 4, 1e-6, None) == bad
+    assert f(*P[:7], 3, 0, 100, 4, 1e-6, None) == bad
+    assert f(*P[:7], 3, 2, 0, 4, 1e-6, None) == bad
+    assert f(*P[:7], 3, 2, 100, 0, 1e-6, None) == bad
+    assert f(*P[:7], 3, 2, 100, 5, 1e-6, None) == kda.KDA_ERR_UNSUPPORTED
+    assert f(*P[:7], 3, 2, 100, 4, 0.0, None) == bad
+    for i, j in ((3, 0), (6, 2), (2, 5)):  # q over qkv, cu_seqlens inside the conv state, state over v
+        p = list(P[:7])
+        p[i] = p[j] + 16
+        assert f(*p, *ok_args, None) == bad, (i, j)
+
+
+@no_gpu
 def test_varlen_refusals(lib):
     f = lib.kda_chunk_prefill_varlen
     bad = kda.KDA_ERR_INVALID_ARG

@@ -107,3 +107,86 @@ def test_prefill_chain_front_end_core_norm(device):
     assert_close("core state", host(st), s_ref)
     r = oracle.gated_rmsnorm(host(out)[:, :T].reshape(B * T, H, D), nx["out_gate"], nx["o_norm"], ki.NORM_EPS)
     assert_within_one_ulp("norm", oracle.bf16_to_f64(host(y.view(torch.int16)).view(np.uint16)), r)
+
+
+def _varlen_fe_inputs(seed, lens, H, K, pad_tokens=5):
+    total = sum(lens) + pad_tokens  # rows past the last sequence belong to none
+    a = ki.front_end_inputs(seed, 1, total, H, K)
+    st = ki.front_end_inputs(seed + 1, len(lens), 1, H, K)["conv_state"]  # one conv state per sequence
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return a["qkv"][0], a["conv_w"], st, cu
+
+
+def _run_varlen(kda, qkv, w, st, cu, H):
+    total = qkv.shape[0]
+    q, k, v = (torch.full((total, H, D), SENTINEL, device="cuda") for _ in range(3))
+    cst = torch.from_numpy(st).cuda()
+    kda.kda_prefill_front_end_varlen(_bits_dev(qkv), _bits_dev(w), cst, torch.from_numpy(cu).cuda(), H, ki.L2_EPS,
+                                     q=q, k=k, v=v)
+    torch.cuda.synchronize()
+    return host(q), host(k), host(v), host(cst)
+
+
+@pytest.mark.parametrize("lens,H,K", [([5, 0, 70, 1, 33], 2, 4), ([1], 1, 4), ([0, 0, 64], 3, 3), ([100, 3, 0], 2, 2),
+                                      ([31, 32, 33, 1, 0, 2], 1, 1)])
+def test_prefill_front_end_varlen_matches_oracle(device, lens, H, K):
+    import kda_gated_delta_core_amd as kda
+    announce(f"kda_prefill_front_end_varlen lens={lens} H={H} K={K}")
+    qkv, w, st, cu = _varlen_fe_inputs(580 + sum(lens), lens, H, K)
+    q, k, v, cst = _run_varlen(kda, qkv, w, st, cu, H)
+    for s, n in enumerate(lens):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if n == 0:
+            assert np.array_equal(cst[s], st[s])  # an empty sequence keeps its conv state
+            continue
+        rq, rk, rv, rst, _ = oracle.decode_front_end(qkv[None, a:b], w, st[s:s + 1], H, ki.L2_EPS)
+        for name, g, r in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+            assert_close(f"seq {s} {name}", g[None, a:b], r, atol=FE_ATOL, rtol=FE_RTOL)
+        assert np.array_equal(cst[s:s + 1], rst)
+    end = int(cu[-1])
+    assert np.all(q[end:] == SENTINEL) and np.all(k[end:] == SENTINEL) and np.all(v[end:] == SENTINEL)
+
+
+def test_prefill_front_end_varlen_equals_dense_per_sequence_bitwise(device):
+    """Each packed sequence gets the bits kda_prefill_front_end gives it alone (B=1)."""
+    import kda_gated_delta_core_amd as kda
+    lens, H, K = [40, 1, 0, 95, 7], 2, 4
+    announce(f"kda_prefill_front_end_varlen vs kda_prefill_front_end per sequence lens={lens}")
+    qkv, w, st, cu = _varlen_fe_inputs(590, lens, H, K)
+    q, k, v, cst = _run_varlen(kda, qkv, w, st, cu, H)
+    for s, n in enumerate(lens):
+        if n == 0:
+            continue
+        a, b = int(cu[s]), int(cu[s + 1])
+        x = {"qkv": qkv[None, a:b].copy(), "conv_w": w, "conv_state": st[s:s + 1].copy()}
+        dq, dk, dv, dst = _run(kda, x, H, 16)
+        for pk, d in ((q, dq), (k, dk), (v, dv)):
+            assert np.array_equal(pk[a:b], d[0, :n]), s
+        assert np.array_equal(cst[s], dst[0]), s
+
+
+def test_varlen_prefill_chain(device):
+    """Varlen front end -> kda_chunk_prefill_varlen against the oracle per sequence (the core on the GPU's
+    q, k, v)."""
+    import kda_gated_delta_core_amd as kda
+    lens, H, K, C = [300, 0, 1, 129, 64], 4, 4, 64
+    announce(f"varlen prefill chain lens={lens} H={H}")
+    qkv, w, st, cu = _varlen_fe_inputs(600, lens, H, K, pad_tokens=0)
+    q, k, v, _ = _run_varlen(kda, qkv, w, st, cu, H)
+    core = ki.varlen_inputs(601, lens, H, -5.0, 0.02)
+    d = {n: torch.from_numpy(core[n]).cuda() for n in ("gate", "beta", "state", "cu_seqlens")}
+    out = kda.kda_chunk_prefill_varlen(torch.from_numpy(q).cuda(), torch.from_numpy(k).cuda(),
+                                       torch.from_numpy(v).cuda(), d["gate"], d["beta"], d["state"], d["cu_seqlens"],
+                                       C)
+    torch.cuda.synchronize()
+    got_o, got_s = host(out), host(d["state"])
+    for s, n in enumerate(lens):
+        if n == 0:
+            assert np.array_equal(got_s[s], core["state"][s])
+            continue
+        a, b = int(cu[s]), int(cu[s + 1])
+        sl = lambda arr: np.ascontiguousarray(arr[None, a:b])
+        o_ref, s_ref, _, _ = oracle.serial(sl(q), sl(k), sl(v), sl(core["gate"]), sl(core["beta"]),
+                                           core["state"][s:s + 1])
+        assert_close(f"seq {s} out", got_o[None, a:b], o_ref)
+        assert_close(f"seq {s} state", got_s[s:s + 1], s_ref)
