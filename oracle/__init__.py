@@ -16,6 +16,10 @@ on a scalar head, chunked == serial, pad independence, linearity, column
 equivariance, continuation).  gated_rmsnorm is pinned against torch's own
 rms_norm and sigmoid in fp64, closed forms (one-hot rows, gate 0 and +-inf),
 scale invariance and unit mean square (tests/test_oracle_norm_pins.py).
+``transition`` (the prefill's final state as an affine map P S + Q of its initial state) is pinned
+against the state the recurrence reaches from random initial states, the explicit product of the
+per-row factors, the matrix determinant lemma, composition of segments and the beta = 0 closed form
+(tests/test_oracle_transition_pins.py).
 """
 from __future__ import annotations
 
@@ -119,6 +123,32 @@ def chunk_stages(q, k, v, gate, beta, S0, b: int, h: int, t0: int, n: int) -> di
         raise ValueError("kda_oracle_chunk_stages rejected its arguments")
     res["S"] = S
     return res
+
+
+def transition(q, k, v, gate, beta, T: int | None = None, nthreads: int = 0):
+    """The final state of a prefill as an affine function of its initial state (kernels page,
+    chunk_scan: the state update of each chunk is linear in the incoming state plus a term from
+    the chunk's values).  Returns (P [B][H][D][D], Q [B][H][D][D]), fp64, such that for every
+    initial state S [D (key)][D (value)] the recurrence over the T rows ends in P @ S + Q.
+
+    Each row maps S to diag(alpha) S + beta k (v - (diag(alpha) S)^T k)^T, which is the linear map
+    (I - beta k k^T) diag(alpha) applied to S plus beta k v^T.  So P is the recurrence started
+    from the identity with every v set to 0 (a key-by-key state, one column per key), and Q is the
+    recurrence started from the zero state."""
+    q, k, v, gate, beta = map(_f32, (q, k, v, gate, beta))
+    B, rows, H, D = _shape(q, beta)
+    eye = np.broadcast_to(np.eye(D), (B, H, D, D))
+    _, P, _, _ = serial(q, k, np.zeros_like(v), gate, beta, eye, T=T, nthreads=nthreads)
+    _, Q, _, _ = serial(q, k, v, gate, beta, np.zeros((B, H, D, D)), T=T, nthreads=nthreads)
+    return P, Q
+
+
+def apply_transition(P, Q, S) -> np.ndarray:
+    """P @ S + Q per (sequence, head), fp64: the state a segment with transition (P, Q) ends in when
+    it starts from S (Q None: P @ S).  With S = Q1 and (P, Q) = (P2, Q2) it composes two segments,
+    and with S = P1 and Q None it gives the composed P2 P1."""
+    out = np.matmul(np.asarray(P, dtype=np.float64), np.asarray(S, dtype=np.float64))
+    return out if Q is None else out + np.asarray(Q, dtype=np.float64)
 
 
 def bf16_to_f64(bits) -> np.ndarray:
