@@ -68,6 +68,13 @@ def prefill_flops(B: int, H: int, T: int, C: int) -> float:
     return float(B) * H * T * (6 * D * D + 5 * C * D + C * C / 3.0)
 
 
+def transition_flops(B: int, H: int, T: int, C: int) -> float:
+    """Per token-head of the segment transition: 4 d^2 for each of P and Q (W S, Ktil^T Delta) + 3 C d
+    (lower-triangular A, W, U) + C^2 / 3 (triangular inverse).  The prepare also builds the output
+    operands of the record, which the transition does not use; they are not counted."""
+    return float(B) * H * T * (8 * D * D + 3 * C * D + C * C / 3.0)
+
+
 def prefill_bytes(B: int, H: int, T: int) -> int:
     return B * H * (2 * STATE_BYTES + T * (4 * D * 4 + D * 4 + 4))
 
@@ -429,6 +436,28 @@ def bench_prefill(torch, kda, ki, name, steps, warmup, timer):
     return w, r, extra
 
 
+def bench_transition(torch, kda, ki, name, T, steps, warmup, timer):
+    """kda_chunk_prefill_transition over the first T tokens of every sequence of workload `name`."""
+    w = ki.WORKLOADS[name]
+    B, H, C = w.batch, w.heads, w.chunk
+    t_pad = -(-T // C) * C
+    tens = {n: torch.empty((B, t_pad, H, D), device="cuda") for n in ("q", "k", "v", "gate")}
+    tens["beta"] = torch.empty((B, t_pad, H), device="cuda")
+    for s in range(B):
+        part = _sequence(ki, w, s, T, t_pad)
+        for n in tens:
+            tens[n][s].copy_(torch.from_numpy(part[n][0]).cuda())
+    P = torch.empty((B, H, D, D), device="cuda")
+    Q = torch.empty((B, H, D, D), device="cuda")
+    ws = torch.empty(kda.kda_chunk_prefill_workspace_bytes(B, H, T, C), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        kda.kda_chunk_prefill_transition(tens["q"], tens["k"], tens["v"], tens["gate"], tens["beta"], T, C,
+                                         trans_p=P, trans_q=Q, workspace=ws)
+
+    return w, timer.run(step, steps, warmup)
+
+
 def _sequence(ki, w, s, T, t_pad):
     import numpy as np
     arrays = {n: np.full((1, t_pad, w.heads, D), 0.0 if w.pad_value is None else w.pad_value, np.float32)
@@ -621,6 +650,18 @@ def main():
                "GB_per_s": prefill_bytes(w.batch, w.heads, w.T) / r["launch_avg_s"] / 1e9}
         res.update(extra)
         workloads[name] = res
+    # segment transitions: a whole T=8192 prefill as one segment, and one device's share of the
+    # 4 x 32768 prefill split into 8 token segments (4 sequences x 4096 tokens)
+    for name, base, T, steps, warm in (("transition_h32_t8192_c64", "prefill_h32_t8192_c64", 8192, 20, 20),
+                                       ("transition_b4_h32_t4096_c64", "prefill_b4_h32_t32768_c64", 4096, 10, 10)):
+        if not want(name):
+            continue
+        log(name)
+        w, r = bench_transition(torch, kda, ki, base, T, args.reps or steps, 0 if args.reps else warm, timer)
+        tf = transition_flops(w.batch, w.heads, T, w.chunk) / r["launch_avg_s"] / 1e12
+        workloads[name] = {"tokens_per_s": w.batch * T / r["s_per_step"], "ms_per_call": r["s_per_step"] * 1e3,
+                           "call_ms": r["launch_avg_s"] * 1e3, "algorithmic_TFLOP_per_s": tf,
+                           "mfma_frac": tf / MFMA_F32_PEAK_TFLOPS}
     for name in ki.VARLEN_WORKLOADS:
         if not want(name):
             continue

@@ -158,6 +158,49 @@ int kda_chunk_prefill_varlen(const float* q, const float* k, const float* v, con
                              int chunk, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Segment transition of a prefill: the final state of kda_chunk_prefill over
+ * these T tokens as an affine function of its initial state (layer page,
+ * Glm5NextKdaLayer::prefill; kernel-table page, chunk_scan, whose per-chunk
+ * update is linear in the incoming state plus a term from the chunk's
+ * values).  Not an operation of the pages: it is the per-device piece of
+ * splitting one long sequence across devices by token segments.  Each device
+ * computes its segment's (P, Q); the pairs are folded in segment order with
+ * kda_state_transition_apply to give every segment its true initial state;
+ * then each device runs kda_chunk_prefill on its segment from that state.
+ *
+ *   q, k, v, gate, beta : as kda_chunk_prefill (rows t >= T ignored)
+ *   trans_p             : [batch][heads][128][128] out, P[i][j] over key indices
+ *   trans_q             : [batch][heads][128 key][128 value] out
+ *   workspace           : >= kda_chunk_prefill_workspace_bytes(batch, heads, T, chunk)
+ *
+ * For every initial state S [128 key][128 value] the prefill's final state is
+ * P S + Q, up to FP32 rounding.  Q is the final state from S = 0; P is the
+ * product over the tokens, later ones on the left, of
+ * (I - beta k k^T) diag(exp(gate)), computed chunk by chunk from the identity.
+ * Both are written whole.  No output rows are produced.  Refusals and accuracy
+ * as kda_chunk_prefill, with trans_p and trans_q taking the place of state and
+ * out in the overlap checks.
+ */
+int kda_chunk_prefill_transition(const float* q, const float* k, const float* v, const float* gate,
+                                 const float* beta, float* trans_p, float* trans_q, int batch, int heads, int T,
+                                 int chunk, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * state <- trans_p state + trans_q for batch * heads states of 128 x 128 FP32,
+ * in place (trans_q NULL: state <- trans_p state).  The fold step of the
+ * segment transitions above: applied to a state it gives the state after the
+ * segment; applied to another segment's Q it composes two segments (P2 Q1 +
+ * Q2), and with trans_q NULL to its P it gives P2 P1.
+ *
+ *   trans_p, trans_q, state : [batch][heads][128][128], 16-byte aligned
+ *
+ * state must not overlap trans_p or trans_q (KDA_ERR_INVALID_ARG).  The
+ * products accumulate in FP32 over the 128 key indices.
+ */
+int kda_state_transition_apply(const float* trans_p, const float* trans_q, float* state, int batch, int heads,
+                               void* stream);
+
+/*
  * One recurrent decode step: one token per sequence (layer page,
  * Glm5NextKdaLayer::decode; kernel-table page, recurrent_smem).  Each head
  * state is read from HBM once and written once; the decayed state stays in

@@ -34,7 +34,7 @@ EXPORTED = ("kda_status_string", "kda_chunk_prefill_workspace_bytes", "kda_chunk
             "kda_recurrent_k", "kda_gated_rmsnorm", "kda_decode_front_end",
             "kda_chunk_prefill_varlen_workspace_bytes", "kda_chunk_prefill_varlen", "kda_recurrent_k_bf16",
             "kda_recurrent_step_bf16", "kda_decode_front_end_bf16", "kda_prefill_front_end",
-            "kda_prefill_front_end_varlen")
+            "kda_prefill_front_end_varlen", "kda_chunk_prefill_transition", "kda_state_transition_apply")
 GATED_RMSNORM_MIN_EPS = 1e-30
 
 _lib = None
@@ -85,6 +85,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_prefill_front_end.restype = i
     lib.kda_prefill_front_end_varlen.argtypes = [p] * 7 + [i] * 4 + [ctypes.c_float, p]
     lib.kda_prefill_front_end_varlen.restype = i
+    lib.kda_chunk_prefill_transition.argtypes = [p] * 7 + [i] * 4 + [p, sz, p]
+    lib.kda_chunk_prefill_transition.restype = i
+    lib.kda_state_transition_apply.argtypes = [p] * 3 + [i, i, p]
+    lib.kda_state_transition_apply.restype = i
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -261,6 +265,54 @@ def kda_chunk_prefill(q, k, v, gate, beta, state, T: int, chunk: int, out=None, 
     if rc != KDA_OK:
         raise KdaError("kda_chunk_prefill", rc)
     return out
+
+
+def kda_chunk_prefill_transition(q, k, v, gate, beta, T: int, chunk: int, trans_p=None, trans_q=None,
+                                 workspace=None, stream=None):
+    """Segment transition of a prefill: (P, Q), [B][H][128][128] each, such that the prefill of these T
+    tokens from any initial state S ends in P S + Q.  Inputs and workspace as kda_chunk_prefill.
+    Returns (trans_p, trans_q)."""
+    B, rows, H = _vec_shapes(q)
+    if chunk not in (16, 32, 64):
+        raise KdaError("kda_chunk_prefill_transition", KDA_ERR_UNSUPPORTED)
+    t_pad = -(-int(T) // chunk) * chunk
+    if rows != t_pad:
+        raise ValueError(f"inputs must hold T_pad = {t_pad} rows per sequence, got {rows}")
+    vs, ss = (B, t_pad, H, HEAD_DIM), (B, H, HEAD_DIM, HEAD_DIM)
+    if trans_p is None:
+        trans_p = torch.empty(ss, dtype=torch.float32, device=q.device)
+    if trans_q is None:
+        trans_q = torch.empty(ss, dtype=torch.float32, device=q.device)
+    need = kda_chunk_prefill_workspace_bytes(B, H, int(T), chunk)
+    if workspace is None:
+        workspace = _workspace(need, q.device, stream)
+    if not (workspace.device.type == "cuda" and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    args = [_check(n, t, vs) for n, t in (("q", q), ("k", k), ("v", v), ("gate", gate))]
+    args.append(_check("beta", beta, (B, t_pad, H)))
+    args.append(_check("trans_p", trans_p, ss))
+    args.append(_check("trans_q", trans_q, ss))
+    rc = load_library().kda_chunk_prefill_transition(*args, B, H, int(T), chunk, workspace.data_ptr(), ws_bytes,
+                                                     _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_chunk_prefill_transition", rc)
+    return trans_p, trans_q
+
+
+def kda_state_transition_apply(trans_p, trans_q, state, stream=None):
+    """state <- trans_p @ state + trans_q in place (trans_q None: trans_p @ state), per (sequence, head);
+    all [B][H][128][128] float32.  Returns ``state``."""
+    if not isinstance(state, torch.Tensor) or state.dim() != 4:
+        raise ValueError("state must be [batch][heads][128][128]")
+    B, H = state.shape[0], state.shape[1]
+    ss = (B, H, HEAD_DIM, HEAD_DIM)
+    args = [_check("trans_p", trans_p, ss), None if trans_q is None else _check("trans_q", trans_q, ss),
+            _check("state", state, ss)]
+    rc = load_library().kda_state_transition_apply(*args, B, H, _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_state_transition_apply", rc)
+    return state
 
 
 def kda_gated_rmsnorm(core, out_gate, o_norm, eps: float, out=None, stream=None):

@@ -113,6 +113,48 @@ KDA_API int kda_chunk_prefill(const float* q, const float* k, const float* v, co
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 
+KDA_API int kda_chunk_prefill_transition(const float* q, const float* k, const float* v, const float* gate,
+                                         const float* beta, float* trans_p, float* trans_q, int batch, int heads,
+                                         int T, int chunk, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!q || !k || !v || !gate || !beta || !trans_p || !trans_q) return KDA_ERR_INVALID_ARG;
+    if (!aligned({q, k, v, gate, trans_p, trans_q, workspace}) || !aligned({beta}, 4)) return KDA_ERR_INVALID_ARG;
+    if (batch < 1 || heads < 1 || T < 1) return KDA_ERR_INVALID_ARG;
+    if (!chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
+    const int64_t need = prefill_ws_bytes(batch, heads, T, chunk);
+    const int64_t t_pad = ((int64_t)T + chunk - 1) / chunk * chunk;
+    const int64_t vec = mul({batch, t_pad, heads, KDA_HEAD_DIM});
+    const int64_t sca = mul({batch, t_pad, heads});
+    const int64_t st = mul({batch, heads, KDA_HEAD_DIM, KDA_HEAD_DIM});
+    if (need < 0 || vec < 0 || sca < 0 || st < 0 || t_pad > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)batch * heads > 0x7fffffffLL / 128) return KDA_ERR_INVALID_ARG;  // scan grid (P and Q groups)
+    if (heads > KDA_PREFILL_MAX_HEADS) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)batch * heads * (t_pad / chunk) > (1LL << 30)) return KDA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < (size_t)need) return KDA_ERR_WORKSPACE;
+    const Range r[] = {{trans_p, st * 4}, {trans_q, st * 4}, {workspace, need}, {q, vec * 4}, {k, vec * 4},
+                       {v, vec * 4},      {gate, vec * 4},   {beta, sca * 4}};
+    if (any_overlap(r, 8, 3)) return KDA_ERR_INVALID_ARG;
+    const int rc = kda::launch_chunk_prefill_transition(q, k, v, gate, beta, trans_p, trans_q, batch, heads, T,
+                                                        (int)t_pad, chunk, static_cast<float*>(workspace),
+                                                        static_cast<hipStream_t>(stream));
+    return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+KDA_API int kda_state_transition_apply(const float* trans_p, const float* trans_q, float* state, int batch,
+                                       int heads, void* stream)
+{
+    if (!trans_p || !state) return KDA_ERR_INVALID_ARG;
+    if (!aligned({trans_p, trans_q, state})) return KDA_ERR_INVALID_ARG;
+    if (batch < 1 || heads < 1 || (int64_t)batch * heads > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
+    const int64_t st = mul({batch, heads, KDA_HEAD_DIM, KDA_HEAD_DIM});
+    if (st < 0) return KDA_ERR_INVALID_ARG;
+    const Range r[] = {{state, st * 4}, {trans_p, st * 4}, {trans_q, trans_q ? st * 4 : 0}};
+    if (any_overlap(r, 3, 1)) return KDA_ERR_INVALID_ARG;
+    const int rc = kda::launch_transition_apply(trans_p, trans_q, state, batch * heads,
+                                                static_cast<hipStream_t>(stream));
+    return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
 namespace {
 
 // records and metadata of the varlen workspace: (record floats, byte size) or -1

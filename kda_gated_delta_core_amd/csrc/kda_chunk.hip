@@ -745,18 +745,21 @@ __device__ __forceinline__ void scan_load(ScanOps<C, NCT>& o, rsrc_t rec, const 
 // The operands of a later chunk are loaded into `nxt` one tile after every
 // group of MFMAs, so the compute unit's vector-memory path takes them while
 // the matrix core works instead of in one burst that the waves wait behind.
-template <int C, int NCT>
+// kTrans: the transition form (no output tiles, no output waves); with homog
+// the chunk's U is taken as zero (Delta = -W S), the homogeneous part of the
+// update.
+template <int C, int NCT, bool kTrans = false>
 __device__ __forceinline__ void scan_chunk(const ScanOps<C, NCT>& cur, ScanOps<C, NCT>& nxt, rsrc_t nrec,
                                            const ScanOffsets& off, floatx4 (*sIn)[NCT][64],
                                            floatx4 (*sOut)[NCT][64], floatx4 (*sDelta)[NCT][64],
                                            float (*sO)[NCT][kOutTile], float* __restrict__ out_b, int out_voff,
                                            int c, bool is_d, int xd, bool is_p, int xp, int wave, int lane, int q4,
-                                           int heads, int T)
+                                           int heads, int T, bool homog = false)
 {
     constexpr int NT = C / 16;
     // at C = 64 every wave has a role in step A: no branch, so the wait counts
     // the compiler derives never merge a path that issued loads with one that did not
-    constexpr bool kAllRoles = 2 * NT == kScanThreads / 64;
+    constexpr bool kAllRoles = !kTrans && 2 * NT == kScanThreads / 64;
     // A. Delta = U - W S (Delta waves) and O = R + P S (output waves)
     if (kAllRoles || is_d || is_p) {
         floatx4 st[8][NCT];
@@ -796,11 +799,12 @@ __device__ __forceinline__ void scan_chunk(const ScanOps<C, NCT>& cur, ScanOps<C
         if (is_d) {
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
+                const float4 u = homog ? make_float4(0.f, 0.f, 0.f, 0.f) : cur.x[ct];
                 floatx4 d;
-                d[0] = cur.x[ct].x - acc[ct][0];
-                d[1] = cur.x[ct].y - acc[ct][1];
-                d[2] = cur.x[ct].z - acc[ct][2];
-                d[3] = cur.x[ct].w - acc[ct][3];
+                d[0] = u.x - acc[ct][0];
+                d[1] = u.y - acc[ct][1];
+                d[2] = u.z - acc[ct][2];
+                d[3] = u.w - acc[ct][3];
                 sDelta[xd][ct][lane] = d;
             }
         } else {
@@ -857,7 +861,7 @@ __device__ __forceinline__ void scan_chunk(const ScanOps<C, NCT>& cur, ScanOps<C
     }
     // C. output tile xd: row lane / 4 of the tile, columns 4 (lane % 4) + 0..3 of
     // each 16-column tile, one 16-byte store per lane and column tile
-    if (is_d) {
+    if (!kTrans && is_d) {
         const int r = lane >> 2, j = lane & 3;
         const int t = c * C + 16 * xd + r;
         if (t < T) {
@@ -873,7 +877,14 @@ __device__ __forceinline__ void scan_chunk(const ScanOps<C, NCT>& cur, ScanOps<C
 // One workgroup per (sequence, head, group of 16 NCT value columns); the 8 / NCT
 // groups of a head are mapped to one XCD (blockIdx % 8) so the head's records
 // are fetched into that XCD's L2 once.
-template <int C, int NCT, class Layout>
+//
+// kTrans: the segment transition instead of the scan, with `state` the Q
+// output and `out` the P output, both [n_bh][128][128] and written whole.  A
+// head gets twice the groups: the first 8 / NCT run the update from the zero
+// state (Q, the final state of the segment from S = 0), the others run its
+// homogeneous part (U taken as zero) from the identity, one column per key
+// (P: the final state from S is P S + Q).  No outputs are produced.
+template <int C, int NCT, class Layout, bool kTrans = false>
 __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(const float* __restrict__ ws,
                                                                   float* __restrict__ state, float* __restrict__ out,
                                                                   int n_bh, int heads, Layout layout)
@@ -881,10 +892,13 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(const float* _
     using G = ChunkGeom<C>;
     constexpr int NT = G::kTiles;
     constexpr int kGroups = 8 / NCT;  // column groups per head
+    constexpr int kSlots = kTrans ? 2 * kGroups : kGroups;
     const int n = blockIdx.x;
     const int xcd = n & 7, k8 = n >> 3;
-    const int slice = k8 % kGroups;
-    const int bh = (k8 / kGroups) * 8 + xcd;
+    const int slot = k8 % kSlots;
+    const bool homog = kTrans && slot >= kGroups;
+    const int slice = homog ? slot - kGroups : slot;
+    const int bh = (k8 / kSlots) * 8 + xcd;
     if (bh >= n_bh) return;
     const SeqPos sq = layout.seq(bh);
     const int nchunks = sq.nchunks, T = sq.T;
@@ -893,15 +907,15 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(const float* _
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
     const int ct0 = NCT * slice, v0 = 16 * ct0;
-    const bool is_d = wave < NT, is_p = wave >= NT && wave < 2 * NT;
+    const bool is_d = wave < NT, is_p = !kTrans && wave >= NT && wave < 2 * NT;
     const int xd = wave, xp = wave - NT;
 
     __shared__ floatx4 sDelta[NT][NCT][64];
     __shared__ floatx4 sS[2][8][NCT][64];
     __shared__ __attribute__((aligned(16))) float sO[NT][NCT][kOutTile];
 
-    float* const S_head = state + (size_t)bh * kD * kD;
-    float* const out_b = out + sq.tok0 * heads * kD;
+    float* const S_head = (homog ? out : state) + (size_t)bh * kD * kD;
+    float* const out_b = kTrans ? nullptr : out + sq.tok0 * heads * kD;
     // byte offset of this lane's output row (16 xd + lane / 4) and columns
     // v0 + 4 (lane % 4) + 0..3 inside a chunk's output rows
     const int out_voff = ((16 * xd + (lane >> 2)) * heads * kD + h * kD + v0 + 4 * (lane & 3)) * 4;
@@ -909,7 +923,11 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(const float* _
     for (int ct = 0; ct < NCT; ++ct) {
         floatx4 st;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st[e] = S_head[(size_t)(16 * wave + 4 * q4 + e) * kD + v0 + 16 * ct + l16];
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * wave + 4 * q4 + e, col = v0 + 16 * ct + l16;
+            if constexpr (kTrans) st[e] = homog && row == col ? 1.f : 0.f;
+            else st[e] = S_head[(size_t)row * kD + col];
+        }
         sS[0][wave][ct][lane] = st;
     }
     const float* const rec0 = ws + sq.rec0 * G::kRecord;
@@ -930,19 +948,19 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(const float* _
     // which a round ends.
     int c = 0;
     for (; c + 3 <= nchunks; c += 3) {
-        scan_chunk<C, NCT>(op0, op2, rec(c + 2), off, sS[c & 1], sS[(c + 1) & 1], sDelta, sO, out_b, out_voff, c, is_d,
-                           xd, is_p, xp, wave, lane, q4, heads, T);
-        scan_chunk<C, NCT>(op1, op0, rec(c + 3), off, sS[(c + 1) & 1], sS[c & 1], sDelta, sO, out_b, out_voff, c + 1,
-                           is_d, xd, is_p, xp, wave, lane, q4, heads, T);
-        scan_chunk<C, NCT>(op2, op1, rec(c + 4), off, sS[c & 1], sS[(c + 1) & 1], sDelta, sO, out_b, out_voff, c + 2,
-                           is_d, xd, is_p, xp, wave, lane, q4, heads, T);
+        scan_chunk<C, NCT, kTrans>(op0, op2, rec(c + 2), off, sS[c & 1], sS[(c + 1) & 1], sDelta, sO, out_b, out_voff, c, is_d,
+                           xd, is_p, xp, wave, lane, q4, heads, T, homog);
+        scan_chunk<C, NCT, kTrans>(op1, op0, rec(c + 3), off, sS[(c + 1) & 1], sS[c & 1], sDelta, sO, out_b, out_voff, c + 1,
+                           is_d, xd, is_p, xp, wave, lane, q4, heads, T, homog);
+        scan_chunk<C, NCT, kTrans>(op2, op1, rec(c + 4), off, sS[c & 1], sS[(c + 1) & 1], sDelta, sO, out_b, out_voff, c + 2,
+                           is_d, xd, is_p, xp, wave, lane, q4, heads, T, homog);
     }
     if (c < nchunks)
-        scan_chunk<C, NCT>(op0, op2, rec(c + 2), off, sS[c & 1], sS[(c + 1) & 1], sDelta, sO, out_b, out_voff, c, is_d,
-                           xd, is_p, xp, wave, lane, q4, heads, T);
+        scan_chunk<C, NCT, kTrans>(op0, op2, rec(c + 2), off, sS[c & 1], sS[(c + 1) & 1], sDelta, sO, out_b, out_voff, c, is_d,
+                           xd, is_p, xp, wave, lane, q4, heads, T, homog);
     if (c + 1 < nchunks)
-        scan_chunk<C, NCT>(op1, op0, rec(c + 3), off, sS[(c + 1) & 1], sS[c & 1], sDelta, sO, out_b, out_voff, c + 1,
-                           is_d, xd, is_p, xp, wave, lane, q4, heads, T);
+        scan_chunk<C, NCT, kTrans>(op1, op0, rec(c + 3), off, sS[(c + 1) & 1], sS[c & 1], sDelta, sO, out_b, out_voff, c + 1,
+                           is_d, xd, is_p, xp, wave, lane, q4, heads, T, homog);
     // the final state is in sS[nchunks & 1]
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -952,18 +970,19 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(const float* _
     }
 }
 
-template <int C, int NCT, class Layout>
+template <int C, int NCT, class Layout, bool kTrans = false>
 static int launch_scan(const float* ws, float* state, float* out, long long n_bh, int heads, const Layout& layout,
                        hipStream_t stream)
 {
-    const unsigned grid = (unsigned)(((n_bh + 7) / 8) * 64 / NCT);
-    hipLaunchKernelGGL((chunk_scan_kernel<C, NCT, Layout>), dim3(grid), dim3(kScanThreads), 0, stream, ws, state,
-                       out, (int)n_bh, heads, layout);
+    const unsigned grid = (unsigned)(((n_bh + 7) / 8) * 64 / NCT * (kTrans ? 2 : 1));
+    hipLaunchKernelGGL((chunk_scan_kernel<C, NCT, Layout, kTrans>), dim3(grid), dim3(kScanThreads), 0, stream, ws,
+                       state, out, (int)n_bh, heads, layout);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-// max_records bounds the layout's record count (exact for the dense layout)
-template <int C, class Layout>
+// max_records bounds the layout's record count (exact for the dense layout).
+// kTrans: state is the Q output and out the P output of the transition form.
+template <int C, class Layout, bool kTrans = false>
 static int launch_chunk(const float* q, const float* k, const float* v, const float* gate, const float* beta,
                         float* state, float* out, long long n_bh, int heads, long long max_records, float* ws,
                         const Layout& layout, hipStream_t stream)
@@ -982,14 +1001,15 @@ static int launch_chunk(const float* q, const float* k, const float* v, const fl
     // 32-column workgroups when 16-column ones would not fit the compute units
     // in one round and 32-column ones still fill them (results are the same
     // bits either way: value columns never mix)
+    const long long slots = kTrans ? 2 : 1;  // the transition form runs P and Q groups
     if constexpr (C == 64) {
-        if (n_bh * 8 > n_cu && n_bh * 4 >= n_cu)
-            return launch_scan<C, 2>(ws, state, out, n_bh, heads, layout, stream);
+        if (n_bh * 8 * slots > n_cu && n_bh * 4 * slots >= n_cu)
+            return launch_scan<C, 2, Layout, kTrans>(ws, state, out, n_bh, heads, layout, stream);
     }
-    return launch_scan<C, 1>(ws, state, out, n_bh, heads, layout, stream);
+    return launch_scan<C, 1, Layout, kTrans>(ws, state, out, n_bh, heads, layout, stream);
 }
 
-template <int C>
+template <int C, bool kTrans = false>
 static int launch_dense(const float* q, const float* k, const float* v, const float* gate, const float* beta,
                         float* state, float* out, int batch, int heads, int T, int t_pad, float* ws,
                         hipStream_t stream)
@@ -997,7 +1017,8 @@ static int launch_dense(const float* q, const float* k, const float* v, const fl
     const int nchunks = t_pad / C;
     const long long n_bh = (long long)batch * heads;
     const DenseLayout layout{heads, T, t_pad, nchunks, (int)(n_bh * nchunks)};
-    return launch_chunk<C>(q, k, v, gate, beta, state, out, n_bh, heads, n_bh * nchunks, ws, layout, stream);
+    return launch_chunk<C, DenseLayout, kTrans>(q, k, v, gate, beta, state, out, n_bh, heads, n_bh * nchunks, ws,
+                                                layout, stream);
 }
 
 int launch_chunk_prefill(const float* q, const float* k, const float* v, const float* gate, const float* beta,
@@ -1010,6 +1031,72 @@ int launch_chunk_prefill(const float* q, const float* k, const float* v, const f
     case 64: return launch_dense<64>(q, k, v, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream);
     default: return -1;
     }
+}
+
+int launch_chunk_prefill_transition(const float* q, const float* k, const float* v, const float* gate,
+                                    const float* beta, float* trans_p, float* trans_q, int batch, int heads, int T,
+                                    int t_pad, int chunk, float* workspace, hipStream_t stream)
+{
+    switch (chunk) {
+    case 16: return launch_dense<16, true>(q, k, v, gate, beta, trans_q, trans_p, batch, heads, T, t_pad, workspace, stream);
+    case 32: return launch_dense<32, true>(q, k, v, gate, beta, trans_q, trans_p, batch, heads, T, t_pad, workspace, stream);
+    case 64: return launch_dense<64, true>(q, k, v, gate, beta, trans_q, trans_p, batch, heads, T, t_pad, workspace, stream);
+    default: return -1;
+    }
+}
+
+// S <- P S + Q for n independent 128 x 128 states (Q null: S <- P S): the
+// fold of segment transitions, and their composition (P2 P1, P2 Q1 + Q2).
+// One workgroup per state.  The whole incoming state is staged in LDS before
+// any of it is overwritten, so S is updated in place; wave w computes rows
+// 16 w .. 16 w + 15 of the result over all 128 columns with the 16x16x4 FP32
+// MFMA, the key index as the reduction, one chain per 16-column tile.
+constexpr int kApplyThreads = 512;
+
+__global__ __launch_bounds__(kApplyThreads) void transition_apply_kernel(const float* __restrict__ P,
+                                                                         const float* __restrict__ Q, float* S, int n)
+{
+    const int u = blockIdx.x;
+    if (u >= n) return;  // the whole workgroup leaves together, before its barrier
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, q4 = lane >> 4;
+    // tile (row block rb, column tile ct), element e of lane l: S[16 rb + 4 (l / 16) + e][16 ct + l % 16]
+    __shared__ floatx4 sS[8][8][64];
+    float* const Su = S + (size_t)u * kD * kD;
+    const float* const Pu = P + (size_t)u * kD * kD;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+        floatx4 st;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st[e] = Su[(size_t)(16 * wave + 4 * q4 + e) * kD + 16 * ct + l16];
+        sS[wave][ct][lane] = st;
+    }
+    __syncthreads();
+    floatx4 acc[8];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            acc[ct][e] = Q ? Q[(size_t)u * kD * kD + (size_t)(16 * wave + 4 * q4 + e) * kD + 16 * ct + l16] : 0.f;
+#pragma unroll
+    for (int tau = 0; tau < 8; ++tau) {
+        // A operand: P[16 w + l % 16][16 tau + 4 (l / 16) + e] for the e-th key step
+        const float4 a = ld4(Pu + (size_t)(16 * wave + l16) * kD + 16 * tau + 4 * q4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) acc[ct] = mfma4(comp(a, e), sS[tau][ct][lane][e], acc[ct]);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Su[(size_t)(16 * wave + 4 * q4 + e) * kD + 16 * ct + l16] = acc[ct][e];
+}
+
+int launch_transition_apply(const float* P, const float* Q, float* S, int n, hipStream_t stream)
+{
+    hipLaunchKernelGGL(transition_apply_kernel, dim3((unsigned)n), dim3(kApplyThreads), 0, stream, P, Q, S, n);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 // Varlen set-up, one workgroup: token offsets clamped to [0, total] and made

@@ -33,6 +33,14 @@ int launch_chunk_prefill(const float* q, const float* k, const float* v, const f
                          float* state, float* out, int batch, int heads, int T, int t_pad, int chunk,
                          float* workspace, hipStream_t stream);
 
+// the transition form of the prefill: P, Q [B][H][128][128], the final state from S being P S + Q
+int launch_chunk_prefill_transition(const float* q, const float* k, const float* v, const float* gate,
+                                    const float* beta, float* trans_p, float* trans_q, int batch, int heads, int T,
+                                    int t_pad, int chunk, float* workspace, hipStream_t stream);
+
+// S <- P S + Q (Q may be null) for n states of 128 x 128, in place
+int launch_transition_apply(const float* P, const float* Q, float* S, int n, hipStream_t stream);
+
 int launch_chunk_prefill_varlen(const float* q, const float* k, const float* v, const float* gate, const float* beta,
                                 float* state, float* out, const int* cu_seqlens, int n_seqs, int heads, int total,
                                 int chunk, float* workspace, size_t meta_offset_floats, long long max_records,

@@ -365,3 +365,42 @@ def test_library_allocates_copies_and_synchronises_nothing():
     assert hip <= allowed, sorted(hip - allowed)
     for bad in ("Malloc", "Free", "Memcpy", "Memset", "Synchronize", "HostRegister"):
         assert not any(bad in name for name in hip), bad
+
+
+@no_gpu
+def test_transition_refusals(lib):
+    f = lib.kda_chunk_prefill_transition
+    bad = kda.KDA_ERR_INVALID_ARG
+    need = kda.kda_chunk_prefill_workspace_bytes(1, 2, 64, 16)
+    for i in range(7):
+        p = list(P[:7])
+        p[i] = None
+        assert f(*p, 1, 2, 64, 16, P[7], need, None) == bad, i
+        p = list(P[:7])
+        p[i] += 8 if i != 4 else 2  # beta needs 4-byte alignment, the rest 16
+        assert f(*p, 1, 2, 64, 16, P[7], need, None) == bad, i
+    assert f(*P[:7], 0, 2, 64, 16, P[7], need, None) == bad
+    assert f(*P[:7], 1, 0, 64, 16, P[7], need, None) == bad
+    assert f(*P[:7], 1, 2, 0, 16, P[7], need, None) == bad
+    assert f(*P[:7], 1, 2, 64, 48, P[7], 1 << 30, None) == kda.KDA_ERR_UNSUPPORTED
+    assert f(*P[:7], 1, 2, 64, 16, P[7], need - 1, None) == kda.KDA_ERR_WORKSPACE
+    assert f(*P[:7], 1, 2, 64, 16, None, need, None) == kda.KDA_ERR_WORKSPACE
+    assert f(*P[:7], 1, 16385, 64, 16, P[7], 1 << 40, None) == bad
+    for i, j in ((5, 0), (6, 5), (5, 6)):  # P over q, Q over P, P over Q
+        p = list(P[:7])
+        p[i] = p[j] + 64
+        assert f(*p, 1, 2, 64, 16, P[7], need, None) == bad, (i, j)
+    assert f(*P[:7], 1, 2, 64, 16, P[6] + 256, need, None) == bad  # workspace over Q
+
+    g = lib.kda_state_transition_apply
+    assert g(None, P[1], P[2], 1, 2, None) == bad
+    assert g(P[0], P[1], None, 1, 2, None) == bad
+    assert g(P[0] + 4, P[1], P[2], 1, 2, None) == bad
+    assert g(P[0], P[1] + 4, P[2], 1, 2, None) == bad
+    assert g(P[0], P[1], P[2] + 4, 1, 2, None) == bad
+    assert g(P[0], P[1], P[2], 0, 2, None) == bad
+    assert g(P[0], P[1], P[2], 1, 0, None) == bad
+    assert g(P[0], P[1], P[0] + 256, 1, 2, None) == bad  # state over P
+    assert g(P[0], P[1], P[1], 1, 2, None) == bad  # state is Q
+    assert g(P[0], None, P[0], 1, 2, None) == bad  # state is P, Q absent
+    assert g(P[0], P[1], P[2], 1 << 20, 1 << 12, None) == bad  # more states than one grid holds

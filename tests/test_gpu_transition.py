@@ -1,0 +1,177 @@
+"""GPU parity of the segment transition (P, Q) of a prefill and of the fold S <- P S + Q, through the
+C ABI, against the fp64 oracle; and the split of one sequence into token segments (each segment's
+transition, the fold in segment order, then each segment's prefill from its folded initial state)
+against the prefill of the whole sequence."""
+import numpy as np
+import pytest
+
+import kda_inputs as ki
+import oracle
+from kda_testlib import SENTINEL, announce, assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _padded(x, t0, t1, C):
+    """Rows [t0, t1) of every input, padded with NaN to a whole number of chunks."""
+    n = t1 - t0
+    t_pad = -(-n // C) * C
+    res = {}
+    for name in ("q", "k", "v", "gate", "beta"):
+        a = x[name][:, t0:t1]
+        pad = np.full((a.shape[0], t_pad - n) + a.shape[2:], np.nan, np.float32)
+        res[name] = dev(np.concatenate([a, pad], axis=1))
+    return res
+
+
+def _transition(kda, seg, T, C):
+    import torch
+    B, _, H, _ = seg["q"].shape
+    P = torch.full((B, H, 128, 128), SENTINEL, device="cuda")
+    Q = torch.full((B, H, 128, 128), SENTINEL, device="cuda")
+    kda.kda_chunk_prefill_transition(seg["q"], seg["k"], seg["v"], seg["gate"], seg["beta"], T, C,
+                                     trans_p=P, trans_q=Q)
+    torch.cuda.synchronize()
+    return P, Q
+
+
+def _check_contract(x, T, P, Q, seed):
+    """P S + Q against the state the oracle's recurrence reaches from a random initial state S: the
+    contract itself, meaningful also where P has decayed below the FP32 range (every row shrinks
+    each key direction it updates, so over long segments P tends to zero whatever the gates)."""
+    S = np.random.default_rng(seed).standard_normal(x["state"].shape).astype(np.float32)
+    sl = lambda n: x[n][:, :T]
+    _, s_ref, _, _ = oracle.serial(sl("q"), sl("k"), sl("v"), sl("gate"), sl("beta"), S)
+    got = np.matmul(host(P).astype(np.float64), S.astype(np.float64)) + host(Q)
+    assert_close("P S + Q", got, s_ref)
+
+
+# Gates near 0 and short segments keep P inside the FP32 range, so P itself is compared; with gates
+# down to -5 (the prefill workloads' range) P underflows within a few dozen tokens and only the
+# contract P S + Q and Q are meaningful.
+@pytest.mark.parametrize("B,H,T,C", [(1, 2, 64, 16), (2, 3, 100, 32), (1, 2, 130, 64), (2, 1, 1, 64),
+                                     (1, 3, 17, 16), (1, 2, 200, 64)])
+def test_transition_matches_oracle(device, B, H, T, C):
+    import kda_gated_delta_core_amd as kda
+    announce(f"kda_chunk_prefill_transition B={B} H={H} T={T} C={C} mild gates")
+    x = ki.make_batch(7000 + T + C, B, H, T, -0.02, 0.02)
+    P, Q = _transition(kda, _padded(x, 0, T, C), T, C)
+    P_ref, Q_ref = oracle.transition(x["q"], x["k"], x["v"], x["gate"], x["beta"])
+    assert float(np.linalg.norm(P_ref)) > 0.1
+    assert_close("P", host(P), P_ref)
+    assert_close("Q", host(Q), Q_ref)
+    _check_contract(x, T, P, Q, 7001)
+
+
+@pytest.mark.parametrize("T,C", [(100, 16), (130, 64), (333, 32)])
+def test_transition_steep_gates(device, T, C):
+    import kda_gated_delta_core_amd as kda
+    B, H = 2, 3
+    announce(f"kda_chunk_prefill_transition B={B} H={H} T={T} C={C} gates to -5")
+    x = ki.make_batch(7050 + T, B, H, T, -5.0, 0.02)
+    P, Q = _transition(kda, _padded(x, 0, T, C), T, C)
+    P_ref, Q_ref = oracle.transition(x["q"], x["k"], x["v"], x["gate"], x["beta"])
+    assert_close("Q", host(Q), Q_ref)
+    assert float(np.abs(host(P) - P_ref).max()) <= 1e-6
+    _check_contract(x, T, P, Q, 7051)
+
+
+def test_transition_mild_gates_long(device):
+    """gates near 0 over many chunks keep P well inside the FP32 range (the homogeneous part is
+    exercised, not decayed away)"""
+    import kda_gated_delta_core_amd as kda
+    B, H, T, C = 1, 2, 1000, 64
+    announce(f"kda_chunk_prefill_transition mild gates B={B} H={H} T={T} C={C}")
+    x = ki.make_batch(7101, B, H, T, -0.005, 0.02)
+    P, Q = _transition(kda, _padded(x, 0, T, C), T, C)
+    P_ref, Q_ref = oracle.transition(x["q"], x["k"], x["v"], x["gate"], x["beta"])
+    assert float(np.abs(P_ref).max()) > 1e-3
+    assert_close("P", host(P), P_ref)
+    assert_close("Q", host(Q), Q_ref)
+    _check_contract(x, T, P, Q, 7102)
+
+
+def test_transition_full_size(device):
+    """the T=8192, H=32, C=64 prefill workload: Q of every head, and P through the contract from the
+    workload's own initial state"""
+    import kda_gated_delta_core_amd as kda
+    w = ki.WORKLOADS["prefill_h32_t8192_c64"]
+    announce(f"kda_chunk_prefill_transition {w.name} seed={w.seed}")
+    x = ki.workload_inputs(w)
+    P, Q = _transition(kda, _padded(x, 0, w.T, w.chunk), w.T, w.chunk)
+    sl = lambda n: x[n][:, :w.T]
+    P_ref, Q_ref = oracle.transition(sl("q"), sl("k"), sl("v"), sl("gate"), sl("beta"))
+    assert_close("Q", host(Q), Q_ref)
+    assert float(np.abs(host(P) - P_ref).max()) <= 1e-6
+    _, s_ref, _, _ = oracle.serial(sl("q"), sl("k"), sl("v"), sl("gate"), sl("beta"), x["state"])
+    got = np.matmul(host(P).astype(np.float64), x["state"].astype(np.float64)) + host(Q)
+    assert_close("P S0 + Q", got, s_ref)
+
+
+def test_apply_matches_oracle(device):
+    import torch
+    import kda_gated_delta_core_amd as kda
+    B, H = 2, 5
+    announce(f"kda_state_transition_apply B={B} H={H}")
+    rng = np.random.default_rng(7200)
+    P = (rng.standard_normal((B, H, 128, 128)) / 8).astype(np.float32)
+    Q = rng.standard_normal((B, H, 128, 128)).astype(np.float32)
+    S = rng.standard_normal((B, H, 128, 128)).astype(np.float32)
+    Pd, Qd = dev(P), dev(Q)
+    Sd = dev(S)
+    kda.kda_state_transition_apply(Pd, Qd, Sd)
+    torch.cuda.synchronize()
+    assert_close("P S + Q", host(Sd), oracle.apply_transition(P, Q, S))
+    Sd = dev(S)
+    kda.kda_state_transition_apply(Pd, None, Sd)
+    torch.cuda.synchronize()
+    assert_close("P S", host(Sd), oracle.apply_transition(P, None, S))
+    assert np.array_equal(host(Pd), P) and np.array_equal(host(Qd), Q), "inputs were written"
+
+
+def test_segments_fold_to_the_whole_prefill(device):
+    """One sequence split at token boundaries that cut chunks: transitions per segment, folded in
+    order from the initial state, then every segment's prefill from its folded initial state gives
+    the whole sequence's outputs and final state."""
+    import torch
+    import kda_gated_delta_core_amd as kda
+    B, H, T, C = 2, 3, 300, 64
+    cuts = [0, 70, 200, 300]
+    announce(f"segment fold B={B} H={H} T={T} C={C} cuts={cuts}")
+    x = ki.make_batch(7300, B, H, T, -3.0, 0.05)
+    S = dev(x["state"])
+    outs, s_in = [], []
+    for t0, t1 in zip(cuts[:-1], cuts[1:]):
+        seg = _padded(x, t0, t1, C)
+        P, Q = _transition(kda, seg, t1 - t0, C)
+        s_in.append(S.clone())
+        kda.kda_state_transition_apply(P, Q, S)
+    folded_final = S
+    for (t0, t1), s0 in zip(zip(cuts[:-1], cuts[1:]), s_in):
+        seg = _padded(x, t0, t1, C)
+        st = s0.clone()
+        out = kda.kda_chunk_prefill(seg["q"], seg["k"], seg["v"], seg["gate"], seg["beta"], st, t1 - t0, C)
+        outs.append(host(out)[:, :t1 - t0])
+        last_state = st
+    torch.cuda.synchronize()
+    o_ref, s_ref, _, _ = oracle.serial(x["q"], x["k"], x["v"], x["gate"], x["beta"], x["state"])
+    assert_close("outputs", np.concatenate(outs, axis=1), o_ref)
+    assert_close("final state (last segment's prefill)", host(last_state), s_ref)
+    assert_close("final state (fold)", host(folded_final), s_ref)
+
+
+def test_transitions_compose(device):
+    """(P2 P1, P2 Q1 + Q2) from two segments equals the transition of their concatenation"""
+    import torch
+    import kda_gated_delta_core_amd as kda
+    B, H, C = 1, 2, 32
+    announce(f"transition composition B={B} H={H} C={C}")
+    x = ki.make_batch(7400, B, H, 150, -0.02, 0.02)
+    P1, Q1 = _transition(kda, _padded(x, 0, 61, C), 61, C)
+    P2, Q2 = _transition(kda, _padded(x, 61, 150, C), 89, C)
+    kda.kda_state_transition_apply(P2, None, P1)  # P1 <- P2 P1
+    kda.kda_state_transition_apply(P2, Q2, Q1)    # Q1 <- P2 Q1 + Q2
+    torch.cuda.synchronize()
+    P_ref, Q_ref = oracle.transition(x["q"], x["k"], x["v"], x["gate"], x["beta"])
+    assert_close("P2 P1", host(P1), P_ref)
+    assert_close("P2 Q1 + Q2", host(Q1), Q_ref)
