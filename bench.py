@@ -458,6 +458,14 @@ def bench_transition(torch, kda, ki, name, T, steps, warmup, timer):
     return w, timer.run(step, steps, warmup)
 
 
+def bench_transition_apply(torch, kda, B, H, steps, warmup, timer):
+    """kda_state_transition_apply on B x H states in place (P = I / 2, so repeated folds stay bounded)."""
+    P = (0.5 * torch.eye(D, device="cuda")).expand(B, H, D, D).contiguous()
+    Q = torch.randn((B, H, D, D), device="cuda")
+    S = torch.randn((B, H, D, D), device="cuda")
+    return timer.run(lambda i: kda.kda_state_transition_apply(P, Q, S), steps, warmup)
+
+
 def _sequence(ki, w, s, T, t_pad):
     import numpy as np
     arrays = {n: np.full((1, t_pad, w.heads, D), 0.0 if w.pad_value is None else w.pad_value, np.float32)
@@ -662,6 +670,14 @@ def main():
         workloads[name] = {"tokens_per_s": w.batch * T / r["s_per_step"], "ms_per_call": r["s_per_step"] * 1e3,
                            "call_ms": r["launch_avg_s"] * 1e3, "algorithmic_TFLOP_per_s": tf,
                            "mfma_frac": tf / MFMA_F32_PEAK_TFLOPS}
+    if want("transition_apply_b4_h32"):
+        # the fold step for 4 sequences x 32 heads: a device folds the pairs of the segments before its own
+        log("transition_apply_b4_h32")
+        r = bench_transition_apply(torch, kda, 4, 32, args.reps or 100, args.warmup, timer)
+        fl = 4 * 32 * 2.0 * D ** 3
+        workloads["transition_apply_b4_h32"] = {"us_per_call": r["s_per_step"] * 1e6,
+                                                "kernel_us": r["launch_avg_s"] * 1e6,
+                                                "algorithmic_TFLOP_per_s": fl / r["launch_avg_s"] / 1e12}
     for name in ki.VARLEN_WORKLOADS:
         if not want(name):
             continue

@@ -178,3 +178,44 @@ def test_graph_replays_of_the_prefill_chain(device):
     # norm's rows for them are zero too and the whole norm output is compared
     _capture_and_replay(kda, "prefill chain", work, reset,
                         lambda: (q[:, :T], k[:, :T], v[:, :T], cst, out[:, :T], st, y, vout, vst))
+
+
+def test_graph_replays_of_the_segment_split(device):
+    """Two segments' transitions, the fold of the first into the sequence's state, and the second
+    segment's prefill from the folded state, captured as one graph."""
+    import kda_gated_delta_core_amd as kda
+    B, H, C = 2, 3, 64
+    T1, T2 = 150, 90
+    announce(f"graph capture: segment transitions + fold + prefill B={B} H={H} T1={T1} T2={T2}")
+    x = ki.make_batch(1530, B, H, T1 + T2, -3.0, 0.05)
+
+    def seg(t0, t1):
+        t_pad = -(-(t1 - t0) // C) * C
+        res = {}
+        for n in ("q", "k", "v", "gate", "beta"):
+            a = x[n][:, t0:t1]
+            res[n] = torch.from_numpy(np.ascontiguousarray(
+                np.concatenate([a, np.zeros((B, t_pad - (t1 - t0)) + a.shape[2:], np.float32)], 1))).cuda()
+        return res
+
+    s1, s2 = seg(0, T1), seg(T1, T1 + T2)
+    st0 = torch.from_numpy(x["state"]).cuda()
+    st = torch.empty_like(st0)
+    P1, Q1, P2, Q2 = (torch.empty((B, H, 128, 128), device="cuda") for _ in range(4))
+    out2 = torch.zeros((B, s2["q"].shape[1], H, 128), device="cuda")
+    ws1 = torch.empty(kda.kda_chunk_prefill_workspace_bytes(B, H, T1, C), dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty(kda.kda_chunk_prefill_workspace_bytes(B, H, T2, C), dtype=torch.uint8, device="cuda")
+
+    def work(s):
+        kda.kda_chunk_prefill_transition(*(s1[n] for n in ("q", "k", "v", "gate", "beta")), T1, C, trans_p=P1,
+                                         trans_q=Q1, workspace=ws1, stream=s)
+        kda.kda_chunk_prefill_transition(*(s2[n] for n in ("q", "k", "v", "gate", "beta")), T2, C, trans_p=P2,
+                                         trans_q=Q2, workspace=ws2, stream=s)
+        kda.kda_state_transition_apply(P1, Q1, st, stream=s)
+        kda.kda_chunk_prefill(*(s2[n] for n in ("q", "k", "v", "gate", "beta")), st, T2, C, out=out2,
+                              workspace=ws2, stream=s)
+
+    def reset():
+        st.copy_(st0)
+
+    _capture_and_replay(kda, "segment split", work, reset, lambda: (P1, Q1, P2, Q2, st, out2[:, :T2]))

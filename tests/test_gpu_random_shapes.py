@@ -91,3 +91,33 @@ def test_random_varlen(device, lens, H, C, seed):
                                            x["state"][s:s + 1])
         assert_close(f"seq {s} out", got_o[None, a:b], o_ref)
         assert_close(f"seq {s} state", got_s[s:s + 1], s_ref)
+
+
+TRANSITION = _cases(8, lambda r: (int(r.integers(1, 3)), int(r.integers(1, 6)), int(r.integers(1, 300)),
+                                  int(r.choice([16, 32, 64])), float(r.uniform(-6.0, 0.0)),
+                                  int(r.integers(0, 10 ** 6))))
+
+
+@pytest.mark.parametrize("B,H,T,C,gate_lo,seed", TRANSITION)
+def test_random_transition(device, B, H, T, C, gate_lo, seed):
+    """the contract P S + Q against the recurrence from a random state, and Q; P itself only where it
+    stays inside the FP32 range (elsewhere within an absolute 1e-6)"""
+    import kda_gated_delta_core_amd as kda
+    announce(f"kda_chunk_prefill_transition B={B} H={H} T={T} C={C} gate_lo={gate_lo:.2f} seed={seed}")
+    t_pad = -(-T // C) * C
+    x = ki.make_batch(seed, B, H, T, gate_lo, 0.02, alloc_rows=t_pad, pad_value=float("nan"))
+    P = torch.full((B, H, 128, 128), SENTINEL, device="cuda")
+    Q = torch.full((B, H, 128, 128), SENTINEL, device="cuda")
+    kda.kda_chunk_prefill_transition(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["gate"]), dev(x["beta"]), T, C,
+                                     trans_p=P, trans_q=Q)
+    torch.cuda.synchronize()
+    sl = lambda a: np.ascontiguousarray(a[:, :T])
+    P_ref, Q_ref = oracle.transition(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["gate"]), sl(x["beta"]))
+    assert_close("Q", host(Q), Q_ref)
+    if float(np.abs(P_ref).max()) > 1e-3:
+        assert_close("P", host(P), P_ref)
+    else:
+        assert float(np.abs(host(P) - P_ref).max()) <= 1e-6
+    S = np.random.default_rng(seed + 1).standard_normal((B, H, 128, 128)).astype(np.float32)
+    _, s_ref, _, _ = oracle.serial(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["gate"]), sl(x["beta"]), S)
+    assert_close("P S + Q", np.matmul(host(P).astype(np.float64), S.astype(np.float64)) + host(Q), s_ref)
