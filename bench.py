@@ -436,8 +436,10 @@ def bench_prefill(torch, kda, ki, name, steps, warmup, timer):
     return w, r, extra
 
 
-def bench_transition(torch, kda, ki, name, T, steps, warmup, timer):
-    """kda_chunk_prefill_transition over the first T tokens of every sequence of workload `name`."""
+def bench_transition(torch, kda, ki, name, T, steps, warmup, timer, n_fold=-1):
+    """kda_chunk_prefill_transition over the first T tokens of every sequence of workload `name`.
+    n_fold >= 0: a device's whole share of a split sequence instead: its transition (records kept),
+    n_fold folds of earlier segments' pairs into the state, then kda_chunk_scan from the kept records."""
     w = ki.WORKLOADS[name]
     B, H, C = w.batch, w.heads, w.chunk
     t_pad = -(-T // C) * C
@@ -451,9 +453,16 @@ def bench_transition(torch, kda, ki, name, T, steps, warmup, timer):
     Q = torch.empty((B, H, D, D), device="cuda")
     ws = torch.empty(kda.kda_chunk_prefill_workspace_bytes(B, H, T, C), dtype=torch.uint8, device="cuda")
 
+    state = torch.zeros((B, H, D, D), device="cuda")
+    out = torch.empty((B, t_pad, H, D), device="cuda")
+
     def step(i):
         kda.kda_chunk_prefill_transition(tens["q"], tens["k"], tens["v"], tens["gate"], tens["beta"], T, C,
                                          trans_p=P, trans_q=Q, workspace=ws)
+        if n_fold >= 0:
+            for _ in range(n_fold):
+                kda.kda_state_transition_apply(P, Q, state)
+            kda.kda_chunk_scan(state, T, C, ws, out=out)
 
     return w, timer.run(step, steps, warmup)
 
@@ -670,6 +679,15 @@ def main():
         workloads[name] = {"tokens_per_s": w.batch * T / r["s_per_step"], "ms_per_call": r["s_per_step"] * 1e3,
                            "call_ms": r["launch_avg_s"] * 1e3, "algorithmic_TFLOP_per_s": tf,
                            "mfma_frac": tf / MFMA_F32_PEAK_TFLOPS}
+    if want("split_device_b4_h32_t4096_c64"):
+        # the last of 8 devices sharing the 4 x 32768 prefill by token segments, without the exchange
+        log("split_device_b4_h32_t4096_c64")
+        w, r = bench_transition(torch, kda, ki, "prefill_b4_h32_t32768_c64", 4096, args.reps or 10,
+                                0 if args.reps else 10, timer, n_fold=7)
+        workloads["split_device_b4_h32_t4096_c64"] = {
+            "ms_per_call": r["s_per_step"] * 1e3, "device_ms": r["launch_avg_s"] * 1e3,
+            "projected_8_device_tokens_per_s_without_exchange": 4 * 32768 / r["s_per_step"],
+            "steps": "transition (records kept) + 7 folds + kda_chunk_scan, one device's share; no exchange"}
     if want("transition_apply_b4_h32"):
         # the fold step for 4 sequences x 32 heads: a device folds the pairs of the segments before its own
         log("transition_apply_b4_h32")

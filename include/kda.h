@@ -90,8 +90,9 @@ const char* kda_status_string(int status);
  * when the arguments are invalid (batch/heads/T < 1, unsupported chunk, size
  * overflow).  The workspace holds, per (sequence, head, chunk), the chunk's
  * WY/UT intermediates written by the prepare kernel and read by the scan
- * kernel (kernel-table page, fields chunk_prepare / chunk_scan).  It is
- * scratch: contents on entry are ignored and undefined on exit.
+ * kernel (kernel-table page, fields chunk_prepare / chunk_scan).  Contents
+ * on entry are ignored.  On exit it holds the call's chunk records, from
+ * which kda_chunk_scan can run the scan again.
  */
 size_t kda_chunk_prefill_workspace_bytes(int batch, int heads, int T, int chunk);
 
@@ -166,7 +167,8 @@ int kda_chunk_prefill_varlen(const float* q, const float* k, const float* v, con
  * splitting one long sequence across devices by token segments.  Each device
  * computes its segment's (P, Q); the pairs are folded in segment order with
  * kda_state_transition_apply to give every segment its true initial state;
- * then each device runs kda_chunk_prefill on its segment from that state.
+ * then each device runs kda_chunk_scan on the records this call left in the
+ * workspace (or kda_chunk_prefill) from that state.
  *
  *   q, k, v, gate, beta : as kda_chunk_prefill (rows t >= T ignored)
  *   trans_p             : [batch][heads][128][128] out, P[i][j] over key indices
@@ -177,13 +179,38 @@ int kda_chunk_prefill_varlen(const float* q, const float* k, const float* v, con
  * P S + Q, up to FP32 rounding.  Q is the final state from S = 0; P is the
  * product over the tokens, later ones on the left, of
  * (I - beta k k^T) diag(exp(gate)), computed chunk by chunk from the identity.
- * Both are written whole.  No output rows are produced.  Refusals and accuracy
+ * Both are written whole.  No output rows are produced.  The workspace is left
+ * holding the chunk records, as after kda_chunk_prefill.  Refusals and accuracy
  * as kda_chunk_prefill, with trans_p and trans_q taking the place of state and
  * out in the overlap checks.
  */
 int kda_chunk_prefill_transition(const float* q, const float* k, const float* v, const float* gate,
                                  const float* beta, float* trans_p, float* trans_q, int batch, int heads, int T,
                                  int chunk, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The scan half of kda_chunk_prefill alone (kernel-table page, chunk_scan),
+ * from the chunk records a preceding kda_chunk_prefill or
+ * kda_chunk_prefill_transition with the same batch, heads, T and chunk left
+ * in the workspace.  It runs the prefill again from another initial state
+ * without recomputing the records.  After a segment's transition and the fold
+ * of the segments before it, this gives the segment's outputs from its true
+ * initial state.
+ *
+ *   state     : [batch][heads][128][128], in: initial state, out: state after token T-1
+ *   out       : [batch][T_pad][heads][128]; rows t < T written, as kda_chunk_prefill
+ *   workspace : the records, at least kda_chunk_prefill_workspace_bytes(batch,
+ *               heads, T, chunk) bytes; read only
+ *
+ * The result equals the bits of kda_chunk_prefill on the inputs the records
+ * were made from, started from `state`.  Records made with other sizes, or
+ * never made, give unspecified values; every access stays inside the
+ * workspace size checked here.  Refusals as kda_chunk_prefill (a null or
+ * short workspace is KDA_ERR_WORKSPACE; out, state and workspace must not
+ * overlap).
+ */
+int kda_chunk_scan(float* state, float* out, int batch, int heads, int T, int chunk, const void* workspace,
+                   size_t workspace_bytes, void* stream);
 
 /*
  * state <- trans_p state + trans_q for batch * heads states of 128 x 128 FP32,

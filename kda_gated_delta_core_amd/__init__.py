@@ -34,7 +34,7 @@ EXPORTED = ("kda_status_string", "kda_chunk_prefill_workspace_bytes", "kda_chunk
             "kda_recurrent_k", "kda_gated_rmsnorm", "kda_decode_front_end",
             "kda_chunk_prefill_varlen_workspace_bytes", "kda_chunk_prefill_varlen", "kda_recurrent_k_bf16",
             "kda_recurrent_step_bf16", "kda_decode_front_end_bf16", "kda_prefill_front_end",
-            "kda_prefill_front_end_varlen", "kda_chunk_prefill_transition", "kda_state_transition_apply")
+            "kda_prefill_front_end_varlen", "kda_chunk_prefill_transition", "kda_state_transition_apply", "kda_chunk_scan")
 GATED_RMSNORM_MIN_EPS = 1e-30
 
 _lib = None
@@ -89,6 +89,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_chunk_prefill_transition.restype = i
     lib.kda_state_transition_apply.argtypes = [p] * 3 + [i, i, p]
     lib.kda_state_transition_apply.restype = i
+    lib.kda_chunk_scan.argtypes = [p, p] + [i] * 4 + [p, sz, p]
+    lib.kda_chunk_scan.restype = i
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -298,6 +300,29 @@ def kda_chunk_prefill_transition(q, k, v, gate, beta, T: int, chunk: int, trans_
     if rc != KDA_OK:
         raise KdaError("kda_chunk_prefill_transition", rc)
     return trans_p, trans_q
+
+
+def kda_chunk_scan(state, T: int, chunk: int, workspace, out=None, stream=None):
+    """The scan half of kda_chunk_prefill alone, from the chunk records a preceding kda_chunk_prefill or
+    kda_chunk_prefill_transition with the same (B, H, T, chunk) left in ``workspace``.  state:
+    [B][H][128][128] (in place); out: [B][T_pad][H][128].  Returns ``out``."""
+    if not isinstance(state, torch.Tensor) or state.dim() != 4:
+        raise ValueError("state must be [batch][heads][128][128]")
+    if chunk not in (16, 32, 64):
+        raise KdaError("kda_chunk_scan", KDA_ERR_UNSUPPORTED)
+    B, H = state.shape[0], state.shape[1]
+    t_pad = -(-int(T) // chunk) * chunk
+    vs = (B, t_pad, H, HEAD_DIM)
+    if out is None:
+        out = torch.empty(vs, dtype=torch.float32, device=state.device)
+    if not (isinstance(workspace, torch.Tensor) and workspace.device.type == "cuda" and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor holding the chunk records")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rc = load_library().kda_chunk_scan(_check("state", state, (B, H, HEAD_DIM, HEAD_DIM)), _check("out", out, vs), B, H,
+                                       int(T), chunk, workspace.data_ptr(), ws_bytes, _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_chunk_scan", rc)
+    return out
 
 
 def kda_state_transition_apply(trans_p, trans_q, state, stream=None):

@@ -140,6 +140,29 @@ KDA_API int kda_chunk_prefill_transition(const float* q, const float* k, const f
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 
+KDA_API int kda_chunk_scan(float* state, float* out, int batch, int heads, int T, int chunk, const void* workspace,
+                           size_t workspace_bytes, void* stream)
+{
+    if (!state || !out) return KDA_ERR_INVALID_ARG;
+    if (!aligned({state, out, workspace})) return KDA_ERR_INVALID_ARG;
+    if (batch < 1 || heads < 1 || T < 1) return KDA_ERR_INVALID_ARG;
+    if (!chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
+    const int64_t need = prefill_ws_bytes(batch, heads, T, chunk);
+    const int64_t t_pad = ((int64_t)T + chunk - 1) / chunk * chunk;
+    const int64_t vec = mul({batch, t_pad, heads, KDA_HEAD_DIM});
+    const int64_t st = mul({batch, heads, KDA_HEAD_DIM, KDA_HEAD_DIM});
+    if (need < 0 || vec < 0 || st < 0 || t_pad > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)batch * heads > 0x7fffffffLL / 64) return KDA_ERR_INVALID_ARG;
+    if (heads > KDA_PREFILL_MAX_HEADS) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)batch * heads * (t_pad / chunk) > (1LL << 30)) return KDA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < (size_t)need) return KDA_ERR_WORKSPACE;
+    const Range r[] = {{out, vec * 4}, {state, st * 4}, {workspace, need}};
+    if (any_overlap(r, 3, 2)) return KDA_ERR_INVALID_ARG;
+    const int rc = kda::launch_chunk_scan(static_cast<const float*>(workspace), state, out, batch, heads, T,
+                                          (int)t_pad, chunk, static_cast<hipStream_t>(stream));
+    return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
 KDA_API int kda_state_transition_apply(const float* trans_p, const float* trans_q, float* state, int batch,
                                        int heads, void* stream)
 {

@@ -980,6 +980,30 @@ static int launch_scan(const float* ws, float* state, float* out, long long n_bh
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+static int compute_units()
+{
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+        return -1;
+    return n_cu;
+}
+
+// The scan with its column-group width: 32-column workgroups when 16-column
+// ones would not fit the compute units in one round and 32-column ones still
+// fill them (results are the same bits either way: value columns never mix).
+template <int C, class Layout, bool kTrans = false>
+static int launch_scan_auto(const float* ws, float* state, float* out, long long n_bh, int heads,
+                            const Layout& layout, int n_cu, hipStream_t stream)
+{
+    const long long slots = kTrans ? 2 : 1;  // the transition form runs P and Q groups
+    if constexpr (C == 64) {
+        if (n_bh * 8 * slots > n_cu && n_bh * 4 * slots >= n_cu)
+            return launch_scan<C, 2, Layout, kTrans>(ws, state, out, n_bh, heads, layout, stream);
+    }
+    return launch_scan<C, 1, Layout, kTrans>(ws, state, out, n_bh, heads, layout, stream);
+}
+
 // max_records bounds the layout's record count (exact for the dense layout).
 // kTrans: state is the Q output and out the P output of the transition form.
 template <int C, class Layout, bool kTrans = false>
@@ -988,25 +1012,15 @@ static int launch_chunk(const float* q, const float* k, const float* v, const fl
                         const Layout& layout, hipStream_t stream)
 {
     // one persistent prepare workgroup per compute unit (its LDS use allows one)
-    int dev = 0, n_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
-        return -1;
+    const int n_cu = compute_units();
+    if (n_cu < 1) return -1;
     const int grid_p = max_records < n_cu ? (int)max_records : n_cu;
     if (grid_p > 0) {
         hipLaunchKernelGGL((chunk_prepare_kernel<C, Layout>), dim3((unsigned)grid_p), dim3(kPrepThreads), 0, stream,
                            q, k, v, gate, beta, ws, heads, layout);
         if (hipGetLastError() != hipSuccess) return -1;
     }
-    // 32-column workgroups when 16-column ones would not fit the compute units
-    // in one round and 32-column ones still fill them (results are the same
-    // bits either way: value columns never mix)
-    const long long slots = kTrans ? 2 : 1;  // the transition form runs P and Q groups
-    if constexpr (C == 64) {
-        if (n_bh * 8 * slots > n_cu && n_bh * 4 * slots >= n_cu)
-            return launch_scan<C, 2, Layout, kTrans>(ws, state, out, n_bh, heads, layout, stream);
-    }
-    return launch_scan<C, 1, Layout, kTrans>(ws, state, out, n_bh, heads, layout, stream);
+    return launch_scan_auto<C, Layout, kTrans>(ws, state, out, n_bh, heads, layout, n_cu, stream);
 }
 
 template <int C, bool kTrans = false>
@@ -1029,6 +1043,30 @@ int launch_chunk_prefill(const float* q, const float* k, const float* v, const f
     case 16: return launch_dense<16>(q, k, v, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream);
     case 32: return launch_dense<32>(q, k, v, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream);
     case 64: return launch_dense<64>(q, k, v, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream);
+    default: return -1;
+    }
+}
+
+// The scan alone, from the records a dense prepare left in ws.
+template <int C>
+static int launch_dense_scan(const float* ws, float* state, float* out, int batch, int heads, int T, int t_pad,
+                             hipStream_t stream)
+{
+    const int nchunks = t_pad / C;
+    const long long n_bh = (long long)batch * heads;
+    const DenseLayout layout{heads, T, t_pad, nchunks, (int)(n_bh * nchunks)};
+    const int n_cu = compute_units();
+    if (n_cu < 1) return -1;
+    return launch_scan_auto<C, DenseLayout>(ws, state, out, n_bh, heads, layout, n_cu, stream);
+}
+
+int launch_chunk_scan(const float* workspace, float* state, float* out, int batch, int heads, int T, int t_pad,
+                      int chunk, hipStream_t stream)
+{
+    switch (chunk) {
+    case 16: return launch_dense_scan<16>(workspace, state, out, batch, heads, T, t_pad, stream);
+    case 32: return launch_dense_scan<32>(workspace, state, out, batch, heads, T, t_pad, stream);
+    case 64: return launch_dense_scan<64>(workspace, state, out, batch, heads, T, t_pad, stream);
     default: return -1;
     }
 }

@@ -38,6 +38,10 @@ int launch_chunk_prefill_transition(const float* q, const float* k, const float*
                                     const float* beta, float* trans_p, float* trans_q, int batch, int heads, int T,
                                     int t_pad, int chunk, float* workspace, hipStream_t stream);
 
+// the scan half of the dense prefill, from the records of a preceding prepare in workspace
+int launch_chunk_scan(const float* workspace, float* state, float* out, int batch, int heads, int T, int t_pad,
+                      int chunk, hipStream_t stream);
+
 // S <- P S + Q (Q may be null) for n states of 128 x 128, in place
 int launch_transition_apply(const float* P, const float* Q, float* S, int n, hipStream_t stream);
 

@@ -404,3 +404,27 @@ def test_transition_refusals(lib):
     assert g(P[0], P[1], P[1], 1, 2, None) == bad  # state is Q
     assert g(P[0], None, P[0], 1, 2, None) == bad  # state is P, Q absent
     assert g(P[0], P[1], P[2], 1 << 20, 1 << 12, None) == bad  # more states than one grid holds
+
+
+@no_gpu
+def test_chunk_scan_refusals(lib):
+    f = lib.kda_chunk_scan
+    bad = kda.KDA_ERR_INVALID_ARG
+    need = kda.kda_chunk_prefill_workspace_bytes(1, 2, 64, 16)
+    ok = (1, 2, 64, 16)
+    assert f(None, P[1], *ok, P[2], need, None) == bad
+    assert f(P[0], None, *ok, P[2], need, None) == bad
+    assert f(P[0], P[1], *ok, None, need, None) == kda.KDA_ERR_WORKSPACE
+    assert f(P[0], P[1], *ok, P[2], need - 1, None) == kda.KDA_ERR_WORKSPACE
+    for i in range(3):
+        p = [P[0], P[1], P[2]]
+        p[i] += 8
+        assert f(p[0], p[1], *ok, p[2], need, None) == bad, i
+    assert f(P[0], P[1], 0, 2, 64, 16, P[2], need, None) == bad
+    assert f(P[0], P[1], 1, 0, 64, 16, P[2], need, None) == bad
+    assert f(P[0], P[1], 1, 2, 0, 16, P[2], need, None) == bad
+    assert f(P[0], P[1], 1, 2, 64, 8, P[2], 1 << 30, None) == kda.KDA_ERR_UNSUPPORTED
+    assert f(P[0], P[1], 1, 16385, 64, 16, P[2], 1 << 40, None) == bad
+    assert f(P[0], P[0] + 256, *ok, P[2], need, None) == bad  # out over state
+    assert f(P[0], P[1], *ok, P[1] + 256, need, None) == bad  # workspace over out
+    assert f(P[0], P[1], *ok, P[0] + 256, need, None) == bad  # workspace over state

@@ -175,3 +175,61 @@ def test_transitions_compose(device):
     P_ref, Q_ref = oracle.transition(x["q"], x["k"], x["v"], x["gate"], x["beta"])
     assert_close("P2 P1", host(P1), P_ref)
     assert_close("P2 Q1 + Q2", host(Q1), Q_ref)
+
+
+def test_chunk_scan_reruns_the_prefill_bitwise(device):
+    """kda_chunk_scan from the records a kda_chunk_prefill left equals a second kda_chunk_prefill from
+    the same initial state bit for bit, and so do the records a transition leaves"""
+    import torch
+    import kda_gated_delta_core_amd as kda
+    B, H, T, C = 2, 3, 250, 64
+    announce(f"kda_chunk_scan B={B} H={H} T={T} C={C}")
+    x = ki.make_batch(7500, B, H, T, -4.0, 0.05)
+    seg = _padded(x, 0, T, C)
+    args = [seg[n] for n in ("q", "k", "v", "gate", "beta")]
+    ws = torch.empty(kda.kda_chunk_prefill_workspace_bytes(B, H, T, C), dtype=torch.uint8, device="cuda")
+    s_a = dev(x["state"])
+    out_a = kda.kda_chunk_prefill(*args, s_a, T, C, workspace=ws)
+    s_b = dev(x["state"])
+    out_b = torch.full_like(out_a, SENTINEL)
+    kda.kda_chunk_scan(s_b, T, C, ws, out=out_b)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a[:, :T], out_b[:, :T]) and torch.equal(s_a, s_b)
+    assert bool((out_b[:, T:] == SENTINEL).all()), "rows >= T were written"
+    kda.kda_chunk_prefill_transition(*args, T, C, workspace=ws)
+    s_c = dev(x["state"])
+    out_c = kda.kda_chunk_scan(s_c, T, C, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a[:, :T], out_c[:, :T]) and torch.equal(s_a, s_c)
+    o_ref, st_ref, _, _ = oracle.serial(x["q"], x["k"], x["v"], x["gate"], x["beta"], x["state"])
+    assert_close("out", host(out_c)[:, :T], o_ref)
+    assert_close("state", host(s_c), st_ref)
+
+
+def test_segments_from_kept_records(device):
+    """the split as a device runs it: transition (records kept), fold, then kda_chunk_scan from the
+    kept records and the folded state, per segment; equals the whole sequence's prefill"""
+    import torch
+    import kda_gated_delta_core_amd as kda
+    B, H, C = 2, 2, 32
+    cuts = [0, 45, 128, 200, 260]
+    announce(f"segments from kept records B={B} H={H} C={C} cuts={cuts}")
+    x = ki.make_batch(7600, B, H, cuts[-1], -2.0, 0.05)
+    segs, wss, trans = [], [], []
+    for t0, t1 in zip(cuts[:-1], cuts[1:]):
+        seg = _padded(x, t0, t1, C)
+        ws = torch.empty(kda.kda_chunk_prefill_workspace_bytes(B, H, t1 - t0, C), dtype=torch.uint8, device="cuda")
+        trans.append(kda.kda_chunk_prefill_transition(*(seg[n] for n in ("q", "k", "v", "gate", "beta")), t1 - t0, C,
+                                                      workspace=ws))
+        segs.append(seg)
+        wss.append(ws)
+    S = dev(x["state"])
+    outs = []
+    for (t0, t1), ws, (P, Q) in zip(zip(cuts[:-1], cuts[1:]), wss, trans):
+        s_in = S.clone()
+        outs.append(host(kda.kda_chunk_scan(s_in, t1 - t0, C, ws))[:, :t1 - t0])
+        kda.kda_state_transition_apply(P, Q, S)
+    torch.cuda.synchronize()
+    o_ref, s_ref, _, _ = oracle.serial(x["q"], x["k"], x["v"], x["gate"], x["beta"], x["state"])
+    assert_close("outputs", np.concatenate(outs, axis=1), o_ref)
+    assert_close("final state (fold)", host(S), s_ref)
