@@ -428,3 +428,31 @@ def test_chunk_scan_refusals(lib):
     assert f(P[0], P[0] + 256, *ok, P[2], need, None) == bad  # out over state
     assert f(P[0], P[1], *ok, P[1] + 256, need, None) == bad  # workspace over out
     assert f(P[0], P[1], *ok, P[0] + 256, need, None) == bad  # workspace over state
+
+
+def test_header_is_plain_c_and_links_from_c(tmp_path):
+    """include/kda.h compiles as C99 and C++ on its own, and a C program links against the library and
+    calls its host-only entry points (no GPU needed)."""
+    src = tmp_path / "use_kda.c"
+    src.write_text(
+        '#include "kda.h"\n#include <stdio.h>\n#include <string.h>\n'
+        "int main(void) {\n"
+        "  size_t ws = kda_chunk_prefill_workspace_bytes(1, 32, 8192, 64);\n"
+        '  if (ws != (size_t)1 * 32 * 128 * (5 * 64 * 128 + 128) * 4) { puts("bad size"); return 1; }\n'
+        "  if (kda_chunk_prefill_workspace_bytes(1, 32, 8192, 48) != 0) return 2;\n"
+        '  if (strstr(kda_status_string(KDA_ERR_WORKSPACE), "WORKSPACE") == NULL) return 3;\n'
+        "  if (kda_recurrent_step(0, 0, 0, 0, 0, 0, 0, 1, 1, 0) != KDA_ERR_INVALID_ARG) return 4;\n"
+        '  puts("ok");\n  return 0;\n}\n')
+    inc = os.path.join(ROOT, "include")
+    for std, comp in (("-std=c99", "gcc"), ("-std=c++17", "g++")):
+        r = subprocess.run([comp, std, "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-x",
+                            "c" if comp == "gcc" else "c++", "-I", inc, "-"], input='#include "kda.h"\n',
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+    exe = tmp_path / "use_kda"
+    libdir = os.path.dirname(kda.LIB_PATH)
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", inc, str(src), "-o", str(exe), "-L", libdir,
+                        "-l:" + os.path.basename(kda.LIB_PATH), "-Wl,-rpath," + libdir], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
