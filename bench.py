@@ -299,9 +299,10 @@ def bench_decode_chain(torch, kda, ki, reps):
     return us, nbytes
 
 
-def bench_prefill_chain(torch, kda, ki, steps, warmup, timer):
+def bench_prefill_chain(torch, kda, ki, steps, warmup, timer, fused=False):
     """The prefill of the block at T=8192 H=32 C=64: prefill front end -> kda_chunk_prefill -> gated RMSNorm
-    of the T rows, timed eagerly as one step."""
+    of the T rows, timed eagerly as one step.  fused: kda_chunk_prefill_fused (the front end inside the
+    prefill) -> gated RMSNorm."""
     B, T, H, K, C, fseed = ki.PREFILL_FRONT_END_WORKLOADS["prefill_front_end_t8192_h32_k4"]
     w = ki.WORKLOADS["prefill_h32_t8192_c64"]
     rows, nh, nseed = ki.NORM_WORKLOADS["gated_rmsnorm_t8192_h32"]
@@ -322,8 +323,11 @@ def bench_prefill_chain(torch, kda, ki, steps, warmup, timer):
     stream = torch.cuda.current_stream()
 
     def step(i):
-        kda.kda_prefill_front_end(qkv, cw, cst, H, C, ki.L2_EPS, q=q, k=k, v=v, stream=stream)
-        kda.kda_chunk_prefill(q, k, v, g, b, st, T, C, out=out, workspace=ws, stream=stream)
+        if fused:
+            kda.kda_chunk_prefill_fused(qkv, cw, cst, g, b, st, C, ki.L2_EPS, out=out, workspace=ws, stream=stream)
+        else:
+            kda.kda_prefill_front_end(qkv, cw, cst, H, C, ki.L2_EPS, q=q, k=k, v=v, stream=stream)
+            kda.kda_chunk_prefill(q, k, v, g, b, st, T, C, out=out, workspace=ws, stream=stream)
         kda.kda_gated_rmsnorm(out[0, :T], og, on, ki.NORM_EPS, out=y, stream=stream)
 
     return timer.run(step, steps, warmup), B * T
@@ -752,6 +756,13 @@ def main():
             "tokens_per_s": tokens / r["s_per_step"], "ms_per_call": r["s_per_step"] * 1e3,
             "device_ms": r["launch_avg_s"] * 1e3,
             "steps": "kda_prefill_front_end + kda_chunk_prefill + gated RMSNorm"}
+    if want("prefill_chain_fused_t8192_h32"):
+        log("prefill_chain_fused_t8192_h32")
+        r, tokens = bench_prefill_chain(torch, kda, ki, args.reps or 20, 0 if args.reps else 60, timer, fused=True)
+        workloads["prefill_chain_fused_t8192_h32"] = {
+            "tokens_per_s": tokens / r["s_per_step"], "ms_per_call": r["s_per_step"] * 1e3,
+            "device_ms": r["launch_avg_s"] * 1e3,
+            "steps": "kda_chunk_prefill_fused (front end inside the prepare) + gated RMSNorm"}
     for name in ki.NORM_WORKLOADS:
         if not want(name):
             continue

@@ -159,6 +159,30 @@ int kda_chunk_prefill_varlen(const float* q, const float* k, const float* v, con
                              int chunk, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kda_prefill_front_end followed by kda_chunk_prefill, fused: the front end
+ * (causal conv1d + SiLU, L2 on q and k; module page, pipeline line) runs
+ * inside the prefill's prepare kernel, which reads the BF16 projections
+ * instead of FP32 q, k, v rows, so those rows never travel through HBM
+ * (workspace page: q_f32 / k_f32 / v_f32 are not needed).
+ *
+ *   qkv        : [batch][T][3 * heads * 128] BF16, q | k | v per token (no padding)
+ *   conv_w     : [3 * heads * 128][conv_kernel] BF16
+ *   conv_state : [batch][3 * heads * 128][conv_kernel], read, then advanced by the T inputs
+ *   gate, beta, state, out, workspace : as kda_chunk_prefill
+ *   conv_kernel: 4 (others KDA_ERR_UNSUPPORTED; kda_prefill_front_end takes 1..4)
+ *   l2_eps     : as kda_prefill_front_end
+ *
+ * The result agrees with kda_prefill_front_end + kda_chunk_prefill within
+ * the stated tolerance, not bit for bit: the sum of squares of each q and k
+ * row is taken in another order.  The conv state ends as kda_prefill_front_end
+ * leaves it (bit for bit).  Refusals as the two calls, plus T * 3 * heads *
+ * 256 above 2^31 - 1 (KDA_ERR_INVALID_ARG).
+ */
+int kda_chunk_prefill_fused(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, const float* gate,
+                            const float* beta, float* state, float* out, int batch, int heads, int T, int chunk,
+                            int conv_kernel, float l2_eps, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Segment transition of a prefill: the final state of kda_chunk_prefill over
  * these T tokens as an affine function of its initial state (layer page,
  * Glm5NextKdaLayer::prefill; kernel-table page, chunk_scan, whose per-chunk

@@ -34,7 +34,8 @@ EXPORTED = ("kda_status_string", "kda_chunk_prefill_workspace_bytes", "kda_chunk
             "kda_recurrent_k", "kda_gated_rmsnorm", "kda_decode_front_end",
             "kda_chunk_prefill_varlen_workspace_bytes", "kda_chunk_prefill_varlen", "kda_recurrent_k_bf16",
             "kda_recurrent_step_bf16", "kda_decode_front_end_bf16", "kda_prefill_front_end",
-            "kda_prefill_front_end_varlen", "kda_chunk_prefill_transition", "kda_state_transition_apply", "kda_chunk_scan")
+            "kda_prefill_front_end_varlen", "kda_chunk_prefill_transition", "kda_state_transition_apply", "kda_chunk_scan",
+            "kda_chunk_prefill_fused")
 GATED_RMSNORM_MIN_EPS = 1e-30
 
 _lib = None
@@ -91,6 +92,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_state_transition_apply.restype = i
     lib.kda_chunk_scan.argtypes = [p, p] + [i] * 4 + [p, sz, p]
     lib.kda_chunk_scan.restype = i
+    lib.kda_chunk_prefill_fused.argtypes = [p] * 7 + [i] * 5 + [ctypes.c_float, p, sz, p]
+    lib.kda_chunk_prefill_fused.restype = i
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -450,6 +453,44 @@ def kda_prefill_front_end(qkv, conv_w, conv_state, heads: int, chunk: int, l2_ep
     if rc != KDA_OK:
         raise KdaError("kda_prefill_front_end", rc)
     return q, k, v
+
+
+def kda_chunk_prefill_fused(qkv, conv_w, conv_state, gate, beta, state, chunk: int, l2_eps: float, out=None,
+                            workspace=None, stream=None):
+    """kda_prefill_front_end + kda_chunk_prefill with the front end fused into the prefill.  Returns ``out``.
+
+    qkv: bfloat16 [B][T][3 H 128]; conv_w: bfloat16 [3 H 128][4]; conv_state: float32 [B][3 H 128][4]
+    (advanced in place); gate: [B][T_pad][H][128]; beta: [B][T_pad][H]; state: [B][H][128][128] (in place);
+    out: [B][T_pad][H][128]; workspace as kda_chunk_prefill.
+    """
+    if not isinstance(qkv, torch.Tensor) or qkv.dim() != 3:
+        raise ValueError("qkv must be [batch][T][3 * heads * 128]")
+    B, T, C = qkv.shape
+    if chunk not in (16, 32, 64):
+        raise KdaError("kda_chunk_prefill_fused", KDA_ERR_UNSUPPORTED)
+    Bg, t_pad, H = _vec_shapes(gate)
+    if Bg != B or C != 3 * H * HEAD_DIM or t_pad != -(-int(T) // chunk) * chunk:
+        raise ValueError("qkv [B][T][3 H 128] and gate [B][T_pad][H][128] do not agree")
+    if conv_w.dim() != 2:
+        raise ValueError("conv_w must be [conv_dim][conv_kernel]")
+    K = conv_w.shape[1]
+    vs = (B, t_pad, H, HEAD_DIM)
+    if out is None:
+        out = torch.empty(vs, dtype=torch.float32, device=qkv.device)
+    need = kda_chunk_prefill_workspace_bytes(B, H, int(T), chunk)
+    if workspace is None:
+        workspace = _workspace(need, qkv.device, stream)
+    if not (workspace.device.type == "cuda" and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    args = [_check("qkv", qkv, (B, T, C), torch.bfloat16), _check("conv_w", conv_w, (C, K), torch.bfloat16),
+            _check("conv_state", conv_state, (B, C, K)), _check("gate", gate, vs), _check("beta", beta, (B, t_pad, H)),
+            _check("state", state, (B, H, HEAD_DIM, HEAD_DIM)), _check("out", out, vs)]
+    rc = load_library().kda_chunk_prefill_fused(*args, B, H, int(T), chunk, K, float(l2_eps), workspace.data_ptr(),
+                                                ws_bytes, _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_chunk_prefill_fused", rc)
+    return out
 
 
 def kda_prefill_front_end_varlen(qkv, conv_w, conv_state, cu_seqlens, heads: int, l2_eps: float, q=None, k=None,

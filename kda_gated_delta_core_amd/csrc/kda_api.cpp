@@ -389,6 +389,42 @@ KDA_API int kda_prefill_front_end(const uint16_t* qkv, const uint16_t* conv_w, f
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 
+KDA_API int kda_chunk_prefill_fused(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, const float* gate,
+                                    const float* beta, float* state, float* out, int batch, int heads, int T, int chunk,
+                                    int conv_kernel, float l2_eps, void* workspace, size_t workspace_bytes,
+                                    void* stream)
+{
+    if (!qkv || !conv_w || !conv_state || !gate || !beta || !state || !out) return KDA_ERR_INVALID_ARG;
+    if (!aligned({qkv, conv_w, conv_state, gate, state, out, workspace}) || !aligned({beta}, 4))
+        return KDA_ERR_INVALID_ARG;
+    if (batch < 1 || heads < 1 || T < 1 || heads > KDA_PREFILL_MAX_HEADS) return KDA_ERR_INVALID_ARG;
+    if (conv_kernel < 1) return KDA_ERR_INVALID_ARG;
+    if (!(isfinite(l2_eps) && l2_eps >= KDA_GATED_RMSNORM_MIN_EPS)) return KDA_ERR_INVALID_ARG;
+    if (!chunk_ok(chunk) || conv_kernel != 4) return KDA_ERR_UNSUPPORTED;
+    const int64_t need = prefill_ws_bytes(batch, heads, T, chunk);
+    const int64_t t_pad = ((int64_t)T + chunk - 1) / chunk * chunk;
+    const int64_t C = 3 * (int64_t)heads * KDA_HEAD_DIM;
+    const int64_t x = mul({batch, T, C});
+    const int64_t w = mul({C, conv_kernel});
+    const int64_t cs = mul({batch, C, conv_kernel});
+    const int64_t vec = mul({batch, t_pad, heads, KDA_HEAD_DIM});
+    const int64_t sca = mul({batch, t_pad, heads});
+    const int64_t st = mul({batch, heads, KDA_HEAD_DIM, KDA_HEAD_DIM});
+    if (need < 0 || x < 0 || w < 0 || cs < 0 || vec < 0 || sca < 0 || st < 0 || t_pad > 0x7fffffffLL)
+        return KDA_ERR_INVALID_ARG;
+    if (mul({T, C, 2}) > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;  // 32-bit byte offsets inside one sequence
+    if ((int64_t)batch * heads > 0x7fffffffLL / 64 || mul({batch, C}) > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)batch * heads * (t_pad / chunk) > (1LL << 30)) return KDA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < (size_t)need) return KDA_ERR_WORKSPACE;
+    const Range r[] = {{out, vec * 4},  {state, st * 4}, {conv_state, cs * 4}, {workspace, need},
+                       {qkv, x * 2},    {conv_w, w * 2}, {gate, vec * 4},      {beta, sca * 4}};
+    if (any_overlap(r, 8, 4)) return KDA_ERR_INVALID_ARG;
+    const int rc = kda::launch_chunk_prefill_fused(qkv, conv_w, conv_state, gate, beta, state, out, batch, heads, T,
+                                                   (int)t_pad, chunk, l2_eps, static_cast<float*>(workspace),
+                                                   static_cast<hipStream_t>(stream));
+    return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
 KDA_API int kda_prefill_front_end_varlen(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q,
                                          float* k, float* v, const int* cu_seqlens, int n_seqs, int heads,
                                          int total_tokens, int conv_kernel, float l2_eps, void* stream)

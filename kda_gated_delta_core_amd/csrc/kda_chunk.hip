@@ -54,6 +54,7 @@
 // at the last row of block R).  Pad rows (t >= T) are replaced by zeros with
 // selects before any arithmetic, so NaN or inf there never reaches a result.
 #include "kda_common.h"
+#include "kda_front_end.h"
 #include "kda_internal.h"
 
 namespace kda {
@@ -90,6 +91,7 @@ struct ChunkPos {
     int nvalid;
     int span;
     int rec;
+    int b, t0, h;  // sequence, first token, head (dense layout; used by the fused front end)
 };
 // One (sequence, head) of the scan: its first token, its length, its chunks
 // and the index of its first record.
@@ -119,6 +121,9 @@ struct DenseLayout {
         p.nvalid = T - c * C < C ? T - c * C : C;
         p.span = C * heads;
         p.rec = (b * heads + h) * nchunks + c;
+        p.b = b;
+        p.t0 = c * C;
+        p.h = h;
         return p;
     }
     __device__ SeqPos seq(int bh) const
@@ -157,6 +162,9 @@ struct VarlenLayout {
         const long long left = (long long)(total - tok) * heads - h;
         p.span = left < C * heads ? (int)left : C * heads;
         p.rec = cb[lo] * heads + h * ns + c;
+        p.b = lo;
+        p.t0 = c * C;
+        p.h = h;
         return p;
     }
     __device__ SeqPos seq(int bh) const
@@ -248,7 +256,9 @@ __device__ __forceinline__ void prep_load_v(float (&vb)[C / 16][4], rsrc_t src, 
 
 // Rows >= T (nvalid and beyond) are replaced by zeros with selects, then the
 // chunk goes to LDS (gate in log2 units).
-template <int C>
+// kFE: k and q are in the fused row order (rows NV4 (tid / 32) + i), the gate
+// in the usual one.
+template <int C, bool kFE = false>
 __device__ __forceinline__ void prep_stage(const PrepInputs<C>& in, float* sK, float* sQ, float* sL, float* sBeta,
                                            int nvalid, int tid)
 {
@@ -259,8 +269,10 @@ __device__ __forceinline__ void prep_stage(const PrepInputs<C>& in, float* sK, f
     for (int i = 0; i < NV4; ++i) {
         const int e = tid + kPrepThreads * i, r = e >> 5, c4 = (e & 31) * 4;
         const bool ok = r < nvalid;
-        lds4_st(&sK[r * LD + c4], ok ? in.k[i] : z4);
-        lds4_st(&sQ[r * LD + c4], ok ? in.q[i] : z4);
+        const int rq = kFE ? NV4 * (tid >> 5) + i : r;
+        const bool okq = rq < nvalid;
+        lds4_st(&sK[rq * LD + c4], okq ? in.k[i] : z4);
+        lds4_st(&sQ[rq * LD + c4], okq ? in.q[i] : z4);
         const float4 g = ok ? in.g[i] : z4;
         lds4_st(&sL[r * LD + c4], make_float4(g.x * kLog2e, g.y * kLog2e, g.z * kLog2e, g.w * kLog2e));
     }
@@ -357,16 +369,212 @@ __device__ __forceinline__ void rec_st4(float* p, float4 v)
     __builtin_nontemporal_store(floatx4{v.x, v.y, v.z, v.w}, reinterpret_cast<floatx4*>(p));
 }
 
+// ---------------------------------------------------------------------------
+// Front end fused into the prepare (dense layout, conv_kernel 4).  Instead of
+// FP32 q, k, v rows the prepare reads the BF16 projections q | k | v
+// [B][T][3][H][128] (workspace page, qkv_proj), and computes for every staged
+// row the front end of the module page's pipeline line: the depthwise causal
+// conv over the token and the three before it (conv weights [3 H 128][4]
+// BF16, slot 3 the newest; tokens before the call from the conv state
+// [B][3 H 128][4] FP32), SiLU, and for q and k the scale 1 / sqrt(sum y^2 +
+// l2_eps) over the head's 128 channels.  q and k are formed in the staging
+// layout (32 lanes of a wave hold one row, 4 channels each; the sum of
+// squares is FP64, reduced over those 32 lanes), v directly in the B-operand
+// layout of the U tiles.  The conv state itself is advanced by a separate
+// launch after the whole prefill.
+struct FeSrc {
+    const unsigned short* qkv;     // [B][T][3][H][128] BF16
+    const unsigned short* conv_w;  // [3 H 128][4] BF16
+    const float* conv_state;       // [B][3 H 128][4] FP32, read only here
+    int T;                         // tokens per sequence in qkv
+    double eps;                    // l2_eps
+};
+constexpr int kFeK = 4;  // conv taps of the fused form
+
+__device__ __forceinline__ uint2 buf_ld_b64(rsrc_t r, int voff, int soff)
+{
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint4 buf_ld_b128u(rsrc_t r, int voff, int soff)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ float fe_bf16(unsigned w, int half) { return bf16_to_f32(half ? (w >> 16) : (w & 0xffffu)); }
+__device__ __forceinline__ float fe_silu(float a)
+{
+    return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504f * a));
+}
+
+// The raw inputs of q or k for the rows one thread stages in the fused form:
+// NV4 consecutive rows NV4 (tid / 32) + i of the chunk (not the rows tid / 32
+// + 16 i of the unfused staging), so that one window of NV4 + kFeK - 1 input
+// rows, channels 4 (tid % 32) + 0..3, feeds all their taps; the conv state of
+// those channels (for the first chunk of a sequence, else not read) and their
+// weights.
+template <int C>
+struct FeRaw {
+    static constexpr int NW = PrepInputs<C>::NV4 + kFeK - 1;  // window rows
+    uint2 x[NW];
+    float4 st[4];
+    uint4 w[2];
+};
+
+// live false: descriptors of zero bytes (loads return zeros, touch nothing)
+template <int C>
+__device__ __forceinline__ void fe_load_qk(FeRaw<C>& r, const FeSrc& fe, int part, const ChunkPos& p, int heads,
+                                           int tid, bool live)
+{
+    const int rowbytes = 3 * heads * kD * 2;
+    const int col = 4 * (tid & 31);
+    const int ch = (part * heads + p.h) * kD + col;  // first channel of the four
+    const rsrc_t src = make_rsrc(fe.qkv + (size_t)p.b * fe.T * 3 * heads * kD, live ? (uint32_t)fe.T * rowbytes : 0u);
+#pragma unroll
+    for (int m = 0; m < FeRaw<C>::NW; ++m) {
+        // rows before the call (t < 0) wrap to offsets at or above 2^31 and rows at or past T
+        // reach the size: both read zeros
+        const int t = p.t0 + PrepInputs<C>::NV4 * (tid >> 5) - (kFeK - 1) + m;
+        r.x[m] = buf_ld_b64(src, (int)((uint32_t)t * (uint32_t)rowbytes + (uint32_t)(ch * 2)), 0);
+    }
+    // descriptors over the head's 128 channels (wave-uniform), the lane's channels as offsets
+    const int ch0 = (part * heads + p.h) * kD;
+    const rsrc_t ss = make_rsrc(fe.conv_state + ((size_t)p.b * 3 * heads * kD + ch0) * kFeK,
+                                live && p.t0 == 0 ? (uint32_t)kD * kFeK * 4u : 0u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.st[j] = buf_ld4(ss, (col + j) * kFeK * 4, 0);
+    const rsrc_t ws = make_rsrc(fe.conv_w + (size_t)ch0 * kFeK, live ? (uint32_t)kD * kFeK * 2u : 0u);
+    r.w[0] = buf_ld_b128u(ws, col * kFeK * 2, 0);
+    r.w[1] = buf_ld_b128u(ws, col * kFeK * 2, 16);
+}
+
+// Sum over the 32 lanes of each half of a wave, returned to every lane of
+// that half: quads, eights, rows of 16 (DPP), then row 0 into row 1 and row 2
+// into row 3 through the row broadcast of lane 15.
+__device__ __forceinline__ double half_wave_sum_f64(double x, int lane)
+{
+    x += dpp_f64<0xB1>(x);        // quad_perm [1, 0, 3, 2]
+    x += dpp_f64<0x4E>(x);        // quad_perm [2, 3, 0, 1]
+    x += dpp_f64<0x141>(x);       // row_half_mirror
+    x += dpp_f64<0x140>(x);       // row_mirror
+    x += dpp_f64<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+    const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+    const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, 31);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), 31);
+    const unsigned lo2 = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, 63);
+    const unsigned hi2 = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), 63);
+    const unsigned a = lane < 32 ? lo : lo2, b = lane < 32 ? hi : hi2;
+    return __longlong_as_double((long long)(((unsigned long long)b << 32) | a));
+}
+
+// conv, SiLU and (l2) the per-row scale for the rows of FeRaw, to the float4
+// pieces prep_stage takes (in the fused row order)
+template <int C>
+__device__ __forceinline__ void fe_finish_qk(const FeRaw<C>& r, float4 (&out)[PrepInputs<C>::NV4], int t0, int tid,
+                                             bool l2, double eps)
+{
+    const int lane = tid & 63;
+#pragma unroll
+    for (int i = 0; i < PrepInputs<C>::NV4; ++i) {
+        float y[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const unsigned wj0 = j < 2 ? (j == 0 ? r.w[0].x : r.w[0].z) : (j == 2 ? r.w[1].x : r.w[1].z);
+            const unsigned wj1 = j < 2 ? (j == 0 ? r.w[0].y : r.w[0].w) : (j == 2 ? r.w[1].y : r.w[1].w);
+            float a = 0.f;
+#pragma unroll
+            for (int k = 0; k < kFeK; ++k) {
+                const int t = t0 + PrepInputs<C>::NV4 * (tid >> 5) + i - (kFeK - 1) + k;
+                float x = fe_bf16(j < 2 ? r.x[i + k].x : r.x[i + k].y, j & 1);
+                // rows that can precede the call (compile time), in a sequence's first chunk only
+                // (t0 == 0 is wave-uniform: the other chunks skip this with a scalar branch): state slot 4 + t
+                if (i + k + 1 < kFeK && t0 == 0) {
+                    const float sv = t == -3 ? r.st[j].y : (t == -2 ? r.st[j].z : r.st[j].w);
+                    x = t < 0 ? sv : x;
+                }
+                const float w = fe_bf16(k < 2 ? wj0 : wj1, k & 1);
+                a = k == 0 ? w * x : fmaf(w, x, a);
+            }
+            y[j] = fe_silu(a);
+        }
+        if (l2) {
+            const double ss = (double)y[0] * y[0] + (double)y[1] * y[1] + (double)y[2] * y[2] + (double)y[3] * y[3];
+            const double x = half_wave_sum_f64(ss, lane) + eps;
+            double rs = __builtin_amdgcn_rsq(x);
+            rs = rs * (1.5 - 0.5 * (x * rs) * rs);  // one Newton step
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] = (float)(y[j] * rs);
+        }
+        out[i] = make_float4(y[0], y[1], y[2], y[3]);
+    }
+}
+
+// v of the current chunk in the B-operand layout of this wave's U tiles
+// (rows 16 y + 4 q4 + e, channel 16 wave + l16): the seven input rows
+// 16 y + 4 q4 - 3 .. 16 y + 4 q4 + 3 per row block, the channel's conv state
+// (first chunk only) and weights
+template <int C>
+struct FeV {
+    unsigned short x[C / 16][7];
+    float4 st;
+    uint2 w;
+};
+template <int C>
+__device__ __forceinline__ void fe_load_v(FeV<C>& r, const FeSrc& fe, const ChunkPos& p, int heads, int wave, int l16,
+                                          int q4)
+{
+    const int rowbytes = 3 * heads * kD * 2;
+    const int ch = (2 * heads + p.h) * kD + 16 * wave + l16;
+    const rsrc_t src = make_rsrc(fe.qkv + (size_t)p.b * fe.T * 3 * heads * kD, (uint32_t)fe.T * rowbytes);
+#pragma unroll
+    for (int y = 0; y < C / 16; ++y)
+#pragma unroll
+        for (int j = 0; j < 7; ++j) {
+            const int t = p.t0 + 16 * y + 4 * q4 - 3 + j;  // out of range as in fe_load_qk
+            r.x[y][j] = __builtin_amdgcn_raw_buffer_load_b16(
+                src, (int)((uint32_t)t * (uint32_t)rowbytes + (uint32_t)(ch * 2)), 0, 0);
+        }
+    // descriptors over the head's v channels (wave-uniform), the lane's channel as the offset
+    const int ch0 = (2 * heads + p.h) * kD, cl = 16 * wave + l16;
+    r.st = buf_ld4(make_rsrc(fe.conv_state + ((size_t)p.b * 3 * heads * kD + ch0) * kFeK,
+                             p.t0 == 0 ? (uint32_t)kD * kFeK * 4u : 0u), cl * kFeK * 4, 0);
+    r.w = buf_ld_b64(make_rsrc(fe.conv_w + (size_t)ch0 * kFeK, (uint32_t)kD * kFeK * 2u), cl * kFeK * 2, 0);
+}
+template <int C>
+__device__ __forceinline__ void fe_finish_v(const FeV<C>& r, float (&vb)[C / 16][4], int t0, int q4)
+{
+#pragma unroll
+    for (int y = 0; y < C / 16; ++y)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float a = 0.f;
+#pragma unroll
+            for (int k = 0; k < kFeK; ++k) {
+                const int t = t0 + 16 * y + 4 * q4 + e - (kFeK - 1) + k;
+                float x = bf16_to_f32(r.x[y][e + k]);
+                if (y == 0 && e + k < kFeK - 1 && t0 == 0) {  // rows that can precede the call, as in fe_finish_qk
+                    const float sv = t == -3 ? r.st.y : (t == -2 ? r.st.z : r.st.w);
+                    x = t < 0 ? sv : x;
+                }
+                const float w = fe_bf16(k < 2 ? r.w.x : r.w.y, k & 1);
+                a = k == 0 ? w * x : fmaf(w, x, a);
+            }
+            vb[y][e] = fe_silu(a);
+        }
+}
+
 // Persistent: one workgroup per CU walks the records gc = blockIdx.x, +gridDim.x,
 // ... of the layout's processing order (the layout gives each one's inputs and
 // its place in the workspace).  The inputs of the next chunk are read into
 // registers while the current one is computed and are staged into LDS at its
 // end.
-template <int C, class Layout>
+//
+// kFE: the front end is fused in (dense layout): q, k and v are formed from
+// the BF16 projections in `fe` (see FeSrc) instead of read as FP32 rows; the
+// q, k, v pointers are then not read.
+template <int C, class Layout, bool kFE = false>
 __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ gate, const float* __restrict__ beta, float* __restrict__ ws, int heads,
-    Layout layout)
+    Layout layout, FeSrc fe)
 {
     using G = ChunkGeom<C>;
     constexpr int NT = G::kTiles, LD = G::kLd, LDC = G::kLdc;
@@ -400,11 +608,19 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
     if (gc < n_total) {
         pos = layout.template chunk<C>(gc);
         const PrepSrc src = prep_src(q, k, v, gate, beta, pos);
-        prep_load_part<C>(in.k, src.k, heads, threadIdx.x);
-        prep_load_part<C>(in.q, src.q, heads, threadIdx.x);
+        if constexpr (kFE) {
+            FeRaw<C> rk, rq;
+            fe_load_qk<C>(rk, fe, 1, pos, heads, threadIdx.x, true);
+            fe_load_qk<C>(rq, fe, 0, pos, heads, threadIdx.x, true);
+            fe_finish_qk<C>(rk, in.k, pos.t0, threadIdx.x, true, fe.eps);
+            fe_finish_qk<C>(rq, in.q, pos.t0, threadIdx.x, true, fe.eps);
+        } else {
+            prep_load_part<C>(in.k, src.k, heads, threadIdx.x);
+            prep_load_part<C>(in.q, src.q, heads, threadIdx.x);
+        }
         prep_load_part<C>(in.g, src.g, heads, threadIdx.x);
         in.beta = prep_load_beta<C>(src.b, heads, threadIdx.x);
-        prep_stage<C>(in, sKr, sQr, sKc, sBeta, pos.nvalid, threadIdx.x);
+        prep_stage<C, kFE>(in, sKr, sQr, sKc, sBeta, pos.nvalid, threadIdx.x);
     }
     __syncthreads();
 
@@ -419,7 +635,9 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         float* const rec = ws + (size_t)pos.rec * G::kRecord;
         float vb[NT][4];  // needed only at step 4c: its latency hides behind steps 2-4
-        prep_load_v<C>(vb, prep_src(q, k, v, gate, beta, pos).v, heads, wave, l16, q4);
+        FeV<C> fv;        // (fused front end: the raw v inputs instead)
+        if constexpr (kFE) fe_load_v<C>(fv, fe, pos, heads, wave, l16, q4);
+        else prep_load_v<C>(vb, prep_src(q, k, v, gate, beta, pos).v, heads, wave, l16, q4);
         const int nvalid = pos.nvalid;
         // The next chunk's inputs are read in three parts, at steps 3, 5 and 6,
         // so the vector-memory path takes them while the matrix cores work.
@@ -488,7 +706,9 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         //     it, (I + A_RR)^-1 by forward substitution (one lane per column),
         //     while waves 0..3 are still on the pairs below the diagonal.
         __builtin_amdgcn_sched_barrier(0);
-        prep_load_part<C>(in.k, nsrc.k, heads, tid);
+        FeRaw<C> rk, rq;  // (fused front end: the next chunk's raw k and q)
+        if constexpr (kFE) fe_load_qk<C>(rk, fe, 1, npos, heads, tid, gn < n_total);
+        else prep_load_part<C>(in.k, nsrc.k, heads, tid);
         __builtin_amdgcn_sched_barrier(0);
         int R, S;
         if (wave >= 4) {
@@ -567,6 +787,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         //     column block: beta e^G o K and beta V at rows 16 y + 4 q4 + e, and
         //     e^G o Q at the same positions (the accumulator layout of the P tiles)
         float bw[NT][4], bu[NT][4], qh[NT][4];
+        if constexpr (kFE) fe_finish_v<C>(fv, vb, pos.t0, q4);
 #pragma unroll
         for (int y = 0; y < NT; ++y)
 #pragma unroll
@@ -589,7 +810,8 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         static_assert(C * LD >= NW * 256, "transpose scratch");
         float* const xpose = sKc + wave * 256;
         __builtin_amdgcn_sched_barrier(0);
-        prep_load_part<C>(in.q, nsrc.q, heads, tid);
+        if constexpr (kFE) fe_load_qk<C>(rq, fe, 0, npos, heads, tid, gn < n_total);
+        else prep_load_part<C>(in.q, nsrc.q, heads, tid);
         __builtin_amdgcn_sched_barrier(0);
         floatx4 wt[NT], ut[NT];
 #pragma unroll
@@ -629,6 +851,12 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         prep_load_part<C>(in.g, nsrc.g, heads, tid);
         in.beta = prep_load_beta<C>(nsrc.b, heads, tid);
         __builtin_amdgcn_sched_barrier(0);
+        // (fused front end) the next chunk's k and q from their raw inputs, which arrived during
+        // steps 3-5; independent of this step's products, so the VALU work can fill the MFMA gaps
+        if constexpr (kFE) {
+            fe_finish_qk<C>(rk, in.k, npos.t0, tid, true, fe.eps);
+            fe_finish_qk<C>(rq, in.q, npos.t0, tid, true, fe.eps);
+        }
         //    Row blocks X and NT - 1 - X go together (equal work, 4 (NT + 1) MFMAs
         //    each way), so four independent accumulation chains keep the matrix
         //    core busy instead of two; each block's sum runs in the same order.
@@ -665,7 +893,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         __syncthreads();
         // stage the next chunk (loaded during this one; after the last chunk the
         // staged copy is unused)
-        prep_stage<C>(in, sKr, sQr, sKc, sBeta, npos.nvalid, tid);
+        prep_stage<C, kFE>(in, sKr, sQr, sKc, sBeta, npos.nvalid, tid);
         pos = npos;
         __syncthreads();
     }
@@ -1017,7 +1245,7 @@ static int launch_chunk(const float* q, const float* k, const float* v, const fl
     const int grid_p = max_records < n_cu ? (int)max_records : n_cu;
     if (grid_p > 0) {
         hipLaunchKernelGGL((chunk_prepare_kernel<C, Layout>), dim3((unsigned)grid_p), dim3(kPrepThreads), 0, stream,
-                           q, k, v, gate, beta, ws, heads, layout);
+                           q, k, v, gate, beta, ws, heads, layout, FeSrc{});
         if (hipGetLastError() != hipSuccess) return -1;
     }
     return launch_scan_auto<C, Layout, kTrans>(ws, state, out, n_bh, heads, layout, n_cu, stream);
@@ -1069,6 +1297,43 @@ int launch_chunk_scan(const float* workspace, float* state, float* out, int batc
     case 64: return launch_dense_scan<64>(workspace, state, out, batch, heads, T, t_pad, stream);
     default: return -1;
     }
+}
+
+// The prefill with the front end fused into the prepare (dense layout)
+template <int C>
+static int launch_dense_fused(const FeSrc& fe, const float* gate, const float* beta, float* state, float* out,
+                              int batch, int heads, int T, int t_pad, float* ws, hipStream_t stream)
+{
+    const int nchunks = t_pad / C;
+    const long long n_bh = (long long)batch * heads;
+    const DenseLayout layout{heads, T, t_pad, nchunks, (int)(n_bh * nchunks)};
+    const int n_cu = compute_units();
+    if (n_cu < 1) return -1;
+    const long long records = n_bh * nchunks;
+    const int grid_p = records < n_cu ? (int)records : n_cu;
+    // q, k, v are not read in this form: the gate pointer stands in for them
+    hipLaunchKernelGGL((chunk_prepare_kernel<C, DenseLayout, true>), dim3((unsigned)grid_p), dim3(kPrepThreads), 0,
+                       stream, gate, gate, gate, gate, beta, ws, heads, layout, fe);
+    if (hipGetLastError() != hipSuccess) return -1;
+    return launch_scan_auto<C, DenseLayout>(ws, state, out, n_bh, heads, layout, n_cu, stream);
+}
+
+int launch_chunk_prefill_fused(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, const float* gate,
+                               const float* beta, float* state, float* out, int batch, int heads, int T, int t_pad,
+                               int chunk, float l2_eps, float* workspace, hipStream_t stream)
+{
+    const FeSrc fe{reinterpret_cast<const unsigned short*>(qkv), reinterpret_cast<const unsigned short*>(conv_w),
+                   conv_state, T, (double)l2_eps};
+    int rc = -1;
+    switch (chunk) {
+    case 16: rc = launch_dense_fused<16>(fe, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream); break;
+    case 32: rc = launch_dense_fused<32>(fe, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream); break;
+    case 64: rc = launch_dense_fused<64>(fe, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream); break;
+    default: return -1;
+    }
+    if (rc != 0) return rc;
+    // every prepare workgroup has read the conv state by now (stream order)
+    return launch_conv_state_advance(qkv, conv_state, batch, heads, T, kFeK, stream);
 }
 
 int launch_chunk_prefill_transition(const float* q, const float* k, const float* v, const float* gate,

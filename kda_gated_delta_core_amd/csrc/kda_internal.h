@@ -33,6 +33,17 @@ int launch_chunk_prefill(const float* q, const float* k, const float* v, const f
                          float* state, float* out, int batch, int heads, int T, int t_pad, int chunk,
                          float* workspace, hipStream_t stream);
 
+// the prefill with the front end fused into the prepare (conv_kernel 4): qkv BF16 [B][T][3][H][128],
+// conv_w BF16 [3 H 128][4], conv state [B][3 H 128][4] (advanced by T inputs), gate, beta, state, out
+// as launch_chunk_prefill
+int launch_chunk_prefill_fused(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, const float* gate,
+                               const float* beta, float* state, float* out, int batch, int heads, int T, int t_pad,
+                               int chunk, float l2_eps, float* workspace, hipStream_t stream);
+
+// the conv state of every (sequence, channel) advanced by the T inputs of qkv [B][T][3 H 128]
+int launch_conv_state_advance(const uint16_t* qkv, float* conv_state, int batch, int heads, int T, int conv_kernel,
+                              hipStream_t stream);
+
 // the transition form of the prefill: P, Q [B][H][128][128], the final state from S being P S + Q
 int launch_chunk_prefill_transition(const float* q, const float* k, const float* v, const float* gate,
                                     const float* beta, float* trans_p, float* trans_q, int batch, int heads, int T,

@@ -456,3 +456,38 @@ def test_header_is_plain_c_and_links_from_c(tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
+
+
+@no_gpu
+def test_fused_prefill_refusals(lib):
+    f = lib.kda_chunk_prefill_fused
+    bad = kda.KDA_ERR_INVALID_ARG
+    need = kda.kda_chunk_prefill_workspace_bytes(1, 2, 64, 16)
+    ok = (1, 2, 64, 16, 4, 1e-6)  # batch, heads, T, chunk, conv_kernel, l2_eps
+    for i in range(7):
+        p = list(P[:7])
+        p[i] = None
+        assert f(*p, *ok, P[7], need, None) == bad, i
+        p = list(P[:7])
+        p[i] += 8 if i != 4 else 2  # beta needs 4-byte alignment, the rest 16
+        assert f(*p, *ok, P[7], need, None) == bad, i
+    assert f(*P[:7], 0, 2, 64, 16, 4, 1e-6, P[7], need, None) == bad
+    assert f(*P[:7], 1, 0, 64, 16, 4, 1e-6, P[7], need, None) == bad
+    assert f(*P[:7], 1, 2, 0, 16, 4, 1e-6, P[7], need, None) == bad
+    assert f(*P[:7], 1, 2, 64, 48, 4, 1e-6, P[7], 1 << 30, None) == kda.KDA_ERR_UNSUPPORTED
+    for K in (1, 2, 3, 5):
+        assert f(*P[:7], 1, 2, 64, 16, K, 1e-6, P[7], need, None) == kda.KDA_ERR_UNSUPPORTED, K
+    assert f(*P[:7], 1, 2, 64, 16, 0, 1e-6, P[7], need, None) == bad
+    assert f(*P[:7], 1, 2, 64, 16, 4, 0.0, P[7], need, None) == bad
+    assert f(*P[:7], 1, 2, 64, 16, 4, float("nan"), P[7], need, None) == bad
+    assert f(*P[:7], *ok, P[7], need - 1, None) == kda.KDA_ERR_WORKSPACE
+    assert f(*P[:7], *ok, None, need, None) == kda.KDA_ERR_WORKSPACE
+    # one sequence's BF16 rows must stay within 32-bit byte offsets: T * 3 * heads * 256 < 2^31
+    far = [(i + 1) << 52 for i in range(8)]
+    T = (1 << 31) // (3 * 16 * 256) + 1
+    assert f(*far[:7], 1, 16, T, 64, 4, 1e-6, far[7], 1 << 62, None) == bad
+    for i, j in ((6, 0), (5, 6), (2, 5), (2, 1)):  # out over qkv, state over out, conv state over state / conv_w
+        p = list(P[:7])
+        p[i] = p[j] + 64
+        assert f(*p, *ok, P[7], need, None) == bad, (i, j)
+    assert f(*P[:7], *ok, P[2] + 64, need, None) == bad  # workspace over the conv state
