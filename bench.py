@@ -374,6 +374,30 @@ def bench_varlen(torch, kda, ki, name, steps, warmup, timer):
     return r, lens, H, C
 
 
+def bench_varlen_fused(torch, kda, ki, name, steps, warmup, timer, K=4):
+    """kda_chunk_prefill_varlen_fused (front end inside the prefill) over a varlen prefill workload, with the
+    front end inputs of the varlen front end workload."""
+    import numpy as np
+    total, H, C, mean_len, seed = ki.VARLEN_WORKLOADS[name]
+    lens = ki.varlen_lengths(seed, total, mean_len)
+    x = ki.varlen_inputs(seed, lens, H, -5.0, 0.02)
+    fx = ki.front_end_inputs(seed, 1, total, H, K)
+    cst = torch.from_numpy(ki.front_end_inputs(seed + 1, len(lens), 1, H, K)["conv_state"]).cuda()
+    bits = lambda a: torch.from_numpy(np.ascontiguousarray(a).view("int16")).view(torch.bfloat16).cuda()
+    qkv, w = bits(fx["qkv"][0]), bits(fx["conv_w"])
+    d = {n: torch.from_numpy(x[n]).cuda() for n in ("gate", "beta", "state", "cu_seqlens")}
+    out = torch.empty((total, H, D), device="cuda")
+    ws = torch.empty(kda.kda_chunk_prefill_varlen_workspace_bytes(len(lens), H, total, C), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        kda.kda_chunk_prefill_varlen_fused(qkv, w, cst, d["gate"], d["beta"], d["state"], d["cu_seqlens"], C,
+                                           ki.L2_EPS, out=out, workspace=ws, stream=stream)
+
+    return timer.run(step, steps, warmup), lens
+
+
 def bench_prefill(torch, kda, ki, name, steps, warmup, timer):
     w = ki.WORKLOADS[name]
     B, H, T, C = w.batch, w.heads, w.T, w.chunk
@@ -756,6 +780,15 @@ def main():
             "tokens_per_s": tokens / r["s_per_step"], "ms_per_call": r["s_per_step"] * 1e3,
             "device_ms": r["launch_avg_s"] * 1e3,
             "steps": "kda_prefill_front_end + kda_chunk_prefill + gated RMSNorm"}
+    for name in ki.VARLEN_WORKLOADS:
+        fname = name.replace("prefill_varlen_", "prefill_varlen_fused_")
+        if not want(fname):
+            continue
+        log(fname)
+        r, lens = bench_varlen_fused(torch, kda, ki, name, args.reps or 20, 0 if args.reps else 20, timer)
+        workloads[fname] = {"tokens_per_s": sum(lens) / r["s_per_step"], "ms_per_call": r["s_per_step"] * 1e3,
+                            "call_ms": r["launch_avg_s"] * 1e3, "sequences": len(lens),
+                            "steps": "kda_chunk_prefill_varlen_fused: the varlen front end inside the varlen prefill"}
     if want("prefill_chain_fused_t8192_h32"):
         log("prefill_chain_fused_t8192_h32")
         r, tokens = bench_prefill_chain(torch, kda, ki, args.reps or 20, 0 if args.reps else 60, timer, fused=True)

@@ -183,6 +183,26 @@ int kda_chunk_prefill_fused(const uint16_t* qkv, const uint16_t* conv_w, float* 
                             int conv_kernel, float l2_eps, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The varlen form of kda_chunk_prefill_fused: kda_prefill_front_end_varlen
+ * followed by kda_chunk_prefill_varlen, with the front end inside the
+ * prefill's prepare kernel.
+ *
+ *   qkv        : [total_tokens][3 * heads * 128] BF16, the sequences back to back
+ *   conv_state : [n_seqs][3 * heads * 128][conv_kernel], one per sequence, advanced by its inputs
+ *   conv_w, conv_kernel (4), l2_eps : as kda_chunk_prefill_fused
+ *   gate, beta, state, out, cu_seqlens, workspace : as kda_chunk_prefill_varlen
+ *
+ * Each sequence's conv window starts from its own conv state.  Agreement with
+ * the separate calls, and refusals, as kda_chunk_prefill_fused and
+ * kda_chunk_prefill_varlen, plus total_tokens * 3 * heads * 256 above
+ * 2^31 - 1 (KDA_ERR_INVALID_ARG).
+ */
+int kda_chunk_prefill_varlen_fused(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, const float* gate,
+                                   const float* beta, float* state, float* out, const int* cu_seqlens, int n_seqs,
+                                   int heads, int total_tokens, int chunk, int conv_kernel, float l2_eps,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Segment transition of a prefill: the final state of kda_chunk_prefill over
  * these T tokens as an affine function of its initial state (layer page,
  * Glm5NextKdaLayer::prefill; kernel-table page, chunk_scan, whose per-chunk

@@ -35,7 +35,7 @@ EXPORTED = ("kda_status_string", "kda_chunk_prefill_workspace_bytes", "kda_chunk
             "kda_chunk_prefill_varlen_workspace_bytes", "kda_chunk_prefill_varlen", "kda_recurrent_k_bf16",
             "kda_recurrent_step_bf16", "kda_decode_front_end_bf16", "kda_prefill_front_end",
             "kda_prefill_front_end_varlen", "kda_chunk_prefill_transition", "kda_state_transition_apply", "kda_chunk_scan",
-            "kda_chunk_prefill_fused")
+            "kda_chunk_prefill_fused", "kda_chunk_prefill_varlen_fused")
 GATED_RMSNORM_MIN_EPS = 1e-30
 
 _lib = None
@@ -94,6 +94,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_chunk_scan.restype = i
     lib.kda_chunk_prefill_fused.argtypes = [p] * 7 + [i] * 5 + [ctypes.c_float, p, sz, p]
     lib.kda_chunk_prefill_fused.restype = i
+    lib.kda_chunk_prefill_varlen_fused.argtypes = [p] * 8 + [i] * 5 + [ctypes.c_float, p, sz, p]
+    lib.kda_chunk_prefill_varlen_fused.restype = i
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -490,6 +492,49 @@ def kda_chunk_prefill_fused(qkv, conv_w, conv_state, gate, beta, state, chunk: i
                                                 ws_bytes, _stream_ptr(stream))
     if rc != KDA_OK:
         raise KdaError("kda_chunk_prefill_fused", rc)
+    return out
+
+
+def kda_chunk_prefill_varlen_fused(qkv, conv_w, conv_state, gate, beta, state, cu_seqlens, chunk: int, l2_eps: float,
+                                   out=None, workspace=None, stream=None):
+    """kda_prefill_front_end_varlen + kda_chunk_prefill_varlen with the front end fused into the prefill.
+    Returns ``out``.
+
+    qkv: bfloat16 [total][3 H 128]; conv_w: bfloat16 [3 H 128][4]; conv_state: float32 [n][3 H 128][4] (in
+    place); gate: [total][H][128]; beta: [total][H]; state: [n][H][128][128] (in place); cu_seqlens: int32
+    CUDA tensor [n + 1]; out: [total][H][128].
+    """
+    if not isinstance(qkv, torch.Tensor) or qkv.dim() != 2:
+        raise ValueError("qkv must be [total_tokens][3 * heads * 128]")
+    total, C = qkv.shape
+    if chunk not in (16, 32, 64):
+        raise KdaError("kda_chunk_prefill_varlen_fused", KDA_ERR_UNSUPPORTED)
+    if not isinstance(gate, torch.Tensor) or gate.dim() != 3 or gate.shape[0] != total:
+        raise ValueError("gate must be [total_tokens][heads][128]")
+    H = gate.shape[1]
+    if C != 3 * H * HEAD_DIM:
+        raise ValueError(f"qkv has {C} channels, expected 3 * {H} * {HEAD_DIM}")
+    if not (isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.dtype == torch.int32 and cu_seqlens.dim() == 1
+            and cu_seqlens.is_cuda and cu_seqlens.is_contiguous()):
+        raise ValueError("cu_seqlens must be a contiguous int32 CUDA tensor [n + 1]")
+    n = cu_seqlens.shape[0] - 1
+    K = conv_w.shape[1] if conv_w.dim() == 2 else 0
+    vs = (total, H, HEAD_DIM)
+    if out is None:
+        out = torch.empty(vs, dtype=torch.float32, device=qkv.device)
+    need = kda_chunk_prefill_varlen_workspace_bytes(n, H, total, chunk)
+    if workspace is None:
+        workspace = _workspace(need, qkv.device, stream)
+    if not (workspace.device.type == "cuda" and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    args = [_check("qkv", qkv, (total, C), torch.bfloat16), _check("conv_w", conv_w, (C, K), torch.bfloat16),
+            _check("conv_state", conv_state, (n, C, K)), _check("gate", gate, vs), _check("beta", beta, (total, H)),
+            _check("state", state, (n, H, HEAD_DIM, HEAD_DIM)), _check("out", out, vs), cu_seqlens.data_ptr()]
+    rc = load_library().kda_chunk_prefill_varlen_fused(*args, n, H, total, chunk, K, float(l2_eps),
+                                                       workspace.data_ptr(), ws_bytes, _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_chunk_prefill_varlen_fused", rc)
     return out
 
 

@@ -236,6 +236,42 @@ KDA_API int kda_chunk_prefill_varlen(const float* q, const float* k, const float
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 
+KDA_API int kda_chunk_prefill_varlen_fused(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state,
+                                           const float* gate, const float* beta, float* state, float* out,
+                                           const int* cu_seqlens, int n_seqs, int heads, int total_tokens, int chunk,
+                                           int conv_kernel, float l2_eps, void* workspace, size_t workspace_bytes,
+                                           void* stream)
+{
+    if (!qkv || !conv_w || !conv_state || !gate || !beta || !state || !out || !cu_seqlens) return KDA_ERR_INVALID_ARG;
+    if (!aligned({qkv, conv_w, conv_state, gate, state, out, workspace}) || !aligned({beta, cu_seqlens}, 4))
+        return KDA_ERR_INVALID_ARG;
+    if (n_seqs < 1 || heads < 1 || total_tokens < 1 || n_seqs > KDA_VARLEN_MAX_SEQS) return KDA_ERR_INVALID_ARG;
+    if (heads > KDA_PREFILL_MAX_HEADS || conv_kernel < 1) return KDA_ERR_INVALID_ARG;
+    if (!(isfinite(l2_eps) && l2_eps >= KDA_GATED_RMSNORM_MIN_EPS)) return KDA_ERR_INVALID_ARG;
+    if (!chunk_ok(chunk) || conv_kernel != 4) return KDA_ERR_UNSUPPORTED;
+    if ((int64_t)n_seqs * heads > 0x7fffffffLL / 64) return KDA_ERR_INVALID_ARG;  // scan grid
+    const VarlenWs w = varlen_ws(n_seqs, heads, total_tokens, chunk);
+    const int64_t C = 3 * (int64_t)heads * KDA_HEAD_DIM;
+    const int64_t x = mul({total_tokens, C});
+    const int64_t cw = mul({C, conv_kernel});
+    const int64_t cs = mul({n_seqs, C, conv_kernel});
+    const int64_t vec = mul({total_tokens, heads, KDA_HEAD_DIM});
+    const int64_t sca = mul({total_tokens, heads});
+    const int64_t st = mul({n_seqs, heads, KDA_HEAD_DIM, KDA_HEAD_DIM});
+    if (w.bytes < 0 || x < 0 || cw < 0 || cs < 0 || vec < 0 || sca < 0 || st < 0) return KDA_ERR_INVALID_ARG;
+    if (mul({total_tokens, C, 2}) > 0x7fffffffLL || mul({n_seqs, C}) > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < (size_t)w.bytes) return KDA_ERR_WORKSPACE;
+    const Range r[] = {{out, vec * 4},   {state, st * 4}, {conv_state, cs * 4}, {workspace, w.bytes},
+                       {qkv, x * 2},     {conv_w, cw * 2}, {gate, vec * 4},     {beta, sca * 4},
+                       {cu_seqlens, ((int64_t)n_seqs + 1) * 4}};
+    if (any_overlap(r, 9, 4)) return KDA_ERR_INVALID_ARG;
+    const int rc = kda::launch_chunk_prefill_varlen_fused(qkv, conv_w, conv_state, gate, beta, state, out, cu_seqlens,
+                                                          n_seqs, heads, total_tokens, chunk, l2_eps,
+                                                          static_cast<float*>(workspace), (size_t)w.meta_offset_floats,
+                                                          w.max_records, static_cast<hipStream_t>(stream));
+    return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
 namespace {
 
 // decode_k with FP32 q, k, v or, when qkv is not null, packed BF16 q | k | v rows

@@ -91,7 +91,9 @@ struct ChunkPos {
     int nvalid;
     int span;
     int rec;
-    int b, t0, h;  // sequence, first token, head (dense layout; used by the fused front end)
+    int b, t0, h;  // sequence, first token of the chunk within it, head (for the fused front end)
+    size_t tok0;   // the sequence's first token in the token stream of the front end's inputs
+    int len;       // the sequence's length
 };
 // One (sequence, head) of the scan: its first token, its length, its chunks
 // and the index of its first record.
@@ -124,6 +126,8 @@ struct DenseLayout {
         p.b = b;
         p.t0 = c * C;
         p.h = h;
+        p.tok0 = (size_t)b * T;
+        p.len = T;
         return p;
     }
     __device__ SeqPos seq(int bh) const
@@ -165,6 +169,8 @@ struct VarlenLayout {
         p.b = lo;
         p.t0 = c * C;
         p.h = h;
+        p.tok0 = (size_t)cu[lo];
+        p.len = len;
         return p;
     }
     __device__ SeqPos seq(int bh) const
@@ -383,10 +389,9 @@ __device__ __forceinline__ void rec_st4(float* p, float4 v)
 // layout of the U tiles.  The conv state itself is advanced by a separate
 // launch after the whole prefill.
 struct FeSrc {
-    const unsigned short* qkv;     // [B][T][3][H][128] BF16
+    const unsigned short* qkv;     // [tokens][3][H][128] BF16: sequence b at rows tok0 .. tok0 + len - 1
     const unsigned short* conv_w;  // [3 H 128][4] BF16
-    const float* conv_state;       // [B][3 H 128][4] FP32, read only here
-    int T;                         // tokens per sequence in qkv
+    const float* conv_state;       // [sequences][3 H 128][4] FP32, read only here
     double eps;                    // l2_eps
 };
 constexpr int kFeK = 4;  // conv taps of the fused form
@@ -427,7 +432,7 @@ __device__ __forceinline__ void fe_load_qk(FeRaw<C>& r, const FeSrc& fe, int par
     const int rowbytes = 3 * heads * kD * 2;
     const int col = 4 * (tid & 31);
     const int ch = (part * heads + p.h) * kD + col;  // first channel of the four
-    const rsrc_t src = make_rsrc(fe.qkv + (size_t)p.b * fe.T * 3 * heads * kD, live ? (uint32_t)fe.T * rowbytes : 0u);
+    const rsrc_t src = make_rsrc(fe.qkv + p.tok0 * 3 * heads * kD, live ? (uint32_t)p.len * rowbytes : 0u);
 #pragma unroll
     for (int m = 0; m < FeRaw<C>::NW; ++m) {
         // rows before the call (t < 0) wrap to offsets at or above 2^31 and rows at or past T
@@ -523,7 +528,7 @@ __device__ __forceinline__ void fe_load_v(FeV<C>& r, const FeSrc& fe, const Chun
 {
     const int rowbytes = 3 * heads * kD * 2;
     const int ch = (2 * heads + p.h) * kD + 16 * wave + l16;
-    const rsrc_t src = make_rsrc(fe.qkv + (size_t)p.b * fe.T * 3 * heads * kD, (uint32_t)fe.T * rowbytes);
+    const rsrc_t src = make_rsrc(fe.qkv + p.tok0 * 3 * heads * kD, (uint32_t)p.len * rowbytes);
 #pragma unroll
     for (int y = 0; y < C / 16; ++y)
 #pragma unroll
@@ -1234,18 +1239,19 @@ static int launch_scan_auto(const float* ws, float* state, float* out, long long
 
 // max_records bounds the layout's record count (exact for the dense layout).
 // kTrans: state is the Q output and out the P output of the transition form.
-template <int C, class Layout, bool kTrans = false>
+// kFE: the prepare with the front end fused in (q, k, v unused; fe its inputs).
+template <int C, class Layout, bool kTrans = false, bool kFE = false>
 static int launch_chunk(const float* q, const float* k, const float* v, const float* gate, const float* beta,
                         float* state, float* out, long long n_bh, int heads, long long max_records, float* ws,
-                        const Layout& layout, hipStream_t stream)
+                        const Layout& layout, hipStream_t stream, const FeSrc& fe = FeSrc{})
 {
     // one persistent prepare workgroup per compute unit (its LDS use allows one)
     const int n_cu = compute_units();
     if (n_cu < 1) return -1;
     const int grid_p = max_records < n_cu ? (int)max_records : n_cu;
     if (grid_p > 0) {
-        hipLaunchKernelGGL((chunk_prepare_kernel<C, Layout>), dim3((unsigned)grid_p), dim3(kPrepThreads), 0, stream,
-                           q, k, v, gate, beta, ws, heads, layout, FeSrc{});
+        hipLaunchKernelGGL((chunk_prepare_kernel<C, Layout, kFE>), dim3((unsigned)grid_p), dim3(kPrepThreads), 0,
+                           stream, q, k, v, gate, beta, ws, heads, layout, fe);
         if (hipGetLastError() != hipSuccess) return -1;
     }
     return launch_scan_auto<C, Layout, kTrans>(ws, state, out, n_bh, heads, layout, n_cu, stream);
@@ -1299,7 +1305,8 @@ int launch_chunk_scan(const float* workspace, float* state, float* out, int batc
     }
 }
 
-// The prefill with the front end fused into the prepare (dense layout)
+// The prefill with the front end fused into the prepare (dense layout).  q, k,
+// v are not read in this form: the gate pointer stands in for them.
 template <int C>
 static int launch_dense_fused(const FeSrc& fe, const float* gate, const float* beta, float* state, float* out,
                               int batch, int heads, int T, int t_pad, float* ws, hipStream_t stream)
@@ -1307,15 +1314,8 @@ static int launch_dense_fused(const FeSrc& fe, const float* gate, const float* b
     const int nchunks = t_pad / C;
     const long long n_bh = (long long)batch * heads;
     const DenseLayout layout{heads, T, t_pad, nchunks, (int)(n_bh * nchunks)};
-    const int n_cu = compute_units();
-    if (n_cu < 1) return -1;
-    const long long records = n_bh * nchunks;
-    const int grid_p = records < n_cu ? (int)records : n_cu;
-    // q, k, v are not read in this form: the gate pointer stands in for them
-    hipLaunchKernelGGL((chunk_prepare_kernel<C, DenseLayout, true>), dim3((unsigned)grid_p), dim3(kPrepThreads), 0,
-                       stream, gate, gate, gate, gate, beta, ws, heads, layout, fe);
-    if (hipGetLastError() != hipSuccess) return -1;
-    return launch_scan_auto<C, DenseLayout>(ws, state, out, n_bh, heads, layout, n_cu, stream);
+    return launch_chunk<C, DenseLayout, false, true>(gate, gate, gate, gate, beta, state, out, n_bh, heads,
+                                                     n_bh * nchunks, ws, layout, stream, fe);
 }
 
 int launch_chunk_prefill_fused(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, const float* gate,
@@ -1323,7 +1323,7 @@ int launch_chunk_prefill_fused(const uint16_t* qkv, const uint16_t* conv_w, floa
                                int chunk, float l2_eps, float* workspace, hipStream_t stream)
 {
     const FeSrc fe{reinterpret_cast<const unsigned short*>(qkv), reinterpret_cast<const unsigned short*>(conv_w),
-                   conv_state, T, (double)l2_eps};
+                   conv_state, (double)l2_eps};
     int rc = -1;
     switch (chunk) {
     case 16: rc = launch_dense_fused<16>(fe, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream); break;
@@ -1450,6 +1450,33 @@ __global__ __launch_bounds__(kSetupThreads) void varlen_setup_kernel(const int* 
         cb[i] = acc;
         prev = cur;
     }
+}
+
+int launch_chunk_prefill_varlen_fused(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state,
+                                      const float* gate, const float* beta, float* state, float* out,
+                                      const int* cu_seqlens, int n_seqs, int heads, int total, int chunk,
+                                      float l2_eps, float* workspace, size_t meta_offset_floats,
+                                      long long max_records, hipStream_t stream)
+{
+    int* const cu = reinterpret_cast<int*>(workspace + meta_offset_floats);
+    int* const cb = cu + (n_seqs + 1);
+    hipLaunchKernelGGL(varlen_setup_kernel, dim3(1), dim3(kSetupThreads), 0, stream, cu_seqlens, n_seqs, total,
+                       chunk, cu, cb);
+    if (hipGetLastError() != hipSuccess) return -1;
+    const VarlenLayout layout{heads, total, n_seqs, cu, cb};
+    const long long n_bh = (long long)n_seqs * heads;
+    const FeSrc fe{reinterpret_cast<const unsigned short*>(qkv), reinterpret_cast<const unsigned short*>(conv_w),
+                   conv_state, (double)l2_eps};
+    int rc = -1;
+    // q, k, v are not read in this form: the gate pointer stands in for them
+    switch (chunk) {
+    case 16: rc = launch_chunk<16, VarlenLayout, false, true>(gate, gate, gate, gate, beta, state, out, n_bh, heads, max_records, workspace, layout, stream, fe); break;
+    case 32: rc = launch_chunk<32, VarlenLayout, false, true>(gate, gate, gate, gate, beta, state, out, n_bh, heads, max_records, workspace, layout, stream, fe); break;
+    case 64: rc = launch_chunk<64, VarlenLayout, false, true>(gate, gate, gate, gate, beta, state, out, n_bh, heads, max_records, workspace, layout, stream, fe); break;
+    default: return -1;
+    }
+    if (rc != 0) return rc;
+    return launch_conv_state_advance_varlen(qkv, conv_state, cu_seqlens, n_seqs, heads, total, 4, stream);
 }
 
 int launch_chunk_prefill_varlen(const float* q, const float* k, const float* v, const float* gate, const float* beta,

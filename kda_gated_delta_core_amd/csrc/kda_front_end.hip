@@ -362,6 +362,22 @@ int launch_conv_state_advance(const uint16_t* qkv, float* conv_state, int batch,
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+int launch_conv_state_advance_varlen(const uint16_t* qkv, float* conv_state, const int* cu_seqlens, int n_seqs,
+                                     int heads, int total, int conv_kernel, hipStream_t stream)
+{
+    const auto* x = reinterpret_cast<const unsigned short*>(qkv);
+    const int C = 3 * heads * kD;
+    const dim3 grid((unsigned)(((long long)n_seqs * C + 255) / 256));
+    switch (conv_kernel) {
+    case 1: hipLaunchKernelGGL(prefill_conv_state_varlen_kernel<1>, grid, dim3(256), 0, stream, x, conv_state, cu_seqlens, n_seqs, C, total); break;
+    case 2: hipLaunchKernelGGL(prefill_conv_state_varlen_kernel<2>, grid, dim3(256), 0, stream, x, conv_state, cu_seqlens, n_seqs, C, total); break;
+    case 3: hipLaunchKernelGGL(prefill_conv_state_varlen_kernel<3>, grid, dim3(256), 0, stream, x, conv_state, cu_seqlens, n_seqs, C, total); break;
+    case 4: hipLaunchKernelGGL(prefill_conv_state_varlen_kernel<4>, grid, dim3(256), 0, stream, x, conv_state, cu_seqlens, n_seqs, C, total); break;
+    default: return -1;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_prefill_front_end_varlen(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q,
                                     float* k, float* v, const int* cu_seqlens, int n_seqs, int heads, int total,
                                     int conv_kernel, float l2_eps, hipStream_t stream)

@@ -40,6 +40,18 @@ int launch_chunk_prefill_fused(const uint16_t* qkv, const uint16_t* conv_w, floa
                                const float* beta, float* state, float* out, int batch, int heads, int T, int t_pad,
                                int chunk, float l2_eps, float* workspace, hipStream_t stream);
 
+// varlen form of the fused prefill: qkv [total][3 H 128], conv state [n][3 H 128][4], the rest as
+// launch_chunk_prefill_varlen
+int launch_chunk_prefill_varlen_fused(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state,
+                                      const float* gate, const float* beta, float* state, float* out,
+                                      const int* cu_seqlens, int n_seqs, int heads, int total, int chunk,
+                                      float l2_eps, float* workspace, size_t meta_offset_floats,
+                                      long long max_records, hipStream_t stream);
+
+// each sequence's conv state advanced by its inputs (qkv [total][3 H 128], offsets read clamped)
+int launch_conv_state_advance_varlen(const uint16_t* qkv, float* conv_state, const int* cu_seqlens, int n_seqs,
+                                     int heads, int total, int conv_kernel, hipStream_t stream);
+
 // the conv state of every (sequence, channel) advanced by the T inputs of qkv [B][T][3 H 128]
 int launch_conv_state_advance(const uint16_t* qkv, float* conv_state, int batch, int heads, int T, int conv_kernel,
                               hipStream_t stream);

@@ -491,3 +491,30 @@ def test_fused_prefill_refusals(lib):
         p[i] = p[j] + 64
         assert f(*p, *ok, P[7], need, None) == bad, (i, j)
     assert f(*P[:7], *ok, P[2] + 64, need, None) == bad  # workspace over the conv state
+
+
+@no_gpu
+def test_varlen_fused_prefill_refusals(lib):
+    f = lib.kda_chunk_prefill_varlen_fused
+    bad = kda.KDA_ERR_INVALID_ARG
+    need = kda.kda_chunk_prefill_varlen_workspace_bytes(3, 2, 100, 16)
+    ok = (3, 2, 100, 16, 4, 1e-6)  # n_seqs, heads, total, chunk, conv_kernel, l2_eps
+    for i in range(8):
+        p = list(P[:8])
+        p[i] = None
+        assert f(*p, *ok, P[8], need, None) == bad, i
+        p = list(P[:8])
+        p[i] += 8 if i not in (4, 7) else 2  # beta and cu_seqlens need 4-byte alignment, the rest 16
+        assert f(*p, *ok, P[8], need, None) == bad, i
+    assert f(*P[:8], 0, 2, 100, 16, 4, 1e-6, P[8], need, None) == bad
+    assert f(*P[:8], (1 << 20) + 1, 2, 100, 16, 4, 1e-6, P[8], 1 << 40, None) == bad
+    assert f(*P[:8], 3, 0, 100, 16, 4, 1e-6, P[8], need, None) == bad
+    assert f(*P[:8], 3, 2, 0, 16, 4, 1e-6, P[8], need, None) == bad
+    assert f(*P[:8], 3, 2, 100, 48, 4, 1e-6, P[8], 1 << 30, None) == kda.KDA_ERR_UNSUPPORTED
+    assert f(*P[:8], 3, 2, 100, 16, 3, 1e-6, P[8], need, None) == kda.KDA_ERR_UNSUPPORTED
+    assert f(*P[:8], 3, 2, 100, 16, 4, -1.0, P[8], need, None) == bad
+    assert f(*P[:8], *ok, P[8], need - 1, None) == kda.KDA_ERR_WORKSPACE
+    for i, j in ((6, 0), (7, 2), (5, 2)):  # out over qkv, cu_seqlens inside the conv state, state over conv state
+        p = list(P[:8])
+        p[i] = p[j] + 64
+        assert f(*p, *ok, P[8], need, None) == bad, (i, j)

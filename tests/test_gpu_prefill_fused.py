@@ -116,3 +116,61 @@ def test_fused_prefill_full_size(device):
     assert_close("out", host(out)[:, :T], o_ref)
     assert_close("state", host(st), s_ref)
     assert np.array_equal(host(cst), c_ref)
+
+
+def _varlen(seed, lens, H, gate_lo=-5.0):
+    total = sum(lens)
+    fx = ki.front_end_inputs(seed, 1, total, H, K)
+    cst = ki.front_end_inputs(seed + 1, len(lens), 1, H, K)["conv_state"]  # one conv state per sequence
+    core = ki.varlen_inputs(seed + 2, lens, H, gate_lo, 0.02)
+    return fx["qkv"][0], fx["conv_w"], cst, core
+
+
+def _varlen_fused(kda, qkv, w, cst, core, C):
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    cst_d, st = d(cst), d(core["state"])
+    out = torch.full(core["q"].shape, SENTINEL, device="cuda")
+    kda.kda_chunk_prefill_varlen_fused(_bits_dev(qkv), _bits_dev(w), cst_d, d(core["gate"]), d(core["beta"]), st,
+                                       d(core["cu_seqlens"]), C, ki.L2_EPS, out=out)
+    torch.cuda.synchronize()
+    return out, st, cst_d
+
+
+@pytest.mark.parametrize("C", [16, 64])
+def test_varlen_fused_prefill_matches_oracle(device, C):
+    """per sequence: the oracle's front end from that sequence's conv state, then its recurrence from that
+    sequence's state; empty and one-token sequences included"""
+    import kda_gated_delta_core_amd as kda
+    lens, H = [100, 1, 0, 257, 64, 3], 2
+    announce(f"kda_chunk_prefill_varlen_fused lens={lens} H={H} C={C}")
+    qkv, w, cst, core = _varlen(9300 + C, lens, H)
+    out, st, cst_d = _varlen_fused(kda, qkv, w, cst, core, C)
+    cu = core["cu_seqlens"]
+    got_out, got_st, got_cst = host(out), host(st), host(cst_d)
+    for s, n in enumerate(lens):
+        a, e = int(cu[s]), int(cu[s + 1])
+        if n == 0:
+            assert np.array_equal(got_st[s], core["state"][s]) and np.array_equal(got_cst[s], cst[s])
+            continue
+        q, k, v, c_ref, _ = oracle.decode_front_end(qkv[None, a:e], w, cst[s:s + 1], H, ki.L2_EPS)
+        o_ref, s_ref, _, _ = oracle.serial(q, k, v, core["gate"][None, a:e], core["beta"][None, a:e],
+                                           core["state"][s:s + 1])
+        assert_close(f"seq {s} out", got_out[a:e], o_ref[0])
+        assert_close(f"seq {s} state", got_st[s], s_ref[0])
+        assert np.array_equal(got_cst[s], c_ref[0]), f"seq {s} conv state"
+
+
+def test_varlen_fused_prefill_against_the_separate_calls(device):
+    import kda_gated_delta_core_amd as kda
+    lens, H, C = [300, 77, 1, 640], 3, 64
+    announce(f"kda_chunk_prefill_varlen_fused vs separate calls lens={lens} H={H} C={C}")
+    qkv, w, cst, core = _varlen(9400, lens, H)
+    out, st, cst_d = _varlen_fused(kda, qkv, w, cst, core, C)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    cst2, st2, cu = d(cst), d(core["state"]), d(core["cu_seqlens"])
+    q, k, v = kda.kda_prefill_front_end_varlen(_bits_dev(qkv), _bits_dev(w), cst2, cu, H, ki.L2_EPS)
+    out2 = kda.kda_chunk_prefill_varlen(q, k, v, d(core["gate"]), d(core["beta"]), st2, cu, C)
+    torch.cuda.synchronize()
+    assert_close("out vs separate", host(out), host(out2))
+    assert_close("state vs separate", host(st), host(st2))
+    assert torch.equal(cst_d, cst2)
