@@ -219,3 +219,43 @@ def test_graph_replays_of_the_segment_split(device):
         st.copy_(st0)
 
     _capture_and_replay(kda, "segment split", work, reset, lambda: (P1, Q1, P2, Q2, st, out2[:, :T2]))
+
+
+def test_graph_replays_of_the_fused_prefills(device):
+    """kda_chunk_prefill_fused and kda_chunk_prefill_varlen_fused captured as one graph"""
+    import kda_gated_delta_core_amd as kda
+    B, T, H, C = 2, 150, 3, 64
+    announce(f"graph capture: fused prefill B={B} T={T} H={H}, varlen fused prefill")
+    t_pad = -(-T // C) * C
+    fx = ki.front_end_inputs(1540, B, T, H, 4)
+    core = ki.make_batch(1541, B, H, T, -5.0, 0.02, alloc_rows=t_pad)
+    qkv, w = _bits(fx["qkv"]), _bits(fx["conv_w"])
+    g, b = torch.from_numpy(core["gate"]).cuda(), torch.from_numpy(core["beta"]).cuda()
+    cst0, st0 = torch.from_numpy(fx["conv_state"]).cuda(), torch.from_numpy(core["state"]).cuda()
+    cst, st = torch.empty_like(cst0), torch.empty_like(st0)
+    out = torch.zeros((B, t_pad, H, 128), device="cuda")
+    ws = torch.empty(kda.kda_chunk_prefill_workspace_bytes(B, H, T, C), dtype=torch.uint8, device="cuda")
+    lens = [70, 0, 1, 130]
+    vfx = ki.front_end_inputs(1542, 1, sum(lens), H, 4)
+    vcst0 = torch.from_numpy(ki.front_end_inputs(1543, len(lens), 1, H, 4)["conv_state"]).cuda()
+    vx = ki.varlen_inputs(1544, lens, H, -5.0, 0.02)
+    vd = {n: torch.from_numpy(vx[n]).cuda() for n in ("gate", "beta", "cu_seqlens")}
+    vqkv = _bits(vfx["qkv"][0])
+    vst0 = torch.from_numpy(vx["state"]).cuda()
+    vcst, vst = torch.empty_like(vcst0), torch.empty_like(vst0)
+    vout = torch.zeros((sum(lens), H, 128), device="cuda")
+    vws = torch.empty(kda.kda_chunk_prefill_varlen_workspace_bytes(len(lens), H, sum(lens), C), dtype=torch.uint8,
+                      device="cuda")
+
+    def work(s):
+        kda.kda_chunk_prefill_fused(qkv, w, cst, g, b, st, C, ki.L2_EPS, out=out, workspace=ws, stream=s)
+        kda.kda_chunk_prefill_varlen_fused(vqkv, w, vcst, vd["gate"], vd["beta"], vst, vd["cu_seqlens"], C,
+                                           ki.L2_EPS, out=vout, workspace=vws, stream=s)
+
+    def reset():
+        cst.copy_(cst0)
+        st.copy_(st0)
+        vcst.copy_(vcst0)
+        vst.copy_(vst0)
+
+    _capture_and_replay(kda, "fused prefills", work, reset, lambda: (out[:, :T], st, cst, vout, vst, vcst))

@@ -121,3 +121,30 @@ def test_random_transition(device, B, H, T, C, gate_lo, seed):
     S = np.random.default_rng(seed + 1).standard_normal((B, H, 128, 128)).astype(np.float32)
     _, s_ref, _, _ = oracle.serial(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["gate"]), sl(x["beta"]), S)
     assert_close("P S + Q", np.matmul(host(P).astype(np.float64), S.astype(np.float64)) + host(Q), s_ref)
+
+
+FUSED = _cases(6, lambda r: (int(r.integers(1, 3)), int(r.integers(1, 5)), int(r.integers(1, 300)),
+                             int(r.choice([16, 32, 64])), float(r.uniform(-9.0, 0.0)), int(r.integers(0, 10 ** 6))))
+
+
+@pytest.mark.parametrize("B,H,T,C,gate_lo,seed", FUSED)
+def test_random_fused_prefill(device, B, H, T, C, gate_lo, seed):
+    """kda_chunk_prefill_fused against the oracle's front end followed by its recurrence"""
+    import kda_gated_delta_core_amd as kda
+    announce(f"kda_chunk_prefill_fused B={B} H={H} T={T} C={C} gate_lo={gate_lo:.2f} seed={seed}")
+    t_pad = -(-T // C) * C
+    fx = ki.front_end_inputs(seed, B, T, H, 4)
+    x = ki.make_batch(seed + 1, B, H, T, gate_lo, 0.02, alloc_rows=t_pad, pad_value=float("nan"))
+    bits = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    cst, st = dev(fx["conv_state"]), dev(x["state"])
+    out = torch.full((B, t_pad, H, 128), SENTINEL, device="cuda")
+    kda.kda_chunk_prefill_fused(bits(fx["qkv"]), bits(fx["conv_w"]), cst, dev(x["gate"]), dev(x["beta"]), st, C,
+                                ki.L2_EPS, out=out)
+    torch.cuda.synchronize()
+    q, k, v, c_ref, _ = oracle.decode_front_end(fx["qkv"], fx["conv_w"], fx["conv_state"], H, ki.L2_EPS)
+    sl = lambda a: np.ascontiguousarray(a[:, :T])
+    o_ref, s_ref, _, _ = oracle.serial(q, k, v, sl(x["gate"]), sl(x["beta"]), x["state"])
+    assert_close("out", host(out)[:, :T], o_ref)
+    assert_close("state", host(st), s_ref)
+    assert np.array_equal(host(cst), c_ref)
+    assert np.all(host(out)[:, T:] == SENTINEL)
