@@ -451,35 +451,25 @@ __device__ __forceinline__ void fe_load_qk(FeRaw<C>& r, const FeSrc& fe, int par
     r.w[1] = buf_ld_b128u(ws, col * kFeK * 2, 16);
 }
 
-// Sum over the 32 lanes of each half of a wave, returned to every lane of
-// that half: quads, eights, rows of 16 (DPP), then row 0 into row 1 and row 2
-// into row 3 through the row broadcast of lane 15.
-__device__ __forceinline__ double half_wave_sum_f64(double x, int lane)
-{
-    x += dpp_f64<0xB1>(x);        // quad_perm [1, 0, 3, 2]
-    x += dpp_f64<0x4E>(x);        // quad_perm [2, 3, 0, 1]
-    x += dpp_f64<0x141>(x);       // row_half_mirror
-    x += dpp_f64<0x140>(x);       // row_mirror
-    x += dpp_f64<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
-    const unsigned long long u = (unsigned long long)__double_as_longlong(x);
-    const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, 31);
-    const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), 31);
-    const unsigned lo2 = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, 63);
-    const unsigned hi2 = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), 63);
-    const unsigned a = lane < 32 ? lo : lo2, b = lane < 32 ? hi : hi2;
-    return __longlong_as_double((long long)(((unsigned long long)b << 32) | a));
-}
-
-// conv, SiLU and (l2) the per-row scale for the rows of FeRaw, to the float4
-// pieces prep_stage takes (in the fused row order)
+// conv, SiLU and the per-row scale 1 / sqrt(sum y^2 + eps) for the rows of k
+// and q (FeRaw), to the float4 pieces prep_stage takes (in the fused row
+// order).  The sum of squares is FP64, reduced over the 32 lanes of each half
+// of a wave (quads, eights, rows of 16 by DPP, then row 0 into row 1 and row 2
+// into row 3 through the row broadcast of lane 15); the 2 NV4 rows' reductions
+// are taken step by step side by side, independent chains the scheduler
+// overlaps.
 template <int C>
-__device__ __forceinline__ void fe_finish_qk(const FeRaw<C>& r, float4 (&out)[PrepInputs<C>::NV4], int t0, int tid,
-                                             bool l2, double eps)
+__device__ __forceinline__ void fe_finish_kq(const FeRaw<C>& rk, const FeRaw<C>& rq, float4 (&ok)[PrepInputs<C>::NV4],
+                                             float4 (&oq)[PrepInputs<C>::NV4], int t0, int tid, double eps)
 {
+    constexpr int NV4 = PrepInputs<C>::NV4, N = 2 * NV4;
     const int lane = tid & 63;
+    float y[N][4];
+    double x[N];
 #pragma unroll
-    for (int i = 0; i < PrepInputs<C>::NV4; ++i) {
-        float y[4];
+    for (int n = 0; n < N; ++n) {
+        const FeRaw<C>& r = n < NV4 ? rk : rq;
+        const int i = n % NV4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const unsigned wj0 = j < 2 ? (j == 0 ? r.w[0].x : r.w[0].z) : (j == 2 ? r.w[1].x : r.w[1].z);
@@ -487,28 +477,46 @@ __device__ __forceinline__ void fe_finish_qk(const FeRaw<C>& r, float4 (&out)[Pr
             float a = 0.f;
 #pragma unroll
             for (int k = 0; k < kFeK; ++k) {
-                const int t = t0 + PrepInputs<C>::NV4 * (tid >> 5) + i - (kFeK - 1) + k;
-                float x = fe_bf16(j < 2 ? r.x[i + k].x : r.x[i + k].y, j & 1);
-                // rows that can precede the call (compile time), in a sequence's first chunk only
-                // (t0 == 0 is wave-uniform: the other chunks skip this with a scalar branch): state slot 4 + t
+                const int t = t0 + NV4 * (tid >> 5) + i - (kFeK - 1) + k;
+                float xv = fe_bf16(j < 2 ? r.x[i + k].x : r.x[i + k].y, j & 1);
                 if (i + k + 1 < kFeK && t0 == 0) {
                     const float sv = t == -3 ? r.st[j].y : (t == -2 ? r.st[j].z : r.st[j].w);
-                    x = t < 0 ? sv : x;
+                    xv = t < 0 ? sv : xv;
                 }
                 const float w = fe_bf16(k < 2 ? wj0 : wj1, k & 1);
-                a = k == 0 ? w * x : fmaf(w, x, a);
+                a = k == 0 ? w * xv : fmaf(w, xv, a);
             }
-            y[j] = fe_silu(a);
+            y[n][j] = fe_silu(a);
         }
-        if (l2) {
-            const double ss = (double)y[0] * y[0] + (double)y[1] * y[1] + (double)y[2] * y[2] + (double)y[3] * y[3];
-            const double x = half_wave_sum_f64(ss, lane) + eps;
-            double rs = __builtin_amdgcn_rsq(x);
-            rs = rs * (1.5 - 0.5 * (x * rs) * rs);  // one Newton step
+        x[n] = (double)y[n][0] * y[n][0] + (double)y[n][1] * y[n][1] + (double)y[n][2] * y[n][2] +
+               (double)y[n][3] * y[n][3];
+    }
+    // the reduction steps, each over all rows before the next
 #pragma unroll
-            for (int j = 0; j < 4; ++j) y[j] = (float)(y[j] * rs);
-        }
-        out[i] = make_float4(y[0], y[1], y[2], y[3]);
+    for (int n = 0; n < N; ++n) x[n] += dpp_f64<0xB1>(x[n]);
+#pragma unroll
+    for (int n = 0; n < N; ++n) x[n] += dpp_f64<0x4E>(x[n]);
+#pragma unroll
+    for (int n = 0; n < N; ++n) x[n] += dpp_f64<0x141>(x[n]);
+#pragma unroll
+    for (int n = 0; n < N; ++n) x[n] += dpp_f64<0x140>(x[n]);
+#pragma unroll
+    for (int n = 0; n < N; ++n) x[n] += dpp_f64<0x142, 0xa>(x[n]);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        const unsigned long long u = (unsigned long long)__double_as_longlong(x[n]);
+        const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, 31);
+        const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), 31);
+        const unsigned lo2 = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, 63);
+        const unsigned hi2 = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), 63);
+        const unsigned a = lane < 32 ? lo : lo2, b = lane < 32 ? hi : hi2;
+        const double tot = __longlong_as_double((long long)(((unsigned long long)b << 32) | a)) + eps;
+        double rs = __builtin_amdgcn_rsq(tot);
+        rs = rs * (1.5 - 0.5 * (tot * rs) * rs);  // one Newton step
+        const float4 o = make_float4((float)(y[n][0] * rs), (float)(y[n][1] * rs), (float)(y[n][2] * rs),
+                                     (float)(y[n][3] * rs));
+        if (n < NV4) ok[n % NV4] = o;
+        else oq[n % NV4] = o;
     }
 }
 
@@ -555,7 +563,7 @@ __device__ __forceinline__ void fe_finish_v(const FeV<C>& r, float (&vb)[C / 16]
             for (int k = 0; k < kFeK; ++k) {
                 const int t = t0 + 16 * y + 4 * q4 + e - (kFeK - 1) + k;
                 float x = bf16_to_f32(r.x[y][e + k]);
-                if (y == 0 && e + k < kFeK - 1 && t0 == 0) {  // rows that can precede the call, as in fe_finish_qk
+                if (y == 0 && e + k < kFeK - 1 && t0 == 0) {  // rows that can precede the call, as in fe_finish_kq
                     const float sv = t == -3 ? r.st.y : (t == -2 ? r.st.z : r.st.w);
                     x = t < 0 ? sv : x;
                 }
@@ -617,8 +625,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
             FeRaw<C> rk, rq;
             fe_load_qk<C>(rk, fe, 1, pos, heads, threadIdx.x, true);
             fe_load_qk<C>(rq, fe, 0, pos, heads, threadIdx.x, true);
-            fe_finish_qk<C>(rk, in.k, pos.t0, threadIdx.x, true, fe.eps);
-            fe_finish_qk<C>(rq, in.q, pos.t0, threadIdx.x, true, fe.eps);
+            fe_finish_kq<C>(rk, rq, in.k, in.q, pos.t0, threadIdx.x, fe.eps);
         } else {
             prep_load_part<C>(in.k, src.k, heads, threadIdx.x);
             prep_load_part<C>(in.q, src.q, heads, threadIdx.x);
@@ -858,10 +865,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         __builtin_amdgcn_sched_barrier(0);
         // (fused front end) the next chunk's k and q from their raw inputs, which arrived during
         // steps 3-5; independent of this step's products, so the VALU work can fill the MFMA gaps
-        if constexpr (kFE) {
-            fe_finish_qk<C>(rk, in.k, npos.t0, tid, true, fe.eps);
-            fe_finish_qk<C>(rq, in.q, npos.t0, tid, true, fe.eps);
-        }
+        if constexpr (kFE) fe_finish_kq<C>(rk, rq, in.k, in.q, npos.t0, tid, fe.eps);
         //    Row blocks X and NT - 1 - X go together (equal work, 4 (NT + 1) MFMAs
         //    each way), so four independent accumulation chains keep the matrix
         //    core busy instead of two; each block's sum runs in the same order.
