@@ -27,7 +27,9 @@ the 256 MB Infinity Cache cannot hold them: every step reads and writes HBM.
 ``roofline`` describes the dominant kernel of the headline (the recurrent
 kernel): algorithmic bytes per launch / average launch duration from HIP
 events around each launch on the launch stream, against 8 TB/s.
-``cpu_baseline`` times the fp64 oracle on the host cores (rank 0, N=1).
+``cpu_baseline`` times the fp64 oracle on the host cores (rank 0, N=1) on the headline workload; the
+same oracle is also timed beside the decode_k workload and the three prefill workloads (each
+workload's ``cpu_oracle`` entry, with the threads it used and the sample it ran).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu]
 """
@@ -528,60 +530,63 @@ def _tail_inputs(ki, w, torch):
 
 
 # ---------------------------------------------------------------- cpu baseline
-def cpu_baseline(ki, budget_s: float = 12.0):
-    """The fp64 oracle (as it stands) on the headline workload: repeated full decode steps of
-    all 64 x 32 heads until about budget_s of CPU time has passed."""
+def _oracle_rate(oracle, x, tokens: int, T: int | None = None, n_snap: int = 0):
+    """One run of the fp64 oracle (as it stands) on x; returns (tokens/s, wall s, threads)."""
+    t0 = time.perf_counter()
+    _, _, _, threads = oracle.serial(x["q"], x["k"], x["v"], x["gate"], x["beta"], x["state"], T=T, n_snap=n_snap)
+    el = time.perf_counter() - t0
+    return tokens / el, el, threads
+
+
+def cpu_baselines(ki, budget_s: float = 10.0):
+    """The fp64 oracle (never tuned for this) timed on the host cores beside every configuration, on
+    the same seeded inputs.  Returns (headline entry, {workload: entry}); input generation is not
+    timed.  Each sample is bounded so the whole baseline stays within about half a minute."""
+    import numpy as np
     import oracle
+    res = {}
+
+    def entry(rate, threads, sample, unit="tokens/s"):
+        return {"value": rate, "unit": unit, "cores": threads, "kind": "oracle",
+                "sample": sample + f"; os.cpu_count()={os.cpu_count()}"}
+
+    # decode B=64 H=32 (headline): repeated full decode steps until ~budget_s of wall time
     w = ki.WORKLOADS["decode_b64_h32"]
     x = ki.workload_inputs(w)
     state = x["state"].astype("float64")
-    reps, t0 = 0, time.perf_counter()
-    threads = 1
+    reps, t0, threads = 0, time.perf_counter(), 1
     while True:
         _, state, _, threads = oracle.serial(x["q"], x["k"], x["v"], x["gate"], x["beta"], state)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 100000:
             break
-    return {"value": w.batch * reps / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} full decode steps (B=64, H=32, one token each) of the fp64 oracle, "
-                      f"{el:.1f} s wall on {threads} threads, os.cpu_count()={os.cpu_count()}"}
-
-
-# ---------------------------------------------------------------- practical HBM ceilings
-def traffic_probe(torch, timer):
-    """The decode kernel's state access pattern with none of its arithmetic (libkda_probe.so):
-    each head state is read and written back in place (decode, B=64 H=32, 8 rotated 128 MiB
-    buffers) or written to five 256 MiB regions (decode_k, B=128 H=32: 4 snapshots + the
-    state).  GB/s of the bytes moved, best of plain and non-temporal accesses."""
-    import ctypes
-    lib = ctypes.CDLL(os.path.join(ROOT, "kda_gated_delta_core_amd", "libkda_probe.so"))
-    lib.probe_state_traffic.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
-                                        ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p]
-    res = {}
-    heads = 64 * 32
-    bufs = [torch.zeros(heads * 16384, device="cuda") for _ in range(8)]
-    best = 0.0
-    for nt in (0, 1):
-        def fn(i, nt=nt):
-            b = bufs[i % 8]
-            assert lib.probe_state_traffic(b.data_ptr(), b.data_ptr(), heads, 1, heads * 16384, nt, None) == 0
-        r = timer.run(fn, 200, 20)
-        best = max(best, 2 * heads * 65536 / r["launch_avg_s"] / 1e9)
-    res["decode_b64_h32_pattern_GB_per_s"] = best
-    del bufs
-    heads = 128 * 32
-    src = torch.zeros(heads * 16384, device="cuda")
-    dst = torch.zeros(5 * heads * 16384, device="cuda")
-    best = 0.0
-    for nt in (0, 1):
-        def fn(i, nt=nt):
-            assert lib.probe_state_traffic(src.data_ptr(), dst.data_ptr(), heads, 5, heads * 16384, nt, None) == 0
-        r = timer.run(fn, 50, 5)
-        best = max(best, 6 * heads * 65536 / r["launch_avg_s"] / 1e9)
-    res["decode_k4_b128_h32_pattern_GB_per_s"] = best
-    for k, v in res.items():
-        log(f"traffic probe {k}: {v:.0f}")
+    res[w.name] = entry(w.batch * reps / el, threads,
+                        f"{reps} full decode steps (B=64, H=32, one token each), {el:.1f} s wall on {threads} threads")
+    # decode_k B=128 H=32 k=4 with 4 snapshots: the whole call
+    w = ki.WORKLOADS["decode_k4_b128_h32"]
+    x = ki.workload_inputs(w)
+    rate, el, th = _oracle_rate(oracle, x, w.batch * w.T, n_snap=w.n_snap)
+    res[w.name] = entry(rate, th, f"one whole call (B=128, H=32, 4 rows, 4 snapshots), {el:.2f} s wall on {th} threads")
+    # prefill T=64 H=2: the whole call
+    w = ki.WORKLOADS["prefill_h2_t64_c16"]
+    x = ki.workload_inputs(w)
+    rate, el, th = _oracle_rate(oracle, x, w.batch * w.T, T=w.T)
+    res[w.name] = entry(rate, th, f"one whole call (T=64, H=2), {el:.4f} s wall on {th} threads")
+    # prefill T=8192 H=32: the whole call (32 independent heads, so at most 32 threads)
+    w = ki.WORKLOADS["prefill_h32_t8192_c64"]
+    x = ki.workload_inputs(w)
+    rate, el, th = _oracle_rate(oracle, x, w.batch * w.T, T=w.T)
+    res[w.name] = entry(rate, th, f"one whole call (T=8192, H=32), {el:.1f} s wall on {th} threads")
+    # prefill 4 x 32768 H=32: the first 4096 tokens of each sequence (an eighth of the call)
+    w = ki.WORKLOADS["prefill_b4_h32_t32768_c64"]
+    Ts = 4096
+    rows = [ki.sequence_rows(w.seed, s, 0, Ts, w.heads, w.gate_lo) for s in range(w.batch)]
+    x = {n: np.ascontiguousarray(np.stack([r[n] for r in rows])) for n in ("q", "k", "v", "gate", "beta")}
+    x["state"] = np.stack([ki.initial_state(w.seed, s, w.heads, w.state_std) for s in range(w.batch)])
+    rate, el, th = _oracle_rate(oracle, x, w.batch * Ts, T=Ts)
+    res[w.name] = entry(rate, th, f"the first {Ts} tokens of each of the 4 sequences, all 32 heads, "
+                                  f"{el:.1f} s wall on {th} threads")
     return res
 
 
@@ -615,8 +620,6 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--copy-probe", action="store_true", help="time a plain 1 GiB device copy kernel (1 GiB read + 1 GiB written per launch) and exit")
     ap.add_argument("--reps", type=int, default=0, help="override the repetitions of every workload (profiling)")
-    ap.add_argument("--traffic-probe", action="store_true",
-                    help="time a traffic-only kernel with the decode and decode_k access patterns and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the core needs no collective and "
@@ -636,10 +639,6 @@ def main():
         # an elementwise kernel (not a runtime blit) so counter collection sees it as a dispatch
         r = timer.run(lambda i: torch.mul(src, 1.0, out=dst), args.reps or 20, 0 if args.reps else 3)
         log(f"copy probe: 1 GiB read + 1 GiB write per launch, {2 * n * 4 / r['launch_avg_s'] / 1e9:.1f} GB/s")
-        return
-
-    if args.traffic_probe:
-        print(json.dumps({"traffic_probe": traffic_probe(torch, timer)}), flush=True)
         return
 
     only = set(filter(None, args.only.split(",")))
@@ -715,7 +714,6 @@ def main():
                                 0 if args.reps else 10, timer, n_fold=7)
         workloads["split_device_b4_h32_t4096_c64"] = {
             "ms_per_call": r["s_per_step"] * 1e3, "device_ms": r["launch_avg_s"] * 1e3,
-            "projected_8_device_tokens_per_s_without_exchange": 4 * 32768 / r["s_per_step"],
             "steps": "transition (records kept) + 7 folds + kda_chunk_scan, one device's share; no exchange"}
     if want("transition_apply_b4_h32"):
         # the fold step for 4 sequences x 32 heads: a device folds the pairs of the segments before its own
@@ -828,8 +826,16 @@ def main():
         })
     line["workloads"] = workloads
     if not args.no_cpu and headline is not None:
-        log("cpu baseline (fp64 oracle)")
-        line["cpu_baseline"] = cpu_baseline(ki)
+        log("cpu baselines (fp64 oracle beside every configuration)")
+        base = cpu_baselines(ki)
+        line["cpu_baseline"] = base["decode_b64_h32"]
+        for name, b in base.items():
+            log(f"oracle {name}: {b['value']:.4g} {b['unit']} ({b['sample']})")
+            if name in workloads:
+                workloads[name]["cpu_oracle"] = b
+                rate = workloads[name].get("tokens_per_s")
+                if rate:
+                    workloads[name]["gpu_over_oracle"] = rate / b["value"]
     print(json.dumps(line), flush=True)
 
 

@@ -10,9 +10,6 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda_amd.so")
 SOURCES = ["kda_api.cpp", "kda_recurrent.hip", "kda_chunk.hip", "kda_norm.hip", "kda_front_end.hip"]
-# measurement tooling, a library of its own (not part of the KDA C ABI)
-PROBE_LIB = os.path.join(PKG, "libkda_probe.so")
-PROBE_SOURCES = ["kda_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -43,12 +40,9 @@ def build(force: bool = True, verbose: bool = False) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     deps = srcs + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
     deps.append(os.path.join(ROOT, "include", "kda.h"))
-    probe_srcs = [os.path.join(CSRC, s) for s in PROBE_SOURCES]
     stale = lambda lib, d: not os.path.exists(lib) or os.path.getmtime(lib) < max(os.path.getmtime(x) for x in d)
     if force or stale(LIB, deps):
         _link(LIB, srcs, verbose)
-    if force or stale(PROBE_LIB, probe_srcs):
-        _link(PROBE_LIB, probe_srcs, verbose)
     return LIB
 
 

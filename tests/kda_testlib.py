@@ -28,10 +28,11 @@ def errors(gpu: np.ndarray, ref: np.ndarray):
     return max_abs, rel
 
 
-def assert_close(name: str, gpu, ref, atol: float = ATOL, rtol: float = RTOL_L2):
+def assert_close(name: str, gpu, ref, atol: float = ATOL, rtol: float = RTOL_L2, quiet: bool = False):
     max_abs, rel = errors(gpu, ref)
     finite = bool(np.isfinite(np.asarray(gpu)).all())
-    print(f"    {name}: max_abs={max_abs:.3e} rel_l2={rel:.3e} finite={finite}", flush=True)
+    if not quiet or not (finite and max_abs <= atol and rel <= rtol):
+        print(f"    {name}: max_abs={max_abs:.3e} rel_l2={rel:.3e} finite={finite}", flush=True)
     assert finite, f"{name}: non-finite values"
     assert max_abs <= atol, f"{name}: max_abs {max_abs:.3e} > {atol}"
     assert rel <= rtol, f"{name}: rel_l2 {rel:.3e} > {rtol}"

@@ -169,29 +169,29 @@ def test_prefill_split_across_calls(device):
 
 
 def test_prefill_h32_t8192_full_size(device):
-    """T=8192, H=32, C=64, pads (one extra chunk too) filled with 1e4; oracle on sampled heads."""
+    """T=8192, H=32, C=64, pads (one extra chunk too) filled with 1e4; every head against the oracle."""
     import kda_gated_delta_core_amd as kda
     w = ki.WORKLOADS["prefill_h32_t8192_c64"]
     announce(f"kda_chunk_prefill {w.name} seed={w.seed} (generating inputs)")
     x = ki.workload_inputs(w)
     announce("running GPU prefill")
     out, st, _ = _prefill(kda, x, w.T, w.chunk)
-    o = host(out)
+    o, s = host(out), host(st)
     assert np.all(o[:, w.T:] == SENTINEL)
-    for h in (0, 13, 31):
-        announce(f"oracle head {h}")
-        sub = {n: np.ascontiguousarray(a[:, :w.T, h:h + 1]) if n != "state" else np.ascontiguousarray(a[:, h:h + 1])
-               for n, a in x.items()}
-        o_ref, s_ref, _, _ = oracle.serial(sub["q"], sub["k"], sub["v"], sub["gate"], sub["beta"], sub["state"])
-        assert_close(f"h{h} core", o[:, :w.T, h:h + 1], o_ref)
-        assert_close(f"h{h} state", host(st)[:, h:h + 1], s_ref)
+    announce("oracle, all 32 heads")
+    o_ref, s_ref, _, _ = oracle.serial(x["q"], x["k"], x["v"], x["gate"], x["beta"], x["state"], T=w.T)
+    assert_close("core", o[:, :w.T], o_ref)
+    assert_close("state", s, s_ref)
+    for h in range(w.heads):  # no head passes on the strength of the others
+        assert_close(f"h{h} core", o[:, :w.T, h], o_ref[:, :, h], quiet=True)
+        assert_close(f"h{h} state", s[:, h], s_ref[:, h], quiet=True)
 
 
-@pytest.mark.timeout(900)
+@pytest.mark.timeout(1200)
 def test_prefill_b4_t32768_then_decode_full_size(device):
     """4 sequences x T=32768, H=32, C=64, gates in [-0.5, 0] (long memory), then 16 decode steps per
-    sequence from the prefilled states (rows T.. of the same streams); the oracle walks one sampled
-    head of each sequence through all T + 16 rows."""
+    sequence from the prefilled states (rows T.. of the same streams); the oracle walks every head of
+    every sequence through all T + 16 rows."""
     import torch
     import kda_gated_delta_core_amd as kda
     w = ki.WORKLOADS["prefill_b4_h32_t32768_c64"]
@@ -214,18 +214,25 @@ def test_prefill_b4_t32768_then_decode_full_size(device):
         outs.append(host(o))
     tail_out = np.concatenate(outs, 1)
     st_end = host(st)
-    for b, h in ((0, 0), (1, 11), (2, 22), (3, 31)):
-        announce(f"oracle sequence {b} head {h}")
-        sub = {n: np.ascontiguousarray(x[n][b:b + 1, :T, h:h + 1]) for n in ("q", "k", "v", "gate", "beta")}
-        o_ref, s_ref, _, _ = oracle.serial(sub["q"], sub["k"], sub["v"], sub["gate"], sub["beta"],
-                                           x["state"][b:b + 1, h:h + 1])
-        o_gpu = out[b:b + 1, :T, h:h + 1].cpu().numpy()
-        assert_close(f"b{b} h{h} core", o_gpu, o_ref)
-        assert_close(f"b{b} h{h} state after prefill", st_pre[b:b + 1, h:h + 1], s_ref)
-        tsub = {n: np.ascontiguousarray(tail[n][b:b + 1, :, h:h + 1]) for n in tail}
+    for b in range(B):
+        announce(f"oracle sequence {b}, all {H} heads")
+        sub = {n: np.ascontiguousarray(x[n][b:b + 1, :T]) for n in ("q", "k", "v", "gate", "beta")}
+        o_ref, s_ref, _, _ = oracle.serial(sub["q"], sub["k"], sub["v"], sub["gate"], sub["beta"], x["state"][b:b + 1])
+        del sub
+        o_gpu = out[b:b + 1, :T].cpu().numpy()
+        assert_close(f"b{b} core", o_gpu, o_ref)
+        assert_close(f"b{b} state after prefill", st_pre[b:b + 1], s_ref)
+        for h in range(H):
+            assert_close(f"b{b} h{h} core", o_gpu[:, :, h], o_ref[:, :, h], quiet=True)
+            assert_close(f"b{b} h{h} state after prefill", st_pre[b:b + 1, h], s_ref[:, h], quiet=True)
+        del o_gpu, o_ref
+        tsub = {n: np.ascontiguousarray(tail[n][b:b + 1]) for n in tail}
         o2, s2, _, _ = oracle.serial(tsub["q"], tsub["k"], tsub["v"], tsub["gate"], tsub["beta"], s_ref)
-        assert_close(f"b{b} h{h} decode tail core", tail_out[b:b + 1, :, h:h + 1], o2)
-        assert_close(f"b{b} h{h} final state", st_end[b:b + 1, h:h + 1], s2)
+        assert_close(f"b{b} decode tail core", tail_out[b:b + 1], o2)
+        assert_close(f"b{b} final state", st_end[b:b + 1], s2)
+        for h in range(H):
+            assert_close(f"b{b} h{h} decode tail core", tail_out[b:b + 1, :, h], o2[:, :, h], quiet=True)
+            assert_close(f"b{b} h{h} final state", st_end[b:b + 1, h], s2[:, h], quiet=True)
 
 
 @pytest.mark.parametrize("B,H,T", [(2, 32, 200), (3, 25, 130)])
@@ -274,8 +281,8 @@ def test_prefill_odd_shapes(device, B, H, T, C):
 
 @pytest.mark.timeout(600)
 def test_prefill_max_heads(device):
-    """KDA_PREFILL_MAX_HEADS heads (the most the header allows) in one call, sampled heads against
-    the oracle."""
+    """KDA_PREFILL_MAX_HEADS heads (the most the header allows) in one call, every head against the
+    oracle."""
     import kda_gated_delta_core_amd as kda
     B, H, T, C = 1, 16384, 20, 16
     announce(f"kda_chunk_prefill max heads B={B} H={H} T={T} C={C}")
@@ -284,9 +291,13 @@ def test_prefill_max_heads(device):
     out, st, _ = _prefill(kda, x, T, C)
     o, s = host(out), host(st)
     assert np.all(o[:, T:] == SENTINEL)
-    sel = [0, 1, 8191, 12345, H - 1]
-    sub = {n: np.ascontiguousarray(a[:, :, sel]) if a.ndim >= 3 and n != "state" else a for n, a in x.items()}
-    sub["state"] = np.ascontiguousarray(x["state"][:, sel])
-    o_ref, s_ref, _, _ = oracle.serial(sub["q"], sub["k"], sub["v"], sub["gate"], sub["beta"], sub["state"], T=T)
-    assert_close("core", o[:, :T][:, :, sel], o_ref)
-    assert_close("state", s[:, sel], s_ref)
+    o_ref, s_ref, _, _ = oracle.serial(x["q"], x["k"], x["v"], x["gate"], x["beta"], x["state"], T=T)
+    assert_close("core", o[:, :T], o_ref)
+    assert_close("state", s, s_ref)
+    # every head within the tolerance on its own (max-abs per head, rel-L2 per head)
+    d = np.abs(o[:, :T].astype(np.float64) - o_ref).max(axis=(0, 1, 3))
+    ds = np.abs(s.astype(np.float64) - s_ref).max(axis=(0, 2, 3))
+    assert d.max() <= 1e-3 and ds.max() <= 1e-3, (int(d.argmax()), float(d.max()), int(ds.argmax()), float(ds.max()))
+    num = np.linalg.norm((o[:, :T].astype(np.float64) - o_ref).transpose(2, 0, 1, 3).reshape(H, -1), axis=1)
+    den = np.linalg.norm(o_ref.transpose(2, 0, 1, 3).reshape(H, -1), axis=1)
+    assert np.all(num <= 1e-4 * den), int(np.argmax(num / den))
