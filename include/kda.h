@@ -128,6 +128,31 @@ int kda_chunk_prefill(const float* q, const float* k, const float* v, const floa
                       size_t workspace_bytes, void* stream);
 
 /*
+ * kda_chunk_prefill for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The chunk records live in a static device array the library
+ * owns, KDA_STATIC_WORKSPACE_BYTES per GPU (held from the first call on that
+ * GPU until the process ends), instead of a caller workspace.  Nothing is
+ * allocated: the first call on a device looks the array's address up once
+ * (hipGetSymbolAddress) and keeps it; later calls reuse it.
+ *
+ *   q, k, v, gate, beta, state, out, batch, heads, T, chunk : as kda_chunk_prefill
+ *
+ * The result equals kda_chunk_prefill's bit for bit (same kernels).  Calls
+ * whose records would exceed the array, i.e. kda_chunk_prefill_workspace_bytes
+ * (batch, heads, T, chunk) > KDA_STATIC_WORKSPACE_BYTES, are refused with
+ * KDA_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU shares
+ * that GPU's array, and the array keeps the last call's records (nothing in
+ * it needs to start at zero): two calls that can run at the same time on one
+ * GPU (different streams, no ordering between them) race on it and give
+ * undefined results; calls ordered on one stream are safe.  Other refusals as
+ * kda_chunk_prefill; KDA_ERR_HIP if the array's address cannot be looked up.
+ */
+#define KDA_STATIC_WORKSPACE_BYTES (256u << 20)
+int kda_chunk_prefill_noalloc(const float* q, const float* k, const float* v, const float* gate, const float* beta,
+                              float* state, float* out, int batch, int heads, int T, int chunk, void* stream);
+
+/*
  * Chunked prefill of a packed batch of sequences of their own lengths
  * (varlen).  Same computation as kda_chunk_prefill for every sequence, with
  * the sequences stored back to back instead of padded to a common length (the

@@ -35,7 +35,8 @@ EXPORTED = ("kda_status_string", "kda_chunk_prefill_workspace_bytes", "kda_chunk
             "kda_chunk_prefill_varlen_workspace_bytes", "kda_chunk_prefill_varlen", "kda_recurrent_k_bf16",
             "kda_recurrent_step_bf16", "kda_decode_front_end_bf16", "kda_prefill_front_end",
             "kda_prefill_front_end_varlen", "kda_chunk_prefill_transition", "kda_state_transition_apply", "kda_chunk_scan",
-            "kda_chunk_prefill_fused", "kda_chunk_prefill_varlen_fused")
+            "kda_chunk_prefill_fused", "kda_chunk_prefill_varlen_fused", "kda_chunk_prefill_noalloc")
+STATIC_WORKSPACE_BYTES = 256 << 20
 GATED_RMSNORM_MIN_EPS = 1e-30
 
 _lib = None
@@ -64,6 +65,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_chunk_prefill_workspace_bytes.restype = sz
     lib.kda_chunk_prefill.argtypes = [p] * 7 + [i] * 4 + [p, sz, p]
     lib.kda_chunk_prefill.restype = i
+    lib.kda_chunk_prefill_noalloc.argtypes = [p] * 7 + [i] * 4 + [p]
+    lib.kda_chunk_prefill_noalloc.restype = i
     lib.kda_recurrent_step.argtypes = [p] * 7 + [i, i, p]
     lib.kda_recurrent_step.restype = i
     lib.kda_recurrent_k.argtypes = [p] * 8 + [i] * 4 + [p]
@@ -271,6 +274,27 @@ def kda_chunk_prefill(q, k, v, gate, beta, state, T: int, chunk: int, out=None, 
                                           _stream_ptr(stream))
     if rc != KDA_OK:
         raise KdaError("kda_chunk_prefill", rc)
+    return out
+
+
+def kda_chunk_prefill_noalloc(q, k, v, gate, beta, state, T: int, chunk: int, out, stream=None):
+    """kda_chunk_prefill with its chunk records in the library's static device array (no workspace,
+    no allocation anywhere; ``out`` must be given).  At most STATIC_WORKSPACE_BYTES of records
+    (kda_chunk_prefill_workspace_bytes); calls that may overlap on one GPU race on the array."""
+    B, rows, H = _vec_shapes(q)
+    if chunk not in (16, 32, 64):
+        raise KdaError("kda_chunk_prefill_noalloc", KDA_ERR_UNSUPPORTED)
+    t_pad = -(-int(T) // chunk) * chunk
+    if rows != t_pad:
+        raise ValueError(f"inputs must hold T_pad = {t_pad} rows per sequence, got {rows}")
+    vs = (B, t_pad, H, HEAD_DIM)
+    args = [_check(n, t, vs) for n, t in (("q", q), ("k", k), ("v", v), ("gate", gate))]
+    args.append(_check("beta", beta, (B, t_pad, H)))
+    args.append(_check("state", state, (B, H, HEAD_DIM, HEAD_DIM)))
+    args.append(_check("out", out, vs))
+    rc = load_library().kda_chunk_prefill_noalloc(*args, B, H, int(T), chunk, _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_chunk_prefill_noalloc", rc)
     return out
 
 

@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kda_internal.h"
 
 #define KDA_API extern "C" __attribute__((visibility("default")))
@@ -110,6 +112,64 @@ KDA_API int kda_chunk_prefill(const float* q, const float* k, const float* v, co
     if (any_overlap(r, 8, 3)) return KDA_ERR_INVALID_ARG;
     const int rc = kda::launch_chunk_prefill(q, k, v, gate, beta, state, out, batch, heads, T, (int)t_pad, chunk,
                                              static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
+    return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+// The chunk records of kda_chunk_prefill_noalloc: a static device array, one
+// copy per GPU at its own address.  In host code `scratch` names a host-side
+// stand-in, never the device memory: every host use goes through the address
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept.
+static __device__ __align__(256) float scratch[KDA_STATIC_WORKSPACE_BYTES / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxDevices];
+
+// this device's copy of `scratch` (looked up on its first use), or nullptr
+float* scratch_address()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch[dev] = static_cast<float*>(p);
+    }
+    return g_scratch[dev];
+}
+
+}  // namespace
+
+KDA_API int kda_chunk_prefill_noalloc(const float* q, const float* k, const float* v, const float* gate,
+                                      const float* beta, float* state, float* out, int batch, int heads, int T,
+                                      int chunk, void* stream)
+{
+    // the argument checks of kda_chunk_prefill, with the array's size in place of a workspace size
+    if (!q || !k || !v || !gate || !beta || !state || !out) return KDA_ERR_INVALID_ARG;
+    if (!aligned({q, k, v, gate, state, out}) || !aligned({beta}, 4)) return KDA_ERR_INVALID_ARG;
+    if (batch < 1 || heads < 1 || T < 1) return KDA_ERR_INVALID_ARG;
+    if (!chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
+    const int64_t need = prefill_ws_bytes(batch, heads, T, chunk);
+    const int64_t t_pad = ((int64_t)T + chunk - 1) / chunk * chunk;
+    const int64_t vec = mul({batch, t_pad, heads, KDA_HEAD_DIM});
+    const int64_t sca = mul({batch, t_pad, heads});
+    const int64_t st = mul({batch, heads, KDA_HEAD_DIM, KDA_HEAD_DIM});
+    if (need < 0 || vec < 0 || sca < 0 || st < 0 || t_pad > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)batch * heads > 0x7fffffffLL / 64) return KDA_ERR_INVALID_ARG;
+    if (heads > KDA_PREFILL_MAX_HEADS) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)batch * heads * (t_pad / chunk) > (1LL << 30)) return KDA_ERR_INVALID_ARG;
+    if (need > (int64_t)KDA_STATIC_WORKSPACE_BYTES) return KDA_ERR_WORKSPACE;
+    const Range r[] = {{out, vec * 4}, {state, st * 4}, {q, vec * 4}, {k, vec * 4},
+                       {v, vec * 4},   {gate, vec * 4}, {beta, sca * 4}};
+    if (any_overlap(r, 7, 2)) return KDA_ERR_INVALID_ARG;
+    float* const ws = scratch_address();
+    if (!ws) return KDA_ERR_HIP;
+    const int rc = kda::launch_chunk_prefill(q, k, v, gate, beta, state, out, batch, heads, T, (int)t_pad, chunk, ws,
+                                             static_cast<hipStream_t>(stream));
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -361,10 +361,37 @@ def test_library_allocates_copies_and_synchronises_nothing():
     hip = {line.split()[-1].split("@")[0] for line in out.splitlines() if "hip" in line.lower()}
     allowed = {"__hipPopCallConfiguration", "__hipPushCallConfiguration", "__hipRegisterFatBinary",
                "__hipRegisterFunction", "__hipUnregisterFatBinary", "hipDeviceGetAttribute", "hipGetDevice",
-               "hipGetLastError", "hipLaunchKernel"}
+               "hipGetLastError", "hipLaunchKernel",
+               # the static records array of kda_chunk_prefill_noalloc: registered, then looked up per device
+               "__hipRegisterVar", "hipGetSymbolAddress"}
     assert hip <= allowed, sorted(hip - allowed)
     for bad in ("Malloc", "Free", "Memcpy", "Memset", "Synchronize", "HostRegister"):
         assert not any(bad in name for name in hip), bad
+
+
+@no_gpu
+def test_prefill_noalloc_refusals(lib):
+    f = lib.kda_chunk_prefill_noalloc
+    for i in range(7):
+        p = list(P[:7])
+        p[i] = None
+        assert f(*p, 1, 2, 64, 16, None) == kda.KDA_ERR_INVALID_ARG
+    assert f(*P[:7], 0, 2, 64, 16, None) == kda.KDA_ERR_INVALID_ARG
+    assert f(*P[:7], 1, 2, 0, 16, None) == kda.KDA_ERR_INVALID_ARG
+    assert f(*P[:7], 1, 2, 64, 48, None) == kda.KDA_ERR_UNSUPPORTED
+    p = list(P[:7])
+    p[6] = P[0] + 64  # out overlapping q
+    assert f(*p, 1, 2, 64, 16, None) == kda.KDA_ERR_INVALID_ARG
+    # records beyond the static array: T=8192, H=32, C=64 needs 673 MB > 256 MiB
+    assert kda.kda_chunk_prefill_workspace_bytes(1, 32, 8192, 64) > kda.STATIC_WORKSPACE_BYTES
+    assert f(*P[:7], 1, 32, 8192, 64, None) == kda.KDA_ERR_WORKSPACE
+    # the largest call that fits (1633 records of 164,352 B at C=64) is not refused for its size: its
+    # size check passes and only the device lookup (no GPU here) can fail
+    rec = 5 * 64 * 128 * 4 + 128 * 4
+    n = kda.STATIC_WORKSPACE_BYTES // rec
+    assert kda.kda_chunk_prefill_workspace_bytes(1, n, 64, 64) <= kda.STATIC_WORKSPACE_BYTES
+    assert kda.kda_chunk_prefill_workspace_bytes(1, n + 1, 64, 64) > kda.STATIC_WORKSPACE_BYTES
+    assert f(*P[:7], 1, n + 1, 64, 64, None) == kda.KDA_ERR_WORKSPACE
 
 
 @no_gpu
