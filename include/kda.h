@@ -114,14 +114,19 @@ size_t kda_chunk_prefill_workspace_bytes(int batch, int heads, int T, int chunk)
  * Rows t >= T of every input may hold anything, NaN and inf included: the
  * kernels select them away before any arithmetic (layer page,
  * prefill_with_pad_fill: positions at or past t are ignored in-kernel).
- * Accuracy: the chunk factorisation splits each pairwise decay
- * exp(G_r - G_s) inside a 16-token block into two FP32 factors taken about
- * the block's eighth row, so a factor can span 8 gates.  Results meet the
- * stated tolerance for every gate >= -9 (tested there); from about -11 on,
- * factors leave the normal FP32 range and the output loses accuracy (the
- * final state does not).  The pages bound the gate from below (config page,
- * gate_lower_bound) without printing the value; the decode entry points
- * have no such limit.
+ * Gate domain: any gate <= 0, -inf included (config page, gate_lower_bound
+ * bounds it from below without printing the value).  Chunks whose gates are
+ * all >= about -8.3 (-12 in log2 units) factor each pairwise decay
+ * exp(G_r - G_s) inside a 16-token block into two FP32 factors about the
+ * block's eighth row; a chunk with a steeper gate takes a second path whose
+ * factors are explicit exponentials of exponent sums <= 0, with two products
+ * on the diagonal blocks, so no factor leaves the FP32 range.  On that path
+ * a gate below about -19.4 (-28 in log2 units) counts as that value: its
+ * decay factor is 2^-28 instead of a smaller one, which moves the state by
+ * less than 2^-28 of its decayed part.  Results agree with the decode entry
+ * points within the stated tolerance for every gate (tested down to -60 and
+ * -inf).  Gates > 0 (growth) are computed as given but are outside this
+ * statement.
  */
 int kda_chunk_prefill(const float* q, const float* k, const float* v, const float* gate, const float* beta,
                       float* state, float* out, int batch, int heads, int T, int chunk, void* workspace,

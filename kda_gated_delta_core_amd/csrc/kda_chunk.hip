@@ -38,9 +38,14 @@
 // each 16-row block (L), so no running sum grows beyond 16 gates.  One pass
 // turns K and Q into tables decayed about row 7 of their own block,
 //   Kr = K o 2^(L - L7),  Qr = Q o 2^(L - L7),  Kc = K o 2^(L7 - L)
-// (each factor spans at most 8 gates, so it stays a normal float for gates
-// down to about -9; below that the diagonal terms flush), with two
-// exponentials per element.
+// (each factor spans at most 8 gates), with two exponentials per element.
+// That keeps every factor a normal float while each gate is >= -12 in log2
+// units; a chunk with a steeper gate (checked while it is staged, so the
+// choice is uniform over the workgroup) takes the steep-gate path instead:
+// K, Q and L stay as they are and each operand is decayed by one exponential
+// of an exponent sum <= 0 (two products, about two reference rows, on the
+// diagonal blocks; see am_below_steep, am_diag_steep), with gates clamped at
+// -kSteepGateClampLog2.
 // Everything else needs only per-channel factors on top of those tables:
 //   diagonal blocks of A, M   Kr Kc^T, Qr Kc^T              (no rescaling)
 //   block pair S < R          (Kr o X_RS)(Kc o Y_S)^T      X_RS = 2^(G7_R - Gend_S),
@@ -264,13 +269,36 @@ __device__ __forceinline__ void prep_load_v(float (&vb)[C / 16][4], rsrc_t src, 
 // chunk goes to LDS (gate in log2 units).
 // kFE: k and q are in the fused row order (rows NV4 (tid / 32) + i), the gate
 // in the usual one.
+// index of block pair (R, S < R) among the pairs below the diagonal
+__device__ __forceinline__ int below_index(int R, int S) { return R * (R - 1) / 2 + S; }
+
+// The decayed tables of the fast path (factors about row 7 of each 16-row
+// block, spanning up to 8 gates) stay inside the normal FP32 range, with room
+// for small key and query components, while every gate of the chunk is at or
+// above -kFastGateLog2 in log2 units (about -8.3 in natural units): 8 gates
+// then span at most 2^96.  A chunk with a steeper gate takes the steep-gate
+// path instead (see chunk_prepare_kernel).
+constexpr float kFastGateLog2 = 12.f;
+// On the steep-gate path every log2 gate below -kSteepGateClampLog2 counts as
+// that value (about -19.4 in natural units): a decay factor of 2^-28 instead of
+// a smaller one, a change below 2^-28 of the decayed state, far under FP32's
+// own rounding of the terms it is added to.  It bounds the factors of the
+// diagonal blocks (4 gates about a reference row) by 2^112.
+constexpr float kSteepGateClampLog2 = 28.f;
+
+// Rows >= T (nvalid and beyond) are replaced by zeros with selects, then the
+// chunk goes to LDS (gate in log2 units).  Each wave also records in
+// sSteep[wave] whether any gate it staged is below -kFastGateLog2 (log2).
+// kFE: k and q are in the fused row order (rows NV4 (tid / 32) + i), the gate
+// in the usual one.
 template <int C, bool kFE = false>
 __device__ __forceinline__ void prep_stage(const PrepInputs<C>& in, float* sK, float* sQ, float* sL, float* sBeta,
-                                           int nvalid, int tid)
+                                           int* sSteep, int nvalid, int tid)
 {
     using G = ChunkGeom<C>;
     constexpr int NV4 = PrepInputs<C>::NV4, LD = G::kLd;
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    bool steep = false;
 #pragma unroll
     for (int i = 0; i < NV4; ++i) {
         const int e = tid + kPrepThreads * i, r = e >> 5, c4 = (e & 31) * 4;
@@ -280,13 +308,90 @@ __device__ __forceinline__ void prep_stage(const PrepInputs<C>& in, float* sK, f
         lds4_st(&sK[rq * LD + c4], okq ? in.k[i] : z4);
         lds4_st(&sQ[rq * LD + c4], okq ? in.q[i] : z4);
         const float4 g = ok ? in.g[i] : z4;
-        lds4_st(&sL[r * LD + c4], make_float4(g.x * kLog2e, g.y * kLog2e, g.z * kLog2e, g.w * kLog2e));
+        const float4 l = make_float4(g.x * kLog2e, g.y * kLog2e, g.z * kLog2e, g.w * kLog2e);
+        steep |= (l.x < -kFastGateLog2) | (l.y < -kFastGateLog2) | (l.z < -kFastGateLog2) | (l.w < -kFastGateLog2);
+        lds4_st(&sL[r * LD + c4], l);
     }
     if (tid < C) sBeta[tid] = tid < nvalid ? in.beta : 0.f;
+    const bool any = __builtin_amdgcn_ballot_w64(steep) != 0;
+    if ((tid & 63) == 0) sSteep[tid >> 6] = any ? 1 : 0;
 }
 
-// index of block pair (R, S < R) among the pairs below the diagonal
-__device__ __forceinline__ int below_index(int R, int S) { return R * (R - 1) / 2 + S; }
+// Steep-gate path.  The LDS tables hold K and Q as staged and L, the
+// block-local cumulative log2 decay (clamped gates), and every operand is
+// decayed by one exponential of an exponent sum, each <= 0 except on the
+// diagonal blocks (below):
+//   pair S < R   row r:    K o 2^(L_r + sX_RS),  sX_RS = sum of the block totals strictly between S and R
+//                column s: K o 2^(sY_S - L_s),   sY_S  = block total of S
+// (both equal the fast path's operands decayed about the last row of block S).
+template <int C, int TAU0, int TAU1>
+__device__ __forceinline__ void am_below_steep(int R, int S, const float* sK, const float* sQ, const float* sL,
+                                               const float* sX, const float* sY, int l16, int q4, floatx4& accA,
+                                               floatx4& accM)
+{
+    constexpr int LD = ChunkGeom<C>::kLd;
+    const int ra = 16 * R + l16, sb = 16 * S + l16;
+    const float* const xv = sX + below_index(R, S) * kD;
+    const float* const yv = sY + S * kD;
+#pragma unroll
+    for (int tau = TAU0; tau < TAU1; ++tau) {
+        const int i0 = 16 * tau + 4 * q4;
+        const float4 kr = lds4(&sK[ra * LD + i0]), qr = lds4(&sQ[ra * LD + i0]), lr = lds4(&sL[ra * LD + i0]);
+        const float4 ks = lds4(&sK[sb * LD + i0]), ls = lds4(&sL[sb * LD + i0]);
+        const float4 x = lds4(&xv[i0]), y = lds4(&yv[i0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float fa = exp2_fast(comp(lr, e) + comp(x, e)), fb = exp2_fast(comp(y, e) - comp(ls, e));
+            const float b = comp(ks, e) * fb;
+            accA = mfma4(comp(kr, e) * fa, b, accA);
+            accM = mfma4(comp(qr, e) * fa, b, accM);
+        }
+    }
+}
+
+// Steep-gate path, diagonal block R: no single reference row keeps both
+// factors of every pair s <= r in range, so two products are taken and
+// selected per element.  Pairs inside one 8-row half use that half's row 3 as
+// the reference (factors span at most 4 gates, so with clamped gates at most
+// 2^112); pairs across the halves (r in rows 8..15, s in rows 0..7) use row 7,
+// the boundary, where both factors are <= 1.  The rows and columns a product
+// must not use are selected to zero; the cross-half elements of the first
+// product can overflow and are discarded by the select.
+template <int C>
+__device__ __forceinline__ void am_diag_steep(int R, const float* sK, const float* sQ, const float* sL, int l16,
+                                              int q4, floatx4& accA, floatx4& accM)
+{
+    constexpr int LD = ChunkGeom<C>::kLd;
+    const int ra = 16 * R + l16, half = l16 >> 3;
+    const int ref = 16 * R + 3 + 8 * half, mid = 16 * R + 7;
+    floatx4 a2 = {0.f, 0.f, 0.f, 0.f}, m2 = {0.f, 0.f, 0.f, 0.f};
+    floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, m1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tau = 0; tau < 8; ++tau) {
+        const int i0 = 16 * tau + 4 * q4;
+        const float4 kr = lds4(&sK[ra * LD + i0]), qr = lds4(&sQ[ra * LD + i0]), lr = lds4(&sL[ra * LD + i0]);
+        const float4 lref = lds4(&sL[ref * LD + i0]), lmid = lds4(&sL[mid * LD + i0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // the A operand is row ra of this lane, the B operand column ra: the same K row
+            const float k = comp(kr, e), q = comp(qr, e), l = comp(lr, e);
+            const float f2a = exp2_fast(l - comp(lref, e)), f2b = exp2_fast(comp(lref, e) - l);
+            const float f1a = half ? exp2_fast(l - comp(lmid, e)) : 0.f;
+            const float f1b = half ? 0.f : exp2_fast(comp(lmid, e) - l);
+            a2 = mfma4(k * f2a, k * f2b, a2);
+            m2 = mfma4(q * f2a, k * f2b, m2);
+            a1 = mfma4(k * f1a, k * f1b, a1);
+            m1 = mfma4(q * f1a, k * f1b, m1);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bool same = ((4 * q4 + e) >> 3) == half;  // row 4 q4 + e and column l16 of the block
+        accA[e] = same ? a2[e] : a1[e];
+        accM[e] = same ? m2[e] : m1[e];
+    }
+}
+
 
 // Partial A and M tile of block pair (R, S <= R) over the channel steps
 // [16 TAU0, 16 TAU1), from the decayed tables: lane l accumulates rows
@@ -611,6 +716,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
     __shared__ float sY[NT * kD];    // 2^(Gend_R - G7_R)
     __shared__ float sX[NX * kD];    // 2^(G7_R - Gend_S), S < R
     __shared__ float sBeta[C];
+    __shared__ int sSteep[NW];       // per wave: a staged gate below -kFastGateLog2 (log2)
 
     const int stride = gridDim.x;
 
@@ -632,7 +738,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         }
         prep_load_part<C>(in.g, src.g, heads, threadIdx.x);
         in.beta = prep_load_beta<C>(src.b, heads, threadIdx.x);
-        prep_stage<C, kFE>(in, sKr, sQr, sKc, sBeta, pos.nvalid, threadIdx.x);
+        prep_stage<C, kFE>(in, sKr, sQr, sKc, sBeta, sSteep, pos.nvalid, threadIdx.x);
     }
     __syncthreads();
 
@@ -660,58 +766,109 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         const ChunkPos npos = gn < n_total ? layout.template chunk<C>(gn) : pos;
         const PrepSrc nsrc = prep_src(q, k, v, gate, beta, npos, gn < n_total);
 
-        // 2. block-local cumulative log2 decay L of each column, then the tables
-        //    decayed about row 7 of the block (L7 and the block totals wait in sE, sF)
-        if (tid < NT * kD) {
-            const int j = tid & (kD - 1), R = tid >> 7;
-            float L[16];
-            float acc = 0.f;
+        // Whether any gate of this chunk is steeper than the fast path's tables allow
+        // (uniform over the workgroup: the staging waves' flags, read into a scalar).
+        int flags = 0;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                acc += sKc[(16 * R + r) * LD + j];
-                L[r] = acc;
-            }
+        for (int w = 0; w < NW; ++w) flags |= sSteep[w];
+        const bool steep = __builtin_amdgcn_readfirstlane(flags) != 0;
+        if (steep) {
+            // 2'. steep gates: L, the block-local cumulative log2 decay of each
+            //     column with every gate clamped at -kSteepGateClampLog2, replaces
+            //     the gates; K and Q stay as staged.  Block totals wait in sE.
+            if (tid < NT * kD) {
+                const int j = tid & (kD - 1), R = tid >> 7;
+                float acc = 0.f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int o = (16 * R + r) * LD + j;
-                const float er = exp2_fast(L[r] - L[7]), ec = exp2_fast(L[7] - L[r]);
-                const float kk = sKr[o];
-                sKr[o] = kk * er;
-                sQr[o] = sQr[o] * er;
-                sKc[o] = kk * ec;
-            }
-            sE[R * kD + j] = L[7];
-            sF[R * kD + j] = L[15];
-        }
-        __syncthreads();
-        //    per-channel factors, each exponent summed from block-local pieces
-        if (tid < kD) {
-            float l7[NT], bl[NT];
-#pragma unroll
-            for (int R = 0; R < NT; ++R) {
-                l7[R] = sE[R * kD + tid];
-                bl[R] = sF[R * kD + tid];
-            }
-            float pre = 0.f;
-#pragma unroll
-            for (int R = 0; R < NT; ++R) {
-                float suf = 0.f;
-#pragma unroll
-                for (int X = R + 1; X < NT; ++X) suf += bl[X];
-                sE[R * kD + tid] = exp2_fast(pre + l7[R]);
-                sF[R * kD + tid] = exp2_fast((bl[R] - l7[R]) + suf);
-                sY[R * kD + tid] = exp2_fast(bl[R] - l7[R]);
-                float mid = 0.f;  // blocks strictly between S and R, summed from R down
-#pragma unroll
-                for (int S = R - 1; S >= 0; --S) {
-                    sX[below_index(R, S) * kD + tid] = exp2_fast(l7[R] + mid);
-                    mid += bl[S];
+                for (int r = 0; r < 16; ++r) {
+                    const int o = (16 * R + r) * LD + j;
+                    const float g = sKc[o];
+                    acc += g < -kSteepGateClampLog2 ? -kSteepGateClampLog2 : g;  // (a NaN gate stays NaN)
+                    sKc[o] = acc;
                 }
-                pre += bl[R];
+                sE[R * kD + j] = acc;
             }
-            rec[G::kOffGam + tid] = exp2_fast(pre);  // gamma = e^{G_last}
+            __syncthreads();
+            //    per-channel exponents (not factors): sE = the block totals before
+            //    R, sF = those from R on (G_last - G_r = sF_R - L_r), sY = block
+            //    total of S, sX = the totals strictly between S and R
+            if (tid < kD) {
+                float bl[NT];
+#pragma unroll
+                for (int R = 0; R < NT; ++R) bl[R] = sE[R * kD + tid];
+                float pre = 0.f, tot = 0.f;
+#pragma unroll
+                for (int R = 0; R < NT; ++R) tot += bl[R];
+#pragma unroll
+                for (int R = 0; R < NT; ++R) {
+                    sE[R * kD + tid] = pre;
+                    sF[R * kD + tid] = tot - pre;
+                    sY[R * kD + tid] = bl[R];
+                    float mid = 0.f;
+#pragma unroll
+                    for (int S = R - 1; S >= 0; --S) {
+                        sX[below_index(R, S) * kD + tid] = mid;
+                        mid += bl[S];
+                    }
+                    pre += bl[R];
+                }
+                rec[G::kOffGam + tid] = exp2_fast(tot);  // gamma = e^{G_last}
+            }
+            __syncthreads();
+        } else {
+            // 2. block-local cumulative log2 decay L of each column, then the tables
+            //    decayed about row 7 of the block (L7 and the block totals wait in sE, sF)
+            if (tid < NT * kD) {
+                const int j = tid & (kD - 1), R = tid >> 7;
+                float L[16];
+                float acc = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    acc += sKc[(16 * R + r) * LD + j];
+                    L[r] = acc;
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int o = (16 * R + r) * LD + j;
+                    const float er = exp2_fast(L[r] - L[7]), ec = exp2_fast(L[7] - L[r]);
+                    const float kk = sKr[o];
+                    sKr[o] = kk * er;
+                    sQr[o] = sQr[o] * er;
+                    sKc[o] = kk * ec;
+                }
+                sE[R * kD + j] = L[7];
+                sF[R * kD + j] = L[15];
+            }
+            __syncthreads();
+            //    per-channel factors, each exponent summed from block-local pieces
+            if (tid < kD) {
+                float l7[NT], bl[NT];
+#pragma unroll
+                for (int R = 0; R < NT; ++R) {
+                    l7[R] = sE[R * kD + tid];
+                    bl[R] = sF[R * kD + tid];
+                }
+                float pre = 0.f;
+#pragma unroll
+                for (int R = 0; R < NT; ++R) {
+                    float suf = 0.f;
+#pragma unroll
+                    for (int X = R + 1; X < NT; ++X) suf += bl[X];
+                    sE[R * kD + tid] = exp2_fast(pre + l7[R]);
+                    sF[R * kD + tid] = exp2_fast((bl[R] - l7[R]) + suf);
+                    sY[R * kD + tid] = exp2_fast(bl[R] - l7[R]);
+                    float mid = 0.f;  // blocks strictly between S and R, summed from R down
+#pragma unroll
+                    for (int S = R - 1; S >= 0; --S) {
+                        sX[below_index(R, S) * kD + tid] = exp2_fast(l7[R] + mid);
+                        mid += bl[S];
+                    }
+                    pre += bl[R];
+                }
+                rec[G::kOffGam + tid] = exp2_fast(pre);  // gamma = e^{G_last}
+            }
+            __syncthreads();
         }
-        __syncthreads();
 
         // 3a. A and M on the 16x16 block pairs (R, S <= R).  Waves 4.. take the
         //     diagonal pairs and, as soon as their block of A is in LDS, invert
@@ -727,7 +884,8 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
             R = S = wave - 4;
             if (R < NT) {
                 floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
-                am_pair<C, 0, 8>(R, S, sKr, sQr, sKc, sX, sY, l16, q4, accA, accM);
+                if (steep) am_diag_steep<C>(R, sKr, sQr, sKc, l16, q4, accA, accM);
+                else am_pair<C, 0, 8>(R, S, sKr, sQr, sKc, sX, sY, l16, q4, accA, accM);
                 am_store<C>(R, S, accA, accM, sA, sM, sBeta, l16, q4);
                 __builtin_amdgcn_wave_barrier();  // the wave reads back the block it wrote
                 if (lane < 16) {
@@ -747,16 +905,20 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         } else if (wave < kBelow) {
             floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
             below_pair(wave, R, S);
-            am_pair<C, 0, 8>(R, S, sKr, sQr, sKc, sX, sY, l16, q4, accA, accM);
+            if (steep) am_below_steep<C, 0, 8>(R, S, sKr, sQr, sKc, sX, sY, l16, q4, accA, accM);
+            else am_pair<C, 0, 8>(R, S, sKr, sQr, sKc, sX, sY, l16, q4, accA, accM);
             am_store<C>(R, S, accA, accM, sA, sM, sBeta, l16, q4);
         }
         floatx4 hA = {0.f, 0.f, 0.f, 0.f}, hM = {0.f, 0.f, 0.f, 0.f};
         const bool split = wave < 2 * kSplit;
         if (split) {
             below_pair(4 + (wave >> 1), R, S);
-            if (wave & 1) am_pair<C, 4, 8>(R, S, sKr, sQr, sKc, sX, sY, l16, q4, hA, hM);
-            else {
-                am_pair<C, 0, 4>(R, S, sKr, sQr, sKc, sX, sY, l16, q4, hA, hM);
+            if (wave & 1) {
+                if (steep) am_below_steep<C, 4, 8>(R, S, sKr, sQr, sKc, sX, sY, l16, q4, hA, hM);
+                else am_pair<C, 4, 8>(R, S, sKr, sQr, sKc, sX, sY, l16, q4, hA, hM);
+            } else {
+                if (steep) am_below_steep<C, 0, 4>(R, S, sKr, sQr, sKc, sX, sY, l16, q4, hA, hM);
+                else am_pair<C, 0, 4>(R, S, sKr, sQr, sKc, sX, sY, l16, q4, hA, hM);
                 sPart[((wave >> 1) * 2 + 0) * 64 + lane] = hA;
                 sPart[((wave >> 1) * 2 + 1) * 64 + lane] = hM;
             }
@@ -764,21 +926,29 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         // 3b. Ktil^T = (e^{G_last - G} o K)^T as A tiles: wave w builds tiles (row
         //     block s of key channels, column block y of chunk rows) for s = w,
         //     one float4 store per lane (lane l: channel 16 s + l%16, rows 16 y + 4(l/16)..)
-#pragma unroll
-        for (int y = 0; y < NT; ++y) {
-            const int i = 16 * wave + l16;
-            const float f = sF[y * kD + i];
-            float4 o;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * y + 4 * q4 + e;
-                const float val = sKc[r * LD + i] * f;
-                if (e == 0) o.x = val;
-                if (e == 1) o.y = val;
-                if (e == 2) o.z = val;
-                if (e == 3) o.w = val;
-            }
+        //     (steep gates: K o 2^(G_last - G_r) directly, sF holding G_last - G at the block start;
+        //     whole loops in each branch, so the fast path carries none of the steep path's work)
+        auto ktil_put = [&](int y, const float4& o) {
             rec_st4(rec + G::kOffKt + ((size_t)(wave * NT + y) * 64 + lane) * 4, o);
+        };
+        if (steep) {
+#pragma unroll
+            for (int y = 0; y < NT; ++y) {
+                const int i = 16 * wave + l16, r = 16 * y + 4 * q4;
+                const float f = sF[y * kD + i];
+                ktil_put(y, make_float4(sKr[r * LD + i] * exp2_fast(f - sKc[r * LD + i]),
+                                        sKr[(r + 1) * LD + i] * exp2_fast(f - sKc[(r + 1) * LD + i]),
+                                        sKr[(r + 2) * LD + i] * exp2_fast(f - sKc[(r + 2) * LD + i]),
+                                        sKr[(r + 3) * LD + i] * exp2_fast(f - sKc[(r + 3) * LD + i])));
+            }
+        } else {
+#pragma unroll
+            for (int y = 0; y < NT; ++y) {
+                const int i = 16 * wave + l16, r = 16 * y + 4 * q4;
+                const float f = sF[y * kD + i];
+                ktil_put(y, make_float4(sKc[r * LD + i] * f, sKc[(r + 1) * LD + i] * f, sKc[(r + 2) * LD + i] * f,
+                                        sKc[(r + 3) * LD + i] * f));
+            }
         }
         __syncthreads();
         // finish the split pairs
@@ -800,16 +970,35 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         //     e^G o Q at the same positions (the accumulator layout of the P tiles)
         float bw[NT][4], bu[NT][4], qh[NT][4];
         if constexpr (kFE) fe_finish_v<C>(fv, vb, pos.t0, q4);
+        //     e^{G_s} at row s_ as a factor on the table: the per-channel 2^(G7) of the block on the
+        //     fast path; on the steep path 2^(G_s) itself, formed from the exponent (sKr, sQr then
+        //     holding K and Q as staged)
+        float ev[NT][4];
+        if (steep) {
+#pragma unroll
+            for (int y = 0; y < NT; ++y)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s_ = 16 * y + 4 * q4 + e, i = 16 * wave + l16;
+                    ev[y][e] = exp2_fast(sE[y * kD + i] + sKc[s_ * LD + i]);
+                }
+        } else {
+#pragma unroll
+            for (int y = 0; y < NT; ++y) {
+                const float f = sE[y * kD + 16 * wave + l16];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ev[y][e] = f;
+            }
+        }
 #pragma unroll
         for (int y = 0; y < NT; ++y)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int s_ = 16 * y + 4 * q4 + e, i = 16 * wave + l16;
                 const float bb = sBeta[s_];
-                const float ev = sE[y * kD + i];
-                bw[y][e] = bb * (sKr[s_ * LD + i] * ev);
+                bw[y][e] = bb * (sKr[s_ * LD + i] * ev[y][e]);
                 bu[y][e] = bb * (s_ < nvalid ? vb[y][e] : 0.f);
-                qh[y][e] = sQr[s_ * LD + i] * ev;
+                qh[y][e] = sQr[s_ * LD + i] * ev[y][e];
             }
 
         // 5. W = T (beta e^G o K) and U = T (beta V) for this wave's 16-column block,
@@ -820,6 +1009,8 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         //    from step 3 until the next chunk is staged: its LDS holds the
         //    wave-private transpose scratch.
         static_assert(C * LD >= NW * 256, "transpose scratch");
+        // (steep gates: step 4c read L from the Kc table, which the transposes now overwrite)
+        if (steep) __syncthreads();
         float* const xpose = sKc + wave * 256;
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (kFE) fe_load_qk<C>(rq, fe, 0, npos, heads, tid, gn < n_total);
@@ -902,7 +1093,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         __syncthreads();
         // stage the next chunk (loaded during this one; after the last chunk the
         // staged copy is unused)
-        prep_stage<C, kFE>(in, sKr, sQr, sKc, sBeta, npos.nvalid, tid);
+        prep_stage<C, kFE>(in, sKr, sQr, sKc, sBeta, sSteep, npos.nvalid, tid);
         pos = npos;
         __syncthreads();
     }

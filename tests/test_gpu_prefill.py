@@ -247,22 +247,54 @@ def test_prefill_wide_column_groups(device, B, H, T):
     _check_against_oracle(x, T, out, st)
 
 
-@pytest.mark.parametrize("C", [16, 64])
-def test_prefill_gate_domain_edges(device, C):
-    """Gates at the edge of the chunked path's stated domain (every gate >= -9): channels at
-    exactly -9 on every row, at 0, alternating runs, gates drawn on [-9, 0]; beta outside
-    [0, 1] as well (any finite beta is allowed)."""
+@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("lo", [-9.0, -12.0, -20.0, -60.0])
+def test_prefill_steep_gates(device, C, lo):
+    """Gates steeper than the fast tables allow (below about -8.3): drawn on [lo, 0], channels at
+    exactly lo on every row, channels with no decay, alternating rows, a head whose first chunk has
+    mild gates (so one call takes both paths), -inf and -1e30 on a few channels, beta outside
+    [0, 1].  Output and state finite and within the tolerance of the fp64 oracle, and the
+    prefill's final state within the tolerance of the decode path walking the same rows."""
+    import torch
     import kda_gated_delta_core_amd as kda
     B, H, T = 2, 3, 150
-    announce(f"kda_chunk_prefill gate-domain edges C={C}")
+    announce(f"kda_chunk_prefill steep gates lo={lo} C={C}")
     t_pad = -(-T // C) * C
-    x = ki.make_batch(8100 + C, B, H, T, -9.0, 0.02, alloc_rows=t_pad, pad_value=-1e30)
-    x["gate"][0, :T, :, :16] = -9.0           # strongest decay allowed, every row
+    x = ki.make_batch(8200 + C, B, H, T, lo, 0.02, alloc_rows=t_pad, pad_value=-1e30)
+    mild = ki.make_batch(8300 + C, B, H, T, -5.0, 0.02)["gate"]
+    x["gate"][0, :T, :, :16] = lo             # the steepest decay on every row
     x["gate"][0, :T, :, 16:32] = 0.0          # no decay
-    x["gate"][1, :T:2, 1, :] = -9.0           # alternating strong / drawn decay
-    x["gate"][1, :T, 2, 64:] = -9.0
+    x["gate"][1, :T:2, 1, :] = lo             # alternating steep / drawn rows
+    x["gate"][1, :C, 2, :] = mild[1, :C, 2]   # a first chunk on the fast path, steep chunks after it
+    x["gate"][1, :T, 0, 100:104] = -np.inf
+    x["gate"][1, :T, 0, 104:108] = -1e30
     x["beta"][1, :T, 2] = 1.7
     x["beta"][0, :T, 1] = -0.3
+    out, st, _ = _prefill(kda, x, T, C)
+    _check_against_oracle(x, T, out, st)
+    # the decode path over the same rows ends in the same state
+    sl = lambda a: dev(np.ascontiguousarray(a[:, :T]))
+    st2 = dev(x["state"])
+    o2 = kda.kda_recurrent_k(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["gate"]), sl(x["beta"]), st2)
+    torch.cuda.synchronize()
+    assert_close("prefill vs decode state", host(st), host(st2))
+    assert_close("prefill vs decode out", host(out)[:, :T], host(o2))
+
+
+@pytest.mark.parametrize("C", [16, 64])
+def test_prefill_gates_at_the_fast_bound(device, C):
+    """Gates on both sides of the switch between the paths, by head: -8.0 on every row (the fast
+    tables at 92 of their 96 bits of range, 8 x 8.0 x log2 e), -8.5 on every row (past the bound,
+    steep path), and the two alternating; all within the tolerance of the oracle."""
+    import kda_gated_delta_core_amd as kda
+    B, H, T = 1, 4, 2 * C + 5
+    announce(f"kda_chunk_prefill gates at the fast bound C={C}")
+    t_pad = -(-T // C) * C
+    x = ki.make_batch(8400 + C, B, H, T, -5.0, 0.02, alloc_rows=t_pad, pad_value=float("nan"))
+    x["gate"][0, :T, 0] = -8.0
+    x["gate"][0, :T, 1] = -8.5
+    x["gate"][0, :T, 2] = -8.0
+    x["gate"][0, :T:2, 2] = -8.5
     out, st, _ = _prefill(kda, x, T, C)
     _check_against_oracle(x, T, out, st)
 

@@ -63,12 +63,14 @@ def test_transition_matches_oracle(device, B, H, T, C):
     _check_contract(x, T, P, Q, 7001)
 
 
-@pytest.mark.parametrize("T,C", [(100, 16), (130, 64), (333, 32)])
-def test_transition_steep_gates(device, T, C):
+@pytest.mark.parametrize("T,C,lo", [(100, 16, -5.0), (130, 64, -5.0), (333, 32, -5.0), (130, 64, -15.0),
+                                    (100, 16, -40.0)])
+def test_transition_steep_gates(device, T, C, lo):
+    """gates drawn down to -5, and down to -15 and -40 (the prefill's steep-gate path)"""
     import kda_gated_delta_core_amd as kda
     B, H = 2, 3
-    announce(f"kda_chunk_prefill_transition B={B} H={H} T={T} C={C} gates to -5")
-    x = ki.make_batch(7050 + T, B, H, T, -5.0, 0.02)
+    announce(f"kda_chunk_prefill_transition B={B} H={H} T={T} C={C} gates to {lo}")
+    x = ki.make_batch(7050 + T + int(-lo), B, H, T, lo, 0.02)
     P, Q = _transition(kda, _padded(x, 0, T, C), T, C)
     P_ref, Q_ref = oracle.transition(x["q"], x["k"], x["v"], x["gate"], x["beta"])
     assert_close("Q", host(Q), Q_ref)
