@@ -20,6 +20,10 @@ scale invariance and unit mean square (tests/test_oracle_norm_pins.py).
 against the state the recurrence reaches from random initial states, the explicit product of the
 per-row factors, the matrix determinant lemma, composition of segments and the beta = 0 closed form
 (tests/test_oracle_transition_pins.py).
+``sigmoid`` is pinned against torch.sigmoid in fp64 and closed forms; ``kda_gate`` (a reading of a
+step whose formula the pages do not print: parity unpinned against the pages) is pinned against
+closed forms of that reading, its bounds and the per-head / per-channel broadcast of its parameters
+(tests/test_oracle_gate_pins.py).
 """
 from __future__ import annotations
 
@@ -155,6 +159,39 @@ def bf16_to_f64(bits) -> np.ndarray:
     """BF16 bit patterns to float64: a BF16 value is the upper 16 bits of an IEEE float32."""
     u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
     return u.view(np.float32).astype(np.float64)
+
+
+def sigmoid(x) -> np.ndarray:
+    """1 / (1 + e^-x) in fp64 (workspace page, field beta: the core takes beta already passed through a
+    sigmoid; module page, pipeline line: beta = sigmoid(b_proj(h))).  Written as e^x / (1 + e^x) for
+    negative x so that neither sign overflows; sigmoid(+inf) = 1, sigmoid(-inf) = 0, NaN stays NaN."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+    e = np.exp(x[~pos])
+    out[~pos] = e / (1.0 + e)
+    return out
+
+
+def kda_gate(g_raw_bits, dt_bias, a_log, lower_bound: float) -> np.ndarray:
+    """The gate, fp64, from its inputs (workspace page, field gate: the bounded log-decay kda_gate
+    produces; field g_raw: f_b(f_a(h)), [T, heads * head_dim] BF16, what kda_gate consumes; config
+    page, Glm5NextKdaWeights::dt_bias [heads * head_dim] F32 and a_log [heads] F32, and
+    Glm5NextKdaConfig::gate_lower_bound).  The pages print no formula; the reading taken is
+
+        gate[b, t, h, i] = lower_bound * sigmoid(exp(a_log[h]) * (g_raw[b, t, h, i] + dt_bias[h, i]))
+
+    a per-channel bias, a per-head positive rate exp(a_log) and a sigmoid that bounds the log-decay
+    to (lower_bound, 0) for lower_bound < 0.  Parity unpinned against the pages (no printed formula
+    or value); the pins check this reading.  g_raw_bits: BF16 patterns [B][T][H][D]; dt_bias
+    [H][D] (or [H * D]); a_log [H]; lower_bound widened from float32 as the C ABI takes it."""
+    g = bf16_to_f64(g_raw_bits)
+    B, T, H, D = g.shape
+    dt = np.asarray(dt_bias, dtype=np.float64).reshape(H, D)
+    rate = np.exp(np.asarray(a_log, dtype=np.float64).reshape(H))
+    lo = float(np.float32(lower_bound))
+    return lo * sigmoid(rate[None, None, :, None] * (g + dt[None, None]))
 
 
 def gated_rmsnorm(core, out_gate_bits, o_norm_bits, eps: float) -> np.ndarray:
