@@ -85,13 +85,32 @@ def prefill_bytes(B: int, H: int, T: int) -> int:
 class Timer:
     """K back-to-back launches between device synchronisations: wall clock for the step time,
     and one pair of HIP events on the launch stream around the K launches for the average
-    launch duration (no event commands between launches, so the kernels run back to back)."""
+    launch duration (no event commands between launches, so the kernels run back to back).
 
-    def __init__(self, torch):
+    Before the W warm-up steps each workload runs untimed for at least PREWARM_S of wall time: after
+    a switch of workload the device takes a few hundred milliseconds to settle (decode_k measured
+    364 us per call after 5 warm-up calls, 299 us after 2000), and the timed steps are meant to see
+    the steady state a serving loop runs in."""
+
+    def __init__(self, torch, prewarm_s: float = 0.3):
         self.torch = torch
+        self.PREWARM_S = prewarm_s
+
+    def prewarm(self, fn):
+        torch = self.torch
+        t0, i = time.perf_counter(), 0
+        while True:
+            for _ in range(8):
+                fn(i)
+                i += 1
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= self.PREWARM_S or i >= 100000:
+                return i
 
     def run(self, fn, steps: int, warmup: int):
         torch = self.torch
+        if self.PREWARM_S > 0:
+            self.prewarm(fn)
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
@@ -139,6 +158,60 @@ def bench_decode(torch, kda, ki, steps, warmup, timer, bf16=False):
     r = timer.run(step, steps, warmup)
     nbytes = decode_bytes(B, H, qkv_bytes=2 if bf16 else 4)
     return w, r, nbytes, n_buf
+
+
+def decode_bytes_gated(B: int, H: int, T: int = 1) -> int:
+    """The gated decode step: state read + write, q, k, v read, g_raw read (BF16), out written, beta logit
+    read, and dt_bias + a_log read once per call."""
+    return B * H * (2 * STATE_BYTES + T * (3 * D * 4 + D * 2 + D * 4 + 4)) + H * (D * 4 + 4)
+
+
+def bench_decode_gated(torch, kda, ki, steps, warmup, timer):
+    """kda_recurrent_step_gated at B=64 H=32: the gate (kda_gate of BF16 g_raw) and beta (sigmoid of the
+    logit) formed in the decode kernel; states rotated over >= 1 GiB as for the plain step."""
+    import numpy as np
+    w = ki.WORKLOADS["decode_b64_h32"]
+    B, H = w.batch, w.heads
+    x = ki.workload_inputs(w)
+    gx = ki.gate_inputs(1013, B, 1, H)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q, k, v = (dev(x[n]) for n in ("q", "k", "v"))
+    g = torch.from_numpy(gx["g_raw"].view(np.int16)).view(torch.bfloat16).cuda()
+    bl, dt, al = dev(gx["beta_logit"]), dev(gx["dt_bias"]), dev(gx["a_log"])
+    n_buf = max(2, -(-(1 << 30) // (B * H * STATE_BYTES)))
+    states = [dev(x["state"]) for _ in range(n_buf)]
+    out = torch.empty((B, 1, H, D), device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        kda.kda_recurrent_step_gated(q, k, v, g, bl, dt, al, ki.GATE_LOWER_BOUND, states[i % n_buf], out=out,
+                                     stream=stream)
+
+    r = timer.run(step, steps, warmup)
+    return w, r, decode_bytes_gated(B, H)
+
+
+def bench_prefill_gated(torch, kda, ki, steps, warmup, timer):
+    """kda_chunk_prefill_gated at T=8192 H=32 C=64: the T=8192 prefill workload's q, k, v and state with
+    the gate inputs of its shape (gate and beta formed in the prepare)."""
+    import numpy as np
+    w = ki.WORKLOADS["prefill_h32_t8192_c64"]
+    B, H, T, C = w.batch, w.heads, w.T, w.chunk
+    t_pad = -(-T // C) * C
+    x = ki.workload_inputs(w)
+    gx = ki.gate_inputs(1012, B, t_pad, H)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q, k, v = (dev(x[n][:, :t_pad]) for n in ("q", "k", "v"))
+    g = torch.from_numpy(gx["g_raw"].view(np.int16)).view(torch.bfloat16).cuda()
+    bl, dt, al = dev(gx["beta_logit"]), dev(gx["dt_bias"]), dev(gx["a_log"])
+    st = dev(x["state"])
+    out = torch.empty((B, t_pad, H, D), device="cuda")
+    ws = torch.empty(kda.kda_chunk_prefill_workspace_bytes(B, H, T, C), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        kda.kda_chunk_prefill_gated(q, k, v, g, bl, dt, al, ki.GATE_LOWER_BOUND, st, T, C, out=out, workspace=ws)
+
+    return w, timer.run(step, steps, warmup)
 
 
 def bench_decode_k(torch, kda, ki, steps, warmup, timer, bf16=False):
@@ -287,9 +360,11 @@ def bench_decode_chain(torch, kda, ki, reps):
     with torch.cuda.graph(graph):
         for z in sets:
             chain(z)
-    for _ in range(3):
-        graph.replay()
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.3:  # untimed, past the device's settling after a switch of workload
+        for _ in range(4):
+            graph.replay()
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -631,7 +706,7 @@ def main():
     import kda_inputs as ki
 
     kda.load_library()
-    timer = Timer(torch)
+    timer = Timer(torch, prewarm_s=0.0 if args.reps else 0.3)  # (profiling runs: only the counted calls)
     if args.copy_probe:
         n = 1 << 28  # 1 GiB of fp32
         src = torch.randn(n, device="cuda")
@@ -678,6 +753,24 @@ def main():
                                                 "us_per_call": r["s_per_step"] * 1e6,
                                                 "kernel_us": r["launch_avg_s"] * 1e6, "GB_per_s": gbs,
                                                 "hbm_frac": gbs / HBM_PEAK_GBS}
+    # the gate (kda_gate of BF16 g_raw) and beta (sigmoid of the logit) formed inside the core kernels
+    if want("decode_gated_b64_h32"):
+        log("decode_gated_b64_h32")
+        w, r, nbytes = bench_decode_gated(torch, kda, ki, args.reps or args.steps, args.warmup, timer)
+        gbs = nbytes / r["launch_avg_s"] / 1e9
+        workloads["decode_gated_b64_h32"] = {"tokens_per_s": w.batch / r["s_per_step"],
+                                             "us_per_step": r["s_per_step"] * 1e6,
+                                             "kernel_us": r["launch_avg_s"] * 1e6, "GB_per_s": gbs,
+                                             "hbm_frac": gbs / HBM_PEAK_GBS}
+    if want("prefill_gated_h32_t8192_c64"):
+        log("prefill_gated_h32_t8192_c64")
+        w, r = bench_prefill_gated(torch, kda, ki, args.reps or 20, 0 if args.reps else 60, timer)
+        tf = prefill_flops(w.batch, w.heads, w.T, w.chunk) / r["launch_avg_s"] / 1e12
+        workloads["prefill_gated_h32_t8192_c64"] = {"tokens_per_s": w.batch * w.T / r["s_per_step"],
+                                                    "ms_per_call": r["s_per_step"] * 1e3,
+                                                    "call_ms": r["launch_avg_s"] * 1e3,
+                                                    "algorithmic_TFLOP_per_s": tf,
+                                                    "mfma_frac": tf / MFMA_F32_PEAK_TFLOPS}
     # (timed calls, untimed warm-up calls): once the T=8192 prefill starts, its calls run up to 30%
     # slower for ~15 ms (a device-level transient: the first few calls are fast, then the time rises
     # and settles back over ~30 calls), so it gets 60 untimed calls before the timed ones

@@ -158,6 +158,40 @@ int kda_chunk_prefill_noalloc(const float* q, const float* k, const float* v, co
                               float* state, float* out, int batch, int heads, int T, int chunk, void* stream);
 
 /*
+ * kda_chunk_prefill with the block's gate and beta steps inside the prefill's
+ * prepare kernel: the gate comes from kda_gate of its projection g_raw and
+ * beta from the sigmoid of its logit, both computed while a chunk is staged,
+ * so neither the FP32 gate nor beta travels through HBM (workspace page,
+ * field gate: the bounded log-decay kda_gate makes from g_raw; field beta:
+ * already passed through a sigmoid; module page, pipeline line: beta =
+ * sigmoid(b_proj(h)); config page, Glm5NextKdaWeights::dt_bias, a_log and
+ * Glm5NextKdaConfig::gate_lower_bound).  The pages name kda_gate's inputs but
+ * print no formula; the reading implemented is
+ *
+ *     gate[b][t][h][i] = gate_lower_bound * sigmoid(exp(a_log[h]) * (g_raw[b][t][h][i] + dt_bias[h][i]))
+ *     beta[b][t][h]    = sigmoid(beta_logit[b][t][h])
+ *
+ * in FP32 (hardware exp2 and reciprocal, each within about one unit in the
+ * last place), a log-decay in [gate_lower_bound, 0].
+ *
+ *   q, k, v, state, out, workspace : as kda_chunk_prefill
+ *   g_raw            : [batch][T_pad][heads][128] BF16 (raw 16-bit patterns), 8-byte aligned
+ *   beta_logit       : [batch][T_pad][heads] FP32
+ *   dt_bias          : [heads][128] FP32 (the config page's [heads * head_dim]), 16-byte aligned
+ *   a_log            : [heads] FP32
+ *   gate_lower_bound : finite and <= 0 (else KDA_ERR_INVALID_ARG)
+ *
+ * Rows t >= T of every input are ignored, as for kda_chunk_prefill.  The
+ * result equals kda_chunk_prefill fed with the gate and beta above within
+ * the stated tolerance (the same kernels after the staging).  Refusals as
+ * kda_chunk_prefill, plus a null, misaligned or overlapping gate input.
+ */
+int kda_chunk_prefill_gated(const float* q, const float* k, const float* v, const uint16_t* g_raw,
+                            const float* beta_logit, const float* dt_bias, const float* a_log, float gate_lower_bound,
+                            float* state, float* out, int batch, int heads, int T, int chunk, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * Chunked prefill of a packed batch of sequences of their own lengths
  * (varlen).  Same computation as kda_chunk_prefill for every sequence, with
  * the sequences stored back to back instead of padded to a common length (the
@@ -334,6 +368,24 @@ int kda_recurrent_step(const float* q, const float* k, const float* v, const flo
 int kda_recurrent_k(const float* q, const float* k, const float* v, const float* gate, const float* beta,
                     float* state, float* out, float* snapshots, int n_snapshots, int batch, int heads, int T,
                     void* stream);
+
+/*
+ * The two decode entry points above with the gate and beta steps inside the
+ * decode kernel's row loads: gate = kda_gate(g_raw) and beta =
+ * sigmoid(beta_logit), the reading and arguments of kda_chunk_prefill_gated
+ * (g_raw [batch][T][heads][128] BF16, beta_logit [batch][T][heads] FP32,
+ * dt_bias [heads][128], a_log [heads], gate_lower_bound finite and <= 0).
+ * Everything else as kda_recurrent_k / kda_recurrent_step; T rows of
+ * kda_recurrent_k_gated equal T successive kda_recurrent_step_gated calls
+ * bit for bit (the same kernel).
+ */
+int kda_recurrent_k_gated(const float* q, const float* k, const float* v, const uint16_t* g_raw,
+                          const float* beta_logit, const float* dt_bias, const float* a_log, float gate_lower_bound,
+                          float* state, float* out, float* snapshots, int n_snapshots, int batch, int heads, int T,
+                          void* stream);
+int kda_recurrent_step_gated(const float* q, const float* k, const float* v, const uint16_t* g_raw,
+                             const float* beta_logit, const float* dt_bias, const float* a_log,
+                             float gate_lower_bound, float* state, float* out, int batch, int heads, void* stream);
 
 /*
  * The two decode entry points above with BF16 q, k, v packed per token, as

@@ -35,7 +35,8 @@ EXPORTED = ("kda_status_string", "kda_chunk_prefill_workspace_bytes", "kda_chunk
             "kda_chunk_prefill_varlen_workspace_bytes", "kda_chunk_prefill_varlen", "kda_recurrent_k_bf16",
             "kda_recurrent_step_bf16", "kda_decode_front_end_bf16", "kda_prefill_front_end",
             "kda_prefill_front_end_varlen", "kda_chunk_prefill_transition", "kda_state_transition_apply", "kda_chunk_scan",
-            "kda_chunk_prefill_fused", "kda_chunk_prefill_varlen_fused", "kda_chunk_prefill_noalloc")
+            "kda_chunk_prefill_fused", "kda_chunk_prefill_varlen_fused", "kda_chunk_prefill_noalloc",
+            "kda_chunk_prefill_gated", "kda_recurrent_k_gated", "kda_recurrent_step_gated")
 STATIC_WORKSPACE_BYTES = 256 << 20
 GATED_RMSNORM_MIN_EPS = 1e-30
 
@@ -67,6 +68,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_chunk_prefill.restype = i
     lib.kda_chunk_prefill_noalloc.argtypes = [p] * 7 + [i] * 4 + [p]
     lib.kda_chunk_prefill_noalloc.restype = i
+    f = ctypes.c_float
+    lib.kda_chunk_prefill_gated.argtypes = [p] * 7 + [f, p, p] + [i] * 4 + [p, sz, p]
+    lib.kda_chunk_prefill_gated.restype = i
+    lib.kda_recurrent_k_gated.argtypes = [p] * 7 + [f, p, p, p] + [i] * 4 + [p]
+    lib.kda_recurrent_k_gated.restype = i
+    lib.kda_recurrent_step_gated.argtypes = [p] * 7 + [f, p, p] + [i, i, p]
+    lib.kda_recurrent_step_gated.restype = i
     lib.kda_recurrent_step.argtypes = [p] * 7 + [i, i, p]
     lib.kda_recurrent_step.restype = i
     lib.kda_recurrent_k.argtypes = [p] * 8 + [i] * 4 + [p]
@@ -295,6 +303,85 @@ def kda_chunk_prefill_noalloc(q, k, v, gate, beta, state, T: int, chunk: int, ou
     rc = load_library().kda_chunk_prefill_noalloc(*args, B, H, int(T), chunk, _stream_ptr(stream))
     if rc != KDA_OK:
         raise KdaError("kda_chunk_prefill_noalloc", rc)
+    return out
+
+
+def _gate_args(g_raw, beta_logit, dt_bias, a_log, B, rows, H):
+    return [_check("g_raw", g_raw, (B, rows, H, HEAD_DIM), torch.bfloat16),
+            _check("beta_logit", beta_logit, (B, rows, H)),
+            _check("dt_bias", dt_bias, (H, HEAD_DIM)),
+            _check("a_log", a_log, (H,))]
+
+
+def kda_chunk_prefill_gated(q, k, v, g_raw, beta_logit, dt_bias, a_log, gate_lower_bound: float, state, T: int,
+                            chunk: int, out=None, workspace=None, stream=None):
+    """kda_chunk_prefill with gate = kda_gate(g_raw) and beta = sigmoid(beta_logit) formed inside the
+    prefill.  g_raw: [B][T_pad][H][128] bfloat16; beta_logit: [B][T_pad][H]; dt_bias: [H][128];
+    a_log: [H]; the rest as kda_chunk_prefill.  Returns ``out``."""
+    B, rows, H = _vec_shapes(q)
+    if chunk not in (16, 32, 64):
+        raise KdaError("kda_chunk_prefill_gated", KDA_ERR_UNSUPPORTED)
+    t_pad = -(-int(T) // chunk) * chunk
+    if rows != t_pad:
+        raise ValueError(f"inputs must hold T_pad = {t_pad} rows per sequence, got {rows}")
+    vs = (B, t_pad, H, HEAD_DIM)
+    if out is None:
+        out = torch.empty(vs, dtype=torch.float32, device=q.device)
+    need = kda_chunk_prefill_workspace_bytes(B, H, int(T), chunk)
+    if workspace is None:
+        workspace = _workspace(need, q.device, stream)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    qkv = [_check(n, t, vs) for n, t in (("q", q), ("k", k), ("v", v))]
+    g, b, dt, al = _gate_args(g_raw, beta_logit, dt_bias, a_log, B, t_pad, H)
+    rc = load_library().kda_chunk_prefill_gated(*qkv, g, b, dt, al, float(gate_lower_bound),
+                                                _check("state", state, (B, H, HEAD_DIM, HEAD_DIM)),
+                                                _check("out", out, vs), B, H, int(T), chunk, workspace.data_ptr(),
+                                                ws_bytes, _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_chunk_prefill_gated", rc)
+    return out
+
+
+def kda_recurrent_k_gated(q, k, v, g_raw, beta_logit, dt_bias, a_log, gate_lower_bound: float, state, out=None,
+                          snapshots=None, n_snapshots: int = 0, stream=None):
+    """kda_recurrent_k with gate = kda_gate(g_raw) and beta = sigmoid(beta_logit) formed in the decode
+    kernel.  g_raw: [B][T][H][128] bfloat16; beta_logit: [B][T][H]; dt_bias: [H][128]; a_log: [H]."""
+    B, T, H = _vec_shapes(q)
+    vs = (B, T, H, HEAD_DIM)
+    if out is None:
+        out = torch.empty(vs, dtype=torch.float32, device=q.device)
+    qkv = [_check(n, t, vs) for n, t in (("q", q), ("k", k), ("v", v))]
+    g, b, dt, al = _gate_args(g_raw, beta_logit, dt_bias, a_log, B, T, H)
+    snap_ptr = None
+    if n_snapshots:
+        if snapshots is None or snapshots.dim() != 5 or snapshots.shape[0] < n_snapshots:
+            raise ValueError("snapshots must be [>= n_snapshots][B][H][128][128]")
+        snap_ptr = _check("snapshots", snapshots, (snapshots.shape[0], B, H, HEAD_DIM, HEAD_DIM))
+    rc = load_library().kda_recurrent_k_gated(*qkv, g, b, dt, al, float(gate_lower_bound),
+                                              _check("state", state, (B, H, HEAD_DIM, HEAD_DIM)),
+                                              _check("out", out, vs), snap_ptr, int(n_snapshots), B, H, T,
+                                              _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_recurrent_k_gated", rc)
+    return out
+
+
+def kda_recurrent_step_gated(q, k, v, g_raw, beta_logit, dt_bias, a_log, gate_lower_bound: float, state, out=None,
+                             stream=None):
+    """One decode step with the gate and beta formed in the kernel (kda_recurrent_k_gated with T = 1)."""
+    B, rows, H = _vec_shapes(q)
+    if rows != 1:
+        raise ValueError("kda_recurrent_step_gated takes one row per sequence")
+    vs = (B, 1, H, HEAD_DIM)
+    if out is None:
+        out = torch.empty(vs, dtype=torch.float32, device=q.device)
+    qkv = [_check(n, t, vs) for n, t in (("q", q), ("k", k), ("v", v))]
+    g, b, dt, al = _gate_args(g_raw, beta_logit, dt_bias, a_log, B, 1, H)
+    rc = load_library().kda_recurrent_step_gated(*qkv, g, b, dt, al, float(gate_lower_bound),
+                                                 _check("state", state, (B, H, HEAD_DIM, HEAD_DIM)),
+                                                 _check("out", out, vs), B, H, _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_recurrent_step_gated", rc)
     return out
 
 

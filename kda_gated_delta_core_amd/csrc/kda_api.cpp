@@ -8,6 +8,7 @@
 
 #include <mutex>
 
+#include "kda_common.h"
 #include "kda_internal.h"
 
 #define KDA_API extern "C" __attribute__((visibility("default")))
@@ -58,6 +59,14 @@ bool aligned(std::initializer_list<const void*> ps, uintptr_t a = 16)
 }
 
 bool chunk_ok(int chunk) { return chunk == 16 || chunk == 32 || chunk == 64; }
+
+// the gate inputs of the *_gated entry points: g_raw [rows][heads][128] BF16 (8-byte aligned),
+// dt_bias [heads][128] (16-byte aligned), a_log [heads], a finite lower bound <= 0
+bool gate_inputs_ok(const uint16_t* g_raw, const float* dt_bias, const float* a_log, float lower)
+{
+    return g_raw && dt_bias && a_log && aligned({g_raw}, 8) && aligned({dt_bias}) && aligned({a_log}, 4) &&
+           isfinite(lower) && lower <= 0.f;
+}
 
 int64_t prefill_ws_bytes(int batch, int heads, int T, int chunk)
 {
@@ -112,6 +121,38 @@ KDA_API int kda_chunk_prefill(const float* q, const float* k, const float* v, co
     if (any_overlap(r, 8, 3)) return KDA_ERR_INVALID_ARG;
     const int rc = kda::launch_chunk_prefill(q, k, v, gate, beta, state, out, batch, heads, T, (int)t_pad, chunk,
                                              static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
+    return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+KDA_API int kda_chunk_prefill_gated(const float* q, const float* k, const float* v, const uint16_t* g_raw,
+                                    const float* beta_logit, const float* dt_bias, const float* a_log,
+                                    float gate_lower_bound, float* state, float* out, int batch, int heads, int T,
+                                    int chunk, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!q || !k || !v || !beta_logit || !state || !out) return KDA_ERR_INVALID_ARG;
+    if (!gate_inputs_ok(g_raw, dt_bias, a_log, gate_lower_bound)) return KDA_ERR_INVALID_ARG;
+    if (!aligned({q, k, v, state, out, workspace}) || !aligned({beta_logit}, 4)) return KDA_ERR_INVALID_ARG;
+    if (batch < 1 || heads < 1 || T < 1) return KDA_ERR_INVALID_ARG;
+    if (!chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
+    const int64_t need = prefill_ws_bytes(batch, heads, T, chunk);
+    const int64_t t_pad = ((int64_t)T + chunk - 1) / chunk * chunk;
+    const int64_t vec = mul({batch, t_pad, heads, KDA_HEAD_DIM});
+    const int64_t sca = mul({batch, t_pad, heads});
+    const int64_t st = mul({batch, heads, KDA_HEAD_DIM, KDA_HEAD_DIM});
+    if (need < 0 || vec < 0 || sca < 0 || st < 0 || t_pad > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)batch * heads > 0x7fffffffLL / 64) return KDA_ERR_INVALID_ARG;
+    if (heads > KDA_PREFILL_MAX_HEADS) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)batch * heads * (t_pad / chunk) > (1LL << 30)) return KDA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < (size_t)need) return KDA_ERR_WORKSPACE;
+    const Range r[] = {{out, vec * 4},        {state, st * 4},          {workspace, need},
+                       {q, vec * 4},          {k, vec * 4},             {v, vec * 4},
+                       {g_raw, vec * 2},      {beta_logit, sca * 4},    {dt_bias, (int64_t)heads * KDA_HEAD_DIM * 4},
+                       {a_log, (int64_t)heads * 4}};
+    if (any_overlap(r, 10, 3)) return KDA_ERR_INVALID_ARG;
+    const kda::GateParams gp{reinterpret_cast<const unsigned short*>(g_raw), dt_bias, a_log, gate_lower_bound};
+    const int rc = kda::launch_chunk_prefill_gated(q, k, v, beta_logit, gp, state, out, batch, heads, T, (int)t_pad,
+                                                   chunk, static_cast<float*>(workspace),
+                                                   static_cast<hipStream_t>(stream));
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -334,12 +375,14 @@ KDA_API int kda_chunk_prefill_varlen_fused(const uint16_t* qkv, const uint16_t* 
 
 namespace {
 
-// decode_k with FP32 q, k, v or, when qkv is not null, packed BF16 q | k | v rows
+// decode_k with FP32 q, k, v or, when qkv is not null, packed BF16 q | k | v rows; with gp, the gate
+// from kda_gate of gp->g_raw (gate must be null) and beta holding logits
 int recurrent_checked(const float* q, const float* k, const float* v, const uint16_t* qkv, const float* gate,
                       const float* beta, float* state, float* out, float* snapshots, int n_snapshots, int batch,
-                      int heads, int T, void* stream)
+                      int heads, int T, void* stream, const kda::GateParams* gp = nullptr)
 {
-    if ((!qkv && (!q || !k || !v)) || !gate || !beta || !state || !out) return KDA_ERR_INVALID_ARG;
+    if ((!qkv && (!q || !k || !v)) || !(gate || gp) || !beta || !state || !out) return KDA_ERR_INVALID_ARG;
+    if (gp && (qkv || !gate_inputs_ok(gp->g_raw, gp->dt_bias, gp->a_log, gp->lower))) return KDA_ERR_INVALID_ARG;
     if (!aligned({q, k, v, qkv, gate, state, out, snapshots}) || !aligned({beta}, 4)) return KDA_ERR_INVALID_ARG;
     if (batch < 1 || heads < 1 || T < 1) return KDA_ERR_INVALID_ARG;
     if (n_snapshots < 0 || n_snapshots > T || (n_snapshots > 0 && !snapshots)) return KDA_ERR_INVALID_ARG;
@@ -349,13 +392,16 @@ int recurrent_checked(const float* q, const float* k, const float* v, const uint
     const int64_t sn = mul({n_snapshots, batch, heads, KDA_HEAD_DIM, KDA_HEAD_DIM});
     if (vec < 0 || sca < 0 || st < 0 || sn < 0) return KDA_ERR_INVALID_ARG;
     if ((int64_t)batch * heads > kda::recurrent_max_units()) return KDA_ERR_INVALID_ARG;
+    const int64_t hd = mul({heads, KDA_HEAD_DIM});
     const Range r[] = {{out, vec * 4},  {state, st * 4}, {n_snapshots ? snapshots : nullptr, sn * 4},
                        {q, vec * 4},    {k, vec * 4},    {v, vec * 4},
-                       {qkv, vec * 6},  {gate, vec * 4}, {beta, sca * 4}};
-    if (any_overlap(r, 9, 3)) return KDA_ERR_INVALID_ARG;
+                       {qkv, vec * 6},  {gate, vec * 4}, {beta, sca * 4},
+                       {gp ? gp->g_raw : nullptr, vec * 2}, {gp ? gp->dt_bias : nullptr, hd * 4},
+                       {gp ? gp->a_log : nullptr, (int64_t)heads * 4}};
+    if (any_overlap(r, 12, 3)) return KDA_ERR_INVALID_ARG;
     const int rc = kda::launch_recurrent(qkv ? nullptr : q, qkv ? nullptr : k, qkv ? nullptr : v, qkv, gate, beta,
                                          state, out, n_snapshots ? snapshots : nullptr, n_snapshots, batch, heads, T,
-                                         static_cast<hipStream_t>(stream));
+                                         static_cast<hipStream_t>(stream), gp);
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -374,6 +420,27 @@ KDA_API int kda_recurrent_step(const float* q, const float* k, const float* v, c
                                float* state, float* out, int batch, int heads, void* stream)
 {
     return kda_recurrent_k(q, k, v, gate, beta, state, out, nullptr, 0, batch, heads, 1, stream);
+}
+
+KDA_API int kda_recurrent_k_gated(const float* q, const float* k, const float* v, const uint16_t* g_raw,
+                                  const float* beta_logit, const float* dt_bias, const float* a_log,
+                                  float gate_lower_bound, float* state, float* out, float* snapshots, int n_snapshots,
+                                  int batch, int heads, int T, void* stream)
+{
+    if (!q || !k || !v) return KDA_ERR_INVALID_ARG;
+    const kda::GateParams gp{reinterpret_cast<const unsigned short*>(g_raw), dt_bias, a_log, gate_lower_bound};
+    if (!gate_inputs_ok(g_raw, dt_bias, a_log, gate_lower_bound)) return KDA_ERR_INVALID_ARG;
+    return recurrent_checked(q, k, v, nullptr, nullptr, beta_logit, state, out, snapshots, n_snapshots, batch, heads,
+                             T, stream, &gp);
+}
+
+KDA_API int kda_recurrent_step_gated(const float* q, const float* k, const float* v, const uint16_t* g_raw,
+                                     const float* beta_logit, const float* dt_bias, const float* a_log,
+                                     float gate_lower_bound, float* state, float* out, int batch, int heads,
+                                     void* stream)
+{
+    return kda_recurrent_k_gated(q, k, v, g_raw, beta_logit, dt_bias, a_log, gate_lower_bound, state, out, nullptr, 0,
+                                 batch, heads, 1, stream);
 }
 
 KDA_API int kda_recurrent_k_bf16(const uint16_t* qkv, const float* gate, const float* beta, float* state, float* out,

@@ -211,12 +211,22 @@ __device__ __forceinline__ void atile_coords(int e, int n_cols, int& row, int& c
 
 constexpr int kPrepThreads = 512;  // 8 waves: one per 16-column block in the W/U stage
 
-// Inputs of one chunk as one thread of chunk_prepare loads them.
+__device__ __forceinline__ uint2 buf_ld_b64(rsrc_t r, int voff, int soff)
+{
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
+// Inputs of one chunk as one thread of chunk_prepare loads them.  With kda_gate inside the prepare (kGate), gr holds the BF16 g_raw pieces in
+// place of g, dt the thread's four dt_bias values and a_log the head's a_log;
+// beta then holds the logit.
 template <int C>
 struct PrepInputs {
     static constexpr int NV4 = C * 32 / kPrepThreads;
     float4 k[NV4], q[NV4], g[NV4];  // row-major [C][128] pieces
     float beta;
+    uint2 gr[NV4];
+    float4 dt;
+    float a_log;
 };
 
 // Raw buffer descriptors over the rows of one chunk of one (sequence, head) in
@@ -250,6 +260,21 @@ template <int C>
 __device__ __forceinline__ float prep_load_beta(rsrc_t src, int heads, int tid)
 {
     return tid < C ? buf_ld1(src, tid * heads * 4, 0) : 0.f;
+}
+
+// kGate: the g_raw pieces of the thread's gate rows (BF16, 8 bytes per row: columns 4 (tid % 32) +
+// 0..3), its four dt_bias values and the head's a_log.  live false: the g_raw descriptor covers
+// zero bytes (loads return zeros) and the parameters are those of head p.h as ever.
+template <int C>
+__device__ __forceinline__ void prep_load_gate(PrepInputs<C>& in, const GateParams& gp, const ChunkPos& p, int heads,
+                                               int tid, bool live = true)
+{
+    const rsrc_t src = make_rsrc(gp.g_raw + p.row0 * kD, live ? (uint32_t)p.span * (kD * 2) : 0u);
+    const int voff = ((tid >> 5) * heads * kD + (tid & 31) * 4) * 2;
+#pragma unroll
+    for (int i = 0; i < PrepInputs<C>::NV4; ++i) in.gr[i] = buf_ld_b64(src, voff, i * 16 * heads * kD * 2);
+    in.dt = ld4(gp.dt_bias + p.h * kD + 4 * (tid & 31));
+    in.a_log = gp.a_log[p.h];
 }
 
 // V of one chunk in the B-operand layout of this wave's U tiles (rows
@@ -291,14 +316,16 @@ constexpr float kSteepGateClampLog2 = 28.f;
 // sSteep[wave] whether any gate it staged is below -kFastGateLog2 (log2).
 // kFE: k and q are in the fused row order (rows NV4 (tid / 32) + i), the gate
 // in the usual one.
-template <int C, bool kFE = false>
+// kGate: the gate is kda_gate of the g_raw pieces (with `lower`) and beta the sigmoid of the logit.
+template <int C, bool kFE = false, bool kGate = false>
 __device__ __forceinline__ void prep_stage(const PrepInputs<C>& in, float* sK, float* sQ, float* sL, float* sBeta,
-                                           int* sSteep, int nvalid, int tid)
+                                           int* sSteep, int nvalid, int tid, float lower = 0.f)
 {
     using G = ChunkGeom<C>;
     constexpr int NV4 = PrepInputs<C>::NV4, LD = G::kLd;
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
     bool steep = false;
+    const float rate = kGate ? exp2_fast(kLog2e * in.a_log) : 0.f;
 #pragma unroll
     for (int i = 0; i < NV4; ++i) {
         const int e = tid + kPrepThreads * i, r = e >> 5, c4 = (e & 31) * 4;
@@ -307,12 +334,23 @@ __device__ __forceinline__ void prep_stage(const PrepInputs<C>& in, float* sK, f
         const bool okq = rq < nvalid;
         lds4_st(&sK[rq * LD + c4], okq ? in.k[i] : z4);
         lds4_st(&sQ[rq * LD + c4], okq ? in.q[i] : z4);
-        const float4 g = ok ? in.g[i] : z4;
-        const float4 l = make_float4(g.x * kLog2e, g.y * kLog2e, g.z * kLog2e, g.w * kLog2e);
+        float4 g;
+        if constexpr (kGate) {
+            const uint2 u = in.gr[i];
+            g = make_float4(kda_gate_f32(bf16_to_f32(u.x & 0xffffu), in.dt.x, rate, lower),
+                            kda_gate_f32(bf16_to_f32(u.x >> 16), in.dt.y, rate, lower),
+                            kda_gate_f32(bf16_to_f32(u.y & 0xffffu), in.dt.z, rate, lower),
+                            kda_gate_f32(bf16_to_f32(u.y >> 16), in.dt.w, rate, lower));
+        } else {
+            g = in.g[i];
+        }
+        // per-component selects (a select of whole float4 values went through scratch memory)
+        const float4 l = make_float4(ok ? g.x * kLog2e : 0.f, ok ? g.y * kLog2e : 0.f, ok ? g.z * kLog2e : 0.f,
+                                     ok ? g.w * kLog2e : 0.f);
         steep |= (l.x < -kFastGateLog2) | (l.y < -kFastGateLog2) | (l.z < -kFastGateLog2) | (l.w < -kFastGateLog2);
         lds4_st(&sL[r * LD + c4], l);
     }
-    if (tid < C) sBeta[tid] = tid < nvalid ? in.beta : 0.f;
+    if (tid < C) sBeta[tid] = tid < nvalid ? (kGate ? sigmoid_f32(in.beta) : in.beta) : 0.f;
     const bool any = __builtin_amdgcn_ballot_w64(steep) != 0;
     if ((tid & 63) == 0) sSteep[tid >> 6] = any ? 1 : 0;
 }
@@ -501,10 +539,6 @@ struct FeSrc {
 };
 constexpr int kFeK = 4;  // conv taps of the fused form
 
-__device__ __forceinline__ uint2 buf_ld_b64(rsrc_t r, int voff, int soff)
-{
-    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
-}
 __device__ __forceinline__ uint4 buf_ld_b128u(rsrc_t r, int voff, int soff)
 {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
@@ -688,11 +722,11 @@ __device__ __forceinline__ void fe_finish_v(const FeV<C>& r, float (&vb)[C / 16]
 // kFE: the front end is fused in (dense layout): q, k and v are formed from
 // the BF16 projections in `fe` (see FeSrc) instead of read as FP32 rows; the
 // q, k, v pointers are then not read.
-template <int C, class Layout, bool kFE = false>
+template <int C, class Layout, bool kFE = false, bool kGate = false>
 __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ gate, const float* __restrict__ beta, float* __restrict__ ws, int heads,
-    Layout layout, FeSrc fe)
+    Layout layout, FeSrc fe, GateParams gp)
 {
     using G = ChunkGeom<C>;
     constexpr int NT = G::kTiles, LD = G::kLd, LDC = G::kLdc;
@@ -736,9 +770,10 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
             prep_load_part<C>(in.k, src.k, heads, threadIdx.x);
             prep_load_part<C>(in.q, src.q, heads, threadIdx.x);
         }
-        prep_load_part<C>(in.g, src.g, heads, threadIdx.x);
+        if constexpr (kGate) prep_load_gate<C>(in, gp, pos, heads, threadIdx.x);
+        else prep_load_part<C>(in.g, src.g, heads, threadIdx.x);
         in.beta = prep_load_beta<C>(src.b, heads, threadIdx.x);
-        prep_stage<C, kFE>(in, sKr, sQr, sKc, sBeta, sSteep, pos.nvalid, threadIdx.x);
+        prep_stage<C, kFE, kGate>(in, sKr, sQr, sKc, sBeta, sSteep, pos.nvalid, threadIdx.x, gp.lower);
     }
     __syncthreads();
 
@@ -1051,7 +1086,8 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         // 6. P = e^G o Q - M W and R = M U.  The W and U accumulator tiles are, lane
         //    for lane, the B operands of the products over the chunk rows.
         __builtin_amdgcn_sched_barrier(0);
-        prep_load_part<C>(in.g, nsrc.g, heads, tid);
+        if constexpr (kGate) prep_load_gate<C>(in, gp, npos, heads, tid, gn < n_total);
+        else prep_load_part<C>(in.g, nsrc.g, heads, tid);
         in.beta = prep_load_beta<C>(nsrc.b, heads, tid);
         __builtin_amdgcn_sched_barrier(0);
         // (fused front end) the next chunk's k and q from their raw inputs, which arrived during
@@ -1093,7 +1129,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         __syncthreads();
         // stage the next chunk (loaded during this one; after the last chunk the
         // staged copy is unused)
-        prep_stage<C, kFE>(in, sKr, sQr, sKc, sBeta, sSteep, npos.nvalid, tid);
+        prep_stage<C, kFE, kGate>(in, sKr, sQr, sKc, sBeta, sSteep, npos.nvalid, tid, gp.lower);
         pos = npos;
         __syncthreads();
     }
@@ -1435,18 +1471,20 @@ static int launch_scan_auto(const float* ws, float* state, float* out, long long
 // max_records bounds the layout's record count (exact for the dense layout).
 // kTrans: state is the Q output and out the P output of the transition form.
 // kFE: the prepare with the front end fused in (q, k, v unused; fe its inputs).
-template <int C, class Layout, bool kTrans = false, bool kFE = false>
+// kGate: kda_gate and the beta sigmoid inside the prepare (gate unused, beta the logits; gp its inputs).
+template <int C, class Layout, bool kTrans = false, bool kFE = false, bool kGate = false>
 static int launch_chunk(const float* q, const float* k, const float* v, const float* gate, const float* beta,
                         float* state, float* out, long long n_bh, int heads, long long max_records, float* ws,
-                        const Layout& layout, hipStream_t stream, const FeSrc& fe = FeSrc{})
+                        const Layout& layout, hipStream_t stream, const FeSrc& fe = FeSrc{},
+                        const GateParams& gp = GateParams{})
 {
     // one persistent prepare workgroup per compute unit (its LDS use allows one)
     const int n_cu = compute_units();
     if (n_cu < 1) return -1;
     const int grid_p = max_records < n_cu ? (int)max_records : n_cu;
     if (grid_p > 0) {
-        hipLaunchKernelGGL((chunk_prepare_kernel<C, Layout, kFE>), dim3((unsigned)grid_p), dim3(kPrepThreads), 0,
-                           stream, q, k, v, gate, beta, ws, heads, layout, fe);
+        hipLaunchKernelGGL((chunk_prepare_kernel<C, Layout, kFE, kGate>), dim3((unsigned)grid_p), dim3(kPrepThreads),
+                           0, stream, q, k, v, gate, beta, ws, heads, layout, fe, gp);
         if (hipGetLastError() != hipSuccess) return -1;
     }
     return launch_scan_auto<C, Layout, kTrans>(ws, state, out, n_bh, heads, layout, n_cu, stream);
@@ -1472,6 +1510,33 @@ int launch_chunk_prefill(const float* q, const float* k, const float* v, const f
     case 16: return launch_dense<16>(q, k, v, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream);
     case 32: return launch_dense<32>(q, k, v, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream);
     case 64: return launch_dense<64>(q, k, v, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream);
+    default: return -1;
+    }
+}
+
+// The prefill with kda_gate and the beta sigmoid inside the prepare (dense layout): beta holds the
+// logits, the gate comes from gp.
+template <int C>
+static int launch_dense_gated(const float* q, const float* k, const float* v, const float* beta_logit,
+                              const GateParams& gp, float* state, float* out, int batch, int heads, int T, int t_pad,
+                              float* ws, hipStream_t stream)
+{
+    const int nchunks = t_pad / C;
+    const long long n_bh = (long long)batch * heads;
+    const DenseLayout layout{heads, T, t_pad, nchunks, (int)(n_bh * nchunks)};
+    // the gate pointer of the plain form is not read: q stands in for it (only its rows' descriptor is made)
+    return launch_chunk<C, DenseLayout, false, false, true>(q, k, v, q, beta_logit, state, out, n_bh, heads,
+                                                            n_bh * nchunks, ws, layout, stream, FeSrc{}, gp);
+}
+
+int launch_chunk_prefill_gated(const float* q, const float* k, const float* v, const float* beta_logit,
+                               const GateParams& gp, float* state, float* out, int batch, int heads, int T, int t_pad,
+                               int chunk, float* workspace, hipStream_t stream)
+{
+    switch (chunk) {
+    case 16: return launch_dense_gated<16>(q, k, v, beta_logit, gp, state, out, batch, heads, T, t_pad, workspace, stream);
+    case 32: return launch_dense_gated<32>(q, k, v, beta_logit, gp, state, out, batch, heads, T, t_pad, workspace, stream);
+    case 64: return launch_dense_gated<64>(q, k, v, beta_logit, gp, state, out, batch, heads, T, t_pad, workspace, stream);
     default: return -1;
     }
 }

@@ -24,6 +24,28 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float x)
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// kda_gate and the beta sigmoid inside a core kernel's loads (workspace page, fields gate and g_raw:
+// the gate is the bounded log-decay kda_gate makes from g_raw; field beta: a sigmoid of its logit;
+// config page, dt_bias per (head, channel), a_log per head, gate_lower_bound).  The pages print no
+// gate formula; the reading implemented is
+//     gate = lower * sigmoid(exp(a_log[h]) * (g_raw + dt_bias[h][i])),   beta = sigmoid(beta logit)
+// evaluated in FP32 with the hardware exp2 and reciprocal (each within about one unit in the last
+// place): a few units of 2^-24 on the gate, far inside the core's tolerance.
+struct GateParams {
+    const unsigned short* g_raw;  // [rows][heads][128] BF16, in the gate's own layout
+    const float* dt_bias;         // [heads][128]
+    const float* a_log;           // [heads]
+    float lower;                  // gate_lower_bound, <= 0
+};
+__device__ __forceinline__ float sigmoid_f32(float z)
+{
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
+__device__ __forceinline__ float kda_gate_f32(float g_raw, float dt_bias, float rate, float lower)
+{
+    return lower * sigmoid_f32(rate * (g_raw + dt_bias));
+}
+
 // Raw buffer access: a descriptor (base address, size in bytes) held in scalar
 // registers plus a 32-bit per-lane byte offset and a wave-uniform byte offset.
 // Lane offsets computed once outside a loop then need no per-iteration vector

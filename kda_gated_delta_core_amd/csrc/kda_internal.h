@@ -23,15 +23,23 @@ namespace kda {
 // lower-triangular decayed Q K^T of the chunk.
 constexpr size_t chunk_record_floats(int C) { return 5 * (size_t)C * 128 + 128; }
 
-// q, k, v FP32 [B][T][H][128]; or, when qkv is not null, q | k | v BF16 [B][T][3][H][128] from qkv
+// q, k, v FP32 [B][T][H][128]; or, when qkv is not null, q | k | v BF16 [B][T][3][H][128] from qkv.
+// gp not null: the gate from kda_gate of gp->g_raw (gate unused), beta holding logits (FP32 q, k, v only)
+struct GateParams;
 int launch_recurrent(const float* q, const float* k, const float* v, const uint16_t* qkv, const float* gate,
                      const float* beta, float* state, float* out, float* snaps, int n_snap, int batch, int heads,
-                     int T, hipStream_t stream);
+                     int T, hipStream_t stream, const GateParams* gp = nullptr);
 long long recurrent_max_units();
 
 int launch_chunk_prefill(const float* q, const float* k, const float* v, const float* gate, const float* beta,
                          float* state, float* out, int batch, int heads, int T, int t_pad, int chunk,
                          float* workspace, hipStream_t stream);
+
+// the prefill with kda_gate and the beta sigmoid inside the prepare: beta_logit [B][T_pad][H] logits,
+// gp the gate inputs (g_raw [B][T_pad][H][128] BF16); the rest as launch_chunk_prefill
+int launch_chunk_prefill_gated(const float* q, const float* k, const float* v, const float* beta_logit,
+                               const GateParams& gp, float* state, float* out, int batch, int heads, int T, int t_pad,
+                               int chunk, float* workspace, hipStream_t stream);
 
 // the prefill with the front end fused into the prepare (conv_kernel 4): qkv BF16 [B][T][3][H][128],
 // conv_w BF16 [3 H 128][4], conv state [B][3 H 128][4] (advanced by T inputs), gate, beta, state, out

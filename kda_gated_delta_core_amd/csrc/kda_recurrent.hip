@@ -8,17 +8,24 @@
 //
 // Memory plan (kernel-table page, recurrent_smem: one state read and one
 // state write per step, the decayed state kept on chip between the two
-// passes).  A workgroup owns one (sequence, head, value slice); its 256
-// threads load the slice of the 64 KiB head state straight into VGPRs with
-// 16-byte loads (thread = 4 adjacent value columns x kRows key rows, a wave
-// covers whole 128-byte row segments), keep it there for all rows of the walk,
-// and write it back once.  The slices of one head go to blocks 8 apart, which
-// the dispatcher places on the same XCD, so each 512-byte state row is read
-// and written through one L2.  Per row the only cross-thread traffic is the
-// reduction of the read-outs over the key index: a xor-shuffle across the
-// row groups inside the wave plus one LDS exchange across the four waves.
-// No atomics: every thread sums in the same fixed order, so results are
+// passes).  A workgroup owns one (sequence, head, 32-column value slice); its
+// 512 threads load the slice of the 64 KiB head state straight into VGPRs
+// with 16-byte loads (thread = 4 adjacent value columns x 2 key rows, a wave
+// covers 8 rows of 128-byte segments), keep it there for all rows of the
+// walk, and write it back once.  The slices of one head go to blocks 8 apart,
+// which the dispatcher places on the same XCD, so each 512-byte state row is
+// read and written through one L2.  Per row the only cross-thread traffic is
+// the reduction of the read-outs over the key index: a xor-shuffle across the
+// row groups inside the wave, then the eight waves' partial sums through LDS,
+// summed once per (value, column group) in wave order and read back.  No
+// atomics: every thread sums in the same fixed order, so results are
 // deterministic.
+//
+// Geometry (measured, interleaved in one process, B=128 H=32 k=4 with 4
+// snapshots / B=64 H=32 step): 512 threads x 4 slices 294 / 45.9 us; 256 x 4
+// 317 / 46.1; 1024 x 2 298 / 47.2; 512 x 2 339 / 46.9; 1024 x 1 306 / 46.6;
+// capping the workgroups per compute unit (LDS padding) was slower in every
+// case (512 x 4 at 3 per CU 312, at 2 per CU 381).
 //
 // Inputs come in two forms: FP32 q, k, v as three [B][T][H][128] arrays, or
 // BF16 q | k | v packed per token as [B][T][3][H][128], the layout the decode
@@ -31,15 +38,19 @@
 
 namespace kda {
 
-template <int NSLICE>
+template <int NSLICE, int THREADS = 256>
 struct RecGeom {
-    static constexpr int kThreads = 256;
+    static constexpr int kThreads = THREADS;
     static constexpr int kCols = kD / NSLICE;           // value columns per workgroup
     static constexpr int kColGroups = kCols / 4;        // float4 column groups
     static constexpr int kRowGroups = kThreads / kColGroups;
     static constexpr int kRows = kD / kRowGroups;       // key rows per thread
     static constexpr int kWaves = kThreads / 64;
     static_assert(kColGroups <= 64 && 64 % kColGroups == 0, "a wave must hold whole row groups");
+    // more than four waves: the waves' partial sums are reduced once per
+    // (value, column group) by one thread each, then read back, instead of
+    // every thread summing every wave
+    static constexpr bool kTwoStage = kWaves > 4;
 };
 
 // Value slices per head.  Part of the arithmetic contract: the reduction tree
@@ -47,7 +58,12 @@ struct RecGeom {
 #ifndef KDA_REC_SLICES
 #define KDA_REC_SLICES 4
 #endif
+#ifndef KDA_REC_THREADS
+#define KDA_REC_THREADS 512
+#endif
 constexpr int kRecSlices = KDA_REC_SLICES;
+constexpr int kRecThreads = KDA_REC_THREADS;
+using RecG = RecGeom<kRecSlices, kRecThreads>;
 
 // The carried state is streamed once per call: non-temporal hints keep it from
 // displacing other data in the caches.
@@ -83,12 +99,12 @@ __device__ __forceinline__ void state_st(float* p, float4 v)
 // update.  Returns the thread's four outputs (stored by row group 0).  The
 // caller has staged the key, query and decay of the row in LDS and passes the
 // thread's four values of v and the row's beta.
-template <int NSLICE>
-__device__ __forceinline__ float4 rec_row(float4 (&s)[RecGeom<NSLICE>::kRows], const float* s_k, const float* s_q,
-                                          const float* s_a, float (*s_red)[9][RecGeom<NSLICE>::kColGroups],
-                                          float4 vv, float bt, int cg, int rg, int wave, int lane)
+template <class G>
+__device__ __forceinline__ float4 rec_row(float4 (&s)[G::kRows], const float* s_k, const float* s_q,
+                                          const float* s_a, float (*s_red)[9][G::kColGroups],
+                                          float (*s_tot)[G::kColGroups], float4 vv, float bt, int cg, int rg,
+                                          int wave, int lane)
 {
-    using G = RecGeom<NSLICE>;
     // decay in place, then partial read-outs with the key and the query
     float red[9];
 #pragma unroll
@@ -126,12 +142,26 @@ __device__ __forceinline__ float4 rec_row(float4 (&s)[RecGeom<NSLICE>::kRows], c
     }
     __syncthreads();
     float tot[9];
+    if constexpr (G::kTwoStage) {
+        const int tid = wave * 64 + lane;
+        if (tid < 9 * G::kColGroups) {
+            const int x = tid / G::kColGroups, c = tid % G::kColGroups;
+            float acc = s_red[0][x][c];
 #pragma unroll
-    for (int x = 0; x < 9; ++x) {
-        float acc = s_red[0][x][cg];
+            for (int w = 1; w < G::kWaves; ++w) acc += s_red[w][x][c];
+            s_tot[x][c] = acc;
+        }
+        __syncthreads();
 #pragma unroll
-        for (int w = 1; w < G::kWaves; ++w) acc += s_red[w][x][cg];
-        tot[x] = acc;
+        for (int x = 0; x < 9; ++x) tot[x] = s_tot[x][cg];
+    } else {
+#pragma unroll
+        for (int x = 0; x < 9; ++x) {
+            float acc = s_red[0][x][cg];
+#pragma unroll
+            for (int w = 1; w < G::kWaves; ++w) acc += s_red[w][x][cg];
+            tot[x] = acc;
+        }
     }
     // delta = beta (v - S^T k);  out = S_dec^T q + (q.k) delta  (= S_new^T q)
     float4 d, o;
@@ -153,16 +183,18 @@ __device__ __forceinline__ float4 rec_row(float4 (&s)[RecGeom<NSLICE>::kRows], c
     return o;
 }
 
-template <int NSLICE, bool kPackedBf16>
-__global__ __launch_bounds__(256) void recurrent_kernel(const float* __restrict__ q, const float* __restrict__ k,
+// kGated: the gate comes from kda_gate of gp.g_raw (gate not read) and beta holds the logits,
+// passed through the sigmoid here (see GateParams).
+template <int NSLICE, bool kPackedBf16, int THREADS = 256, bool kGated = false>
+__global__ __launch_bounds__(THREADS) void recurrent_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                         const float* __restrict__ v,
                                                         const unsigned short* __restrict__ qkv,
                                                         const float* __restrict__ gate,
                                                         const float* __restrict__ beta, float* __restrict__ state,
                                                         float* __restrict__ out, float* __restrict__ snaps,
-                                                        int n_snap, int batch, int heads, int T)
+                                                        int n_snap, int batch, int heads, int T, GateParams gp)
 {
-    using G = RecGeom<NSLICE>;
+    using G = RecGeom<NSLICE, THREADS>;
     const int tid = threadIdx.x;
     // blocks come in groups of 8 * NSLICE: 8 heads, slice s of head j at 8 s + j
     const int r = blockIdx.x % (8 * NSLICE);
@@ -178,6 +210,16 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const float* __restrict_
 
     __shared__ float s_k[kD], s_q[kD], s_a[kD];
     __shared__ float s_red[G::kWaves][9][G::kColGroups];
+    __shared__ float s_tot[G::kTwoStage ? 9 : 1][G::kColGroups];
+
+    // per-head rate of the gate (kGated)
+    const float rate = kGated ? __builtin_amdgcn_exp2f(1.4426950408889634f * gp.a_log[h]) : 0.f;
+    auto decay = [&](size_t row) {  // e^{gate} of channel tid in row `row`
+        if constexpr (kGated)
+            return expf(kda_gate_f32(bf16_to_f32(gp.g_raw[row * kD + tid]), gp.dt_bias[h * kD + tid], rate, gp.lower));
+        else
+            return expf(gate[row * kD + tid]);
+    };
 
     float* const S_head = state + (size_t)bh * kD * kD;
     float4 s[G::kRows];
@@ -195,9 +237,9 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const float* __restrict_
             if (tid < kD) {
                 s_k[tid] = bf16_to_f32(x[part + tid]);
                 s_q[tid] = bf16_to_f32(x[tid]);
-                s_a[tid] = expf(gate[row * kD + tid]);
+                s_a[tid] = decay(row);
             }
-            bt = beta[row];
+            bt = kGated ? sigmoid_f32(beta[row]) : beta[row];
             const uint2 u = *reinterpret_cast<const uint2*>(x + 2 * part + col);
             vv = make_float4(bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xffffu),
                              bf16_to_f32(u.y >> 16));
@@ -205,13 +247,13 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const float* __restrict_
             if (tid < kD) {
                 s_k[tid] = k[row * kD + tid];
                 s_q[tid] = q[row * kD + tid];
-                s_a[tid] = expf(gate[row * kD + tid]);
+                s_a[tid] = decay(row);
             }
-            bt = beta[row];
+            bt = kGated ? sigmoid_f32(beta[row]) : beta[row];
             vv = ld4(v + row * kD + col);
         }
         __syncthreads();
-        const float4 o = rec_row<NSLICE>(s, s_k, s_q, s_a, s_red, vv, bt, cg, rg, wave, lane);
+        const float4 o = rec_row<G>(s, s_k, s_q, s_a, s_red, s_tot, vv, bt, cg, rg, wave, lane);
         if (rg == 0) st4(out + row * kD + col, o);
         if (t < n_snap) {
             // snapshots are ordinary (cacheable) stores: a caller verifying
@@ -227,16 +269,21 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const float* __restrict_
 
 int launch_recurrent(const float* q, const float* k, const float* v, const uint16_t* qkv, const float* gate,
                      const float* beta, float* state, float* out, float* snaps, int n_snap, int batch, int heads,
-                     int T, hipStream_t stream)
+                     int T, hipStream_t stream, const GateParams* gp)
 {
     const unsigned grid = ((unsigned)batch * (unsigned)heads + 7u) / 8u * 8u * kRecSlices;
     const auto* x = reinterpret_cast<const unsigned short*>(qkv);
-    if (qkv)
-        hipLaunchKernelGGL((recurrent_kernel<kRecSlices, true>), dim3(grid), dim3(256), 0, stream, nullptr, nullptr,
-                           nullptr, x, gate, beta, state, out, snaps, n_snap, batch, heads, T);
+    if (gp)
+        hipLaunchKernelGGL((recurrent_kernel<kRecSlices, false, kRecThreads, true>), dim3(grid), dim3(kRecThreads), 0,
+                           stream, q, k, v, nullptr, nullptr, beta, state, out, snaps, n_snap, batch, heads, T, *gp);
+    else if (qkv)
+        hipLaunchKernelGGL((recurrent_kernel<kRecSlices, true, kRecThreads>), dim3(grid), dim3(kRecThreads), 0, stream,
+                           nullptr, nullptr, nullptr, x, gate, beta, state, out, snaps, n_snap, batch, heads, T,
+                           GateParams{});
     else
-        hipLaunchKernelGGL((recurrent_kernel<kRecSlices, false>), dim3(grid), dim3(256), 0, stream, q, k, v, nullptr,
-                           gate, beta, state, out, snaps, n_snap, batch, heads, T);
+        hipLaunchKernelGGL((recurrent_kernel<kRecSlices, false, kRecThreads>), dim3(grid), dim3(kRecThreads), 0,
+                           stream, q, k, v, nullptr, gate, beta, state, out, snaps, n_snap, batch, heads, T,
+                           GateParams{});
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -62,6 +62,10 @@ L2_EPS = 1e-6
 ID_STATE, ID_Q, ID_K, ID_V, ID_GATE, ID_BETA = 0, 1, 2, 3, 4, 5
 ID_CORE, ID_OUT_GATE, ID_O_NORM = 6, 7, 8
 ID_QKV, ID_CONV_W, ID_CONV_STATE = 9, 10, 11
+ID_G_RAW, ID_BETA_LOGIT, ID_DT_BIAS, ID_A_LOG = 12, 13, 14, 15
+# gate_lower_bound of the gated workloads (the pages name the key, not its value): -5, the lower end of
+# the workloads' gate range
+GATE_LOWER_BOUND = -5.0
 # (batch, rows, heads, conv_kernel, seed) of the decode front-end workloads: one decode step of the
 # B=64 H=32 workload, and the k=4 rows of the B=128 decode_k workload
 FRONT_END_WORKLOADS = {
@@ -258,6 +262,22 @@ def front_end_inputs(seed: int, batch: int, rows: int, heads: int, conv_kernel: 
         st[b] = (s.astype(np.uint32) << 16).view(np.float32)
     w = 0.5 * _rng(seed, ID_CONV_W, 0, 0).standard_normal((C, conv_kernel), dtype=np.float32)
     return {"qkv": qkv, "conv_w": to_bf16_bits(w.astype(np.float32)), "conv_state": st}
+
+
+def gate_inputs(seed: int, batch: int, rows: int, heads: int) -> dict:
+    """Inputs of the gate and beta steps that precede the core: g_raw [B][rows][H][D] standard normal
+    rounded to BF16 patterns (a projection output of unit scale), beta_logit [B][rows][H] standard
+    normal (so beta = sigmoid of it has the distribution of the other workloads' beta), dt_bias [H][D]
+    0.5 * standard normal, a_log [H] 0.5 * standard normal (rates exp(a_log) around 1).  With the
+    lower bound -5 the gates then spread over (-5, 0) like the other workloads' U[-5, 0]."""
+    g = np.empty((batch, rows, heads, D), dtype=np.uint16)
+    bl = np.empty((batch, rows, heads), dtype=np.float32)
+    for b in range(batch):
+        g[b] = to_bf16_bits(_rng(seed, ID_G_RAW, b, 0).standard_normal((rows, heads, D), dtype=np.float32))
+        bl[b] = _rng(seed, ID_BETA_LOGIT, b, 0).standard_normal((rows, heads), dtype=np.float32)
+    dt = (0.5 * _rng(seed, ID_DT_BIAS, 0, 0).standard_normal((heads, D))).astype(np.float32)
+    al = (0.5 * _rng(seed, ID_A_LOG, 0, 0).standard_normal(heads)).astype(np.float32)
+    return {"g_raw": g, "beta_logit": bl, "dt_bias": dt, "a_log": al}
 
 
 def varlen_lengths(seed: int, total: int, mean_len: int) -> list:

@@ -395,6 +395,35 @@ def test_prefill_noalloc_refusals(lib):
 
 
 @no_gpu
+def test_gated_refusals(lib):
+    """the gate inputs of the gated entry points: null, misaligned, overlapping, or a lower bound that
+    is positive or not finite"""
+    q, k, v, g, b, dt, al, st, out, ws = P[:10]
+    pf = lambda *a, lb=-5.0, ws_=ws: lib.kda_chunk_prefill_gated(*a, lb, st, out, 1, 2, 64, 16, ws_, 1 << 30, None)
+    for i in range(7):
+        a = [q, k, v, g, b, dt, al]
+        a[i] = None
+        assert pf(*a) == kda.KDA_ERR_INVALID_ARG, i
+    assert pf(q, k, v, g + 4, b, dt, al) == kda.KDA_ERR_INVALID_ARG      # g_raw 8-byte aligned
+    assert pf(q, k, v, g, b, dt + 8, al) == kda.KDA_ERR_INVALID_ARG      # dt_bias 16-byte aligned
+    assert pf(q, k, v, g, b, dt, al, lb=0.5) == kda.KDA_ERR_INVALID_ARG
+    assert pf(q, k, v, g, b, dt, al, lb=float("-inf")) == kda.KDA_ERR_INVALID_ARG
+    assert pf(q, k, v, g, b, dt, al, lb=float("nan")) == kda.KDA_ERR_INVALID_ARG
+    assert pf(q, k, v, g, b, out + 64, al) == kda.KDA_ERR_INVALID_ARG    # dt_bias inside out
+    assert pf(q, k, v, g, b, dt, al, ws_=None) == kda.KDA_ERR_WORKSPACE
+    rk = lambda *a, lb=-5.0: lib.kda_recurrent_k_gated(*a, lb, st, out, None, 0, 2, 3, 4, None)
+    for i in range(7):
+        a = [q, k, v, g, b, dt, al]
+        a[i] = None
+        assert rk(*a) == kda.KDA_ERR_INVALID_ARG, i
+    assert rk(q, k, v, g, b, dt, al, lb=1.0) == kda.KDA_ERR_INVALID_ARG
+    assert rk(q, k, v, g + 2, b, dt, al) == kda.KDA_ERR_INVALID_ARG
+    assert rk(q, k, v, g, st + 4, dt, al) == kda.KDA_ERR_INVALID_ARG    # beta logits inside state
+    assert lib.kda_recurrent_step_gated(q, k, v, None, b, dt, al, -5.0, st, out, 2, 3, None) == \
+        kda.KDA_ERR_INVALID_ARG
+
+
+@no_gpu
 def test_transition_refusals(lib):
     f = lib.kda_chunk_prefill_transition
     bad = kda.KDA_ERR_INVALID_ARG
