@@ -327,10 +327,12 @@ def bench_prefill_front_end(torch, kda, ki, name, steps, warmup, timer):
     return r, per_set, n_set, B * T
 
 
-def bench_decode_chain(torch, kda, ki, reps):
+def bench_decode_chain(torch, kda, ki, reps, fused=False):
     """The decode step of the block on BF16 q | k | v: front end -> kda_recurrent_step_bf16 -> gated RMSNorm
     at B=64 H=32, captured as one HIP graph of 8 steps, each on its own state set (8 x 128 MiB of recurrent
-    state, so replays stream HBM), replayed back to back.  Returns (us per step, bytes per step)."""
+    state, so replays stream HBM), replayed back to back.  fused: front end -> kda_recurrent_step_bf16_norm
+    (the norm inside the decode kernel, the FP32 core rows not stored).  Returns (us per step, bytes per
+    step)."""
     w = ki.WORKLOADS["decode_b64_h32"]
     B, H = w.batch, w.heads
     FB, FT, FH, K, fseed = ki.FRONT_END_WORKLOADS["front_end_b64_h32_k4"]
@@ -350,8 +352,12 @@ def bench_decode_chain(torch, kda, ki, reps):
 
     def chain(z):
         kda.kda_decode_front_end_bf16(qkv, cw, z["cst"], H, ki.L2_EPS, conv_out=z["co"])
-        kda.kda_recurrent_step_bf16(z["co"], g, b, z["st"], out=z["out"])
-        kda.kda_gated_rmsnorm(z["out"].view(B, H, D), og, on, ki.NORM_EPS, out=z["y"])
+        if fused:
+            kda.kda_recurrent_step_bf16_norm(z["co"], g, b, z["st"], og.view(B, 1, H, D), on, ki.NORM_EPS,
+                                             y=z["y"].view(B, 1, H, D), want_core=False)
+        else:
+            kda.kda_recurrent_step_bf16(z["co"], g, b, z["st"], out=z["out"])
+            kda.kda_gated_rmsnorm(z["out"].view(B, H, D), og, on, ki.NORM_EPS, out=z["y"])
 
     for z in sets:
         chain(z)
@@ -372,7 +378,11 @@ def bench_decode_chain(torch, kda, ki, reps):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / (reps * n_set)
-    nbytes = (front_end_bytes(B, 1, H, K, 0, out_bytes=2) + decode_bytes(B, H, qkv_bytes=2) + norm_bytes(B, H))
+    if fused:  # the core rows stay on chip: the norm reads only its gate and weight and writes y
+        nbytes = (front_end_bytes(B, 1, H, K, 0, out_bytes=2) + decode_bytes(B, H, qkv_bytes=2) - B * H * D * 4
+                  + B * H * D * 4 + 2 * D)
+    else:
+        nbytes = (front_end_bytes(B, 1, H, K, 0, out_bytes=2) + decode_bytes(B, H, qkv_bytes=2) + norm_bytes(B, H))
     return us, nbytes
 
 
@@ -864,6 +874,13 @@ def main():
             "tokens_per_s": 64 / (us * 1e-6), "us_per_step": us, "GB_per_s": nbytes / (us * 1e-6) / 1e9,
             "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "steps": "front end (BF16 out) + kda_recurrent_step_bf16 + gated RMSNorm, replayed from one HIP graph"}
+    if want("decode_chain_fused_bf16_b64_h32"):
+        log("decode_chain_fused_bf16_b64_h32")
+        us, nbytes = bench_decode_chain(torch, kda, ki, args.reps or 50, fused=True)
+        workloads["decode_chain_fused_bf16_b64_h32"] = {
+            "tokens_per_s": 64 / (us * 1e-6), "us_per_step": us, "GB_per_s": nbytes / (us * 1e-6) / 1e9,
+            "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "steps": "front end (BF16 out) + kda_recurrent_step_bf16_norm (norm fused), replayed from one HIP graph"}
     if want("prefill_chain_t8192_h32"):
         log("prefill_chain_t8192_h32")
         r, tokens = bench_prefill_chain(torch, kda, ki, args.reps or 20, 0 if args.reps else 60, timer)

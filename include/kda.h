@@ -411,6 +411,36 @@ int kda_recurrent_step_bf16(const uint16_t* qkv, const float* gate, const float*
                             int batch, int heads, void* stream);
 
 /*
+ * The BF16 decode forms above with the block's next step fused in: the
+ * sigmoid-gated RMSNorm of every output row (see kda_gated_rmsnorm) is done
+ * by the decode kernel itself, so the core's FP32 rows need not travel
+ * through HBM to a second kernel (module page, pipeline line; workspace page,
+ * fields core, out_gate and o_norm_out).  One workgroup holds a whole head
+ * here, so the 128 channels of a row meet in one wave.
+ *
+ *   qkv, gate, beta, state, snapshots, n_snapshots : as kda_recurrent_k_bf16
+ *   out      : [batch][T][heads][128] FP32 core rows, or NULL (then not stored)
+ *   out_gate : [batch][T][heads][128] BF16, the output gate
+ *   o_norm   : [128] BF16;  eps: as kda_gated_rmsnorm
+ *   y        : [batch][T][heads][128] BF16, the normalised rows (o_norm_out)
+ *
+ * y is within one BF16 unit in the last place of the exact norm of the core
+ * rows the call computes (the scale is formed in FP64 over the 128 squares
+ * in another order than kda_gated_rmsnorm's, so the two agree bit for bit
+ * except where that order moves the scale by its last bit).  The core rows,
+ * state and snapshots are within the stated tolerance of kda_recurrent_k_bf16
+ * (another reduction tree: a whole-head workgroup); T rows of
+ * kda_recurrent_k_bf16_norm equal T successive kda_recurrent_step_bf16_norm
+ * calls bit for bit.  Refusals as kda_recurrent_k_bf16 and kda_gated_rmsnorm.
+ */
+int kda_recurrent_k_bf16_norm(const uint16_t* qkv, const float* gate, const float* beta, float* state, float* out,
+                              const uint16_t* out_gate, const uint16_t* o_norm, float eps, uint16_t* y,
+                              float* snapshots, int n_snapshots, int batch, int heads, int T, void* stream);
+int kda_recurrent_step_bf16_norm(const uint16_t* qkv, const float* gate, const float* beta, float* state, float* out,
+                                 const uint16_t* out_gate, const uint16_t* o_norm, float eps, uint16_t* y, int batch,
+                                 int heads, void* stream);
+
+/*
  * The step after the core: sigmoid-gated RMSNorm of the core's output (module
  * page, pipeline line: the core output goes through a sigmoid-gated RMSNorm
  * with weight o_norm and gate g_b(g_a(h)) before o_proj; the page notes that

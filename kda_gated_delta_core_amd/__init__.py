@@ -36,7 +36,8 @@ EXPORTED = ("kda_status_string", "kda_chunk_prefill_workspace_bytes", "kda_chunk
             "kda_recurrent_step_bf16", "kda_decode_front_end_bf16", "kda_prefill_front_end",
             "kda_prefill_front_end_varlen", "kda_chunk_prefill_transition", "kda_state_transition_apply", "kda_chunk_scan",
             "kda_chunk_prefill_fused", "kda_chunk_prefill_varlen_fused", "kda_chunk_prefill_noalloc",
-            "kda_chunk_prefill_gated", "kda_recurrent_k_gated", "kda_recurrent_step_gated")
+            "kda_chunk_prefill_gated", "kda_recurrent_k_gated", "kda_recurrent_step_gated",
+            "kda_recurrent_k_bf16_norm", "kda_recurrent_step_bf16_norm")
 STATIC_WORKSPACE_BYTES = 256 << 20
 GATED_RMSNORM_MIN_EPS = 1e-30
 
@@ -75,6 +76,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_recurrent_k_gated.restype = i
     lib.kda_recurrent_step_gated.argtypes = [p] * 7 + [f, p, p] + [i, i, p]
     lib.kda_recurrent_step_gated.restype = i
+    lib.kda_recurrent_k_bf16_norm.argtypes = [p] * 7 + [f, p, p] + [i] * 4 + [p]
+    lib.kda_recurrent_k_bf16_norm.restype = i
+    lib.kda_recurrent_step_bf16_norm.argtypes = [p] * 7 + [f, p] + [i, i, p]
+    lib.kda_recurrent_step_bf16_norm.restype = i
     lib.kda_recurrent_step.argtypes = [p] * 7 + [i, i, p]
     lib.kda_recurrent_step.restype = i
     lib.kda_recurrent_k.argtypes = [p] * 8 + [i] * 4 + [p]
@@ -454,6 +459,54 @@ def kda_state_transition_apply(trans_p, trans_q, state, stream=None):
     if rc != KDA_OK:
         raise KdaError("kda_state_transition_apply", rc)
     return state
+
+
+def kda_recurrent_k_bf16_norm(qkv, gate, beta, state, out_gate, o_norm, eps: float, y=None, out=None,
+                              snapshots=None, n_snapshots: int = 0, want_core: bool = True, stream=None):
+    """kda_recurrent_k_bf16 with the gated RMSNorm of every output row fused in.  Returns (y, out): y
+    [B][T][H][128] bfloat16; out the FP32 core rows (None when want_core is False and out is None)."""
+    B, T, H, qkv_ptr = _packed_qkv(qkv, gate)
+    vs = (B, T, H, HEAD_DIM)
+    if y is None:
+        y = torch.empty(vs, dtype=torch.bfloat16, device=qkv.device)
+    if out is None and want_core:
+        out = torch.empty(vs, dtype=torch.float32, device=qkv.device)
+    snap_ptr = None
+    if n_snapshots:
+        if snapshots is None or snapshots.dim() != 5 or snapshots.shape[0] < n_snapshots:
+            raise ValueError("snapshots must be [>= n_snapshots][B][H][128][128]")
+        snap_ptr = _check("snapshots", snapshots, (snapshots.shape[0], B, H, HEAD_DIM, HEAD_DIM))
+    rc = load_library().kda_recurrent_k_bf16_norm(
+        qkv_ptr, _check("gate", gate, vs),
+        _check("beta", beta, (B, T, H)), _check("state", state, (B, H, HEAD_DIM, HEAD_DIM)),
+        _check("out", out, vs) if out is not None else None, _check("out_gate", out_gate, vs, torch.bfloat16),
+        _check("o_norm", o_norm, (HEAD_DIM,), torch.bfloat16), float(eps), _check("y", y, vs, torch.bfloat16),
+        snap_ptr, int(n_snapshots), B, H, T, _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_recurrent_k_bf16_norm", rc)
+    return y, out
+
+
+def kda_recurrent_step_bf16_norm(qkv, gate, beta, state, out_gate, o_norm, eps: float, y=None, out=None,
+                                 want_core: bool = True, stream=None):
+    """One BF16 decode step with the gated RMSNorm fused in (kda_recurrent_k_bf16_norm with T = 1)."""
+    B, T, H, qkv_ptr = _packed_qkv(qkv, gate)
+    if T != 1:
+        raise ValueError("kda_recurrent_step_bf16_norm takes one row per sequence")
+    vs = (B, 1, H, HEAD_DIM)
+    if y is None:
+        y = torch.empty(vs, dtype=torch.bfloat16, device=qkv.device)
+    if out is None and want_core:
+        out = torch.empty(vs, dtype=torch.float32, device=qkv.device)
+    rc = load_library().kda_recurrent_step_bf16_norm(
+        qkv_ptr, _check("gate", gate, vs),
+        _check("beta", beta, (B, 1, H)), _check("state", state, (B, H, HEAD_DIM, HEAD_DIM)),
+        _check("out", out, vs) if out is not None else None, _check("out_gate", out_gate, vs, torch.bfloat16),
+        _check("o_norm", o_norm, (HEAD_DIM,), torch.bfloat16), float(eps), _check("y", y, vs, torch.bfloat16), B, H,
+        _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_recurrent_step_bf16_norm", rc)
+    return y, out
 
 
 def kda_gated_rmsnorm(core, out_gate, o_norm, eps: float, out=None, stream=None):

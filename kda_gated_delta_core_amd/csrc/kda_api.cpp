@@ -457,6 +457,41 @@ KDA_API int kda_recurrent_step_bf16(const uint16_t* qkv, const float* gate, cons
     return kda_recurrent_k_bf16(qkv, gate, beta, state, out, nullptr, 0, batch, heads, 1, stream);
 }
 
+KDA_API int kda_recurrent_k_bf16_norm(const uint16_t* qkv, const float* gate, const float* beta, float* state,
+                                      float* out, const uint16_t* out_gate, const uint16_t* o_norm, float eps,
+                                      uint16_t* y, float* snapshots, int n_snapshots, int batch, int heads, int T,
+                                      void* stream)
+{
+    if (!qkv || !gate || !beta || !state || !out_gate || !o_norm || !y) return KDA_ERR_INVALID_ARG;
+    if (!aligned({qkv, gate, state, out, snapshots, out_gate, o_norm, y}) || !aligned({beta}, 4))
+        return KDA_ERR_INVALID_ARG;
+    if (!(isfinite(eps) && eps >= KDA_GATED_RMSNORM_MIN_EPS)) return KDA_ERR_INVALID_ARG;
+    if (batch < 1 || heads < 1 || T < 1) return KDA_ERR_INVALID_ARG;
+    if (n_snapshots < 0 || n_snapshots > T || (n_snapshots > 0 && !snapshots)) return KDA_ERR_INVALID_ARG;
+    const int64_t vec = mul({batch, T, heads, KDA_HEAD_DIM});
+    const int64_t sca = mul({batch, T, heads});
+    const int64_t st = mul({batch, heads, KDA_HEAD_DIM, KDA_HEAD_DIM});
+    const int64_t sn = mul({n_snapshots, batch, heads, KDA_HEAD_DIM, KDA_HEAD_DIM});
+    if (vec < 0 || sca < 0 || st < 0 || sn < 0) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)batch * heads > 0x7fffffffLL - 8) return KDA_ERR_INVALID_ARG;  // one workgroup per head
+    const Range r[] = {{y, vec * 2},       {state, st * 4},        {out, vec * 4},
+                       {n_snapshots ? snapshots : nullptr, sn * 4}, {qkv, vec * 6}, {gate, vec * 4},
+                       {beta, sca * 4},    {out_gate, vec * 2},    {o_norm, KDA_HEAD_DIM * 2}};
+    if (any_overlap(r, 9, 4)) return KDA_ERR_INVALID_ARG;
+    const int rc = kda::launch_recurrent_norm(qkv, gate, beta, state, out, n_snapshots ? snapshots : nullptr,
+                                              n_snapshots, batch, heads, T, out_gate, o_norm, y, eps,
+                                              static_cast<hipStream_t>(stream));
+    return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+KDA_API int kda_recurrent_step_bf16_norm(const uint16_t* qkv, const float* gate, const float* beta, float* state,
+                                         float* out, const uint16_t* out_gate, const uint16_t* o_norm, float eps,
+                                         uint16_t* y, int batch, int heads, void* stream)
+{
+    return kda_recurrent_k_bf16_norm(qkv, gate, beta, state, out, out_gate, o_norm, eps, y, nullptr, 0, batch, heads,
+                                     1, stream);
+}
+
 KDA_API int kda_gated_rmsnorm(const float* core, const uint16_t* out_gate, const uint16_t* o_norm, uint16_t* out,
                               int rows, int heads, float eps, void* stream)
 {

@@ -183,17 +183,34 @@ __device__ __forceinline__ float4 rec_row(float4 (&s)[G::kRows], const float* s_
     return o;
 }
 
+// The sigmoid-gated RMSNorm of each output row (module page, pipeline line: the core's output goes
+// through an RMSNorm with weight o_norm, gated by a sigmoid of g_b(g_a(h))), done where a whole-head
+// workgroup has the row: y = x / sqrt(mean(x^2) + eps) * o_norm * sigmoid(out_gate), the sum of
+// squares and the scale in FP64, the products in FP32, y rounded to BF16 (the arithmetic of
+// gated_rmsnorm_kernel, with the 128 squares summed in another order).
+struct NormParams {
+    const unsigned short* out_gate;  // [B][T][H][128] BF16
+    const unsigned short* o_norm;    // [128] BF16
+    unsigned short* y;               // [B][T][H][128] BF16
+    double eps;
+};
+__device__ __forceinline__ float norm_sigmoid(float g) { return 1.0f / (1.0f + expf(-g)); }
+
 // kGated: the gate comes from kda_gate of gp.g_raw (gate not read) and beta holds the logits,
 // passed through the sigmoid here (see GateParams).
-template <int NSLICE, bool kPackedBf16, int THREADS = 256, bool kGated = false>
+// kNorm (whole-head workgroups only): each output row also goes through the gated RMSNorm into
+// np.y; out may then be null (the FP32 row is not stored).
+template <int NSLICE, bool kPackedBf16, int THREADS = 256, bool kGated = false, bool kNorm = false>
 __global__ __launch_bounds__(THREADS) void recurrent_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                         const float* __restrict__ v,
                                                         const unsigned short* __restrict__ qkv,
                                                         const float* __restrict__ gate,
                                                         const float* __restrict__ beta, float* __restrict__ state,
                                                         float* __restrict__ out, float* __restrict__ snaps,
-                                                        int n_snap, int batch, int heads, int T, GateParams gp)
+                                                        int n_snap, int batch, int heads, int T, GateParams gp,
+                                                        NormParams np = NormParams{})
 {
+    static_assert(!kNorm || NSLICE == 1, "the fused norm needs the whole row in one workgroup");
     using G = RecGeom<NSLICE, THREADS>;
     const int tid = threadIdx.x;
     // blocks come in groups of 8 * NSLICE: 8 heads, slice s of head j at 8 s + j
@@ -254,7 +271,26 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(const float* __restr
         }
         __syncthreads();
         const float4 o = rec_row<G>(s, s_k, s_q, s_a, s_red, s_tot, vv, bt, cg, rg, wave, lane);
-        if (rg == 0) st4(out + row * kD + col, o);
+        if (rg == 0 && (!kNorm || out)) st4(out + row * kD + col, o);
+        if constexpr (kNorm) {
+            // row group 0 (lanes 0..31 of wave 0) holds the 128 outputs, 4 adjacent columns a lane
+            if (rg == 0) {
+                double ss = (double)o.x * o.x + (double)o.y * o.y + (double)o.z * o.z + (double)o.w * o.w;
+#pragma unroll
+                for (int off = 1; off < G::kColGroups; off <<= 1) ss += __shfl_xor(ss, off, G::kColGroups);
+                const double r = 1.0 / sqrt(ss * (1.0 / kD) + np.eps);
+                const uint2 g2 = *reinterpret_cast<const uint2*>(np.out_gate + row * kD + col);
+                const uint2 w2 = *reinterpret_cast<const uint2*>(np.o_norm + col);
+                const float x[4] = {o.x, o.y, o.z, o.w};
+                const unsigned gb[4] = {g2.x & 0xffffu, g2.x >> 16, g2.y & 0xffffu, g2.y >> 16};
+                const unsigned wb[4] = {w2.x & 0xffffu, w2.x >> 16, w2.y & 0xffffu, w2.y >> 16};
+                unsigned yb[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    yb[e] = f32_to_bf16((float)(x[e] * r) * bf16_to_f32(wb[e]) * norm_sigmoid(bf16_to_f32(gb[e])));
+                *reinterpret_cast<uint2*>(np.y + row * kD + col) = make_uint2(yb[0] | (yb[1] << 16), yb[2] | (yb[3] << 16));
+            }
+        }
         if (t < n_snap) {
             // snapshots are ordinary (cacheable) stores: a caller verifying
             // speculative rows reads the accepted one back soon after
@@ -284,6 +320,24 @@ int launch_recurrent(const float* q, const float* k, const float* v, const uint1
         hipLaunchKernelGGL((recurrent_kernel<kRecSlices, false, kRecThreads>), dim3(grid), dim3(kRecThreads), 0,
                            stream, q, k, v, nullptr, gate, beta, state, out, snaps, n_snap, batch, heads, T,
                            GateParams{});
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// The decode step / k-row walk on BF16 q | k | v with the gated RMSNorm of every output row fused
+// in: one 1024-thread workgroup per (sequence, head), the whole row in one wave.
+constexpr int kNormRecThreads = 1024;
+
+int launch_recurrent_norm(const uint16_t* qkv, const float* gate, const float* beta, float* state, float* out,
+                          float* snaps, int n_snap, int batch, int heads, int T, const uint16_t* out_gate,
+                          const uint16_t* o_norm, uint16_t* y, float eps, hipStream_t stream)
+{
+    const unsigned grid = ((unsigned)batch * (unsigned)heads + 7u) / 8u * 8u;
+    const NormParams np{reinterpret_cast<const unsigned short*>(out_gate),
+                        reinterpret_cast<const unsigned short*>(o_norm), reinterpret_cast<unsigned short*>(y),
+                        (double)eps};
+    hipLaunchKernelGGL((recurrent_kernel<1, true, kNormRecThreads, false, true>), dim3(grid), dim3(kNormRecThreads), 0,
+                       stream, nullptr, nullptr, nullptr, reinterpret_cast<const unsigned short*>(qkv), gate, beta,
+                       state, out, snaps, n_snap, batch, heads, T, GateParams{}, np);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -424,6 +424,24 @@ def test_gated_refusals(lib):
 
 
 @no_gpu
+def test_decode_norm_refusals(lib):
+    qkv, g, b, st, out, og, on, y, sn = P[:9]
+    f = lambda *a, eps=1e-6, n=0, snp=None: lib.kda_recurrent_k_bf16_norm(*a[:7], eps, a[7], snp, n, 2, 3, 4, None)
+    for i in (0, 1, 2, 3, 5, 6, 7):
+        a = [qkv, g, b, st, out, og, on, y]
+        a[i] = None
+        assert f(*a) == kda.KDA_ERR_INVALID_ARG, i
+    assert f(qkv, g, b, st, out, og, on, y, eps=0.0) == kda.KDA_ERR_INVALID_ARG
+    assert f(qkv, g, b, st, out, og, on, y, eps=float("nan")) == kda.KDA_ERR_INVALID_ARG
+    assert f(qkv, g, b, st, out, og, on, y, n=5, snp=sn) == kda.KDA_ERR_INVALID_ARG   # n_snapshots > T
+    assert f(qkv, g, b, st, out, og, on, y, n=1) == kda.KDA_ERR_INVALID_ARG           # snapshots NULL
+    assert f(qkv, g, b, st, out, og, on, st + 64) == kda.KDA_ERR_INVALID_ARG          # y inside state
+    assert f(qkv, g, b, st, out, og, on, y + 2) == kda.KDA_ERR_INVALID_ARG            # y misaligned
+    assert lib.kda_recurrent_step_bf16_norm(qkv, g, b, st, out, None, on, 1e-6, y, 2, 3, None) == \
+        kda.KDA_ERR_INVALID_ARG
+
+
+@no_gpu
 def test_transition_refusals(lib):
     f = lib.kda_chunk_prefill_transition
     bad = kda.KDA_ERR_INVALID_ARG
