@@ -485,9 +485,10 @@ def bench_varlen_fused(torch, kda, ki, name, steps, warmup, timer, K=4):
     return timer.run(step, steps, warmup), lens
 
 
-def bench_prefill(torch, kda, ki, name, steps, warmup, timer):
+def bench_prefill(torch, kda, ki, name, steps, warmup, timer, chunk=None):
+    """kda_chunk_prefill on workload `name` (chunk: another chunk width on the same inputs)."""
     w = ki.WORKLOADS[name]
-    B, H, T, C = w.batch, w.heads, w.T, w.chunk
+    B, H, T, C = w.batch, w.heads, w.T, chunk or w.chunk
     t_pad = -(-T // C) * C
     dev = lambda a: torch.from_numpy(a).cuda()
     tens = {}
@@ -798,6 +799,18 @@ def main():
                "GB_per_s": prefill_bytes(w.batch, w.heads, w.T) / r["launch_avg_s"] / 1e9}
         res.update(extra)
         workloads[name] = res
+    # the T=8192 workload at the narrower chunk widths (the same inputs, rows >= T still the pad)
+    for C in (32, 16):
+        name = f"prefill_h32_t8192_c{C}"
+        if not want(name):
+            continue
+        log(name)
+        w, r, _ = bench_prefill(torch, kda, ki, "prefill_h32_t8192_c64", args.reps or 20, 0 if args.reps else 60,
+                                timer, chunk=C)
+        tf = prefill_flops(w.batch, w.heads, w.T, C) / r["launch_avg_s"] / 1e12
+        workloads[name] = {"tokens_per_s": w.batch * w.T / r["s_per_step"], "ms_per_call": r["s_per_step"] * 1e3,
+                           "call_ms": r["launch_avg_s"] * 1e3, "algorithmic_TFLOP_per_s": tf,
+                           "mfma_frac": tf / MFMA_F32_PEAK_TFLOPS}
     # segment transitions: a whole T=8192 prefill as one segment, and one device's share of the
     # 4 x 32768 prefill split into 8 token segments (4 sequences x 4096 tokens)
     for name, base, T, steps, warm in (("transition_h32_t8192_c64", "prefill_h32_t8192_c64", 8192, 20, 20),

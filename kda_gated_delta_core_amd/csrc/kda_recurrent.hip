@@ -231,45 +231,76 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(const float* __restr
 
     // per-head rate of the gate (kGated)
     const float rate = kGated ? __builtin_amdgcn_exp2f(1.4426950408889634f * gp.a_log[h]) : 0.f;
-    auto decay = [&](size_t row) {  // e^{gate} of channel tid in row `row`
-        if constexpr (kGated)
-            return expf(kda_gate_f32(bf16_to_f32(gp.g_raw[row * kD + tid]), gp.dt_bias[h * kD + tid], rate, gp.lower));
-        else
-            return expf(gate[row * kD + tid]);
-    };
+    const float dtb = kGated && tid < kD ? gp.dt_bias[h * kD + tid] : 0.f;  // the head's bias of channel tid
 
     float* const S_head = state + (size_t)bh * kD * kD;
     float4 s[G::kRows];
 #pragma unroll
     for (int m = 0; m < G::kRows; ++m) s[m] = state_ld(S_head + (size_t)(rg + G::kRowGroups * m) * kD + col);
 
+    // A row's inputs as loaded, still raw: the next row's are requested right after the current one
+    // is staged (into the same registers), ahead of the current row's stores, so the wait for them
+    // never covers a store (the vector memory counter counts loads and stores in order).  Widening, the gate's exponential and
+    // the sigmoids happen only when a row is staged.
+    struct RowIn {
+        float q, k, g;      // FP32 q, k and the gate (FP32 forms)
+        unsigned qb, kb;    // BF16 q, k (packed form), g_raw (gated form: in gb)
+        unsigned gb;
+        float b;            // beta, or its logit (gated form)
+        float4 v;           // FP32 v
+        uint2 vb;           // BF16 v (packed form)
+    };
+    auto load_row = [&](int tt, RowIn& r) {
+        const size_t rr = ((size_t)b * T + tt) * heads + h;  // (b, tt, h)
+        if constexpr (kPackedBf16) {
+            // q of head h in token (b, tt); k and v follow at a stride of heads * 128
+            const unsigned short* const x = qkv + (((size_t)b * T + tt) * 3 * heads + h) * kD;
+            const size_t part = (size_t)heads * kD;
+            if (tid < kD) {
+                r.kb = x[part + tid];
+                r.qb = x[tid];
+                r.g = gate[rr * kD + tid];
+            }
+            r.vb = *reinterpret_cast<const uint2*>(x + 2 * part + col);
+        } else {
+            if (tid < kD) {
+                r.k = k[rr * kD + tid];
+                r.q = q[rr * kD + tid];
+                if constexpr (kGated) r.gb = gp.g_raw[rr * kD + tid];
+                else r.g = gate[rr * kD + tid];
+            }
+            r.v = ld4(v + rr * kD + col);
+        }
+        r.b = beta[rr];
+    };
+    RowIn cur;
+    load_row(0, cur);
     for (int t = 0; t < T; ++t) {
         const size_t row = ((size_t)b * T + t) * heads + h;  // (b, t, h)
         float bt;
         float4 vv;
-        if constexpr (kPackedBf16) {
-            // q of head h in token (b, t); k and v follow at a stride of heads * 128
-            const unsigned short* const x = qkv + (((size_t)b * T + t) * 3 * heads + h) * kD;
-            const size_t part = (size_t)heads * kD;
-            if (tid < kD) {
-                s_k[tid] = bf16_to_f32(x[part + tid]);
-                s_q[tid] = bf16_to_f32(x[tid]);
-                s_a[tid] = decay(row);
+        if (tid < kD) {
+            if constexpr (kPackedBf16) {
+                s_k[tid] = bf16_to_f32(cur.kb);
+                s_q[tid] = bf16_to_f32(cur.qb);
+            } else {
+                s_k[tid] = cur.k;
+                s_q[tid] = cur.q;
             }
-            bt = kGated ? sigmoid_f32(beta[row]) : beta[row];
-            const uint2 u = *reinterpret_cast<const uint2*>(x + 2 * part + col);
-            vv = make_float4(bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xffffu),
-                             bf16_to_f32(u.y >> 16));
-        } else {
-            if (tid < kD) {
-                s_k[tid] = k[row * kD + tid];
-                s_q[tid] = q[row * kD + tid];
-                s_a[tid] = decay(row);
-            }
-            bt = kGated ? sigmoid_f32(beta[row]) : beta[row];
-            vv = ld4(v + row * kD + col);
+            if constexpr (kGated)
+                s_a[tid] = expf(kda_gate_f32(bf16_to_f32(cur.gb), dtb, rate, gp.lower));
+            else
+                s_a[tid] = expf(cur.g);
         }
+        bt = kGated ? sigmoid_f32(cur.b) : cur.b;
+        if constexpr (kPackedBf16)
+            vv = make_float4(bf16_to_f32(cur.vb.x & 0xffffu), bf16_to_f32(cur.vb.x >> 16),
+                             bf16_to_f32(cur.vb.y & 0xffffu), bf16_to_f32(cur.vb.y >> 16));
+        else
+            vv = cur.v;
         __syncthreads();
+        // the next row's inputs, into the registers the staging above has just consumed
+        if (t + 1 < T) load_row(t + 1, cur);
         const float4 o = rec_row<G>(s, s_k, s_q, s_a, s_red, s_tot, vv, bt, cg, rg, wave, lane);
         if (rg == 0 && (!kNorm || out)) st4(out + row * kD + col, o);
         if constexpr (kNorm) {
@@ -292,11 +323,11 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(const float* __restr
             }
         }
         if (t < n_snap) {
-            // snapshots are ordinary (cacheable) stores: a caller verifying
-            // speculative rows reads the accepted one back soon after
+            // snapshots are streamed like the state (non-temporal stores): at 512 threads x 4
+            // slices that made decode_k ~2% faster than cacheable stores (interleaved A/B)
             float* snap = snaps + ((size_t)t * batch * heads + bh) * kD * kD;
 #pragma unroll
-            for (int m = 0; m < G::kRows; ++m) st4(snap + (size_t)(rg + G::kRowGroups * m) * kD + col, s[m]);
+            for (int m = 0; m < G::kRows; ++m) state_st(snap + (size_t)(rg + G::kRowGroups * m) * kD + col, s[m]);
         }
     }
 #pragma unroll
