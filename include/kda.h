@@ -70,8 +70,9 @@ extern "C" {
 #define KDA_VARLEN_MAX_SEQS (1 << 20)
 /* Smallest eps kda_gated_rmsnorm and the front ends accept. */
 #define KDA_GATED_RMSNORM_MIN_EPS 1e-30f
-/* Largest conv_kernel the front ends accept (config page, validate:
- * the conv kernels keep the sliding window in 4 registers). */
+/* Largest conv_kernel the front ends accept: the config page's validation
+ * caps the window at four taps, and the kernels here hold the window of
+ * every channel in four registers. */
 #define KDA_FRONT_END_MAX_CONV_KERNEL 4
 
 typedef enum {
@@ -195,8 +196,8 @@ int kda_chunk_prefill_gated(const float* q, const float* k, const float* v, cons
  * Chunked prefill of a packed batch of sequences of their own lengths
  * (varlen).  Same computation as kda_chunk_prefill for every sequence, with
  * the sequences stored back to back instead of padded to a common length (the
- * pages pad prefill buffers per call to a whole number of chunks, workspace
- * page; here each sequence's last chunk is cut at its end instead).
+ * workspace page sizes its prefill buffers in whole chunks; here each
+ * sequence's last chunk is cut at its end instead).
  *
  *   q, k, v, gate, out : [total_tokens][heads][128];  beta : [total_tokens][heads]
  *   state              : [n_seqs][heads][128][128], read and updated in place
@@ -227,7 +228,7 @@ int kda_chunk_prefill_varlen(const float* q, const float* k, const float* v, con
  * (causal conv1d + SiLU, L2 on q and k; module page, pipeline line) runs
  * inside the prefill's prepare kernel, which reads the BF16 projections
  * instead of FP32 q, k, v rows, so those rows never travel through HBM
- * (workspace page: q_f32 / k_f32 / v_f32 are not needed).
+ * (workspace page, fields q_f32 / k_f32 / v_f32: unused on this path).
  *
  *   qkv        : [batch][T][3 * heads * 128] BF16, q | k | v per token (no padding)
  *   conv_w     : [3 * heads * 128][conv_kernel] BF16
@@ -473,9 +474,10 @@ int kda_gated_rmsnorm(const float* core, const uint16_t* out_gate, const uint16_
 /*
  * The step before the core on the decode path: the depthwise causal conv1d
  * update, SiLU and L2 on q and k in one call (module page, pipeline line:
- * conv1d + SiLU, then L2 on q and k only, v never normalised; decode fuses
- * conv, SiLU and L2 in one kernel; the conv state keeps conv_kernel slots and
- * is shifted left before convolving).  T rows of each sequence are walked in
+ * conv1d and SiLU on q, k, v, then L2 on q and k alone, so v is never
+ * normalised; the decode form there is a single kernel too; the conv state
+ * holds conv_kernel slots that move one place toward the oldest before each
+ * convolution).  T rows of each sequence are walked in
  * order (T = 1 for a decode step, T = k for decode_k).  For every row and
  * every channel c of conv_dim = 3 * heads * 128 (q | k | v, in that order):
  *
@@ -534,8 +536,9 @@ int kda_decode_front_end_bf16(const uint16_t* qkv, const uint16_t* conv_w, float
  * The step before the core on the prefill path: the same conv1d update, SiLU
  * and L2 on q and k as kda_decode_front_end, over the T tokens of a prefill,
  * written into the chunk-padded FP32 inputs kda_chunk_prefill reads
- * (workspace page, q_f32 / k_f32 / v_f32: [T_pad, qkv] FP32, post-L2 q,
- * post-L2 k, raw v, prefill only; module page, pipeline line).  The pages
+ * (workspace page, fields q_f32 / k_f32 / v_f32: the FP32 padded prefill
+ * inputs, q and k after their L2 step and v as convolved; module page,
+ * pipeline line).  The pages
  * round the conv output to BF16 (conv_out) before the L2; here conv, SiLU
  * and L2 are one pass and the values stay FP32 throughout.
  *

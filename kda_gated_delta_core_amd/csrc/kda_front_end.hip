@@ -1,9 +1,9 @@
 // Decode front end of the KDA block, gfx950: the depthwise causal conv1d
 // update, SiLU, and L2 on q and k, fused into one kernel whose output is the
-// q, k, v the recurrent core consumes (module page, pipeline line: conv1d +
-// SiLU, then L2 on q and k only; decode fuses conv, SiLU and L2 in one kernel;
-// the conv state keeps conv_kernel slots and is shifted left before
-// convolving).  Per sequence, token and channel c of the conv_dim = 3 H 128
+// q, k, v the recurrent core consumes (module page, pipeline line: conv1d and
+// SiLU on q, k, v, then L2 on q and k alone; on that page the decode form does
+// all three steps in a single kernel, and the conv state holds conv_kernel
+// slots that shift by one before each convolution).  Per sequence, token and channel c of the conv_dim = 3 H 128
 // channels (q | k | v):
 //
 //     slots <- (slots[1], ..., slots[K-1], x_c)        K = conv_kernel <= 4

@@ -210,9 +210,9 @@ def gated_rmsnorm(core, out_gate_bits, o_norm_bits, eps: float) -> np.ndarray:
 
 
 def decode_front_end(qkv_bits, conv_w_bits, conv_state, heads: int, l2_eps: float, n_snap: int = 0):
-    """The decode front end, fp64, token by token (module page, pipeline line: conv1d + SiLU, then L2
-    on q and k only; the conv state keeps conv_kernel slots and is shifted left before convolving;
-    decode fuses conv, SiLU and L2.  Workspace page, qkv_proj [T, conv_dim] BF16 with q | k | v per
+    """The decode front end, fp64, token by token (module page, pipeline line: conv1d and SiLU on
+    q, k, v, then L2 on q and k alone; the conv state holds conv_kernel slots that move one place
+    toward the oldest before each convolution.  Workspace page, qkv_proj [T, conv_dim] BF16 with q | k | v per
     token; config page, Glm5NextKdaWeights::conv [conv_dim, conv_kernel] BF16 (depthwise, no bias),
     conv_state_elems [conv_dim, conv_kernel] FP32, l2_eps applied as 1/sqrt(sum + eps)).
 
