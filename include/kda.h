@@ -533,6 +533,61 @@ int kda_decode_front_end_bf16(const uint16_t* qkv, const uint16_t* conv_w, float
                               float l2_eps, void* stream);
 
 /*
+ * The whole decode step of the block between its projections, in one kernel:
+ * the decode front end (conv1d update, SiLU, L2 on q and k), the recurrence,
+ * and the sigmoid-gated RMSNorm of every output row (module page, pipeline
+ * line, from the conv to the norm; workspace page, fields qkv_proj, conv_out,
+ * core and o_norm_out).  One workgroup holds a whole head: three of its waves
+ * run the front end of the head's q, k and v vectors with the code of
+ * kda_decode_front_end, so the FP32 q, k, v never leave the chip, and the
+ * core's rows go through the norm where the workgroup has them.
+ *
+ *   qkv_proj, conv_w, conv_state, conv_snapshots, conv_kernel, l2_eps :
+ *            as kda_decode_front_end (qkv_proj its qkv)
+ *   gate, beta, state, snapshots, n_snapshots : as kda_recurrent_k; one
+ *            n_snapshots counts both kinds of snapshot (both pointers
+ *            non-NULL when it is > 0)
+ *   out_gate, o_norm, norm_eps, y : as kda_recurrent_k_bf16_norm (its eps)
+ *   out    : [batch][T][heads][128] FP32 core rows, or NULL (then not stored)
+ *
+ * conv_state and conv_snapshots equal kda_decode_front_end's bit for bit, and
+ * so do the q, k, v the recurrence consumes; the core rows, state and
+ * snapshots are within the stated tolerance of kda_decode_front_end followed
+ * by kda_recurrent_k (a whole-head reduction tree here, unrounded q, k, v
+ * rather than kda_decode_front_end_bf16's BF16 ones); y is within one BF16
+ * unit in the last place of the norm of the call's own core rows.  T rows of
+ * kda_decode_fused_k equal T successive kda_decode_fused_step calls bit for
+ * bit.  Refusals: those of kda_decode_front_end and kda_recurrent_k_bf16_norm.
+ */
+int kda_decode_fused_k(const uint16_t* qkv_proj, const uint16_t* conv_w, float* conv_state, float* conv_snapshots,
+                       const float* gate, const float* beta, float* state, float* snapshots, int n_snapshots,
+                       const uint16_t* out_gate, const uint16_t* o_norm, float norm_eps, float l2_eps, uint16_t* y,
+                       float* out, int batch, int heads, int T, int conv_kernel, void* stream);
+int kda_decode_fused_step(const uint16_t* qkv_proj, const uint16_t* conv_w, float* conv_state, const float* gate,
+                          const float* beta, float* state, const uint16_t* out_gate, const uint16_t* o_norm,
+                          float norm_eps, float l2_eps, uint16_t* y, float* out, int batch, int heads,
+                          int conv_kernel, void* stream);
+
+/*
+ * kda_decode_fused_k / kda_decode_fused_step with the gate and beta formed in
+ * the kernel from the gate's projection and beta's logits, as
+ * kda_recurrent_k_gated forms them (g_raw, beta_logit, dt_bias, a_log,
+ * gate_lower_bound as there; gate and beta are not taken).  Everything else as
+ * kda_decode_fused_k; refusals also those of kda_recurrent_k_gated.
+ */
+int kda_decode_fused_k_gated(const uint16_t* qkv_proj, const uint16_t* conv_w, float* conv_state,
+                             float* conv_snapshots, const uint16_t* g_raw, const float* beta_logit,
+                             const float* dt_bias, const float* a_log, float gate_lower_bound, float* state,
+                             float* snapshots, int n_snapshots, const uint16_t* out_gate, const uint16_t* o_norm,
+                             float norm_eps, float l2_eps, uint16_t* y, float* out, int batch, int heads, int T,
+                             int conv_kernel, void* stream);
+int kda_decode_fused_step_gated(const uint16_t* qkv_proj, const uint16_t* conv_w, float* conv_state,
+                                const uint16_t* g_raw, const float* beta_logit, const float* dt_bias,
+                                const float* a_log, float gate_lower_bound, float* state, const uint16_t* out_gate,
+                                const uint16_t* o_norm, float norm_eps, float l2_eps, uint16_t* y, float* out,
+                                int batch, int heads, int conv_kernel, void* stream);
+
+/*
  * The step before the core on the prefill path: the same conv1d update, SiLU
  * and L2 on q and k as kda_decode_front_end, over the T tokens of a prefill,
  * written into the chunk-padded FP32 inputs kda_chunk_prefill reads

@@ -37,7 +37,8 @@ EXPORTED = ("kda_status_string", "kda_chunk_prefill_workspace_bytes", "kda_chunk
             "kda_prefill_front_end_varlen", "kda_chunk_prefill_transition", "kda_state_transition_apply", "kda_chunk_scan",
             "kda_chunk_prefill_fused", "kda_chunk_prefill_varlen_fused", "kda_chunk_prefill_noalloc",
             "kda_chunk_prefill_gated", "kda_recurrent_k_gated", "kda_recurrent_step_gated",
-            "kda_recurrent_k_bf16_norm", "kda_recurrent_step_bf16_norm")
+            "kda_recurrent_k_bf16_norm", "kda_recurrent_step_bf16_norm", "kda_decode_fused_k", "kda_decode_fused_step",
+            "kda_decode_fused_k_gated", "kda_decode_fused_step_gated")
 STATIC_WORKSPACE_BYTES = 256 << 20
 GATED_RMSNORM_MIN_EPS = 1e-30
 
@@ -80,6 +81,14 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_recurrent_k_bf16_norm.restype = i
     lib.kda_recurrent_step_bf16_norm.argtypes = [p] * 7 + [f, p] + [i, i, p]
     lib.kda_recurrent_step_bf16_norm.restype = i
+    lib.kda_decode_fused_k.argtypes = [p] * 8 + [i] + [p] * 2 + [f, f, p, p] + [i] * 4 + [p]
+    lib.kda_decode_fused_k.restype = i
+    lib.kda_decode_fused_step.argtypes = [p] * 8 + [f, f, p, p] + [i] * 3 + [p]
+    lib.kda_decode_fused_step.restype = i
+    lib.kda_decode_fused_k_gated.argtypes = [p] * 8 + [f, p, p, i, p, p, f, f, p, p] + [i] * 4 + [p]
+    lib.kda_decode_fused_k_gated.restype = i
+    lib.kda_decode_fused_step_gated.argtypes = [p] * 7 + [f, p, p, p, f, f, p, p] + [i] * 3 + [p]
+    lib.kda_decode_fused_step_gated.restype = i
     lib.kda_recurrent_step.argtypes = [p] * 7 + [i, i, p]
     lib.kda_recurrent_step.restype = i
     lib.kda_recurrent_k.argtypes = [p] * 8 + [i] * 4 + [p]
@@ -506,6 +515,107 @@ def kda_recurrent_step_bf16_norm(qkv, gate, beta, state, out_gate, o_norm, eps: 
         _stream_ptr(stream))
     if rc != KDA_OK:
         raise KdaError("kda_recurrent_step_bf16_norm", rc)
+    return y, out
+
+
+def _fused_args(qkv_proj, conv_w, conv_state, heads, out_gate, o_norm, y, out, snapshots, conv_snapshots,
+                n_snapshots, want_core):
+    if not isinstance(qkv_proj, torch.Tensor) or qkv_proj.dim() != 3:
+        raise ValueError("qkv_proj must be [batch][T][3 * heads * 128]")
+    B, T, C = qkv_proj.shape
+    if C != 3 * heads * HEAD_DIM:
+        raise ValueError(f"qkv_proj has {C} channels, expected 3 * {heads} * {HEAD_DIM}")
+    if conv_w.dim() != 2:
+        raise ValueError("conv_w must be [conv_dim][conv_kernel]")
+    K = conv_w.shape[1]
+    vs = (B, T, heads, HEAD_DIM)
+    if y is None:
+        y = torch.empty(vs, dtype=torch.bfloat16, device=qkv_proj.device)
+    if out is None and want_core:
+        out = torch.empty(vs, dtype=torch.float32, device=qkv_proj.device)
+    snap_ptr = csnap_ptr = None
+    if n_snapshots:
+        if snapshots is None or snapshots.dim() != 5 or snapshots.shape[0] < n_snapshots:
+            raise ValueError("snapshots must be [>= n_snapshots][B][H][128][128]")
+        if conv_snapshots is None or conv_snapshots.dim() != 4 or conv_snapshots.shape[0] < n_snapshots:
+            raise ValueError("conv_snapshots must be [>= n_snapshots][B][conv_dim][conv_kernel]")
+        snap_ptr = _check("snapshots", snapshots, (snapshots.shape[0], B, heads, HEAD_DIM, HEAD_DIM))
+        csnap_ptr = _check("conv_snapshots", conv_snapshots, (conv_snapshots.shape[0], B, C, K))
+    head = [_check("qkv_proj", qkv_proj, (B, T, C), torch.bfloat16), _check("conv_w", conv_w, (C, K), torch.bfloat16),
+            _check("conv_state", conv_state, (B, C, K))]
+    tail = [_check("out_gate", out_gate, vs, torch.bfloat16), _check("o_norm", o_norm, (HEAD_DIM,), torch.bfloat16)]
+    return B, T, K, vs, y, out, snap_ptr, csnap_ptr, head, tail
+
+
+def kda_decode_fused_k(qkv_proj, conv_w, conv_state, gate, beta, state, out_gate, o_norm, heads: int,
+                       norm_eps: float, l2_eps: float, y=None, out=None, snapshots=None, conv_snapshots=None,
+                       n_snapshots: int = 0, want_core: bool = True, stream=None):
+    """The decode walk from the raw projections in one kernel: front end, recurrence and gated RMSNorm.
+    qkv_proj: bfloat16 [B][T][3 H 128]; conv_w, conv_state: as kda_decode_front_end; gate: [B][T][H][128];
+    beta: [B][T][H]; state in place; out_gate: bfloat16 [B][T][H][128]; o_norm: bfloat16 [128].
+    Returns (y, out): y bfloat16 [B][T][H][128]; out the FP32 core rows (None without want_core)."""
+    B, T, K, vs, y, out, sp, cp, head, tail = _fused_args(qkv_proj, conv_w, conv_state, heads, out_gate, o_norm, y,
+                                                          out, snapshots, conv_snapshots, n_snapshots, want_core)
+    rc = load_library().kda_decode_fused_k(
+        *head, cp, _check("gate", gate, vs), _check("beta", beta, (B, T, heads)),
+        _check("state", state, (B, heads, HEAD_DIM, HEAD_DIM)), sp, int(n_snapshots), *tail, float(norm_eps),
+        float(l2_eps), _check("y", y, vs, torch.bfloat16), _check("out", out, vs) if out is not None else None, B,
+        heads, T, K, _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_decode_fused_k", rc)
+    return y, out
+
+
+def kda_decode_fused_step(qkv_proj, conv_w, conv_state, gate, beta, state, out_gate, o_norm, heads: int,
+                          norm_eps: float, l2_eps: float, y=None, out=None, want_core: bool = True, stream=None):
+    """One decode step from the raw projections (kda_decode_fused_k with T = 1).  Returns (y, out)."""
+    B, T, K, vs, y, out, _, _, head, tail = _fused_args(qkv_proj, conv_w, conv_state, heads, out_gate, o_norm, y,
+                                                        out, None, None, 0, want_core)
+    if T != 1:
+        raise ValueError("kda_decode_fused_step takes one row per sequence")
+    rc = load_library().kda_decode_fused_step(
+        *head, _check("gate", gate, vs), _check("beta", beta, (B, 1, heads)),
+        _check("state", state, (B, heads, HEAD_DIM, HEAD_DIM)), *tail, float(norm_eps), float(l2_eps),
+        _check("y", y, vs, torch.bfloat16), _check("out", out, vs) if out is not None else None, B, heads, K,
+        _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_decode_fused_step", rc)
+    return y, out
+
+
+def kda_decode_fused_k_gated(qkv_proj, conv_w, conv_state, g_raw, beta_logit, dt_bias, a_log, gate_lower_bound: float,
+                             state, out_gate, o_norm, heads: int, norm_eps: float, l2_eps: float, y=None, out=None,
+                             snapshots=None, conv_snapshots=None, n_snapshots: int = 0, want_core: bool = True,
+                             stream=None):
+    """kda_decode_fused_k with the gate and beta formed in the kernel from g_raw and beta_logit (as
+    kda_recurrent_k_gated).  Returns (y, out)."""
+    B, T, K, vs, y, out, sp, cp, head, tail = _fused_args(qkv_proj, conv_w, conv_state, heads, out_gate, o_norm, y,
+                                                          out, snapshots, conv_snapshots, n_snapshots, want_core)
+    g, b, dt, al = _gate_args(g_raw, beta_logit, dt_bias, a_log, B, T, heads)
+    rc = load_library().kda_decode_fused_k_gated(
+        *head, cp, g, b, dt, al, float(gate_lower_bound), _check("state", state, (B, heads, HEAD_DIM, HEAD_DIM)), sp,
+        int(n_snapshots), *tail, float(norm_eps), float(l2_eps), _check("y", y, vs, torch.bfloat16),
+        _check("out", out, vs) if out is not None else None, B, heads, T, K, _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_decode_fused_k_gated", rc)
+    return y, out
+
+
+def kda_decode_fused_step_gated(qkv_proj, conv_w, conv_state, g_raw, beta_logit, dt_bias, a_log,
+                                gate_lower_bound: float, state, out_gate, o_norm, heads: int, norm_eps: float,
+                                l2_eps: float, y=None, out=None, want_core: bool = True, stream=None):
+    """One gated decode step from the raw projections (kda_decode_fused_k_gated with T = 1)."""
+    B, T, K, vs, y, out, _, _, head, tail = _fused_args(qkv_proj, conv_w, conv_state, heads, out_gate, o_norm, y,
+                                                        out, None, None, 0, want_core)
+    if T != 1:
+        raise ValueError("kda_decode_fused_step_gated takes one row per sequence")
+    g, b, dt, al = _gate_args(g_raw, beta_logit, dt_bias, a_log, B, 1, heads)
+    rc = load_library().kda_decode_fused_step_gated(
+        *head, g, b, dt, al, float(gate_lower_bound), _check("state", state, (B, heads, HEAD_DIM, HEAD_DIM)), *tail,
+        float(norm_eps), float(l2_eps), _check("y", y, vs, torch.bfloat16),
+        _check("out", out, vs) if out is not None else None, B, heads, K, _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_decode_fused_step_gated", rc)
     return y, out
 
 

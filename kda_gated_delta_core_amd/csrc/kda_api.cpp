@@ -540,6 +540,60 @@ int front_end_checked(const uint16_t* qkv, const uint16_t* conv_w, float* conv_s
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 
+// The decode step from the raw projections (front end, gate, core, gated RMSNorm in one kernel).
+int decode_fused_checked(const uint16_t* qkv_proj, const uint16_t* conv_w, float* conv_state, float* conv_snapshots,
+                         const float* gate, const float* beta, const kda::GateParams* gp, float* state,
+                         float* snapshots, int n_snapshots, const uint16_t* out_gate, const uint16_t* o_norm,
+                         float norm_eps, float l2_eps, uint16_t* y, float* out, int batch, int heads, int T,
+                         int conv_kernel, void* stream)
+{
+    if (!qkv_proj || !conv_w || !conv_state || !beta || !state || !out_gate || !o_norm || !y)
+        return KDA_ERR_INVALID_ARG;
+    if (gp ? !gate_inputs_ok(gp->g_raw, gp->dt_bias, gp->a_log, gp->lower) : !gate) return KDA_ERR_INVALID_ARG;
+    if (!aligned({qkv_proj, conv_w, conv_state, conv_snapshots, gate, state, snapshots, out_gate, o_norm, y, out}) ||
+        !aligned({beta}, 4))
+        return KDA_ERR_INVALID_ARG;
+    if (batch < 1 || heads < 1 || T < 1 || heads > KDA_PREFILL_MAX_HEADS) return KDA_ERR_INVALID_ARG;
+    if (n_snapshots < 0 || n_snapshots > T || (n_snapshots > 0 && (!snapshots || !conv_snapshots)))
+        return KDA_ERR_INVALID_ARG;
+    if (conv_kernel < 1) return KDA_ERR_INVALID_ARG;
+    if (!(isfinite(norm_eps) && norm_eps >= KDA_GATED_RMSNORM_MIN_EPS)) return KDA_ERR_INVALID_ARG;
+    if (!(isfinite(l2_eps) && l2_eps >= KDA_GATED_RMSNORM_MIN_EPS)) return KDA_ERR_INVALID_ARG;
+    if (conv_kernel > KDA_FRONT_END_MAX_CONV_KERNEL) return KDA_ERR_UNSUPPORTED;
+    const int64_t C = 3 * (int64_t)heads * KDA_HEAD_DIM;
+    const int64_t x = mul({batch, T, C});
+    const int64_t w = mul({C, conv_kernel});
+    const int64_t cst = mul({batch, C, conv_kernel});
+    const int64_t csn = mul({n_snapshots, batch, C, conv_kernel});
+    const int64_t vec = mul({batch, T, heads, KDA_HEAD_DIM});
+    const int64_t sca = mul({batch, T, heads});
+    const int64_t st = mul({batch, heads, KDA_HEAD_DIM, KDA_HEAD_DIM});
+    const int64_t sn = mul({n_snapshots, batch, heads, KDA_HEAD_DIM, KDA_HEAD_DIM});
+    if (x < 0 || w < 0 || cst < 0 || csn < 0 || vec < 0 || sca < 0 || st < 0 || sn < 0) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)batch * heads > 0x7fffffffLL - 8) return KDA_ERR_INVALID_ARG;  // one workgroup per head
+    if (!n_snapshots) snapshots = conv_snapshots = nullptr;
+    const Range r[] = {{y, vec * 2},
+                       {state, st * 4},
+                       {out, vec * 4},
+                       {snapshots, sn * 4},
+                       {conv_state, cst * 4},
+                       {conv_snapshots, csn * 4},
+                       {qkv_proj, x * 2},
+                       {conv_w, w * 2},
+                       {gate, vec * 4},
+                       {beta, sca * 4},
+                       {out_gate, vec * 2},
+                       {o_norm, KDA_HEAD_DIM * 2},
+                       {gp ? gp->g_raw : nullptr, vec * 2},
+                       {gp ? gp->dt_bias : nullptr, (int64_t)heads * KDA_HEAD_DIM * 4},
+                       {gp ? gp->a_log : nullptr, (int64_t)heads * 4}};
+    if (any_overlap(r, 15, 6)) return KDA_ERR_INVALID_ARG;
+    const int rc = kda::launch_decode_fused(qkv_proj, conv_w, conv_state, conv_snapshots, gate, beta, gp, state, out,
+                                            snapshots, n_snapshots, batch, heads, T, conv_kernel, out_gate, o_norm, y,
+                                            norm_eps, l2_eps, static_cast<hipStream_t>(stream));
+    return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // namespace
 
 KDA_API int kda_decode_front_end(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q, float* k,
@@ -650,4 +704,49 @@ KDA_API int kda_prefill_front_end_varlen(const uint16_t* qkv, const uint16_t* co
                                                         total_tokens, conv_kernel, l2_eps,
                                                         static_cast<hipStream_t>(stream));
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+KDA_API int kda_decode_fused_k(const uint16_t* qkv_proj, const uint16_t* conv_w, float* conv_state,
+                               float* conv_snapshots, const float* gate, const float* beta, float* state,
+                               float* snapshots, int n_snapshots, const uint16_t* out_gate, const uint16_t* o_norm,
+                               float norm_eps, float l2_eps, uint16_t* y, float* out, int batch, int heads, int T,
+                               int conv_kernel, void* stream)
+{
+    return decode_fused_checked(qkv_proj, conv_w, conv_state, conv_snapshots, gate, beta, nullptr, state, snapshots,
+                                n_snapshots, out_gate, o_norm, norm_eps, l2_eps, y, out, batch, heads, T, conv_kernel,
+                                stream);
+}
+
+KDA_API int kda_decode_fused_step(const uint16_t* qkv_proj, const uint16_t* conv_w, float* conv_state,
+                                  const float* gate, const float* beta, float* state, const uint16_t* out_gate,
+                                  const uint16_t* o_norm, float norm_eps, float l2_eps, uint16_t* y, float* out,
+                                  int batch, int heads, int conv_kernel, void* stream)
+{
+    return kda_decode_fused_k(qkv_proj, conv_w, conv_state, nullptr, gate, beta, state, nullptr, 0, out_gate, o_norm,
+                              norm_eps, l2_eps, y, out, batch, heads, 1, conv_kernel, stream);
+}
+
+KDA_API int kda_decode_fused_k_gated(const uint16_t* qkv_proj, const uint16_t* conv_w, float* conv_state,
+                                     float* conv_snapshots, const uint16_t* g_raw, const float* beta_logit,
+                                     const float* dt_bias, const float* a_log, float gate_lower_bound, float* state,
+                                     float* snapshots, int n_snapshots, const uint16_t* out_gate,
+                                     const uint16_t* o_norm, float norm_eps, float l2_eps, uint16_t* y, float* out,
+                                     int batch, int heads, int T, int conv_kernel, void* stream)
+{
+    const kda::GateParams gp{reinterpret_cast<const unsigned short*>(g_raw), dt_bias, a_log, gate_lower_bound};
+    return decode_fused_checked(qkv_proj, conv_w, conv_state, conv_snapshots, nullptr, beta_logit, &gp, state,
+                                snapshots, n_snapshots, out_gate, o_norm, norm_eps, l2_eps, y, out, batch, heads, T,
+                                conv_kernel, stream);
+}
+
+KDA_API int kda_decode_fused_step_gated(const uint16_t* qkv_proj, const uint16_t* conv_w, float* conv_state,
+                                        const uint16_t* g_raw, const float* beta_logit, const float* dt_bias,
+                                        const float* a_log, float gate_lower_bound, float* state,
+                                        const uint16_t* out_gate, const uint16_t* o_norm, float norm_eps,
+                                        float l2_eps, uint16_t* y, float* out, int batch, int heads, int conv_kernel,
+                                        void* stream)
+{
+    return kda_decode_fused_k_gated(qkv_proj, conv_w, conv_state, nullptr, g_raw, beta_logit, dt_bias, a_log,
+                                    gate_lower_bound, state, nullptr, 0, out_gate, o_norm, norm_eps, l2_eps, y, out,
+                                    batch, heads, 1, conv_kernel, stream);
 }

@@ -32,6 +32,11 @@ int launch_recurrent(const float* q, const float* k, const float* v, const uint1
 long long recurrent_max_units();
 // the BF16 decode with the gated RMSNorm of every output row fused in: y [B][T][H][128] BF16 from
 // out_gate (same layout) and o_norm [128]; out (FP32 core rows) may be null
+int launch_decode_fused(const uint16_t* qkv_proj, const uint16_t* conv_w, float* conv_state, float* conv_snaps,
+                        const float* gate, const float* beta, const GateParams* gp, float* state, float* out,
+                        float* snaps, int n_snap, int batch, int heads, int T, int conv_kernel,
+                        const uint16_t* out_gate, const uint16_t* o_norm, uint16_t* y, float eps, float l2_eps,
+                        hipStream_t stream);
 int launch_recurrent_norm(const uint16_t* qkv, const float* gate, const float* beta, float* state, float* out,
                           float* snaps, int n_snap, int batch, int heads, int T, const uint16_t* out_gate,
                           const uint16_t* o_norm, uint16_t* y, float eps, hipStream_t stream);

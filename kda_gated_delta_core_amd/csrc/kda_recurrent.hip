@@ -34,6 +34,7 @@
 // body is shared, so the BF16 form on BF16 data gives the bits of the FP32
 // form on the widened values.
 #include "kda_common.h"
+#include "kda_front_end.h"
 #include "kda_internal.h"
 
 namespace kda {
@@ -196,11 +197,24 @@ struct NormParams {
 };
 __device__ __forceinline__ float norm_sigmoid(float g) { return 1.0f / (1.0f + expf(-g)); }
 
+// The decode front end inside the kernel (FE_K = conv_kernel > 0): `qkv` then holds the raw BF16
+// projections ([B][T][3 H 128], q | k | v per token), and waves 0, 1, 2 of the whole-head
+// workgroup run the front end of the head's q, k and v vectors with the code of
+// kda_decode_front_end (fe_load, fe_row, fe_store: the same bits), keeping their conv slots in
+// registers for all T rows.
+struct FeParams {
+    const unsigned short* conv_w;  // [3 H 128][K] BF16
+    float* conv_state;             // [B][3 H 128][K] FP32, updated in place
+    float* conv_snaps;             // [n_snap][B][3 H 128][K] FP32 or null
+    double l2_eps;
+};
+
 // kGated: the gate comes from kda_gate of gp.g_raw (gate not read) and beta holds the logits,
 // passed through the sigmoid here (see GateParams).
 // kNorm (whole-head workgroups only): each output row also goes through the gated RMSNorm into
 // np.y; out may then be null (the FP32 row is not stored).
-template <int NSLICE, bool kPackedBf16, int THREADS = 256, bool kGated = false, bool kNorm = false>
+// FE_K > 0 (whole-head workgroups with kNorm): the front end runs first (see FeParams).
+template <int NSLICE, bool kPackedBf16, int THREADS = 256, bool kGated = false, bool kNorm = false, int FE_K = 0>
 __global__ __launch_bounds__(THREADS) void recurrent_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                         const float* __restrict__ v,
                                                         const unsigned short* __restrict__ qkv,
@@ -208,9 +222,11 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(const float* __restr
                                                         const float* __restrict__ beta, float* __restrict__ state,
                                                         float* __restrict__ out, float* __restrict__ snaps,
                                                         int n_snap, int batch, int heads, int T, GateParams gp,
-                                                        NormParams np = NormParams{})
+                                                        NormParams np = NormParams{}, FeParams fp = FeParams{})
 {
     static_assert(!kNorm || NSLICE == 1, "the fused norm needs the whole row in one workgroup");
+    constexpr bool kFE = FE_K > 0;
+    static_assert(!kFE || (kNorm && !kPackedBf16 && THREADS >= 3 * 64), "front end: whole-head FP32 staging");
     using G = RecGeom<NSLICE, THREADS>;
     const int tid = threadIdx.x;
     // blocks come in groups of 8 * NSLICE: 8 heads, slice s of head j at 8 s + j
@@ -226,12 +242,21 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(const float* __restr
     const int col = slice * G::kCols + 4 * cg;
 
     __shared__ float s_k[kD], s_q[kD], s_a[kD];
+    __shared__ float s_v[kFE ? kD : 1];
     __shared__ float s_red[G::kWaves][9][G::kColGroups];
     __shared__ float s_tot[G::kTwoStage ? 9 : 1][G::kColGroups];
 
     // per-head rate of the gate (kGated)
     const float rate = kGated ? __builtin_amdgcn_exp2f(1.4426950408889634f * gp.a_log[h]) : 0.f;
     const float dtb = kGated && tid < kD ? gp.dt_bias[h * kD + tid] : 0.f;  // the head's bias of channel tid
+
+    // front end: wave p < 3 owns the head's vector of part p (q, k, v), channels lane and lane + 64
+    const int Cdim = 3 * heads * kD;
+    const size_t fe_cv = ((size_t)(wave < 3 ? wave : 0) * heads + h) * kD;  // first channel of the vector
+    FeLane<kFE ? FE_K : 1> fl;
+    if constexpr (kFE) {
+        if (wave < 3) fe_load(fl, fp.conv_w, fp.conv_state + ((size_t)b * Cdim + fe_cv) * FE_K, fe_cv, lane);
+    }
 
     float* const S_head = state + (size_t)bh * kD * kD;
     float4 s[G::kRows];
@@ -249,10 +274,21 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(const float* __restr
         float b;            // beta, or its logit (gated form)
         float4 v;           // FP32 v
         uint2 vb;           // BF16 v (packed form)
+        unsigned short x0, x1;  // front end: the raw projections of the wave's two channels
     };
     auto load_row = [&](int tt, RowIn& r) {
         const size_t rr = ((size_t)b * T + tt) * heads + h;  // (b, tt, h)
-        if constexpr (kPackedBf16) {
+        if constexpr (kFE) {
+            if (wave < 3) {
+                const unsigned short* const x = qkv + ((size_t)b * T + tt) * Cdim + fe_cv + lane;
+                r.x0 = x[0];
+                r.x1 = x[64];
+            }
+            if (tid < kD) {
+                if constexpr (kGated) r.gb = gp.g_raw[rr * kD + tid];
+                else r.g = gate[rr * kD + tid];
+            }
+        } else if constexpr (kPackedBf16) {
             // q of head h in token (b, tt); k and v follow at a stride of heads * 128
             const unsigned short* const x = qkv + (((size_t)b * T + tt) * 3 * heads + h) * kD;
             const size_t part = (size_t)heads * kD;
@@ -279,11 +315,22 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(const float* __restr
         const size_t row = ((size_t)b * T + t) * heads + h;  // (b, t, h)
         float bt;
         float4 vv;
+        if constexpr (kFE) {
+            if (wave < 3) {
+                float y[2];
+                fe_row(fl, cur.x0, cur.x1, wave < 2, fp.l2_eps, y);
+                float* const dst = wave == 0 ? s_q : (wave == 1 ? s_k : s_v);
+                dst[lane] = y[0];
+                dst[lane + 64] = y[1];
+                if (t < n_snap && fp.conv_snaps)
+                    fe_store(fl, fp.conv_snaps + (((size_t)t * batch + b) * Cdim + fe_cv) * FE_K, lane);
+            }
+        }
         if (tid < kD) {
             if constexpr (kPackedBf16) {
                 s_k[tid] = bf16_to_f32(cur.kb);
                 s_q[tid] = bf16_to_f32(cur.qb);
-            } else {
+            } else if constexpr (!kFE) {
                 s_k[tid] = cur.k;
                 s_q[tid] = cur.q;
             }
@@ -293,12 +340,15 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(const float* __restr
                 s_a[tid] = expf(cur.g);
         }
         bt = kGated ? sigmoid_f32(cur.b) : cur.b;
-        if constexpr (kPackedBf16)
+        if constexpr (kFE)
+            vv = make_float4(0.f, 0.f, 0.f, 0.f);  // read from s_v after the barrier
+        else if constexpr (kPackedBf16)
             vv = make_float4(bf16_to_f32(cur.vb.x & 0xffffu), bf16_to_f32(cur.vb.x >> 16),
                              bf16_to_f32(cur.vb.y & 0xffffu), bf16_to_f32(cur.vb.y >> 16));
         else
             vv = cur.v;
         __syncthreads();
+        if constexpr (kFE) vv = make_float4(s_v[col], s_v[col + 1], s_v[col + 2], s_v[col + 3]);
         // the next row's inputs, into the registers the staging above has just consumed
         if (t + 1 < T) load_row(t + 1, cur);
         const float4 o = rec_row<G>(s, s_k, s_q, s_a, s_red, s_tot, vv, bt, cg, rg, wave, lane);
@@ -332,6 +382,9 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(const float* __restr
     }
 #pragma unroll
     for (int m = 0; m < G::kRows; ++m) state_st(S_head + (size_t)(rg + G::kRowGroups * m) * kD + col, s[m]);
+    if constexpr (kFE) {
+        if (wave < 3) fe_store(fl, fp.conv_state + ((size_t)b * Cdim + fe_cv) * FE_K, lane);
+    }
 }
 
 int launch_recurrent(const float* q, const float* k, const float* v, const uint16_t* qkv, const float* gate,
@@ -370,6 +423,47 @@ int launch_recurrent_norm(const uint16_t* qkv, const float* gate, const float* b
     hipLaunchKernelGGL((recurrent_kernel<1, true, kNormRecThreads, false, true>), dim3(grid), dim3(kNormRecThreads), 0,
                        stream, nullptr, nullptr, nullptr, reinterpret_cast<const unsigned short*>(qkv), gate, beta,
                        state, out, snaps, n_snap, batch, heads, T, GateParams{}, np);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// The whole decode step from the raw projections: front end, gate, core and gated RMSNorm in one
+// kernel (the geometry of launch_recurrent_norm).
+template <int K, bool kGated>
+static void launch_fused_k(unsigned grid, const unsigned short* x, const float* gate, const float* beta, float* state,
+                           float* out, float* snaps, int n_snap, int batch, int heads, int T, const GateParams& gp,
+                           const NormParams& np, const FeParams& fp, hipStream_t stream)
+{
+    hipLaunchKernelGGL((recurrent_kernel<1, false, kNormRecThreads, kGated, true, K>), dim3(grid),
+                       dim3(kNormRecThreads), 0, stream, nullptr, nullptr, nullptr, x, gate, beta, state, out, snaps,
+                       n_snap, batch, heads, T, gp, np, fp);
+}
+
+int launch_decode_fused(const uint16_t* qkv_proj, const uint16_t* conv_w, float* conv_state, float* conv_snaps,
+                        const float* gate, const float* beta, const GateParams* gp, float* state, float* out,
+                        float* snaps, int n_snap, int batch, int heads, int T, int conv_kernel,
+                        const uint16_t* out_gate, const uint16_t* o_norm, uint16_t* y, float eps, float l2_eps,
+                        hipStream_t stream)
+{
+    const unsigned grid = ((unsigned)batch * (unsigned)heads + 7u) / 8u * 8u;
+    const auto* x = reinterpret_cast<const unsigned short*>(qkv_proj);
+    const NormParams np{reinterpret_cast<const unsigned short*>(out_gate),
+                        reinterpret_cast<const unsigned short*>(o_norm), reinterpret_cast<unsigned short*>(y),
+                        (double)eps};
+    const FeParams fp{reinterpret_cast<const unsigned short*>(conv_w), conv_state, conv_snaps, (double)l2_eps};
+    const GateParams g = gp ? *gp : GateParams{};
+#define KDA_FUSED_CASE(K)                                                                                         \
+    case K:                                                                                                       \
+        if (gp) launch_fused_k<K, true>(grid, x, nullptr, beta, state, out, snaps, n_snap, batch, heads, T, g, np, fp, stream); \
+        else launch_fused_k<K, false>(grid, x, gate, beta, state, out, snaps, n_snap, batch, heads, T, g, np, fp, stream); \
+        break;
+    switch (conv_kernel) {
+        KDA_FUSED_CASE(1)
+        KDA_FUSED_CASE(2)
+        KDA_FUSED_CASE(3)
+        KDA_FUSED_CASE(4)
+    default: return -1;
+    }
+#undef KDA_FUSED_CASE
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -442,6 +442,52 @@ def test_decode_norm_refusals(lib):
 
 
 @no_gpu
+def test_decode_fused_refusals(lib):
+    Q = [0x10000000000 * (i + 1) for i in range(16)]
+    bad = kda.KDA_ERR_INVALID_ARG
+    x, w, cs, csn, g, b, st, sn, og, on, y, out = Q[:12]
+
+    def f(*a, n=0, neps=1e-6, leps=1e-6, T=4, K=4):
+        x_, w_, cs_, csn_, g_, b_, st_, sn_, og_, on_, y_, out_ = a
+        return lib.kda_decode_fused_k(x_, w_, cs_, csn_, g_, b_, st_, sn_, n, og_, on_, neps, leps, y_, out_, 2, 3, T,
+                                      K, None)
+    ok = [x, w, cs, csn, g, b, st, sn, og, on, y, out]
+    for i in (0, 1, 2, 4, 5, 6, 8, 9, 10):
+        a = list(ok)
+        a[i] = None
+        assert f(*a) == bad, i
+    for i in (0, 1, 2, 4, 6, 8, 9, 10, 11):
+        a = list(ok)
+        a[i] += 8
+        assert f(*a) == bad, i
+    assert f(*ok, neps=0.0) == bad
+    assert f(*ok, leps=float("inf")) == bad
+    assert f(*ok, n=5) == bad                                   # n_snapshots > T
+    a = list(ok); a[3] = None
+    assert f(*a, n=1) == bad                                    # conv snapshots NULL
+    a = list(ok); a[7] = None
+    assert f(*a, n=1) == bad                                    # state snapshots NULL
+    assert f(*ok, K=0) == bad
+    assert f(*ok, K=5) == kda.KDA_ERR_UNSUPPORTED
+    assert f(*ok, T=0) == bad
+    a = list(ok); a[10] = st + 64
+    assert f(*a) == bad                                         # y inside state
+    a = list(ok); a[2] = x
+    assert f(*a) == bad                                         # conv state over the projections
+    assert lib.kda_decode_fused_step(x, w, cs, None, b, st, og, on, 1e-6, 1e-6, y, out, 2, 3, 4, None) == bad
+    assert lib.kda_decode_fused_step(x, w, cs, g, b, st, og, on, 1e-6, 1e-6, y, out, 2, 3, 7, None) == \
+        kda.KDA_ERR_UNSUPPORTED
+    gr, bl, dt, al = Q[12:16]
+    fg = lib.kda_decode_fused_k_gated
+    assert fg(x, w, cs, csn, None, bl, dt, al, -5.0, st, sn, 0, og, on, 1e-6, 1e-6, y, out, 2, 3, 4, 4, None) == bad
+    assert fg(x, w, cs, csn, gr, bl, dt, al, 1.0, st, sn, 0, og, on, 1e-6, 1e-6, y, out, 2, 3, 4, 4, None) == bad
+    assert fg(x, w, cs, csn, gr + 2, bl, dt, al, -5.0, st, sn, 0, og, on, 1e-6, 1e-6, y, out, 2, 3, 4, 4, None) == bad
+    assert fg(x, w, cs, csn, gr, st + 4, dt, al, -5.0, st, sn, 0, og, on, 1e-6, 1e-6, y, out, 2, 3, 4, 4, None) == bad
+    assert lib.kda_decode_fused_step_gated(x, w, cs, gr, bl, None, al, -5.0, st, og, on, 1e-6, 1e-6, y, out, 2, 3, 4,
+                                           None) == bad
+
+
+@no_gpu
 def test_transition_refusals(lib):
     f = lib.kda_chunk_prefill_transition
     bad = kda.KDA_ERR_INVALID_ARG
