@@ -327,11 +327,20 @@ def bench_prefill_front_end(torch, kda, ki, name, steps, warmup, timer):
     return r, per_set, n_set, B * T
 
 
-def bench_decode_chain(torch, kda, ki, reps, fused=False):
+def fused_decode_bytes(B: int, H: int, K: int) -> int:
+    """One decode step from the raw projections in one kernel: BF16 qkv_proj read, FP32 conv state read
+    and written, state read and written, FP32 gate and beta read, BF16 out_gate read, BF16 y written, and
+    the BF16 conv weights and norm weight read once."""
+    C = 3 * H * D
+    return B * C * 2 + B * C * K * 4 * 2 + B * H * (2 * STATE_BYTES + D * 4 + 4 + D * 2 + D * 2) + C * K * 2 + 2 * D
+
+
+def bench_decode_chain(torch, kda, ki, reps, fused=False, whole=False):
     """The decode step of the block on BF16 q | k | v: front end -> kda_recurrent_step_bf16 -> gated RMSNorm
     at B=64 H=32, captured as one HIP graph of 8 steps, each on its own state set (8 x 128 MiB of recurrent
     state, so replays stream HBM), replayed back to back.  fused: front end -> kda_recurrent_step_bf16_norm
-    (the norm inside the decode kernel, the FP32 core rows not stored).  Returns (us per step, bytes per
+    (the norm inside the decode kernel, the FP32 core rows not stored).  whole: kda_decode_fused_step
+    (front end, core and norm in one kernel, the core rows not stored).  Returns (us per step, bytes per
     step)."""
     w = ki.WORKLOADS["decode_b64_h32"]
     B, H = w.batch, w.heads
@@ -351,6 +360,10 @@ def bench_decode_chain(torch, kda, ki, reps, fused=False):
                  y=torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")) for _ in range(n_set)]
 
     def chain(z):
+        if whole:
+            kda.kda_decode_fused_step(qkv, cw, z["cst"], g, b, z["st"], og.view(B, 1, H, D), on, H, ki.NORM_EPS,
+                                      ki.L2_EPS, y=z["y"].view(B, 1, H, D), want_core=False)
+            return
         kda.kda_decode_front_end_bf16(qkv, cw, z["cst"], H, ki.L2_EPS, conv_out=z["co"])
         if fused:
             kda.kda_recurrent_step_bf16_norm(z["co"], g, b, z["st"], og.view(B, 1, H, D), on, ki.NORM_EPS,
@@ -378,7 +391,9 @@ def bench_decode_chain(torch, kda, ki, reps, fused=False):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / (reps * n_set)
-    if fused:  # the core rows stay on chip: the norm reads only its gate and weight and writes y
+    if whole:
+        nbytes = fused_decode_bytes(B, H, K)
+    elif fused:  # the core rows stay on chip: the norm reads only its gate and weight and writes y
         nbytes = (front_end_bytes(B, 1, H, K, 0, out_bytes=2) + decode_bytes(B, H, qkv_bytes=2) - B * H * D * 4
                   + B * H * D * 4 + 2 * D)
     else:
@@ -894,6 +909,14 @@ def main():
             "tokens_per_s": 64 / (us * 1e-6), "us_per_step": us, "GB_per_s": nbytes / (us * 1e-6) / 1e9,
             "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "steps": "front end (BF16 out) + kda_recurrent_step_bf16_norm (norm fused), replayed from one HIP graph"}
+    if want("decode_fused_b64_h32"):
+        log("decode_fused_b64_h32")
+        us, nbytes = bench_decode_chain(torch, kda, ki, args.reps or 50, whole=True)
+        workloads["decode_fused_b64_h32"] = {
+            "tokens_per_s": 64 / (us * 1e-6), "us_per_step": us, "GB_per_s": nbytes / (us * 1e-6) / 1e9,
+            "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "steps": "kda_decode_fused_step (front end, core and gated RMSNorm in one kernel), replayed from one "
+                     "HIP graph"}
     if want("prefill_chain_t8192_h32"):
         log("prefill_chain_t8192_h32")
         r, tokens = bench_prefill_chain(torch, kda, ki, args.reps or 20, 0 if args.reps else 60, timer)

@@ -258,11 +258,6 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(const float* __restr
         if (wave < 3) fe_load(fl, fp.conv_w, fp.conv_state + ((size_t)b * Cdim + fe_cv) * FE_K, fe_cv, lane);
     }
 
-    float* const S_head = state + (size_t)bh * kD * kD;
-    float4 s[G::kRows];
-#pragma unroll
-    for (int m = 0; m < G::kRows; ++m) s[m] = state_ld(S_head + (size_t)(rg + G::kRowGroups * m) * kD + col);
-
     // A row's inputs as loaded, still raw: the next row's are requested right after the current one
     // is staged (into the same registers), ahead of the current row's stores, so the wait for them
     // never covers a store (the vector memory counter counts loads and stores in order).  Widening, the gate's exponential and
@@ -309,8 +304,14 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(const float* __restr
         }
         r.b = beta[rr];
     };
+    // the first row's inputs go out before the state: loads complete in order, so the row can be
+    // staged (and, with the front end inside, its conv, SiLU and L2 computed) while the state streams in
     RowIn cur;
     load_row(0, cur);
+    float* const S_head = state + (size_t)bh * kD * kD;
+    float4 s[G::kRows];
+#pragma unroll
+    for (int m = 0; m < G::kRows; ++m) s[m] = state_ld(S_head + (size_t)(rg + G::kRowGroups * m) * kD + col);
     for (int t = 0; t < T; ++t) {
         const size_t row = ((size_t)b * T + t) * heads + h;  // (b, t, h)
         float bt;
