@@ -248,6 +248,26 @@ int kda_chunk_prefill_fused(const uint16_t* qkv, const uint16_t* conv_w, float* 
                             int conv_kernel, float l2_eps, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kda_chunk_prefill_fused with the gate and beta steps inside the prepare as
+ * well (as kda_chunk_prefill_gated forms them): the prefill of the block from
+ * its raw projections, q | k | v, the gate's projection and beta's logits.
+ *
+ *   g_raw, beta_logit, dt_bias, a_log, gate_lower_bound : as
+ *            kda_chunk_prefill_gated (rows [batch][T_pad])
+ *   everything else : as kda_chunk_prefill_fused
+ *
+ * The result agrees with kda_prefill_front_end + kda_chunk_prefill_gated
+ * within the stated tolerance (the q and k sums of squares in another order);
+ * the conv state ends bit for bit as there.  Refusals: those of
+ * kda_chunk_prefill_fused and kda_chunk_prefill_gated.
+ */
+int kda_chunk_prefill_fused_gated(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state,
+                                  const uint16_t* g_raw, const float* beta_logit, const float* dt_bias,
+                                  const float* a_log, float gate_lower_bound, float* state, float* out, int batch,
+                                  int heads, int T, int chunk, int conv_kernel, float l2_eps, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * The varlen form of kda_chunk_prefill_fused: kda_prefill_front_end_varlen
  * followed by kda_chunk_prefill_varlen, with the front end inside the
  * prefill's prepare kernel.

@@ -38,7 +38,7 @@ EXPORTED = ("kda_status_string", "kda_chunk_prefill_workspace_bytes", "kda_chunk
             "kda_chunk_prefill_fused", "kda_chunk_prefill_varlen_fused", "kda_chunk_prefill_noalloc",
             "kda_chunk_prefill_gated", "kda_recurrent_k_gated", "kda_recurrent_step_gated",
             "kda_recurrent_k_bf16_norm", "kda_recurrent_step_bf16_norm", "kda_decode_fused_k", "kda_decode_fused_step",
-            "kda_decode_fused_k_gated", "kda_decode_fused_step_gated")
+            "kda_decode_fused_k_gated", "kda_decode_fused_step_gated", "kda_chunk_prefill_fused_gated")
 STATIC_WORKSPACE_BYTES = 256 << 20
 GATED_RMSNORM_MIN_EPS = 1e-30
 
@@ -119,6 +119,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_chunk_scan.restype = i
     lib.kda_chunk_prefill_fused.argtypes = [p] * 7 + [i] * 5 + [ctypes.c_float, p, sz, p]
     lib.kda_chunk_prefill_fused.restype = i
+    lib.kda_chunk_prefill_fused_gated.argtypes = [p] * 7 + [f] + [p] * 2 + [i] * 5 + [f, p, sz, p]
+    lib.kda_chunk_prefill_fused_gated.restype = i
     lib.kda_chunk_prefill_varlen_fused.argtypes = [p] * 8 + [i] * 5 + [ctypes.c_float, p, sz, p]
     lib.kda_chunk_prefill_varlen_fused.restype = i
     if path == LIB_PATH:
@@ -766,6 +768,44 @@ def kda_chunk_prefill_fused(qkv, conv_w, conv_state, gate, beta, state, chunk: i
                                                 ws_bytes, _stream_ptr(stream))
     if rc != KDA_OK:
         raise KdaError("kda_chunk_prefill_fused", rc)
+    return out
+
+
+def kda_chunk_prefill_fused_gated(qkv, conv_w, conv_state, g_raw, beta_logit, dt_bias, a_log,
+                                  gate_lower_bound: float, state, chunk: int, l2_eps: float, out=None, workspace=None,
+                                  stream=None):
+    """kda_chunk_prefill_fused with the gate and beta formed in the prepare from g_raw ([B][T_pad][H][128]
+    bfloat16) and beta_logit ([B][T_pad][H]) as kda_chunk_prefill_gated forms them.  Returns ``out``."""
+    if not isinstance(qkv, torch.Tensor) or qkv.dim() != 3:
+        raise ValueError("qkv must be [batch][T][3 * heads * 128]")
+    B, T, C = qkv.shape
+    if chunk not in (16, 32, 64):
+        raise KdaError("kda_chunk_prefill_fused_gated", KDA_ERR_UNSUPPORTED)
+    if not isinstance(g_raw, torch.Tensor) or g_raw.dim() != 4:
+        raise ValueError("g_raw must be [B][T_pad][H][128]")
+    Bg, t_pad, H = g_raw.shape[0], g_raw.shape[1], g_raw.shape[2]
+    if Bg != B or C != 3 * H * HEAD_DIM or t_pad != -(-int(T) // chunk) * chunk:
+        raise ValueError("qkv [B][T][3 H 128] and g_raw [B][T_pad][H][128] do not agree")
+    if conv_w.dim() != 2:
+        raise ValueError("conv_w must be [conv_dim][conv_kernel]")
+    K = conv_w.shape[1]
+    vs = (B, t_pad, H, HEAD_DIM)
+    if out is None:
+        out = torch.empty(vs, dtype=torch.float32, device=qkv.device)
+    need = kda_chunk_prefill_workspace_bytes(B, H, int(T), chunk)
+    if workspace is None:
+        workspace = _workspace(need, qkv.device, stream)
+    if not (workspace.device.type == "cuda" and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    g, b, dt, al = _gate_args(g_raw, beta_logit, dt_bias, a_log, B, t_pad, H)
+    rc = load_library().kda_chunk_prefill_fused_gated(
+        _check("qkv", qkv, (B, T, C), torch.bfloat16), _check("conv_w", conv_w, (C, K), torch.bfloat16),
+        _check("conv_state", conv_state, (B, C, K)), g, b, dt, al, float(gate_lower_bound),
+        _check("state", state, (B, H, HEAD_DIM, HEAD_DIM)), _check("out", out, vs), B, H, int(T), chunk, K,
+        float(l2_eps), workspace.data_ptr(), ws_bytes, _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_chunk_prefill_fused_gated", rc)
     return out
 
 

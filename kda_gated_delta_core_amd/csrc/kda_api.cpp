@@ -641,12 +641,15 @@ KDA_API int kda_prefill_front_end(const uint16_t* qkv, const uint16_t* conv_w, f
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 
-KDA_API int kda_chunk_prefill_fused(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, const float* gate,
-                                    const float* beta, float* state, float* out, int batch, int heads, int T, int chunk,
-                                    int conv_kernel, float l2_eps, void* workspace, size_t workspace_bytes,
-                                    void* stream)
+namespace {
+
+int prefill_fused_checked(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, const float* gate,
+                          const float* beta, const kda::GateParams* gp, float* state, float* out, int batch, int heads,
+                          int T, int chunk, int conv_kernel, float l2_eps, void* workspace, size_t workspace_bytes,
+                          void* stream)
 {
-    if (!qkv || !conv_w || !conv_state || !gate || !beta || !state || !out) return KDA_ERR_INVALID_ARG;
+    if (!qkv || !conv_w || !conv_state || !beta || !state || !out) return KDA_ERR_INVALID_ARG;
+    if (gp ? !gate_inputs_ok(gp->g_raw, gp->dt_bias, gp->a_log, gp->lower) : !gate) return KDA_ERR_INVALID_ARG;
     if (!aligned({qkv, conv_w, conv_state, gate, state, out, workspace}) || !aligned({beta}, 4))
         return KDA_ERR_INVALID_ARG;
     if (batch < 1 || heads < 1 || T < 1 || heads > KDA_PREFILL_MAX_HEADS) return KDA_ERR_INVALID_ARG;
@@ -668,13 +671,44 @@ KDA_API int kda_chunk_prefill_fused(const uint16_t* qkv, const uint16_t* conv_w,
     if ((int64_t)batch * heads > 0x7fffffffLL / 64 || mul({batch, C}) > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
     if ((int64_t)batch * heads * (t_pad / chunk) > (1LL << 30)) return KDA_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < (size_t)need) return KDA_ERR_WORKSPACE;
-    const Range r[] = {{out, vec * 4},  {state, st * 4}, {conv_state, cs * 4}, {workspace, need},
-                       {qkv, x * 2},    {conv_w, w * 2}, {gate, vec * 4},      {beta, sca * 4}};
-    if (any_overlap(r, 8, 4)) return KDA_ERR_INVALID_ARG;
-    const int rc = kda::launch_chunk_prefill_fused(qkv, conv_w, conv_state, gate, beta, state, out, batch, heads, T,
-                                                   (int)t_pad, chunk, l2_eps, static_cast<float*>(workspace),
+    const Range r[] = {{out, vec * 4},
+                       {state, st * 4},
+                       {conv_state, cs * 4},
+                       {workspace, need},
+                       {qkv, x * 2},
+                       {conv_w, w * 2},
+                       {gate, vec * 4},
+                       {beta, sca * 4},
+                       {gp ? gp->g_raw : nullptr, vec * 2},
+                       {gp ? gp->dt_bias : nullptr, (int64_t)heads * KDA_HEAD_DIM * 4},
+                       {gp ? gp->a_log : nullptr, (int64_t)heads * 4}};
+    if (any_overlap(r, 11, 4)) return KDA_ERR_INVALID_ARG;
+    const int rc = kda::launch_chunk_prefill_fused(qkv, conv_w, conv_state, gate, beta, gp, state, out, batch, heads,
+                                                   T, (int)t_pad, chunk, l2_eps, static_cast<float*>(workspace),
                                                    static_cast<hipStream_t>(stream));
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+KDA_API int kda_chunk_prefill_fused(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, const float* gate,
+                                    const float* beta, float* state, float* out, int batch, int heads, int T, int chunk,
+                                    int conv_kernel, float l2_eps, void* workspace, size_t workspace_bytes,
+                                    void* stream)
+{
+    return prefill_fused_checked(qkv, conv_w, conv_state, gate, beta, nullptr, state, out, batch, heads, T, chunk,
+                                 conv_kernel, l2_eps, workspace, workspace_bytes, stream);
+}
+
+KDA_API int kda_chunk_prefill_fused_gated(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state,
+                                          const uint16_t* g_raw, const float* beta_logit, const float* dt_bias,
+                                          const float* a_log, float gate_lower_bound, float* state, float* out,
+                                          int batch, int heads, int T, int chunk, int conv_kernel, float l2_eps,
+                                          void* workspace, size_t workspace_bytes, void* stream)
+{
+    const kda::GateParams gp{reinterpret_cast<const unsigned short*>(g_raw), dt_bias, a_log, gate_lower_bound};
+    return prefill_fused_checked(qkv, conv_w, conv_state, nullptr, beta_logit, &gp, state, out, batch, heads, T,
+                                 chunk, conv_kernel, l2_eps, workspace, workspace_bytes, stream);
 }
 
 KDA_API int kda_prefill_front_end_varlen(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q,

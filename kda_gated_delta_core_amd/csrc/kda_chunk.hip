@@ -1567,28 +1567,34 @@ int launch_chunk_scan(const float* workspace, float* state, float* out, int batc
 
 // The prefill with the front end fused into the prepare (dense layout).  q, k,
 // v are not read in this form: the gate pointer stands in for them.
+// With gp, kda_gate and the beta sigmoid are inside the prepare too (gate not read, beta the logits),
+// and beta stands in for every unread pointer.
 template <int C>
-static int launch_dense_fused(const FeSrc& fe, const float* gate, const float* beta, float* state, float* out,
-                              int batch, int heads, int T, int t_pad, float* ws, hipStream_t stream)
+static int launch_dense_fused(const FeSrc& fe, const float* gate, const float* beta, const GateParams* gp,
+                              float* state, float* out, int batch, int heads, int T, int t_pad, float* ws,
+                              hipStream_t stream)
 {
     const int nchunks = t_pad / C;
     const long long n_bh = (long long)batch * heads;
     const DenseLayout layout{heads, T, t_pad, nchunks, (int)(n_bh * nchunks)};
+    if (gp)
+        return launch_chunk<C, DenseLayout, false, true, true>(beta, beta, beta, beta, beta, state, out, n_bh, heads,
+                                                               n_bh * nchunks, ws, layout, stream, fe, *gp);
     return launch_chunk<C, DenseLayout, false, true>(gate, gate, gate, gate, beta, state, out, n_bh, heads,
                                                      n_bh * nchunks, ws, layout, stream, fe);
 }
 
 int launch_chunk_prefill_fused(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, const float* gate,
-                               const float* beta, float* state, float* out, int batch, int heads, int T, int t_pad,
-                               int chunk, float l2_eps, float* workspace, hipStream_t stream)
+                               const float* beta, const GateParams* gp, float* state, float* out, int batch, int heads,
+                               int T, int t_pad, int chunk, float l2_eps, float* workspace, hipStream_t stream)
 {
     const FeSrc fe{reinterpret_cast<const unsigned short*>(qkv), reinterpret_cast<const unsigned short*>(conv_w),
                    conv_state, (double)l2_eps};
     int rc = -1;
     switch (chunk) {
-    case 16: rc = launch_dense_fused<16>(fe, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream); break;
-    case 32: rc = launch_dense_fused<32>(fe, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream); break;
-    case 64: rc = launch_dense_fused<64>(fe, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream); break;
+    case 16: rc = launch_dense_fused<16>(fe, gate, beta, gp, state, out, batch, heads, T, t_pad, workspace, stream); break;
+    case 32: rc = launch_dense_fused<32>(fe, gate, beta, gp, state, out, batch, heads, T, t_pad, workspace, stream); break;
+    case 64: rc = launch_dense_fused<64>(fe, gate, beta, gp, state, out, batch, heads, T, t_pad, workspace, stream); break;
     default: return -1;
     }
     if (rc != 0) return rc;

@@ -55,8 +55,8 @@ int launch_chunk_prefill_gated(const float* q, const float* k, const float* v, c
 // conv_w BF16 [3 H 128][4], conv state [B][3 H 128][4] (advanced by T inputs), gate, beta, state, out
 // as launch_chunk_prefill
 int launch_chunk_prefill_fused(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, const float* gate,
-                               const float* beta, float* state, float* out, int batch, int heads, int T, int t_pad,
-                               int chunk, float l2_eps, float* workspace, hipStream_t stream);
+                               const float* beta, const GateParams* gp, float* state, float* out, int batch, int heads,
+                               int T, int t_pad, int chunk, float l2_eps, float* workspace, hipStream_t stream);
 
 // varlen form of the fused prefill: qkv [total][3 H 128], conv state [n][3 H 128][4], the rest as
 // launch_chunk_prefill_varlen

@@ -488,6 +488,31 @@ def test_decode_fused_refusals(lib):
 
 
 @no_gpu
+def test_prefill_fused_gated_refusals(lib):
+    Q = [0x10000000000 * (i + 1) for i in range(12)]
+    bad = kda.KDA_ERR_INVALID_ARG
+    x, w, cs, gr, bl, dt, al, st, out, ws = Q[:10]
+    need = kda.kda_chunk_prefill_workspace_bytes(2, 3, 100, 64)
+    f = lambda *a, lo=-5.0, C=64, K=4, eps=1e-6, wsb=need: lib.kda_chunk_prefill_fused_gated(
+        *a[:7], lo, a[7], a[8], 2, 3, 100, C, K, eps, a[9], wsb, None)
+    ok = [x, w, cs, gr, bl, dt, al, st, out, ws]
+    for i in range(9):
+        a = list(ok)
+        a[i] = None
+        assert f(*a) == bad, i
+    assert f(*ok, lo=0.5) == bad
+    assert f(*ok, lo=float("nan")) == bad
+    assert f(*ok, eps=0.0) == bad
+    assert f(*ok, C=48) == kda.KDA_ERR_UNSUPPORTED
+    assert f(*ok, K=3) == kda.KDA_ERR_UNSUPPORTED
+    assert f(*ok, wsb=need - 1) == kda.KDA_ERR_WORKSPACE
+    a = list(ok); a[3] += 2
+    assert f(*a) == bad                                        # g_raw misaligned
+    a = list(ok); a[4] = st + 4
+    assert f(*a) == bad                                        # beta logits inside state
+
+
+@no_gpu
 def test_transition_refusals(lib):
     f = lib.kda_chunk_prefill_transition
     bad = kda.KDA_ERR_INVALID_ARG

@@ -174,3 +174,63 @@ def test_varlen_fused_prefill_against_the_separate_calls(device):
     assert_close("out vs separate", host(out), host(out2))
     assert_close("state vs separate", host(st), host(st2))
     assert torch.equal(cst_d, cst2)
+
+
+def _gate_inputs_padded(seed, B, T, H, t_pad):
+    """kda_gate inputs with NaN in the pad rows (rows >= T), which the prefill must ignore."""
+    gx = ki.gate_inputs(seed, B, t_pad, H)
+    gx["g_raw"][:, T:] = 0x7FC0            # BF16 NaN
+    gx["beta_logit"][:, T:] = np.nan
+    return gx
+
+
+def _gate_dev(gx):
+    return (_bits_dev(gx["g_raw"]), torch.from_numpy(gx["beta_logit"]).cuda(), torch.from_numpy(gx["dt_bias"]).cuda(),
+            torch.from_numpy(gx["a_log"]).cuda())
+
+
+@pytest.mark.parametrize("B,T,H,C", [(1, 64, 2, 16), (2, 100, 3, 32), (1, 130, 2, 64), (2, 1, 1, 64)])
+def test_fused_gated_prefill_matches_oracle(device, B, T, H, C):
+    """kda_chunk_prefill_fused_gated against the oracle's front end, kda_gate and sigmoid, then its
+    recurrence; pad rows of every input hold NaN and must not reach a result"""
+    import kda_gated_delta_core_amd as kda
+    announce(f"kda_chunk_prefill_fused_gated B={B} T={T} H={H} C={C}")
+    fx, core, t_pad = _inputs(9300 + T + C, B, T, H, C)
+    gx = _gate_inputs_padded(9350 + T, B, T, H, t_pad)
+    cst = torch.from_numpy(fx["conv_state"]).cuda()
+    st = torch.from_numpy(core["state"]).cuda()
+    out = torch.full((B, t_pad, H, D), SENTINEL, device="cuda")
+    kda.kda_chunk_prefill_fused_gated(_bits_dev(fx["qkv"]), _bits_dev(fx["conv_w"]), cst, *_gate_dev(gx),
+                                      ki.GATE_LOWER_BOUND, st, C, ki.L2_EPS, out=out)
+    torch.cuda.synchronize()
+    q, k, v, c_ref, _ = oracle.decode_front_end(fx["qkv"], fx["conv_w"], fx["conv_state"], H, ki.L2_EPS)
+    gate = oracle.kda_gate(gx["g_raw"][:, :T], gx["dt_bias"], gx["a_log"], ki.GATE_LOWER_BOUND).astype(np.float32)
+    beta = oracle.sigmoid(gx["beta_logit"][:, :T]).astype(np.float32)
+    o_ref, s_ref, _, _ = oracle.serial(q, k, v, gate, beta, core["state"])
+    assert_close("out", host(out)[:, :T], o_ref)
+    assert_close("state", host(st), s_ref)
+    assert np.array_equal(host(cst), c_ref), "conv state"
+    assert np.all(host(out)[:, T:] == SENTINEL), "rows >= T of out were written"
+
+
+def test_fused_gated_prefill_against_the_separate_calls(device):
+    """kda_prefill_front_end + kda_chunk_prefill_gated on the same inputs: within tolerance, conv state
+    bit for bit"""
+    import kda_gated_delta_core_amd as kda
+    B, T, H, C = 2, 1000, 8, 64
+    announce(f"kda_chunk_prefill_fused_gated vs separate calls B={B} T={T} H={H} C={C}")
+    fx, core, t_pad = _inputs(9400, B, T, H, C)
+    gx = _gate_inputs_padded(9450, B, T, H, t_pad)
+    g = _gate_dev(gx)
+    cst = torch.from_numpy(fx["conv_state"]).cuda()
+    st = torch.from_numpy(core["state"]).cuda()
+    out = kda.kda_chunk_prefill_fused_gated(_bits_dev(fx["qkv"]), _bits_dev(fx["conv_w"]), cst, *g,
+                                            ki.GATE_LOWER_BOUND, st, C, ki.L2_EPS)
+    cst2 = torch.from_numpy(fx["conv_state"]).cuda()
+    q, k, v = kda.kda_prefill_front_end(_bits_dev(fx["qkv"]), _bits_dev(fx["conv_w"]), cst2, H, C, ki.L2_EPS)
+    st2 = torch.from_numpy(core["state"]).cuda()
+    out2 = kda.kda_chunk_prefill_gated(q, k, v, *g, ki.GATE_LOWER_BOUND, st2, T, C)
+    torch.cuda.synchronize()
+    assert_close("out vs separate", host(out)[:, :T], host(out2)[:, :T])
+    assert_close("state vs separate", host(st), host(st2))
+    assert torch.equal(cst, cst2)
