@@ -327,12 +327,39 @@ def bench_prefill_front_end(torch, kda, ki, name, steps, warmup, timer):
     return r, per_set, n_set, B * T
 
 
-def fused_decode_bytes(B: int, H: int, K: int) -> int:
-    """One decode step from the raw projections in one kernel: BF16 qkv_proj read, FP32 conv state read
-    and written, state read and written, FP32 gate and beta read, BF16 out_gate read, BF16 y written, and
-    the BF16 conv weights and norm weight read once."""
+def fused_decode_bytes(B: int, H: int, K: int, T: int = 1, n_snap: int = 0) -> int:
+    """The decode walk from the raw projections in one kernel: BF16 qkv_proj read, FP32 conv state read
+    and written (and n_snap conv snapshots written), state read and written (and n_snap snapshots), FP32
+    gate and beta read, BF16 out_gate read and BF16 y written per row, and the BF16 conv weights and norm
+    weight read once."""
     C = 3 * H * D
-    return B * C * 2 + B * C * K * 4 * 2 + B * H * (2 * STATE_BYTES + D * 4 + 4 + D * 2 + D * 2) + C * K * 2 + 2 * D
+    return (B * T * C * 2 + B * C * K * 4 * (2 + n_snap) + B * H * (2 + n_snap) * STATE_BYTES
+            + B * T * H * (D * 4 + 4 + D * 2 + D * 2) + C * K * 2 + 2 * D)
+
+
+def bench_decode_fused_k(torch, kda, ki, steps, warmup, timer):
+    """kda_decode_fused_k at B=128 H=32, 4 rows with 4 snapshots of both states (the decode_k workload from
+    the raw projections), states rotated over >= 1 GiB."""
+    w = ki.WORKLOADS["decode_k4_b128_h32"]
+    B, H, T, n = w.batch, w.heads, w.T, w.n_snap
+    K = 4
+    x = ki.workload_inputs(w)
+    fx = ki.front_end_inputs(41, B, T, H, K)
+    nx = ki.norm_inputs(42, B * T, H)
+    bits = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).cuda()
+    qkv, cw = bits(fx["qkv"]), bits(fx["conv_w"])
+    og, on = bits(nx["out_gate"]).view(B, T, H, D), bits(nx["o_norm"])
+    g, b = torch.from_numpy(x["gate"]).cuda(), torch.from_numpy(x["beta"]).cuda()
+    n_set = max(2, -(-(1 << 30) // (B * H * STATE_BYTES)))
+    sts = [torch.from_numpy(x["state"]).cuda() for _ in range(n_set)]
+    cst = torch.from_numpy(fx["conv_state"]).cuda()
+    snaps = torch.empty((n, B, H, D, D), device="cuda")
+    csn = torch.empty((n, B, 3 * H * D, K), device="cuda")
+    y = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
+    r = timer.run(lambda i: kda.kda_decode_fused_k(qkv, cw, cst, g, b, sts[i % n_set], og, on, H, ki.NORM_EPS,
+                                                   ki.L2_EPS, y=y, snapshots=snaps, conv_snapshots=csn,
+                                                   n_snapshots=n, want_core=False), steps, warmup)
+    return r, B * T, fused_decode_bytes(B, H, K, T, n), n_set
 
 
 def bench_decode_chain(torch, kda, ki, reps, fused=False, whole=False):
@@ -917,6 +944,16 @@ def main():
             "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "steps": "kda_decode_fused_step (front end, core and gated RMSNorm in one kernel), replayed from one "
                      "HIP graph"}
+    if want("decode_fused_k4_b128_h32"):
+        log("decode_fused_k4_b128_h32")
+        r, tokens, nbytes, n_set = bench_decode_fused_k(torch, kda, ki, args.reps or args.steps, 0 if args.reps else
+                                                        args.warmup, timer)
+        gbs = nbytes / r["launch_avg_s"] / 1e9
+        workloads["decode_fused_k4_b128_h32"] = {
+            "tokens_per_s": tokens / r["s_per_step"], "us_per_call": r["s_per_step"] * 1e6,
+            "kernel_us": r["launch_avg_s"] * 1e6, "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "state_buffers_rotated": n_set,
+            "steps": "kda_decode_fused_k: 4 rows, 4 snapshots of the state and of the conv state, y only"}
     if want("prefill_chain_t8192_h32"):
         log("prefill_chain_t8192_h32")
         r, tokens = bench_prefill_chain(torch, kda, ki, args.reps or 20, 0 if args.reps else 60, timer)

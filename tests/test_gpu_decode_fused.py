@@ -69,7 +69,7 @@ def _oracle_gate_beta(x, gx, gated):
 @pytest.mark.parametrize("B,T,H,K,n_snap,gated", [(64, 1, 32, 4, 0, False), (64, 1, 32, 4, 0, True),
                                                   (3, 5, 2, 3, 3, False), (2, 4, 3, 1, 4, True),
                                                   (17, 4, 9, 4, 2, True), (1, 1, 1, 2, 0, False),
-                                                  (5, 3, 4, 2, 1, False)])
+                                                  (5, 3, 4, 2, 1, False), (128, 4, 32, 4, 4, True)])
 def test_fused_decode_matches_oracle(device, B, T, H, K, n_snap, gated):
     import kda_gated_delta_core_amd as kda
     announce(f"kda_decode_fused{'_gated' if gated else ''} B={B} T={T} H={H} K={K} n_snap={n_snap}")
