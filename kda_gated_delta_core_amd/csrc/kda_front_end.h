@@ -51,13 +51,20 @@ __device__ __forceinline__ void fe_store(const FeLane<K>& f, float* st, int lane
 }
 
 // One DPP lane move of a double (both 32-bit halves with the same control);
-// lanes outside ROW_MASK get 0.
+// lanes outside ROW_MASK get 0.  With every row enabled (the quad permutes and
+// mirrors, which have a source for every lane) no old value is needed.
 template <int CTRL, int ROW_MASK = 0xf>
 __device__ __forceinline__ double dpp_f64(double x)
 {
     const unsigned long long u = (unsigned long long)__double_as_longlong(x);
-    const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)u, CTRL, ROW_MASK, 0xf, false);
-    const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), CTRL, ROW_MASK, 0xf, false);
+    unsigned lo, hi;
+    if constexpr (ROW_MASK == 0xf) {
+        lo = (unsigned)__builtin_amdgcn_mov_dpp((int)(unsigned)u, CTRL, 0xf, 0xf, false);
+        hi = (unsigned)__builtin_amdgcn_mov_dpp((int)(unsigned)(u >> 32), CTRL, 0xf, 0xf, false);
+    } else {
+        lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)u, CTRL, ROW_MASK, 0xf, false);
+        hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), CTRL, ROW_MASK, 0xf, false);
+    }
     return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
