@@ -1478,10 +1478,19 @@ static int launch_chunk(const float* q, const float* k, const float* v, const fl
                         const Layout& layout, hipStream_t stream, const FeSrc& fe = FeSrc{},
                         const GateParams& gp = GateParams{})
 {
-    // one persistent prepare workgroup per compute unit (its LDS use allows one)
+    // persistent prepare workgroups, as many per compute unit as its resources allow (one at C = 64,
+    // where the LDS tables take all but 5 KiB; more at the narrower chunks, so that more chunks'
+    // latency chains overlap).  Which workgroup takes which record does not change a bit.
     const int n_cu = compute_units();
     if (n_cu < 1) return -1;
-    const int grid_p = max_records < n_cu ? (int)max_records : n_cu;
+    int per_cu = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chunk_prepare_kernel<C, Layout, kFE, kGate>,
+                                                     kPrepThreads, 0) != hipSuccess || per_cu < 1) {
+        (void)hipGetLastError();  // a failed query leaves no error behind for the launch check below
+        per_cu = 1;
+    }
+    const long long slots = (long long)n_cu * per_cu;
+    const int grid_p = (int)(max_records < slots ? max_records : slots);
     if (grid_p > 0) {
         hipLaunchKernelGGL((chunk_prepare_kernel<C, Layout, kFE, kGate>), dim3((unsigned)grid_p), dim3(kPrepThreads),
                            0, stream, q, k, v, gate, beta, ws, heads, layout, fe, gp);
