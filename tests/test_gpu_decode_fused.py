@@ -146,3 +146,37 @@ def test_fused_decode_k_rows_equal_steps(device, gated):
     assert torch.equal(st2, st) and torch.equal(cs2, cs)
     y3, o3, st3, _, _, _ = _call(kda, fe, x, og, on, gx, H, gated, 0, want_core=False)
     assert o3 is None and torch.equal(y3, y) and torch.equal(st3, st)
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_fused_decode_edges(device, gated):
+    """Edge rows through the whole fused step: a sequence whose projections and conv state are all zero
+    (q = k = v = 0, so the state only decays and the core rows and y are exactly 0); saturated gates and
+    beta (gate 0 and -40 with beta 0 and 1 in the plain form; g_raw and beta logits at +-30 in the gated
+    form); all against the oracle chain."""
+    import kda_gated_delta_core_amd as kda
+    B, T, H, K = 3, 3, 2, 4
+    announce(f"kda_decode_fused{'_gated' if gated else ''} edges B={B} T={T} H={H}")
+    fe, x, og, on, gx = _inputs(9890, B, T, H, K)
+    fe["qkv"][0] = 0
+    fe["conv_state"][0] = 0.0
+    x["gate"][1, :, 0] = 0.0
+    x["gate"][1, :, 1] = -40.0
+    x["beta"][1, 0] = 0.0
+    x["beta"][1, 1] = 1.0
+    gx["g_raw"][1, :, 0] = ki.to_bf16_bits(np.float32(30.0))
+    gx["g_raw"][1, :, 1] = ki.to_bf16_bits(np.float32(-30.0))
+    gx["beta_logit"][1, 0] = 30.0
+    gx["beta_logit"][1, 1] = -30.0
+    out = torch.full((B, T, H, D), SENTINEL, device="cuda")
+    y, o, st, cs, _, _ = _call(kda, fe, x, og, on, gx, H, gated, 0, out=out)
+    rq, rk, rv, rcs, _ = oracle.decode_front_end(fe["qkv"], fe["conv_w"], fe["conv_state"], H, ki.L2_EPS)
+    gate, beta = _oracle_gate_beta(x, gx, gated)
+    o_ref, s_ref, _, _ = oracle.serial(rq, rk, rv, gate, beta, x["state"])
+    got = host(o)
+    assert not np.any(got[0]) and not np.any(oracle.bf16_to_f64(_bits_host(y))[0]), "zero sequence"
+    assert_close("core", got, o_ref)
+    assert_close("state", host(st), s_ref)
+    assert np.array_equal(host(cs), rcs), "conv state"
+    y_ref = oracle.gated_rmsnorm(got.astype(np.float64), og, on, ki.NORM_EPS)
+    assert_within_one_ulp("y", oracle.bf16_to_f64(_bits_host(y)), y_ref)
