@@ -41,6 +41,12 @@ __device__ __forceinline__ float sigmoid_f32(float z)
 {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
 }
+// 1 / sqrt(x) for x > 0 in FP64: the hardware estimate and one Newton step
+__device__ __forceinline__ double norm_rsqrt(double x)
+{
+    const double r = __builtin_amdgcn_rsq(x);
+    return r * (1.5 - 0.5 * (x * r) * r);
+}
 __device__ __forceinline__ float kda_gate_f32(float g_raw, float dt_bias, float rate, float lower)
 {
     return lower * sigmoid_f32(rate * (g_raw + dt_bias));

@@ -17,7 +17,11 @@
 // sum of squares and the scale 1 / sqrt(mean + eps) are formed in FP64 (each
 // FP32 square is exact there, the 128-term sum cannot overflow or flush), so
 // every finite core gives an accurate scale; the rest is FP32 and the result
-// is rounded to BF16 to nearest even.
+// is rounded to BF16 to nearest even.  The scale is the hardware FP64
+// reciprocal square root refined by one Newton step, the sigmoid the hardware
+// exp2 and reciprocal (within a few units of 2^-24): with the IEEE divisions
+// and the accurate expf of each element the kernel spent as long in its
+// arithmetic as in its memory traffic.
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -31,7 +35,6 @@ constexpr int kGroups = kNormThreads / kLanes;           // vector groups per bl
 constexpr int kGroupVecs = 2;                            // vectors per group
 constexpr int kVecPerBlock = kGroups * kGroupVecs;
 
-__device__ __forceinline__ float sigmoid(float g) { return 1.0f / (1.0f + expf(-g)); }
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // 8 BF16 values
 
@@ -73,12 +76,12 @@ __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(const float
         for (int k = 0; k < 8; ++k) ss += (double)x[k] * x[k];
 #pragma unroll
         for (int off = 1; off < kLanes; off <<= 1) ss += __shfl_xor(ss, off, kLanes);
-        const double r = 1.0 / sqrt(ss * (1.0 / kD) + eps);
+        const double r = norm_rsqrt(ss * (1.0 / kD) + eps);
         u32x4 o;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const float ya = (float)(x[2 * k] * r) * w8[2 * k] * sigmoid(bf16_to_f32(g[i][k] & 0xffffu));
-            const float yb = (float)(x[2 * k + 1] * r) * w8[2 * k + 1] * sigmoid(bf16_to_f32(g[i][k] >> 16));
+            const float ya = (float)(x[2 * k] * r) * w8[2 * k] * sigmoid_f32(bf16_to_f32(g[i][k] & 0xffffu));
+            const float yb = (float)(x[2 * k + 1] * r) * w8[2 * k + 1] * sigmoid_f32(bf16_to_f32(g[i][k] >> 16));
             o[k] = f32_to_bf16(ya) | (f32_to_bf16(yb) << 16);
         }
         const long long vec = v0 + kGroups * i;

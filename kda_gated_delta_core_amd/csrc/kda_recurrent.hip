@@ -195,7 +195,7 @@ struct NormParams {
     unsigned short* y;               // [B][T][H][128] BF16
     double eps;
 };
-__device__ __forceinline__ float norm_sigmoid(float g) { return 1.0f / (1.0f + expf(-g)); }
+
 
 // The decode front end inside the kernel (FE_K = conv_kernel > 0): `qkv` then holds the raw BF16
 // projections ([B][T][3 H 128], q | k | v per token), and waves 0, 1, 2 of the whole-head
@@ -360,7 +360,7 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(const float* __restr
                 double ss = (double)o.x * o.x + (double)o.y * o.y + (double)o.z * o.z + (double)o.w * o.w;
 #pragma unroll
                 for (int off = 1; off < G::kColGroups; off <<= 1) ss += __shfl_xor(ss, off, G::kColGroups);
-                const double r = 1.0 / sqrt(ss * (1.0 / kD) + np.eps);
+                const double r = norm_rsqrt(ss * (1.0 / kD) + np.eps);
                 const uint2 g2 = *reinterpret_cast<const uint2*>(np.out_gate + row * kD + col);
                 const uint2 w2 = *reinterpret_cast<const uint2*>(np.o_norm + col);
                 const float x[4] = {o.x, o.y, o.z, o.w};
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(const float* __restr
                 unsigned yb[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    yb[e] = f32_to_bf16((float)(x[e] * r) * bf16_to_f32(wb[e]) * norm_sigmoid(bf16_to_f32(gb[e])));
+                    yb[e] = f32_to_bf16((float)(x[e] * r) * bf16_to_f32(wb[e]) * sigmoid_f32(bf16_to_f32(gb[e])));
                 *reinterpret_cast<uint2*>(np.y + row * kD + col) = make_uint2(yb[0] | (yb[1] << 16), yb[2] | (yb[3] << 16));
             }
         }
