@@ -33,6 +33,13 @@
 // SiLU and, on the decode path, L2).  BF16 widens to FP32 exactly and the row
 // body is shared, so the BF16 form on BF16 data gives the bits of the FP32
 // form on the widened values.
+//
+// Further forms of the same kernel (template switches): the gate and beta
+// formed from their raw projections (kGated); the sigmoid-gated RMSNorm of
+// every output row (kNorm, whole-head workgroups, the row then meeting in one
+// wave); and, with the norm, the decode front end run by three of the
+// workgroup's waves on the raw projections (FE_K = conv_kernel), so the
+// whole step of the block between its projections is one kernel.
 #include "kda_common.h"
 #include "kda_front_end.h"
 #include "kda_internal.h"
