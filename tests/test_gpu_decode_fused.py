@@ -71,9 +71,28 @@ def _oracle_gate_beta(x, gx, gated):
                                                   (17, 4, 9, 4, 2, True), (1, 1, 1, 2, 0, False),
                                                   (5, 3, 4, 2, 1, False), (128, 4, 32, 4, 4, True)])
 def test_fused_decode_matches_oracle(device, B, T, H, K, n_snap, gated):
+    _against_oracle(B, T, H, K, n_snap, gated, 9800 + 7 * B + T + K)
+
+
+def _random_case(r):
+    B, T, H, K = int(r.integers(1, 21)), int(r.integers(1, 7)), int(r.integers(1, 11)), int(r.integers(1, 5))
+    return B, T, H, K, int(r.integers(0, T + 1)), bool(r.integers(0, 2)), int(r.integers(0, 10 ** 6))
+
+
+_RNG = np.random.default_rng(20261203)
+RANDOM = [_random_case(_RNG) for _ in range(8)]
+
+
+@pytest.mark.parametrize("B,T,H,K,n_snap,gated,seed", RANDOM)
+def test_fused_decode_random_shapes(device, B, T, H, K, n_snap, gated, seed):
+    """Seeded random batch, rows, heads, conv width, snapshot count and gate form against the oracle."""
+    _against_oracle(B, T, H, K, n_snap, gated, seed)
+
+
+def _against_oracle(B, T, H, K, n_snap, gated, seed):
     import kda_gated_delta_core_amd as kda
-    announce(f"kda_decode_fused{'_gated' if gated else ''} B={B} T={T} H={H} K={K} n_snap={n_snap}")
-    fe, x, og, on, gx = _inputs(9800 + 7 * B + T + K, B, T, H, K)
+    announce(f"kda_decode_fused{'_gated' if gated else ''} B={B} T={T} H={H} K={K} n_snap={n_snap} seed={seed}")
+    fe, x, og, on, gx = _inputs(seed, B, T, H, K)
     out = torch.full((B, T, H, D), SENTINEL, device="cuda")
     y, o, st, cs, snaps, csn = _call(kda, fe, x, og, on, gx, H, gated, n_snap, out=out)
     rq, rk, rv, rcs, rcsn = oracle.decode_front_end(fe["qkv"], fe["conv_w"], fe["conv_state"], H, ki.L2_EPS, n_snap)

@@ -259,3 +259,49 @@ def test_graph_replays_of_the_fused_prefills(device):
         vst.copy_(vst0)
 
     _capture_and_replay(kda, "fused prefills", work, reset, lambda: (out[:, :T], st, cst, vout, vst, vcst))
+
+
+def test_graph_replays_of_the_fused_decode(device):
+    """kda_decode_fused_step and kda_decode_fused_k_gated (3 rows, snapshots of both states) captured as one
+    graph, the form the decode loop replays."""
+    import kda_gated_delta_core_amd as kda
+    B, H, K, T = 8, 4, 4, 3
+    announce(f"graph capture: fused decode step B={B} H={H}, gated fused walk k={T}")
+    fx1 = ki.front_end_inputs(1550, B, 1, H, K)
+    c1 = ki.make_batch(1551, B, H, 1, -5.0, 0.02)
+    n1 = ki.norm_inputs(1552, B, H)
+    fx2 = ki.front_end_inputs(1553, B, T, H, K)
+    c2 = ki.make_batch(1554, B, H, T, -5.0, 0.02)
+    n2 = ki.norm_inputs(1555, B * T, H)
+    gx = ki.gate_inputs(1556, B, T, H)
+    q1, w1, og1, on1 = _bits(fx1["qkv"]), _bits(fx1["conv_w"]), _bits(n1["out_gate"]).view(B, 1, H, 128), \
+        _bits(n1["o_norm"])
+    q2, w2, og2, on2 = _bits(fx2["qkv"]), _bits(fx2["conv_w"]), _bits(n2["out_gate"]).view(B, T, H, 128), \
+        _bits(n2["o_norm"])
+    g1, b1 = torch.from_numpy(c1["gate"]).cuda(), torch.from_numpy(c1["beta"]).cuda()
+    graw, blog = _bits(gx["g_raw"]), torch.from_numpy(gx["beta_logit"]).cuda()
+    dtb, alog = torch.from_numpy(gx["dt_bias"]).cuda(), torch.from_numpy(gx["a_log"]).cuda()
+    cs10, st10 = torch.from_numpy(fx1["conv_state"]).cuda(), torch.from_numpy(c1["state"]).cuda()
+    cs20, st20 = torch.from_numpy(fx2["conv_state"]).cuda(), torch.from_numpy(c2["state"]).cuda()
+    cs1, st1, cs2, st2 = (torch.empty_like(t) for t in (cs10, st10, cs20, st20))
+    y1 = torch.empty((B, 1, H, 128), dtype=torch.bfloat16, device="cuda")
+    o1 = torch.empty((B, 1, H, 128), device="cuda")
+    y2 = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device="cuda")
+    o2 = torch.empty((B, T, H, 128), device="cuda")
+    snaps = torch.empty((T, B, H, 128, 128), device="cuda")
+    csn = torch.empty((T,) + tuple(cs20.shape), device="cuda")
+
+    def work(s):
+        kda.kda_decode_fused_step(q1, w1, cs1, g1, b1, st1, og1, on1, H, ki.NORM_EPS, ki.L2_EPS, y=y1, out=o1,
+                                  stream=s)
+        kda.kda_decode_fused_k_gated(q2, w2, cs2, graw, blog, dtb, alog, ki.GATE_LOWER_BOUND, st2, og2, on2, H,
+                                     ki.NORM_EPS, ki.L2_EPS, y=y2, out=o2, snapshots=snaps, conv_snapshots=csn,
+                                     n_snapshots=T, stream=s)
+
+    def reset():
+        cs1.copy_(cs10)
+        st1.copy_(st10)
+        cs2.copy_(cs20)
+        st2.copy_(st20)
+
+    _capture_and_replay(kda, "fused decode", work, reset, lambda: (y1, o1, st1, cs1, y2, o2, st2, cs2, snaps, csn))
