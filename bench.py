@@ -987,6 +987,20 @@ def main():
         workloads[name] = {"tokens_per_s": rows / r["s_per_step"], "us_per_call": r["s_per_step"] * 1e6,
                            "kernel_us": r["launch_avg_s"] * 1e6, "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
                            "buffer_sets_rotated": n_set}
+    copy_gbs = None
+    if want("copy_ceiling"):
+        # the practical HBM ceiling beside the vendor peak: a plain 1 GiB device copy (torch's elementwise
+        # kernel, 1 GiB read + 1 GiB written per launch), timed like the workloads
+        log("copy_ceiling")
+        n = 1 << 28
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        r = timer.run(lambda i: torch.mul(src, 1.0, out=dst), args.reps or 20, 3)
+        copy_gbs = 2 * n * 4 / r["launch_avg_s"] / 1e9
+        workloads["copy_ceiling"] = {"GB_per_s": copy_gbs, "hbm_frac": copy_gbs / HBM_PEAK_GBS,
+                                     "kernel_us": r["launch_avg_s"] * 1e6,
+                                     "steps": "1 GiB read + 1 GiB written per launch by a plain copy kernel"}
+        del src, dst
     for name, res in workloads.items():
         log(f"{name}: " + ", ".join(f"{k}={v:.4g}" if isinstance(v, float) else f"{k}={v}"
                                     for k, v in res.items()))
@@ -1005,7 +1019,8 @@ def main():
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
                          "kernel": "recurrent_kernel", "algorithmic_bytes_per_launch": nbytes,
-                         "kernel_avg_us": r["launch_avg_s"] * 1e6},
+                         "kernel_avg_us": r["launch_avg_s"] * 1e6, "copy_GB_per_s": copy_gbs,
+                         "frac_of_copy": gbs / copy_gbs if copy_gbs else None},
         })
     line["workloads"] = workloads
     if not args.no_cpu and headline is not None:

@@ -187,6 +187,28 @@ def test_prefill_h32_t8192_full_size(device):
         assert_close(f"h{h} state", s[:, h], s_ref[:, h], quiet=True)
 
 
+def test_prefill_h32_t8155_in_chunk_pads(device):
+    """The T=8192 H=32 workload cut to T=8155: the last chunk holds 37 real rows and 27 pad rows of 1e4
+    (plus the extra pad chunk), so the pad select inside a chunk is exercised at full size; every head
+    against the oracle."""
+    import kda_gated_delta_core_amd as kda
+    w = ki.WORKLOADS["prefill_h32_t8192_c64"]
+    T = 8155
+    announce(f"kda_chunk_prefill {w.name} cut to T={T} seed={w.seed} (generating inputs)")
+    x = ki.workload_inputs(w, T=T)
+    assert x["q"].shape[1] > T and np.all(x["q"][:, T:] == w.pad_value)
+    out, st, _ = _prefill(kda, x, T, w.chunk)
+    o, s = host(out), host(st)
+    assert np.all(o[:, T:] == SENTINEL)
+    announce("oracle, all 32 heads")
+    o_ref, s_ref, _, _ = oracle.serial(x["q"], x["k"], x["v"], x["gate"], x["beta"], x["state"], T=T)
+    assert_close("core", o[:, :T], o_ref)
+    assert_close("state", s, s_ref)
+    for h in range(w.heads):
+        assert_close(f"h{h} core", o[:, :T, h], o_ref[:, :, h], quiet=True)
+        assert_close(f"h{h} state", s[:, h], s_ref[:, h], quiet=True)
+
+
 @pytest.mark.timeout(1200)
 def test_prefill_b4_t32768_then_decode_full_size(device):
     """4 sequences x T=32768, H=32, C=64, gates in [-0.5, 0] (long memory), then 16 decode steps per
