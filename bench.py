@@ -674,9 +674,16 @@ def cpu_baselines(ki, budget_s: float = 10.0):
     import oracle
     res = {}
 
+    cpu_model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu_model)
+    except OSError:
+        pass
+
     def entry(rate, threads, sample, unit="tokens/s"):
         return {"value": rate, "unit": unit, "cores": threads, "kind": "oracle",
-                "sample": sample + f"; os.cpu_count()={os.cpu_count()}"}
+                "sample": sample + f"; os.cpu_count()={os.cpu_count()}", "cpu": cpu_model}
 
     # decode B=64 H=32 (headline): repeated full decode steps until ~budget_s of wall time
     w = ki.WORKLOADS["decode_b64_h32"]
