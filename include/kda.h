@@ -350,8 +350,9 @@ int kda_chunk_scan(float* state, float* out, int batch, int heads, int T, int ch
  *
  *   trans_p, trans_q, state : [batch][heads][128][128], 16-byte aligned
  *
- * state must not overlap trans_p or trans_q (KDA_ERR_INVALID_ARG).  The
- * products accumulate in FP32 over the 128 key indices.
+ * state must not overlap trans_p or trans_q (KDA_ERR_INVALID_ARG); batch *
+ * heads above 2^22 - 8 (the launch's grid limit) is refused the same way.
+ * The products accumulate in FP32 over the 128 key indices.
  */
 int kda_state_transition_apply(const float* trans_p, const float* trans_q, float* state, int batch, int heads,
                                void* stream);

@@ -269,7 +269,8 @@ KDA_API int kda_state_transition_apply(const float* trans_p, const float* trans_
 {
     if (!trans_p || !state) return KDA_ERR_INVALID_ARG;
     if (!aligned({trans_p, trans_q, state})) return KDA_ERR_INVALID_ARG;
-    if (batch < 1 || heads < 1 || (int64_t)batch * heads > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
+    // two workgroups of 512 threads per state: the grid's work-items stay below 2^32
+    if (batch < 1 || heads < 1 || (int64_t)batch * heads > (1LL << 22) - 8) return KDA_ERR_INVALID_ARG;
     const int64_t st = mul({batch, heads, KDA_HEAD_DIM, KDA_HEAD_DIM});
     if (st < 0) return KDA_ERR_INVALID_ARG;
     const Range r[] = {{state, st * 4}, {trans_p, st * 4}, {trans_q, trans_q ? st * 4 : 0}};

@@ -1625,55 +1625,72 @@ int launch_chunk_prefill_transition(const float* q, const float* k, const float*
 
 // S <- P S + Q for n independent 128 x 128 states (Q null: S <- P S): the
 // fold of segment transitions, and their composition (P2 P1, P2 Q1 + Q2).
-// One workgroup per state.  The whole incoming state is staged in LDS before
-// any of it is overwritten, so S is updated in place; wave w computes rows
-// 16 w .. 16 w + 15 of the result over all 128 columns with the 16x16x4 FP32
-// MFMA, the key index as the reduction, one chain per 16-column tile.
+// The value columns of a state are independent (column j of the result needs
+// column j of S and Q and all of P), so each state is split over
+// kApplyGroups workgroups of 16 kApplyNct columns; they take block indices 8
+// apart, which the dispatcher places on one XCD, so P is fetched into one L2.
+// A workgroup stages its columns of the incoming state in LDS before any of
+// them is overwritten, so S is updated in place; wave w computes rows
+// 16 w .. 16 w + 15 of its columns with the 16x16x4 FP32 MFMA, the key index
+// as the reduction, two chains per 16-column tile (even and odd key steps).
 constexpr int kApplyThreads = 512;
+constexpr int kApplyNct = 4;                 // 16-column tiles per workgroup
+constexpr int kApplyGroups = 8 / kApplyNct;  // workgroups per state
 
 __global__ __launch_bounds__(kApplyThreads) void transition_apply_kernel(const float* __restrict__ P,
                                                                          const float* __restrict__ Q, float* S, int n)
 {
-    const int u = blockIdx.x;
+    // block b: state 8 (b / (8 G)) + b % 8, column group (b / 8) % G
+    const int b = blockIdx.x;
+    const int u = 8 * (b / (8 * kApplyGroups)) + b % 8, grp = (b / 8) % kApplyGroups;
     if (u >= n) return;  // the whole workgroup leaves together, before its barrier
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
-    // tile (row block rb, column tile ct), element e of lane l: S[16 rb + 4 (l / 16) + e][16 ct + l % 16]
-    __shared__ floatx4 sS[8][8][64];
+    const int c0 = 16 * kApplyNct * grp;  // first column of the group
+    // tile (row block rb, column tile ct), element e of lane l: S[16 rb + 4 (l / 16) + e][c0 + 16 ct + l % 16]
+    __shared__ floatx4 sS[8][kApplyNct][64];
     float* const Su = S + (size_t)u * kD * kD;
     const float* const Pu = P + (size_t)u * kD * kD;
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
+    for (int ct = 0; ct < kApplyNct; ++ct) {
         floatx4 st;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st[e] = Su[(size_t)(16 * wave + 4 * q4 + e) * kD + 16 * ct + l16];
+        for (int e = 0; e < 4; ++e) st[e] = Su[(size_t)(16 * wave + 4 * q4 + e) * kD + c0 + 16 * ct + l16];
         sS[wave][ct][lane] = st;
     }
     __syncthreads();
-    floatx4 acc[8];
+    floatx4 acc[kApplyNct], acc2[kApplyNct];
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
+    for (int ct = 0; ct < kApplyNct; ++ct) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            acc[ct][e] = Q ? Q[(size_t)u * kD * kD + (size_t)(16 * wave + 4 * q4 + e) * kD + 16 * ct + l16] : 0.f;
+            acc[ct][e] = Q ? Q[(size_t)u * kD * kD + (size_t)(16 * wave + 4 * q4 + e) * kD + c0 + 16 * ct + l16]
+                           : 0.f;
+        acc2[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int tau = 0; tau < 8; ++tau) {
         // A operand: P[16 w + l % 16][16 tau + 4 (l / 16) + e] for the e-th key step
         const float4 a = ld4(Pu + (size_t)(16 * wave + l16) * kD + 16 * tau + 4 * q4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+        for (int e = 0; e < 4; e += 2)
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) acc[ct] = mfma4(comp(a, e), sS[tau][ct][lane][e], acc[ct]);
+            for (int ct = 0; ct < kApplyNct; ++ct) {
+                acc[ct] = mfma4(comp(a, e), sS[tau][ct][lane][e], acc[ct]);
+                acc2[ct] = mfma4(comp(a, e + 1), sS[tau][ct][lane][e + 1], acc2[ct]);
+            }
     }
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
+    for (int ct = 0; ct < kApplyNct; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Su[(size_t)(16 * wave + 4 * q4 + e) * kD + 16 * ct + l16] = acc[ct][e];
+        for (int e = 0; e < 4; ++e)
+            Su[(size_t)(16 * wave + 4 * q4 + e) * kD + c0 + 16 * ct + l16] = acc[ct][e] + acc2[ct][e];
 }
 
 int launch_transition_apply(const float* P, const float* Q, float* S, int n, hipStream_t stream)
 {
-    hipLaunchKernelGGL(transition_apply_kernel, dim3((unsigned)n), dim3(kApplyThreads), 0, stream, P, Q, S, n);
+    const long long blocks = (long long)((n + 7) / 8) * 8 * kApplyGroups;  // n padded to whole groups of 8
+    hipLaunchKernelGGL(transition_apply_kernel, dim3((unsigned)blocks), dim3(kApplyThreads), 0, stream, P, Q, S, n);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -551,6 +551,7 @@ def test_transition_refusals(lib):
     assert g(P[0], P[1], P[1], 1, 2, None) == bad  # state is Q
     assert g(P[0], None, P[0], 1, 2, None) == bad  # state is P, Q absent
     assert g(P[0], P[1], P[2], 1 << 20, 1 << 12, None) == bad  # more states than one grid holds
+    assert g(P[0], P[1], P[2], 1, (1 << 22) - 7, None) == bad  # one state past the grid limit
 
 
 @no_gpu

@@ -110,12 +110,13 @@ def test_transition_full_size(device):
     assert_close("P S0 + Q", got, s_ref)
 
 
-def test_apply_matches_oracle(device):
+@pytest.mark.parametrize("B,H", [(2, 5), (2, 8), (1, 1), (3, 11)])
+def test_apply_matches_oracle(device, B, H):
+    """Whole and partial groups of eight states (each state split over column groups)."""
     import torch
     import kda_gated_delta_core_amd as kda
-    B, H = 2, 5
     announce(f"kda_state_transition_apply B={B} H={H}")
-    rng = np.random.default_rng(7200)
+    rng = np.random.default_rng(7200 + B * H)
     P = (rng.standard_normal((B, H, 128, 128)) / 8).astype(np.float32)
     Q = rng.standard_normal((B, H, 128, 128)).astype(np.float32)
     S = rng.standard_normal((B, H, 128, 128)).astype(np.float32)
