@@ -554,6 +554,20 @@ def bench_prefill(torch, kda, ki, name, steps, warmup, timer, chunk=None):
 
     r = timer.run(step, steps, warmup)
     extra = {}
+    if C == 64 and T >= 1024:
+        # the call's two kernels apart: kda_chunk_scan alone from the records the last call left in the
+        # workspace gives the scan's time; the prepare's is the rest of the call
+        def scan_step(i):
+            kda.kda_chunk_scan(state, T, C, ws, out=out)
+
+        rs = timer.run(scan_step, steps, 3)
+        scan_s = rs["launch_avg_s"]
+        prep_s = max(r["launch_avg_s"] - scan_s, 1e-9)
+        scan_fl = 6.0 * D * D * B * H * T
+        prep_bytes = 4 * B * t_pad * H * D * 4 + B * t_pad * H * 4 + ws.numel()  # inputs read, records written
+        extra = {"scan_ms": scan_s * 1e3, "scan_mfma_frac": scan_fl / scan_s / 1e12 / MFMA_F32_PEAK_TFLOPS,
+                 "prepare_ms": prep_s * 1e3, "prepare_GB_per_s": prep_bytes / prep_s / 1e9,
+                 "prepare_hbm_frac": prep_bytes / prep_s / 1e9 / HBM_PEAK_GBS}
     if w.tail_steps:
         # decode steps continuing from the prefill's final state (rows T.. of the same streams)
         state.copy_(state0)
@@ -589,8 +603,8 @@ def bench_prefill(torch, kda, ki, name, steps, warmup, timer, chunk=None):
             graph_us = e0.elapsed_time(e1) * 1e3 / (5 * w.tail_steps)
         except Exception as exc:  # capture unavailable: report the wall rate only
             log(f"tail graph timing skipped: {exc}")
-        extra = {"tail_steps": w.tail_steps, "tail_us_per_step": rt["s_per_step"] * 1e6,
-                 "tail_graph_us_per_step": graph_us, "tail_tokens_per_s": B / rt["s_per_step"]}
+        extra.update({"tail_steps": w.tail_steps, "tail_us_per_step": rt["s_per_step"] * 1e6,
+                      "tail_graph_us_per_step": graph_us, "tail_tokens_per_s": B / rt["s_per_step"]})
     return w, r, extra
 
 
@@ -1008,6 +1022,10 @@ def main():
                                      "kernel_us": r["launch_avg_s"] * 1e6,
                                      "steps": "1 GiB read + 1 GiB written per launch by a plain copy kernel"}
         del src, dst
+    if copy_gbs:
+        for res in workloads.values():
+            if "prepare_GB_per_s" in res:
+                res["prepare_frac_of_copy"] = res["prepare_GB_per_s"] / copy_gbs
     for name, res in workloads.items():
         log(f"{name}: " + ", ".join(f"{k}={v:.4g}" if isinstance(v, float) else f"{k}={v}"
                                     for k, v in res.items()))
