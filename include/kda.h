@@ -98,9 +98,9 @@ const char* kda_status_string(int status);
 size_t kda_chunk_prefill_workspace_bytes(int batch, int heads, int T, int chunk);
 
 /*
- * Chunked prefill over T tokens per sequence, starting from the carried
- * state (layer page, Glm5NextKdaLayer::prefill; kernel-table page,
- * chunk_prepare + chunk_scan).
+ * The chunked prefill: T tokens of each sequence continue its recurrent
+ * state from wherever the previous call left it (layer page,
+ * Glm5NextKdaLayer::prefill; kernel-table page, chunk_prepare + chunk_scan).
  *
  *   q, k, v, gate : [batch][T_pad][heads][128], T_pad = ceil(T/chunk)*chunk
  *   beta          : [batch][T_pad][heads]
@@ -113,8 +113,9 @@ size_t kda_chunk_prefill_workspace_bytes(int batch, int heads, int T, int chunk)
  *                   (else KDA_ERR_INVALID_ARG)
  *
  * Rows t >= T of every input may hold anything, NaN and inf included: the
- * kernels select them away before any arithmetic (layer page,
- * prefill_with_pad_fill: positions at or past t are ignored in-kernel).
+ * kernels select them away before any arithmetic (the layer page's
+ * prefill_with_pad_fill fills the padded tails with a test value for exactly
+ * this property).
  * Gate domain: any gate <= 0, -inf included (config page, gate_lower_bound
  * bounds it from below without printing the value).  Chunks whose gates are
  * all >= about -8.3 (-12 in log2 units) factor each pairwise decay
@@ -230,7 +231,7 @@ int kda_chunk_prefill_varlen(const float* q, const float* k, const float* v, con
  * instead of FP32 q, k, v rows, so those rows never travel through HBM
  * (workspace page, fields q_f32 / k_f32 / v_f32: unused on this path).
  *
- *   qkv        : [batch][T][3 * heads * 128] BF16, q | k | v per token (no padding)
+ *   qkv        : [batch][T][3 * heads * 128] BF16; each token's row holds its q, then k, then v channels (no padding)
  *   conv_w     : [3 * heads * 128][conv_kernel] BF16
  *   conv_state : [batch][3 * heads * 128][conv_kernel], read, then advanced by the T inputs
  *   gate, beta, state, out, workspace : as kda_chunk_prefill
@@ -378,14 +379,15 @@ int kda_recurrent_step(const float* q, const float* k, const float* v, const flo
  *
  *   q, k, v, gate, out : [batch][T][heads][128];  beta : [batch][T][heads]
  *   state              : [batch][heads][128][128]; out: state after row T-1
- *   snapshots          : [n_snapshots][batch][heads][128][128]; snapshot t
- *                        receives the state after row t, for t < n_snapshots
+ *   snapshots          : [n_snapshots][batch][heads][128][128]; slot t holds
+ *                        the state as row t left it, for t < n_snapshots
  *                        (rows past n_snapshots take none); may be NULL when
  *                        n_snapshots == 0
  *   n_snapshots        : 0 <= n_snapshots <= T
  *
  * T == 0 is refused (the layer page refuses k == 0).  out, the final state
- * and every snapshot equal T successive kda_recurrent_step calls bit for bit.
+ * and every snapshot are bitwise the results of T successive
+ * kda_recurrent_step calls.
  */
 int kda_recurrent_k(const float* q, const float* k, const float* v, const float* gate, const float* beta,
                     float* state, float* out, float* snapshots, int n_snapshots, int batch, int heads, int T,
@@ -465,8 +467,9 @@ int kda_recurrent_step_bf16_norm(const uint16_t* qkv, const float* gate, const f
 /*
  * The step after the core: sigmoid-gated RMSNorm of the core's output (module
  * page, pipeline line: the core output goes through a sigmoid-gated RMSNorm
- * with weight o_norm and gate g_b(g_a(h)) before o_proj; the page notes that
- * o_norm gates with a sigmoid, not SiLU).  Independently for every row r and
+ * with weight o_norm and gate g_b(g_a(h)) before o_proj; the gate goes
+ * through the logistic sigmoid there, unlike the SiLU-gated norm the page
+ * also names).  Independently for every row r and
  * head h, over the 128 value channels j of x = core[r][h]:
  *
  *     out[r][h][j] = x_j / sqrt(mean_i x_i^2 + eps) * o_norm[j] * sigmoid(out_gate[r][h][j])
@@ -508,7 +511,7 @@ int kda_gated_rmsnorm(const float* core, const uint16_t* out_gate, const uint16_
  *     q, k  : each head's 128 values scaled by 1 / sqrt(sum y^2 + l2_eps); v as is
  *
  *   qkv            : [batch][T][conv_dim] BF16 (workspace page, qkv_proj:
- *                    [T, conv_dim] BF16, q | k | v per token)
+ *                    [T, conv_dim] BF16, one row of q, k and v channels a token)
  *   conv_w         : [conv_dim][conv_kernel] BF16, no bias (config page,
  *                    Glm5NextKdaWeights::conv)
  *   conv_state     : [batch][conv_dim][conv_kernel] FP32, read and updated in
@@ -618,7 +621,7 @@ int kda_decode_fused_step_gated(const uint16_t* qkv_proj, const uint16_t* conv_w
  * round the conv output to BF16 (conv_out) before the L2; here conv, SiLU
  * and L2 are one pass and the values stay FP32 throughout.
  *
- *   qkv        : [batch][T][conv_dim] BF16, q | k | v per token (qkv_proj)
+ *   qkv        : [batch][T][conv_dim] BF16, a token's q, k, v channels in one row (qkv_proj)
  *   conv_w     : [conv_dim][conv_kernel] BF16
  *   conv_state : [batch][conv_dim][conv_kernel] FP32, read, then advanced in
  *                place by the T inputs (afterwards it holds the inputs of the

@@ -1,7 +1,7 @@
 // Sigmoid-gated RMSNorm of the core's output, gfx950: the step that follows
 // the KDA core in the block (module page, pipeline line: the core's output
 // goes through a sigmoid-gated RMSNorm with the o_norm weight and the output
-// gate g_b(g_a(h)), then to o_proj; o_norm gates with a sigmoid, not SiLU).
+// gate g_b(g_a(h)), then to o_proj; the gate passes through a logistic sigmoid, not a SiLU).
 // Per (token, head), over the 128 value channels j:
 //
 //     y_j = core_j / sqrt(mean_i core_i^2 + eps) * w_j * sigmoid(g_j)

@@ -28,9 +28,9 @@
 // case (512 x 4 at 3 per CU 312, at 2 per CU 381).
 //
 // Inputs come in two forms: FP32 q, k, v as three [B][T][H][128] arrays, or
-// BF16 q | k | v packed per token as [B][T][3][H][128], the layout the decode
-// front end writes (workspace page, conv_out: BF16 [T, conv_dim] after conv,
-// SiLU and, on the decode path, L2).  BF16 widens to FP32 exactly and the row
+// BF16 q, k and v packed in one row a token as [B][T][3][H][128], the layout
+// the decode front end writes (workspace page, conv_out: the BF16 output of the
+// convolution and SiLU, with the L2 of q and k already applied when decoding).  BF16 widens to FP32 exactly and the row
 // body is shared, so the BF16 form on BF16 data gives the bits of the FP32
 // form on the widened values.
 //
@@ -205,7 +205,7 @@ struct NormParams {
 
 
 // The decode front end inside the kernel (FE_K = conv_kernel > 0): `qkv` then holds the raw BF16
-// projections ([B][T][3 H 128], q | k | v per token), and waves 0, 1, 2 of the whole-head
+// projections ([B][T][3 H 128], a token's q, k, v channels in one row), and waves 0, 1, 2 of the whole-head
 // workgroup run the front end of the head's q, k and v vectors with the code of
 // kda_decode_front_end (fe_load, fe_row, fe_store: the same bits), keeping their conv slots in
 // registers for all T rows.

@@ -212,9 +212,9 @@ def gated_rmsnorm(core, out_gate_bits, o_norm_bits, eps: float) -> np.ndarray:
 def decode_front_end(qkv_bits, conv_w_bits, conv_state, heads: int, l2_eps: float, n_snap: int = 0):
     """The decode front end, fp64, token by token (module page, pipeline line: conv1d and SiLU on
     q, k, v, then L2 on q and k alone; the conv state holds conv_kernel slots that move one place
-    toward the oldest before each convolution.  Workspace page, qkv_proj [T, conv_dim] BF16 with q | k | v per
-    token; config page, Glm5NextKdaWeights::conv [conv_dim, conv_kernel] BF16 (depthwise, no bias),
-    conv_state_elems [conv_dim, conv_kernel] FP32, l2_eps applied as 1/sqrt(sum + eps)).
+    toward the oldest before each convolution.  Workspace page, qkv_proj [T, conv_dim] BF16, one row of q, k and
+    v channels a token; config page, Glm5NextKdaWeights::conv [conv_dim, conv_kernel] BF16 (depthwise, no bias),
+    conv_state_elems [conv_dim, conv_kernel] FP32, l2_eps added to the sum of squares inside the square root).
 
     qkv_bits [B][T][3 H D] and conv_w_bits [3 H D][K] are BF16 patterns, conv_state [B][3 H D][K]
     (not modified).  Per token: the K slots shift left by one and the new input enters the last

@@ -88,7 +88,7 @@ def test_prefill_pad_values_are_ignored_bitwise(device):
 
 def test_prefill_workspace_stages(device):
     """The chunk record the prepare kernel writes, stage by stage against the oracle's
-    intermediates (workspace page: the oracle compares stage by stage)."""
+    intermediates (workspace page: the numeric check runs one stage at a time)."""
     import kda_gated_delta_core_amd as kda
     T, C, H = 150, 64, 2
     announce(f"kda_chunk_prefill stages T={T} C={C}")

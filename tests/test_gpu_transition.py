@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _padded(x, t0, t1, C):
-    """Rows [t0, t1) of every input, padded with NaN to a whole number of chunks."""
+    """Rows [t0, t1) of every input, NaN rows appended up to the next multiple of the chunk width."""
     n = t1 - t0
     t_pad = -(-n // C) * C
     res = {}
