@@ -129,3 +129,44 @@ def test_decode_k_rollback_to_a_snapshot(device):
     torch.cuda.synchronize()
     assert torch.equal(out2, out[:, 2:])
     assert torch.equal(st2, st)
+
+
+@pytest.mark.timeout(600)
+def test_decode_step_state_past_4gib(device):
+    """66,000 heads in one call: the state spans 4.03 GiB, so the byte offsets of the last heads pass
+    2^32; every head against the oracle, and the heads past 2^32 on their own."""
+    import kda_gated_delta_core_amd as kda
+    B, H = 500, 132
+    announce(f"kda_recurrent_step B={B} H={H} (state {B * H * 65536 / 2 ** 30:.2f} GiB)")
+    x = ki.make_batch(9300, B, H, 1, -5.0, 0.02)
+    out, st = _run_step(kda, x, B, H)
+    o_ref, s_ref, _, _ = oracle.serial(x["q"], x["k"], x["v"], x["gate"], x["beta"], x["state"])
+    assert_close("out", out, o_ref)
+    assert_close("state", st, s_ref)
+    first = 2 ** 32 // 65536  # the first head whose state starts at or past 2^32 bytes
+    assert B * H > first
+    assert_close("heads past 2^32: out", out.reshape(B * H, 128)[first:], o_ref.reshape(B * H, 128)[first:])
+    assert_close("heads past 2^32: state", st.reshape(B * H, 128, 128)[first:],
+                 s_ref.reshape(B * H, 128, 128)[first:])
+
+
+@pytest.mark.timeout(600)
+def test_decode_k_snapshots_past_4gib(device):
+    """8 rows and 8 snapshots of 8,448 heads: the snapshot array spans 4.1 GiB, so the last snapshots'
+    byte offsets pass 2^32; every snapshot, the rows and the final state against the oracle."""
+    import torch
+    import kda_gated_delta_core_amd as kda
+    B, H, T = 66, 128, 8
+    announce(f"kda_recurrent_k B={B} H={H} k={T} (snapshots {T * B * H * 65536 / 2 ** 30:.2f} GiB)")
+    x = ki.make_batch(9301, B, H, T, -5.0, 0.02)
+    st = dev(x["state"])
+    snaps = torch.full((T, B, H, 128, 128), SENTINEL, device="cuda")
+    out = kda.kda_recurrent_k(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["gate"]), dev(x["beta"]), st,
+                              snapshots=snaps, n_snapshots=T)
+    torch.cuda.synchronize()
+    o_ref, s_ref, sn_ref, _ = oracle.serial(x["q"], x["k"], x["v"], x["gate"], x["beta"], x["state"], n_snap=T)
+    assert_close("out", host(out), o_ref)
+    assert_close("state", host(st), s_ref)
+    assert T * B * H * 65536 > 2 ** 32
+    for t in range(T):
+        assert_close(f"snapshot[{t}]", host(snaps[t]), sn_ref[t])

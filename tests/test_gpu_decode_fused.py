@@ -199,3 +199,11 @@ def test_fused_decode_edges(device, gated):
     assert np.array_equal(host(cs), rcs), "conv state"
     y_ref = oracle.gated_rmsnorm(got.astype(np.float64), og, on, ki.NORM_EPS)
     assert_within_one_ulp("y", oracle.bf16_to_f64(_bits_host(y)), y_ref)
+
+
+@pytest.mark.timeout(600)
+def test_fused_decode_state_past_4gib(device):
+    """The whole-head kernel over 66,000 heads: the state spans 4.03 GiB, so the last heads' byte offsets
+    pass 2^32; every head against the oracle."""
+    B, H = 500, 132
+    _against_oracle(B, 1, H, 4, 0, False, 9310)
