@@ -355,3 +355,39 @@ def test_prefill_max_heads(device):
     num = np.linalg.norm((o[:, :T].astype(np.float64) - o_ref).transpose(2, 0, 1, 3).reshape(H, -1), axis=1)
     den = np.linalg.norm(o_ref.transpose(2, 0, 1, 3).reshape(H, -1), axis=1)
     assert np.all(num <= 1e-4 * den), int(np.argmax(num / den))
+
+
+@pytest.mark.timeout(600)
+def test_prefill_inputs_past_4gib(device):
+    """65 sequences of 1,024 tokens at H=128: each input array spans 4.06 GiB, so the last sequence's
+    q, k, v, gate and out rows lie past 2^32 bytes (its records past 21 GB).  That sequence holds the
+    seeded inputs and is checked against the oracle on every head; the others hold zeros."""
+    import torch
+    import kda_gated_delta_core_amd as kda
+    B, H, T, C = 65, 128, 1024, 64
+    last = B - 1
+    announce(f"kda_chunk_prefill B={B} H={H} T={T} C={C} (inputs {B * T * H * 512 / 2 ** 30:.2f} GiB each)")
+    assert last * T * H * 512 >= 2 ** 32
+    rows = ki.sequence_rows(9320, last, 0, T, H, -5.0)
+    st0 = ki.initial_state(9320, last, H, 0.02)
+    tens = {n: torch.zeros((B, T, H, 128), device="cuda") for n in ("q", "k", "v", "gate")}
+    tens["beta"] = torch.zeros((B, T, H), device="cuda")
+    for n in tens:
+        tens[n][last].copy_(torch.from_numpy(rows[n]))
+    st = torch.zeros((B, H, 128, 128), device="cuda")
+    st[last].copy_(torch.from_numpy(st0))
+    out = torch.full((B, T, H, 128), SENTINEL, device="cuda")
+    ws = torch.empty(kda.kda_chunk_prefill_workspace_bytes(B, H, T, C), dtype=torch.uint8, device="cuda")
+    kda.kda_chunk_prefill(tens["q"], tens["k"], tens["v"], tens["gate"], tens["beta"], st, T, C, out=out,
+                          workspace=ws)
+    torch.cuda.synchronize()
+    del ws, tens
+    o, s = host(out[last:]), host(st[last:])
+    o_ref, s_ref, _, _ = oracle.serial(*(rows[n][None] for n in ("q", "k", "v", "gate", "beta")), st0[None])
+    assert_close("core", o, o_ref)
+    assert_close("state", s, s_ref)
+    for h in range(H):
+        assert_close(f"h{h} core", o[:, :, h], o_ref[:, :, h], quiet=True)
+        assert_close(f"h{h} state", s[:, h], s_ref[:, h], quiet=True)
+    # the zero sequences stay zero: nothing leaked across the 2^32 boundary into them
+    assert not bool(out[:last].abs().amax().item()) and not bool(st[:last].abs().amax().item())
