@@ -5,28 +5,29 @@ Headline (the ``value`` of the JSON line): single-token decode of 64
 sequences x 32 heads, FP32 128x128 key-major state per head updated in place
 (kda_recurrent_step), in tokens/s.  One step = one call over the whole batch.
 The same run also times the other workloads of the core and reports each
-under ``workloads``: the T=8192 chunked prefill, the k=4 decode_k with
-snapshots, the 4 x 32768 long-context prefill followed by 16 decode steps,
-the small T=64 prefill, a packed prefill of 23 sequences of mixed lengths
-(32768 tokens, kda_chunk_prefill_varlen), the decode front end before the core
-(kda_decode_front_end: conv1d update + SiLU + L2, one step at B=64 and the
-k=4 rows at B=128), and the sigmoid-gated RMSNorm after it (kda_gated_rmsnorm)
-on the output of the T=8192 prefill and of a decode step.  The decode step,
-decode_k and the front end are also timed in their BF16 forms (the front end
-writing BF16 q | k | v packed per token, the core reading them).  The
-prefill's front end (kda_prefill_front_end) is timed at the T=8192 H=32
-prefill's shape.  Two chain lines time the block's steps together: the
-decode step on BF16 q | k | v (front end, core, gated RMSNorm) replayed from
-one HIP graph over 8 state sets, and the T=8192 prefill (front end, chunked
-prefill, gated RMSNorm).
+under ``workloads``:
+  * decode: decode_k (k=4, 4 snapshots, B=128), the BF16 q | k | v forms, the gated form (gate and
+    beta formed inside), the whole step from the raw projections in one kernel (kda_decode_fused_step,
+    kda_decode_fused_k), and two chains replayed from one HIP graph (front end + core + gated RMSNorm
+    as three kernels, and with the norm fused into the core);
+  * prefill: T=8192 H=32 at chunk 64 / 32 / 16 (at 64 also split into the scan alone, kda_chunk_scan
+    on the kept records, and the prepare as the rest of the call), 4 x 32768 followed by 16 decode
+    steps, T=64 H=2, the gated form, 23 packed sequences of mixed lengths (kda_chunk_prefill_varlen),
+    the front end fused into the prepare (dense and packed), and the chain front end + prefill + norm;
+  * the token-segment split's per-device pieces: the segment transition, the fold S <- P S + Q, and
+    one device's share of the 4 x 32768 prefill cut into 8 segments (no exchange);
+  * the front ends (decode and prefill, FP32 and BF16 outputs) and the gated RMSNorm on their own;
+  * copy_ceiling: a plain 1 GiB device copy, the practical HBM ceiling beside the vendor's 8 TB/s.
 
 Inputs are seeded synthetic tensors (kda_inputs) resident in HBM before the
 timed region.  Decode states are rotated over buffers totalling >= 1 GiB so
 the 256 MB Infinity Cache cannot hold them: every step reads and writes HBM.
 
 ``roofline`` describes the dominant kernel of the headline (the recurrent
-kernel): algorithmic bytes per launch / average launch duration from HIP
-events around each launch on the launch stream, against 8 TB/s.
+kernel): algorithmic bytes per launch / average launch duration (one HIP event
+pair on the launch stream around back-to-back launches), against 8 TB/s, with
+the counter-measured traffic from the committed rocprofv3 summary while it
+matches the kernel source, and the fraction of the plain copy's rate.
 ``cpu_baseline`` times the fp64 oracle on the host cores (rank 0, N=1) on the headline workload; the
 same oracle is also timed beside the decode_k workload and the three prefill workloads (each
 workload's ``cpu_oracle`` entry, with the threads it used and the sample it ran).
