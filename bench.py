@@ -12,7 +12,8 @@ under ``workloads``:
     as three kernels, and with the norm fused into the core);
   * prefill: T=8192 H=32 at chunk 64 / 32 / 16 (at 64 also split into the scan alone, kda_chunk_scan
     on the kept records, and the prepare as the rest of the call), 4 x 32768 followed by 16 decode
-    steps, T=64 H=2, the gated form, 23 packed sequences of mixed lengths (kda_chunk_prefill_varlen),
+    steps, T=64 H=2, the gated form, BF16 q | k | v (kda_chunk_prefill_bf16), 23 packed sequences of
+    mixed lengths (kda_chunk_prefill_varlen),
     the front end fused into the prepare (dense and packed), and the chain front end + prefill + norm;
   * the token-segment split's per-device pieces: the segment transition, the fold S <- P S + Q, and
     one device's share of the 4 x 32768 prefill cut into 8 segments (no exchange);
@@ -211,6 +212,26 @@ def bench_prefill_gated(torch, kda, ki, steps, warmup, timer):
 
     def step(i):
         kda.kda_chunk_prefill_gated(q, k, v, g, bl, dt, al, ki.GATE_LOWER_BOUND, st, T, C, out=out, workspace=ws)
+
+    return w, timer.run(step, steps, warmup)
+
+
+def bench_prefill_bf16(torch, kda, ki, steps, warmup, timer):
+    """kda_chunk_prefill_bf16 at T=8192 H=32 C=64: the T=8192 prefill workload with q, k, v rounded to BF16
+    and packed per token."""
+    import numpy as np
+    w = ki.WORKLOADS["prefill_h32_t8192_c64"]
+    B, H, T, C = w.batch, w.heads, w.T, w.chunk
+    t_pad = -(-T // C) * C
+    x = ki.workload_inputs(w)
+    qkv = _packed_bf16(torch, ki, {n: np.ascontiguousarray(x[n][:, :t_pad]) for n in ("q", "k", "v")})
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    g, b, st = dev(x["gate"][:, :t_pad]), dev(x["beta"][:, :t_pad]), dev(x["state"])
+    out = torch.empty((B, t_pad, H, D), device="cuda")
+    ws = torch.empty(kda.kda_chunk_prefill_workspace_bytes(B, H, T, C), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        kda.kda_chunk_prefill_bf16(qkv, g, b, st, T, C, out=out, workspace=ws)
 
     return w, timer.run(step, steps, warmup)
 
@@ -846,6 +867,15 @@ def main():
                                                     "call_ms": r["launch_avg_s"] * 1e3,
                                                     "algorithmic_TFLOP_per_s": tf,
                                                     "mfma_frac": tf / MFMA_F32_PEAK_TFLOPS}
+    if want("prefill_bf16_h32_t8192_c64"):
+        log("prefill_bf16_h32_t8192_c64")
+        w, r = bench_prefill_bf16(torch, kda, ki, args.reps or 20, 0 if args.reps else 60, timer)
+        tf = prefill_flops(w.batch, w.heads, w.T, w.chunk) / r["launch_avg_s"] / 1e12
+        workloads["prefill_bf16_h32_t8192_c64"] = {"tokens_per_s": w.batch * w.T / r["s_per_step"],
+                                                   "ms_per_call": r["s_per_step"] * 1e3,
+                                                   "call_ms": r["launch_avg_s"] * 1e3,
+                                                   "algorithmic_TFLOP_per_s": tf,
+                                                   "mfma_frac": tf / MFMA_F32_PEAK_TFLOPS}
     # (timed calls, untimed warm-up calls): once the T=8192 prefill starts, its calls run up to 30%
     # slower for ~15 ms (a device-level transient: the first few calls are fast, then the time rises
     # and settles back over ~30 calls), so it gets 60 untimed calls before the timed ones

@@ -194,6 +194,27 @@ int kda_chunk_prefill_gated(const float* q, const float* k, const float* v, cons
                             size_t workspace_bytes, void* stream);
 
 /*
+ * kda_chunk_prefill on BF16 q, k and v packed per token, the row layout of the
+ * decode path's BF16 forms with the prefill's padding.  The pages keep the
+ * prefill's q, k, v in FP32 (workspace page, fields q_f32 / k_f32 / v_f32);
+ * this form is for callers that hold them in BF16 (module page: the block's
+ * projections run in BF16), and it halves what the prefill reads for them.
+ *
+ *   qkv                            : [batch][T_pad][3][heads][128] BF16 (raw 16-bit patterns): q, then k,
+ *                                    then v of every head for each token, 16-byte aligned
+ *   gate, beta, state, out, workspace : as kda_chunk_prefill
+ *
+ * BF16 widens to FP32 exactly where a chunk is staged and the arithmetic is
+ * that of kda_chunk_prefill, so the results equal kda_chunk_prefill on the
+ * widened q, k, v bit for bit (rows t >= T ignored alike, the same gate
+ * domain).  Refusals are those of kda_chunk_prefill, with qkv in place of q,
+ * k and v.
+ */
+int kda_chunk_prefill_bf16(const uint16_t* qkv, const float* gate, const float* beta, float* state, float* out,
+                           int batch, int heads, int T, int chunk, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
  * Chunked prefill of a packed batch of sequences of their own lengths
  * (varlen).  Same computation as kda_chunk_prefill for every sequence, with
  * the sequences stored back to back instead of padded to a common length (the

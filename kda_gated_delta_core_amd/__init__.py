@@ -38,7 +38,8 @@ EXPORTED = ("kda_status_string", "kda_chunk_prefill_workspace_bytes", "kda_chunk
             "kda_chunk_prefill_fused", "kda_chunk_prefill_varlen_fused", "kda_chunk_prefill_noalloc",
             "kda_chunk_prefill_gated", "kda_recurrent_k_gated", "kda_recurrent_step_gated",
             "kda_recurrent_k_bf16_norm", "kda_recurrent_step_bf16_norm", "kda_decode_fused_k", "kda_decode_fused_step",
-            "kda_decode_fused_k_gated", "kda_decode_fused_step_gated", "kda_chunk_prefill_fused_gated")
+            "kda_decode_fused_k_gated", "kda_decode_fused_step_gated", "kda_chunk_prefill_fused_gated",
+            "kda_chunk_prefill_bf16")
 STATIC_WORKSPACE_BYTES = 256 << 20
 GATED_RMSNORM_MIN_EPS = 1e-30
 
@@ -104,6 +105,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_recurrent_k_bf16.argtypes = [p] * 6 + [i] * 4 + [p]
     lib.kda_recurrent_k_bf16.restype = i
     lib.kda_recurrent_step_bf16.argtypes = [p] * 5 + [i, i, p]
+    lib.kda_chunk_prefill_bf16.argtypes = [p] * 5 + [i] * 4 + [p, sz, p]
+    lib.kda_chunk_prefill_bf16.restype = i
     lib.kda_recurrent_step_bf16.restype = i
     lib.kda_decode_front_end_bf16.argtypes = [p] * 5 + [i] * 5 + [ctypes.c_float, p]
     lib.kda_decode_front_end_bf16.restype = i
@@ -265,6 +268,36 @@ def kda_recurrent_step_bf16(qkv, gate, beta, state, out=None, stream=None):
     rc = load_library().kda_recurrent_step_bf16(*args, B, H, _stream_ptr(stream))
     if rc != KDA_OK:
         raise KdaError("kda_recurrent_step_bf16", rc)
+    return out
+
+
+def kda_chunk_prefill_bf16(qkv, gate, beta, state, T: int, chunk: int, out=None, workspace=None, stream=None):
+    """kda_chunk_prefill with BF16 q | k | v packed per token.  Returns ``out``.
+
+    qkv: bfloat16 [B][T_pad][3 H 128] (or [B][T_pad][3][H][128]); gate, out: [B][T_pad][H][128];
+    beta: [B][T_pad][H]; state and workspace as kda_chunk_prefill.
+    """
+    if chunk not in (16, 32, 64):
+        raise KdaError("kda_chunk_prefill_bf16", KDA_ERR_UNSUPPORTED)
+    B, rows, H, qkv_ptr = _packed_qkv(qkv, gate)
+    t_pad = -(-int(T) // chunk) * chunk
+    if rows != t_pad:
+        raise ValueError(f"inputs must hold T_pad = {t_pad} rows per sequence, got {rows}")
+    vs = (B, t_pad, H, HEAD_DIM)
+    if out is None:
+        out = torch.empty(vs, dtype=torch.float32, device=gate.device)
+    need = kda_chunk_prefill_workspace_bytes(B, H, int(T), chunk)
+    if workspace is None:
+        workspace = _workspace(need, gate.device, stream)
+    if not (workspace.device.type == "cuda" and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rc = load_library().kda_chunk_prefill_bf16(qkv_ptr, _check("gate", gate, vs), _check("beta", beta, (B, t_pad, H)),
+                                               _check("state", state, (B, H, HEAD_DIM, HEAD_DIM)),
+                                               _check("out", out, vs), B, H, int(T), chunk, workspace.data_ptr(),
+                                               ws_bytes, _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_chunk_prefill_bf16", rc)
     return out
 
 

@@ -124,6 +124,33 @@ KDA_API int kda_chunk_prefill(const float* q, const float* k, const float* v, co
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 
+KDA_API int kda_chunk_prefill_bf16(const uint16_t* qkv, const float* gate, const float* beta, float* state, float* out,
+                                   int batch, int heads, int T, int chunk, void* workspace, size_t workspace_bytes,
+                                   void* stream)
+{
+    if (!qkv || !gate || !beta || !state || !out) return KDA_ERR_INVALID_ARG;
+    if (!aligned({qkv, gate, state, out, workspace}) || !aligned({beta}, 4)) return KDA_ERR_INVALID_ARG;
+    if (batch < 1 || heads < 1 || T < 1) return KDA_ERR_INVALID_ARG;
+    if (!chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
+    const int64_t need = prefill_ws_bytes(batch, heads, T, chunk);
+    const int64_t t_pad = ((int64_t)T + chunk - 1) / chunk * chunk;
+    const int64_t x = mul({batch, t_pad, 3, heads, KDA_HEAD_DIM});
+    const int64_t vec = mul({batch, t_pad, heads, KDA_HEAD_DIM});
+    const int64_t sca = mul({batch, t_pad, heads});
+    const int64_t st = mul({batch, heads, KDA_HEAD_DIM, KDA_HEAD_DIM});
+    if (need < 0 || x < 0 || vec < 0 || sca < 0 || st < 0 || t_pad > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)batch * heads > 0x7fffffffLL / 64) return KDA_ERR_INVALID_ARG;  // scan grid
+    if (heads > KDA_PREFILL_MAX_HEADS) return KDA_ERR_INVALID_ARG;  // 32-bit in-chunk byte offsets
+    if ((int64_t)batch * heads * (t_pad / chunk) > (1LL << 30)) return KDA_ERR_INVALID_ARG;  // chunk index
+    if (!workspace || workspace_bytes < (size_t)need) return KDA_ERR_WORKSPACE;
+    const Range r[] = {{out, vec * 4}, {state, st * 4}, {workspace, need}, {qkv, x * 2}, {gate, vec * 4},
+                       {beta, sca * 4}};
+    if (any_overlap(r, 6, 3)) return KDA_ERR_INVALID_ARG;
+    const int rc = kda::launch_chunk_prefill_bf16(qkv, gate, beta, state, out, batch, heads, T, (int)t_pad, chunk,
+                                                  static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
+    return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
 KDA_API int kda_chunk_prefill_gated(const float* q, const float* k, const float* v, const uint16_t* g_raw,
                                     const float* beta_logit, const float* dt_bias, const float* a_log,
                                     float gate_lower_bound, float* state, float* out, int batch, int heads, int T,

@@ -229,6 +229,17 @@ struct PrepInputs {
     float a_log;
 };
 
+// With BF16 q, k, v: the k and q pieces of the chunk being staged as loaded (four
+// BF16 values each) and this chunk's v values, raw; empty for FP32 inputs.
+template <int C, bool kB16>
+struct PrepRaw16 {
+};
+template <int C>
+struct PrepRaw16<C, true> {
+    uint2 kb[PrepInputs<C>::NV4], qb[PrepInputs<C>::NV4];
+    unsigned short vr[C / 16][4];
+};
+
 // Raw buffer descriptors over the rows of one chunk of one (sequence, head) in
 // each input, from row p.row0 and p.span rows long (rows past the end of the
 // buffers read as zeros).  With `live` false the descriptors cover zero bytes:
@@ -262,6 +273,33 @@ __device__ __forceinline__ float prep_load_beta(rsrc_t src, int heads, int tid)
     return tid < C ? buf_ld1(src, tid * heads * 4, 0) : 0.f;
 }
 
+// BF16 q, k, v packed per token as [tokens][3][heads][128] (the FP32 forms'
+// rows with the three parts side by side): descriptors over part `part` of
+// head p.h for the chunk's tokens, 3 heads 128 values apart from token to
+// token.  Dense layout: every chunk has C tokens allocated (T_pad rows).
+template <int C>
+__device__ __forceinline__ rsrc_t prep_src_b16(const unsigned short* qkv, int part, int heads, const ChunkPos& p,
+                                               bool live)
+{
+    const size_t tok = (p.row0 - (size_t)p.h) / (size_t)heads;  // the chunk's first token
+    const size_t base = (tok * 3 + (size_t)part) * heads * kD + (size_t)p.h * kD;
+    const uint32_t bytes = live ? (uint32_t)(((size_t)(C - 1) * 3 * heads * kD + kD) * 2) : 0u;
+    return make_rsrc(qkv + base, bytes);
+}
+// prep_load_part for BF16 rows: the same pieces (rows tid/32 + 16 i, columns 4 (tid % 32) + 0..3), 8 bytes each
+template <int C>
+__device__ __forceinline__ void prep_load_part_b16(uint2 (&dst)[PrepInputs<C>::NV4], rsrc_t src, int heads, int tid)
+{
+    const int voff = ((tid >> 5) * 3 * heads * kD + (tid & 31) * 4) * 2;
+#pragma unroll
+    for (int i = 0; i < PrepInputs<C>::NV4; ++i) dst[i] = buf_ld_b64(src, voff, i * 16 * 3 * heads * kD * 2);
+}
+__device__ __forceinline__ float4 bf16x4(uint2 u)
+{
+    return make_float4(bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xffffu),
+                       bf16_to_f32(u.y >> 16));
+}
+
 // kGate: the g_raw pieces of the thread's gate rows (BF16, 8 bytes per row: columns 4 (tid % 32) +
 // 0..3), its four dt_bias values and the head's a_log.  live false: the g_raw descriptor covers
 // zero bytes (loads return zeros) and the parameters are those of head p.h as ever.
@@ -288,6 +326,18 @@ __device__ __forceinline__ void prep_load_v(float (&vb)[C / 16][4], rsrc_t src, 
     for (int y = 0; y < C / 16; ++y)
 #pragma unroll
         for (int e = 0; e < 4; ++e) vb[y][e] = buf_ld1(src, voff, (16 * y + e) * heads * kD * 4);
+}
+// prep_load_v for BF16 rows: the raw values, widened where they are used
+template <int C>
+__device__ __forceinline__ void prep_load_v_b16(unsigned short (&vr)[C / 16][4], rsrc_t src, int heads, int wave,
+                                                int l16, int q4)
+{
+    const int voff = (4 * q4 * 3 * heads * kD + 16 * wave + l16) * 2;
+#pragma unroll
+    for (int y = 0; y < C / 16; ++y)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            vr[y][e] = __builtin_amdgcn_raw_buffer_load_b16(src, voff, (16 * y + e) * 3 * heads * kD * 2, 0);
 }
 
 // Rows >= T (nvalid and beyond) are replaced by zeros with selects, then the
@@ -317,9 +367,11 @@ constexpr float kSteepGateClampLog2 = 28.f;
 // kFE: k and q are in the fused row order (rows NV4 (tid / 32) + i), the gate
 // in the usual one.
 // kGate: the gate is kda_gate of the g_raw pieces (with `lower`) and beta the sigmoid of the logit.
-template <int C, bool kFE = false, bool kGate = false>
+// kB16: k and q are BF16 pieces (kb, qb), widened exactly here.
+template <int C, bool kFE = false, bool kGate = false, bool kB16 = false>
 __device__ __forceinline__ void prep_stage(const PrepInputs<C>& in, float* sK, float* sQ, float* sL, float* sBeta,
-                                           int* sSteep, int nvalid, int tid, float lower = 0.f)
+                                           int* sSteep, int nvalid, int tid, float lower = 0.f,
+                                           const PrepRaw16<C, kB16>& raw = {})
 {
     using G = ChunkGeom<C>;
     constexpr int NV4 = PrepInputs<C>::NV4, LD = G::kLd;
@@ -332,8 +384,13 @@ __device__ __forceinline__ void prep_stage(const PrepInputs<C>& in, float* sK, f
         const bool ok = r < nvalid;
         const int rq = kFE ? NV4 * (tid >> 5) + i : r;
         const bool okq = rq < nvalid;
-        lds4_st(&sK[rq * LD + c4], okq ? in.k[i] : z4);
-        lds4_st(&sQ[rq * LD + c4], okq ? in.q[i] : z4);
+        if constexpr (kB16) {
+            lds4_st(&sK[rq * LD + c4], okq ? bf16x4(raw.kb[i]) : z4);
+            lds4_st(&sQ[rq * LD + c4], okq ? bf16x4(raw.qb[i]) : z4);
+        } else {
+            lds4_st(&sK[rq * LD + c4], okq ? in.k[i] : z4);
+            lds4_st(&sQ[rq * LD + c4], okq ? in.q[i] : z4);
+        }
         float4 g;
         if constexpr (kGate) {
             const uint2 u = in.gr[i];
@@ -722,7 +779,9 @@ __device__ __forceinline__ void fe_finish_v(const FeV<C>& r, float (&vb)[C / 16]
 // kFE: the front end is fused in (dense layout): q, k and v are formed from
 // the BF16 projections in `fe` (see FeSrc) instead of read as FP32 rows; the
 // q, k, v pointers are then not read.
-template <int C, class Layout, bool kFE = false, bool kGate = false>
+// kB16 (dense layout): q, k, v are BF16, packed per token as [B][T_pad][3][heads][128]
+// at `q` (k and v unused), and widened exactly where they are staged.
+template <int C, class Layout, bool kFE = false, bool kGate = false, bool kB16 = false>
 __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ gate, const float* __restrict__ beta, float* __restrict__ ws, int heads,
@@ -757,6 +816,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
     const int n_total = layout.records();
     int gc = blockIdx.x;
     PrepInputs<C> in;
+    PrepRaw16<C, kB16> raw;
     ChunkPos pos;  // of the gc-th record in processing order
     if (gc < n_total) {
         pos = layout.template chunk<C>(gc);
@@ -766,6 +826,10 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
             fe_load_qk<C>(rk, fe, 1, pos, heads, threadIdx.x, true);
             fe_load_qk<C>(rq, fe, 0, pos, heads, threadIdx.x, true);
             fe_finish_kq<C>(rk, rq, in.k, in.q, pos.t0, threadIdx.x, fe.eps);
+        } else if constexpr (kB16) {
+            const auto* qkv = reinterpret_cast<const unsigned short*>(q);
+            prep_load_part_b16<C>(raw.kb, prep_src_b16<C>(qkv, 1, heads, pos, true), heads, threadIdx.x);
+            prep_load_part_b16<C>(raw.qb, prep_src_b16<C>(qkv, 0, heads, pos, true), heads, threadIdx.x);
         } else {
             prep_load_part<C>(in.k, src.k, heads, threadIdx.x);
             prep_load_part<C>(in.q, src.q, heads, threadIdx.x);
@@ -773,7 +837,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         if constexpr (kGate) prep_load_gate<C>(in, gp, pos, heads, threadIdx.x);
         else prep_load_part<C>(in.g, src.g, heads, threadIdx.x);
         in.beta = prep_load_beta<C>(src.b, heads, threadIdx.x);
-        prep_stage<C, kFE, kGate>(in, sKr, sQr, sKc, sBeta, sSteep, pos.nvalid, threadIdx.x, gp.lower);
+        prep_stage<C, kFE, kGate, kB16>(in, sKr, sQr, sKc, sBeta, sSteep, pos.nvalid, threadIdx.x, gp.lower, raw);
     }
     __syncthreads();
 
@@ -790,6 +854,9 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         float vb[NT][4];  // needed only at step 4c: its latency hides behind steps 2-4
         FeV<C> fv;        // (fused front end: the raw v inputs instead)
         if constexpr (kFE) fe_load_v<C>(fv, fe, pos, heads, wave, l16, q4);
+        else if constexpr (kB16)
+            prep_load_v_b16<C>(raw.vr, prep_src_b16<C>(reinterpret_cast<const unsigned short*>(q), 2, heads, pos, true),
+                               heads, wave, l16, q4);
         else prep_load_v<C>(vb, prep_src(q, k, v, gate, beta, pos).v, heads, wave, l16, q4);
         const int nvalid = pos.nvalid;
         // The next chunk's inputs are read in three parts, at steps 3, 5 and 6,
@@ -912,6 +979,11 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         __builtin_amdgcn_sched_barrier(0);
         FeRaw<C> rk, rq;  // (fused front end: the next chunk's raw k and q)
         if constexpr (kFE) fe_load_qk<C>(rk, fe, 1, npos, heads, tid, gn < n_total);
+        else if constexpr (kB16)
+            prep_load_part_b16<C>(raw.kb,
+                                  prep_src_b16<C>(reinterpret_cast<const unsigned short*>(q), 1, heads, npos,
+                                                  gn < n_total),
+                                  heads, tid);
         else prep_load_part<C>(in.k, nsrc.k, heads, tid);
         __builtin_amdgcn_sched_barrier(0);
         int R, S;
@@ -1032,7 +1104,8 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
                 const int s_ = 16 * y + 4 * q4 + e, i = 16 * wave + l16;
                 const float bb = sBeta[s_];
                 bw[y][e] = bb * (sKr[s_ * LD + i] * ev[y][e]);
-                bu[y][e] = bb * (s_ < nvalid ? vb[y][e] : 0.f);
+                if constexpr (kB16) bu[y][e] = bb * (s_ < nvalid ? bf16_to_f32(raw.vr[y][e]) : 0.f);
+                else bu[y][e] = bb * (s_ < nvalid ? vb[y][e] : 0.f);
                 qh[y][e] = sQr[s_ * LD + i] * ev[y][e];
             }
 
@@ -1049,6 +1122,11 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         float* const xpose = sKc + wave * 256;
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (kFE) fe_load_qk<C>(rq, fe, 0, npos, heads, tid, gn < n_total);
+        else if constexpr (kB16)
+            prep_load_part_b16<C>(raw.qb,
+                                  prep_src_b16<C>(reinterpret_cast<const unsigned short*>(q), 0, heads, npos,
+                                                  gn < n_total),
+                                  heads, tid);
         else prep_load_part<C>(in.q, nsrc.q, heads, tid);
         __builtin_amdgcn_sched_barrier(0);
         floatx4 wt[NT], ut[NT];
@@ -1129,7 +1207,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
         __syncthreads();
         // stage the next chunk (loaded during this one; after the last chunk the
         // staged copy is unused)
-        prep_stage<C, kFE, kGate>(in, sKr, sQr, sKc, sBeta, sSteep, npos.nvalid, tid, gp.lower);
+        prep_stage<C, kFE, kGate, kB16>(in, sKr, sQr, sKc, sBeta, sSteep, npos.nvalid, tid, gp.lower, raw);
         pos = npos;
         __syncthreads();
     }
@@ -1472,7 +1550,7 @@ static int launch_scan_auto(const float* ws, float* state, float* out, long long
 // kTrans: state is the Q output and out the P output of the transition form.
 // kFE: the prepare with the front end fused in (q, k, v unused; fe its inputs).
 // kGate: kda_gate and the beta sigmoid inside the prepare (gate unused, beta the logits; gp its inputs).
-template <int C, class Layout, bool kTrans = false, bool kFE = false, bool kGate = false>
+template <int C, class Layout, bool kTrans = false, bool kFE = false, bool kGate = false, bool kB16 = false>
 static int launch_chunk(const float* q, const float* k, const float* v, const float* gate, const float* beta,
                         float* state, float* out, long long n_bh, int heads, long long max_records, float* ws,
                         const Layout& layout, hipStream_t stream, const FeSrc& fe = FeSrc{},
@@ -1484,7 +1562,7 @@ static int launch_chunk(const float* q, const float* k, const float* v, const fl
     const int n_cu = compute_units();
     if (n_cu < 1) return -1;
     int per_cu = 1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chunk_prepare_kernel<C, Layout, kFE, kGate>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chunk_prepare_kernel<C, Layout, kFE, kGate, kB16>,
                                                      kPrepThreads, 0) != hipSuccess || per_cu < 1) {
         (void)hipGetLastError();  // a failed query leaves no error behind for the launch check below
         per_cu = 1;
@@ -1492,7 +1570,7 @@ static int launch_chunk(const float* q, const float* k, const float* v, const fl
     const long long slots = (long long)n_cu * per_cu;
     const int grid_p = (int)(max_records < slots ? max_records : slots);
     if (grid_p > 0) {
-        hipLaunchKernelGGL((chunk_prepare_kernel<C, Layout, kFE, kGate>), dim3((unsigned)grid_p), dim3(kPrepThreads),
+        hipLaunchKernelGGL((chunk_prepare_kernel<C, Layout, kFE, kGate, kB16>), dim3((unsigned)grid_p), dim3(kPrepThreads),
                            0, stream, q, k, v, gate, beta, ws, heads, layout, fe, gp);
         if (hipGetLastError() != hipSuccess) return -1;
     }
@@ -1519,6 +1597,30 @@ int launch_chunk_prefill(const float* q, const float* k, const float* v, const f
     case 16: return launch_dense<16>(q, k, v, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream);
     case 32: return launch_dense<32>(q, k, v, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream);
     case 64: return launch_dense<64>(q, k, v, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream);
+    default: return -1;
+    }
+}
+
+// The prefill on BF16 q | k | v rows ([B][T_pad][3][heads][128]), passed to the prepare as its q pointer.
+template <int C>
+static int launch_dense_b16(const uint16_t* qkv, const float* gate, const float* beta, float* state, float* out,
+                            int batch, int heads, int T, int t_pad, float* ws, hipStream_t stream)
+{
+    const int nchunks = t_pad / C;
+    const long long n_bh = (long long)batch * heads;
+    const DenseLayout layout{heads, T, t_pad, nchunks, (int)(n_bh * nchunks)};
+    const float* const x = reinterpret_cast<const float*>(qkv);
+    return launch_chunk<C, DenseLayout, false, false, false, true>(x, x, x, gate, beta, state, out, n_bh, heads,
+                                                                  n_bh * nchunks, ws, layout, stream);
+}
+
+int launch_chunk_prefill_bf16(const uint16_t* qkv, const float* gate, const float* beta, float* state, float* out,
+                              int batch, int heads, int T, int t_pad, int chunk, float* workspace, hipStream_t stream)
+{
+    switch (chunk) {
+    case 16: return launch_dense_b16<16>(qkv, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream);
+    case 32: return launch_dense_b16<32>(qkv, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream);
+    case 64: return launch_dense_b16<64>(qkv, gate, beta, state, out, batch, heads, T, t_pad, workspace, stream);
     default: return -1;
     }
 }

@@ -45,6 +45,10 @@ int launch_chunk_prefill(const float* q, const float* k, const float* v, const f
                          float* state, float* out, int batch, int heads, int T, int t_pad, int chunk,
                          float* workspace, hipStream_t stream);
 
+// the prefill on BF16 q | k | v rows qkv [B][T_pad][3][H][128]; the rest as launch_chunk_prefill
+int launch_chunk_prefill_bf16(const uint16_t* qkv, const float* gate, const float* beta, float* state, float* out,
+                              int batch, int heads, int T, int t_pad, int chunk, float* workspace, hipStream_t stream);
+
 // the prefill with kda_gate and the beta sigmoid inside the prepare: beta_logit [B][T_pad][H] logits,
 // gp the gate inputs (g_raw [B][T_pad][H][128] BF16); the rest as launch_chunk_prefill
 int launch_chunk_prefill_gated(const float* q, const float* k, const float* v, const float* beta_logit,

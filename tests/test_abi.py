@@ -108,6 +108,42 @@ def test_prefill_refusals(lib):
 
 
 @no_gpu
+def test_prefill_bf16_refusals(lib):
+    f = lib.kda_chunk_prefill_bf16
+    bad = kda.KDA_ERR_INVALID_ARG
+    need = kda.kda_chunk_prefill_workspace_bytes(1, 2, 64, 16)
+    # qkv, gate, beta, state, out
+    for i in range(5):
+        p = list(P[:5])
+        p[i] = None
+        assert f(*p, 1, 2, 64, 16, P[7], need, None) == bad, i
+    for i in (0, 1, 3, 4):  # 16-byte alignment (beta: 4)
+        p = list(P[:5])
+        p[i] += 8
+        assert f(*p, 1, 2, 64, 16, P[7], need, None) == bad, i
+    p = list(P[:5])
+    p[2] += 2
+    assert f(*p, 1, 2, 64, 16, P[7], need, None) == bad
+    assert f(*P[:5], 0, 2, 64, 16, P[7], need, None) == bad
+    assert f(*P[:5], 1, 0, 64, 16, P[7], need, None) == bad
+    assert f(*P[:5], 1, 2, 0, 16, P[7], need, None) == bad
+    for C in (0, 8, 48, 128):
+        assert f(*P[:5], 1, 2, 64, C, P[7], 1 << 30, None) == kda.KDA_ERR_UNSUPPORTED
+    assert f(*P[:5], 1, 2, 64, 16, P[7], need - 1, None) == kda.KDA_ERR_WORKSPACE
+    assert f(*P[:5], 1, 2, 64, 16, None, need, None) == kda.KDA_ERR_WORKSPACE
+    # out over the packed rows (64 rows x 3 x 2 heads x 128 BF16 = 96 KiB), state over out, workspace over state
+    p = list(P[:5])
+    p[4] = P[0] + 90 * 1024
+    assert f(*p, 1, 2, 64, 16, P[7], need, None) == bad
+    p = list(P[:5])
+    p[3] = P[4] + 4096
+    assert f(*p, 1, 2, 64, 16, P[7], need, None) == bad
+    assert f(*P[:5], 1, 2, 64, 16, P[3] + 128, need, None) == bad
+    assert f(*P[:5], 1, 16385, 64, 16, P[7], 1 << 40, None) == bad  # heads past the in-chunk offsets
+    assert f(*P[:5], 1 << 20, 1 << 10, 1 << 20, 64, P[7], 1 << 62, None) == bad  # size overflow
+
+
+@no_gpu
 def test_recurrent_refusals(lib):
     for i in range(7):
         p = list(P[:7])
