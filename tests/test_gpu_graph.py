@@ -305,3 +305,27 @@ def test_graph_replays_of_the_fused_decode(device):
         st2.copy_(st20)
 
     _capture_and_replay(kda, "fused decode", work, reset, lambda: (y1, o1, st1, cs1, y2, o2, st2, cs2, snaps, csn))
+
+
+def test_graph_replays_of_the_bf16_prefill(device):
+    """kda_chunk_prefill_bf16 (BF16 q | k | v packed per token) captured as one graph."""
+    import kda_gated_delta_core_amd as kda
+    B, T, H, C = 2, 150, 3, 64
+    announce(f"graph capture: BF16 prefill B={B} T={T} H={H}")
+    t_pad = -(-T // C) * C
+    x = ki.make_batch(1560, B, H, T, -5.0, 0.02, alloc_rows=t_pad)
+    bits = np.stack([ki.to_bf16_bits(x[n]) for n in ("q", "k", "v")], axis=2)
+    qkv = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    g, b = torch.from_numpy(x["gate"]).cuda(), torch.from_numpy(x["beta"]).cuda()
+    st0 = torch.from_numpy(x["state"]).cuda()
+    st = torch.empty_like(st0)
+    out = torch.zeros((B, t_pad, H, 128), device="cuda")
+    ws = torch.empty(kda.kda_chunk_prefill_workspace_bytes(B, H, T, C), dtype=torch.uint8, device="cuda")
+
+    def work(s):
+        kda.kda_chunk_prefill_bf16(qkv, g, b, st, T, C, out=out, workspace=ws, stream=s)
+
+    def reset():
+        st.copy_(st0)
+
+    _capture_and_replay(kda, "BF16 prefill", work, reset, lambda: (out[:, :T], st))
