@@ -246,6 +246,21 @@ int kda_chunk_prefill_varlen(const float* q, const float* k, const float* v, con
                              int chunk, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kda_chunk_prefill_varlen on BF16 q, k and v packed per token, as
+ * kda_chunk_prefill_bf16 is to kda_chunk_prefill.
+ *
+ *   qkv : [total_tokens][3][heads][128] BF16 (raw 16-bit patterns), 16-byte aligned
+ *   gate, beta, state, out, cu_seqlens, workspace : as kda_chunk_prefill_varlen
+ *
+ * The results equal kda_chunk_prefill_varlen on the widened q, k, v bit for
+ * bit.  Refusals are those of kda_chunk_prefill_varlen, with qkv in place of
+ * q, k and v.
+ */
+int kda_chunk_prefill_varlen_bf16(const uint16_t* qkv, const float* gate, const float* beta, float* state, float* out,
+                                  const int* cu_seqlens, int n_seqs, int heads, int total_tokens, int chunk,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * kda_prefill_front_end followed by kda_chunk_prefill, fused: the front end
  * (causal conv1d + SiLU, L2 on q and k; module page, pipeline line) runs
  * inside the prefill's prepare kernel, which reads the BF16 projections

@@ -39,7 +39,7 @@ EXPORTED = ("kda_status_string", "kda_chunk_prefill_workspace_bytes", "kda_chunk
             "kda_chunk_prefill_gated", "kda_recurrent_k_gated", "kda_recurrent_step_gated",
             "kda_recurrent_k_bf16_norm", "kda_recurrent_step_bf16_norm", "kda_decode_fused_k", "kda_decode_fused_step",
             "kda_decode_fused_k_gated", "kda_decode_fused_step_gated", "kda_chunk_prefill_fused_gated",
-            "kda_chunk_prefill_bf16")
+            "kda_chunk_prefill_bf16", "kda_chunk_prefill_varlen_bf16")
 STATIC_WORKSPACE_BYTES = 256 << 20
 GATED_RMSNORM_MIN_EPS = 1e-30
 
@@ -97,6 +97,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_chunk_prefill_varlen_workspace_bytes.argtypes = [i, i, i, i]
     lib.kda_chunk_prefill_varlen_workspace_bytes.restype = sz
     lib.kda_chunk_prefill_varlen.argtypes = [p] * 8 + [i] * 4 + [p, sz, p]
+    lib.kda_chunk_prefill_varlen_bf16.argtypes = [p] * 6 + [i] * 4 + [p, sz, p]
+    lib.kda_chunk_prefill_varlen_bf16.restype = ctypes.c_int
     lib.kda_chunk_prefill_varlen.restype = i
     lib.kda_gated_rmsnorm.argtypes = [p] * 4 + [i, i, ctypes.c_float, p]
     lib.kda_gated_rmsnorm.restype = i
@@ -918,6 +920,41 @@ def kda_prefill_front_end_varlen(qkv, conv_w, conv_state, cu_seqlens, heads: int
 
 def kda_chunk_prefill_varlen_workspace_bytes(n_seqs: int, heads: int, total_tokens: int, chunk: int) -> int:
     return int(load_library().kda_chunk_prefill_varlen_workspace_bytes(n_seqs, heads, total_tokens, chunk))
+
+
+def kda_chunk_prefill_varlen_bf16(qkv, gate, beta, state, cu_seqlens, chunk: int, out=None, workspace=None,
+                                  stream=None):
+    """kda_chunk_prefill_varlen with BF16 q | k | v packed per token.  Returns ``out``.
+
+    qkv: bfloat16 [total][3 H 128] (or [total][3][H][128]); gate, out: [total][H][128]; the rest as
+    kda_chunk_prefill_varlen.
+    """
+    if not isinstance(gate, torch.Tensor) or gate.dim() != 3 or gate.shape[-1] != HEAD_DIM:
+        raise ValueError(f"gate must be [total_tokens][heads][{HEAD_DIM}]")
+    total, H, _ = gate.shape
+    if not isinstance(qkv, torch.Tensor) or qkv.dim() not in (2, 4):
+        raise ValueError("qkv must be [total][3 * heads * 128] or [total][3][heads][128]")
+    qshape = (total, 3 * H * HEAD_DIM) if qkv.dim() == 2 else (total, 3, H, HEAD_DIM)
+    if not (isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.dim() == 1 and cu_seqlens.numel() >= 2):
+        raise ValueError("cu_seqlens must be a 1-d tensor of n_seqs + 1 offsets")
+    n = cu_seqlens.numel() - 1
+    vs = (total, H, HEAD_DIM)
+    if out is None:
+        out = torch.empty(vs, dtype=torch.float32, device=gate.device)
+    need = kda_chunk_prefill_varlen_workspace_bytes(n, H, total, chunk)
+    if workspace is None:
+        workspace = _workspace(need, gate.device, stream)
+    if not (workspace.device.type == "cuda" and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    args = [_check("qkv", qkv, qshape, torch.bfloat16), _check("gate", gate, vs), _check("beta", beta, (total, H)),
+            _check("state", state, (n, H, HEAD_DIM, HEAD_DIM)), _check("out", out, vs),
+            _check("cu_seqlens", cu_seqlens, (n + 1,), torch.int32)]
+    rc = load_library().kda_chunk_prefill_varlen_bf16(*args, n, H, total, chunk, workspace.data_ptr(),
+                                                      workspace.numel() * workspace.element_size(),
+                                                      _stream_ptr(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_chunk_prefill_varlen_bf16", rc)
+    return out
 
 
 def kda_chunk_prefill_varlen(q, k, v, gate, beta, state, cu_seqlens, chunk: int, out=None, workspace=None,

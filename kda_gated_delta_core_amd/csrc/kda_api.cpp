@@ -365,6 +365,33 @@ KDA_API int kda_chunk_prefill_varlen(const float* q, const float* k, const float
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 
+KDA_API int kda_chunk_prefill_varlen_bf16(const uint16_t* qkv, const float* gate, const float* beta, float* state,
+                                          float* out, const int* cu_seqlens, int n_seqs, int heads, int total_tokens,
+                                          int chunk, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!qkv || !gate || !beta || !state || !out || !cu_seqlens) return KDA_ERR_INVALID_ARG;
+    if (!aligned({qkv, gate, state, out, workspace}) || !aligned({beta, cu_seqlens}, 4)) return KDA_ERR_INVALID_ARG;
+    if (n_seqs < 1 || heads < 1 || total_tokens < 1 || n_seqs > KDA_VARLEN_MAX_SEQS) return KDA_ERR_INVALID_ARG;
+    if (!chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
+    if (heads > KDA_PREFILL_MAX_HEADS) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)n_seqs * heads > 0x7fffffffLL / 64) return KDA_ERR_INVALID_ARG;  // scan grid
+    const VarlenWs w = varlen_ws(n_seqs, heads, total_tokens, chunk);
+    const int64_t x = mul({total_tokens, 3, heads, KDA_HEAD_DIM});
+    const int64_t vec = mul({total_tokens, heads, KDA_HEAD_DIM});
+    const int64_t sca = mul({total_tokens, heads});
+    const int64_t st = mul({n_seqs, heads, KDA_HEAD_DIM, KDA_HEAD_DIM});
+    if (w.bytes < 0 || x < 0 || vec < 0 || sca < 0 || st < 0) return KDA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < (size_t)w.bytes) return KDA_ERR_WORKSPACE;
+    const Range r[] = {{out, vec * 4},  {state, st * 4}, {workspace, w.bytes}, {qkv, x * 2},
+                       {gate, vec * 4}, {beta, sca * 4}, {cu_seqlens, ((int64_t)n_seqs + 1) * 4}};
+    if (any_overlap(r, 7, 3)) return KDA_ERR_INVALID_ARG;
+    const int rc = kda::launch_chunk_prefill_varlen_bf16(qkv, gate, beta, state, out, cu_seqlens, n_seqs, heads,
+                                                         total_tokens, chunk, static_cast<float*>(workspace),
+                                                         (size_t)w.meta_offset_floats, w.max_records,
+                                                         static_cast<hipStream_t>(stream));
+    return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
 KDA_API int kda_chunk_prefill_varlen_fused(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state,
                                            const float* gate, const float* beta, float* state, float* out,
                                            const int* cu_seqlens, int n_seqs, int heads, int total_tokens, int chunk,

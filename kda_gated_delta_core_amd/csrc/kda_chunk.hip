@@ -275,15 +275,17 @@ __device__ __forceinline__ float prep_load_beta(rsrc_t src, int heads, int tid)
 
 // BF16 q, k, v packed per token as [tokens][3][heads][128] (the FP32 forms'
 // rows with the three parts side by side): descriptors over part `part` of
-// head p.h for the chunk's tokens, 3 heads 128 values apart from token to
-// token.  Dense layout: every chunk has C tokens allocated (T_pad rows).
+// head p.h for the tokens the chunk can read (p.span rows of the FP32 layout:
+// C tokens, fewer at the end of packed sequences), 3 heads 128 values apart
+// from token to token.
 template <int C>
 __device__ __forceinline__ rsrc_t prep_src_b16(const unsigned short* qkv, int part, int heads, const ChunkPos& p,
                                                bool live)
 {
-    const size_t tok = (p.row0 - (size_t)p.h) / (size_t)heads;  // the chunk's first token
+    const size_t tok = (p.row0 - (size_t)p.h) / (size_t)heads;             // the chunk's first token
+    const size_t avail = ((size_t)p.span + (size_t)p.h) / (size_t)heads;   // tokens from there to the end
     const size_t base = (tok * 3 + (size_t)part) * heads * kD + (size_t)p.h * kD;
-    const uint32_t bytes = live ? (uint32_t)(((size_t)(C - 1) * 3 * heads * kD + kD) * 2) : 0u;
+    const uint32_t bytes = live && avail ? (uint32_t)(((avail - 1) * 3 * heads * kD + kD) * 2) : 0u;
     return make_rsrc(qkv + base, bytes);
 }
 // prep_load_part for BF16 rows: the same pieces (rows tid/32 + 16 i, columns 4 (tid % 32) + 0..3), 8 bytes each
@@ -779,8 +781,9 @@ __device__ __forceinline__ void fe_finish_v(const FeV<C>& r, float (&vb)[C / 16]
 // kFE: the front end is fused in (dense layout): q, k and v are formed from
 // the BF16 projections in `fe` (see FeSrc) instead of read as FP32 rows; the
 // q, k, v pointers are then not read.
-// kB16 (dense layout): q, k, v are BF16, packed per token as [B][T_pad][3][heads][128]
-// at `q` (k and v unused), and widened exactly where they are staged.
+// kB16: q, k, v are BF16, packed per token as [B][T_pad][3][heads][128] (dense) or
+// [total][3][heads][128] (packed sequences) at `q` (k and v unused), and widened
+// exactly where they are staged.
 template <int C, class Layout, bool kFE = false, bool kGate = false, bool kB16 = false>
 __global__ __launch_bounds__(kPrepThreads) void chunk_prepare_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
@@ -1873,10 +1876,10 @@ int launch_chunk_prefill_varlen_fused(const uint16_t* qkv, const uint16_t* conv_
     return launch_conv_state_advance_varlen(qkv, conv_state, cu_seqlens, n_seqs, heads, total, 4, stream);
 }
 
-int launch_chunk_prefill_varlen(const float* q, const float* k, const float* v, const float* gate, const float* beta,
-                                float* state, float* out, const int* cu_seqlens, int n_seqs, int heads, int total,
-                                int chunk, float* workspace, size_t meta_offset_floats, long long max_records,
-                                hipStream_t stream)
+template <bool kB16>
+static int launch_varlen(const float* q, const float* k, const float* v, const float* gate, const float* beta,
+                         float* state, float* out, const int* cu_seqlens, int n_seqs, int heads, int total, int chunk,
+                         float* workspace, size_t meta_offset_floats, long long max_records, hipStream_t stream)
 {
     int* const cu = reinterpret_cast<int*>(workspace + meta_offset_floats);
     int* const cb = cu + (n_seqs + 1);
@@ -1886,11 +1889,36 @@ int launch_chunk_prefill_varlen(const float* q, const float* k, const float* v, 
     const VarlenLayout layout{heads, total, n_seqs, cu, cb};
     const long long n_bh = (long long)n_seqs * heads;
     switch (chunk) {
-    case 16: return launch_chunk<16>(q, k, v, gate, beta, state, out, n_bh, heads, max_records, workspace, layout, stream);
-    case 32: return launch_chunk<32>(q, k, v, gate, beta, state, out, n_bh, heads, max_records, workspace, layout, stream);
-    case 64: return launch_chunk<64>(q, k, v, gate, beta, state, out, n_bh, heads, max_records, workspace, layout, stream);
+    case 16:
+        return launch_chunk<16, VarlenLayout, false, false, false, kB16>(q, k, v, gate, beta, state, out, n_bh, heads,
+                                                                         max_records, workspace, layout, stream);
+    case 32:
+        return launch_chunk<32, VarlenLayout, false, false, false, kB16>(q, k, v, gate, beta, state, out, n_bh, heads,
+                                                                         max_records, workspace, layout, stream);
+    case 64:
+        return launch_chunk<64, VarlenLayout, false, false, false, kB16>(q, k, v, gate, beta, state, out, n_bh, heads,
+                                                                         max_records, workspace, layout, stream);
     default: return -1;
     }
+}
+
+int launch_chunk_prefill_varlen_bf16(const uint16_t* qkv, const float* gate, const float* beta, float* state,
+                                     float* out, const int* cu_seqlens, int n_seqs, int heads, int total, int chunk,
+                                     float* workspace, size_t meta_offset_floats, long long max_records,
+                                     hipStream_t stream)
+{
+    const float* const x = reinterpret_cast<const float*>(qkv);
+    return launch_varlen<true>(x, x, x, gate, beta, state, out, cu_seqlens, n_seqs, heads, total, chunk, workspace,
+                               meta_offset_floats, max_records, stream);
+}
+
+int launch_chunk_prefill_varlen(const float* q, const float* k, const float* v, const float* gate, const float* beta,
+                                float* state, float* out, const int* cu_seqlens, int n_seqs, int heads, int total,
+                                int chunk, float* workspace, size_t meta_offset_floats, long long max_records,
+                                hipStream_t stream)
+{
+    return launch_varlen<false>(q, k, v, gate, beta, state, out, cu_seqlens, n_seqs, heads, total, chunk, workspace,
+                                meta_offset_floats, max_records, stream);
 }
 
 }  // namespace kda

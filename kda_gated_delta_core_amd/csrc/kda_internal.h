@@ -95,6 +95,12 @@ int launch_chunk_prefill_varlen(const float* q, const float* k, const float* v, 
                                 int chunk, float* workspace, size_t meta_offset_floats, long long max_records,
                                 hipStream_t stream);
 
+// the varlen prefill on BF16 q | k | v rows qkv [total][3][H][128]; the rest as launch_chunk_prefill_varlen
+int launch_chunk_prefill_varlen_bf16(const uint16_t* qkv, const float* gate, const float* beta, float* state,
+                                     float* out, const int* cu_seqlens, int n_seqs, int heads, int total, int chunk,
+                                     float* workspace, size_t meta_offset_floats, long long max_records,
+                                     hipStream_t stream);
+
 // outputs FP32 q, k, v [B][T][H][128]; or, when conv_out is not null, BF16 [B][T][3][H][128] there
 int launch_front_end(const uint16_t* qkv, const uint16_t* conv_w, float* conv_state, float* q, float* k, float* v,
                      uint16_t* conv_out, float* snaps, int n_snap, int batch, int heads, int T, int conv_kernel,

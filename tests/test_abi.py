@@ -144,6 +144,35 @@ def test_prefill_bf16_refusals(lib):
 
 
 @no_gpu
+def test_varlen_bf16_refusals(lib):
+    f = lib.kda_chunk_prefill_varlen_bf16
+    bad = kda.KDA_ERR_INVALID_ARG
+    need = kda.kda_chunk_prefill_varlen_workspace_bytes(2, 2, 100, 16)
+    # qkv, gate, beta, state, out, cu_seqlens
+    for i in range(6):
+        p = list(P[:6])
+        p[i] = None
+        assert f(*p, 2, 2, 100, 16, P[7], need, None) == bad, i
+    for i, off in ((0, 8), (1, 8), (2, 2), (3, 8), (4, 8), (5, 2)):
+        p = list(P[:6])
+        p[i] += off
+        assert f(*p, 2, 2, 100, 16, P[7], need, None) == bad, i
+    assert f(*P[:6], 0, 2, 100, 16, P[7], need, None) == bad
+    assert f(*P[:6], 2, 0, 100, 16, P[7], need, None) == bad
+    assert f(*P[:6], 2, 2, 0, 16, P[7], need, None) == bad
+    assert f(*P[:6], (1 << 20) + 1, 2, 100, 16, P[7], 1 << 40, None) == bad
+    for C in (0, 8, 48, 128):
+        assert f(*P[:6], 2, 2, 100, C, P[7], 1 << 30, None) == kda.KDA_ERR_UNSUPPORTED
+    assert f(*P[:6], 2, 2, 100, 16, P[7], need - 1, None) == kda.KDA_ERR_WORKSPACE
+    assert f(*P[:6], 2, 2, 100, 16, None, need, None) == kda.KDA_ERR_WORKSPACE
+    p = list(P[:6])
+    p[4] = P[0] + 1024  # out over the packed rows
+    assert f(*p, 2, 2, 100, 16, P[7], need, None) == bad
+    assert f(*P[:6], 2, 2, 100, 16, P[5], need, None) == bad  # workspace over cu_seqlens
+    assert f(*P[:6], 2, 16385, 100, 16, P[7], 1 << 40, None) == bad
+
+
+@no_gpu
 def test_recurrent_refusals(lib):
     for i in range(7):
         p = list(P[:7])

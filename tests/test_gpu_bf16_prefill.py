@@ -75,3 +75,38 @@ def test_bf16_prefill_full_size_matches_oracle(device):
     for h in range(w.heads):
         assert_close(f"h{h} core", o[:, :T, h], o_ref[:, :, h], quiet=True)
         assert_close(f"h{h} state", s[:, h], s_ref[:, h], quiet=True)
+
+
+@pytest.mark.parametrize("C", [16, 32, 64])
+def test_varlen_bf16_equals_fp32_varlen_on_widened_inputs(device, C):
+    """kda_chunk_prefill_varlen_bf16: packed sequences (empty, one-token, ragged and multi-chunk ones, and
+    rows after the last sequence), bit for bit equal to kda_chunk_prefill_varlen on the widened values."""
+    import kda_gated_delta_core_amd as kda
+    lens = [0, 1, 70, 130, 5, 200, 64]
+    H = 3
+    announce(f"kda_chunk_prefill_varlen_bf16 lens={lens} H={H} C={C}")
+    x = ki.varlen_inputs(9450 + C, lens, H, -5.0, 0.02, pad_tokens=9)
+    total = x["q"].shape[0]
+    parts = [_bf16(x[n]) for n in ("q", "k", "v")]
+    packed = np.ascontiguousarray(np.stack([p[0] for p in parts], axis=1))  # [total][3][H][128]
+    qw, kw, vw = (p[1] for p in parts)
+    g, b, cu = dev(x["gate"]), dev(x["beta"]), torch.from_numpy(x["cu_seqlens"]).cuda()
+    st16, st32 = dev(x["state"]), dev(x["state"])
+    o16 = torch.full((total, H, 128), SENTINEL, device="cuda")
+    o32 = torch.full((total, H, 128), SENTINEL, device="cuda")
+    kda.kda_chunk_prefill_varlen_bf16(_bits_dev(packed), g, b, st16, cu, C, out=o16)
+    kda.kda_chunk_prefill_varlen(dev(qw), dev(kw), dev(vw), g, b, st32, cu, C, out=o32)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32), "out differs from kda_chunk_prefill_varlen on the widened inputs"
+    assert torch.equal(st16, st32), "state differs from kda_chunk_prefill_varlen on the widened inputs"
+    assert bool((o16[sum(lens):] == SENTINEL).all()), "rows after the last sequence were written"
+    # and the oracle on the widened values, sequence by sequence
+    o = host(o16)
+    for s, (a, e) in enumerate(zip(x["cu_seqlens"][:-1], x["cu_seqlens"][1:])):
+        if e == a:
+            assert np.array_equal(host(st16)[s], x["state"][s]), "an empty sequence's state changed"
+            continue
+        sub = [np.ascontiguousarray(t[None, a:e]) for t in (qw, kw, vw, x["gate"], x["beta"])]
+        o_ref, s_ref, _, _ = oracle.serial(*sub, x["state"][s:s + 1])
+        assert_close(f"seq {s} out", o[None, a:e], o_ref)
+        assert_close(f"seq {s} state", host(st16)[s:s + 1], s_ref)
