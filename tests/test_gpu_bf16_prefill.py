@@ -110,3 +110,21 @@ def test_varlen_bf16_equals_fp32_varlen_on_widened_inputs(device, C):
         o_ref, s_ref, _, _ = oracle.serial(*sub, x["state"][s:s + 1])
         assert_close(f"seq {s} out", o[None, a:e], o_ref)
         assert_close(f"seq {s} state", host(st16)[s:s + 1], s_ref)
+
+
+_RNG = np.random.default_rng(20261204)
+RANDOM = [(int(_RNG.integers(1, 4)), int(_RNG.integers(1, 9)), int(_RNG.integers(1, 400)),
+           int(_RNG.choice([16, 32, 64])), float(_RNG.uniform(-20.0, 0.0)), int(_RNG.integers(0, 10 ** 6)))
+          for _ in range(8)]
+
+
+@pytest.mark.parametrize("B,H,T,C,lo,seed", RANDOM)
+def test_bf16_prefill_random_shapes(device, B, H, T, C, lo, seed):
+    """Seeded random batch, heads, length, chunk width and gate range: bit for bit the FP32 prefill on the
+    widened values."""
+    import kda_gated_delta_core_amd as kda
+    announce(f"kda_chunk_prefill_bf16 B={B} H={H} T={T} C={C} gates [{lo:.1f}, 0] seed={seed}")
+    t_pad = -(-T // C) * C
+    x = ki.make_batch(seed, B, H, T, lo, 0.02, alloc_rows=t_pad, pad_value=float("nan"))
+    (o16, s16), (o32, s32), _ = _both(kda, x, T, C)
+    assert torch.equal(o16, o32) and torch.equal(s16, s32)
